@@ -1,0 +1,242 @@
+"""Benchmark of the HiLS attention hot path on one MI355X.
+
+One step = the whole prefill forward (landmark summaries, chunk scoring + top-K,
+intra-chunk attention + inter-chunk fusion) over the 345M-class workload
+(B=1, H=16, d=64, T=8192, S=64, K=16, bf16 storage, float32 accumulation),
+inputs resident in HBM. Also reported: 128K-context decode (256 steps, one query
+per step, incremental summaries), per-kernel roofline fractions measured with
+HIP events on the stream the kernels run on, and the CPU oracle timed on a
+bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_counts(w, idx_host):
+    """Per-step algorithmic work of each kernel (bytes that must move / flops)."""
+    B, T, H, Hkv, d, S, K = w.B, w.T, w.H, w.Hkv, w.d, w.S, w.K
+    NC = T // S
+    esz = 2  # bf16
+    sel_pairs = int((idx_host >= 0).sum())                 # (row, selected chunk) pairs
+    own_keys = B * H * sum(i % S + 1 for i in range(T))    # causal own-chunk key visits
+    key_visits = sel_pairs * S + own_keys
+    cand = B * H * sum(i // S for i in range(T))           # scored candidates
+    summ_bytes = B * T * Hkv * d * esz + B * NC * H * d * esz + B * NC * H * (d + 2) * 4
+    score_flops = 2 * d * cand
+    score_bytes = B * T * H * d * esz + B * NC * H * (d + 1) * 4 + B * T * H * K * 8
+    attend_flops = 4 * d * key_visits
+    attend_bytes = (2 * B * T * H * d * esz + 2 * B * T * Hkv * d * esz + B * T * H * K * 8
+                    + B * T * H * 8)
+    return dict(summarize=dict(bytes=summ_bytes), score_topk=dict(flops=score_flops,
+                bytes=score_bytes), attend_fuse=dict(flops=attend_flops, bytes=attend_bytes),
+                key_visits=key_visits, sel_pairs=sel_pairs, candidates=cand)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the HiLS path here runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import hierarchical_sparse_attention_amd as hsa
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = synth.workloads()["prefill_345m"]
+    log(f"generating {w.name} inputs")
+    x = synth.make_inputs(w)
+    t = {k: torch.from_numpy(x[k]).to(dev, torch.bfloat16) for k in ("Q", "K", "V", "Ql")}
+    B, T, H, Hkv, d, S, K = w.B, w.T, w.H, w.Hkv, w.d, w.S, w.K
+    NC = T // S
+    stream = torch.cuda.current_stream()
+
+    # persistent outputs so the timed region allocates only workspaces (cached by torch)
+    ksum = torch.empty(B, NC, H, d, device=dev)
+    ent = torch.empty(B, NC, H, device=dev)
+    lse_l = torch.empty(B, NC, H, device=dev)
+    idx = torch.empty(B, T, H, K, dtype=torch.int32, device=dev)
+    score = torch.empty(B, T, H, K, device=dev)
+    O = torch.empty_like(t["Q"])
+    lse_own = torch.empty(B, T, H, device=dev)
+    lse_tot = torch.empty(B, T, H, device=dev)
+
+    def k_sum():
+        hsa.summarize(t["K"], t["Ql"], S, ksum=ksum, ent=ent, lse_l=lse_l)
+
+    def k_score():
+        hsa.score_topk(t["Q"], ksum, ent, K, S, 0, T, Hkv=Hkv, idx=idx, score=score)
+
+    def k_attend():
+        hsa.attend_fuse(t["Q"], t["K"], t["V"], idx, score, S, O=O, lse_own=lse_own,
+                        lse_tot=lse_tot)
+
+    def step():
+        k_sum()
+        k_score()
+        k_attend()
+
+    log("warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # per-kernel durations with HIP events on the stream the kernels run on
+    kern = {}
+    for name, fn in (("summarize", k_sum), ("score_topk", k_score), ("attend_fuse", k_attend)):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        kern[name] = ev[0].elapsed_time(ev[1]) / args.steps  # ms per launch
+    idx_host = idx.cpu().numpy()
+    cnt = algorithmic_counts(w, idx_host)
+    ach_attend = cnt["attend_fuse"]["flops"] / (kern["attend_fuse"] * 1e-3) / 1e12
+    ach_score_bw = cnt["score_topk"]["bytes"] / (kern["score_topk"] * 1e-3) / 1e9
+    ach_sum = cnt["summarize"]["bytes"] / (kern["summarize"] * 1e-3) / 1e9
+    dominant = max(kern, key=kern.get)
+    if dominant == "summarize":
+        roof = dict(bound="hbm", achieved=ach_sum, peak=HBM_PEAK_GBS, unit="GB/s")
+    elif dominant == "score_topk":
+        roof = dict(bound="hbm", achieved=ach_score_bw, peak=HBM_PEAK_GBS, unit="GB/s")
+    else:
+        roof = dict(bound="mfma", achieved=ach_attend, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dominant
+    roof["ms_per_launch"] = kern[dominant]
+
+    extra = {"kernels_ms": kern,
+             "attend_tflops": ach_attend, "summarize_gbs": ach_sum, "score_topk_gbs": ach_score_bw,
+             "key_visits": cnt["key_visits"], "candidates": cnt["candidates"]}
+
+    # ---------------------------------------------------------------- decode
+    if not args.no_decode:
+        wd = synth.workloads()["decode_128k"]
+        log("generating decode_128k inputs")
+        xd = synth.make_inputs(wd)
+        td = {k: torch.from_numpy(xd[k]).to(dev, torch.bfloat16) for k in ("Q", "K", "V", "Ql")}
+        del xd
+        NCd = wd.T // wd.S
+        dk = torch.empty(1, NCd, wd.H, wd.d, device=dev)
+        de = torch.empty(1, NCd, wd.H, device=dev)
+        dl = torch.empty(1, NCd, wd.H, device=dev)
+        p0 = wd.q_pos0
+        hsa.summarize(td["K"], td["Ql"], wd.S, 0, p0 // wd.S, Tkv=p0, ksum=dk, ent=de, lse_l=dl)
+        didx = torch.empty(1, 1, wd.H, wd.K, dtype=torch.int32, device=dev)
+        dsc = torch.empty(1, 1, wd.H, wd.K, device=dev)
+        dO = torch.empty(1, 1, wd.H, wd.d, dtype=torch.bfloat16, device=dev)
+        dlo = torch.empty(1, 1, wd.H, device=dev)
+        dlt = torch.empty(1, 1, wd.H, device=dev)
+        nsteps = min(args.decode_steps, wd.rows_q)
+
+        def dstep(s):
+            p = p0 + s
+            if (p % wd.S) == 0 and p > p0:  # chunk p/S - 1 just completed
+                c = p // wd.S - 1
+                hsa.summarize(td["K"], td["Ql"], wd.S, c, c + 1, Tkv=p, ksum=dk, ent=de,
+                              lse_l=dl)
+            q = td["Q"][:, s:s + 1]
+            hsa.score_topk(q, dk, de, wd.K, wd.S, p, p + 1, Hkv=wd.Hkv, idx=didx, score=dsc)
+            hsa.attend_fuse(q, td["K"], td["V"], didx, dsc, wd.S, p, p + 1, O=dO, lse_own=dlo,
+                            lse_tot=dlt)
+
+        for s in range(8):
+            dstep(s)
+        torch.cuda.synchronize()
+        # restore summaries for the timed pass (warmup summarised nothing new: p < p0+64)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for s in range(nsteps):
+            dstep(s)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        dec_us = ev[0].elapsed_time(ev[1]) * 1e3 / nsteps
+        dec_bytes = (NCd * wd.H * (wd.d + 1) * 4 + wd.K * wd.S * wd.H * wd.d * 2 * 2
+                     + 32 * wd.H * wd.d * 2 * 2)
+        extra["decode_us_per_token"] = dec_us
+        extra["decode_gbs_wallclock"] = dec_bytes / (dec_us * 1e-6) / 1e9
+        extra["decode_steps"] = nsteps
+
+    # ---------------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rng = np.random.default_rng(0)
+        nrows = 4096
+        rows = np.sort(rng.choice(B * T * H, size=nrows, replace=False))
+        log(f"cpu baseline: oracle on {nrows} sampled rows")
+        t0 = time.perf_counter()
+        oks, oent, _ = oracle.summarize(x["K"], x["Ql"], S)
+        t_sum = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oidx, osc, _ = oracle.score_topk(x["Q"], oks, oent, S, K, rows=rows)
+        oracle.attend_fuse(x["Q"], x["K"], x["V"], oidx, osc, S, rows=rows)
+        t_rows = time.perf_counter() - t0
+        t_full = t_sum + t_rows * (B * T * H) / nrows
+        cpu = {"value": B * T / t_full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"all {NC * H} landmark summaries + {nrows} of {B * T * H} (row, head) "
+                         f"queries scored/selected/attended, scaled to the full step "
+                         f"({t_sum:.2f}s + {t_rows:.2f}s measured)"}
+
+    out = {
+        "metric": "HiLS prefill tokens/s + 128K decode us/token; % of HBM BW / bf16 MFMA peak",
+        "value": B * T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_345m: B=1 H=16 Hkv=16 d=64 T=8192 S=64 K=16, N(0,1) "
+                               "+ 1 planted-peak chunk", "global_batch": B, "seq_len": T,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

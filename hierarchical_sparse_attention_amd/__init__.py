@@ -1,0 +1,220 @@
+"""Python binding of libhils, the MI355X HiLS attention library.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in include/hils.h. torch supplies device memory and the current HIP
+stream. There is no CPU fallback: if libhils.so is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["HilsError", "lib", "make_dims", "summarize", "score_topk", "attend_fuse", "backward",
+           "forward", "workspace_size", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhils.so")
+
+HILS_F32, HILS_BF16 = 0, 1
+OP_SUMMARIZE, OP_SCORE_TOPK, OP_ATTEND_FUSE, OP_BACKWARD = 0, 1, 2, 3
+STATUS = {0: "HILS_OK", 1: "HILS_ERR_INVALID_ARG", 2: "HILS_ERR_UNSUPPORTED",
+          3: "HILS_ERR_WORKSPACE", 4: "HILS_ERR_HIP"}
+EXPORTS = ("hils_workspace_size", "hils_summarize", "hils_score_topk", "hils_attend_fuse",
+           "hils_backward", "hils_status_string", "hils_version")
+
+
+class hils_dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Tq", ctypes.c_int32), ("Tkv", ctypes.c_int32),
+                ("Tkv_cap", ctypes.c_int32), ("NC_cap", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("q_pos0", ctypes.c_int64), ("scale", ctypes.c_float),
+                ("reserved2", ctypes.c_float)]
+
+
+class HilsError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def lib():
+    """Load libhils.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m hierarchical_sparse_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, VP, SZ = ctypes.POINTER(hils_dims), ctypes.c_void_p, ctypes.c_size_t
+        i32 = ctypes.c_int32
+        L.hils_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(SZ)]
+        L.hils_summarize.argtypes = [P, VP, VP, i32, i32, VP, VP, VP, VP, SZ, VP]
+        L.hils_score_topk.argtypes = [P, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.hils_attend_fuse.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.hils_backward.argtypes = [P] + [VP] * 15 + [VP, SZ, VP]
+        L.hils_status_string.argtypes = [ctypes.c_int]
+        L.hils_status_string.restype = ctypes.c_char_p
+        L.hils_version.restype = i32
+        for f in ("hils_workspace_size", "hils_summarize", "hils_score_topk", "hils_attend_fuse",
+                  "hils_backward"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return HILS_F32
+    if t.dtype == torch.bfloat16:
+        return HILS_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def make_dims(B, Tq, Tkv, H, Hkv, d, S, K, dtype, q_pos0=0, scale=0.0, Tkv_cap=0,
+              NC_cap=0) -> hils_dims:
+    return hils_dims(B, Tq, Tkv, Tkv_cap, NC_cap, H, Hkv, d, S, K, dtype, 0, q_pos0, scale, 0.0)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise HilsError(fn, st)
+
+
+def _need(t: torch.Tensor, name: str, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def workspace_size(dims: hils_dims, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("hils_workspace_size", lib().hils_workspace_size(ctypes.byref(dims), op, ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(dims, op, device):
+    n = workspace_size(dims, op)
+    return (torch.empty(max(n, 256), dtype=torch.uint8, device=device), n)
+
+
+def summarize(K: torch.Tensor, Ql: torch.Tensor, S: int = 64, c_begin: int = 0,
+              c_end: Optional[int] = None, Tkv: Optional[int] = None, scale: float = 0.0,
+              ksum=None, ent=None, lse_l=None):
+    """Landmark summaries of chunks [c_begin, c_end). K [B,Tcap,Hkv,d], Ql [B,NCcap,H,d].
+
+    Returns (ksum [B,NCcap,H,d] f32, ent [B,NCcap,H] f32, lse_l [B,NCcap,H] f32).
+    """
+    B, Tcap, Hkv, d = K.shape
+    NCcap, H = Ql.shape[1], Ql.shape[2]
+    Tkv = Tcap if Tkv is None else Tkv
+    c_end = Tkv // S if c_end is None else c_end
+    _need(K, "K"), _need(Ql, "Ql", (B, NCcap, H, d), K.dtype)
+    dev = K.device
+    ksum = torch.empty(B, NCcap, H, d, dtype=torch.float32, device=dev) if ksum is None else ksum
+    ent = torch.empty(B, NCcap, H, dtype=torch.float32, device=dev) if ent is None else ent
+    lse_l = torch.empty(B, NCcap, H, dtype=torch.float32, device=dev) if lse_l is None else lse_l
+    _need(ksum, "ksum", (B, NCcap, H, d), torch.float32)
+    _need(ent, "ent", (B, NCcap, H), torch.float32)
+    _need(lse_l, "lse_l", (B, NCcap, H), torch.float32)
+    dims = make_dims(B, 0, Tkv, H, Hkv, d, S, 1, _dtype_code(K), 0, scale, Tcap, NCcap)
+    _check("hils_summarize", lib().hils_summarize(
+        ctypes.byref(dims), _ptr(K), _ptr(Ql), c_begin, c_end, _ptr(ksum), _ptr(ent), _ptr(lse_l),
+        None, 0, _stream(dev)))
+    return ksum, ent, lse_l
+
+
+def score_topk(Q: torch.Tensor, ksum: torch.Tensor, ent: torch.Tensor, K_sel: int, S: int = 64,
+               q_pos0: int = 0, Tkv: Optional[int] = None, scale: float = 0.0, Hkv: int = 1,
+               idx=None, score=None):
+    """Top-K chunk selection for query rows at positions q_pos0.. -> (idx int32, score f32)."""
+    B, Tq, H, d = Q.shape
+    NCcap = ksum.shape[1]
+    Tkv = q_pos0 + Tq if Tkv is None else Tkv
+    _need(Q, "Q"), _need(ksum, "ksum", (B, NCcap, H, d), torch.float32)
+    _need(ent, "ent", (B, NCcap, H), torch.float32)
+    dev = Q.device
+    idx = torch.empty(B, Tq, H, K_sel, dtype=torch.int32, device=dev) if idx is None else idx
+    score = torch.empty(B, Tq, H, K_sel, dtype=torch.float32, device=dev) if score is None else score
+    _need(idx, "idx", (B, Tq, H, K_sel), torch.int32)
+    _need(score, "score", (B, Tq, H, K_sel), torch.float32)
+    dims = make_dims(B, Tq, Tkv, H, Hkv, d, S, K_sel, _dtype_code(Q), q_pos0, scale,
+                     max(Tkv, NCcap * S), NCcap)
+    ws, n = _workspace(dims, OP_SCORE_TOPK, dev)
+    _check("hils_score_topk", lib().hils_score_topk(
+        ctypes.byref(dims), _ptr(Q), _ptr(ksum), _ptr(ent), _ptr(idx), _ptr(score), _ptr(ws), n,
+        _stream(dev)))
+    return idx, score
+
+
+def attend_fuse(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor,
+                score: torch.Tensor, S: int = 64, q_pos0: int = 0, Tkv: Optional[int] = None,
+                scale: float = 0.0, O=None, lse_own=None, lse_tot=None):
+    """Hierarchical attention -> (O [B,Tq,H,d], lse_own [B,Tq,H], lse_tot [B,Tq,H])."""
+    B, Tq, H, d = Q.shape
+    Tcap, Hkv = K.shape[1], K.shape[2]
+    K_sel = idx.shape[-1]
+    Tkv = Tcap if Tkv is None else Tkv
+    _need(Q, "Q"), _need(K, "K", (B, Tcap, Hkv, d), Q.dtype), _need(V, "V", (B, Tcap, Hkv, d), Q.dtype)
+    _need(idx, "idx", (B, Tq, H, K_sel), torch.int32)
+    _need(score, "score", (B, Tq, H, K_sel), torch.float32)
+    dev = Q.device
+    O = torch.empty_like(Q) if O is None else O
+    lse_own = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if lse_own is None else lse_own
+    lse_tot = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if lse_tot is None else lse_tot
+    _need(O, "O", Q.shape, Q.dtype)
+    dims = make_dims(B, Tq, Tkv, H, Hkv, d, S, K_sel, _dtype_code(Q), q_pos0, scale, Tcap, 0)
+    ws, n = _workspace(dims, OP_ATTEND_FUSE, dev)
+    _check("hils_attend_fuse", lib().hils_attend_fuse(
+        ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(score), _ptr(O),
+        _ptr(lse_own), _ptr(lse_tot), _ptr(ws), n, _stream(dev)))
+    return O, lse_own, lse_tot
+
+
+def forward(Q, K, V, Ql, K_sel: int, S: int = 64, scale: float = 0.0):
+    """Prefill forward: summaries, selection, attention. Returns a dict of tensors."""
+    ksum, ent, lse_l = summarize(K, Ql, S, scale=scale)
+    idx, score = score_topk(Q, ksum, ent, K_sel, S, 0, K.shape[1], scale, Hkv=K.shape[2])
+    O, lse_own, lse_tot = attend_fuse(Q, K, V, idx, score, S, 0, scale=scale)
+    return dict(ksum=ksum, ent=ent, lse_l=lse_l, idx=idx, score=score, O=O, lse_own=lse_own,
+                lse_tot=lse_tot)
+
+
+def backward(Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, dO, S: int = 64,
+             scale: float = 0.0):
+    """Gradients (dQ, dK, dV, dQl) of sum(dO * O) with the selection held fixed."""
+    B, T, H, d = Q.shape
+    Hkv = K.shape[2]
+    K_sel = idx.shape[-1]
+    NC = Ql.shape[1]
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (Ql, "Ql"), (dO, "dO")):
+        _need(t, n, dtype=Q.dtype)
+    _need(ksum, "ksum", (B, NC, H, d), torch.float32)
+    _need(idx, "idx", (B, T, H, K_sel), torch.int32)
+    dev = Q.device
+    dQ, dK, dV, dQl = (torch.empty_like(x) for x in (Q, K, V, Ql))
+    dims = make_dims(B, T, T, H, Hkv, d, S, K_sel, _dtype_code(Q), 0, scale, T, NC)
+    ws, n = _workspace(dims, OP_BACKWARD, dev)
+    _check("hils_backward", lib().hils_backward(
+        ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(Ql), _ptr(ksum), _ptr(ent),
+        _ptr(lse_l), _ptr(idx), _ptr(score), _ptr(lse_tot), _ptr(dO), _ptr(dQ), _ptr(dK),
+        _ptr(dV), _ptr(dQl), _ptr(ws), n, _stream(dev)))
+    return dQ, dK, dV, dQl

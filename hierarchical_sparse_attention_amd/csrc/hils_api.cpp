@@ -1,0 +1,165 @@
+// C-ABI entry points of libhils: argument validation, workspace sizing and
+// kernel dispatch. Every check happens before anything is enqueued.
+#include <cmath>
+#include <cstdint>
+
+#include "hils.h"
+#include "hils_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hils_status resolve(const hils_dims* in, hils::Dims* out) {
+  if (in == nullptr || out == nullptr) return HILS_ERR_INVALID_ARG;
+  const hils_dims& d = *in;
+  if (d.reserved != 0 || d.reserved2 != 0.0f) return HILS_ERR_INVALID_ARG;
+  if (d.B < 1 || d.Tq < 0 || d.Tkv < 1 || d.H < 1 || d.Hkv < 1 || d.H % d.Hkv != 0)
+    return HILS_ERR_INVALID_ARG;
+  if (d.dtype != HILS_F32 && d.dtype != HILS_BF16) return HILS_ERR_INVALID_ARG;
+  if (d.S < 1 || d.d < 1 || d.K < 1) return HILS_ERR_INVALID_ARG;
+  if (d.S != hils::kChunk || (d.d != 64 && d.d != 128) || d.K > 64) return HILS_ERR_UNSUPPORTED;
+  if (d.q_pos0 < 0 || d.q_pos0 + d.Tq > d.Tkv) return HILS_ERR_INVALID_ARG;
+  if (d.Tkv_cap < 0 || d.NC_cap < 0) return HILS_ERR_INVALID_ARG;
+  const int Tcap = d.Tkv_cap ? d.Tkv_cap : d.Tkv;
+  if (Tcap < d.Tkv) return HILS_ERR_INVALID_ARG;
+  const int NCcap = d.NC_cap ? d.NC_cap : Tcap / d.S;
+  if (NCcap < d.Tkv / d.S) return HILS_ERR_INVALID_ARG;
+  if (!std::isfinite(d.scale) || d.scale < 0.0f) return HILS_ERR_INVALID_ARG;
+  out->B = d.B;
+  out->Tq = d.Tq;
+  out->Tkv = d.Tkv;
+  out->Tcap = Tcap;
+  out->NCcap = NCcap;
+  out->H = d.H;
+  out->Hkv = d.Hkv;
+  out->G = d.H / d.Hkv;
+  out->d = d.d;
+  out->S = d.S;
+  out->K = d.K;
+  out->bf16 = d.dtype == HILS_BF16;
+  out->q_pos0 = d.q_pos0;
+  out->scale = d.scale != 0.0f ? d.scale : 1.0f / std::sqrt((float)d.d);
+  return HILS_OK;
+}
+
+hils_status backward_shape_ok(const hils::Dims& dm) {
+  if (dm.q_pos0 != 0 || dm.Tq != dm.Tkv || dm.Tkv % dm.S != 0) return HILS_ERR_UNSUPPORTED;
+  return HILS_OK;
+}
+
+hils_status from_hip(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_ERR_HIP; }
+
+hils_status check_ws(size_t need, const void* ws, size_t ws_bytes) {
+  if (need == 0) return HILS_OK;
+  if (ws_bytes < need) return HILS_ERR_WORKSPACE;
+  if (!aligned16(ws)) return HILS_ERR_INVALID_ARG;
+  return HILS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hils_status hils_workspace_size(const hils_dims* dims, int op, size_t* bytes) {
+  hils::Dims dm;
+  if (bytes == nullptr) return HILS_ERR_INVALID_ARG;
+  hils_status st = resolve(dims, &dm);
+  if (st != HILS_OK) return st;
+  switch (op) {
+    case HILS_OP_SUMMARIZE: *bytes = 0; return HILS_OK;
+    case HILS_OP_SCORE_TOPK: *bytes = hils::score_topk_ws_bytes(dm); return HILS_OK;
+    case HILS_OP_ATTEND_FUSE: *bytes = hils::attend_ws_bytes(dm); return HILS_OK;
+    case HILS_OP_BACKWARD:
+      st = backward_shape_ok(dm);
+      if (st != HILS_OK) return st;
+      *bytes = hils::backward_ws_bytes(dm);
+      return HILS_OK;
+    default: return HILS_ERR_INVALID_ARG;
+  }
+}
+
+hils_status hils_summarize(const hils_dims* dims, const void* K, const void* Ql, int32_t c_begin,
+                           int32_t c_end, float* ksum, float* ent, float* lse_l, void* ws,
+                           size_t ws_bytes, hils_stream stream) {
+  (void)ws;
+  (void)ws_bytes;
+  hils::Dims dm;
+  hils_status st = resolve(dims, &dm);
+  if (st != HILS_OK) return st;
+  if (c_begin < 0 || c_end < c_begin || c_end > dm.Tkv / dm.S || c_end > dm.NCcap)
+    return HILS_ERR_INVALID_ARG;
+  if (c_end == c_begin) return HILS_OK;
+  if (!aligned16(K) || !aligned16(Ql) || !aligned16(ksum) || !aligned16(ent)) return HILS_ERR_INVALID_ARG;
+  if (lse_l != nullptr && !aligned16(lse_l)) return HILS_ERR_INVALID_ARG;
+  return from_hip(hils::launch_summarize(dm, K, Ql, c_begin, c_end, ksum, ent, lse_l,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+hils_status hils_score_topk(const hils_dims* dims, const void* Q, const float* ksum,
+                            const float* ent, int32_t* idx, float* score, void* ws,
+                            size_t ws_bytes, hils_stream stream) {
+  hils::Dims dm;
+  hils_status st = resolve(dims, &dm);
+  if (st != HILS_OK) return st;
+  if (dm.Tq == 0) return HILS_OK;
+  if (!aligned16(Q) || !aligned16(ksum) || !aligned16(ent) || !aligned16(idx) || !aligned16(score))
+    return HILS_ERR_INVALID_ARG;
+  st = check_ws(hils::score_topk_ws_bytes(dm), ws, ws_bytes);
+  if (st != HILS_OK) return st;
+  return from_hip(hils::launch_score_topk(dm, Q, ksum, ent, idx, score, ws,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K, const void* V,
+                             const int32_t* idx, const float* score, void* O, float* lse_own,
+                             float* lse_tot, void* ws, size_t ws_bytes, hils_stream stream) {
+  hils::Dims dm;
+  hils_status st = resolve(dims, &dm);
+  if (st != HILS_OK) return st;
+  if (dm.Tq == 0) return HILS_OK;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(idx) || !aligned16(score) ||
+      !aligned16(O))
+    return HILS_ERR_INVALID_ARG;
+  if ((lse_own != nullptr && !aligned16(lse_own)) || (lse_tot != nullptr && !aligned16(lse_tot)))
+    return HILS_ERR_INVALID_ARG;
+  st = check_ws(hils::attend_ws_bytes(dm), ws, ws_bytes);
+  if (st != HILS_OK) return st;
+  return from_hip(hils::launch_attend_fuse(dm, Q, K, V, idx, score, O, lse_own, lse_tot, ws,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+hils_status hils_backward(const hils_dims* dims, const void* Q, const void* K, const void* V,
+                          const void* Ql, const float* ksum, const float* ent,
+                          const float* lse_l, const int32_t* idx, const float* score,
+                          const float* lse_tot, const void* dO, void* dQ, void* dK, void* dV,
+                          void* dQl, void* ws, size_t ws_bytes, hils_stream stream) {
+  hils::Dims dm;
+  hils_status st = resolve(dims, &dm);
+  if (st != HILS_OK) return st;
+  st = backward_shape_ok(dm);
+  if (st != HILS_OK) return st;
+  const void* in[] = {Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, dO, dQ, dK, dV, dQl};
+  for (const void* p : in)
+    if (!aligned16(p)) return HILS_ERR_INVALID_ARG;
+  st = check_ws(hils::backward_ws_bytes(dm), ws, ws_bytes);
+  if (st != HILS_OK) return st;
+  return from_hip(hils::launch_backward(dm, Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, dO,
+                                        dQ, dK, dV, dQl, ws,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char* hils_status_string(hils_status status) {
+  switch (status) {
+    case HILS_OK: return "HILS_OK";
+    case HILS_ERR_INVALID_ARG: return "HILS_ERR_INVALID_ARG: null, misaligned or inconsistent argument";
+    case HILS_ERR_UNSUPPORTED: return "HILS_ERR_UNSUPPORTED: shape outside S=64, d in {64,128}, K<=64";
+    case HILS_ERR_WORKSPACE: return "HILS_ERR_WORKSPACE: workspace smaller than hils_workspace_size";
+    case HILS_ERR_HIP: return "HILS_ERR_HIP: kernel launch failed";
+    default: return "unknown hils_status";
+  }
+}
+
+int32_t hils_version(void) { return 100; }
+
+}  // extern "C"

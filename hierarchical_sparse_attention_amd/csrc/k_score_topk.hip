@@ -1,0 +1,244 @@
+// Chunk scoring and top-K selection (note §5.2: s^_{i,c} = q_i.k'_c/sqrt(d) + b'_c,
+// I_i = {c in C_i : rank_desc(s^_{i,c}) < K}).
+//
+// Two kernels share one float32 score function (chunk_score), so every path
+// produces bit-identical scores and therefore identical selections:
+//  * rows path (prefill): one thread per query row; summaries are staged in LDS
+//    in blocks and broadcast to all rows of the workgroup; each thread keeps its
+//    row's running top-K list (score desc, chunk id asc) in LDS.
+//  * split path (decode, few rows, many candidates): candidates of a row are
+//    split over workgroups (one candidate per thread), each workgroup writes its
+//    local top-K to the workspace, and a merge kernel ranks the union. The global
+//    top-K is a subset of the union of local top-Ks, so the merge is exact.
+// The order key is total: (score descending, chunk id ascending).
+#include <cfloat>
+#include <climits>
+
+#include "hils_internal.h"
+
+namespace hils {
+namespace {
+
+constexpr int kBlockChunks = 32;  // summaries staged per LDS block (rows path)
+constexpr int kSplit = 256;       // candidates per workgroup (split path)
+constexpr int kMergeMax = 4096;   // entries the merge kernel ranks in LDS
+
+__host__ __device__ inline int rows_per_wg(int K) { return K <= 16 ? 256 : (K <= 32 ? 128 : 64); }
+
+// key order: a before b
+__device__ __forceinline__ bool before(float sa, int ca, float sb, int cb) {
+  return sa > sb || (sa == sb && ca < cb);
+}
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void k_score_rows(Dims dm, const void* __restrict__ Q,
+                                                    const float* __restrict__ ksum,
+                                                    const float* __restrict__ ent,
+                                                    int32_t* __restrict__ idx,
+                                                    float* __restrict__ score) {
+  __shared__ float kb[kBlockChunks][D];
+  __shared__ float eb[kBlockChunks];
+  __shared__ float ls[4096];
+  __shared__ int li[4096];
+  const int R = blockDim.x, t = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int K = dm.K;
+  const int i = blockIdx.x * R + t;
+  const bool valid = i < dm.Tq;
+  const int last = min(dm.Tq, (int)(blockIdx.x + 1) * R) - 1;
+  const int n = valid ? (int)((dm.q_pos0 + i) / dm.S) : 0;
+  const int nmax = (int)((dm.q_pos0 + last) / dm.S);
+
+  float q[D];
+  if (valid) {
+    load_row<BF16, D>(Q, (((long long)b * dm.Tq + i) * dm.H + h) * D, q);
+  } else {
+#pragma unroll
+    for (int e = 0; e < D; ++e) q[e] = 0.0f;
+  }
+  int cnt = 0;
+  for (int c0 = 0; c0 < nmax; c0 += kBlockChunks) {
+    const int nb = min(kBlockChunks, nmax - c0);
+    for (int x = t; x < nb * D; x += R) {
+      const int cc = x / D, e = x % D;
+      kb[cc][e] = ksum[(((long long)b * dm.NCcap + c0 + cc) * dm.H + h) * D + e];
+    }
+    for (int x = t; x < nb; x += R) eb[x] = ent[((long long)b * dm.NCcap + c0 + x) * dm.H + h];
+    __syncthreads();
+    const int lim = min(nb, n - c0);
+    for (int cc = 0; cc < lim; ++cc) {
+      const float s = chunk_score<D>(q, kb[cc], dm.scale, eb[cc]);
+      const int c = c0 + cc;
+      if (cnt < K || s > ls[(K - 1) * R + t]) {
+        int pos = cnt < K ? cnt : K - 1;
+        while (pos > 0) {
+          const float prev = ls[(pos - 1) * R + t];
+          if (!(prev < s)) break;  // equal scores keep the earlier (lower) chunk first
+          ls[pos * R + t] = prev;
+          li[pos * R + t] = li[(pos - 1) * R + t];
+          --pos;
+        }
+        ls[pos * R + t] = s;
+        li[pos * R + t] = c;
+        if (cnt < K) ++cnt;
+      }
+    }
+    __syncthreads();
+  }
+  if (!valid) return;
+  const long long o = (((long long)b * dm.Tq + i) * dm.H + h) * K;
+  for (int k = 0; k < cnt; ++k) {
+    const int c = li[k * R + t];
+    int rank = 0;
+    for (int k2 = 0; k2 < cnt; ++k2) rank += li[k2 * R + t] < c;
+    idx[o + rank] = c;
+    score[o + rank] = ls[k * R + t];
+  }
+  for (int k = cnt; k < K; ++k) {
+    idx[o + k] = -1;
+    score[o + k] = -INFINITY;
+  }
+}
+
+// Split path, stage 1: grid (splits, rows); thread t scores candidate split*256+t.
+template <bool BF16, int D>
+__global__ __launch_bounds__(kSplit) void k_score_split(Dims dm, const void* __restrict__ Q,
+                                                       const float* __restrict__ ksum,
+                                                       const float* __restrict__ ent,
+                                                       float* __restrict__ ws_s,
+                                                       int* __restrict__ ws_i, int nsplit) {
+  __shared__ float qs[D];
+  __shared__ float ss[kSplit];
+  const int split = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+  const int h = r % dm.H, i = (r / dm.H) % dm.Tq, b = r / (dm.H * dm.Tq);
+  const int n = (int)((dm.q_pos0 + i) / dm.S);
+  const int c = split * kSplit + t;
+  for (int e = t; e < D; e += kSplit) qs[e] = load_elem<BF16>(Q, (long long)r * D + e);
+  __syncthreads();
+  float s = -INFINITY;
+  const bool valid = c < n;
+  if (valid) {
+    float q[D], kr[D];
+#pragma unroll
+    for (int e = 0; e < D; ++e) q[e] = qs[e];
+    const long long sidx = ((long long)b * dm.NCcap + c) * dm.H + h;
+    load_row<false, D>(ksum, sidx * D, kr);
+    s = chunk_score<D>(q, kr, dm.scale, ent[sidx]);
+  }
+  ss[t] = s;
+  __syncthreads();
+  if (!valid) return;
+  const int nvalid = min(kSplit, n - split * kSplit);
+  int rank = 0;
+  for (int t2 = 0; t2 < nvalid; ++t2) rank += before(ss[t2], split * kSplit + t2, s, c);
+  if (rank < dm.K) {
+    const long long o = ((long long)r * nsplit + split) * dm.K + rank;
+    ws_s[o] = s;
+    ws_i[o] = c;
+  }
+}
+
+// Split path, stage 2: one workgroup per row ranks the union of local lists.
+__global__ __launch_bounds__(256) void k_topk_merge(Dims dm, const float* __restrict__ ws_s,
+                                                    const int* __restrict__ ws_i, int nsplit,
+                                                    int32_t* __restrict__ idx,
+                                                    float* __restrict__ score) {
+  __shared__ float es[kMergeMax];
+  __shared__ int ec[kMergeMax];
+  __shared__ float sel_s[64];
+  __shared__ int sel_c[64];
+  const int r = blockIdx.x, t = threadIdx.x;
+  const int i = (r / dm.H) % dm.Tq;
+  const int n = (int)((dm.q_pos0 + i) / dm.S);
+  const int K = dm.K;
+  // gather the valid entries of each split's list
+  int E = 0;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const int nv = min(K, max(0, min(kSplit, n - sp * kSplit)));
+    for (int k = t; k < nv; k += blockDim.x) {
+      const long long o = ((long long)r * nsplit + sp) * K + k;
+      es[E + k] = ws_s[o];
+      ec[E + k] = ws_i[o];
+    }
+    E += nv;
+  }
+  __syncthreads();
+  const int cnt = min(K, n);
+  for (int x = t; x < E; x += blockDim.x) {
+    const float s = es[x];
+    const int c = ec[x];
+    int rank = 0;
+    for (int y = 0; y < E; ++y) rank += before(es[y], ec[y], s, c);
+    if (rank < cnt) {
+      sel_s[rank] = s;
+      sel_c[rank] = c;
+    }
+  }
+  __syncthreads();
+  const long long o = (long long)r * K;
+  if (t < cnt) {
+    const int c = sel_c[t];
+    int pos = 0;
+    for (int k = 0; k < cnt; ++k) pos += sel_c[k] < c;
+    idx[o + pos] = c;
+    score[o + pos] = sel_s[t];
+  } else if (t < K) {
+    idx[o + t] = -1;
+    score[o + t] = -INFINITY;
+  }
+}
+
+int max_candidates(const Dims& dm) {
+  if (dm.Tq <= 0) return 0;
+  return (int)((dm.q_pos0 + dm.Tq - 1) / dm.S);
+}
+
+int split_count(const Dims& dm) { return (max_candidates(dm) + kSplit - 1) / kSplit; }
+
+bool use_split(const Dims& dm) {
+  const long long rows = (long long)dm.B * dm.Tq * dm.H;
+  const int ns = split_count(dm);
+  return rows <= 4096 && ns >= 1 && (long long)ns * dm.K <= kMergeMax;
+}
+
+template <bool BF16, int D>
+hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const float* ent,
+                    int32_t* idx, float* score, void* ws, hipStream_t st) {
+  if (use_split(dm)) {
+    const int ns = split_count(dm);
+    const long long rows = (long long)dm.B * dm.Tq * dm.H;
+    float* ws_s = reinterpret_cast<float*>(ws);
+    int* ws_i = reinterpret_cast<int*>(ws_s + rows * ns * dm.K);
+    hipLaunchKernelGGL((k_score_split<BF16, D>), dim3(ns, rows), dim3(kSplit), 0, st, dm, Q, ksum,
+                       ent, ws_s, ws_i, ns);
+    hipLaunchKernelGGL(k_topk_merge, dim3(rows), dim3(256), 0, st, dm, ws_s, ws_i, ns, idx,
+                       score);
+  } else {
+    const int R = rows_per_wg(dm.K);
+    dim3 grid((dm.Tq + R - 1) / R, dm.H, dm.B);
+    hipLaunchKernelGGL((k_score_rows<BF16, D>), grid, dim3(R), 0, st, dm, Q, ksum, ent, idx,
+                       score);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t score_topk_ws_bytes(const Dims& dm) {
+  if (!use_split(dm)) return 0;
+  const long long rows = (long long)dm.B * dm.Tq * dm.H;
+  return (size_t)rows * split_count(dm) * dm.K * (sizeof(float) + sizeof(int));
+}
+
+hipError_t launch_score_topk(const Dims& dm, const void* Q, const float* ksum, const float* ent,
+                             int32_t* idx, float* score, void* ws, hipStream_t st) {
+  if ((long long)dm.B * dm.Tq * dm.H == 0) return hipSuccess;
+  if (dm.bf16) {
+    return dm.d == 64 ? launch_t<true, 64>(dm, Q, ksum, ent, idx, score, ws, st)
+                      : launch_t<true, 128>(dm, Q, ksum, ent, idx, score, ws, st);
+  }
+  return dm.d == 64 ? launch_t<false, 64>(dm, Q, ksum, ent, idx, score, ws, st)
+                    : launch_t<false, 128>(dm, Q, ksum, ent, idx, score, ws, st);
+}
+
+}  // namespace hils

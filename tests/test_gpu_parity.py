@@ -1,0 +1,313 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Oracle inputs never come from the GPU: stage tests feed oracle outputs (e.g.
+the oracle's selection) into the GPU kernels, never the reverse. Selection is
+compared bit-exactly on rows whose oracle K-th/(K+1)-th score gap is at least
+1e-4; excluded rows are counted. Outputs use |x-y| <= tol|y| + tol*rms(y).
+"""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_amd as hsa
+import oracle
+import synth
+from hils_testutil import (NEAR_TIE, TOL_BF16, TOL_F32, TOL_GRAD_BF16, assert_close,
+                           compare_selection, say)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(device=DEV, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+def host(t):
+    return t.detach().float().cpu().numpy() if t.dtype != torch.int32 else t.cpu().numpy()
+
+
+def out_tol(w):
+    return TOL_BF16 if w.dtype == "bf16" else TOL_F32
+
+
+SMALL = {
+    "f32_d64_B2": synth.small("f32_d64_B2", B=2, T=640, H=2, Hkv=1, d=64, K=4, dtype="f32"),
+    "bf16_gqa_ragged": synth.small("bf16_gqa_ragged", B=1, T=704, H=4, Hkv=2, d=64, K=5,
+                                   dtype="bf16", n_planted=2),
+    "bf16_d128_gqa4": synth.small("bf16_d128_gqa4", B=1, T=1024, H=8, Hkv=2, d=128, K=6,
+                                  dtype="bf16", n_planted=1, n_uniform=2),
+    "f32_d128": synth.small("f32_d128", B=1, T=512, H=2, Hkv=2, d=128, K=3, dtype="f32"),
+    "f32_kmax": synth.small("f32_kmax", B=1, T=4224, H=1, Hkv=1, d=64, K=64, dtype="f32"),
+    "single_chunk": synth.small("single_chunk", B=1, T=64, H=2, Hkv=1, d=64, K=2, dtype="bf16"),
+}
+_cache = {}
+
+
+def case(name):
+    if name not in _cache:
+        w = SMALL[name] if name in SMALL else synth.workloads()[name]
+        x = synth.make_inputs(w)
+        _cache[name] = (w, x)
+    return _cache[name]
+
+
+def gpu_forward(w, x):
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
+    f = hsa.forward(t["Q"], t["K"], t["V"], t["Ql"], w.K, w.S)
+    torch.cuda.synchronize()
+    return t, f
+
+
+@pytest.mark.parametrize("name", list(SMALL) + ["tiny_f32"])
+def test_summarize(name):
+    w, x = case(name)
+    say(f"[summarize] {name}")
+    t = {k: dev(x[k], w.dtype) for k in ("K", "Ql")}
+    ksum, ent, lse = hsa.summarize(t["K"], t["Ql"], w.S)
+    torch.cuda.synchronize()
+    oks, oent, olse = oracle.summarize(x["K"], x["Ql"], w.S)
+    assert_close(host(ksum), oks, TOL_F32, "ksum")
+    assert_close(host(ent), oent, TOL_F32, "ent")
+    assert_close(host(lse), olse, TOL_F32, "lse_l")
+
+
+@pytest.mark.parametrize("name", list(SMALL) + ["tiny_f32"])
+def test_forward_end_to_end(name):
+    w, x = case(name)
+    say(f"[forward] {name}")
+    t, f = gpu_forward(w, x)
+    o = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K)
+    excl, eq = compare_selection(host(f["idx"]), o["idx"], o["gap"], w.K)
+    say(f"  near-tie rows excluded: {int(excl.sum())}/{excl.size}; differing among them: "
+        f"{int((~eq).sum())}")
+    sel = eq[..., None].repeat(w.K, -1) & (o["idx"] >= 0)
+    assert_close(host(f["score"])[sel], o["score"][sel], TOL_F32, "score")
+    assert np.all(host(f["score"])[eq[..., None].repeat(w.K, -1) & (o["idx"] < 0)] == -np.inf)
+    assert_close(host(f["O"])[eq], o["O"][eq], out_tol(w), "O")
+    assert_close(host(f["lse_own"])[eq], o["lse_own"][eq], TOL_F32, "lse_own")
+    assert_close(host(f["lse_tot"])[eq], o["lse_tot"][eq], TOL_F32, "lse_tot")
+
+
+@pytest.mark.parametrize("name", ["f32_d64_B2", "bf16_d128_gqa4", "tiny_f32"])
+def test_attend_stage_with_oracle_selection(name):
+    """attend_fuse fed the oracle's selection and scores covers every row, near-ties included."""
+    w, x = case(name)
+    say(f"[attend stage] {name}")
+    o = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K)
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V")}
+    idx = torch.from_numpy(o["idx"]).to(DEV)
+    score = torch.from_numpy(o["score"].astype(np.float32)).to(DEV)
+    O, lo, lt = hsa.attend_fuse(t["Q"], t["K"], t["V"], idx, score, w.S)
+    torch.cuda.synchronize()
+    assert_close(host(O), o["O"], out_tol(w), "O")
+    assert_close(host(lo), o["lse_own"], TOL_F32, "lse_own")
+    assert_close(host(lt), o["lse_tot"], TOL_F32, "lse_tot")
+
+
+@pytest.mark.parametrize("name", ["bf16_gqa_ragged", "f32_kmax"])
+def test_decode_rows_equal_prefill_rows(name):
+    """A query scored alone (split path) selects what the prefill pass selected, bit for bit,
+    and attends to the same output (decode = prefill row)."""
+    w, x = case(name)
+    say(f"[decode=prefill] {name}")
+    t, f = gpu_forward(w, x)
+    idx_p, sc_p, O_p = host(f["idx"]), host(f["score"]), host(f["O"])
+    for p in (63, 64, 300, w.T - 65, w.T - 1):
+        q = t["Q"][:, p:p + 1].contiguous()
+        idx, sc = hsa.score_topk(q, f["ksum"], f["ent"], w.K, w.S, q_pos0=p, Tkv=p + 1,
+                                 Hkv=w.Hkv)
+        O, lo, lt = hsa.attend_fuse(q, t["K"], t["V"], idx, sc, w.S, q_pos0=p, Tkv=p + 1)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(idx)[:, 0], idx_p[:, p])
+        np.testing.assert_array_equal(host(sc)[:, 0], sc_p[:, p])
+        np.testing.assert_array_equal(host(O)[:, 0], O_p[:, p])
+
+
+def test_empty_query_range_is_noop():
+    w, x = case("bf16_gqa_ragged")
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
+    ksum, ent, _ = hsa.summarize(t["K"], t["Ql"], w.S)
+    q = t["Q"][:, :0].contiguous()
+    idx, sc = hsa.score_topk(q, ksum, ent, w.K, w.S, Tkv=w.T, Hkv=w.Hkv)
+    O, lo, lt = hsa.attend_fuse(q, t["K"], t["V"], idx, sc, w.S)
+    torch.cuda.synchronize()
+    assert O.numel() == 0
+
+
+def test_incremental_summaries_match_full():
+    """Summarising chunk ranges one at a time (decode) equals one pass over all chunks."""
+    w, x = case("bf16_d128_gqa4")
+    say("[summarize incremental]")
+    t = {k: dev(x[k], w.dtype) for k in ("K", "Ql")}
+    full = hsa.summarize(t["K"], t["Ql"], w.S)
+    parts = [torch.full_like(a, float("nan")) for a in full]
+    for c in range(w.NC):
+        hsa.summarize(t["K"], t["Ql"], w.S, c, c + 1, ksum=parts[0], ent=parts[1],
+                      lse_l=parts[2])
+    torch.cuda.synchronize()
+    for a, b in zip(full, parts):
+        assert torch.equal(a, b)
+
+
+def test_forward_deterministic():
+    w, x = case("bf16_d128_gqa4")
+    _, f1 = gpu_forward(w, x)
+    _, f2 = gpu_forward(w, x)
+    for k in f1:
+        assert torch.equal(f1[k], f2[k]), k
+
+
+# ------------------------------------------------------------------ full-size workloads
+def sampled_rows(w, n, seed):
+    rng = np.random.default_rng(seed)
+    B, Tq, H = w.B, w.rows_q, w.H
+    rows = rng.choice(B * Tq * H, size=n, replace=False)
+    # always include the last row of each batch element and a chunk-0 row
+    extra = [((b * Tq + Tq - 1) * H + H - 1) for b in range(B)] + [3 * H]
+    return np.unique(np.concatenate([rows, extra]))
+
+
+@pytest.mark.parametrize("name", ["prefill_345m", "prefill_7b_gqa"])
+def test_full_size_prefill_sampled(name):
+    w, x = case(name)
+    say(f"[full prefill] {name}: B{w.B} T{w.T} H{w.H}/{w.Hkv} d{w.d} K{w.K}")
+    t, f = gpu_forward(w, x)
+    ksum, ent, lse = oracle.summarize(x["K"], x["Ql"], w.S)
+    assert_close(host(f["ksum"]), ksum, TOL_F32, "ksum")
+    assert_close(host(f["ent"]), ent, TOL_F32, "ent")
+    rows = sampled_rows(w, 384, 7)
+    idx, score, gap = oracle.score_topk(x["Q"], ksum, ent, w.S, w.K, rows=rows)
+    O, lo, lt = oracle.attend_fuse(x["Q"], x["K"], x["V"], idx, score, w.S, rows=rows)
+    flat = lambda a: a.reshape(-1, *a.shape[3:])  # noqa: E731
+    gi, gs = flat(host(f["idx"]))[rows], flat(host(f["score"]))[rows]
+    excl, eq = compare_selection(gi, flat(idx)[rows], flat(gap)[rows], w.K)
+    say(f"  sampled rows {len(rows)}, near-tie excluded {int(excl.sum())}")
+    m = eq[:, None].repeat(w.K, 1) & (flat(idx)[rows] >= 0)
+    assert_close(gs[m], flat(score)[rows][m], TOL_F32, "score")
+    assert_close(flat(host(f["O"]))[rows][eq], flat(O)[rows][eq], out_tol(w), "O")
+    assert_close(flat(host(f["lse_tot"]))[rows][eq], flat(lt)[rows][eq], TOL_F32, "lse_tot")
+    # every row: selection is valid (ascending, distinct, causal, padded only when n < K)
+    gi_all = host(f["idx"])
+    n = (np.arange(w.T) // w.S)[None, :, None]
+    cnt = (gi_all >= 0).sum(-1)
+    assert np.all(cnt == np.minimum(n, w.K))
+    srt = np.where(gi_all >= 0, gi_all, np.iinfo(np.int32).max)
+    assert np.all(np.diff(srt, axis=-1) > 0)
+    assert np.all(gi_all < n[..., None])
+
+
+def test_full_size_decode_sampled_steps():
+    w, x = case("decode_128k")
+    say(f"[full decode] cache {w.T} H{w.H} d{w.d} K{w.K}")
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
+    ksum, ent, lse = hsa.summarize(t["K"], t["Ql"], w.S)
+    oks, oent, _ = oracle.summarize(x["K"], x["Ql"], w.S)
+    assert_close(host(ksum), oks, TOL_F32, "ksum")
+    for step in (0, 63, 64, 200, 255):
+        p = w.q_pos0 + step
+        q = t["Q"][:, step:step + 1].contiguous()
+        idx, sc = hsa.score_topk(q, ksum, ent, w.K, w.S, q_pos0=p, Tkv=p + 1, Hkv=w.Hkv)
+        O, lo, lt = hsa.attend_fuse(q, t["K"], t["V"], idx, sc, w.S, q_pos0=p, Tkv=p + 1)
+        torch.cuda.synchronize()
+        qn = x["Q"][:, step:step + 1]
+        oidx, osc, ogap = oracle.score_topk(qn, oks, oent, w.S, w.K, q_pos0=p)
+        oO, olo, olt = oracle.attend_fuse(qn, x["K"][:, :p + 1], x["V"][:, :p + 1], oidx, osc,
+                                          w.S, q_pos0=p)
+        excl, eq = compare_selection(host(idx), oidx, ogap, w.K)
+        assert_close(host(O)[eq], oO[eq], TOL_BF16, f"O step {step}")
+        assert_close(host(lt)[eq], olt[eq], TOL_F32, f"lse_tot step {step}")
+
+
+# ------------------------------------------------------------------ backward
+BWD = {
+    "bwd_bf16_gqa": synth.small("bwd_bf16_gqa", B=2, T=512, H=4, Hkv=2, d=64, K=3, dtype="bf16",
+                                need_dO=True),
+    "bwd_f32": synth.small("bwd_f32", B=1, T=640, H=2, Hkv=1, d=64, K=4, dtype="f32",
+                           need_dO=True),
+    "bwd_f32_d128": synth.small("bwd_f32_d128", B=1, T=256, H=2, Hkv=1, d=128, K=2,
+                                dtype="f32", need_dO=True),
+}
+
+
+def gpu_train(w, x):
+    t, f = gpu_forward(w, x)
+    dO = dev(x["dO"], w.dtype)
+    g = hsa.backward(t["Q"], t["K"], t["V"], t["Ql"], f["ksum"], f["ent"], f["lse_l"], f["idx"],
+                     f["score"], f["lse_tot"], dO, w.S)
+    torch.cuda.synchronize()
+    return f, g
+
+
+@pytest.mark.parametrize("name", list(BWD))
+def test_backward_small(name):
+    w = BWD[name]
+    x = synth.make_inputs(w)
+    say(f"[backward] {name}")
+    f, g = gpu_train(w, x)
+    o = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K)
+    excl, eq = compare_selection(host(f["idx"]), o["idx"], o["gap"], w.K)
+    assert eq.all(), "small backward cases need identical selections"
+    og = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], o["idx"], x["dO"], w.S)
+    tol = TOL_GRAD_BF16 if w.dtype == "bf16" else TOL_F32
+    for nm, a, b in zip(("dQ", "dK", "dV", "dQl"), g, og):
+        assert_close(host(a), b, tol, nm)
+
+
+def test_backward_deterministic():
+    w = BWD["bwd_bf16_gqa"]
+    x = synth.make_inputs(w)
+    _, g1 = gpu_train(w, x)
+    _, g2 = gpu_train(w, x)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_full_size_training_backward_sampled():
+    w, x = case("train_345m")
+    say(f"[full backward] B{w.B} T{w.T} H{w.H} d{w.d} K{w.K}")
+    f, g = gpu_train(w, x)
+    ksum, ent, _ = oracle.summarize(x["K"], x["Ql"], w.S)
+    c_min = w.NC - 5
+    # rows that can select chunks >= c_min, plus sampled rows for dQ
+    late = np.array([(b * w.T + i) * w.H + h for b in range(w.B)
+                     for i in range(c_min * w.S, w.T) for h in range(w.H)])
+    dq_rows = sampled_rows(w, 96, 11)
+    rows = np.unique(np.concatenate([late, dq_rows]))
+    idx, score, gap = oracle.score_topk(x["Q"], ksum, ent, w.S, w.K, rows=rows)
+    gi = host(f["idx"]).reshape(-1, w.K)
+    oi = idx.reshape(-1, w.K)
+    differ = rows[np.any(gi[rows] != oi[rows], axis=1)]
+    assert np.all(gap.reshape(-1)[differ] < NEAR_TIE)
+    row_mask = np.zeros(w.B * w.T * w.H, np.uint8)
+    row_mask[np.setdiff1d(dq_rows, differ)] = 1
+    kv_mask = np.zeros((w.B, w.NC, w.Hkv), np.uint8)
+    chosen = [(0, w.NC - 1, 0), (0, w.NC - 3, 5), (1, w.NC - 2, 15), (1, c_min, 7)]
+    # drop a chunk if a row whose selection differs touches it
+    keep = []
+    for b, c, gh in chosen:
+        touched = False
+        for r in differ:
+            h = r % w.H
+            if r // (w.T * w.H) == b and h // (w.H // w.Hkv) == gh and (
+                    c in gi[r] or c in oi[r]):
+                touched = True
+        if not touched:
+            keep.append((b, c, gh))
+            kv_mask[b, c, gh] = 1
+    say(f"  rows with differing near-tie selections: {len(differ)}; chunks checked {keep}")
+    oidx_full = np.full((w.B, w.T, w.H, w.K), -1, np.int32)
+    oidx_full.reshape(-1, w.K)[rows] = oi[rows]
+    og = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], oidx_full, x["dO"], w.S,
+                         row_mask=row_mask.reshape(w.B, w.T, w.H), kv_mask=kv_mask)
+    dQ, dK, dV, dQl = (host(a) for a in g)
+    rm = row_mask.astype(bool)
+    assert_close(dQ.reshape(-1, w.d)[rm], og[0].reshape(-1, w.d)[rm], TOL_GRAD_BF16, "dQ")
+    for b, c, gh in keep:
+        sl = slice(c * w.S, (c + 1) * w.S)
+        assert_close(dK[b, sl, gh], og[1][b, sl, gh], TOL_GRAD_BF16, f"dK {b,c,gh}")
+        assert_close(dV[b, sl, gh], og[2][b, sl, gh], TOL_GRAD_BF16, f"dV {b,c,gh}")
+        G = w.H // w.Hkv
+        assert_close(dQl[b, c, gh * G:(gh + 1) * G], og[3][b, c, gh * G:(gh + 1) * G],
+                     TOL_GRAD_BF16, f"dQl {b,c,gh}")
