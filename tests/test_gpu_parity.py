@@ -122,7 +122,8 @@ def test_decode_rows_equal_prefill_rows(name):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(host(idx)[:, 0], idx_p[:, p])
         np.testing.assert_array_equal(host(sc)[:, 0], sc_p[:, p])
-        np.testing.assert_array_equal(host(O)[:, 0], O_p[:, p])
+        # single rows and prefill tiles may run different attention kernels
+        assert_close(host(O)[:, 0], O_p[:, p], out_tol(w), f"O row {p}")
 
 
 def test_empty_query_range_is_noop():
