@@ -108,9 +108,10 @@ hipError_t launch_score_topk(const Dims& dm, const void* Q, const float* ksum, c
                              int32_t* idx, float* score, void* ws, hipStream_t st);
 
 size_t attend_ws_bytes(const Dims& dm);
+size_t attend_mfma_ws_bytes(const Dims& dm);
 bool attend_mfma_try(const Dims& dm, const void* Q, const void* K, const void* V,
                      const int32_t* idx, const float* score, void* O, float* lse_own,
-                     float* lse_tot, hipStream_t st, hipError_t* err);
+                     float* lse_tot, void* ws, hipStream_t st, hipError_t* err);
 hipError_t launch_attend_fuse(const Dims& dm, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* score, void* O, float* lse_own,
                               float* lse_tot, void* ws, hipStream_t st);

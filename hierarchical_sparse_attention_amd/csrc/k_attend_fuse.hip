@@ -122,18 +122,16 @@ hipError_t launch_t(const Dims& dm, const void* Q, const void* K, const void* V,
 
 }  // namespace
 
-size_t attend_ws_bytes(const Dims&) { return 0; }
+size_t attend_ws_bytes(const Dims& dm) { return attend_mfma_ws_bytes(dm); }
 
 hipError_t launch_attend_fuse(const Dims& dm, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* score, void* O, float* lse_own,
                               float* lse_tot, void* ws, hipStream_t st) {
-  (void)ws;
   if ((long long)dm.B * dm.Tq * dm.H == 0) return hipSuccess;
-  // prefill-sized problems run on matrix cores; single rows (decode) use the rows kernel
-  if (dm.Tq >= 64) {
-    hipError_t err = hipSuccess;
-    if (attend_mfma_try(dm, Q, K, V, idx, score, O, lse_own, lse_tot, st, &err)) return err;
-  }
+  // prefill-sized bf16 problems run on matrix cores; single rows (decode) and
+  // float32 inputs use the rows kernel
+  hipError_t err = hipSuccess;
+  if (attend_mfma_try(dm, Q, K, V, idx, score, O, lse_own, lse_tot, ws, st, &err)) return err;
   if (dm.bf16) {
     return dm.d == 64 ? launch_t<true, 64>(dm, Q, K, V, idx, score, O, lse_own, lse_tot, st)
                       : launch_t<true, 128>(dm, Q, K, V, idx, score, O, lse_own, lse_tot, st);
