@@ -19,7 +19,7 @@ OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhils.so")
 ARCH = "gfx950"
 
-SOURCES = ["hils_api.cpp", "k_summarize.hip", "k_score_topk.hip", "k_attend_fuse.hip",
+SOURCES = ["hils_api.cpp", "k_summarize.hip", "k_score_topk.hip", "k_score_mfma.hip", "k_attend_fuse.hip",
            "k_attend_mfma.hip", "k_backward.hip"]
 
 FLAGS = [

@@ -104,6 +104,13 @@ hipError_t launch_summarize(const Dims& dm, const void* K, const void* Ql, int c
                             float* ksum, float* ent, float* lse_l, hipStream_t st);
 
 size_t score_topk_ws_bytes(const Dims& dm);
+size_t score_mfma_prefill_ws_bytes(const Dims& dm);
+hipError_t launch_score_mfma_prefill(const Dims& dm, const void* Q, const float* ksum,
+                                     const float* ent, int32_t* idx, float* score, void* ws,
+                                     hipStream_t st);
+hipError_t launch_score_mfma_split(const Dims& dm, const void* Q, const float* ksum,
+                                   const float* ent, float* ws_s, int* ws_i, int nsplit,
+                                   hipStream_t st);
 hipError_t launch_score_topk(const Dims& dm, const void* Q, const float* ksum, const float* ent,
                              int32_t* idx, float* score, void* ws, hipStream_t st);
 

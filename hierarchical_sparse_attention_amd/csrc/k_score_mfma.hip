@@ -1,0 +1,315 @@
+// Chunk scoring and top-K selection on bf16 MFMA (note §5.2: s^_{i,c} =
+// q_i.k'_c/sqrt(d) + b'_c, I_i = {c in C_i : rank_desc(s^_{i,c}) < K}).
+//
+// The summary key k'_c is float32. With q exactly bf16, the dot product is
+// computed on matrix cores from a two-term split k' = hi + lo (hi = bf16(k'),
+// lo = bf16(k' - hi)): every product q_e * hi_e and q_e * lo_e is exact in
+// float32, the MFMA accumulates in float32, and the dropped remainder is below
+// 2^-17 |k'_e|, so the score matches a float32 dot product to rounding level.
+//
+// All bf16 paths (prefill tiles and decode splits) run the same MFMA sequence per
+// (row, chunk) element: acc = sum over 32-wide feature steps of q.hi then q.lo,
+// then s = acc * scale + ent. An element of an MFMA result depends only on its
+// own row of A and column of B, so every path yields bit-identical scores and
+// therefore identical selections.
+//
+// Prefill: one wavefront owns 64 query rows of one head. Candidates are scored
+// 64 at a time into LDS (16 x 16 MFMA blocks, rows on M, chunks on N); then each
+// lane takes one row and keeps its running top list in registers: in groups of
+// 16 candidates, a compare against the list's last score marks the few that can
+// enter, and those are inserted with a compare-exchange pass.
+// Decode: candidates of a row are split over workgroups; each writes its local
+// top-K (rank counting) and the merge kernel of the float32 path ranks the union.
+#include "hils_internal.h"
+
+namespace hils {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSplitM = 256;  // candidates per decode workgroup
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &u, 16);
+  return r;
+}
+
+// hi/lo split of 8 float32 values into two bf16x8 fragments (round to nearest even).
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = (__bf16)x[j];
+    hi[j] = h;
+    lo[j] = (__bf16)(x[j] - (float)h);
+  }
+}
+
+// Score accumulation for one 16x16 block: sum_ds q.hi + q.lo, fixed order.
+template <int D>
+__device__ __forceinline__ floatx4 score_block(const uint4* qa, const bf16x8* hi, const bf16x8* lo) {
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ds]), hi[ds], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ds]), lo[ds], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Split copy of the summary keys: ks[b][c][h][0:D] = hi, [D:2D] = lo.
+template <int D>
+__global__ __launch_bounds__(256) void k_ksplit(Dims dm, int nc, const float* __restrict__ ksum,
+                                                uint16_t* __restrict__ ks) {
+  const long long n8 = (long long)dm.B * nc * dm.H * (D / 8);
+  for (long long x = blockIdx.x * 256LL + threadIdx.x; x < n8; x += (long long)gridDim.x * 256) {
+    const long long rowi = x / (D / 8);
+    const int c8 = (int)(x % (D / 8));
+    const int h = (int)(rowi % dm.H);
+    const long long bc = rowi / dm.H;
+    const int c = (int)(bc % nc), b = (int)(bc / nc);
+    const float* src = ksum + (((long long)b * dm.NCcap + c) * dm.H + h) * D + c8 * 8;
+    float v[8];
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float4 bb = *reinterpret_cast<const float4*>(src + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = bb.x; v[5] = bb.y; v[6] = bb.z; v[7] = bb.w;
+    bf16x8 hi, lo;
+    split8(v, hi, lo);
+    uint16_t* dst = ks + rowi * 2 * D + c8 * 8;
+    __builtin_memcpy(dst, &hi, 16);
+    __builtin_memcpy(dst + D, &lo, 16);
+  }
+}
+
+// Running top-KM list of one row in registers, sorted by (score desc, chunk asc).
+// Inserting is a fixed compare-exchange pass (no dynamic indexing); a candidate
+// that loses every comparison falls off the end. Candidates arrive in ascending
+// chunk order and compare strictly, so equal scores keep the lower chunk first.
+template <int KM>
+struct TopList {
+  float s[KM];
+  int c[KM];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int k = 0; k < KM; ++k) { s[k] = -INFINITY; c[k] = 0x7fffffff; }
+  }
+  __device__ __forceinline__ void insert(float x, int xc) {
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      const bool take = x > s[k];
+      const float ts = s[k];
+      const int tc = c[k];
+      s[k] = take ? x : ts;
+      c[k] = take ? xc : tc;
+      x = take ? ts : x;
+      xc = take ? tc : xc;
+    }
+  }
+};
+
+template <int D, int KM>
+__global__ __launch_bounds__(64) void k_score_mfma(Dims dm, int nc, const uint16_t* __restrict__ Q,
+                                                   const uint16_t* __restrict__ ks,
+                                                   const float* __restrict__ ent,
+                                                   int32_t* __restrict__ idx,
+                                                   float* __restrict__ score) {
+  __shared__ float sS[64][65];
+  const int lane = threadIdx.x, c = lane & 15, g = lane >> 4;
+  const int h = blockIdx.y, b = blockIdx.z, K = dm.K;
+  const int i0 = blockIdx.x * 64;
+  const int nrows = min(64, dm.Tq - i0);
+  const int my_n = lane < nrows ? (int)((dm.q_pos0 + i0 + lane) / dm.S) : 0;
+  const int nmax = (int)((dm.q_pos0 + i0 + nrows - 1) / dm.S);
+
+  // A fragments: rows 16mb + c, features 32ds + 8g .. +8
+  uint4 qa[4][D / 32];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = 16 * mb + c;
+    const bool v = m < nrows;
+    const long long off = (((long long)b * dm.Tq + i0 + m) * dm.H + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+      qa[mb][ds] = v ? *reinterpret_cast<const uint4*>(Q + off + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
+  }
+  TopList<KM> top;
+  top.init();
+  for (int c0 = 0; c0 < nmax; c0 += 64) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int chunk = c0 + 16 * nb + c;
+      const bool cv = chunk < nmax;
+      bf16x8 hi[D / 32], lo[D / 32];
+      const uint16_t* src = ks + (((long long)b * nc + (cv ? chunk : 0)) * dm.H + h) * 2 * D;
+#pragma unroll
+      for (int ds = 0; ds < D / 32; ++ds) {
+        const uint4 uh = cv ? *reinterpret_cast<const uint4*>(src + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
+        const uint4 ul = cv ? *reinterpret_cast<const uint4*>(src + D + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
+        hi[ds] = as_bf16x8(uh);
+        lo[ds] = as_bf16x8(ul);
+      }
+      const float e = cv ? ent[((long long)b * dm.NCcap + chunk) * dm.H + h] : 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const floatx4 acc = score_block<D>(qa[mb], hi, lo);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sS[16 * mb + 4 * g + r][16 * nb + c] = fmaf(acc[r], dm.scale, e);
+      }
+    }
+    __syncthreads();
+    // lane = row. In sub-blocks of 16 candidates: mark the ones that beat the
+    // row's current KM-th score, then insert them (all lanes step together).
+    const int lim = min(64, my_n - c0);
+#pragma unroll 1
+    for (int sb = 0; sb < 4; ++sb) {
+      const float theta = top.s[KM - 1];
+      uint32_t mask = 0;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int j = 16 * sb + jj;
+        mask |= (j < lim && sS[lane][j] > theta) ? (1u << jj) : 0u;
+      }
+      int todo = __popc(mask);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) todo = max(todo, __shfl_xor(todo, o, 64));
+      for (int p = 0; p < todo; ++p) {
+        const int jj = mask ? __ffs(mask) - 1 : 0;
+        const float x = mask ? sS[lane][16 * sb + jj] : -INFINITY;
+        mask &= mask - 1;
+        top.insert(x, c0 + 16 * sb + jj);
+      }
+    }
+    __syncthreads();
+  }
+  if (lane >= nrows) return;
+  const int cnt = min(K, my_n);
+  const long long o = (((long long)b * dm.Tq + i0 + lane) * dm.H + h) * K;
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    int rank = 0;
+#pragma unroll
+    for (int k2 = 0; k2 < KM; ++k2) rank += (k2 < cnt && top.c[k2] < top.c[k]) ? 1 : 0;
+    if (k < cnt) {
+      idx[o + rank] = top.c[k];
+      score[o + rank] = top.s[k];
+    }
+  }
+  for (int k = cnt; k < K; ++k) {
+    idx[o + k] = -1;
+    score[o + k] = -INFINITY;
+  }
+}
+
+// key order: a before b
+__device__ __forceinline__ bool before(float sa, int ca, float sb, int cb) {
+  return sa > sb || (sa == sb && ca < cb);
+}
+
+// Decode split: grid (splits, rows); one wavefront scores 256 candidates of one row
+// (the row sits in M position 0 of each block; other positions are zero) and
+// writes the split's local top-K.
+template <int D>
+__global__ __launch_bounds__(64) void k_score_split_mfma(Dims dm, const uint16_t* __restrict__ Q,
+                                                         const float* __restrict__ ksum,
+                                                         const float* __restrict__ ent,
+                                                         float* __restrict__ ws_s,
+                                                         int* __restrict__ ws_i, int nsplit) {
+  __shared__ float ss[kSplitM];
+  const int split = blockIdx.x, r = blockIdx.y, lane = threadIdx.x, c = lane & 15, g = lane >> 4;
+  const int h = r % dm.H, i = (r / dm.H) % dm.Tq, b = r / (dm.H * dm.Tq);
+  const int n = (int)((dm.q_pos0 + i) / dm.S);
+  const int cbase = split * kSplitM;
+  uint4 qa[D / 32];
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds)
+    qa[ds] = c == 0 ? *reinterpret_cast<const uint4*>(Q + (long long)r * D + 32 * ds + 8 * g)
+                    : make_uint4(0, 0, 0, 0);
+  for (int nb = 0; nb < kSplitM / 16; ++nb) {
+    const int chunk = cbase + 16 * nb + c;
+    const bool cv = chunk < n;
+    bf16x8 hi[D / 32], lo[D / 32];
+    const float* src = ksum + (((long long)b * dm.NCcap + (cv ? chunk : 0)) * dm.H + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      float v[8];
+      if (cv) {
+        const float4 a = *reinterpret_cast<const float4*>(src + 32 * ds + 8 * g);
+        const float4 bb = *reinterpret_cast<const float4*>(src + 32 * ds + 8 * g + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = bb.x; v[5] = bb.y; v[6] = bb.z; v[7] = bb.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 0.f;
+      }
+      split8(v, hi[ds], lo[ds]);
+    }
+    const float e = cv ? ent[((long long)b * dm.NCcap + chunk) * dm.H + h] : 0.f;
+    const floatx4 acc = score_block<D>(qa, hi, lo);
+    if (g == 0) ss[16 * nb + c] = cv ? fmaf(acc[0], dm.scale, e) : -INFINITY;
+  }
+  __syncthreads();
+  const int nvalid = max(0, min(kSplitM, n - cbase));
+  for (int x = lane; x < nvalid; x += 64) {
+    const float s = ss[x];
+    const int cx = cbase + x;
+    int rank = 0;
+    for (int y = 0; y < nvalid; ++y) rank += before(ss[y], cbase + y, s, cx);
+    if (rank < dm.K) {
+      const long long o = ((long long)r * nsplit + split) * dm.K + rank;
+      ws_s[o] = s;
+      ws_i[o] = cx;
+    }
+  }
+}
+
+}  // namespace
+
+int score_mfma_split_size() { return kSplitM; }
+
+size_t score_mfma_prefill_ws_bytes(const Dims& dm) {
+  const int nc = (int)((dm.q_pos0 + dm.Tq - 1) / dm.S);
+  return (size_t)dm.B * (size_t)(nc > 0 ? nc : 1) * dm.H * 2 * dm.d * sizeof(uint16_t);
+}
+
+hipError_t launch_score_mfma_prefill(const Dims& dm, const void* Q, const float* ksum,
+                                     const float* ent, int32_t* idx, float* score, void* ws,
+                                     hipStream_t st) {
+  const int nc = max(1, (int)((dm.q_pos0 + dm.Tq - 1) / dm.S));
+  uint16_t* ks = reinterpret_cast<uint16_t*>(ws);
+  const long long n8 = (long long)dm.B * nc * dm.H * (dm.d / 8);
+  const int grid = (int)std::min<long long>((n8 + 255) / 256, 4096);
+  dim3 g3((dm.Tq + 63) / 64, dm.H, dm.B);
+  if (dm.d == 64) {
+    hipLaunchKernelGGL((k_ksplit<64>), dim3(grid), dim3(256), 0, st, dm, nc, ksum, ks);
+    if (dm.K <= 16)
+      hipLaunchKernelGGL((k_score_mfma<64, 16>), g3, dim3(64), 0, st, dm, nc,
+                         reinterpret_cast<const uint16_t*>(Q), ks, ent, idx, score);
+    else
+      hipLaunchKernelGGL((k_score_mfma<64, 64>), g3, dim3(64), 0, st, dm, nc,
+                         reinterpret_cast<const uint16_t*>(Q), ks, ent, idx, score);
+  } else {
+    hipLaunchKernelGGL((k_ksplit<128>), dim3(grid), dim3(256), 0, st, dm, nc, ksum, ks);
+    if (dm.K <= 16)
+      hipLaunchKernelGGL((k_score_mfma<128, 16>), g3, dim3(64), 0, st, dm, nc,
+                         reinterpret_cast<const uint16_t*>(Q), ks, ent, idx, score);
+    else
+      hipLaunchKernelGGL((k_score_mfma<128, 64>), g3, dim3(64), 0, st, dm, nc,
+                         reinterpret_cast<const uint16_t*>(Q), ks, ent, idx, score);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_mfma_split(const Dims& dm, const void* Q, const float* ksum,
+                                   const float* ent, float* ws_s, int* ws_i, int nsplit,
+                                   hipStream_t st) {
+  const long long rows = (long long)dm.B * dm.Tq * dm.H;
+  if (dm.d == 64)
+    hipLaunchKernelGGL((k_score_split_mfma<64>), dim3(nsplit, rows), dim3(64), 0, st, dm,
+                       reinterpret_cast<const uint16_t*>(Q), ksum, ent, ws_s, ws_i, nsplit);
+  else
+    hipLaunchKernelGGL((k_score_split_mfma<128>), dim3(nsplit, rows), dim3(64), 0, st, dm,
+                       reinterpret_cast<const uint16_t*>(Q), ksum, ent, ws_s, ws_i, nsplit);
+  return hipGetLastError();
+}
+
+}  // namespace hils

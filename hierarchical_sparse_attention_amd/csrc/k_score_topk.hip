@@ -1,8 +1,9 @@
 // Chunk scoring and top-K selection (note §5.2: s^_{i,c} = q_i.k'_c/sqrt(d) + b'_c,
 // I_i = {c in C_i : rank_desc(s^_{i,c}) < K}).
 //
-// Two kernels share one float32 score function (chunk_score), so every path
-// produces bit-identical scores and therefore identical selections:
+// Float32 inputs. (bf16 inputs are scored on matrix cores, k_score_mfma.hip; the
+// split/merge structure below is shared.) Two kernels share one float32 score
+// function (chunk_score), so both produce bit-identical scores and selections:
 //  * rows path (prefill): one thread per query row; summaries are staged in LDS
 //    in blocks and broadcast to all rows of the workgroup; each thread keeps its
 //    row's running top-K list (score desc, chunk id asc) in LDS.
@@ -209,10 +210,19 @@ hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const floa
     const long long rows = (long long)dm.B * dm.Tq * dm.H;
     float* ws_s = reinterpret_cast<float*>(ws);
     int* ws_i = reinterpret_cast<int*>(ws_s + rows * ns * dm.K);
-    hipLaunchKernelGGL((k_score_split<BF16, D>), dim3(ns, rows), dim3(kSplit), 0, st, dm, Q, ksum,
-                       ent, ws_s, ws_i, ns);
+    hipError_t e;
+    if (BF16) {
+      e = launch_score_mfma_split(dm, Q, ksum, ent, ws_s, ws_i, ns, st);
+    } else {
+      hipLaunchKernelGGL((k_score_split<BF16, D>), dim3(ns, rows), dim3(kSplit), 0, st, dm, Q,
+                         ksum, ent, ws_s, ws_i, ns);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_topk_merge, dim3(rows), dim3(256), 0, st, dm, ws_s, ws_i, ns, idx,
                        score);
+  } else if (BF16) {
+    return launch_score_mfma_prefill(dm, Q, ksum, ent, idx, score, ws, st);
   } else {
     const int R = rows_per_wg(dm.K);
     dim3 grid((dm.Tq + R - 1) / R, dm.H, dm.B);
@@ -225,7 +235,7 @@ hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const floa
 }  // namespace
 
 size_t score_topk_ws_bytes(const Dims& dm) {
-  if (!use_split(dm)) return 0;
+  if (!use_split(dm)) return dm.bf16 ? score_mfma_prefill_ws_bytes(dm) : 0;
   const long long rows = (long long)dm.B * dm.Tq * dm.H;
   return (size_t)rows * split_count(dm) * dm.K * (sizeof(float) + sizeof(int));
 }
