@@ -180,14 +180,33 @@ def main():
         for s in range(8):
             dstep(s)
         torch.cuda.synchronize()
-        # restore summaries for the timed pass (warmup summarised nothing new: p < p0+64)
+        # eager (one host call per kernel launch)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
         for s in range(nsteps):
             dstep(s)
         ev[1].record(stream)
         torch.cuda.synchronize()
-        dec_us = ev[0].elapsed_time(ev[1]) * 1e3 / nsteps
+        extra["decode_us_per_token_eager"] = ev[0].elapsed_time(ev[1]) * 1e3 / nsteps
+        # HIP graph: the whole sequence of decode steps captured once and replayed
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for s in range(nsteps):
+                    dstep(s)
+        stream.wait_stream(cap)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        reps = 3
+        ev[0].record(stream)
+        for _ in range(reps):
+            graph.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        dec_us = ev[0].elapsed_time(ev[1]) * 1e3 / (nsteps * reps)
         dec_bytes = (NCd * wd.H * (wd.d + 1) * 4 + wd.K * wd.S * wd.H * wd.d * 2 * 2
                      + 32 * wd.H * wd.d * 2 * 2)
         extra["decode_us_per_token"] = dec_us

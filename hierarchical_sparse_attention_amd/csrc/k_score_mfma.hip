@@ -28,7 +28,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSplitM = 256;  // candidates per decode workgroup
+constexpr int kSplitM = 128;  // candidates per decode workgroup
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
   bf16x8 r;
@@ -202,21 +202,24 @@ __global__ __launch_bounds__(64) void k_score_mfma(Dims dm, int nc, const uint16
 }
 
 // key order: a before b
+// (branch-free: both operands are always read, so rank loops keep loads in flight)
 __device__ __forceinline__ bool before(float sa, int ca, float sb, int cb) {
-  return sa > sb || (sa == sb && ca < cb);
+  return (sa > sb) | ((sa == sb) & (ca < cb));
 }
 
-// Decode split: grid (splits, rows); one wavefront scores 256 candidates of one row
-// (the row sits in M position 0 of each block; other positions are zero) and
-// writes the split's local top-K.
+// Decode split: grid (splits, rows); a workgroup of 4 wavefronts scores the
+// kSplitM candidates of one row, 32 per wavefront (the row sits in M position 0
+// of each 16x16 block; other positions are zero), and writes the split's local
+// top-K, ranked in LDS.
 template <int D>
-__global__ __launch_bounds__(64) void k_score_split_mfma(Dims dm, const uint16_t* __restrict__ Q,
-                                                         const float* __restrict__ ksum,
-                                                         const float* __restrict__ ent,
-                                                         float* __restrict__ ws_s,
-                                                         int* __restrict__ ws_i, int nsplit) {
+__global__ __launch_bounds__(256) void k_score_split_mfma(Dims dm, const uint16_t* __restrict__ Q,
+                                                          const float* __restrict__ ksum,
+                                                          const float* __restrict__ ent,
+                                                          float* __restrict__ ws_s,
+                                                          int* __restrict__ ws_i, int nsplit) {
   __shared__ float ss[kSplitM];
-  const int split = blockIdx.x, r = blockIdx.y, lane = threadIdx.x, c = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6, c = lane & 15, g = lane >> 4;
   const int h = r % dm.H, i = (r / dm.H) % dm.Tq, b = r / (dm.H * dm.Tq);
   const int n = (int)((dm.q_pos0 + i) / dm.S);
   const int cbase = split * kSplitM;
@@ -225,46 +228,59 @@ __global__ __launch_bounds__(64) void k_score_split_mfma(Dims dm, const uint16_t
   for (int ds = 0; ds < D / 32; ++ds)
     qa[ds] = c == 0 ? *reinterpret_cast<const uint4*>(Q + (long long)r * D + 32 * ds + 8 * g)
                     : make_uint4(0, 0, 0, 0);
-  for (int nb = 0; nb < kSplitM / 16; ++nb) {
-    const int chunk = cbase + 16 * nb + c;
+  // this wavefront's summary rows are all loaded before any is used (invalid
+  // chunks read chunk 0 and are discarded), so the loads overlap
+  constexpr int NBW = kSplitM / 16 / 4;
+  float4 raw[NBW][D / 32][2];
+  float ev[NBW];
+#pragma unroll
+  for (int q = 0; q < NBW; ++q) {
+    const int chunk = cbase + 16 * (NBW * w + q) + c;
     const bool cv = chunk < n;
-    bf16x8 hi[D / 32], lo[D / 32];
     const float* src = ksum + (((long long)b * dm.NCcap + (cv ? chunk : 0)) * dm.H + h) * D;
 #pragma unroll
     for (int ds = 0; ds < D / 32; ++ds) {
-      float v[8];
-      if (cv) {
-        const float4 a = *reinterpret_cast<const float4*>(src + 32 * ds + 8 * g);
-        const float4 bb = *reinterpret_cast<const float4*>(src + 32 * ds + 8 * g + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = bb.x; v[5] = bb.y; v[6] = bb.z; v[7] = bb.w;
-      } else {
+      raw[q][ds][0] = *reinterpret_cast<const float4*>(src + 32 * ds + 8 * g);
+      raw[q][ds][1] = *reinterpret_cast<const float4*>(src + 32 * ds + 8 * g + 4);
+    }
+    ev[q] = ent[((long long)b * dm.NCcap + (cv ? chunk : 0)) * dm.H + h];
+  }
+#pragma unroll
+  for (int q = 0; q < NBW; ++q) {
+    const int nb = NBW * w + q;
+    const int chunk = cbase + 16 * nb + c;
+    const bool cv = chunk < n;
+    bf16x8 hi[D / 32], lo[D / 32];
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      const float4 a = raw[q][ds][0], bb = raw[q][ds][1];
+      float v[8] = {a.x, a.y, a.z, a.w, bb.x, bb.y, bb.z, bb.w};
+      if (!cv) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = 0.f;
       }
       split8(v, hi[ds], lo[ds]);
     }
-    const float e = cv ? ent[((long long)b * dm.NCcap + chunk) * dm.H + h] : 0.f;
     const floatx4 acc = score_block<D>(qa, hi, lo);
-    if (g == 0) ss[16 * nb + c] = cv ? fmaf(acc[0], dm.scale, e) : -INFINITY;
+    if (g == 0) ss[16 * nb + c] = cv ? fmaf(acc[0], dm.scale, ev[q]) : -INFINITY;
   }
   __syncthreads();
   const int nvalid = max(0, min(kSplitM, n - cbase));
-  for (int x = lane; x < nvalid; x += 64) {
-    const float s = ss[x];
-    const int cx = cbase + x;
+  if (t < nvalid) {
+    const float sv = ss[t];
+    const int cx = cbase + t;
     int rank = 0;
-    for (int y = 0; y < nvalid; ++y) rank += before(ss[y], cbase + y, s, cx);
+#pragma unroll 8
+    for (int y = 0; y < nvalid; ++y) rank += before(ss[y], cbase + y, sv, cx);
     if (rank < dm.K) {
       const long long o = ((long long)r * nsplit + split) * dm.K + rank;
-      ws_s[o] = s;
+      ws_s[o] = sv;
       ws_i[o] = cx;
     }
   }
 }
 
 }  // namespace
-
-int score_mfma_split_size() { return kSplitM; }
 
 size_t score_mfma_prefill_ws_bytes(const Dims& dm) {
   const int nc = (int)((dm.q_pos0 + dm.Tq - 1) / dm.S);
@@ -304,10 +320,10 @@ hipError_t launch_score_mfma_split(const Dims& dm, const void* Q, const float* k
                                    hipStream_t st) {
   const long long rows = (long long)dm.B * dm.Tq * dm.H;
   if (dm.d == 64)
-    hipLaunchKernelGGL((k_score_split_mfma<64>), dim3(nsplit, rows), dim3(64), 0, st, dm,
+    hipLaunchKernelGGL((k_score_split_mfma<64>), dim3(nsplit, rows), dim3(256), 0, st, dm,
                        reinterpret_cast<const uint16_t*>(Q), ksum, ent, ws_s, ws_i, nsplit);
   else
-    hipLaunchKernelGGL((k_score_split_mfma<128>), dim3(nsplit, rows), dim3(64), 0, st, dm,
+    hipLaunchKernelGGL((k_score_split_mfma<128>), dim3(nsplit, rows), dim3(256), 0, st, dm,
                        reinterpret_cast<const uint16_t*>(Q), ksum, ent, ws_s, ws_i, nsplit);
   return hipGetLastError();
 }

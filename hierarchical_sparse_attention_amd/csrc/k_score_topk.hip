@@ -21,14 +21,15 @@ namespace hils {
 namespace {
 
 constexpr int kBlockChunks = 32;  // summaries staged per LDS block (rows path)
-constexpr int kSplit = 256;       // candidates per workgroup (split path)
+constexpr int kSplit = 128;       // candidates per workgroup (split path)
 constexpr int kMergeMax = 4096;   // entries the merge kernel ranks in LDS
 
 __host__ __device__ inline int rows_per_wg(int K) { return K <= 16 ? 256 : (K <= 32 ? 128 : 64); }
 
 // key order: a before b
+// (branch-free: both operands are always read, so rank loops keep loads in flight)
 __device__ __forceinline__ bool before(float sa, int ca, float sb, int cb) {
-  return sa > sb || (sa == sb && ca < cb);
+  return (sa > sb) | ((sa == sb) & (ca < cb));
 }
 
 template <bool BF16, int D>
@@ -140,7 +141,9 @@ __global__ __launch_bounds__(kSplit) void k_score_split(Dims dm, const void* __r
 }
 
 // Split path, stage 2: one workgroup per row ranks the union of local lists.
-__global__ __launch_bounds__(256) void k_topk_merge(Dims dm, const float* __restrict__ ws_s,
+// Split sp holds min(K, candidates in the split) entries at slots sp*K ...; every
+// slot is loaded at once (invalid slots become (-inf, INT_MAX)) and ranked.
+__global__ __launch_bounds__(1024) void k_topk_merge(Dims dm, const float* __restrict__ ws_s,
                                                     const int* __restrict__ ws_i, int nsplit,
                                                     int32_t* __restrict__ idx,
                                                     float* __restrict__ score) {
@@ -152,16 +155,14 @@ __global__ __launch_bounds__(256) void k_topk_merge(Dims dm, const float* __rest
   const int i = (r / dm.H) % dm.Tq;
   const int n = (int)((dm.q_pos0 + i) / dm.S);
   const int K = dm.K;
-  // gather the valid entries of each split's list
-  int E = 0;
-  for (int sp = 0; sp < nsplit; ++sp) {
+  const int E = nsplit * K;
+  for (int x = t; x < E; x += blockDim.x) {
+    const int sp = x / K, k = x % K;
     const int nv = min(K, max(0, min(kSplit, n - sp * kSplit)));
-    for (int k = t; k < nv; k += blockDim.x) {
-      const long long o = ((long long)r * nsplit + sp) * K + k;
-      es[E + k] = ws_s[o];
-      ec[E + k] = ws_i[o];
-    }
-    E += nv;
+    const long long o = (long long)r * E + x;
+    const bool v = k < nv;
+    es[x] = v ? ws_s[o] : -INFINITY;
+    ec[x] = v ? ws_i[o] : 0x7fffffff;
   }
   __syncthreads();
   const int cnt = min(K, n);
@@ -169,8 +170,9 @@ __global__ __launch_bounds__(256) void k_topk_merge(Dims dm, const float* __rest
     const float s = es[x];
     const int c = ec[x];
     int rank = 0;
+#pragma unroll 8
     for (int y = 0; y < E; ++y) rank += before(es[y], ec[y], s, c);
-    if (rank < cnt) {
+    if (c != 0x7fffffff && rank < cnt) {
       sel_s[rank] = s;
       sel_c[rank] = c;
     }
@@ -219,8 +221,10 @@ hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const floa
       e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_topk_merge, dim3(rows), dim3(256), 0, st, dm, ws_s, ws_i, ns, idx,
-                       score);
+    const int E = ns * dm.K;  // one thread per entry when they fit in a workgroup
+    const int nt = E <= 1024 ? ((E + 63) / 64) * 64 : 1024;
+    hipLaunchKernelGGL(k_topk_merge, dim3(rows), dim3(max(nt, 64)), 0, st, dm, ws_s, ws_i, ns,
+                       idx, score);
   } else if (BF16) {
     return launch_score_mfma_prefill(dm, Q, ksum, ent, idx, score, ws, st);
   } else {
