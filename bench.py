@@ -24,6 +24,15 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attend_fuse_prefill_345m_traffic.json")
+# sources of the kernels behind hils_attend_fuse on the prefill path
+ATTEND_SOURCES = ["hierarchical_sparse_attention_amd/csrc/k_attend_mfma.hip",
+                  "hierarchical_sparse_attention_amd/csrc/k_attend_fuse.hip",
+                  "hierarchical_sparse_attention_amd/csrc/hils_internal.h"]
+COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -32,7 +41,72 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the 7B-class GQA prefill and the training-step timings")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="run 3 prefill steps and one calibration copy, for counter collection")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs into the traffic record")
     return ap.parse_args()
+
+
+def sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTEND_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def write_traffic_record(fetch_csv, write_csv):
+    """HBM bytes per attend launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by the same counter's reading for an elementwise copy (neg) of
+    COPY_BYTES."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        out = {}
+        for (name, _), v in acc.items():
+            out.setdefault(name, []).append(v)
+        return out
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, pat):
+        ks = [k for k in d if pat in k]
+        vals = [v for k in ks for v in d[k]]
+        return sum(vals) / len(vals) * 1024.0 if vals else None  # bytes per dispatch
+
+    f_copy, w_copy = pick(fetch, "neg"), pick(write, "neg")
+    f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    rec = {"sources_hash": sources_hash(), "copy_bytes": COPY_BYTES,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for pat in ("k_vt_prep", "k_attend_mfma"):
+        fb, wb = pick(fetch, pat), pick(write, pat)
+        if fb is not None:
+            rec["kernels"][pat] = {"fetch_bytes": fb * f_scale, "write_bytes": wb * w_scale}
+    rec["attend_call_bytes"] = sum(v["fetch_bytes"] + v["write_bytes"]
+                                   for v in rec["kernels"].values())
+    os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def read_traffic_record():
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+    except (OSError, ValueError):
+        return None
+    return rec if rec.get("sources_hash") == sources_hash() else None
 
 
 def log(msg):
@@ -61,6 +135,9 @@ def algorithmic_counts(w, idx_host):
 
 def main():
     args = parse()
+    if args.traffic:
+        write_traffic_record(*args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the HiLS path here runs on a single MI355X).", file=sys.stderr)
@@ -104,6 +181,17 @@ def main():
         k_score()
         k_attend()
 
+    if args.pmc_run:
+        for _ in range(3):
+            step()
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # one elementwise kernel: COPY_BYTES read, COPY_BYTES written
+        torch.cuda.synchronize()
+        log("pmc run done")
+        return
+
     log("warmup")
     for _ in range(args.warmup):
         step()
@@ -138,9 +226,13 @@ def main():
     else:
         roof = dict(bound="mfma", achieved=ach_attend, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = dominant
+    rec = read_traffic_record() if dominant == "attend_fuse" else None
+    roof["traffic"] = rec["attend_call_bytes"] if rec else None
+    roof["kernel"] = ("hils_attend_fuse (k_vt_prep + k_attend_mfma)" if dominant == "attend_fuse"
+                      else dominant)
     roof["ms_per_launch"] = kern[dominant]
+    roof["algorithmic"] = (cnt["attend_fuse"] if dominant == "attend_fuse"
+                           else cnt[dominant])
 
     extra = {"kernels_ms": kern,
              "attend_tflops": ach_attend, "summarize_gbs": ach_sum, "score_topk_gbs": ach_score_bw,
@@ -212,6 +304,58 @@ def main():
         extra["decode_us_per_token"] = dec_us
         extra["decode_gbs_wallclock"] = dec_bytes / (dec_us * 1e-6) / 1e9
         extra["decode_steps"] = nsteps
+
+    # ------------------------------------------- 7B-class GQA prefill, training step
+    def ev_ms(fn, reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    if not args.no_extra_configs:
+        for name in ("prefill_7b_gqa", "train_345m"):
+            wx = synth.workloads()[name]
+            log(f"generating {name} inputs")
+            xx = synth.make_inputs(wx)
+            keys = ("Q", "K", "V", "Ql") + (("dO",) if wx.need_dO else ())
+            tx = {k: torch.from_numpy(xx[k]).to(dev, torch.bfloat16) for k in keys}
+            del xx
+            fw = hsa.forward(tx["Q"], tx["K"], tx["V"], tx["Ql"], wx.K, wx.S)
+            ksx, enx, llx, ix, scx = (fw[k] for k in ("ksum", "ent", "lse_l", "idx", "score"))
+            Ox, lox, ltx = fw["O"], fw["lse_own"], fw["lse_tot"]
+            calls = {
+                "summarize": lambda: hsa.summarize(tx["K"], tx["Ql"], wx.S, ksum=ksx, ent=enx,
+                                                   lse_l=llx),
+                "score_topk": lambda: hsa.score_topk(tx["Q"], ksx, enx, wx.K, wx.S, 0, wx.T,
+                                                     Hkv=wx.Hkv, idx=ix, score=scx),
+                "attend_fuse": lambda: hsa.attend_fuse(tx["Q"], tx["K"], tx["V"], ix, scx, wx.S,
+                                                       O=Ox, lse_own=lox, lse_tot=ltx),
+            }
+            if wx.need_dO:
+                calls["backward"] = lambda: hsa.backward(tx["Q"], tx["K"], tx["V"], tx["Ql"], ksx,
+                                                         enx, llx, ix, scx, ltx, tx["dO"], wx.S)
+            for fn in calls.values():
+                fn()
+            torch.cuda.synchronize()
+            km = {k: ev_ms(fn, 5) for k, fn in calls.items()}
+            cx = algorithmic_counts(wx, ix.cpu().numpy())
+            fwd_ms = km["summarize"] + km["score_topk"] + km["attend_fuse"]
+            rec = {"kernels_ms": km, "forward_ms": fwd_ms,
+                   "attend_tflops": cx["attend_fuse"]["flops"] / (km["attend_fuse"] * 1e-3) / 1e12,
+                   "score_topk_tflops": cx["score_topk"]["flops"] / (km["score_topk"] * 1e-3) / 1e12,
+                   "summarize_gbs": cx["summarize"]["bytes"] / (km["summarize"] * 1e-3) / 1e9}
+            if wx.need_dO:
+                bwd_flops = 10 * wx.d * cx["key_visits"]
+                rec["backward_tflops"] = bwd_flops / (km["backward"] * 1e-3) / 1e12
+                rec["train_tokens_per_s"] = wx.B * wx.T / ((fwd_ms + km["backward"]) * 1e-3)
+            else:
+                rec["prefill_tokens_per_s"] = wx.B * wx.T / (fwd_ms * 1e-3)
+            extra[name] = rec
+            del tx, fw, calls
+            torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
