@@ -46,10 +46,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 template <int D>
 struct Cfg {
   static constexpr int RMAX = D == 64 ? 256 : 128;  // rows per workgroup
-  static constexpr int AP = D + 1;                  // accumulator row pitch (words)
+  static constexpr int AP = D + 2;                  // accumulator row pitch (words, even)
+  static constexpr int QP = D + 8;                  // LDS query row pitch (bf16)
   static constexpr int KF = 4 * (D / 32);           // K fragments (uint4) per lane per chunk
   static constexpr int VF = (D / 16) * 2;           // V^T fragments per lane per chunk
-  static constexpr bool PREFETCH = D == 64;         // second fragment set in registers
+  static constexpr bool PREFETCH = D == 64;         // second fragment set, LDS reads ahead
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
@@ -214,31 +215,85 @@ __device__ __forceinline__ void tile_core(const Frag<D>& f, const uint4* qv, int
   }
 }
 
+// Scores, weights and values of one 16-row tile of a selected chunk, fast path:
+// u_j = 2^(s_j scale2) with no running maximum and no reference, since the
+// intra-chunk normalisation divides any common factor out. The caller checks
+// that the weight sum is in [2^-64, 2^64] and otherwise redoes the tile with
+// tile_core. The row sum comes out of the matrix core as a ones row of
+// the PV product, i.e. it is the sum of the bf16-rounded weights that multiply
+// the values.
+template <int D>
+__device__ __forceinline__ void tile_ref(const Frag<D>& f, const uint4* qv, float scale2,
+                                         floatx4* o, float* z) {
+  floatx4 s[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.k[kb * (D / 32) + ds]),
+                                                      as_bf16x8(qv[ds]), s[kb], 0, 0, 0);
+  }
+  bf16x8 pf[2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      pf[kb >> 1][(kb & 1) * 4 + r] = (__bf16)fast_exp2(s[kb][r] * scale2);
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    o[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.v[db * 2 + ks]), pf[ks], o[db],
+                                                      0, 0, 0);
+  }
+  const __bf16 one = (__bf16)1.0f;
+  const bf16x8 ones = {one, one, one, one, one, one, one, one};
+  floatx4 zz = floatx4{0.f, 0.f, 0.f, 0.f};
+  zz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[0], zz, 0, 0, 0);
+  zz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[1], zz, 0, 0, 0);
+  *z = zz[0];
+}
+
 // ------------------------------------------------------------------ main kernel
+// Accumulator column of feature 16 db + 4 g + r (the O^T fragment element r of
+// block db held by lane group g). The four lane groups of one LDS atomic land 16
+// banks apart, so rows that are a few apart (the usual spacing of the rows that
+// picked a chunk) do not pile onto the same banks.
+__host__ __device__ __forceinline__ int acc_col(int db, int g, int r) {
+  return 64 * (db >> 2) + 16 * g + 4 * (db & 3) + r;
+}
+
 struct Smem {
-  int* acc;     // [R][AP] fixed point (float during the own-chunk phase)
-  uint32_t* ent;
-  float* lw;    // fusion log2-weight (s^ - Lambda) log2(e) of each entry
+  int* acc;       // [R][AP] fixed point (float during the own-chunk phase)
+  uint16_t* qs;   // [R][QP] the workgroup's query rows (bf16)
+  uint32_t* ent;  // row-list entries, chunk-major: rho | k << 16
+  float* lw;      // per entry: its chunk score times log2(e)
   int* cnt;
   int* off;
   int* cur;
   int* nz;
-  float* lown;
-  float* lam;
-  int* rowid;
+  float* lown;    // own-chunk log-mass, then the own weight in fixed-point units
+  float* lam;     // Lambda times log2(e)
+  float* pm;      // per (row, group of 8 slots): max score and sum of exp(score - max)
+  float* pz;
+  int* nsel;      // per row: number of selected-chunk terms added to its accumulator
   int* misc;
 };
 
 template <int D>
 __host__ __device__ inline size_t smem_bytes(int R, int K, int ncr) {
-  return (size_t)R * Cfg<D>::AP * 4 + (size_t)R * K * 8 + 4 * (size_t)(ncr + 1) * 4 +
-         3 * (size_t)R * 4 + 32 * 4;
+  return (size_t)R * Cfg<D>::AP * 4 + (size_t)R * Cfg<D>::QP * 2 + (size_t)R * K * 8 +
+         4 * (size_t)(ncr + 1) * 4 + 3 * (size_t)R * 4 + 2 * (size_t)R * ((K + 7) / 8) * 4 +
+         32 * 4;
 }
 
 template <int D>
 __device__ __forceinline__ Smem carve(char* base, int R, int K, int ncr) {
   Smem s;
   s.acc = reinterpret_cast<int*>(base); base += (size_t)R * Cfg<D>::AP * 4;
+  s.qs = reinterpret_cast<uint16_t*>(base); base += (size_t)R * Cfg<D>::QP * 2;
   s.ent = reinterpret_cast<uint32_t*>(base); base += (size_t)R * K * 4;
   s.lw = reinterpret_cast<float*>(base); base += (size_t)R * K * 4;
   s.cnt = reinterpret_cast<int*>(base); base += (ncr + 1) * 4;
@@ -247,7 +302,9 @@ __device__ __forceinline__ Smem carve(char* base, int R, int K, int ncr) {
   s.nz = reinterpret_cast<int*>(base); base += (ncr + 1) * 4;
   s.lown = reinterpret_cast<float*>(base); base += R * 4;
   s.lam = reinterpret_cast<float*>(base); base += R * 4;
-  s.rowid = reinterpret_cast<int*>(base); base += R * 4;
+  s.pm = reinterpret_cast<float*>(base); base += (size_t)R * ((K + 7) / 8) * 4;
+  s.pz = reinterpret_cast<float*>(base); base += (size_t)R * ((K + 7) / 8) * 4;
+  s.nsel = reinterpret_cast<int*>(base); base += R * 4;
   s.misc = reinterpret_cast<int*>(base);
   return s;
 }
@@ -285,6 +342,152 @@ __device__ __forceinline__ int block_exclusive_scan(int* a, int n, int* scratch)
   return total;
 }
 
+// Query fragment of workgroup row rho from LDS (zero for an empty tile column).
+template <int D>
+__device__ __forceinline__ void lds_q(uint4* qv, const uint16_t* qs, int rho, bool valid) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds)
+    qv[ds] = valid ? *reinterpret_cast<const uint4*>(qs + rho * Cfg<D>::QP + 32 * ds + 8 * g)
+                   : make_uint4(0, 0, 0, 0);
+}
+
+// Own-chunk work items are the (own chunk, 16-row tile) pairs in chunk order;
+// each wave takes a contiguous run of them so it mostly stays on one chunk.
+// Returns false when `item` is past the last one.
+__device__ __forceinline__ bool own_item(int item, long long p0, int S, int G, int Rv,
+                                         int own_first, int own_last, int* oc_out, int* ra_out,
+                                         int* rb_out, int* tl_out) {
+  for (int oc = own_first; oc <= own_last; ++oc) {
+    const int ra = (int)max(0LL, (long long)oc * S - p0) * G;
+    const int rb = (int)min((long long)Rv, ((long long)oc * S + S - p0) * G);
+    const int ntile = (rb - ra + 15) / 16;
+    if (item < ntile) {
+      *oc_out = oc, *ra_out = ra, *rb_out = rb, *tl_out = item;
+      return true;
+    }
+    item -= ntile;
+  }
+  return false;
+}
+
+__device__ __forceinline__ int own_item_count(long long p0, int S, int G, int Rv, int own_first,
+                                              int own_last) {
+  int n = 0;
+  for (int oc = own_first; oc <= own_last; ++oc) {
+    const int ra = (int)max(0LL, (long long)oc * S - p0) * G;
+    const int rb = (int)min((long long)Rv, ((long long)oc * S + S - p0) * G);
+    n += (rb - ra + 15) / 16;
+  }
+  return n;
+}
+
+// Adds one tile's normalised, fused-weighted output to its rows' fixed-point
+// accumulators: weight 2^(lw2 - lam2) / z (lw2 = s^ log2 e, lam2 = Lambda log2 e).
+// The conversion to an integer is one fma: for |v| < 2^22, v + 1.5 2^23 is a
+// float whose bit pattern is 0x4B400000 + round(v). Two neighbouring columns a, b
+// share one 64-bit word and one 64-bit integer atomic: the word gains
+// bits(b) 2^32 + bits(a), and the sum of such words is exact mod 2^64 whatever the
+// order. The offsets (kMagic (2^32 + 1) per added term) are removed at the end.
+constexpr float kMagicF = 12582912.0f;  // 1.5 * 2^23
+constexpr uint32_t kMagic = 0x4B400000u;
+
+template <int D>
+__device__ __forceinline__ void accumulate_tile(const Smem& sm, const floatx4* o, float z,
+                                                uint32_t en, float lw2, float lam2,
+                                                float fx_scale) {
+  const int gl = (threadIdx.x & 63) >> 4;
+  const float fw = fast_exp2(lw2 - lam2) * __builtin_amdgcn_rcpf(z) * fx_scale;
+  int* ar = sm.acc + (int)(en & 0xFFFFu) * Cfg<D>::AP;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; q += 2) {
+      const uint64_t lo = __float_as_uint(fmaf(o[db][q], fw, kMagicF));
+      const uint64_t hi = __float_as_uint(fmaf(o[db][q + 1], fw, kMagicF));
+      atomicAdd(reinterpret_cast<unsigned long long*>(ar + acc_col(db, gl, q)),
+                (unsigned long long)((hi << 32) | lo));
+    }
+}
+
+// Weight sums of the fast path that are safe to use (see tile_ref).
+__device__ __forceinline__ bool z_ok(float z) { return z >= 0x1p-64f && z <= 0x1p64f; }
+
+// Row-list entry e of a chunk, clamped to the last entry so every LDS read is of
+// real data (a lane past the end computes a copy of the last row and does not
+// accumulate it); reads happen without branches, so they stay in flight.
+template <int D>
+__device__ __forceinline__ void read_entry(const Smem& sm, int e0, int n, int e, bool* v,
+                                           uint32_t* en, float* lw, float* lm, uint4* q) {
+  *v = e < n;
+  const int ec = e0 + min(e, n - 1);
+  *en = sm.ent[ec];
+  *lw = sm.lw[ec];
+  const int rho = (int)(*en & 0xFFFFu);
+  *lm = sm.lam[rho];
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds)
+    q[ds] = *reinterpret_cast<const uint4*>(sm.qs + rho * Cfg<D>::QP + 32 * ds + 8 * g);
+}
+
+// All tiles of one selected chunk (fragments in f) for the rows that picked it,
+// NT independent tiles per step (two for d = 64, so their matrix-core and vector
+// work interleave). The next step's entries, query fragments and row normalisers
+// are read from LDS while the current step runs. When the fast path's weight sum
+// is out of range on any lane (or `fast` is off) the step is redone with the
+// running-maximum tile.
+template <int D, int NT>
+__device__ __forceinline__ void run_chunk(const Frag<D>& f, const Smem& sm, int c, float scale2,
+                                          bool fast, float fx_scale) {
+  const int col = threadIdx.x & 15;
+  const int e0 = sm.off[c], n = sm.cnt[c];
+  const int nstep = (n + 16 * NT - 1) / (16 * NT);
+  bool v[NT];
+  uint32_t en[NT];
+  float lw[NT], lm[NT];
+  uint4 q[NT][D / 32];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) read_entry<D>(sm, e0, n, 16 * i + col, &v[i], &en[i], &lw[i], &lm[i], q[i]);
+  for (int st = 0; st < nstep; ++st) {
+    bool vn[NT];
+    uint32_t enn[NT];
+    float lwn[NT], lmn[NT];
+    uint4 qn[NT][D / 32];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      read_entry<D>(sm, e0, n, 16 * NT * (st + 1) + 16 * i + col, &vn[i], &enn[i], &lwn[i],
+                    &lmn[i], qn[i]);
+    floatx4 o[NT][D / 16];
+    float z[NT];
+    bool bad = !fast;
+    if (fast) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i) tile_ref<D>(f, q[i], scale2, o[i], &z[i]);
+      bool b = false;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) b |= !z_ok(z[i]);
+      bad = __builtin_amdgcn_ballot_w64(b) != 0;
+    }
+    if (bad) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        float m2;
+        tile_core<D, false>(f, q[i], kChunk, scale2, o[i], &z[i], &m2);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      if (v[i]) accumulate_tile<D>(sm, o[i], z[i], en[i], lw[i], lm[i], fx_scale);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      v[i] = vn[i], en[i] = enn[i], lw[i] = lwn[i], lm[i] = lmn[i];
+#pragma unroll
+      for (int ds = 0; ds < D / 32; ++ds) q[i][ds] = qn[i][ds];
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     Dims dm, int R, int Rq, int ncr_cap, int nqb, int nct, const uint16_t* __restrict__ Q,
@@ -311,51 +514,101 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   const long long vt_base = ((long long)b * dm.Hkv + g) * nct * (long long)D * kChunk;
   const float* vmx = vmax + ((long long)b * dm.Hkv + g) * nct;
   const float scale2 = dm.scale * kLog2e;
+  // global row of workgroup row rho (query position qi0 + rho / G, head g G + rho % G)
+  auto row_of = [&](int rho) -> long long {
+    return ((long long)b * dm.Tq + qi0 + rho / G) * dm.H + (long long)g * G + rho % G;
+  };
 
-  // ---- setup: row table and per-chunk row lists (counting sort of the selections)
-  for (int c = t; c <= ncr; c += kThreads) sm.cnt[c] = 0;
-  for (int rho = t; rho < Rv; rho += kThreads)
-    sm.rowid[rho] = (int)(((long long)b * dm.Tq + qi0 + rho / G) * dm.H + (long long)g * G + rho % G);
-  __syncthreads();
-  for (int rho = t; rho < Rv; rho += kThreads) {
-    const long long r = sm.rowid[rho];
-    const int own = (int)((p0 + rho / G) / S);
-    for (int k = 0; k < Ksel; ++k) {
-      const int c = idx[r * Ksel + k];
-      if (c >= 0 && c < own) atomicAdd(&sm.cnt[c], 1);
+  // own-chunk items of this wave; for d = 64 the first fragment is requested now
+  // and lands during the set-up
+  const int n_own = own_item_count(p0, S, G, Rv, own_first, own_last);
+  const int per_wave = (n_own + kWaves - 1) / kWaves;
+  const int item0 = w * per_wave, item_end = min(n_own, item0 + per_wave);
+  Frag<D> f, f2;
+  int o_oc = 0, o_ra = 0, o_rb = 0, o_tl = 0;
+  bool o_have = item0 < item_end &&
+                own_item(item0, p0, S, G, Rv, own_first, own_last, &o_oc, &o_ra, &o_rb, &o_tl);
+  if (C::PREFETCH && o_have)
+    load_frag<D>(f, K, Vt, kv_base, kv_stride, o_oc, vt_base + (long long)o_oc * D * kChunk, dm.Tkv);
+
+  // ---- set-up: every global read of the set-up is issued first
+  const int kgroups = (Ksel + 7) / 8;  // Rv * kgroups <= kThreads (see plan)
+  const bool has_item = t < Rv * kgroups;
+  const int it_rho = t / kgroups, it_k0 = (t % kgroups) * 8;
+  const int it_own = (int)((p0 + it_rho / G) / S);
+  int cs[8];
+  float ss[8];
+  {
+    const long long r = has_item ? row_of(it_rho) : 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool in = has_item && it_k0 + j < Ksel;
+      cs[j] = in ? idx[r * Ksel + it_k0 + j] : -1;
+      ss[j] = in ? score[r * Ksel + it_k0 + j] : -INFINITY;
     }
   }
+  const int nqv = Rv * (D / 8);  // <= 4 * kThreads (see plan)
+  auto ldq = [&](int j) -> uint4 {  // past the end: reload the last piece (in bounds)
+    const int x = min(t + j * kThreads, nqv - 1);
+    return *reinterpret_cast<const uint4*>(Q + row_of(x / (D / 8)) * D + (x % (D / 8)) * 8);
+  };
+  auto stq = [&](int j, uint4 v) {
+    const int x = t + j * kThreads;
+    if (x < nqv) *reinterpret_cast<uint4*>(sm.qs + (x / (D / 8)) * C::QP + (x % (D / 8)) * 8) = v;
+  };
+  const uint4 qv0 = ldq(0), qv1 = ldq(1), qv2 = ldq(2), qv3 = ldq(3);
+  const float vpre = t <= own_last ? vmx[t] : 0.f;
+
+  for (int c = t; c <= ncr; c += kThreads) sm.cnt[c] = 0;
+  for (int rho = t; rho < Rv; rho += kThreads) sm.nsel[rho] = 0;
+  __syncthreads();
+  stq(0, qv0), stq(1, qv1), stq(2, qv2), stq(3, qv3);
+  int nmine = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (cs[j] >= 0 && cs[j] < it_own) {
+      atomicAdd(&sm.cnt[cs[j]], 1);
+      ++nmine;
+    }
+  if (nmine) atomicAdd(&sm.nsel[it_rho], nmine);
   __syncthreads();
   for (int c = t; c < ncr; c += kThreads) {
     sm.off[c] = sm.cnt[c];
     sm.nz[c] = sm.cnt[c] > 0 ? 1 : 0;
   }
   __syncthreads();
-  const int nent = block_exclusive_scan(sm.off, ncr, sm.misc);
+  block_exclusive_scan(sm.off, ncr, sm.misc);
   const int nnz = block_exclusive_scan(sm.nz, ncr, sm.misc + 8);
   for (int c = t; c < ncr; c += kThreads) sm.cur[c] = sm.off[c];
   __syncthreads();
-  for (int rho = t; rho < Rv; rho += kThreads) {
-    const long long r = sm.rowid[rho];
-    const int own = (int)((p0 + rho / G) / S);
-    for (int k = 0; k < Ksel; ++k) {
-      const int c = idx[r * Ksel + k];
-      if (c >= 0 && c < own) {
-        const int p = atomicAdd(&sm.cur[c], 1);
-        sm.ent[p] = (uint32_t)rho | ((uint32_t)k << 16);
-      }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (cs[j] >= 0 && cs[j] < it_own) {
+      const int p = atomicAdd(&sm.cur[cs[j]], 1);
+      sm.ent[p] = (uint32_t)it_rho | ((uint32_t)(it_k0 + j) << 16);
+      sm.lw[p] = ss[j] * kLog2e;
     }
+  if (has_item) {  // partial log-sum-exp of this group of scores (padding holds -inf)
+    float m8 = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m8 = fmaxf(m8, ss[j]);
+    float z8 = 0.f;
+    if (m8 > -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z8 += expf(ss[j] - m8);
+    }
+    sm.pm[t] = m8;
+    sm.pz[t] = z8;
   }
   __syncthreads();
   // compacted list of non-empty chunks (chunk c goes to slot nz[c]) and the bound
   // max|V| over every chunk this workgroup reads
   float vm = 0.f;
-  for (int c = t; c < ncr; c += kThreads)
-    if (sm.cnt[c] > 0) {
-      sm.cur[sm.nz[c]] = c;
-      vm = fmaxf(vm, vmx[c]);
-    }
-  for (int c = own_first + t; c <= own_last; c += kThreads) vm = fmaxf(vm, vmx[c]);
+  for (int c = t; c <= own_last; c += kThreads) {
+    const bool used = c >= own_first || sm.cnt[c] > 0;
+    if (c < ncr && sm.cnt[c] > 0) sm.cur[sm.nz[c]] = c;
+    if (used) vm = fmaxf(vm, c == t ? vpre : vmx[c]);
+  }
   vm = wave_max(vm);
   if (lane == 0) reinterpret_cast<float*>(sm.misc)[16 + w] = vm;
   __syncthreads();
@@ -364,144 +617,122 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   for (int x = 0; x < kWaves; ++x)
     vmax_wg = fmaxf(vmax_wg, reinterpret_cast<float*>(sm.misc)[16 + x]);
   // fixed point: every partial sum is a sub-convex combination of values, so its
-  // magnitude is at most max|V| < 2^ex, mapped below 2^29
+  // magnitude is at most max|V| < 2^ex, mapped below 2^21 (each term then fits
+  // the one-fma conversion of accumulate_tile)
   int ex = 0;
   frexpf(fmaxf(vmax_wg, 1e-30f), &ex);
-  const float fx_scale = ldexpf(1.0f, 29 - ex);
-  const float fx_inv = ldexpf(1.0f, ex - 29);
+  const float fx_scale = ldexpf(1.0f, 21 - ex);
+  const float fx_inv = ldexpf(1.0f, ex - 21);
+  // fast path: weight sums below 2^64 and values below 2^50 keep every partial
+  // product of the PV step finite
+  const bool fast = vmax_wg < 0x1p50f;
 
-  // ---- own chunks: causal, normalised; items (own chunk, 16-row tile) round robin
-  {
-    Frag<D> f;
-    int loaded = -1;
-    int item = 0;
-    for (int oc = own_first; oc <= own_last; ++oc) {
-      const int ra = (int)max(0LL, (long long)oc * S - p0) * G;
-      const int rb = (int)min((long long)Rv, ((long long)oc * S + S - p0) * G);
-      const int ntile = (rb - ra + 15) / 16;
-      for (int tl = 0; tl < ntile; ++tl, ++item) {
-        if (item % kWaves != w) continue;
-        if (loaded != oc) {
-          load_frag<D>(f, K, Vt, kv_base, kv_stride, oc, vt_base + (long long)oc * D * kChunk, dm.Tkv);
-          loaded = oc;
-        }
-        const int rho = ra + 16 * tl + col;
-        const bool valid = rho < rb;
-        const long long r = valid ? sm.rowid[rho] : 0;
-        const int nk = valid ? (int)(p0 + rho / G - (long long)oc * S) + 1 : 0;
-        uint4 qv[D / 32];
-        load_q<D>(qv, Q, r, valid);
-        floatx4 o[D / 16];
-        float z, m2;
-        tile_core<D, true>(f, qv, nk, scale2, o, &z, &m2);
-        if (valid) {
-          const float inv = 1.0f / z;
-          float* ar = reinterpret_cast<float*>(sm.acc + rho * C::AP);
+  // ---- own chunks: causal, normalised (float accumulators for now)
+  for (int item = item0; o_have; ) {
+    if (!C::PREFETCH)
+      load_frag<D>(f, K, Vt, kv_base, kv_stride, o_oc, vt_base + (long long)o_oc * D * kChunk,
+                   dm.Tkv);
+    const int rho = o_ra + 16 * o_tl + col;
+    const bool valid = rho < o_rb;
+    const int nk = valid ? (int)(p0 + rho / G - (long long)o_oc * S) + 1 : 0;
+    uint4 qo[D / 32];
+    lds_q<D>(qo, sm.qs, rho, valid);
+    floatx4 o[D / 16];
+    float z, m2;
+    tile_core<D, true>(f, qo, nk, scale2, o, &z, &m2);
+    if (valid) {
+      const float inv = __builtin_amdgcn_rcpf(z);
+      float* ar = reinterpret_cast<float*>(sm.acc + rho * C::AP);
 #pragma unroll
-          for (int db = 0; db < D / 16; ++db)
+      for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ar[16 * db + 4 * gl + q] = o[db][q] * inv;
-          if (gl == 0) sm.lown[rho] = (m2 + __log2f(z)) * kLn2;
-        }
-      }
+        for (int q = 0; q < 4; ++q) ar[acc_col(db, gl, q)] = o[db][q] * inv;
+      if (gl == 0) sm.lown[rho] = (m2 + __log2f(z)) * kLn2;
     }
+    const int prev = o_oc;
+    ++item;
+    o_have = item < item_end &&
+             own_item(item, p0, S, G, Rv, own_first, own_last, &o_oc, &o_ra, &o_rb, &o_tl);
+    if (C::PREFETCH && o_have && o_oc != prev)
+      load_frag<D>(f, K, Vt, kv_base, kv_stride, o_oc, vt_base + (long long)o_oc * D * kChunk,
+                   dm.Tkv);
   }
+  // the first selected chunk's fragment is requested before the fusion set-up
+  if (C::PREFETCH && w < nnz)
+    load_frag<D>(f, K, Vt, kv_base, kv_stride, sm.cur[w],
+                 vt_base + (long long)sm.cur[w] * D * kChunk, dm.Tkv);
   __syncthreads();
 
-  // ---- fusion normaliser per row; own contribution to fixed point
+  // ---- fusion normaliser per row from the own log-mass and the score partials
   for (int rho = t; rho < Rv; rho += kThreads) {
-    const long long r = sm.rowid[rho];
     const float lo = sm.lown[rho];
     float mx = lo;
-    for (int k = 0; k < Ksel; ++k) mx = fmaxf(mx, score[r * Ksel + k]);
+    for (int kg = 0; kg < kgroups; ++kg) mx = fmaxf(mx, sm.pm[rho * kgroups + kg]);
     float z = expf(lo - mx);
-    for (int k = 0; k < Ksel; ++k) z += expf(score[r * Ksel + k] - mx);
+    for (int kg = 0; kg < kgroups; ++kg) {
+      const float zg = sm.pz[rho * kgroups + kg];
+      if (zg > 0.f) z += zg * expf(sm.pm[rho * kgroups + kg] - mx);
+    }
     const float lam = mx + logf(z);
-    sm.lam[rho] = lam;
-    const float a = expf(lo - lam) * fx_scale;
-    int* ar = sm.acc + rho * C::AP;
-    for (int e = 0; e < D; ++e) ar[e] = (int)(__int_as_float(ar[e]) * a);
+    sm.lam[rho] = lam * kLog2e;
+    sm.lown[rho] = expf(lo - lam) * fx_scale;
+    const long long r = row_of(rho);
     if (lse_own) lse_own[r] = lo;
     if (lse_tot) lse_tot[r] = lam;
   }
   __syncthreads();
-  for (int e = t; e < nent; e += kThreads) {
-    const uint32_t en = sm.ent[e];
-    const int rho = (int)(en & 0xFFFFu), k = (int)(en >> 16);
-    sm.lw[e] = (score[(long long)sm.rowid[rho] * Ksel + k] - sm.lam[rho]) * kLog2e;
+  // own contribution to fixed point: columns 2k, 2k + 1 become the 64-bit word
+  // b 2^32 + a of their signed values
+  for (int x = t; x < Rv * (D / 2); x += kThreads) {
+    const int rho = x / (D / 2), e = 2 * (x % (D / 2));
+    int64_t* a = reinterpret_cast<int64_t*>(sm.acc + rho * C::AP + e);
+    const float2 v = *reinterpret_cast<const float2*>(a);
+    const float w = sm.lown[rho];
+    *a = (int64_t)(int)(v.y * w) * 4294967296LL + (int64_t)(int)(v.x * w);
   }
   __syncthreads();
 
-  // ---- selected chunks: chunk u belongs to wavefront u mod 8; no barriers
-  {
-    Frag<D> f, fn;
-    if (w < nnz)
-      load_frag<D>(f, K, Vt, kv_base, kv_stride, sm.cur[w],
-                   vt_base + (long long)sm.cur[w] * D * kChunk, dm.Tkv);
+  // ---- selected chunks: chunk u belongs to wavefront u mod 8; no barriers.
+  if (!C::PREFETCH) {
     for (int u = w; u < nnz; u += kWaves) {
-      const int c = sm.cur[u];
-      const bool more = u + kWaves < nnz;
-      if (C::PREFETCH && more)
-        load_frag<D>(fn, K, Vt, kv_base, kv_stride, sm.cur[u + kWaves],
-                     vt_base + (long long)sm.cur[u + kWaves] * D * kChunk, dm.Tkv);
-      const int e0 = sm.off[c], n = sm.cnt[c];
-      const int ntile = (n + 15) / 16;
-      uint4 qv[D / 32];
-      {
-        const bool v0 = col < n;
-        const int rho0 = v0 ? (int)(sm.ent[e0 + col] & 0xFFFFu) : 0;
-        load_q<D>(qv, Q, v0 ? sm.rowid[rho0] : 0, v0);
-      }
-      for (int tl = 0; tl < ntile; ++tl) {
-        const int e = 16 * tl + col;
-        const bool valid = e < n;
-        const uint32_t en = valid ? sm.ent[e0 + e] : 0u;
-        const int rho = (int)(en & 0xFFFFu);
-        const float lw2 = valid ? sm.lw[e0 + e] : 0.f;
-        uint4 qc[D / 32];
-#pragma unroll
-        for (int ds = 0; ds < D / 32; ++ds) qc[ds] = qv[ds];
-        if (tl + 1 < ntile) {  // prefetch the next tile's query fragments
-          const int e1 = e + 16;
-          const bool v1 = e1 < n;
-          const int rho1 = v1 ? (int)(sm.ent[e0 + e1] & 0xFFFFu) : 0;
-          load_q<D>(qv, Q, v1 ? sm.rowid[rho1] : 0, v1);
-        }
-        floatx4 o[D / 16];
-        float z, m2;
-        tile_core<D, false>(f, qc, kChunk, scale2, o, &z, &m2);
-        if (valid) {
-          const float fw = fast_exp2(lw2) / z * fx_scale;
-          int* ar = sm.acc + rho * C::AP;
-#pragma unroll
-          for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) atomicAdd(ar + 16 * db + 4 * gl + q, (int)(o[db][q] * fw));
-        }
-      }
-      if (more) {
-        if (C::PREFETCH) {
-          f = fn;
-        } else {
-          load_frag<D>(f, K, Vt, kv_base, kv_stride, sm.cur[u + kWaves],
-                       vt_base + (long long)sm.cur[u + kWaves] * D * kChunk, dm.Tkv);
-        }
-      }
+      load_frag<D>(f, K, Vt, kv_base, kv_stride, sm.cur[u],
+                   vt_base + (long long)sm.cur[u] * D * kChunk, dm.Tkv);
+      run_chunk<D, 1>(f, sm, sm.cur[u], scale2, fast, fx_scale);
     }
+  }
+  // d = 64: two fragment sets alternate, one consumed while the next chunk's lands
+  // in the other. The prefetches are unconditional (the chunk index is clamped at
+  // the end of the list) so that every path has the same loads in flight and
+  // waiting for the current set never waits for the one behind it.
+  for (int u = w; C::PREFETCH && u < nnz; u += 2 * kWaves) {
+    const int ua = sm.cur[min(u + kWaves, nnz - 1)], ub = sm.cur[min(u + 2 * kWaves, nnz - 1)];
+    load_frag<D>(f2, K, Vt, kv_base, kv_stride, ua, vt_base + (long long)ua * D * kChunk, dm.Tkv);
+    run_chunk<D, 2>(f, sm, sm.cur[u], scale2, fast, fx_scale);
+    if (u + kWaves >= nnz) break;
+    load_frag<D>(f, K, Vt, kv_base, kv_stride, ub, vt_base + (long long)ub * D * kChunk, dm.Tkv);
+    run_chunk<D, 2>(f2, sm, ua, scale2, fast, fx_scale);
   }
   __syncthreads();
 
   // ---- write O (bf16, round to nearest even)
   for (int x = t; x < Rv * (D / 8); x += kThreads) {
     const int rho = x / (D / 8), c8 = x % (D / 8);
-    const int* ar = sm.acc + rho * C::AP + c8 * 8;
+    const int* ar = sm.acc + rho * C::AP;
+    const uint64_t off = (uint64_t)sm.nsel[rho] * ((uint64_t)kMagic * 4294967297ull);
+    // features 8 c8 .. 8 c8 + 7 are columns acc_col(db, g, 0..3) for g = 2 (c8 & 1),
+    // 2 (c8 & 1) + 1 and db = c8 / 2; each pair of columns is one 64-bit word
+    const int db = c8 >> 1, g0 = 2 * (c8 & 1);
     uint32_t ow[4];
 #pragma unroll
-    for (int y = 0; y < 4; ++y)
-      ow[y] = (uint32_t)f32_to_bf16_bits((float)ar[2 * y] * fx_inv) |
-              ((uint32_t)f32_to_bf16_bits((float)ar[2 * y + 1] * fx_inv) << 16);
-    *reinterpret_cast<uint4*>(O + (long long)sm.rowid[rho] * D + c8 * 8) =
-        make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    for (int y = 0; y < 4; ++y) {
+      const int g = g0 + (y >> 1), r = 2 * (y & 1);
+      const int64_t xw = (int64_t)(*reinterpret_cast<const uint64_t*>(ar + acc_col(db, g, r)) - off);
+      const int a = (int)(uint32_t)xw;
+      const int b = (int)((xw - a) >> 32);
+      ow[y] = (uint32_t)f32_to_bf16_bits((float)a * fx_inv) |
+              ((uint32_t)f32_to_bf16_bits((float)b * fx_inv) << 16);
+    }
+    *reinterpret_cast<uint4*>(O + row_of(rho) * D + c8 * 8) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
   }
 }
 
@@ -524,6 +755,9 @@ bool plan(const Dims& dm, Plan* p) {
   r = rq * dm.G;
   const size_t b = smem_bytes<D>(r, dm.K, ncr);
   if (b > limit) return false;
+  // the set-up gives each thread at most one (row, 8 selections) item and four
+  // 16-byte pieces of the query rows
+  if (r * ((dm.K + 7) / 8) > kThreads || r * (D / 8) > 4 * kThreads) return false;
   p->R = r;
   p->Rq = rq;
   p->ncr = ncr;

@@ -106,6 +106,46 @@ def test_attend_stage_with_oracle_selection(name):
     assert_close(host(lt), o["lse_tot"], TOL_F32, "lse_tot")
 
 
+@pytest.mark.parametrize("name", ["bf16_gqa_ragged", "bf16_d128_gqa4"])
+def test_attend_stage_scores_far_from_chunk_mass(name):
+    """Scores that are not HiLS chunk scores (offsets of up to +-100 from the oracle's,
+    so exp(s - score) over a chunk can overflow or vanish) still give the oracle's output:
+    the intra-chunk softmax must not depend on the score being close to the chunk's mass."""
+    w, x = case(name)
+    say(f"[attend stage, shifted scores] {name}")
+    o = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K)
+    rng = np.random.default_rng(7)
+    sc = (o["score"] + rng.uniform(-100.0, 100.0, o["score"].shape)).astype(np.float32)
+    sc[o["idx"] < 0] = -np.inf
+    O_ref, lo_ref, lt_ref = oracle.attend_fuse(x["Q"], x["K"], x["V"], o["idx"], sc, w.S)
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V")}
+    idx = torch.from_numpy(o["idx"]).to(DEV)
+    score = torch.from_numpy(sc).to(DEV)
+    O, lo, lt = hsa.attend_fuse(t["Q"], t["K"], t["V"], idx, score, w.S)
+    torch.cuda.synchronize()
+    assert_close(host(O), O_ref, out_tol(w), "O")
+    assert_close(host(lo), lo_ref, TOL_F32, "lse_own")
+    assert_close(host(lt), lt_ref, TOL_F32, "lse_tot")
+
+
+@pytest.mark.parametrize("name", ["bf16_gqa_ragged", "bf16_d128_gqa4"])
+def test_attend_stage_large_logits(name):
+    """Queries scaled by 32 (exact in bf16) make logits of several hundred, so weights
+    taken without a running maximum would overflow: the kernels must still match."""
+    w, x = case(name)
+    say(f"[attend stage, large logits] {name}")
+    Q = x["Q"] * 32.0
+    o = oracle.forward(Q, x["K"], x["V"], x["Ql"], w.S, w.K)
+    t = {k: dev(v, w.dtype) for k, v in (("Q", Q), ("K", x["K"]), ("V", x["V"]))}
+    idx = torch.from_numpy(o["idx"]).to(DEV)
+    score = torch.from_numpy(o["score"].astype(np.float32)).to(DEV)
+    O, lo, lt = hsa.attend_fuse(t["Q"], t["K"], t["V"], idx, score, w.S)
+    torch.cuda.synchronize()
+    assert_close(host(O), o["O"], out_tol(w), "O")
+    assert_close(host(lo), o["lse_own"], TOL_F32, "lse_own")
+    assert_close(host(lt), o["lse_tot"], TOL_F32, "lse_tot")
+
+
 @pytest.mark.parametrize("name", ["bf16_gqa_ragged", "f32_kmax"])
 def test_decode_rows_equal_prefill_rows(name):
     """A query scored alone (split path) selects what the prefill pass selected, bit for bit,
