@@ -18,7 +18,7 @@ hils_status resolve(const hils_dims* in, hils::Dims* out) {
     return HILS_ERR_INVALID_ARG;
   if (d.dtype != HILS_F32 && d.dtype != HILS_BF16) return HILS_ERR_INVALID_ARG;
   if (d.S < 1 || d.d < 1 || d.K < 1) return HILS_ERR_INVALID_ARG;
-  if (d.S != hils::kChunk || (d.d != 64 && d.d != 128) || d.K > 64) return HILS_ERR_UNSUPPORTED;
+  if (d.S != hils::kChunk || (d.d != 64 && d.d != 128) || d.K > hils::kMaxSel) return HILS_ERR_UNSUPPORTED;
   if (d.q_pos0 < 0 || d.q_pos0 + d.Tq > d.Tkv) return HILS_ERR_INVALID_ARG;
   if (d.Tkv_cap < 0 || d.NC_cap < 0) return HILS_ERR_INVALID_ARG;
   const int Tcap = d.Tkv_cap ? d.Tkv_cap : d.Tkv;

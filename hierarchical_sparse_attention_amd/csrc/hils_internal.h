@@ -8,6 +8,7 @@ namespace hils {
 
 constexpr int kWave = 64;   // CDNA wavefront width
 constexpr int kChunk = 64;  // supported chunk size S (one key per lane)
+constexpr int kMaxSel = 64;  // largest supported top-K
 
 // Dimensions after validation and defaulting (see hils_dims in hils.h).
 struct Dims {
@@ -99,6 +100,135 @@ __device__ __forceinline__ float chunk_score(const float* q, const float* kbar, 
   return fmaf(acc, scale, ent);
 }
 
+// Top-K order key: (score descending, chunk id ascending). Branch-free, so rank
+// loops keep their loads in flight.
+__device__ __forceinline__ bool topk_before(float sa, int ca, float sb, int cb) {
+  return (sa > sb) | ((sa == sb) & (ca < cb));
+}
+
+// Final top-K of row r from nsplit local lists (split sp covers candidates
+// [sp * split_size, (sp + 1) * split_size) and holds min(K, its candidates)
+// entries, best first, at ws[(r * nsplit + sp) * K ...]). The global top-K is a
+// subset of the union of the local ones, so ranking the union is exact. Every
+// thread of the workgroup takes part; es/ec (16-byte aligned) hold nsplit * K
+// entries rounded up to a multiple of 32, sel_s/sel_c K. Writes idx ascending by chunk id (padding -1) and score (padding -inf).
+__device__ __forceinline__ void topk_merge_row(const Dims& dm, long long r, int n,
+                                               const float* ws_s, const int* ws_i, int nsplit,
+                                               int split_size, int32_t* idx, float* score,
+                                               float* es, int* ec, float* sel_s, int* sel_c) {
+  const int t = threadIdx.x, nt = blockDim.x, K = dm.K;
+  const int E = nsplit * K, E4 = (E + 31) & ~31;  // es/ec padded to a multiple of 32
+  for (int x = t; x < E4; x += nt) {
+    const int sp = x / K, k = x % K;
+    const int nv = x < E ? min(K, max(0, min(split_size, n - sp * split_size))) : 0;
+    const long long o = r * E + min(x, E - 1);  // read unconditionally (in bounds), so
+    const float sv = ws_s[o];                   // both loads are in flight together
+    const int cv = ws_i[o];
+    const bool v = k < nv;
+    es[x] = v ? sv : -INFINITY;
+    ec[x] = v ? cv : 0x7fffffff;
+  }
+  __syncthreads();
+  const int cnt = min(K, n);
+  const float4* es4 = reinterpret_cast<const float4*>(es);
+  const int4* ec4 = reinterpret_cast<const int4*>(ec);
+  for (int x = t; x < E; x += nt) {
+    const float s = es[x];
+    const int c = ec[x];
+    int rank = 0;
+    for (int y0 = 0; y0 < E4 / 4; y0 += 8) {  // 16 LDS reads in flight per step
+      float4 a[8];
+      int4 ca[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        a[j] = es4[y0 + j];
+        ca[j] = ec4[y0 + j];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        rank += topk_before(a[j].x, ca[j].x, s, c) + topk_before(a[j].y, ca[j].y, s, c) +
+                topk_before(a[j].z, ca[j].z, s, c) + topk_before(a[j].w, ca[j].w, s, c);
+    }
+    if (c != 0x7fffffff && rank < cnt) {
+      sel_s[rank] = s;
+      sel_c[rank] = c;
+    }
+  }
+  __syncthreads();
+  const long long o = r * K;
+  for (int k = t; k < K; k += nt) {
+    if (k < cnt) {
+      const int c = sel_c[k];
+      int pos = 0;
+      for (int k2 = 0; k2 < cnt; ++k2) pos += sel_c[k2] < c;
+      idx[o + pos] = c;
+      score[o + pos] = sel_s[k];
+    } else {
+      idx[o + k] = -1;
+      score[o + k] = -INFINITY;
+    }
+  }
+}
+
+// Wave-level top-K merge of at most 64 sorted local lists (lane l holds list l in
+// registers, best first): K rounds of a wave-wide maximum over the list heads,
+// the winning list advancing by one. Keys are 64-bit, (ordered score bits,
+// ~chunk id), so larger is better and ties go to the lower chunk id. Lane k ends
+// with the round-k winner in (*wh, *wl); returns the number of rounds with a
+// winner. KM >= K.
+__device__ __forceinline__ uint32_t order_bits(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_float(uint32_t h) {
+  return __uint_as_float((h >> 31) ? (h & 0x7FFFFFFFu) : ~h);
+}
+template <int CTRL>
+__device__ __forceinline__ void key_max_dpp(uint32_t& h, uint32_t& l) {
+  const uint32_t ph = (uint32_t)__builtin_amdgcn_mov_dpp((int)h, CTRL, 0xF, 0xF, true);
+  const uint32_t pl = (uint32_t)__builtin_amdgcn_mov_dpp((int)l, CTRL, 0xF, 0xF, true);
+  const bool gt = (ph > h) | ((ph == h) & (pl > l));
+  h = gt ? ph : h;
+  l = gt ? pl : l;
+}
+__device__ __forceinline__ void key_max_pair(uint32_t& h, uint32_t& l, uint32_t h0, uint32_t l0,
+                                             uint32_t h1, uint32_t l1) {
+  const bool gt = (h1 > h0) | ((h1 == h0) & (l1 > l0));
+  h = gt ? h1 : h0;
+  l = gt ? l1 : l0;
+}
+__device__ __forceinline__ void key_wave_max(uint32_t& h, uint32_t& l) {
+  key_max_dpp<0xB1>(h, l);   // quad_perm [1,0,3,2]
+  key_max_dpp<0x4E>(h, l);   // quad_perm [2,3,0,1]
+  key_max_dpp<0x141>(h, l);  // row_half_mirror
+  key_max_dpp<0x140>(h, l);  // row_mirror
+  auto a = __builtin_amdgcn_permlane16_swap(h, h, false, false);
+  auto b = __builtin_amdgcn_permlane16_swap(l, l, false, false);
+  key_max_pair(h, l, a[0], b[0], a[1], b[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(h, h, false, false);
+  auto d = __builtin_amdgcn_permlane32_swap(l, l, false, false);
+  key_max_pair(h, l, c[0], d[0], c[1], d[1]);
+}
+template <int KM>
+__device__ __forceinline__ int wave_merge_lists(uint32_t (&lh)[KM], uint32_t (&ll)[KM], int K,
+                                                uint32_t* wh, uint32_t* wl) {
+  const int lane = threadIdx.x & 63;
+  int found = 0;
+  for (int k = 0; k < K; ++k) {
+    uint32_t h = lh[0], l = ll[0];
+    key_wave_max(h, l);
+    if (h == 0 && l == 0) break;  // every list exhausted (wave-uniform)
+    if (lane == k) *wh = h, *wl = l;
+    if (lh[0] == h && ll[0] == l) {  // the winning list (keys are unique) drops its head
+#pragma unroll
+      for (int j = 0; j + 1 < KM; ++j) lh[j] = lh[j + 1], ll[j] = ll[j + 1];
+      lh[KM - 1] = 0, ll[KM - 1] = 0;
+    }
+    ++found;
+  }
+  return found;
+}
+
 // ---------------------------------------------------------------- launches
 hipError_t launch_summarize(const Dims& dm, const void* K, const void* Ql, int c_begin, int c_end,
                             float* ksum, float* ent, float* lse_l, hipStream_t st);
@@ -108,6 +238,11 @@ size_t score_mfma_prefill_ws_bytes(const Dims& dm);
 hipError_t launch_score_mfma_prefill(const Dims& dm, const void* Q, const float* ksum,
                                      const float* ent, int32_t* idx, float* score, void* ws,
                                      hipStream_t st);
+constexpr int kSplitMfma = 128;  // candidates per workgroup of the bf16 decode scoring
+constexpr int kRowCand = 8192;   // most candidates the one-workgroup-per-row scoring handles
+// One workgroup per query row (bf16, few rows); returns false when it does not apply.
+bool score_row_mfma_try(const Dims& dm, const void* Q, const float* ksum, const float* ent,
+                        int32_t* idx, float* score, hipStream_t st, hipError_t* err);
 hipError_t launch_score_mfma_split(const Dims& dm, const void* Q, const float* ksum,
                                    const float* ent, float* ws_s, int* ws_i, int nsplit,
                                    hipStream_t st);

@@ -110,11 +110,173 @@ __global__ __launch_bounds__(256) void k_attend_rows(Dims dm, const void* __rest
 }
 
 // ---------------------------------------------------------------- decode
-// Few query rows (decode): the work is split over (row, slot) pairs so a single
-// query still spreads over the chip. Slot k < K attends selected chunk idx[k],
-// slot K the causal own chunk. Each pair writes its normalised output and its
-// log-mass to the workspace; a combine kernel then applies the inter-chunk
-// softmax per row in a fixed slot order.
+// Few query rows (decode): one wavefront per (slot, row): slot k < K attends
+// selected chunk idx[k], slot K the causal own chunk. Each writes its normalised
+// output and log-mass to the workspace; a combine kernel then applies the
+// inter-chunk softmax per row in a fixed slot order.
+// bf16 key and value rows are read with 16-byte loads in one layout: the wave's
+// lanes form NG = 64 / LP groups of LP = d / 8 lanes; group q holds rows
+// NV q .. NV q + NV - 1 (NV = d / 8) and lane l % LP of the group the features
+// 8 (l % LP) .. + 8 of those rows, so each load instruction reads whole rows.
+// Logits: per-lane partial dots summed over the group's lanes; softmax across
+// groups; values: per-lane partial outputs summed across groups. Cross-lane
+// steps use DPP and permlane swaps.
+template <int D>
+struct DecodeCfg {
+  static constexpr int LP = D / 8;                // lanes per row
+  static constexpr int NG = kWave / LP;           // row groups
+  static constexpr int NV = kChunk / NG;          // rows per group (16-byte pieces per lane)
+};
+
+// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror, row_ror:8
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140,
+              kDppRor8 = 0x128;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// sum over the LP lanes of a group (LP = 8 or 16)
+template <int LP>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  if (LP == 16) v += dpp<kDppMirror>(v);
+  return v;
+}
+__device__ __forceinline__ float swap16_32(float x, bool mx) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = mx ? fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])) : __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return mx ? fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])) : __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// max / sum across the NG groups (lanes that differ in l / LP)
+template <int LP>
+__device__ __forceinline__ float cross_max(float v) {
+  if (LP == 8) v = fmaxf(v, dpp<kDppRor8>(v));
+  return swap16_32(v, true);
+}
+template <int LP>
+__device__ __forceinline__ float cross_sum(float v) {
+  if (LP == 8) v += dpp<kDppRor8>(v);
+  return swap16_32(v, false);
+}
+
+template <int D>
+struct SlotRegs {
+  uint4 k[DecodeCfg<D>::NV];
+  uint4 v[DecodeCfg<D>::NV];
+};
+
+template <int D>
+__device__ __forceinline__ void slot_load(SlotRegs<D>& x, const uint16_t* K, const uint16_t* V,
+                                          long long kv_base, long long kv_stride, long long key0,
+                                          int nk) {
+  using C = DecodeCfg<D>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j0 = C::NV * (lane / C::LP), f0 = 8 * (lane % C::LP);
+#pragma unroll
+  for (int m = 0; m < C::NV; ++m) {
+    const long long off = kv_base + (key0 + min(j0 + m, nk - 1)) * kv_stride + f0;
+    x.k[m] = *reinterpret_cast<const uint4*>(K + off);
+    x.v[m] = *reinterpret_cast<const uint4*>(V + off);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void slot_compute(const SlotRegs<D>& x, const Dims& dm,
+                                             const uint16_t* qs, int nk, float* o_out,
+                                             float* l_out) {
+  using C = DecodeCfg<D>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j0 = C::NV * (lane / C::LP), f0 = 8 * (lane % C::LP);
+  const uint4 qv = *reinterpret_cast<const uint4*>(qs + f0);  // this lane's 8 query features
+  const uint32_t qa[4] = {qv.x, qv.y, qv.z, qv.w};
+  float s[C::NV];
+#pragma unroll
+  for (int m = 0; m < C::NV; ++m) {
+    const uint32_t ka[4] = {x.k[m].x, x.k[m].y, x.k[m].z, x.k[m].w};
+    float part = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      part = fmaf(__uint_as_float(qa[k] << 16), __uint_as_float(ka[k] << 16), part);
+      part = fmaf(__uint_as_float(qa[k] & 0xFFFF0000u), __uint_as_float(ka[k] & 0xFFFF0000u), part);
+    }
+    s[m] = group_sum<C::LP>(part);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < C::NV; ++m) {
+    s[m] = j0 + m < nk ? s[m] * dm.scale : -INFINITY;
+    mx = fmaxf(mx, s[m]);
+  }
+  mx = cross_max<C::LP>(mx);
+  float z = 0.0f;
+#pragma unroll
+  for (int m = 0; m < C::NV; ++m) {
+    s[m] = expf(s[m] - mx);  // 0 for masked keys
+    z += s[m];
+  }
+  z = cross_sum<C::LP>(z);
+  const float L = mx + logf(z);
+  const float iz = 1.0f / z;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int m = 0; m < C::NV; ++m) {
+    const float pj = s[m] * iz;
+    const uint32_t va[4] = {x.v[m].x, x.v[m].y, x.v[m].z, x.v[m].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[2 * k] = fmaf(pj, __uint_as_float(va[k] << 16), acc[2 * k]);
+      acc[2 * k + 1] = fmaf(pj, __uint_as_float(va[k] & 0xFFFF0000u), acc[2 * k + 1]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = cross_sum<C::LP>(acc[e]);
+  if (lane < C::LP) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o_out[f0 + e] = acc[e];
+  }
+  if (lane == 0) *l_out = L;
+}
+
+// float32 slot: lane j owns key j for the logits, lane e features e (+ 64 x).
+template <int D>
+__device__ __forceinline__ void decode_slot_f32(const Dims& dm, const float* qs, const float* K,
+                                                const float* V, long long kv_base, long long key0,
+                                                int nk, float* o_out, float* l_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const long long kv_stride = (long long)dm.Hkv * D;
+  const bool valid = lane < nk;
+  float kr[D];
+  load_row<false, D>(K, kv_base + (key0 + min(lane, nk - 1)) * kv_stride, kr);
+  float dot = 0.0f;
+#pragma unroll
+  for (int e = 0; e < D; ++e) dot = fmaf(qs[e], kr[e], dot);
+  const float s = valid ? dot * dm.scale : -INFINITY;
+  const float m = wave_max(s);
+  const float L = m + logf(wave_sum(valid ? expf(s - m) : 0.0f));
+  const float p = valid ? expf(s - L) : 0.0f;
+  float acc[D / kWave];
+#pragma unroll
+  for (int x = 0; x < D / kWave; ++x) acc[x] = 0.0f;
+  for (int j = 0; j < nk; ++j) {
+    const float pj = lane_bcast(p, j);
+    const long long row = kv_base + (key0 + j) * kv_stride;
+#pragma unroll
+    for (int x = 0; x < D / kWave; ++x) acc[x] = fmaf(pj, V[row + lane + kWave * x], acc[x]);
+  }
+#pragma unroll
+  for (int x = 0; x < D / kWave; ++x) o_out[lane + kWave * x] = acc[x];
+  if (lane == 0) *l_out = L;
+}
+
+// Slot kernel: grid (K + 1, rows), one wavefront per (slot, row); writes the
+// slot's normalised output and log-mass (-inf for padding) to the workspace.
+// Spreading the slots over workgroups keeps many chunk reads in flight at once.
 template <bool BF16, int D>
 __global__ __launch_bounds__(64) void k_decode_partial(Dims dm, const void* __restrict__ Q,
                                                        const void* __restrict__ K,
@@ -122,18 +284,28 @@ __global__ __launch_bounds__(64) void k_decode_partial(Dims dm, const void* __re
                                                        const int32_t* __restrict__ idx,
                                                        float* __restrict__ part_o,
                                                        float* __restrict__ part_l) {
+  __shared__ __align__(16) uint16_t qh[D];
+  __shared__ __align__(16) float qf[D];
   const int slot = blockIdx.x, lane = threadIdx.x;
   const long long r = blockIdx.y;
   const int h = (int)(r % dm.H), i = (int)((r / dm.H) % dm.Tq);
   const int b = (int)(r / ((long long)dm.H * dm.Tq));
   const int g = h / dm.G;
   const long long pos = dm.q_pos0 + i, own = pos / dm.S;
-  const long long po = (r * (dm.K + 1) + slot);
+  const long long po = r * (dm.K + 1) + slot;
+  const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
+  const long long kv_stride = (long long)dm.Hkv * D;
+  // query and selection read together (unconditionally, indices in bounds)
+  const int c = idx[r * dm.K + min(slot, dm.K - 1)];
+#pragma unroll
+  for (int x = 0; x < D / kWave; ++x) {
+    if (BF16) qh[lane + kWave * x] = reinterpret_cast<const uint16_t*>(Q)[r * D + lane + kWave * x];
+    else qf[lane + kWave * x] = reinterpret_cast<const float*>(Q)[r * D + lane + kWave * x];
+  }
   long long key0;
   int nk;
   if (slot < dm.K) {
-    const int c = idx[r * dm.K + slot];
-    if (c < 0 || c >= own) {  // padding slot
+    if (c < 0 || c >= own) {  // padding slot: no mass
       if (lane == 0) part_l[po] = -INFINITY;
       return;
     }
@@ -143,45 +315,22 @@ __global__ __launch_bounds__(64) void k_decode_partial(Dims dm, const void* __re
     key0 = own * dm.S;
     nk = (int)(pos - key0) + 1;
   }
-  const long long kv_stride = (long long)dm.Hkv * D;
-  const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
-  // every load is issued before the softmax: q, the lane's key row, and for
-  // o[e] = sum_j p_j V[j][e] (lane = feature) all 64 value rows (rows beyond nk
-  // are clamped in bounds and carry p_j = 0)
-  float q[D];
-  load_row<BF16, D>(Q, r * D, q);
-  const bool valid = lane < nk;
-  float kr[D];
-  load_row<BF16, D>(K, kv_base + (key0 + min(lane, nk - 1)) * kv_stride, kr);
-  float vv[kChunk][D / kWave];
-#pragma unroll
-  for (int j = 0; j < kChunk; ++j) {
-    const long long row = key0 + min(j, nk - 1);
-#pragma unroll
-    for (int x = 0; x < D / kWave; ++x)
-      vv[j][x] = load_elem<BF16>(V, kv_base + row * kv_stride + lane + kWave * x);
+  if (BF16) {
+    SlotRegs<D> rg;
+    slot_load<D>(rg, reinterpret_cast<const uint16_t*>(K), reinterpret_cast<const uint16_t*>(V),
+                 kv_base, kv_stride, key0, nk);
+    __syncthreads();
+    slot_compute<D>(rg, dm, qh, nk, part_o + po * D, part_l + po);
+  } else {
+    __syncthreads();
+    decode_slot_f32<D>(dm, qf, reinterpret_cast<const float*>(K), reinterpret_cast<const float*>(V),
+                       kv_base, key0, nk, part_o + po * D, part_l + po);
   }
-  float dot = 0.0f;
-#pragma unroll
-  for (int e = 0; e < D; ++e) dot = fmaf(q[e], kr[e], dot);
-  const float s = valid ? dot * dm.scale : -INFINITY;
-  const float m = wave_max(s);
-  const float L = m + logf(wave_sum(valid ? expf(s - m) : 0.0f));
-  const float p = valid ? expf(s - L) : 0.0f;
-  float acc[D / kWave];
-#pragma unroll
-  for (int x = 0; x < D / kWave; ++x) acc[x] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kChunk; ++j) {
-    const float pj = lane_bcast(p, j);
-#pragma unroll
-    for (int x = 0; x < D / kWave; ++x) acc[x] = fmaf(pj, vv[j][x], acc[x]);
-  }
-#pragma unroll
-  for (int x = 0; x < D / kWave; ++x) part_o[po * D + lane + kWave * x] = acc[x];
-  if (lane == 0) part_l[po] = L;
 }
 
+// Combine kernel: one wavefront per row applies the inter-chunk softmax to the
+// slots in a fixed order (selected slots by their chunk score, the own slot by
+// its exact log-mass).
 template <bool BF16, int D>
 __global__ __launch_bounds__(64) void k_decode_combine(Dims dm, const float* __restrict__ score,
                                                        const float* __restrict__ part_o,
@@ -189,40 +338,50 @@ __global__ __launch_bounds__(64) void k_decode_combine(Dims dm, const float* __r
                                                        void* __restrict__ O,
                                                        float* __restrict__ lse_own,
                                                        float* __restrict__ lse_tot) {
+  constexpr int X = D / kWave;
+  constexpr int KF = 16;  // slots whose partials are read in the first round trip
   const long long r = blockIdx.x;
   const int lane = threadIdx.x, Ks = dm.K;
   const long long pb = r * (Ks + 1);
-  // logits: selected slots use their chunk score, the own slot its exact log-mass
+  const int kl = min(lane, Ks - 1);
+  // every read is issued before any is used; rows of padding slots were not
+  // written and are read only to keep the loads unconditional (weight 0)
   const float l_own = part_l[pb + Ks];
-  float lg = -INFINITY;
-  if (lane < Ks && part_l[pb + lane] != -INFINITY) lg = score[r * Ks + lane];
+  const float pl = part_l[pb + kl];
+  const float sc = score[r * Ks + kl];
+  float po_own[X], pv[KF][X];
+#pragma unroll
+  for (int x = 0; x < X; ++x) po_own[x] = part_o[(pb + Ks) * D + lane + kWave * x];
+#pragma unroll
+  for (int k = 0; k < KF; ++k)
+#pragma unroll
+    for (int x = 0; x < X; ++x) pv[k][x] = part_o[(pb + min(k, Ks)) * D + lane + kWave * x];
+  const float lg = (lane < Ks && pl != -INFINITY) ? sc : -INFINITY;
   const float mx = fmaxf(wave_max(lg), l_own);
   const float Lambda = mx + logf(wave_sum(lane < Ks ? expf(lg - mx) : 0.0f) + expf(l_own - mx));
   const float a = lane < Ks ? expf(lg - Lambda) : 0.0f;
   const float a_own = expf(l_own - Lambda);
-  float acc[D / kWave];
+  float acc[X];
 #pragma unroll
-  for (int x = 0; x < D / kWave; ++x) acc[x] = 0.0f;
-  for (int k0 = 0; k0 < Ks; k0 += 8) {
-    float pv[8][D / kWave];
+  for (int x = 0; x < X; ++x) acc[x] = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
+  for (int k = 0; k < KF; ++k) {
+    const float ak = k < Ks ? lane_bcast(a, k) : 0.0f;
+    if (ak != 0.0f) {  // wave-uniform; padding and absent slots are skipped
 #pragma unroll
-      for (int x = 0; x < D / kWave; ++x)
-        pv[kk][x] = k0 + kk < Ks ? part_o[(pb + k0 + kk) * D + lane + kWave * x] : 0.0f;
+      for (int x = 0; x < X; ++x) acc[x] = fmaf(ak, pv[k][x], acc[x]);
+    }
+  }
+  for (int k = KF; k < Ks; ++k) {  // K > 16
+    const float ak = lane_bcast(a, k);
+    if (ak != 0.0f) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      // padding slots wrote no partial: their (unwritten) values are never used
-      const float ak = k0 + kk < Ks ? lane_bcast(a, k0 + kk) : 0.0f;
-      if (ak != 0.0f) {  // wave-uniform
-#pragma unroll
-        for (int x = 0; x < D / kWave; ++x) acc[x] = fmaf(ak, pv[kk][x], acc[x]);
-      }
+      for (int x = 0; x < X; ++x) acc[x] = fmaf(ak, part_o[(pb + k) * D + lane + kWave * x], acc[x]);
     }
   }
 #pragma unroll
-  for (int x = 0; x < D / kWave; ++x) {
-    acc[x] = fmaf(a_own, part_o[(pb + Ks) * D + lane + kWave * x], acc[x]);
+  for (int x = 0; x < X; ++x) {
+    acc[x] = fmaf(a_own, po_own[x], acc[x]);
     store_elem<BF16>(O, r * D + lane + kWave * x, acc[x]);
   }
   if (lane == 0) {

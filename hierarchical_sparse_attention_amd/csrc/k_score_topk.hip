@@ -21,15 +21,13 @@ namespace hils {
 namespace {
 
 constexpr int kBlockChunks = 32;  // summaries staged per LDS block (rows path)
-constexpr int kSplit = 128;       // candidates per workgroup (split path)
+constexpr int kSplit = kSplitMfma;  // candidates per workgroup (split path, both dtypes)
 constexpr int kMergeMax = 4096;   // entries the merge kernel ranks in LDS
 
 __host__ __device__ inline int rows_per_wg(int K) { return K <= 16 ? 256 : (K <= 32 ? 128 : 64); }
 
-// key order: a before b
-// (branch-free: both operands are always read, so rank loops keep loads in flight)
 __device__ __forceinline__ bool before(float sa, int ca, float sb, int cb) {
-  return (sa > sb) | ((sa == sb) & (ca < cb));
+  return topk_before(sa, ca, sb, cb);
 }
 
 template <bool BF16, int D>
@@ -141,53 +139,57 @@ __global__ __launch_bounds__(kSplit) void k_score_split(Dims dm, const void* __r
 }
 
 // Split path, stage 2: one workgroup per row ranks the union of local lists.
-// Split sp holds min(K, candidates in the split) entries at slots sp*K ...; every
-// slot is loaded at once (invalid slots become (-inf, INT_MAX)) and ranked.
 __global__ __launch_bounds__(1024) void k_topk_merge(Dims dm, const float* __restrict__ ws_s,
                                                     const int* __restrict__ ws_i, int nsplit,
                                                     int32_t* __restrict__ idx,
                                                     float* __restrict__ score) {
-  __shared__ float es[kMergeMax];
-  __shared__ int ec[kMergeMax];
+  __shared__ __align__(16) float es[kMergeMax];
+  __shared__ __align__(16) int ec[kMergeMax];
   __shared__ float sel_s[64];
   __shared__ int sel_c[64];
-  const int r = blockIdx.x, t = threadIdx.x;
+  const int r = blockIdx.x;
   const int i = (r / dm.H) % dm.Tq;
   const int n = (int)((dm.q_pos0 + i) / dm.S);
-  const int K = dm.K;
-  const int E = nsplit * K;
-  for (int x = t; x < E; x += blockDim.x) {
-    const int sp = x / K, k = x % K;
-    const int nv = min(K, max(0, min(kSplit, n - sp * kSplit)));
-    const long long o = (long long)r * E + x;
-    const bool v = k < nv;
-    es[x] = v ? ws_s[o] : -INFINITY;
-    ec[x] = v ? ws_i[o] : 0x7fffffff;
+  topk_merge_row(dm, r, n, ws_s, ws_i, nsplit, kSplit, idx, score, es, ec, sel_s, sel_c);
+}
+
+// Split path, stage 2 for at most 64 splits: one wavefront per row merges the
+// sorted local lists held in registers (lane = split).
+template <int KM>
+__global__ __launch_bounds__(64) void k_topk_merge_wave(Dims dm, const float* __restrict__ ws_s,
+                                                        const int* __restrict__ ws_i, int nsplit,
+                                                        int32_t* __restrict__ idx,
+                                                        float* __restrict__ score) {
+  __shared__ int sel_c[64];
+  const int r = blockIdx.x, lane = threadIdx.x, K = dm.K;
+  const int i = (r / dm.H) % dm.Tq;
+  const int n = (int)((dm.q_pos0 + i) / dm.S);
+  const int nv = lane < nsplit ? min(K, max(0, min(kSplit, n - lane * kSplit))) : 0;
+  const long long base = ((long long)r * nsplit + min(lane, nsplit - 1)) * K;
+  uint32_t lh[KM], ll[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {  // all loads in flight together (in bounds, masked after)
+    const int jj = min(j, K - 1);
+    const float sv = ws_s[base + jj];
+    const int cv = ws_i[base + jj];
+    const bool v = j < nv;
+    lh[j] = v ? order_bits(sv) : 0u;
+    ll[j] = v ? ~(uint32_t)cv : 0u;
   }
-  __syncthreads();
-  const int cnt = min(K, n);
-  for (int x = t; x < E; x += blockDim.x) {
-    const float s = es[x];
-    const int c = ec[x];
-    int rank = 0;
-#pragma unroll 8
-    for (int y = 0; y < E; ++y) rank += before(es[y], ec[y], s, c);
-    if (c != 0x7fffffff && rank < cnt) {
-      sel_s[rank] = s;
-      sel_c[rank] = c;
-    }
-  }
-  __syncthreads();
+  uint32_t wh = 0, wl = 0;
+  const int cnt = wave_merge_lists<KM>(lh, ll, K, &wh, &wl);
+  const int c = (int)~wl;
+  if (lane < cnt) sel_c[lane] = c;
+  __builtin_amdgcn_wave_barrier();
   const long long o = (long long)r * K;
-  if (t < cnt) {
-    const int c = sel_c[t];
+  if (lane < cnt) {
     int pos = 0;
-    for (int k = 0; k < cnt; ++k) pos += sel_c[k] < c;
+    for (int k2 = 0; k2 < cnt; ++k2) pos += sel_c[k2] < c;
     idx[o + pos] = c;
-    score[o + pos] = sel_s[t];
-  } else if (t < K) {
-    idx[o + t] = -1;
-    score[o + t] = -INFINITY;
+    score[o + pos] = order_float(wh);
+  } else if (lane < K) {
+    idx[o + lane] = -1;
+    score[o + lane] = -INFINITY;
   }
 }
 
@@ -208,6 +210,8 @@ template <bool BF16, int D>
 hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const float* ent,
                     int32_t* idx, float* score, void* ws, hipStream_t st) {
   if (use_split(dm)) {
+    hipError_t err = hipSuccess;
+    if (score_row_mfma_try(dm, Q, ksum, ent, idx, score, st, &err)) return err;
     const int ns = split_count(dm);
     const long long rows = (long long)dm.B * dm.Tq * dm.H;
     float* ws_s = reinterpret_cast<float*>(ws);
@@ -221,6 +225,15 @@ hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const floa
       e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
+    if (ns <= 64) {  // one wavefront per row, lists in registers
+      if (dm.K <= 16)
+        hipLaunchKernelGGL(k_topk_merge_wave<16>, dim3(rows), dim3(64), 0, st, dm, ws_s, ws_i, ns,
+                           idx, score);
+      else
+        hipLaunchKernelGGL(k_topk_merge_wave<64>, dim3(rows), dim3(64), 0, st, dm, ws_s, ws_i, ns,
+                           idx, score);
+      return hipGetLastError();
+    }
     const int E = ns * dm.K;  // one thread per entry when they fit in a workgroup
     const int nt = E <= 1024 ? ((E + 63) / 64) * 64 : 1024;
     hipLaunchKernelGGL(k_topk_merge, dim3(rows), dim3(max(nt, 64)), 0, st, dm, ws_s, ws_i, ns,

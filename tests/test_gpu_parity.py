@@ -146,7 +146,7 @@ def test_attend_stage_large_logits(name):
     assert_close(host(lt), o["lse_tot"], TOL_F32, "lse_tot")
 
 
-@pytest.mark.parametrize("name", ["bf16_gqa_ragged", "f32_kmax"])
+@pytest.mark.parametrize("name", ["bf16_gqa_ragged", "bf16_d128_gqa4", "f32_kmax"])
 def test_decode_rows_equal_prefill_rows(name):
     """A query scored alone (split path) selects what the prefill pass selected, bit for bit,
     and attends to the same output (decode = prefill row)."""
