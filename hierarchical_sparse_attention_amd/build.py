@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libhils.so")
 ARCH = "gfx950"
 
 SOURCES = ["hils_api.cpp", "k_summarize.hip", "k_score_topk.hip", "k_score_mfma.hip", "k_attend_fuse.hip",
-           "k_attend_mfma.hip", "k_backward.hip"]
+           "k_attend_mfma.hip", "k_backward.hip", "k_backward_mfma.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -259,6 +259,14 @@ hipError_t launch_attend_fuse(const Dims& dm, const void* Q, const void* K, cons
                               float* lse_tot, void* ws, hipStream_t st);
 
 size_t backward_ws_bytes(const Dims& dm);
+size_t backward_mfma_ws_bytes(const Dims& dm);
+// bf16, d = 64 prefill backward on matrix cores; returns false when it does not apply.
+bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void* V,
+                       const void* Ql, const float* ksum, const float* ent, const float* lse_l,
+                       const int32_t* idx, const float* score, const float* lse_tot,
+                       const void* dO, void* dQ, void* dK, void* dV, void* dQl, float* ws_dsh,
+                       float* ws_D, const uint32_t* bm, int words, void* ws_mfma, hipStream_t st,
+                       hipError_t* err);
 hipError_t launch_backward(const Dims& dm, const void* Q, const void* K, const void* V,
                            const void* Ql, const float* ksum, const float* ent, const float* lse_l,
                            const int32_t* idx, const float* score, const float* lse_tot,

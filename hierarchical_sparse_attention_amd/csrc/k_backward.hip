@@ -43,7 +43,7 @@ __device__ __forceinline__ float dot_bcast(const float* xs, const float* row) {
 }
 
 struct WsLayout {
-  size_t dsh, dr, bitmap, total;
+  size_t dsh, dr, bitmap, mfma, total;
   int words;  // bitmap words per (b, h, c)
 };
 
@@ -56,7 +56,8 @@ WsLayout ws_layout(const Dims& dm) {
   L.dr = up(rows * dm.K * sizeof(float));
   L.bitmap = L.dr + up(rows * sizeof(float));
   const int NC = dm.Tkv / dm.S;
-  L.total = L.bitmap + up((size_t)dm.B * dm.H * NC * L.words * sizeof(uint32_t));
+  L.mfma = L.bitmap + up((size_t)dm.B * dm.H * NC * L.words * sizeof(uint32_t));
+  L.total = L.mfma + backward_mfma_ws_bytes(dm);
   return L;
 }
 
@@ -398,11 +399,15 @@ hipError_t launch_t(const Dims& dm, const void* Q, const void* K, const void* V,
   float* Dr = reinterpret_cast<float*>(base + L.dr);
   uint32_t* bm = reinterpret_cast<uint32_t*>(base + L.bitmap);
   const int NC = dm.Tkv / dm.S;
-  hipLaunchKernelGGL((k_bwd_rows<BF16, D>), dim3((dm.Tq + 3) / 4, dm.H, dm.B), dim3(256), 0, st,
-                     dm, Q, K, V, ksum, idx, score, lse_tot, dO, dQ, dsh, Dr);
   const long long nbm = (long long)dm.B * dm.H * NC * L.words;
   hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, bm, nbm);
   hipLaunchKernelGGL(k_sel_bitmap, dim3(1024), dim3(256), 0, st, dm, idx, bm, L.words);
+  hipError_t err = hipSuccess;
+  if (backward_mfma_try(dm, Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, dO, dQ, dK, dV,
+                        dQl, dsh, Dr, bm, L.words, base + L.mfma, st, &err))
+    return err;
+  hipLaunchKernelGGL((k_bwd_rows<BF16, D>), dim3((dm.Tq + 3) / 4, dm.H, dm.B), dim3(256), 0, st,
+                     dm, Q, K, V, ksum, idx, score, lse_tot, dO, dQ, dsh, Dr);
   hipLaunchKernelGGL((k_bwd_kv<BF16, D>), dim3(NC, dm.Hkv, dm.B), dim3(256), 0, st, dm, Q, K, V,
                      Ql, ksum, ent, lse_l, idx, score, lse_tot, dO, dsh, Dr, bm, L.words, dK, dV,
                      dQl);

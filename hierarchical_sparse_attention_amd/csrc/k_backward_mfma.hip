@@ -1,0 +1,1029 @@
+// Training backward of HiLS attention on bf16 MFMA (gfx950), d = 64.
+//
+// Same gradients as the rows/chunk kernels of k_backward.hip (note §5.3: the
+// chunk score enters the forward weights, so the loss gradient reaches the
+// query, the summary key, the entropy bias and through the landmark softmax
+// (note §5.1) the landmark query and the keys). Per row i with fused weights
+// alpha_c = exp(s^_c - Lambda), intra-chunk softmax P, u_j = dO.v_j,
+// r_c = sum_j P_j u_j and D = sum_c alpha_c r_c + sum_own w_j u_j:
+//   selected chunk: ds_j = alpha_c P_j (u_j - r_c), value weight alpha_c P_j,
+//                   ds^_c = alpha_c (r_c - D)
+//   own chunk:      ds_j = w_j (u_j - D), w_j = exp(s_j - Lambda)
+//   dQ = scale (sum ds_j k_j + sum_c ds^_c k'_c),  dK_j += scale ds_j q,
+//   dV_j += weight dO,  dk'_c = scale sum_i ds^_ic q_i,  db'_c = sum_i ds^_ic,
+//   ds'_j = p'_j [dk'.(k_j - k'_c) + db' (L' - s'_j - b'_c)],
+//   dQl = scale sum_j ds'_j k_j,  dK_j += p'_j dk'_c + scale ds'_j Ql.
+//
+// Kernels (no floating-point atomics; integer or fixed-order sums, so the
+// gradients are bitwise reproducible):
+//   k_bwd_prep   : per (chunk, kv head) K^T in MFMA k-slot order and bounds
+//                  (max |k|, max ||v||) for the fixed-point dQ accumulator
+//   k_bwd_q      : query side, one workgroup per (kv head, block of rows), the
+//                  rows' selections counting-sorted by chunk as in the forward;
+//                  per 16-row tile S^T = K Q^T and U^T = V dO^T on MFMA, then
+//                  dQ^T += K^T dS^T on MFMA into integer LDS accumulators;
+//                  writes dQ, ds^ per (row, slot) and D per row
+//   k_sel_bitmap : (k_backward.hip) rows that selected each chunk
+//   k_bwd_kv_mfma: key side, one workgroup per (chunk, kv head); the rows that
+//                  selected the chunk (ascending) and the chunk's own rows in
+//                  32-row tiles: S^T, U^T on MFMA, weights and dS written
+//                  transposed to LDS, dK += dS^T Q and dV += A^T dO on MFMA;
+//                  then the summary and landmark backward; writes dK, dV, dQl.
+#include "hils_internal.h"
+
+namespace hils {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = 64;
+constexpr int kLanes = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int KF = 4 * (D / 32);  // row fragments (uint4) of a 64-key chunk per lane
+constexpr int VF = (D / 16) * 2;  // transposed-chunk fragments per lane
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &u, 16);
+  return r;
+}
+__device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma(uint4 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float xmax_16_32(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xsum_16_32(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float bf(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// MFMA 16x16x32 bf16 lane layout (lane l, g = l / 16, c = l % 16):
+//   A[m = c][k = 8g + j], B[k = 8g + j][n = c], D[m = 4g + r][n = c].
+// S^T block kb of a chunk gives lane l keys 16 kb + 4g + r of tile row c. For a
+// product whose k dimension is the chunk's keys, k-slot 8g + j of step ks holds
+// key 32 ks + 4g + j (j < 4) or 32 ks + 16 + 4g + (j - 4) (j >= 4): exactly the
+// S^T values the lane holds, so weights need no data movement; K^T is stored in
+// that key order (k_bwd_prep).
+
+// ------------------------------------------------------------------ prep
+// Kt[b][g][c][e][p] = K[key(p)][e] (k-slot order, zero beyond Tkv);
+// bnd[b][g][c] = (max |k|, max_j ||v_j||).
+__global__ __launch_bounds__(256) void k_bwd_prep(Dims dm, int nct, const uint16_t* __restrict__ K,
+                                                  const uint16_t* __restrict__ V,
+                                                  uint16_t* __restrict__ Kt,
+                                                  float2* __restrict__ bnd) {
+  __shared__ uint16_t ks[kChunk][D + 8];
+  __shared__ float red[2][4];
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const long long kv_stride = (long long)dm.Hkv * D;
+  const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
+  float km = 0.f, vn = 0.f;
+  for (int u = t; u < kChunk * D / 8; u += 256) {
+    const int j = u / (D / 8), c8 = u % (D / 8);
+    const long long row = (long long)c * kChunk + j;
+    const bool in = row < dm.Tkv;
+    const uint4 kv = in ? *reinterpret_cast<const uint4*>(K + kv_base + row * kv_stride + c8 * 8)
+                        : make_uint4(0, 0, 0, 0);
+    const uint4 vv = in ? *reinterpret_cast<const uint4*>(V + kv_base + row * kv_stride + c8 * 8)
+                        : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&ks[j][c8 * 8]) = kv;
+    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
+    float v2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      km = fmaxf(km, fmaxf(fabsf(__uint_as_float(kw[q] << 16)), fabsf(__uint_as_float(kw[q] & 0xFFFF0000u))));
+      const float a = __uint_as_float(vw[q] << 16), bb = __uint_as_float(vw[q] & 0xFFFF0000u);
+      v2 = fmaf(a, a, fmaf(bb, bb, v2));
+    }
+    // squared norm of row j: the D / 8 pieces of a row sit in consecutive lanes
+#pragma unroll
+    for (int o = 1; o < D / 8; o <<= 1) v2 += __shfl_xor(v2, o, kLanes);
+    vn = fmaxf(vn, v2);
+  }
+  km = wave_max(km);
+  vn = wave_max(vn);
+  if ((t & 63) == 0) red[0][t >> 6] = km, red[1][t >> 6] = vn;
+  __syncthreads();
+  const long long cbase = (((long long)b * dm.Hkv + g) * nct + c) * (long long)D * kChunk;
+  for (int u = t; u < D * 8; u += 256) {
+    const int e = u / 8, p8 = u % 8;  // feature e, k-slots 8 p8 .. 8 p8 + 7
+    const int kstep = p8 / 4, gg = p8 % 4;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j0 = 2 * q, j1 = 2 * q + 1;
+      const int k0 = 32 * kstep + (j0 < 4 ? 4 * gg + j0 : 16 + 4 * gg + j0 - 4);
+      const int k1 = 32 * kstep + (j1 < 4 ? 4 * gg + j1 : 16 + 4 * gg + j1 - 4);
+      w[q] = (uint32_t)ks[k0][e] | ((uint32_t)ks[k1][e] << 16);
+    }
+    *reinterpret_cast<uint4*>(Kt + cbase + (long long)e * kChunk + p8 * 8) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (t == 0)
+    bnd[((long long)b * dm.Hkv + g) * nct + c] =
+        make_float2(fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3])),
+                    sqrtf(fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]))));
+}
+
+// ------------------------------------------------------------------ query side
+constexpr int kQThreads = 512;
+constexpr int kQWaves = kQThreads / 64;
+constexpr int kQRows = 128;  // rows per workgroup (positions x heads of one kv head)
+constexpr int QP = D + 8;    // LDS row pitch of query / dO rows (bf16)
+constexpr int AP = D + 1;    // accumulator row pitch (words)
+
+struct QFrag {
+  uint4 k[KF];   // K rows:  k[kb * 2 + ds] = K[16 kb + c][32 ds + 8g .. +8]
+  uint4 v[KF];   // V rows, same layout
+  uint4 kt[VF];  // K^T:     kt[db * 2 + ks] = K^T[16 db + c][k-slots 32 ks + 8g .. +8]
+};
+
+__device__ __forceinline__ void load_qfrag(QFrag& f, const uint16_t* K, const uint16_t* V,
+                                           const uint16_t* Kt, long long kv_base,
+                                           long long kv_stride, int chunk, long long kt_base,
+                                           long long Tkv) {
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      const long long row = min((long long)chunk * kChunk + 16 * kb + c, Tkv - 1);
+      const long long off = kv_base + row * kv_stride + 32 * ds + 8 * g;
+      f.k[kb * 2 + ds] = *reinterpret_cast<const uint4*>(K + off);
+      f.v[kb * 2 + ds] = *reinterpret_cast<const uint4*>(V + off);
+    }
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      f.kt[db * 2 + ks] = *reinterpret_cast<const uint4*>(
+          Kt + kt_base + (long long)(16 * db + c) * kChunk + 32 * ks + 8 * g);
+}
+
+// S^T (scaled, log2 units) and U^T of one 16-row tile: lane l holds keys
+// 16 kb + 4g + r of tile row c in s[kb][r], u[kb][r].
+__device__ __forceinline__ void tile_su(const QFrag& f, const uint4* q, const uint4* o,
+                                        floatx4* s, floatx4* u) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    u[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      s[kb] = mfma(f.k[kb * 2 + ds], q[ds], s[kb]);
+      u[kb] = mfma(f.v[kb * 2 + ds], o[ds], u[kb]);
+    }
+  }
+}
+
+// dQ^T partial of a tile: sum_j ds_j k_j, with ds given in S^T layout.
+__device__ __forceinline__ void tile_dq(const QFrag& f, const floatx4* ds, floatx4* dq) {
+  bf16x8 pf[2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pf[kb >> 1][(kb & 1) * 4 + r] = (__bf16)ds[kb][r];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    dq[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) dq[db] = mfma(f.kt[db * 2 + ks], pf[ks], dq[db]);
+  }
+}
+
+__device__ __forceinline__ void lds_frag2(uint4* x, const uint16_t* base, int rho, bool valid) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int ds = 0; ds < 2; ++ds)
+    x[ds] = valid ? *reinterpret_cast<const uint4*>(base + rho * QP + 32 * ds + 8 * g)
+                  : make_uint4(0, 0, 0, 0);
+}
+
+struct QSmem {
+  int* acc;       // [R][AP] dQ / scale in fixed point
+  uint16_t* qs;   // [R][QP] query rows
+  uint16_t* os;   // [R][QP] dO rows
+  uint32_t* ent;  // chunk-major entries rho | k << 16
+  float* rr;      // [R][K]: r per (row, slot), then ds^
+  int* cnt;
+  int* off;
+  int* cur;
+  int* nz;
+  float* lam;     // Lambda (natural log)
+  float* aown;    // alpha of the own chunk
+  float* rown;    // r of the own chunk
+  float* dv;      // D
+  int* misc;
+};
+
+__host__ __device__ inline size_t q_smem_bytes(int R, int K, int ncr) {
+  return (size_t)R * AP * 4 + 2 * (size_t)R * QP * 2 + (size_t)R * K * 8 +
+         4 * (size_t)(ncr + 1) * 4 + 4 * (size_t)R * 4 + 64 * 4;
+}
+
+__device__ __forceinline__ QSmem q_carve(char* p, int R, int K, int ncr) {
+  QSmem s;
+  s.acc = reinterpret_cast<int*>(p); p += (size_t)R * AP * 4;
+  s.qs = reinterpret_cast<uint16_t*>(p); p += (size_t)R * QP * 2;
+  s.os = reinterpret_cast<uint16_t*>(p); p += (size_t)R * QP * 2;
+  s.ent = reinterpret_cast<uint32_t*>(p); p += (size_t)R * K * 4;
+  s.rr = reinterpret_cast<float*>(p); p += (size_t)R * K * 4;
+  s.cnt = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
+  s.off = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
+  s.cur = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
+  s.nz = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
+  s.lam = reinterpret_cast<float*>(p); p += R * 4;
+  s.aown = reinterpret_cast<float*>(p); p += R * 4;
+  s.rown = reinterpret_cast<float*>(p); p += R * 4;
+  s.dv = reinterpret_cast<float*>(p); p += R * 4;
+  s.misc = reinterpret_cast<int*>(p);
+  return s;
+}
+
+// In-place exclusive scan of n ints by the workgroup; returns the total.
+__device__ __forceinline__ int q_scan(int* a, int n, int* scratch) {
+  const int t = threadIdx.x;
+  const int seg = (n + kQThreads - 1) / kQThreads;
+  const int lo = min(n, t * seg), hi = min(n, lo + seg);
+  int s = 0;
+  for (int x = lo; x < hi; ++x) s += a[x];
+  const int lane = t & 63, w = t >> 6;
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) scratch[w] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int x = 0; x < kQWaves; ++x) {
+    const int v = scratch[x];
+    before += x < w ? v : 0;
+    total += v;
+  }
+  int run = before + incl - s;
+  for (int x = lo; x < hi; ++x) {
+    const int v = a[x];
+    a[x] = run;
+    run += v;
+  }
+  __syncthreads();
+  return total;
+}
+
+// Own-chunk tile items: (own chunk, 16-row tile) pairs in chunk order.
+__device__ __forceinline__ bool q_own_item(int item, long long p0, int S, int G, int Rv,
+                                           int own_first, int own_last, int* oc, int* ra, int* rb,
+                                           int* tl) {
+  for (int c = own_first; c <= own_last; ++c) {
+    const int a = (int)max(0LL, (long long)c * S - p0) * G;
+    const int bnd = (int)min((long long)Rv, ((long long)c * S + S - p0) * G);
+    const int nt = (bnd - a + 15) / 16;
+    if (item < nt) {
+      *oc = c, *ra = a, *rb = bnd, *tl = item;
+      return true;
+    }
+    item -= nt;
+  }
+  return false;
+}
+
+__global__ __launch_bounds__(kQThreads) void k_bwd_q(
+    Dims dm, int R, int Rq, int ncr_cap, int nqb, int nct, const uint16_t* __restrict__ Q,
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ Kt, const float2* __restrict__ bnd,
+    const float* __restrict__ ksum, const int32_t* __restrict__ idx,
+    const float* __restrict__ score, const float* __restrict__ lse_tot,
+    const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, float* __restrict__ ws_dsh,
+    float* __restrict__ ws_D) {
+  extern __shared__ __align__(16) char smem_raw[];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 15, gl = lane >> 4;
+  const int G = dm.G, Ksel = dm.K, S = dm.S;
+  const int L = blockIdx.x;
+  const int g = L % dm.Hkv, qb = (L / dm.Hkv) % nqb, b = L / (dm.Hkv * nqb);
+  const int qi0 = qb * Rq;
+  const int nq = min(Rq, dm.Tq - qi0);
+  const int Rv = nq * G;
+  const long long p0 = dm.q_pos0 + qi0;
+  const int own_first = (int)(p0 / S), own_last = (int)((p0 + nq - 1) / S);
+  const int ncr = own_last;
+  QSmem sm = q_carve(smem_raw, R, Ksel, ncr_cap);
+  const long long kv_stride = (long long)dm.Hkv * D;
+  const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
+  const long long kt_base = ((long long)b * dm.Hkv + g) * nct * (long long)D * kChunk;
+  const float2* bd = bnd + ((long long)b * dm.Hkv + g) * nct;
+  const float scale2 = dm.scale * kLog2e;
+  auto row_of = [&](int rho) -> long long {
+    return ((long long)b * dm.Tq + qi0 + rho / G) * dm.H + (long long)g * G + rho % G;
+  };
+
+  // ---- set-up: query and dO rows, Lambda, counting sort of the selections
+  for (int c = t; c <= ncr; c += kQThreads) sm.cnt[c] = 0;
+  for (int x = t; x < Rv * (D / 8); x += kQThreads) {
+    const int rho = x / (D / 8), c8 = x % (D / 8);
+    const long long r = row_of(rho);
+    *reinterpret_cast<uint4*>(sm.qs + rho * QP + c8 * 8) =
+        *reinterpret_cast<const uint4*>(Q + r * D + c8 * 8);
+    *reinterpret_cast<uint4*>(sm.os + rho * QP + c8 * 8) =
+        *reinterpret_cast<const uint4*>(dO + r * D + c8 * 8);
+  }
+  for (int rho = t; rho < Rv; rho += kQThreads) sm.lam[rho] = lse_tot[row_of(rho)];
+  __syncthreads();
+  for (int rho = t; rho < Rv; rho += kQThreads) {
+    const long long r = row_of(rho);
+    const int own = (int)((p0 + rho / G) / S);
+    for (int k = 0; k < Ksel; ++k) {
+      const int c = idx[r * Ksel + k];
+      if (c >= 0 && c < own) atomicAdd(&sm.cnt[c], 1);
+    }
+  }
+  __syncthreads();
+  for (int c = t; c < ncr; c += kQThreads) {
+    sm.off[c] = sm.cnt[c];
+    sm.nz[c] = sm.cnt[c] > 0 ? 1 : 0;
+  }
+  __syncthreads();
+  q_scan(sm.off, ncr, sm.misc);
+  const int nnz = q_scan(sm.nz, ncr, sm.misc + 8);
+  for (int c = t; c < ncr; c += kQThreads) sm.cur[c] = sm.off[c];
+  __syncthreads();
+  for (int rho = t; rho < Rv; rho += kQThreads) {
+    const long long r = row_of(rho);
+    const int own = (int)((p0 + rho / G) / S);
+    for (int k = 0; k < Ksel; ++k) {
+      const int c = idx[r * Ksel + k];
+      sm.rr[rho * Ksel + k] = 0.f;
+      if (c >= 0 && c < own) {
+        const int p = atomicAdd(&sm.cur[c], 1);
+        sm.ent[p] = (uint32_t)rho | ((uint32_t)k << 16);
+      }
+    }
+  }
+  // bound of every partial sum of dQ / scale (see the file comment): with
+  // |u| <= ||dO|| max||v||, sum_j |ds_j| <= 2 alpha max|u| per chunk and
+  // |ds^_c| <= 2 alpha_c max|u|, |dQ / scale| <= 4 max||dO|| max||v|| max|k|
+  float dn = 0.f;
+  for (int rho = t; rho < Rv; rho += kQThreads) {
+    float n2 = 0.f;
+    for (int e = 0; e < D; ++e) {
+      const float x = bf(sm.os[rho * QP + e]);
+      n2 = fmaf(x, x, n2);
+    }
+    dn = fmaxf(dn, n2);
+  }
+  __syncthreads();
+  float km = 0.f, vn = 0.f;
+  for (int c = t; c <= own_last; c += kQThreads)
+    if (c >= own_first || (c < ncr && sm.cnt[c] > 0)) {
+      const float2 bb = bd[c];
+      km = fmaxf(km, bb.x);
+      vn = fmaxf(vn, bb.y);
+    }
+  for (int c = t; c < ncr; c += kQThreads)
+    if (sm.cnt[c] > 0) sm.cur[sm.nz[c]] = c;
+  dn = wave_max(dn), km = wave_max(km), vn = wave_max(vn);
+  float* redf = reinterpret_cast<float*>(sm.misc) + 16;
+  if (lane == 0) redf[w] = dn, redf[8 + w] = km, redf[16 + w] = vn;
+  __syncthreads();
+  float dnw = 0.f, kmw = 0.f, vnw = 0.f;
+#pragma unroll
+  for (int x = 0; x < kQWaves; ++x)
+    dnw = fmaxf(dnw, redf[x]), kmw = fmaxf(kmw, redf[8 + x]), vnw = fmaxf(vnw, redf[16 + x]);
+  int ex = 0;
+  frexpf(fmaxf(4.f * sqrtf(dnw) * vnw * kmw, 1e-30f), &ex);
+  const float fx_scale = ldexpf(1.0f, 29 - ex);
+  const float fx_inv = ldexpf(1.0f, ex - 29);
+  for (int x = t; x < R * AP; x += kQThreads) sm.acc[x] = 0;
+  __syncthreads();
+
+  const int n_own = [&]() {
+    int n = 0;
+    for (int c = own_first; c <= own_last; ++c) {
+      const int a = (int)max(0LL, (long long)c * S - p0) * G;
+      const int e = (int)min((long long)Rv, ((long long)c * S + S - p0) * G);
+      n += (e - a + 15) / 16;
+    }
+    return n;
+  }();
+
+  // ---- own chunks, pass 1: own log-mass, alpha_own and r_own per row
+  for (int item = w; item < n_own; item += kQWaves) {
+    int oc, ra, rb, tl;
+    q_own_item(item, p0, S, G, Rv, own_first, own_last, &oc, &ra, &rb, &tl);
+    QFrag f;
+    load_qfrag(f, K, V, Kt, kv_base, kv_stride, oc, kt_base + (long long)oc * D * kChunk, dm.Tkv);
+    const int rho = ra + 16 * tl + col;
+    const bool valid = rho < rb;
+    const int nk = valid ? (int)(p0 + rho / G - (long long)oc * S) + 1 : 0;
+    uint4 q[2], o[2];
+    lds_frag2(q, sm.qs, rho, valid);
+    lds_frag2(o, sm.os, rho, valid);
+    floatx4 s[4], u[4];
+    tile_su(f, q, o, s, u);
+    float m = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * kb + 4 * gl + r;
+        s[kb][r] = j < nk ? s[kb][r] * scale2 : -INFINITY;
+        m = fmaxf(m, s[kb][r]);
+      }
+    m = xmax_16_32(m);
+    if (!valid) m = 0.f;
+    float z = 0.f, zu = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = exp2f(s[kb][r] - m);
+        z += e;
+        zu = fmaf(e, u[kb][r], zu);
+      }
+    z = xsum_16_32(z);
+    zu = xsum_16_32(zu);
+    if (valid && gl == 0) {
+      const float lown = (m + __log2f(z)) * kLn2;
+      sm.aown[rho] = expf(lown - sm.lam[rho]);
+      sm.rown[rho] = zu / z;
+    }
+  }
+
+  // ---- selected chunks: chunk u belongs to wave u mod 8
+  for (int uu = w; uu < nnz; uu += kQWaves) {
+    const int c = sm.cur[uu];
+    QFrag f;
+    load_qfrag(f, K, V, Kt, kv_base, kv_stride, c, kt_base + (long long)c * D * kChunk, dm.Tkv);
+    const int e0 = sm.off[c], n = sm.cnt[c];
+    for (int tl = 0; tl < (n + 15) / 16; ++tl) {
+      const int e = 16 * tl + col;
+      const bool valid = e < n;
+      const uint32_t en = valid ? sm.ent[e0 + e] : 0u;
+      const int rho = (int)(en & 0xFFFFu), k = (int)(en >> 16);
+      uint4 q[2], o[2];
+      lds_frag2(q, sm.qs, rho, valid);
+      lds_frag2(o, sm.os, rho, valid);
+      const float alpha = valid ? expf(score[row_of(rho) * Ksel + k] - sm.lam[rho]) : 0.f;
+      floatx4 s[4], u[4];
+      tile_su(f, q, o, s, u);
+      float m = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[kb][r] *= scale2;
+          m = fmaxf(m, s[kb][r]);
+        }
+      m = xmax_16_32(m);
+      float z = 0.f, zu = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[kb][r] = exp2f(s[kb][r] - m);
+          z += s[kb][r];
+          zu = fmaf(s[kb][r], u[kb][r], zu);
+        }
+      z = xsum_16_32(z);
+      zu = xsum_16_32(zu);
+      const float iz = 1.0f / z, rc = zu * iz;
+      floatx4 ds[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ds[kb][r] = alpha * s[kb][r] * iz * (u[kb][r] - rc);
+      floatx4 dq[D / 16];
+      tile_dq(f, ds, dq);
+      if (valid) {
+        if (gl == 0) sm.rr[rho * Ksel + k] = rc;
+        int* ar = sm.acc + rho * AP;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            atomicAdd(ar + 16 * db + 4 * gl + r, (int)(dq[db][r] * fx_scale));
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- per row: D and the score gradients ds^ (to the workspace and LDS)
+  for (int rho = t; rho < Rv; rho += kQThreads) {
+    const long long r = row_of(rho);
+    const int own = (int)((p0 + rho / G) / S);
+    const float lam = sm.lam[rho];
+    float Dsum = sm.aown[rho] * sm.rown[rho];
+    for (int k = 0; k < Ksel; ++k) {
+      const int c = idx[r * Ksel + k];
+      if (c >= 0 && c < own) Dsum = fmaf(expf(score[r * Ksel + k] - lam), sm.rr[rho * Ksel + k], Dsum);
+    }
+    for (int k = 0; k < Ksel; ++k) {
+      const int c = idx[r * Ksel + k];
+      float dsh = 0.f;
+      if (c >= 0 && c < own) dsh = expf(score[r * Ksel + k] - lam) * (sm.rr[rho * Ksel + k] - Dsum);
+      sm.rr[rho * Ksel + k] = dsh;
+      ws_dsh[r * Ksel + k] = dsh;
+    }
+    sm.dv[rho] = Dsum;
+    ws_D[r] = Dsum;
+  }
+  __syncthreads();
+  // dQ += sum_c ds^_c k'_c (one thread per (row, feature): plain adds)
+  for (int x = t; x < Rv * D; x += kQThreads) {
+    const int rho = x / D, e = x % D;
+    const long long r = row_of(rho);
+    const int h = g * G + rho % G;
+    float acc = 0.f;
+    for (int k = 0; k < Ksel; ++k) {
+      const float dsh = sm.rr[rho * Ksel + k];
+      if (dsh != 0.f) {
+        const int c = idx[r * Ksel + k];
+        acc = fmaf(dsh, ksum[(((long long)b * dm.NCcap + c) * dm.H + h) * D + e], acc);
+      }
+    }
+    sm.acc[rho * AP + e] += (int)(acc * fx_scale);
+  }
+  __syncthreads();
+
+  // ---- own chunks, pass 2: ds_j = w_j (u_j - D)
+  for (int item = w; item < n_own; item += kQWaves) {
+    int oc, ra, rb, tl;
+    q_own_item(item, p0, S, G, Rv, own_first, own_last, &oc, &ra, &rb, &tl);
+    QFrag f;
+    load_qfrag(f, K, V, Kt, kv_base, kv_stride, oc, kt_base + (long long)oc * D * kChunk, dm.Tkv);
+    const int rho = ra + 16 * tl + col;
+    const bool valid = rho < rb;
+    const int nk = valid ? (int)(p0 + rho / G - (long long)oc * S) + 1 : 0;
+    uint4 q[2], o[2];
+    lds_frag2(q, sm.qs, rho, valid);
+    lds_frag2(o, sm.os, rho, valid);
+    const float lam2 = valid ? sm.lam[rho] * kLog2e : 0.f;
+    const float Dr = valid ? sm.dv[rho] : 0.f;
+    floatx4 s[4], u[4];
+    tile_su(f, q, o, s, u);
+    floatx4 ds[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * kb + 4 * gl + r;
+        const float wj = j < nk ? exp2f(s[kb][r] * scale2 - lam2) : 0.f;
+        ds[kb][r] = wj * (u[kb][r] - Dr);
+      }
+    floatx4 dq[D / 16];
+    tile_dq(f, ds, dq);
+    if (valid) {
+      int* ar = sm.acc + rho * AP;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          atomicAdd(ar + 16 * db + 4 * gl + r, (int)(dq[db][r] * fx_scale));
+    }
+  }
+  __syncthreads();
+
+  // ---- dQ = scale * accumulator (bf16, round to nearest even)
+  const float out_scale = fx_inv * dm.scale;
+  for (int x = t; x < Rv * (D / 8); x += kQThreads) {
+    const int rho = x / (D / 8), c8 = x % (D / 8);
+    uint32_t ow[4];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int e0 = 8 * c8 + 2 * y;
+      ow[y] = (uint32_t)f32_to_bf16_bits((float)sm.acc[rho * AP + e0] * out_scale) |
+              ((uint32_t)f32_to_bf16_bits((float)sm.acc[rho * AP + e0 + 1] * out_scale) << 16);
+    }
+    *reinterpret_cast<uint4*>(dQ + row_of(rho) * D + c8 * 8) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  }
+}
+
+// ------------------------------------------------------------------ key side
+// One workgroup per (chunk, kv head, batch); each wavefront takes every fourth
+// 32-row tile of the row list and keeps dK, dV for all 64 keys x 64 features in
+// registers; the four wavefronts' partial sums are added in a fixed order at
+// the end. Transposes go through wavefront-private LDS.
+constexpr int kKThreads = 256;
+constexpr int kKWaves = kKThreads / 64;
+constexpr int kTileRows = 32;
+constexpr int TP = kTileRows + 8;  // LDS pitch of transposed tiles (bf16)
+constexpr int kListMax = 2048;
+
+struct KWave {
+  uint16_t qt[D][TP];       // Q^T of the tile
+  uint16_t ot[D][TP];       // dO^T of the tile
+  uint16_t at[kChunk][TP];  // value weights, transposed [key][row]
+  uint16_t dt[kChunk][TP];  // dS, transposed [key][row]
+};
+struct KSmem {
+  KWave wv[kKWaves];
+  int rows[kListMax];    // row list segment: global row index
+  float aux[kListMax];   // alpha (selecting rows) or D (own rows)
+  float dshv[kListMax];  // ds^ of (row, chunk) for selecting rows
+  float dkb[kKWaves][D];  // per-wave dk' partial sums, then the total
+  float dbw[kKWaves];
+  float sp[kChunk];      // p'_j
+  float sdp[kChunk];     // ds'_j
+};
+static_assert(sizeof(KSmem) <= 160 * 1024, "key-side LDS");
+
+__global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
+    Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ Ql,
+    const float* __restrict__ ksum, const float* __restrict__ ent,
+    const float* __restrict__ lse_l, const int32_t* __restrict__ idx,
+    const float* __restrict__ score, const float* __restrict__ lse_tot,
+    const uint16_t* __restrict__ dO, const float* __restrict__ ws_dsh,
+    const float* __restrict__ ws_D, const uint32_t* __restrict__ bm, int words,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, uint16_t* __restrict__ dQl) {
+  extern __shared__ __align__(16) char smem_raw[];
+  KSmem& sm = *reinterpret_cast<KSmem*>(smem_raw);
+  __shared__ int list_n;
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 15, gl = lane >> 4;
+  const int NC = dm.Tkv / dm.S, Ksel = dm.K, G = dm.G;
+  const float scale2 = dm.scale * kLog2e;
+  const long long kv_stride = (long long)dm.Hkv * D;
+  const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
+  const long long key0 = (long long)c * kChunk;
+  KWave& wv = sm.wv[w];
+
+  // the chunk's K and V rows as MFMA A fragments
+  uint4 kf[KF], vf[KF];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      const long long off = kv_base + (key0 + 16 * kb + col) * kv_stride + 32 * ds + 8 * gl;
+      kf[kb * 2 + ds] = *reinterpret_cast<const uint4*>(K + off);
+      vf[kb * 2 + ds] = *reinterpret_cast<const uint4*>(V + off);
+    }
+  // dK / scale and dV: block [kb][fb] holds keys 16 kb + 4 gl + r x features 16 fb + col
+  floatx4 dka[4][4], dva[4][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) dka[kb][fb] = dva[kb][fb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // one 32-row tile of this wavefront: rows sm.rows[e0 .. e0 + nr)
+  auto run_tile = [&](int e0, int nr, bool own_rows, float& dkb_lane, float& db_acc) {
+    uint4 qf[2][2], of[2][2];
+    float aux[2];
+    int rpos[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const bool v = 16 * hf + col < nr;
+      const int e = e0 + min(16 * hf + col, nr - 1);
+      const long long r = sm.rows[e];
+#pragma unroll
+      for (int ds = 0; ds < 2; ++ds) {
+        qf[hf][ds] = *reinterpret_cast<const uint4*>(Q + r * D + 32 * ds + 8 * gl);
+        of[hf][ds] = *reinterpret_cast<const uint4*>(dO + r * D + 32 * ds + 8 * gl);
+        if (!v) qf[hf][ds] = of[hf][ds] = make_uint4(0, 0, 0, 0);
+      }
+      aux[hf] = v ? sm.aux[e] : 0.f;
+      rpos[hf] = (int)((r / dm.H) % dm.Tq);
+    }
+    const float lam0 = own_rows ? lse_tot[sm.rows[e0 + min(col, nr - 1)]] : 0.f;
+    const float lam1 = own_rows ? lse_tot[sm.rows[e0 + min(16 + col, nr - 1)]] : 0.f;
+    // Q^T and dO^T of the tile from the fragments (this wavefront's LDS)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int ds = 0; ds < 2; ++ds) {
+        const uint32_t qw[4] = {qf[hf][ds].x, qf[hf][ds].y, qf[hf][ds].z, qf[hf][ds].w};
+        const uint32_t ow[4] = {of[hf][ds].x, of[hf][ds].y, of[hf][ds].z, of[hf][ds].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = 32 * ds + 8 * gl + 2 * q;
+          wv.qt[e][16 * hf + col] = (uint16_t)(qw[q] & 0xFFFFu);
+          wv.qt[e + 1][16 * hf + col] = (uint16_t)(qw[q] >> 16);
+          wv.ot[e][16 * hf + col] = (uint16_t)(ow[q] & 0xFFFFu);
+          wv.ot[e + 1][16 * hf + col] = (uint16_t)(ow[q] >> 16);
+        }
+      }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      floatx4 s[4], u[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = u[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < 2; ++ds) {
+          s[kb] = mfma(kf[kb * 2 + ds], qf[hf][ds], s[kb]);
+          u[kb] = mfma(vf[kb * 2 + ds], of[hf][ds], u[kb]);
+        }
+      }
+      const bool v = 16 * hf + col < nr;
+      floatx4 a[4], d[4];
+      if (own_rows) {
+        const float lam2 = (hf ? lam1 : lam0) * kLog2e, Dr = aux[hf];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const long long kp = key0 + 16 * kb + 4 * gl + r;
+            const float wj = (v && kp <= rpos[hf]) ? exp2f(s[kb][r] * scale2 - lam2) : 0.f;
+            a[kb][r] = wj;
+            d[kb][r] = wj * (u[kb][r] - Dr);
+          }
+      } else {
+        float m = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) m = fmaxf(m, s[kb][r] * scale2);
+        m = xmax_16_32(m);
+        float z = 0.f, zu = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            s[kb][r] = exp2f(s[kb][r] * scale2 - m);
+            z += s[kb][r];
+            zu = fmaf(s[kb][r], u[kb][r], zu);
+          }
+        z = xsum_16_32(z);
+        zu = xsum_16_32(zu);
+        const float iz = 1.0f / z, rc = zu * iz, al = v ? aux[hf] : 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = al * s[kb][r] * iz;
+            a[kb][r] = p;
+            d[kb][r] = p * (u[kb][r] - rc);
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 16 * kb + 4 * gl + r;
+          wv.at[key][16 * hf + col] = f32_to_bf16_bits(a[kb][r]);
+          wv.dt[key][16 * hf + col] = f32_to_bf16_bits(d[kb][r]);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // summary key gradient of the selecting rows: lane e: dk'[e] += ds^ q[e]
+    if (!own_rows) {
+      for (int rr = 0; rr < nr; ++rr) {
+        const float dsh = sm.dshv[e0 + rr];
+        dkb_lane = fmaf(dsh, bf(wv.qt[lane][rr]), dkb_lane);
+        db_acc += dsh;
+      }
+    }
+    // dV += A^T dO, dK += dS^T Q over the tile's 32 rows (k dimension = rows)
+    uint4 obf[4], qbf[4];
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+      obf[fb] = *reinterpret_cast<const uint4*>(&wv.ot[16 * fb + col][8 * gl]);
+      qbf[fb] = *reinterpret_cast<const uint4*>(&wv.qt[16 * fb + col][8 * gl]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint4 af = *reinterpret_cast<const uint4*>(&wv.at[16 * kb + col][8 * gl]);
+      const uint4 df = *reinterpret_cast<const uint4*>(&wv.dt[16 * kb + col][8 * gl]);
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        dva[kb][fb] = mfma(af, obf[fb], dva[kb][fb]);
+        dka[kb][fb] = mfma(df, qbf[fb], dka[kb][fb]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    float dkb_lane = 0.f;  // dk' / scale for feature `lane`
+    float db = 0.f;
+    // own rows: the chunk's positions (causal), one 32-row tile per wavefront
+    for (int x = t; x < kChunk; x += kKThreads) {
+      const long long pos = min(key0 + x, (long long)dm.Tq - 1);
+      const long long r = ((long long)b * dm.Tq + pos) * dm.H + h;
+      sm.rows[x] = (int)r;
+      sm.aux[x] = ws_D[r];
+    }
+    __syncthreads();
+    const int n_own = (int)min((long long)kChunk, dm.Tq - key0);
+    for (int e0 = kTileRows * w; e0 < n_own; e0 += kTileRows * kKWaves)
+      run_tile(e0, min(kTileRows, n_own - e0), true, dkb_lane, db);
+    __syncthreads();
+    // rows that selected this chunk, ascending, in segments of the bitmap
+    const uint32_t* bmw = bm + (((long long)b * dm.H + h) * NC + c) * words;
+    for (int w0 = (int)((key0 + kChunk) / 32); w0 < words; w0 += kLanes) {
+      if (w == 0) {
+        const uint32_t word = (w0 + lane < words) ? bmw[w0 + lane] : 0u;
+        const int cnt = __popc(word);
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < kLanes; o <<= 1) {
+          const int y = __shfl_up(incl, o, kLanes);
+          if (lane >= o) incl += y;
+        }
+        int p = incl - cnt;
+        uint32_t bits = word;
+        while (bits) {
+          const int bit = __ffs(bits) - 1;
+          bits &= bits - 1;
+          sm.rows[p++] = (int)(((long long)b * dm.Tq + (w0 + lane) * 32 + bit) * dm.H + h);
+        }
+        if (lane == kLanes - 1) list_n = incl;
+      }
+      __syncthreads();
+      const int n = list_n;
+      // slot of the chunk in each row's selection (one vector read of the row's
+      // selections), its fusion weight alpha and its ds^
+      for (int e = t; e < n; e += kKThreads) {
+        const long long r = sm.rows[e];
+        int slot = 0;
+        for (int k0 = 0; k0 < Ksel; k0 += 4) {
+          int4 v;
+          if (((Ksel & 3) == 0)) {
+            v = *reinterpret_cast<const int4*>(idx + r * Ksel + k0);
+          } else {
+            v.x = idx[r * Ksel + k0];
+            v.y = k0 + 1 < Ksel ? idx[r * Ksel + k0 + 1] : -1;
+            v.z = k0 + 2 < Ksel ? idx[r * Ksel + k0 + 2] : -1;
+            v.w = k0 + 3 < Ksel ? idx[r * Ksel + k0 + 3] : -1;
+          }
+          slot = v.x == c ? k0 : slot;
+          slot = v.y == c ? k0 + 1 : slot;
+          slot = v.z == c ? k0 + 2 : slot;
+          slot = v.w == c ? k0 + 3 : slot;
+        }
+        sm.aux[e] = expf(score[r * Ksel + slot] - lse_tot[r]);
+        sm.dshv[e] = ws_dsh[r * Ksel + slot];
+      }
+      __syncthreads();
+      for (int e0 = kTileRows * w; e0 < n; e0 += kTileRows * kKWaves)
+        run_tile(e0, min(kTileRows, n - e0), false, dkb_lane, db);
+      __syncthreads();
+    }
+    // ---- summary and landmark backward of (chunk c, head h)
+    sm.dkb[w][lane] = dkb_lane;
+    if (lane == 0) sm.dbw[w] = db;
+    __syncthreads();
+    if (t < D)  // fixed order over the wavefronts
+      sm.dkb[0][t] = (((sm.dkb[0][t] + sm.dkb[1][t]) + sm.dkb[2][t]) + sm.dkb[3][t]) * dm.scale;
+    __syncthreads();
+    const long long sidx = ((long long)b * dm.NCcap + c) * dm.H + h;
+    if (w == 0) {  // lane j: key j of the chunk
+      const uint16_t* kr = K + kv_base + (key0 + lane) * kv_stride;
+      const uint16_t* ql = Ql + sidx * D;
+      const float* kbar = ksum + sidx * D;
+      float s1 = 0.f, t1 = 0.f;
+      for (int e = 0; e < D; ++e) {
+        const float kje = bf(kr[e]);
+        s1 = fmaf(bf(ql[e]), kje, s1);
+        t1 = fmaf(sm.dkb[0][e], kje - kbar[e], t1);
+      }
+      s1 *= dm.scale;
+      const float Lp = lse_l[sidx], bias = ent[sidx];
+      const float dbv = ((sm.dbw[0] + sm.dbw[1]) + sm.dbw[2]) + sm.dbw[3];
+      const float p1 = expf(s1 - Lp);
+      sm.sp[lane] = p1;
+      sm.sdp[lane] = p1 * (t1 + dbv * (Lp - s1 - bias));
+    }
+    __syncthreads();
+    if (t < D) {  // dQl = scale sum_j ds'_j k_j
+      float acc = 0.f;
+      for (int j = 0; j < kChunk; ++j) acc = fmaf(sm.sdp[j], bf(K[kv_base + (key0 + j) * kv_stride + t]), acc);
+      dQl[sidx * D + t] = f32_to_bf16_bits(acc * dm.scale);
+    }
+    // dK_j += p'_j dk' + scale ds'_j Ql: added once, by wavefront 0's accumulators
+    if (w == 0) {
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        const float dk_e = sm.dkb[0][16 * fb + col];
+        const float ql_e = bf(Ql[sidx * D + 16 * fb + col]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * kb + 4 * gl + r;
+            dka[kb][fb][r] += (sm.sp[j] * dk_e) / dm.scale + sm.sdp[j] * ql_e;
+          }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- dK = scale * (sum of the wavefronts' accumulators), dV; fixed order
+  float* red = reinterpret_cast<float*>(&sm.wv[0]);  // [64 keys][64 features], reused
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int ww = 0; ww < kKWaves; ++ww) {
+      if (w == ww) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int o = (16 * kb + 4 * gl + r) * D + 16 * fb + col;
+              const float v = pass == 0 ? dka[kb][fb][r] : dva[kb][fb][r];
+              red[o] = ww == 0 ? v : red[o] + v;
+            }
+      }
+      __syncthreads();
+    }
+    uint16_t* out = pass == 0 ? dK : dV;
+    const float sc = pass == 0 ? dm.scale : 1.0f;
+    for (int x = t; x < kChunk * D; x += kKThreads) {
+      const int j = x / D, e = x % D;
+      out[kv_base + (key0 + j) * kv_stride + e] = f32_to_bf16_bits(red[x] * sc);
+    }
+    __syncthreads();
+  }
+}
+
+struct BPlan {
+  int R, Rq, ncr, nqb, nct;
+  size_t smem, kt_bytes, bnd_bytes;
+};
+
+bool bwd_plan(const Dims& dm, BPlan* p) {
+  if (!dm.bf16 || dm.d != 64 || dm.Tq < 64 || dm.q_pos0 != 0) return false;
+  int r = kQRows;
+  while (r > 16 && r * dm.K > 2048) r /= 2;
+  int rq = r / dm.G;
+  if (rq < 1) return false;
+  const int ncr = (dm.Tq - 1) / dm.S + 1;
+  while (rq > 1 && q_smem_bytes(rq * dm.G, dm.K, ncr) > 160 * 1024) rq -= max(1, rq / 8);
+  r = rq * dm.G;
+  p->smem = q_smem_bytes(r, dm.K, ncr);
+  if (p->smem > 160 * 1024) return false;
+  p->R = r;
+  p->Rq = rq;
+  p->ncr = ncr;
+  p->nqb = (dm.Tq + rq - 1) / rq;
+  p->nct = dm.Tkv / dm.S;
+  p->kt_bytes = (size_t)dm.B * dm.Hkv * p->nct * D * kChunk * 2;
+  p->bnd_bytes = (size_t)dm.B * dm.Hkv * p->nct * sizeof(float2);
+  return true;
+}
+
+}  // namespace
+
+size_t backward_mfma_ws_bytes(const Dims& dm) {
+  BPlan p;
+  if (!bwd_plan(dm, &p)) return 0;
+  return ((p.kt_bytes + 255) & ~(size_t)255) + ((p.bnd_bytes + 255) & ~(size_t)255);
+}
+
+bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void* V,
+                       const void* Ql, const float* ksum, const float* ent, const float* lse_l,
+                       const int32_t* idx, const float* score, const float* lse_tot,
+                       const void* dO, void* dQ, void* dK, void* dV, void* dQl, float* ws_dsh,
+                       float* ws_D, const uint32_t* bm, int words, void* ws_mfma, hipStream_t st,
+                       hipError_t* err) {
+  BPlan p;
+  if (!bwd_plan(dm, &p)) return false;
+  char* base = reinterpret_cast<char*>(ws_mfma);
+  uint16_t* Kt = reinterpret_cast<uint16_t*>(base);
+  float2* bnd = reinterpret_cast<float2*>(base + ((p.kt_bytes + 255) & ~(size_t)255));
+  const auto* Qh = reinterpret_cast<const uint16_t*>(Q);
+  const auto* Kh = reinterpret_cast<const uint16_t*>(K);
+  const auto* Vh = reinterpret_cast<const uint16_t*>(V);
+  hipLaunchKernelGGL(k_bwd_prep, dim3(p.nct, dm.Hkv, dm.B), dim3(256), 0, st, dm, p.nct, Kh, Vh,
+                     Kt, bnd);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_q),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.smem);
+  if (e != hipSuccess) {
+    *err = e;
+    return true;
+  }
+  hipLaunchKernelGGL(k_bwd_q, dim3(dm.B * p.nqb * dm.Hkv), dim3(kQThreads), p.smem, st, dm, p.R,
+                     p.Rq, p.ncr, p.nqb, p.nct, Qh, Kh, Vh, Kt, bnd, ksum, idx, score, lse_tot,
+                     reinterpret_cast<const uint16_t*>(dO), reinterpret_cast<uint16_t*>(dQ),
+                     ws_dsh, ws_D);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_kv_mfma),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(KSmem));
+  if (e != hipSuccess) {
+    *err = e;
+    return true;
+  }
+  hipLaunchKernelGGL(k_bwd_kv_mfma, dim3(p.nct, dm.Hkv, dm.B), dim3(kKThreads), sizeof(KSmem), st, dm, Qh, Kh,
+                     Vh, reinterpret_cast<const uint16_t*>(Ql), ksum, ent, lse_l, idx, score,
+                     lse_tot, reinterpret_cast<const uint16_t*>(dO), ws_dsh, ws_D, bm, words,
+                     reinterpret_cast<uint16_t*>(dK), reinterpret_cast<uint16_t*>(dV),
+                     reinterpret_cast<uint16_t*>(dQl));
+  *err = hipGetLastError();
+  return true;
+}
+
+}  // namespace hils
