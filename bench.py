@@ -336,7 +336,8 @@ def main():
             }
             if wx.need_dO:
                 calls["backward"] = lambda: hsa.backward(tx["Q"], tx["K"], tx["V"], tx["Ql"], ksx,
-                                                         enx, llx, ix, scx, ltx, tx["dO"], wx.S)
+                                                         enx, llx, ix, scx, ltx, Ox, tx["dO"],
+                                                         wx.S)
             for fn in calls.values():
                 fn()
             torch.cuda.synchronize()

@@ -57,7 +57,7 @@ def lib():
         L.hils_summarize.argtypes = [P, VP, VP, i32, i32, VP, VP, VP, VP, SZ, VP]
         L.hils_score_topk.argtypes = [P, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.hils_attend_fuse.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
-        L.hils_backward.argtypes = [P] + [VP] * 15 + [VP, SZ, VP]
+        L.hils_backward.argtypes = [P] + [VP] * 16 + [VP, SZ, VP]
         L.hils_status_string.argtypes = [ctypes.c_int]
         L.hils_status_string.restype = ctypes.c_char_p
         L.hils_version.restype = i32
@@ -198,14 +198,15 @@ def forward(Q, K, V, Ql, K_sel: int, S: int = 64, scale: float = 0.0):
                 lse_tot=lse_tot)
 
 
-def backward(Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, dO, S: int = 64,
+def backward(Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, S: int = 64,
              scale: float = 0.0):
-    """Gradients (dQ, dK, dV, dQl) of sum(dO * O) with the selection held fixed."""
+    """Gradients (dQ, dK, dV, dQl) of sum(dO * O) with the selection held fixed; O is the
+    forward's output."""
     B, T, H, d = Q.shape
     Hkv = K.shape[2]
     K_sel = idx.shape[-1]
     NC = Ql.shape[1]
-    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (Ql, "Ql"), (dO, "dO")):
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (Ql, "Ql"), (O, "O"), (dO, "dO")):
         _need(t, n, dtype=Q.dtype)
     _need(ksum, "ksum", (B, NC, H, d), torch.float32)
     _need(idx, "idx", (B, T, H, K_sel), torch.int32)
@@ -215,6 +216,6 @@ def backward(Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, dO, S: int = 64
     ws, n = _workspace(dims, OP_BACKWARD, dev)
     _check("hils_backward", lib().hils_backward(
         ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(Ql), _ptr(ksum), _ptr(ent),
-        _ptr(lse_l), _ptr(idx), _ptr(score), _ptr(lse_tot), _ptr(dO), _ptr(dQ), _ptr(dK),
+        _ptr(lse_l), _ptr(idx), _ptr(score), _ptr(lse_tot), _ptr(O), _ptr(dO), _ptr(dQ), _ptr(dK),
         _ptr(dV), _ptr(dQl), _ptr(ws), n, _stream(dev)))
     return dQ, dK, dV, dQl

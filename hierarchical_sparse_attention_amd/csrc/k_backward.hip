@@ -20,7 +20,8 @@
 // Kernels (no floating-point atomics; fixed summation orders => deterministic):
 //   k_bwd_rows : one wavefront per row -> dQ, ds^ per slot, D_i (workspace)
 //   k_sel_bitmap: bit i of word [b,h,c] set when row i selected chunk c (atomicOr
-//                 commutes, so the bitmap does not depend on thread order)
+//                 commutes, so the bitmap does not depend on thread order);
+//                 k_sel_bitmap_lds builds blocks of it in LDS and writes them once
 //   k_bwd_kv   : one workgroup per (chunk, kv head, batch) -> dK, dV, dQl, walking
 //                the rows that selected the chunk in ascending order.
 #include "hils_internal.h"
@@ -181,6 +182,33 @@ __global__ void k_sel_bitmap(Dims dm, const int32_t* __restrict__ idx, uint32_t*
     const int b = (int)(r / ((long long)dm.H * dm.Tq));
     if (c < 0 || c >= (dm.q_pos0 + i) / dm.S || c >= NC) continue;
     atomicOr(&bm[(((long long)b * dm.H + h) * NC + c) * words + i / 32], 1u << (i % 32));
+  }
+}
+
+// Same bitmaps built per (block of wpw words = 32 wpw positions, head, batch)
+// in LDS and written once: no global atomics and no clearing pass.
+__global__ __launch_bounds__(256) void k_sel_bitmap_lds(Dims dm, const int32_t* __restrict__ idx,
+                                                        uint32_t* __restrict__ bm, int words,
+                                                        int wpw) {
+  extern __shared__ uint32_t lb[];  // [NC][wpw]
+  const int NC = dm.Tkv / dm.S;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int w0 = blockIdx.x * wpw;
+  const int nw = min(wpw, words - w0);
+  for (int x = threadIdx.x; x < NC * wpw; x += blockDim.x) lb[x] = 0u;
+  __syncthreads();
+  const int i0 = w0 * 32, ni = min(nw * 32, dm.Tq - i0);
+  for (int x = threadIdx.x; x < ni * dm.K; x += blockDim.x) {
+    const int ii = x / dm.K, k = x % dm.K;
+    const int i = i0 + ii;
+    const int c = idx[(((long long)b * dm.Tq + i) * dm.H + h) * dm.K + k];
+    if (c < 0 || c >= (dm.q_pos0 + i) / dm.S || c >= NC) continue;
+    atomicOr(&lb[c * wpw + ii / 32], 1u << (ii % 32));
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < NC * nw; x += blockDim.x) {
+    const int c = x / nw, ww = x % nw;
+    bm[(((long long)b * dm.H + h) * NC + c) * words + w0 + ww] = lb[c * wpw + ww];
   }
 }
 
@@ -391,20 +419,28 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, const void* __restrict_
 template <bool BF16, int D>
 hipError_t launch_t(const Dims& dm, const void* Q, const void* K, const void* V, const void* Ql,
                     const float* ksum, const float* ent, const float* lse_l, const int32_t* idx,
-                    const float* score, const float* lse_tot, const void* dO, void* dQ, void* dK,
-                    void* dV, void* dQl, void* ws, hipStream_t st) {
+                    const float* score, const float* lse_tot, const void* O, const void* dO,
+                    void* dQ, void* dK, void* dV, void* dQl, void* ws, hipStream_t st) {
   const WsLayout L = ws_layout(dm);
   char* base = reinterpret_cast<char*>(ws);
   float* dsh = reinterpret_cast<float*>(base + L.dsh);
   float* Dr = reinterpret_cast<float*>(base + L.dr);
   uint32_t* bm = reinterpret_cast<uint32_t*>(base + L.bitmap);
   const int NC = dm.Tkv / dm.S;
-  const long long nbm = (long long)dm.B * dm.H * NC * L.words;
-  hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, bm, nbm);
-  hipLaunchKernelGGL(k_sel_bitmap, dim3(1024), dim3(256), 0, st, dm, idx, bm, L.words);
+  // words per bitmap block: as many as 64 KiB of LDS holds, at most 16
+  int wpw = 16;
+  while (wpw > 1 && (size_t)NC * wpw * 4 > 65536) wpw /= 2;
+  if ((size_t)NC * wpw * 4 <= 65536) {
+    hipLaunchKernelGGL(k_sel_bitmap_lds, dim3((L.words + wpw - 1) / wpw, dm.H, dm.B), dim3(256),
+                       (size_t)NC * wpw * 4, st, dm, idx, bm, L.words, wpw);
+  } else {
+    const long long nbm = (long long)dm.B * dm.H * NC * L.words;
+    hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, bm, nbm);
+    hipLaunchKernelGGL(k_sel_bitmap, dim3(1024), dim3(256), 0, st, dm, idx, bm, L.words);
+  }
   hipError_t err = hipSuccess;
-  if (backward_mfma_try(dm, Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, dO, dQ, dK, dV,
-                        dQl, dsh, Dr, bm, L.words, base + L.mfma, st, &err))
+  if (backward_mfma_try(dm, Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, dQ, dK,
+                        dV, dQl, Dr, bm, L.words, base + L.mfma, st, &err))
     return err;
   hipLaunchKernelGGL((k_bwd_rows<BF16, D>), dim3((dm.Tq + 3) / 4, dm.H, dm.B), dim3(256), 0, st,
                      dm, Q, K, V, ksum, idx, score, lse_tot, dO, dQ, dsh, Dr);
@@ -421,12 +457,12 @@ size_t backward_ws_bytes(const Dims& dm) { return ws_layout(dm).total; }
 hipError_t launch_backward(const Dims& dm, const void* Q, const void* K, const void* V,
                            const void* Ql, const float* ksum, const float* ent, const float* lse_l,
                            const int32_t* idx, const float* score, const float* lse_tot,
-                           const void* dO, void* dQ, void* dK, void* dV, void* dQl, void* ws,
-                           hipStream_t st) {
+                           const void* O, const void* dO, void* dQ, void* dK, void* dV,
+                           void* dQl, void* ws, hipStream_t st) {
   if ((long long)dm.B * dm.Tq * dm.H == 0) return hipSuccess;
 #define HILS_BWD(BF, DD)                                                                      \
-  return launch_t<BF, DD>(dm, Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, dO, dQ, dK, \
-                          dV, dQl, ws, st)
+  return launch_t<BF, DD>(dm, Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, dQ, \
+                          dK, dV, dQl, ws, st)
   if (dm.bf16) {
     if (dm.d == 64) HILS_BWD(true, 64);
     HILS_BWD(true, 128);

@@ -5,7 +5,7 @@
 // query, the summary key, the entropy bias and through the landmark softmax
 // (note §5.1) the landmark query and the keys). Per row i with fused weights
 // alpha_c = exp(s^_c - Lambda), intra-chunk softmax P, u_j = dO.v_j,
-// r_c = sum_j P_j u_j and D = sum_c alpha_c r_c + sum_own w_j u_j:
+// r_c = sum_j P_j u_j and D = sum_c alpha_c r_c + sum_own w_j u_j = dO.O:
 //   selected chunk: ds_j = alpha_c P_j (u_j - r_c), value weight alpha_c P_j,
 //                   ds^_c = alpha_c (r_c - D)
 //   own chunk:      ds_j = w_j (u_j - D), w_j = exp(s_j - Lambda)
@@ -20,15 +20,17 @@
 //                  (max |k|, max ||v||) for the fixed-point dQ accumulator
 //   k_bwd_q      : query side, one workgroup per (kv head, block of rows), the
 //                  rows' selections counting-sorted by chunk as in the forward;
-//                  per 16-row tile S^T = K Q^T and U^T = V dO^T on MFMA, then
-//                  dQ^T += K^T dS^T on MFMA into integer LDS accumulators;
-//                  writes dQ, ds^ per (row, slot) and D per row
+//                  D = dO.O from the forward output; per 16-row tile
+//                  S^T = K Q^T and U^T = V dO^T on MFMA, then dQ^T += K^T dS^T
+//                  on MFMA (plus ds^ k') into integer LDS accumulators; writes
+//                  dQ and D per row
 //   k_sel_bitmap : (k_backward.hip) rows that selected each chunk
 //   k_bwd_kv_mfma: key side, one workgroup per (chunk, kv head); the rows that
 //                  selected the chunk (ascending) and the chunk's own rows in
 //                  32-row tiles: S^T, U^T on MFMA, weights and dS written
-//                  transposed to LDS, dK += dS^T Q and dV += A^T dO on MFMA;
-//                  then the summary and landmark backward; writes dK, dV, dQl.
+//                  transposed to LDS, dK += dS^T Q and dV += A^T dO on MFMA,
+//                  ds^ = alpha (r - D) into dk' and db'; then the summary and
+//                  landmark backward; writes dK, dV, dQl.
 #include "hils_internal.h"
 
 namespace hils {
@@ -40,7 +42,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int D = 64;
 constexpr int kLanes = 64;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int KF = 4 * (D / 32);  // row fragments (uint4) of a 64-key chunk per lane
 constexpr int VF = (D / 16) * 2;  // transposed-chunk fragments per lane
 
@@ -216,21 +217,18 @@ struct QSmem {
   uint16_t* qs;   // [R][QP] query rows
   uint16_t* os;   // [R][QP] dO rows
   uint32_t* ent;  // chunk-major entries rho | k << 16
-  float* rr;      // [R][K]: r per (row, slot), then ds^
   int* cnt;
   int* off;
   int* cur;
   int* nz;
   float* lam;     // Lambda (natural log)
-  float* aown;    // alpha of the own chunk
-  float* rown;    // r of the own chunk
-  float* dv;      // D
+  float* dv;      // D = dO . O
   int* misc;
 };
 
 __host__ __device__ inline size_t q_smem_bytes(int R, int K, int ncr) {
-  return (size_t)R * AP * 4 + 2 * (size_t)R * QP * 2 + (size_t)R * K * 8 +
-         4 * (size_t)(ncr + 1) * 4 + 4 * (size_t)R * 4 + 64 * 4;
+  return (size_t)R * AP * 4 + 2 * (size_t)R * QP * 2 + (size_t)R * K * 4 +
+         4 * (size_t)(ncr + 1) * 4 + 2 * (size_t)R * 4 + 64 * 4;
 }
 
 __device__ __forceinline__ QSmem q_carve(char* p, int R, int K, int ncr) {
@@ -239,14 +237,11 @@ __device__ __forceinline__ QSmem q_carve(char* p, int R, int K, int ncr) {
   s.qs = reinterpret_cast<uint16_t*>(p); p += (size_t)R * QP * 2;
   s.os = reinterpret_cast<uint16_t*>(p); p += (size_t)R * QP * 2;
   s.ent = reinterpret_cast<uint32_t*>(p); p += (size_t)R * K * 4;
-  s.rr = reinterpret_cast<float*>(p); p += (size_t)R * K * 4;
   s.cnt = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
   s.off = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
   s.cur = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
   s.nz = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
   s.lam = reinterpret_cast<float*>(p); p += R * 4;
-  s.aown = reinterpret_cast<float*>(p); p += R * 4;
-  s.rown = reinterpret_cast<float*>(p); p += R * 4;
   s.dv = reinterpret_cast<float*>(p); p += R * 4;
   s.misc = reinterpret_cast<int*>(p);
   return s;
@@ -302,13 +297,23 @@ __device__ __forceinline__ bool q_own_item(int item, long long p0, int S, int G,
   return false;
 }
 
+// Add a tile's dQ^T (lane: features 16 db + 4g + r of tile row c) to the row's
+// fixed-point accumulator.
+__device__ __forceinline__ void q_accumulate(int* acc_row, const floatx4* dq, float fx_scale) {
+  const int gl = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) atomicAdd(acc_row + 16 * db + 4 * gl + r, (int)(dq[db][r] * fx_scale));
+}
+
 __global__ __launch_bounds__(kQThreads) void k_bwd_q(
     Dims dm, int R, int Rq, int ncr_cap, int nqb, int nct, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ Kt, const float2* __restrict__ bnd,
     const float* __restrict__ ksum, const int32_t* __restrict__ idx,
     const float* __restrict__ score, const float* __restrict__ lse_tot,
-    const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ, float* __restrict__ ws_dsh,
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ,
     float* __restrict__ ws_D) {
   extern __shared__ __align__(16) char smem_raw[];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 15, gl = lane >> 4;
@@ -331,25 +336,45 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
     return ((long long)b * dm.Tq + qi0 + rho / G) * dm.H + (long long)g * G + rho % G;
   };
 
-  // ---- set-up: query and dO rows, Lambda, counting sort of the selections
+  // ---- set-up: query and dO rows, D = dO . O, Lambda, counting sort of the selections
   for (int c = t; c <= ncr; c += kQThreads) sm.cnt[c] = 0;
+  float dn = 0.f;  // max ||dO||^2 over the rows
   for (int x = t; x < Rv * (D / 8); x += kQThreads) {
     const int rho = x / (D / 8), c8 = x % (D / 8);
     const long long r = row_of(rho);
-    *reinterpret_cast<uint4*>(sm.qs + rho * QP + c8 * 8) =
-        *reinterpret_cast<const uint4*>(Q + r * D + c8 * 8);
-    *reinterpret_cast<uint4*>(sm.os + rho * QP + c8 * 8) =
-        *reinterpret_cast<const uint4*>(dO + r * D + c8 * 8);
+    const uint4 qv = *reinterpret_cast<const uint4*>(Q + r * D + c8 * 8);
+    const uint4 ov = *reinterpret_cast<const uint4*>(dO + r * D + c8 * 8);
+    const uint4 yv = *reinterpret_cast<const uint4*>(O + r * D + c8 * 8);
+    *reinterpret_cast<uint4*>(sm.qs + rho * QP + c8 * 8) = qv;
+    *reinterpret_cast<uint4*>(sm.os + rho * QP + c8 * 8) = ov;
+    const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w}, yw[4] = {yv.x, yv.y, yv.z, yv.w};
+    float dd = 0.f, n2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float o0 = __uint_as_float(ow[q] << 16), o1 = __uint_as_float(ow[q] & 0xFFFF0000u);
+      const float y0 = __uint_as_float(yw[q] << 16), y1 = __uint_as_float(yw[q] & 0xFFFF0000u);
+      dd = fmaf(o0, y0, fmaf(o1, y1, dd));
+      n2 = fmaf(o0, o0, fmaf(o1, o1, n2));
+    }
+    // the D / 8 pieces of a row sit in consecutive lanes
+#pragma unroll
+    for (int o = 1; o < D / 8; o <<= 1) {
+      dd += __shfl_xor(dd, o, kLanes);
+      n2 += __shfl_xor(n2, o, kLanes);
+    }
+    if (c8 == 0) {
+      sm.dv[rho] = dd;
+      ws_D[r] = dd;
+    }
+    dn = fmaxf(dn, n2);
   }
   for (int rho = t; rho < Rv; rho += kQThreads) sm.lam[rho] = lse_tot[row_of(rho)];
   __syncthreads();
-  for (int rho = t; rho < Rv; rho += kQThreads) {
-    const long long r = row_of(rho);
+  for (int x = t; x < Rv * Ksel; x += kQThreads) {
+    const int rho = x / Ksel, k = x % Ksel;
     const int own = (int)((p0 + rho / G) / S);
-    for (int k = 0; k < Ksel; ++k) {
-      const int c = idx[r * Ksel + k];
-      if (c >= 0 && c < own) atomicAdd(&sm.cnt[c], 1);
-    }
+    const int c = idx[row_of(rho) * Ksel + k];
+    if (c >= 0 && c < own) atomicAdd(&sm.cnt[c], 1);
   }
   __syncthreads();
   for (int c = t; c < ncr; c += kQThreads) {
@@ -361,30 +386,18 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
   const int nnz = q_scan(sm.nz, ncr, sm.misc + 8);
   for (int c = t; c < ncr; c += kQThreads) sm.cur[c] = sm.off[c];
   __syncthreads();
-  for (int rho = t; rho < Rv; rho += kQThreads) {
-    const long long r = row_of(rho);
+  for (int x = t; x < Rv * Ksel; x += kQThreads) {
+    const int rho = x / Ksel, k = x % Ksel;
     const int own = (int)((p0 + rho / G) / S);
-    for (int k = 0; k < Ksel; ++k) {
-      const int c = idx[r * Ksel + k];
-      sm.rr[rho * Ksel + k] = 0.f;
-      if (c >= 0 && c < own) {
-        const int p = atomicAdd(&sm.cur[c], 1);
-        sm.ent[p] = (uint32_t)rho | ((uint32_t)k << 16);
-      }
+    const int c = idx[row_of(rho) * Ksel + k];
+    if (c >= 0 && c < own) {
+      const int p = atomicAdd(&sm.cur[c], 1);
+      sm.ent[p] = (uint32_t)rho | ((uint32_t)k << 16);
     }
   }
   // bound of every partial sum of dQ / scale (see the file comment): with
   // |u| <= ||dO|| max||v||, sum_j |ds_j| <= 2 alpha max|u| per chunk and
   // |ds^_c| <= 2 alpha_c max|u|, |dQ / scale| <= 4 max||dO|| max||v|| max|k|
-  float dn = 0.f;
-  for (int rho = t; rho < Rv; rho += kQThreads) {
-    float n2 = 0.f;
-    for (int e = 0; e < D; ++e) {
-      const float x = bf(sm.os[rho * QP + e]);
-      n2 = fmaf(x, x, n2);
-    }
-    dn = fmaxf(dn, n2);
-  }
   __syncthreads();
   float km = 0.f, vn = 0.f;
   for (int c = t; c <= own_last; c += kQThreads)
@@ -420,7 +433,7 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
     return n;
   }();
 
-  // ---- own chunks, pass 1: own log-mass, alpha_own and r_own per row
+  // ---- own chunks: ds_j = w_j (u_j - D), w_j = exp(s_j - Lambda)
   for (int item = w; item < n_own; item += kQWaves) {
     int oc, ra, rb, tl;
     q_own_item(item, p0, S, G, Rv, own_first, own_last, &oc, &ra, &rb, &tl);
@@ -428,151 +441,13 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
     load_qfrag(f, K, V, Kt, kv_base, kv_stride, oc, kt_base + (long long)oc * D * kChunk, dm.Tkv);
     const int rho = ra + 16 * tl + col;
     const bool valid = rho < rb;
+    const int rc = valid ? rho : ra;
     const int nk = valid ? (int)(p0 + rho / G - (long long)oc * S) + 1 : 0;
     uint4 q[2], o[2];
-    lds_frag2(q, sm.qs, rho, valid);
-    lds_frag2(o, sm.os, rho, valid);
-    floatx4 s[4], u[4];
-    tile_su(f, q, o, s, u);
-    float m = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * kb + 4 * gl + r;
-        s[kb][r] = j < nk ? s[kb][r] * scale2 : -INFINITY;
-        m = fmaxf(m, s[kb][r]);
-      }
-    m = xmax_16_32(m);
-    if (!valid) m = 0.f;
-    float z = 0.f, zu = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = exp2f(s[kb][r] - m);
-        z += e;
-        zu = fmaf(e, u[kb][r], zu);
-      }
-    z = xsum_16_32(z);
-    zu = xsum_16_32(zu);
-    if (valid && gl == 0) {
-      const float lown = (m + __log2f(z)) * kLn2;
-      sm.aown[rho] = expf(lown - sm.lam[rho]);
-      sm.rown[rho] = zu / z;
-    }
-  }
-
-  // ---- selected chunks: chunk u belongs to wave u mod 8
-  for (int uu = w; uu < nnz; uu += kQWaves) {
-    const int c = sm.cur[uu];
-    QFrag f;
-    load_qfrag(f, K, V, Kt, kv_base, kv_stride, c, kt_base + (long long)c * D * kChunk, dm.Tkv);
-    const int e0 = sm.off[c], n = sm.cnt[c];
-    for (int tl = 0; tl < (n + 15) / 16; ++tl) {
-      const int e = 16 * tl + col;
-      const bool valid = e < n;
-      const uint32_t en = valid ? sm.ent[e0 + e] : 0u;
-      const int rho = (int)(en & 0xFFFFu), k = (int)(en >> 16);
-      uint4 q[2], o[2];
-      lds_frag2(q, sm.qs, rho, valid);
-      lds_frag2(o, sm.os, rho, valid);
-      const float alpha = valid ? expf(score[row_of(rho) * Ksel + k] - sm.lam[rho]) : 0.f;
-      floatx4 s[4], u[4];
-      tile_su(f, q, o, s, u);
-      float m = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s[kb][r] *= scale2;
-          m = fmaxf(m, s[kb][r]);
-        }
-      m = xmax_16_32(m);
-      float z = 0.f, zu = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s[kb][r] = exp2f(s[kb][r] - m);
-          z += s[kb][r];
-          zu = fmaf(s[kb][r], u[kb][r], zu);
-        }
-      z = xsum_16_32(z);
-      zu = xsum_16_32(zu);
-      const float iz = 1.0f / z, rc = zu * iz;
-      floatx4 ds[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ds[kb][r] = alpha * s[kb][r] * iz * (u[kb][r] - rc);
-      floatx4 dq[D / 16];
-      tile_dq(f, ds, dq);
-      if (valid) {
-        if (gl == 0) sm.rr[rho * Ksel + k] = rc;
-        int* ar = sm.acc + rho * AP;
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            atomicAdd(ar + 16 * db + 4 * gl + r, (int)(dq[db][r] * fx_scale));
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- per row: D and the score gradients ds^ (to the workspace and LDS)
-  for (int rho = t; rho < Rv; rho += kQThreads) {
-    const long long r = row_of(rho);
-    const int own = (int)((p0 + rho / G) / S);
-    const float lam = sm.lam[rho];
-    float Dsum = sm.aown[rho] * sm.rown[rho];
-    for (int k = 0; k < Ksel; ++k) {
-      const int c = idx[r * Ksel + k];
-      if (c >= 0 && c < own) Dsum = fmaf(expf(score[r * Ksel + k] - lam), sm.rr[rho * Ksel + k], Dsum);
-    }
-    for (int k = 0; k < Ksel; ++k) {
-      const int c = idx[r * Ksel + k];
-      float dsh = 0.f;
-      if (c >= 0 && c < own) dsh = expf(score[r * Ksel + k] - lam) * (sm.rr[rho * Ksel + k] - Dsum);
-      sm.rr[rho * Ksel + k] = dsh;
-      ws_dsh[r * Ksel + k] = dsh;
-    }
-    sm.dv[rho] = Dsum;
-    ws_D[r] = Dsum;
-  }
-  __syncthreads();
-  // dQ += sum_c ds^_c k'_c (one thread per (row, feature): plain adds)
-  for (int x = t; x < Rv * D; x += kQThreads) {
-    const int rho = x / D, e = x % D;
-    const long long r = row_of(rho);
-    const int h = g * G + rho % G;
-    float acc = 0.f;
-    for (int k = 0; k < Ksel; ++k) {
-      const float dsh = sm.rr[rho * Ksel + k];
-      if (dsh != 0.f) {
-        const int c = idx[r * Ksel + k];
-        acc = fmaf(dsh, ksum[(((long long)b * dm.NCcap + c) * dm.H + h) * D + e], acc);
-      }
-    }
-    sm.acc[rho * AP + e] += (int)(acc * fx_scale);
-  }
-  __syncthreads();
-
-  // ---- own chunks, pass 2: ds_j = w_j (u_j - D)
-  for (int item = w; item < n_own; item += kQWaves) {
-    int oc, ra, rb, tl;
-    q_own_item(item, p0, S, G, Rv, own_first, own_last, &oc, &ra, &rb, &tl);
-    QFrag f;
-    load_qfrag(f, K, V, Kt, kv_base, kv_stride, oc, kt_base + (long long)oc * D * kChunk, dm.Tkv);
-    const int rho = ra + 16 * tl + col;
-    const bool valid = rho < rb;
-    const int nk = valid ? (int)(p0 + rho / G - (long long)oc * S) + 1 : 0;
-    uint4 q[2], o[2];
-    lds_frag2(q, sm.qs, rho, valid);
-    lds_frag2(o, sm.os, rho, valid);
-    const float lam2 = valid ? sm.lam[rho] * kLog2e : 0.f;
-    const float Dr = valid ? sm.dv[rho] : 0.f;
+    lds_frag2(q, sm.qs, rc, true);
+    lds_frag2(o, sm.os, rc, true);
+    const float lam2 = sm.lam[rc] * kLog2e;
+    const float Dr = sm.dv[rc];
     floatx4 s[4], u[4];
     tile_su(f, q, o, s, u);
     floatx4 ds[4];
@@ -586,13 +461,71 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
       }
     floatx4 dq[D / 16];
     tile_dq(f, ds, dq);
-    if (valid) {
-      int* ar = sm.acc + rho * AP;
+    if (valid) q_accumulate(sm.acc + rho * AP, dq, fx_scale);
+  }
+
+  // ---- selected chunks (chunk u belongs to wave u mod 8):
+  //      ds_j = alpha P_j (u_j - r), plus ds^ = alpha (r - D) times the summary key
+  for (int uu = w; uu < nnz; uu += kQWaves) {
+    const int c = sm.cur[uu];
+    QFrag f;
+    load_qfrag(f, K, V, Kt, kv_base, kv_stride, c, kt_base + (long long)c * D * kChunk, dm.Tkv);
+    const int e0 = sm.off[c], n = sm.cnt[c];
+    for (int tl = 0; tl < (n + 15) / 16; ++tl) {
+      const int e = 16 * tl + col;
+      const bool valid = e < n;
+      const uint32_t en = sm.ent[e0 + min(e, n - 1)];
+      const int rho = (int)(en & 0xFFFFu), k = (int)(en >> 16);
+      const long long r = row_of(rho);
+      const float sc = score[r * Ksel + k];
+      const float* kbar = ksum + (((long long)b * dm.NCcap + c) * dm.H + (long long)g * G + rho % G) * D + 4 * gl;
+      float4 kb4[D / 16];
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db)
+      for (int db = 0; db < D / 16; ++db) kb4[db] = *reinterpret_cast<const float4*>(kbar + 16 * db);
+      uint4 q[2], o[2];
+      lds_frag2(q, sm.qs, rho, true);
+      lds_frag2(o, sm.os, rho, true);
+      const float lam = sm.lam[rho], Dr = sm.dv[rho];
+      floatx4 s[4], u[4];
+      tile_su(f, q, o, s, u);
+      float m = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          atomicAdd(ar + 16 * db + 4 * gl + r, (int)(dq[db][r] * fx_scale));
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2) {
+          s[kb][r2] *= scale2;
+          m = fmaxf(m, s[kb][r2]);
+        }
+      m = xmax_16_32(m);
+      float z = 0.f, zu = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2) {
+          s[kb][r2] = exp2f(s[kb][r2] - m);
+          z += s[kb][r2];
+          zu = fmaf(s[kb][r2], u[kb][r2], zu);
+        }
+      z = xsum_16_32(z);
+      zu = xsum_16_32(zu);
+      const float alpha = valid ? expf(sc - lam) : 0.f;
+      const float iz = 1.0f / z, rcv = zu * iz;
+      floatx4 ds[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2) ds[kb][r2] = alpha * s[kb][r2] * iz * (u[kb][r2] - rcv);
+      floatx4 dq[D / 16];
+      tile_dq(f, ds, dq);
+      const float dsh = alpha * (rcv - Dr);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        dq[db][0] = fmaf(dsh, kb4[db].x, dq[db][0]);
+        dq[db][1] = fmaf(dsh, kb4[db].y, dq[db][1]);
+        dq[db][2] = fmaf(dsh, kb4[db].z, dq[db][2]);
+        dq[db][3] = fmaf(dsh, kb4[db].w, dq[db][3]);
+      }
+      if (valid) q_accumulate(sm.acc + rho * AP, dq, fx_scale);
     }
   }
   __syncthreads();
@@ -633,7 +566,7 @@ struct KSmem {
   KWave wv[kKWaves];
   int rows[kListMax];    // row list segment: global row index
   float aux[kListMax];   // alpha (selecting rows) or D (own rows)
-  float dshv[kListMax];  // ds^ of (row, chunk) for selecting rows
+  float dvl[kListMax];   // D of the selecting rows
   float dkb[kKWaves][D];  // per-wave dk' partial sums, then the total
   float dbw[kKWaves];
   float sp[kChunk];      // p'_j
@@ -647,8 +580,8 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     const float* __restrict__ ksum, const float* __restrict__ ent,
     const float* __restrict__ lse_l, const int32_t* __restrict__ idx,
     const float* __restrict__ score, const float* __restrict__ lse_tot,
-    const uint16_t* __restrict__ dO, const float* __restrict__ ws_dsh,
-    const float* __restrict__ ws_D, const uint32_t* __restrict__ bm, int words,
+    const uint16_t* __restrict__ dO, const float* __restrict__ ws_D,
+    const uint32_t* __restrict__ bm, int words,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, uint16_t* __restrict__ dQl) {
   extern __shared__ __align__(16) char smem_raw[];
   KSmem& sm = *reinterpret_cast<KSmem*>(smem_raw);
@@ -680,9 +613,9 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     for (int fb = 0; fb < 4; ++fb) dka[kb][fb] = dva[kb][fb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // one 32-row tile of this wavefront: rows sm.rows[e0 .. e0 + nr)
-  auto run_tile = [&](int e0, int nr, bool own_rows, float& dkb_lane, float& db_acc) {
+  auto run_tile = [&](int e0, int nr, bool own_rows, float (&dkp)[2][8], float& dbp) {
     uint4 qf[2][2], of[2][2];
-    float aux[2];
+    float aux[2], dvr[2];
     int rpos[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -696,6 +629,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         if (!v) qf[hf][ds] = of[hf][ds] = make_uint4(0, 0, 0, 0);
       }
       aux[hf] = v ? sm.aux[e] : 0.f;
+      dvr[hf] = own_rows ? 0.f : sm.dvl[e];
       rpos[hf] = (int)((r / dm.H) % dm.Tq);
     }
     const float lam0 = own_rows ? lse_tot[sm.rows[e0 + min(col, nr - 1)]] : 0.f;
@@ -768,6 +702,18 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
             a[kb][r] = p;
             d[kb][r] = p * (u[kb][r] - rc);
           }
+        // ds^ = alpha (r - D): summary key and bias gradients of the row
+        const float dsh = al * (rc - dvr[hf]);
+        dbp += dsh;
+#pragma unroll
+        for (int ds = 0; ds < 2; ++ds) {
+          const uint32_t qw[4] = {qf[hf][ds].x, qf[hf][ds].y, qf[hf][ds].z, qf[hf][ds].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            dkp[ds][2 * q] = fmaf(dsh, __uint_as_float(qw[q] << 16), dkp[ds][2 * q]);
+            dkp[ds][2 * q + 1] = fmaf(dsh, __uint_as_float(qw[q] & 0xFFFF0000u), dkp[ds][2 * q + 1]);
+          }
+        }
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -779,14 +725,6 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         }
     }
     __builtin_amdgcn_wave_barrier();
-    // summary key gradient of the selecting rows: lane e: dk'[e] += ds^ q[e]
-    if (!own_rows) {
-      for (int rr = 0; rr < nr; ++rr) {
-        const float dsh = sm.dshv[e0 + rr];
-        dkb_lane = fmaf(dsh, bf(wv.qt[lane][rr]), dkb_lane);
-        db_acc += dsh;
-      }
-    }
     // dV += A^T dO, dK += dS^T Q over the tile's 32 rows (k dimension = rows)
     uint4 obf[4], qbf[4];
 #pragma unroll
@@ -809,8 +747,14 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
 
   for (int hh = 0; hh < G; ++hh) {
     const int h = g * G + hh;
-    float dkb_lane = 0.f;  // dk' / scale for feature `lane`
-    float db = 0.f;
+    // per-lane partial sums of dk' / scale (features 32 ds + 8 gl + j of the
+    // lane's rows) and of db'
+    float dkp[2][8];
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dkp[ds][j] = 0.f;
+    float dbp = 0.f;
     // own rows: the chunk's positions (causal), one 32-row tile per wavefront
     for (int x = t; x < kChunk; x += kKThreads) {
       const long long pos = min(key0 + x, (long long)dm.Tq - 1);
@@ -821,7 +765,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     __syncthreads();
     const int n_own = (int)min((long long)kChunk, dm.Tq - key0);
     for (int e0 = kTileRows * w; e0 < n_own; e0 += kTileRows * kKWaves)
-      run_tile(e0, min(kTileRows, n_own - e0), true, dkb_lane, db);
+      run_tile(e0, min(kTileRows, n_own - e0), true, dkp, dbp);
     __syncthreads();
     // rows that selected this chunk, ascending, in segments of the bitmap
     const uint32_t* bmw = bm + (((long long)b * dm.H + h) * NC + c) * words;
@@ -847,7 +791,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
       __syncthreads();
       const int n = list_n;
       // slot of the chunk in each row's selection (one vector read of the row's
-      // selections), its fusion weight alpha and its ds^
+      // selections), its fusion weight alpha and the row's D
       for (int e = t; e < n; e += kKThreads) {
         const long long r = sm.rows[e];
         int slot = 0;
@@ -867,16 +811,30 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
           slot = v.w == c ? k0 + 3 : slot;
         }
         sm.aux[e] = expf(score[r * Ksel + slot] - lse_tot[r]);
-        sm.dshv[e] = ws_dsh[r * Ksel + slot];
+        sm.dvl[e] = ws_D[r];
       }
       __syncthreads();
       for (int e0 = kTileRows * w; e0 < n; e0 += kTileRows * kKWaves)
-        run_tile(e0, min(kTileRows, n - e0), false, dkb_lane, db);
+        run_tile(e0, min(kTileRows, n - e0), false, dkp, dbp);
       __syncthreads();
     }
     // ---- summary and landmark backward of (chunk c, head h)
-    sm.dkb[w][lane] = dkb_lane;
-    if (lane == 0) sm.dbw[w] = db;
+    // sum the partials over the 16 rows (lanes col) of each lane group
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+#pragma unroll
+      for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dkp[ds][j] += __shfl_xor(dkp[ds][j], o, kLanes);
+      dbp += __shfl_xor(dbp, o, kLanes);
+    }
+    if (col == 0) {
+#pragma unroll
+      for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sm.dkb[w][32 * ds + 8 * gl + j] = dkp[ds][j];
+    }
+    if (lane == 0) sm.dbw[w] = dbp;
     __syncthreads();
     if (t < D)  // fixed order over the wavefronts
       sm.dkb[0][t] = (((sm.dkb[0][t] + sm.dkb[1][t]) + sm.dkb[2][t]) + sm.dkb[3][t]) * dm.scale;
@@ -988,7 +946,7 @@ size_t backward_mfma_ws_bytes(const Dims& dm) {
 bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void* V,
                        const void* Ql, const float* ksum, const float* ent, const float* lse_l,
                        const int32_t* idx, const float* score, const float* lse_tot,
-                       const void* dO, void* dQ, void* dK, void* dV, void* dQl, float* ws_dsh,
+                       const void* O, const void* dO, void* dQ, void* dK, void* dV, void* dQl,
                        float* ws_D, const uint32_t* bm, int words, void* ws_mfma, hipStream_t st,
                        hipError_t* err) {
   BPlan p;
@@ -1009,8 +967,8 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
   }
   hipLaunchKernelGGL(k_bwd_q, dim3(dm.B * p.nqb * dm.Hkv), dim3(kQThreads), p.smem, st, dm, p.R,
                      p.Rq, p.ncr, p.nqb, p.nct, Qh, Kh, Vh, Kt, bnd, ksum, idx, score, lse_tot,
-                     reinterpret_cast<const uint16_t*>(dO), reinterpret_cast<uint16_t*>(dQ),
-                     ws_dsh, ws_D);
+                     reinterpret_cast<const uint16_t*>(O), reinterpret_cast<const uint16_t*>(dO),
+                     reinterpret_cast<uint16_t*>(dQ), ws_D);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_kv_mfma),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(KSmem));
   if (e != hipSuccess) {
@@ -1019,7 +977,7 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
   }
   hipLaunchKernelGGL(k_bwd_kv_mfma, dim3(p.nct, dm.Hkv, dm.B), dim3(kKThreads), sizeof(KSmem), st, dm, Qh, Kh,
                      Vh, reinterpret_cast<const uint16_t*>(Ql), ksum, ent, lse_l, idx, score,
-                     lse_tot, reinterpret_cast<const uint16_t*>(dO), ws_dsh, ws_D, bm, words,
+                     lse_tot, reinterpret_cast<const uint16_t*>(dO), ws_D, bm, words,
                      reinterpret_cast<uint16_t*>(dK), reinterpret_cast<uint16_t*>(dV),
                      reinterpret_cast<uint16_t*>(dQl));
   *err = hipGetLastError();

@@ -136,15 +136,18 @@ hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K
  * sum(dO * O) through the inter-chunk softmax (scores and own log-mass), the
  * intra-chunk softmaxes, the scores (Q, ksum, ent) and the landmark softmax
  * (Ql, K). dK/dV sum over the query heads of each kv head. Inputs are the
- * forward's: Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot. Requires a
+ * forward's: Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot and its
+ * output O, which gives each row's D = dO . O (the weighted mean of dO . v
+ * over everything the row attends to). Requires a
  * prefill layout (q_pos0 == 0, Tq == Tkv, Tkv % S == 0). Deterministic: no
  * floating-point atomics.
  */
 hils_status hils_backward(const hils_dims* dims, const void* Q, const void* K, const void* V,
                           const void* Ql, const float* ksum, const float* ent,
                           const float* lse_l, const int32_t* idx, const float* score,
-                          const float* lse_tot, const void* dO, void* dQ, void* dK, void* dV,
-                          void* dQl, void* ws, size_t ws_bytes, hils_stream stream);
+                          const float* lse_tot, const void* O, const void* dO, void* dQ,
+                          void* dK, void* dV, void* dQl, void* ws, size_t ws_bytes,
+                          hils_stream stream);
 
 /* Static description of a status code. */
 const char* hils_status_string(hils_status status);

@@ -282,7 +282,7 @@ def gpu_train(w, x):
     t, f = gpu_forward(w, x)
     dO = dev(x["dO"], w.dtype)
     g = hsa.backward(t["Q"], t["K"], t["V"], t["Ql"], f["ksum"], f["ent"], f["lse_l"], f["idx"],
-                     f["score"], f["lse_tot"], dO, w.S)
+                     f["score"], f["lse_tot"], f["O"], dO, w.S)
     torch.cuda.synchronize()
     return f, g
 
