@@ -546,33 +546,77 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
 }
 
 // ------------------------------------------------------------------ key side
-// One workgroup per (chunk, kv head, batch); each wavefront takes every fourth
-// 32-row tile of the row list and keeps dK, dV for all 64 keys x 64 features in
-// registers; the four wavefronts' partial sums are added in a fixed order at
-// the end. Transposes go through wavefront-private LDS.
+// One workgroup per (chunk, kv head, batch) with four wavefronts. The chunk's
+// own 64 rows (two 32-row tiles) followed by the rows that selected it
+// (ascending) form a list of 32-row tiles; wavefront w takes tiles w, w + 4, ...
+// and keeps dK, dV for all 64 keys x 64 features in registers; the four partial
+// sums are added in a fixed order at the end. A tile's Q and dO rows and its
+// weights go to wavefront-private LDS in natural row-major order and come back
+// as MFMA operands with k along the rows through the LDS transpose read; the
+// next tile's rows are loaded while the current one is computed.
 constexpr int kKThreads = 256;
 constexpr int kKWaves = kKThreads / 64;
 constexpr int kTileRows = 32;
-constexpr int TP = kTileRows + 8;  // LDS pitch of transposed tiles (bf16)
-constexpr int kListMax = 2048;
+constexpr int TP = D + 8;  // LDS row pitch of 64-wide bf16 tiles
+// a list segment: the own rows (first segment) plus 64 bitmap words of rows
+constexpr int kListMax = kChunk + 64 * 32;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// LDS transpose read (ds_read_b64_tr_b16): in each group of 16 lanes, lane
+// 4j + a gives the address of four consecutive 16-bit elements and lane 4a + b
+// receives element b of lanes 4j + a, j = 0..3.
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  uint2 u;
+  __builtin_memcpy(&u, &r, 8);
+  return u;
+}
+// MFMA operand with k along the rows of a [32][TP] row-major LDS tile: lane
+// (c, g) gets m[8g + j][n0 + c], j = 0..7 (k-slot 8g + j = row 8g + j).
+__device__ __forceinline__ uint4 lds_kfrag(const uint16_t* m, int n0) {
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+  const uint16_t* p = m + (8 * g + (c >> 2)) * TP + n0 + 4 * (c & 3);
+  const uint2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * TP);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+// four floats to bf16, round to nearest even (packed hardware conversion)
+__device__ __forceinline__ uint2 pack4_bf16(const floatx4& v) {
+  const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  uint2 u;
+  __builtin_memcpy(&u, &h, 8);
+  return u;
+}
 
 struct KWave {
-  uint16_t qt[D][TP];       // Q^T of the tile
-  uint16_t ot[D][TP];       // dO^T of the tile
-  uint16_t at[kChunk][TP];  // value weights, transposed [key][row]
-  uint16_t dt[kChunk][TP];  // dS, transposed [key][row]
+  uint16_t qs[kTileRows][TP];   // Q rows of the tile
+  uint16_t os[kTileRows][TP];   // dO rows of the tile
+  uint16_t as[kTileRows][TP];   // value weights [row][key]
+  uint16_t dsm[kTileRows][TP];  // dS [row][key]
 };
 struct KSmem {
   KWave wv[kKWaves];
-  int rows[kListMax];    // row list segment: global row index
-  float aux[kListMax];   // alpha (selecting rows) or D (own rows)
-  float dvl[kListMax];   // D of the selecting rows
-  float dkb[kKWaves][D];  // per-wave dk' partial sums, then the total
+  uint16_t kc[kChunk][TP];  // the chunk's keys
+  int rows[kListMax];       // list segment: position of the row
+  float aux[kListMax];      // own rows: D; selecting rows: alpha
+  float dvl[kListMax];      // own rows: Lambda; selecting rows: D
+  float dkb[kKWaves][D];    // per-wave dk' partials, then the total
+  float dql[kKWaves][D];
   float dbw[kKWaves];
-  float sp[kChunk];      // p'_j
-  float sdp[kChunk];     // ds'_j
+  float qlv[D], kbv[D];
+  float sp[kChunk];         // p'_j
+  float sdp[kChunk];        // ds'_j
 };
 static_assert(sizeof(KSmem) <= 160 * 1024, "key-side LDS");
+static_assert(kListMax >= kChunk + kLanes * 32, "list segment capacity");
+static_assert(sizeof(KWave) >= kChunk * D * sizeof(float), "final reduction buffer");
+
+struct KTile {
+  uint4 qf[2][2], of[2][2];  // B operands: Q / dO of rows 16 hf + c, features 32 ds + 8g ..
+  float aux[2], dvr[2];
+  int rpos[2];
+};
 
 __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -590,12 +634,13 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 15, gl = lane >> 4;
   const int NC = dm.Tkv / dm.S, Ksel = dm.K, G = dm.G;
   const float scale2 = dm.scale * kLog2e;
+  const float inv_scale = 1.0f / dm.scale;
   const long long kv_stride = (long long)dm.Hkv * D;
   const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
   const long long key0 = (long long)c * kChunk;
   KWave& wv = sm.wv[w];
 
-  // the chunk's K and V rows as MFMA A fragments
+  // the chunk's K and V rows as MFMA A fragments, and K in LDS
   uint4 kf[KF], vf[KF];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
@@ -605,6 +650,11 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
       kf[kb * 2 + ds] = *reinterpret_cast<const uint4*>(K + off);
       vf[kb * 2 + ds] = *reinterpret_cast<const uint4*>(V + off);
     }
+  for (int x = t; x < kChunk * D / 8; x += kKThreads) {
+    const int j = x / (D / 8), c8 = x % (D / 8);
+    *reinterpret_cast<uint4*>(&sm.kc[j][c8 * 8]) =
+        *reinterpret_cast<const uint4*>(K + kv_base + (key0 + j) * kv_stride + c8 * 8);
+  }
   // dK / scale and dV: block [kb][fb] holds keys 16 kb + 4 gl + r x features 16 fb + col
   floatx4 dka[4][4], dva[4][4];
 #pragma unroll
@@ -612,43 +662,36 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) dka[kb][fb] = dva[kb][fb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // one 32-row tile of this wavefront: rows sm.rows[e0 .. e0 + nr)
-  auto run_tile = [&](int e0, int nr, bool own_rows, float (&dkp)[2][8], float& dbp) {
-    uint4 qf[2][2], of[2][2];
-    float aux[2], dvr[2];
-    int rpos[2];
+  long long row_base = 0;  // row index of position 0 of the current head
+  auto load_tile = [&](int e0, int nr, bool own_rows) {
+    KTile T;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const bool v = 16 * hf + col < nr;
       const int e = e0 + min(16 * hf + col, nr - 1);
-      const long long r = sm.rows[e];
+      const int pos = sm.rows[e];
+      const long long r = row_base + (long long)pos * dm.H;
 #pragma unroll
       for (int ds = 0; ds < 2; ++ds) {
-        qf[hf][ds] = *reinterpret_cast<const uint4*>(Q + r * D + 32 * ds + 8 * gl);
-        of[hf][ds] = *reinterpret_cast<const uint4*>(dO + r * D + 32 * ds + 8 * gl);
-        if (!v) qf[hf][ds] = of[hf][ds] = make_uint4(0, 0, 0, 0);
+        T.qf[hf][ds] = *reinterpret_cast<const uint4*>(Q + r * D + 32 * ds + 8 * gl);
+        T.of[hf][ds] = *reinterpret_cast<const uint4*>(dO + r * D + 32 * ds + 8 * gl);
       }
-      aux[hf] = v ? sm.aux[e] : 0.f;
-      dvr[hf] = own_rows ? 0.f : sm.dvl[e];
-      rpos[hf] = (int)((r / dm.H) % dm.Tq);
+      T.aux[hf] = v ? sm.aux[e] : 0.f;
+      T.dvr[hf] = sm.dvl[e];
+      T.rpos[hf] = v ? pos : -1;
     }
-    const float lam0 = own_rows ? lse_tot[sm.rows[e0 + min(col, nr - 1)]] : 0.f;
-    const float lam1 = own_rows ? lse_tot[sm.rows[e0 + min(16 + col, nr - 1)]] : 0.f;
-    // Q^T and dO^T of the tile from the fragments (this wavefront's LDS)
+    (void)own_rows;
+    return T;
+  };
+
+  // one 32-row tile; rows beyond nr get zero weights (their Q / dO are a valid row's)
+  auto compute_tile = [&](const KTile& T, bool own_rows, float (&dkp)[2][8], float& dbp) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int ds = 0; ds < 2; ++ds) {
-        const uint32_t qw[4] = {qf[hf][ds].x, qf[hf][ds].y, qf[hf][ds].z, qf[hf][ds].w};
-        const uint32_t ow[4] = {of[hf][ds].x, of[hf][ds].y, of[hf][ds].z, of[hf][ds].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = 32 * ds + 8 * gl + 2 * q;
-          wv.qt[e][16 * hf + col] = (uint16_t)(qw[q] & 0xFFFFu);
-          wv.qt[e + 1][16 * hf + col] = (uint16_t)(qw[q] >> 16);
-          wv.ot[e][16 * hf + col] = (uint16_t)(ow[q] & 0xFFFFu);
-          wv.ot[e + 1][16 * hf + col] = (uint16_t)(ow[q] >> 16);
-        }
+        *reinterpret_cast<uint4*>(&wv.qs[16 * hf + col][32 * ds + 8 * gl]) = T.qf[hf][ds];
+        *reinterpret_cast<uint4*>(&wv.os[16 * hf + col][32 * ds + 8 * gl]) = T.of[hf][ds];
       }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -658,20 +701,20 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         s[kb] = u[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ds = 0; ds < 2; ++ds) {
-          s[kb] = mfma(kf[kb * 2 + ds], qf[hf][ds], s[kb]);
-          u[kb] = mfma(vf[kb * 2 + ds], of[hf][ds], u[kb]);
+          s[kb] = mfma(kf[kb * 2 + ds], T.qf[hf][ds], s[kb]);
+          u[kb] = mfma(vf[kb * 2 + ds], T.of[hf][ds], u[kb]);
         }
       }
-      const bool v = 16 * hf + col < nr;
       floatx4 a[4], d[4];
       if (own_rows) {
-        const float lam2 = (hf ? lam1 : lam0) * kLog2e, Dr = aux[hf];
+        // w_j = exp(s_j - Lambda) over keys up to the row's position
+        const float lam2 = T.dvr[hf] * kLog2e, Dr = T.aux[hf];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const long long kp = key0 + 16 * kb + 4 * gl + r;
-            const float wj = (v && kp <= rpos[hf]) ? exp2f(s[kb][r] * scale2 - lam2) : 0.f;
+            const float wj = kp <= T.rpos[hf] ? __builtin_amdgcn_exp2f(s[kb][r] * scale2 - lam2) : 0.f;
             a[kb][r] = wj;
             d[kb][r] = wj * (u[kb][r] - Dr);
           }
@@ -687,13 +730,13 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            s[kb][r] = exp2f(s[kb][r] * scale2 - m);
+            s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r] * scale2 - m);
             z += s[kb][r];
             zu = fmaf(s[kb][r], u[kb][r], zu);
           }
         z = xsum_16_32(z);
         zu = xsum_16_32(zu);
-        const float iz = 1.0f / z, rc = zu * iz, al = v ? aux[hf] : 0.f;
+        const float iz = 1.0f / z, rc = zu * iz, al = T.aux[hf];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -703,11 +746,11 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
             d[kb][r] = p * (u[kb][r] - rc);
           }
         // ds^ = alpha (r - D): summary key and bias gradients of the row
-        const float dsh = al * (rc - dvr[hf]);
+        const float dsh = al * (rc - T.dvr[hf]);
         dbp += dsh;
 #pragma unroll
         for (int ds = 0; ds < 2; ++ds) {
-          const uint32_t qw[4] = {qf[hf][ds].x, qf[hf][ds].y, qf[hf][ds].z, qf[hf][ds].w};
+          const uint32_t qw[4] = {T.qf[hf][ds].x, T.qf[hf][ds].y, T.qf[hf][ds].z, T.qf[hf][ds].w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             dkp[ds][2 * q] = fmaf(dsh, __uint_as_float(qw[q] << 16), dkp[ds][2 * q]);
@@ -716,26 +759,23 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         }
       }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = 16 * kb + 4 * gl + r;
-          wv.at[key][16 * hf + col] = f32_to_bf16_bits(a[kb][r]);
-          wv.dt[key][16 * hf + col] = f32_to_bf16_bits(d[kb][r]);
-        }
+      for (int kb = 0; kb < 4; ++kb) {
+        *reinterpret_cast<uint2*>(&wv.as[16 * hf + col][16 * kb + 4 * gl]) = pack4_bf16(a[kb]);
+        *reinterpret_cast<uint2*>(&wv.dsm[16 * hf + col][16 * kb + 4 * gl]) = pack4_bf16(d[kb]);
+      }
     }
     __builtin_amdgcn_wave_barrier();
     // dV += A^T dO, dK += dS^T Q over the tile's 32 rows (k dimension = rows)
     uint4 obf[4], qbf[4];
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
-      obf[fb] = *reinterpret_cast<const uint4*>(&wv.ot[16 * fb + col][8 * gl]);
-      qbf[fb] = *reinterpret_cast<const uint4*>(&wv.qt[16 * fb + col][8 * gl]);
+      obf[fb] = lds_kfrag(&wv.os[0][0], 16 * fb);
+      qbf[fb] = lds_kfrag(&wv.qs[0][0], 16 * fb);
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const uint4 af = *reinterpret_cast<const uint4*>(&wv.at[16 * kb + col][8 * gl]);
-      const uint4 df = *reinterpret_cast<const uint4*>(&wv.dt[16 * kb + col][8 * gl]);
+      const uint4 af = lds_kfrag(&wv.as[0][0], 16 * kb);
+      const uint4 df = lds_kfrag(&wv.dsm[0][0], 16 * kb);
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) {
         dva[kb][fb] = mfma(af, obf[fb], dva[kb][fb]);
@@ -745,8 +785,10 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     __builtin_amdgcn_wave_barrier();
   };
 
+  const int first_word = (int)((key0 + kChunk) / 32);
   for (int hh = 0; hh < G; ++hh) {
     const int h = g * G + hh;
+    row_base = (long long)b * dm.Tq * dm.H + h;
     // per-lane partial sums of dk' / scale (features 32 ds + 8 gl + j of the
     // lane's rows) and of db'
     float dkp[2][8];
@@ -755,21 +797,11 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
 #pragma unroll
       for (int j = 0; j < 8; ++j) dkp[ds][j] = 0.f;
     float dbp = 0.f;
-    // own rows: the chunk's positions (causal), one 32-row tile per wavefront
-    for (int x = t; x < kChunk; x += kKThreads) {
-      const long long pos = min(key0 + x, (long long)dm.Tq - 1);
-      const long long r = ((long long)b * dm.Tq + pos) * dm.H + h;
-      sm.rows[x] = (int)r;
-      sm.aux[x] = ws_D[r];
-    }
-    __syncthreads();
-    const int n_own = (int)min((long long)kChunk, dm.Tq - key0);
-    for (int e0 = kTileRows * w; e0 < n_own; e0 += kTileRows * kKWaves)
-      run_tile(e0, min(kTileRows, n_own - e0), true, dkp, dbp);
-    __syncthreads();
-    // rows that selected this chunk, ascending, in segments of the bitmap
     const uint32_t* bmw = bm + (((long long)b * dm.H + h) * NC + c) * words;
-    for (int w0 = (int)((key0 + kChunk) / 32); w0 < words; w0 += kLanes) {
+    for (int w0 = first_word;; w0 += kLanes) {
+      // list segment: the chunk's own rows first (first segment only), then the
+      // rows whose bitmap bits lie in words w0 .. w0 + 63, ascending
+      const int base = w0 == first_word ? kChunk : 0;
       if (w == 0) {
         const uint32_t word = (w0 + lane < words) ? bmw[w0 + lane] : 0u;
         const int cnt = __popc(word);
@@ -779,45 +811,68 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
           const int y = __shfl_up(incl, o, kLanes);
           if (lane >= o) incl += y;
         }
-        int p = incl - cnt;
+        int p = base + incl - cnt;
         uint32_t bits = word;
         while (bits) {
           const int bit = __ffs(bits) - 1;
           bits &= bits - 1;
-          sm.rows[p++] = (int)(((long long)b * dm.Tq + (w0 + lane) * 32 + bit) * dm.H + h);
+          sm.rows[p++] = (w0 + lane) * 32 + bit;
         }
-        if (lane == kLanes - 1) list_n = incl;
+        if (lane == kLanes - 1) list_n = base + incl;
       }
+      if (base > 0 && t < kChunk) sm.rows[t] = (int)key0 + t;
       __syncthreads();
       const int n = list_n;
-      // slot of the chunk in each row's selection (one vector read of the row's
-      // selections), its fusion weight alpha and the row's D
+      // per row: own rows D and Lambda; selecting rows alpha (slot of the chunk
+      // in the row's selection, one vector read) and D
+      // (selection indices and scores read together, no dependent load)
       for (int e = t; e < n; e += kKThreads) {
-        const long long r = sm.rows[e];
-        int slot = 0;
+        const long long r = row_base + (long long)sm.rows[e] * dm.H;
+        const float Dr = ws_D[r], lam = lse_tot[r];
+        float sc = 0.f;
         for (int k0 = 0; k0 < Ksel; k0 += 4) {
           int4 v;
-          if (((Ksel & 3) == 0)) {
+          float4 f;
+          if ((Ksel & 3) == 0) {
             v = *reinterpret_cast<const int4*>(idx + r * Ksel + k0);
+            f = *reinterpret_cast<const float4*>(score + r * Ksel + k0);
           } else {
             v.x = idx[r * Ksel + k0];
             v.y = k0 + 1 < Ksel ? idx[r * Ksel + k0 + 1] : -1;
             v.z = k0 + 2 < Ksel ? idx[r * Ksel + k0 + 2] : -1;
             v.w = k0 + 3 < Ksel ? idx[r * Ksel + k0 + 3] : -1;
+            f.x = score[r * Ksel + k0];
+            f.y = k0 + 1 < Ksel ? score[r * Ksel + k0 + 1] : 0.f;
+            f.z = k0 + 2 < Ksel ? score[r * Ksel + k0 + 2] : 0.f;
+            f.w = k0 + 3 < Ksel ? score[r * Ksel + k0 + 3] : 0.f;
           }
-          slot = v.x == c ? k0 : slot;
-          slot = v.y == c ? k0 + 1 : slot;
-          slot = v.z == c ? k0 + 2 : slot;
-          slot = v.w == c ? k0 + 3 : slot;
+          sc = v.x == c ? f.x : sc;
+          sc = v.y == c ? f.y : sc;
+          sc = v.z == c ? f.z : sc;
+          sc = v.w == c ? f.w : sc;
         }
-        sm.aux[e] = expf(score[r * Ksel + slot] - lse_tot[r]);
-        sm.dvl[e] = ws_D[r];
+        sm.aux[e] = e < base ? Dr : expf(sc - lam);
+        sm.dvl[e] = e < base ? lam : Dr;
       }
       __syncthreads();
-      for (int e0 = kTileRows * w; e0 < n; e0 += kTileRows * kKWaves)
-        run_tile(e0, min(kTileRows, n - e0), false, dkp, dbp);
+      int e0 = kTileRows * w;
+      if (e0 < n) {
+        KTile cur = load_tile(e0, min(kTileRows, n - e0), e0 < base);
+        for (;;) {
+          const int e1 = e0 + kTileRows * kKWaves;
+          const bool more = e1 < n;
+          const int ep = more ? e1 : e0;
+          const KTile nxt = load_tile(ep, min(kTileRows, n - ep), ep < base);
+          compute_tile(cur, e0 < base, dkp, dbp);
+          if (!more) break;
+          cur = nxt;
+          e0 = e1;
+        }
+      }
       __syncthreads();
+      if (w0 + kLanes >= words) break;
     }
+
     // ---- summary and landmark backward of (chunk c, head h)
     // sum the partials over the 16 rows (lanes col) of each lane group
 #pragma unroll
@@ -836,19 +891,26 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     }
     if (lane == 0) sm.dbw[w] = dbp;
     __syncthreads();
-    if (t < D)  // fixed order over the wavefronts
-      sm.dkb[0][t] = (((sm.dkb[0][t] + sm.dkb[1][t]) + sm.dkb[2][t]) + sm.dkb[3][t]) * dm.scale;
-    __syncthreads();
     const long long sidx = ((long long)b * dm.NCcap + c) * dm.H + h;
+    if (t < D) {  // fixed order over the wavefronts
+      sm.dkb[0][t] = (((sm.dkb[0][t] + sm.dkb[1][t]) + sm.dkb[2][t]) + sm.dkb[3][t]) * dm.scale;
+      sm.qlv[t] = bf(Ql[sidx * D + t]);
+      sm.kbv[t] = ksum[sidx * D + t];
+    }
+    __syncthreads();
     if (w == 0) {  // lane j: key j of the chunk
-      const uint16_t* kr = K + kv_base + (key0 + lane) * kv_stride;
-      const uint16_t* ql = Ql + sidx * D;
-      const float* kbar = ksum + sidx * D;
       float s1 = 0.f, t1 = 0.f;
-      for (int e = 0; e < D; ++e) {
-        const float kje = bf(kr[e]);
-        s1 = fmaf(bf(ql[e]), kje, s1);
-        t1 = fmaf(sm.dkb[0][e], kje - kbar[e], t1);
+#pragma unroll
+      for (int e8 = 0; e8 < D / 8; ++e8) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(&sm.kc[lane][8 * e8]);
+        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = 8 * e8 + 2 * q;
+          const float k0v = __uint_as_float(kw[q] << 16), k1v = __uint_as_float(kw[q] & 0xFFFF0000u);
+          s1 = fmaf(sm.qlv[e], k0v, fmaf(sm.qlv[e + 1], k1v, s1));
+          t1 = fmaf(sm.dkb[0][e], k0v - sm.kbv[e], fmaf(sm.dkb[0][e + 1], k1v - sm.kbv[e + 1], t1));
+        }
       }
       s1 *= dm.scale;
       const float Lp = lse_l[sidx], bias = ent[sidx];
@@ -858,52 +920,61 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
       sm.sdp[lane] = p1 * (t1 + dbv * (Lp - s1 - bias));
     }
     __syncthreads();
-    if (t < D) {  // dQl = scale sum_j ds'_j k_j
+    {  // dQl = scale sum_j ds'_j k_j: wave w sums keys 16 w .. 16 w + 15
       float acc = 0.f;
-      for (int j = 0; j < kChunk; ++j) acc = fmaf(sm.sdp[j], bf(K[kv_base + (key0 + j) * kv_stride + t]), acc);
-      dQl[sidx * D + t] = f32_to_bf16_bits(acc * dm.scale);
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) acc = fmaf(sm.sdp[16 * w + jj], bf(sm.kc[16 * w + jj][lane]), acc);
+      sm.dql[w][lane] = acc;
     }
+    __syncthreads();
+    if (t < D)
+      dQl[sidx * D + t] = f32_to_bf16_bits(
+          (((sm.dql[0][t] + sm.dql[1][t]) + sm.dql[2][t]) + sm.dql[3][t]) * dm.scale);
     // dK_j += p'_j dk' + scale ds'_j Ql: added once, by wavefront 0's accumulators
     if (w == 0) {
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) {
         const float dk_e = sm.dkb[0][16 * fb + col];
-        const float ql_e = bf(Ql[sidx * D + 16 * fb + col]);
+        const float ql_e = sm.qlv[16 * fb + col];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = 16 * kb + 4 * gl + r;
-            dka[kb][fb][r] += (sm.sp[j] * dk_e) / dm.scale + sm.sdp[j] * ql_e;
+            dka[kb][fb][r] += sm.sp[j] * dk_e * inv_scale + sm.sdp[j] * ql_e;
           }
       }
     }
     __syncthreads();
   }
 
-  // ---- dK = scale * (sum of the wavefronts' accumulators), dV; fixed order
-  float* red = reinterpret_cast<float*>(&sm.wv[0]);  // [64 keys][64 features], reused
+  // ---- dK = scale * (sum of the wavefronts' accumulators), dV; each wavefront
+  // writes its partial sums to its own LDS region, then a fixed-order sum
+  float* red = reinterpret_cast<float*>(&sm.wv[w]);  // [64 keys][64 features]
   for (int pass = 0; pass < 2; ++pass) {
-    for (int ww = 0; ww < kKWaves; ++ww) {
-      if (w == ww) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int fb = 0; fb < 4; ++fb)
+      for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int o = (16 * kb + 4 * gl + r) * D + 16 * fb + col;
-              const float v = pass == 0 ? dka[kb][fb][r] : dva[kb][fb][r];
-              red[o] = ww == 0 ? v : red[o] + v;
-            }
-      }
-      __syncthreads();
-    }
+        for (int r = 0; r < 4; ++r)
+          red[(16 * kb + 4 * gl + r) * D + 16 * fb + col] = pass == 0 ? dka[kb][fb][r] : dva[kb][fb][r];
+    __syncthreads();
+    const float* r0 = reinterpret_cast<const float*>(&sm.wv[0]);
+    const float* r1 = reinterpret_cast<const float*>(&sm.wv[1]);
+    const float* r2 = reinterpret_cast<const float*>(&sm.wv[2]);
+    const float* r3 = reinterpret_cast<const float*>(&sm.wv[3]);
     uint16_t* out = pass == 0 ? dK : dV;
     const float sc = pass == 0 ? dm.scale : 1.0f;
-    for (int x = t; x < kChunk * D; x += kKThreads) {
-      const int j = x / D, e = x % D;
-      out[kv_base + (key0 + j) * kv_stride + e] = f32_to_bf16_bits(red[x] * sc);
+    for (int x = t; x < kChunk * D / 4; x += kKThreads) {
+      const int j = x / (D / 4), e = 4 * (x % (D / 4)), o = j * D + e;
+      const float4 a0 = *reinterpret_cast<const float4*>(r0 + o);
+      const float4 a1 = *reinterpret_cast<const float4*>(r1 + o);
+      const float4 a2 = *reinterpret_cast<const float4*>(r2 + o);
+      const float4 a3 = *reinterpret_cast<const float4*>(r3 + o);
+      const floatx4 v = {(((a0.x + a1.x) + a2.x) + a3.x) * sc, (((a0.y + a1.y) + a2.y) + a3.y) * sc,
+                         (((a0.z + a1.z) + a2.z) + a3.z) * sc, (((a0.w + a1.w) + a2.w) + a3.w) * sc};
+      *reinterpret_cast<uint2*>(out + kv_base + (key0 + j) * kv_stride + e) = pack4_bf16(v);
     }
     __syncthreads();
   }
