@@ -427,6 +427,10 @@ hipError_t launch_t(const Dims& dm, const void* Q, const void* K, const void* V,
   float* Dr = reinterpret_cast<float*>(base + L.dr);
   uint32_t* bm = reinterpret_cast<uint32_t*>(base + L.bitmap);
   const int NC = dm.Tkv / dm.S;
+  hipError_t err = hipSuccess;
+  if (backward_mfma_try(dm, Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, dQ, dK,
+                        dV, dQl, Dr, base + L.mfma, st, &err))
+    return err;
   // words per bitmap block: as many as 64 KiB of LDS holds, at most 16
   int wpw = 16;
   while (wpw > 1 && (size_t)NC * wpw * 4 > 65536) wpw /= 2;
@@ -438,10 +442,6 @@ hipError_t launch_t(const Dims& dm, const void* Q, const void* K, const void* V,
     hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, bm, nbm);
     hipLaunchKernelGGL(k_sel_bitmap, dim3(1024), dim3(256), 0, st, dm, idx, bm, L.words);
   }
-  hipError_t err = hipSuccess;
-  if (backward_mfma_try(dm, Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, dQ, dK,
-                        dV, dQl, Dr, bm, L.words, base + L.mfma, st, &err))
-    return err;
   hipLaunchKernelGGL((k_bwd_rows<BF16, D>), dim3((dm.Tq + 3) / 4, dm.H, dm.B), dim3(256), 0, st,
                      dm, Q, K, V, ksum, idx, score, lse_tot, dO, dQ, dsh, Dr);
   hipLaunchKernelGGL((k_bwd_kv<BF16, D>), dim3(NC, dm.Hkv, dm.B), dim3(256), 0, st, dm, Q, K, V,

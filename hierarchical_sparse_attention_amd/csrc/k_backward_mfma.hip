@@ -545,6 +545,117 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
   }
 }
 
+// ------------------------------------------------------------------ selection lists
+// For every (b, h, chunk c): the rows that selected c (positions ascending) with
+// their fusion weight alpha = exp(s^ - Lambda) and D, stored contiguously, so
+// that the key side reads its rows' data in one coalesced pass. Built in three
+// deterministic passes over blocks of kLBlk positions: per-block counts, an
+// exclusive scan per (b, h) in (chunk, block) order, and a fill that ranks each
+// selecting position within its block by popcounts of a block bitmap.
+constexpr int kLBlk = 512;  // positions per block (16 bitmap words)
+
+__global__ __launch_bounds__(256) void k_sel_count(Dims dm, int nblk, const int32_t* __restrict__ idx,
+                                                   int* __restrict__ cnt) {
+  extern __shared__ int lcnt[];  // [NC]
+  const int NC = dm.Tkv / dm.S;
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  for (int x = threadIdx.x; x < NC; x += blockDim.x) lcnt[x] = 0;
+  __syncthreads();
+  const int i0 = blk * kLBlk, ni = min(kLBlk, dm.Tq - i0);
+  for (int x = threadIdx.x; x < ni * dm.K; x += blockDim.x) {
+    const int i = i0 + x / dm.K, k = x % dm.K;
+    const int c = idx[(((long long)b * dm.Tq + i) * dm.H + h) * dm.K + k];
+    if (c >= 0 && c < (int)((dm.q_pos0 + i) / dm.S) && c < NC) atomicAdd(&lcnt[c], 1);
+  }
+  __syncthreads();
+  int* out = cnt + ((long long)b * dm.H + h) * NC * nblk;
+  for (int c = threadIdx.x; c < NC; c += blockDim.x) out[(long long)c * nblk + blk] = lcnt[c];
+}
+
+// In place: cnt[b][h][c][blk] -> offset of the block's entries of chunk c in the
+// (b, h) list space; lstart / llen per (b, h, c).
+__global__ __launch_bounds__(256) void k_sel_scan(Dims dm, int nblk, int* __restrict__ cnt,
+                                                  int* __restrict__ lstart, int* __restrict__ llen) {
+  __shared__ int wtot[4];
+  const int NC = dm.Tkv / dm.S;
+  const long long bh = (long long)blockIdx.y * dm.H + blockIdx.x;
+  int* a = cnt + bh * NC * nblk;
+  const int n = NC * nblk;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int seg = (n + 255) / 256;
+  const int lo = min(n, t * seg), hi = min(n, lo + seg);
+  int s = 0;
+  for (int x = lo; x < hi; ++x) s += a[x];
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wtot[w] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    before += x < w ? wtot[x] : 0;
+    total += wtot[x];
+  }
+  int run = before + incl - s;
+  for (int x = lo; x < hi; ++x) {
+    const int v = a[x];
+    a[x] = run;
+    run += v;
+  }
+  __syncthreads();
+  for (int c = t; c < NC; c += 256) {
+    const int st = a[(long long)c * nblk];
+    const int en = c + 1 < NC ? a[(long long)(c + 1) * nblk] : total;
+    lstart[bh * NC + c] = st;
+    llen[bh * NC + c] = en - st;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32_t* __restrict__ idx,
+                                                  const float* __restrict__ score,
+                                                  const float* __restrict__ lse_tot,
+                                                  const float* __restrict__ ws_D,
+                                                  const int* __restrict__ off,
+                                                  int* __restrict__ e_pos, float* __restrict__ e_alpha,
+                                                  float* __restrict__ e_d) {
+  extern __shared__ uint32_t lfill[];
+  const int NC = dm.Tkv / dm.S;
+  constexpr int W = kLBlk / 32;
+  uint32_t* lb = lfill;                                   // [NC][W] bitmap of the block
+  int* lo = reinterpret_cast<int*>(lfill + (size_t)NC * W);  // [NC] entry offsets
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const long long bh = (long long)b * dm.H + h;
+  for (int x = threadIdx.x; x < NC * W; x += blockDim.x) lb[x] = 0u;
+  for (int c = threadIdx.x; c < NC; c += blockDim.x) lo[c] = off[(bh * NC + c) * nblk + blk];
+  __syncthreads();
+  const int i0 = blk * kLBlk, ni = min(kLBlk, dm.Tq - i0);
+  for (int x = threadIdx.x; x < ni * dm.K; x += blockDim.x) {
+    const int ii = x / dm.K, k = x % dm.K, i = i0 + ii;
+    const int c = idx[(((long long)b * dm.Tq + i) * dm.H + h) * dm.K + k];
+    if (c >= 0 && c < (int)((dm.q_pos0 + i) / dm.S) && c < NC)
+      atomicOr(&lb[c * W + ii / 32], 1u << (ii % 32));
+  }
+  __syncthreads();
+  const long long ebase = bh * (long long)dm.Tq * dm.K;
+  for (int x = threadIdx.x; x < ni * dm.K; x += blockDim.x) {
+    const int ii = x / dm.K, k = x % dm.K, i = i0 + ii;
+    const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
+    const int c = idx[r * dm.K + k];
+    if (c < 0 || c >= (int)((dm.q_pos0 + i) / dm.S) || c >= NC) continue;
+    const int wd = ii / 32;
+    int rank = __popc(lb[c * W + wd] & ((1u << (ii % 32)) - 1u));
+    for (int ww = 0; ww < wd; ++ww) rank += __popc(lb[c * W + ww]);
+    const long long e = ebase + lo[c] + rank;
+    e_pos[e] = i;
+    e_alpha[e] = expf(score[r * dm.K + k] - lse_tot[r]);
+    e_d[e] = ws_D[r];
+  }
+}
+
 // ------------------------------------------------------------------ key side
 // One workgroup per (chunk, kv head, batch) with four wavefronts. The chunk's
 // own 64 rows (two 32-row tiles) followed by the rows that selected it
@@ -557,8 +668,9 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
 constexpr int kKThreads = 256;
 constexpr int kKWaves = kKThreads / 64;
 constexpr int kTileRows = 32;
-constexpr int TP = D + 8;  // LDS row pitch of 64-wide bf16 tiles
-// a list segment: the own rows (first segment) plus 64 bitmap words of rows
+constexpr int TP = D + 8;       // LDS row pitch of 64-wide bf16 tiles
+constexpr int TPD = D + 16;     // dS tile: keys, then ds^ in column D, zeros up to D + 15
+// a list segment: the own rows (first segment) plus up to 2048 selecting rows
 constexpr int kListMax = kChunk + 64 * 32;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -572,12 +684,13 @@ __device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
   __builtin_memcpy(&u, &r, 8);
   return u;
 }
-// MFMA operand with k along the rows of a [32][TP] row-major LDS tile: lane
+// MFMA operand with k along the rows of a [32][P] row-major LDS tile: lane
 // (c, g) gets m[8g + j][n0 + c], j = 0..7 (k-slot 8g + j = row 8g + j).
+template <int P>
 __device__ __forceinline__ uint4 lds_kfrag(const uint16_t* m, int n0) {
   const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
-  const uint16_t* p = m + (8 * g + (c >> 2)) * TP + n0 + 4 * (c & 3);
-  const uint2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * TP);
+  const uint16_t* p = m + (8 * g + (c >> 2)) * P + n0 + 4 * (c & 3);
+  const uint2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * P);
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -593,7 +706,7 @@ struct KWave {
   uint16_t qs[kTileRows][TP];   // Q rows of the tile
   uint16_t os[kTileRows][TP];   // dO rows of the tile
   uint16_t as[kTileRows][TP];   // value weights [row][key]
-  uint16_t dsm[kTileRows][TP];  // dS [row][key]
+  uint16_t dsm[kTileRows][TPD]; // dS [row][key], ds^ of the row in column D
 };
 struct KSmem {
   KWave wv[kKWaves];
@@ -609,7 +722,6 @@ struct KSmem {
   float sdp[kChunk];        // ds'_j
 };
 static_assert(sizeof(KSmem) <= 160 * 1024, "key-side LDS");
-static_assert(kListMax >= kChunk + kLanes * 32, "list segment capacity");
 static_assert(sizeof(KWave) >= kChunk * D * sizeof(float), "final reduction buffer");
 
 struct KTile {
@@ -625,14 +737,14 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     const float* __restrict__ lse_l, const int32_t* __restrict__ idx,
     const float* __restrict__ score, const float* __restrict__ lse_tot,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws_D,
-    const uint32_t* __restrict__ bm, int words,
+    const int* __restrict__ lstart, const int* __restrict__ llen, const int* __restrict__ e_pos,
+    const float* __restrict__ e_alpha, const float* __restrict__ e_d,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, uint16_t* __restrict__ dQl) {
   extern __shared__ __align__(16) char smem_raw[];
   KSmem& sm = *reinterpret_cast<KSmem*>(smem_raw);
-  __shared__ int list_n;
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 15, gl = lane >> 4;
-  const int NC = dm.Tkv / dm.S, Ksel = dm.K, G = dm.G;
+  const int NC = dm.Tkv / dm.S, G = dm.G;
   const float scale2 = dm.scale * kLog2e;
   const float inv_scale = 1.0f / dm.scale;
   const long long kv_stride = (long long)dm.Hkv * D;
@@ -655,6 +767,8 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     *reinterpret_cast<uint4*>(&sm.kc[j][c8 * 8]) =
         *reinterpret_cast<const uint4*>(K + kv_base + (key0 + j) * kv_stride + c8 * 8);
   }
+  // columns D + 1 .. D + 15 of the dS tiles stay zero
+  for (int x = lane; x < kTileRows * 15; x += kLanes) wv.dsm[x / 15][D + 1 + x % 15] = 0;
   // dK / scale and dV: block [kb][fb] holds keys 16 kb + 4 gl + r x features 16 fb + col
   floatx4 dka[4][4], dva[4][4];
 #pragma unroll
@@ -685,7 +799,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
   };
 
   // one 32-row tile; rows beyond nr get zero weights (their Q / dO are a valid row's)
-  auto compute_tile = [&](const KTile& T, bool own_rows, float (&dkp)[2][8], float& dbp) {
+  auto compute_tile = [&](const KTile& T, bool own_rows, floatx4 (&dkq)[4], float& dbp) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -706,6 +820,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         }
       }
       floatx4 a[4], d[4];
+      float dsh = 0.f;
       if (own_rows) {
         // w_j = exp(s_j - Lambda) over keys up to the row's position
         const float lam2 = T.dvr[hf] * kLog2e, Dr = T.aux[hf];
@@ -713,8 +828,8 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const long long kp = key0 + 16 * kb + 4 * gl + r;
-            const float wj = kp <= T.rpos[hf] ? __builtin_amdgcn_exp2f(s[kb][r] * scale2 - lam2) : 0.f;
+            const int kp = (int)key0 + 16 * kb + 4 * gl + r;
+            const float wj = kp <= T.rpos[hf] ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale2, -lam2)) : 0.f;
             a[kb][r] = wj;
             d[kb][r] = wj * (u[kb][r] - Dr);
           }
@@ -722,42 +837,33 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         float m = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) m = fmaxf(m, s[kb][r] * scale2);
-        m = xmax_16_32(m);
+          m = fmaxf(m, fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3])));
+        m = xmax_16_32(m) * scale2;  // scale2 > 0
         float z = 0.f, zu = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r] * scale2 - m);
+            s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale2, -m));
             z += s[kb][r];
             zu = fmaf(s[kb][r], u[kb][r], zu);
           }
         z = xsum_16_32(z);
         zu = xsum_16_32(zu);
-        const float iz = 1.0f / z, rc = zu * iz, al = T.aux[hf];
+        const float iz = 1.0f / z, rc = zu * iz, al = T.aux[hf], cf = al * iz;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = al * s[kb][r] * iz;
+            const float p = cf * s[kb][r];
             a[kb][r] = p;
             d[kb][r] = p * (u[kb][r] - rc);
           }
-        // ds^ = alpha (r - D): summary key and bias gradients of the row
-        const float dsh = al * (rc - T.dvr[hf]);
+        // ds^ = alpha (r - D) of the row: db' here, dk' through the dS tile
+        dsh = al * (rc - T.dvr[hf]);
         dbp += dsh;
-#pragma unroll
-        for (int ds = 0; ds < 2; ++ds) {
-          const uint32_t qw[4] = {T.qf[hf][ds].x, T.qf[hf][ds].y, T.qf[hf][ds].z, T.qf[hf][ds].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            dkp[ds][2 * q] = fmaf(dsh, __uint_as_float(qw[q] << 16), dkp[ds][2 * q]);
-            dkp[ds][2 * q + 1] = fmaf(dsh, __uint_as_float(qw[q] & 0xFFFF0000u), dkp[ds][2 * q + 1]);
-          }
-        }
       }
+      if (gl == 0) wv.dsm[16 * hf + col][D] = __builtin_bit_cast(uint16_t, (__bf16)dsh);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         *reinterpret_cast<uint2*>(&wv.as[16 * hf + col][16 * kb + 4 * gl]) = pack4_bf16(a[kb]);
@@ -769,90 +875,57 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     uint4 obf[4], qbf[4];
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
-      obf[fb] = lds_kfrag(&wv.os[0][0], 16 * fb);
-      qbf[fb] = lds_kfrag(&wv.qs[0][0], 16 * fb);
+      obf[fb] = lds_kfrag<TP>(&wv.os[0][0], 16 * fb);
+      qbf[fb] = lds_kfrag<TP>(&wv.qs[0][0], 16 * fb);
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const uint4 af = lds_kfrag(&wv.as[0][0], 16 * kb);
-      const uint4 df = lds_kfrag(&wv.dsm[0][0], 16 * kb);
+      const uint4 af = lds_kfrag<TP>(&wv.as[0][0], 16 * kb);
+      const uint4 df = lds_kfrag<TPD>(&wv.dsm[0][0], 16 * kb);
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) {
         dva[kb][fb] = mfma(af, obf[fb], dva[kb][fb]);
         dka[kb][fb] = mfma(df, qbf[fb], dka[kb][fb]);
       }
     }
+    // dk' / scale += sum over the rows of ds^ q (row 0 of this product)
+    {
+      const uint4 hf5 = lds_kfrag<TPD>(&wv.dsm[0][0], D);
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) dkq[fb] = mfma(hf5, qbf[fb], dkq[fb]);
+    }
     __builtin_amdgcn_wave_barrier();
   };
 
-  const int first_word = (int)((key0 + kChunk) / 32);
   for (int hh = 0; hh < G; ++hh) {
     const int h = g * G + hh;
     row_base = (long long)b * dm.Tq * dm.H + h;
-    // per-lane partial sums of dk' / scale (features 32 ds + 8 gl + j of the
-    // lane's rows) and of db'
-    float dkp[2][8];
+    // dk' / scale (lane (col, 0) element 0 of block fb: feature 16 fb + col)
+    // and the lane's partial sum of db'
+    floatx4 dkq[4];
 #pragma unroll
-    for (int ds = 0; ds < 2; ++ds)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dkp[ds][j] = 0.f;
+    for (int fb = 0; fb < 4; ++fb) dkq[fb] = floatx4{0.f, 0.f, 0.f, 0.f};
     float dbp = 0.f;
-    const uint32_t* bmw = bm + (((long long)b * dm.H + h) * NC + c) * words;
-    for (int w0 = first_word;; w0 += kLanes) {
-      // list segment: the chunk's own rows first (first segment only), then the
-      // rows whose bitmap bits lie in words w0 .. w0 + 63, ascending
-      const int base = w0 == first_word ? kChunk : 0;
-      if (w == 0) {
-        const uint32_t word = (w0 + lane < words) ? bmw[w0 + lane] : 0u;
-        const int cnt = __popc(word);
-        int incl = cnt;
-#pragma unroll
-        for (int o = 1; o < kLanes; o <<= 1) {
-          const int y = __shfl_up(incl, o, kLanes);
-          if (lane >= o) incl += y;
-        }
-        int p = base + incl - cnt;
-        uint32_t bits = word;
-        while (bits) {
-          const int bit = __ffs(bits) - 1;
-          bits &= bits - 1;
-          sm.rows[p++] = (w0 + lane) * 32 + bit;
-        }
-        if (lane == kLanes - 1) list_n = base + incl;
+    const long long bh = (long long)b * dm.H + h;
+    const int LN = llen[bh * NC + c];
+    const long long lsrc = bh * (long long)dm.Tq * dm.K + lstart[bh * NC + c];
+    constexpr int kSeg = kListMax - kChunk;
+    for (int s0 = 0;; s0 += kSeg) {
+      // list segment: the chunk's own rows first (first segment only), then
+      // selecting rows s0 .. s0 + kSeg of the chunk's list
+      const int base = s0 == 0 ? kChunk : 0;
+      const int ns = min(kSeg, LN - s0);
+      const int n = base + ns;
+      if (base > 0 && t < kChunk) {
+        const long long r = row_base + (key0 + t) * dm.H;
+        sm.rows[t] = (int)key0 + t;
+        sm.aux[t] = ws_D[r];
+        sm.dvl[t] = lse_tot[r];
       }
-      if (base > 0 && t < kChunk) sm.rows[t] = (int)key0 + t;
-      __syncthreads();
-      const int n = list_n;
-      // per row: own rows D and Lambda; selecting rows alpha (slot of the chunk
-      // in the row's selection, one vector read) and D
-      // (selection indices and scores read together, no dependent load)
-      for (int e = t; e < n; e += kKThreads) {
-        const long long r = row_base + (long long)sm.rows[e] * dm.H;
-        const float Dr = ws_D[r], lam = lse_tot[r];
-        float sc = 0.f;
-        for (int k0 = 0; k0 < Ksel; k0 += 4) {
-          int4 v;
-          float4 f;
-          if ((Ksel & 3) == 0) {
-            v = *reinterpret_cast<const int4*>(idx + r * Ksel + k0);
-            f = *reinterpret_cast<const float4*>(score + r * Ksel + k0);
-          } else {
-            v.x = idx[r * Ksel + k0];
-            v.y = k0 + 1 < Ksel ? idx[r * Ksel + k0 + 1] : -1;
-            v.z = k0 + 2 < Ksel ? idx[r * Ksel + k0 + 2] : -1;
-            v.w = k0 + 3 < Ksel ? idx[r * Ksel + k0 + 3] : -1;
-            f.x = score[r * Ksel + k0];
-            f.y = k0 + 1 < Ksel ? score[r * Ksel + k0 + 1] : 0.f;
-            f.z = k0 + 2 < Ksel ? score[r * Ksel + k0 + 2] : 0.f;
-            f.w = k0 + 3 < Ksel ? score[r * Ksel + k0 + 3] : 0.f;
-          }
-          sc = v.x == c ? f.x : sc;
-          sc = v.y == c ? f.y : sc;
-          sc = v.z == c ? f.z : sc;
-          sc = v.w == c ? f.w : sc;
-        }
-        sm.aux[e] = e < base ? Dr : expf(sc - lam);
-        sm.dvl[e] = e < base ? lam : Dr;
+      for (int e = t; e < ns; e += kKThreads) {
+        sm.rows[base + e] = e_pos[lsrc + s0 + e];
+        sm.aux[base + e] = e_alpha[lsrc + s0 + e];
+        sm.dvl[base + e] = e_d[lsrc + s0 + e];
       }
       __syncthreads();
       int e0 = kTileRows * w;
@@ -863,31 +936,23 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
           const bool more = e1 < n;
           const int ep = more ? e1 : e0;
           const KTile nxt = load_tile(ep, min(kTileRows, n - ep), ep < base);
-          compute_tile(cur, e0 < base, dkp, dbp);
+          compute_tile(cur, e0 < base, dkq, dbp);
           if (!more) break;
           cur = nxt;
           e0 = e1;
         }
       }
       __syncthreads();
-      if (w0 + kLanes >= words) break;
+      if (s0 + kSeg >= LN) break;
     }
 
     // ---- summary and landmark backward of (chunk c, head h)
-    // sum the partials over the 16 rows (lanes col) of each lane group
+    // db': sum over the 16 rows (lanes col) of a lane group
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
+    for (int o = 1; o < 16; o <<= 1) dbp += __shfl_xor(dbp, o, kLanes);
+    if (gl == 0) {
 #pragma unroll
-      for (int ds = 0; ds < 2; ++ds)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dkp[ds][j] += __shfl_xor(dkp[ds][j], o, kLanes);
-      dbp += __shfl_xor(dbp, o, kLanes);
-    }
-    if (col == 0) {
-#pragma unroll
-      for (int ds = 0; ds < 2; ++ds)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sm.dkb[w][32 * ds + 8 * gl + j] = dkp[ds][j];
+      for (int fb = 0; fb < 4; ++fb) sm.dkb[w][16 * fb + col] = dkq[fb][0];
     }
     if (lane == 0) sm.dbw[w] = dbp;
     __syncthreads();
@@ -981,8 +1046,8 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
 }
 
 struct BPlan {
-  int R, Rq, ncr, nqb, nct;
-  size_t smem, kt_bytes, bnd_bytes;
+  int R, Rq, ncr, nqb, nct, nblk;
+  size_t smem, kt_bytes, bnd_bytes, cnt_bytes, ls_bytes, ent_bytes, fill_smem;
 };
 
 bool bwd_plan(const Dims& dm, BPlan* p) {
@@ -1003,28 +1068,49 @@ bool bwd_plan(const Dims& dm, BPlan* p) {
   p->nct = dm.Tkv / dm.S;
   p->kt_bytes = (size_t)dm.B * dm.Hkv * p->nct * D * kChunk * 2;
   p->bnd_bytes = (size_t)dm.B * dm.Hkv * p->nct * sizeof(float2);
+  p->nblk = (dm.Tq + kLBlk - 1) / kLBlk;
+  p->cnt_bytes = (size_t)dm.B * dm.H * p->nct * p->nblk * sizeof(int);
+  p->ls_bytes = (size_t)dm.B * dm.H * p->nct * sizeof(int);
+  p->ent_bytes = (size_t)dm.B * dm.H * dm.Tq * dm.K * sizeof(int);
+  p->fill_smem = (size_t)p->nct * (kLBlk / 32 + 1) * sizeof(int);
+  if (p->fill_smem > 160 * 1024) return false;
   return true;
 }
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
 size_t backward_mfma_ws_bytes(const Dims& dm) {
   BPlan p;
   if (!bwd_plan(dm, &p)) return 0;
-  return ((p.kt_bytes + 255) & ~(size_t)255) + ((p.bnd_bytes + 255) & ~(size_t)255);
+  return up256(p.kt_bytes) + up256(p.bnd_bytes) + up256(p.cnt_bytes) + 2 * up256(p.ls_bytes) +
+         3 * up256(p.ent_bytes);
 }
 
 bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void* V,
                        const void* Ql, const float* ksum, const float* ent, const float* lse_l,
                        const int32_t* idx, const float* score, const float* lse_tot,
                        const void* O, const void* dO, void* dQ, void* dK, void* dV, void* dQl,
-                       float* ws_D, const uint32_t* bm, int words, void* ws_mfma, hipStream_t st,
-                       hipError_t* err) {
+                       float* ws_D, void* ws_mfma, hipStream_t st, hipError_t* err) {
   BPlan p;
   if (!bwd_plan(dm, &p)) return false;
   char* base = reinterpret_cast<char*>(ws_mfma);
   uint16_t* Kt = reinterpret_cast<uint16_t*>(base);
-  float2* bnd = reinterpret_cast<float2*>(base + ((p.kt_bytes + 255) & ~(size_t)255));
+  base += up256(p.kt_bytes);
+  float2* bnd = reinterpret_cast<float2*>(base);
+  base += up256(p.bnd_bytes);
+  int* cnt = reinterpret_cast<int*>(base);
+  base += up256(p.cnt_bytes);
+  int* lstart = reinterpret_cast<int*>(base);
+  base += up256(p.ls_bytes);
+  int* llen = reinterpret_cast<int*>(base);
+  base += up256(p.ls_bytes);
+  int* e_pos = reinterpret_cast<int*>(base);
+  base += up256(p.ent_bytes);
+  float* e_alpha = reinterpret_cast<float*>(base);
+  base += up256(p.ent_bytes);
+  float* e_d = reinterpret_cast<float*>(base);
   const auto* Qh = reinterpret_cast<const uint16_t*>(Q);
   const auto* Kh = reinterpret_cast<const uint16_t*>(K);
   const auto* Vh = reinterpret_cast<const uint16_t*>(V);
@@ -1040,6 +1126,17 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
                      p.Rq, p.ncr, p.nqb, p.nct, Qh, Kh, Vh, Kt, bnd, ksum, idx, score, lse_tot,
                      reinterpret_cast<const uint16_t*>(O), reinterpret_cast<const uint16_t*>(dO),
                      reinterpret_cast<uint16_t*>(dQ), ws_D);
+  hipLaunchKernelGGL(k_sel_count, dim3(p.nblk, dm.H, dm.B), dim3(256), (size_t)p.nct * sizeof(int),
+                     st, dm, p.nblk, idx, cnt);
+  hipLaunchKernelGGL(k_sel_scan, dim3(dm.H, dm.B), dim3(256), 0, st, dm, p.nblk, cnt, lstart, llen);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sel_fill),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.fill_smem);
+  if (e != hipSuccess) {
+    *err = e;
+    return true;
+  }
+  hipLaunchKernelGGL(k_sel_fill, dim3(p.nblk, dm.H, dm.B), dim3(256), p.fill_smem, st, dm, p.nblk,
+                     idx, score, lse_tot, ws_D, cnt, e_pos, e_alpha, e_d);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_kv_mfma),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(KSmem));
   if (e != hipSuccess) {
@@ -1048,7 +1145,8 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
   }
   hipLaunchKernelGGL(k_bwd_kv_mfma, dim3(p.nct, dm.Hkv, dm.B), dim3(kKThreads), sizeof(KSmem), st, dm, Qh, Kh,
                      Vh, reinterpret_cast<const uint16_t*>(Ql), ksum, ent, lse_l, idx, score,
-                     lse_tot, reinterpret_cast<const uint16_t*>(dO), ws_D, bm, words,
+                     lse_tot, reinterpret_cast<const uint16_t*>(dO), ws_D, lstart, llen, e_pos,
+                     e_alpha, e_d,
                      reinterpret_cast<uint16_t*>(dK), reinterpret_cast<uint16_t*>(dV),
                      reinterpret_cast<uint16_t*>(dQl));
   *err = hipGetLastError();
