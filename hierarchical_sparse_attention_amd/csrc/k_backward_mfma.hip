@@ -620,8 +620,7 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
                                                   const float* __restrict__ lse_tot,
                                                   const float* __restrict__ ws_D,
                                                   const int* __restrict__ off,
-                                                  int* __restrict__ e_pos, float* __restrict__ e_alpha,
-                                                  float* __restrict__ e_d) {
+                                                  int4* __restrict__ srec) {
   extern __shared__ uint32_t lfill[];
   const int NC = dm.Tkv / dm.S;
   constexpr int W = kLBlk / 32;
@@ -649,10 +648,9 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
     const int wd = ii / 32;
     int rank = __popc(lb[c * W + wd] & ((1u << (ii % 32)) - 1u));
     for (int ww = 0; ww < wd; ++ww) rank += __popc(lb[c * W + ww]);
-    const long long e = ebase + lo[c] + rank;
-    e_pos[e] = i;
-    e_alpha[e] = expf(score[r * dm.K + k] - lse_tot[r]);
-    e_d[e] = ws_D[r];
+    // one 16-byte record: position, alpha, D
+    srec[ebase + lo[c] + rank] = make_int4(i, __float_as_int(expf(score[r * dm.K + k] - lse_tot[r])),
+                                          __float_as_int(ws_D[r]), 0);
   }
 }
 
@@ -737,8 +735,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     const float* __restrict__ lse_l, const int32_t* __restrict__ idx,
     const float* __restrict__ score, const float* __restrict__ lse_tot,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws_D,
-    const int* __restrict__ lstart, const int* __restrict__ llen, const int* __restrict__ e_pos,
-    const float* __restrict__ e_alpha, const float* __restrict__ e_d,
+    const int* __restrict__ lstart, const int* __restrict__ llen, const int4* __restrict__ srec,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, uint16_t* __restrict__ dQl) {
   extern __shared__ __align__(16) char smem_raw[];
   KSmem& sm = *reinterpret_cast<KSmem*>(smem_raw);
@@ -923,9 +920,10 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         sm.dvl[t] = lse_tot[r];
       }
       for (int e = t; e < ns; e += kKThreads) {
-        sm.rows[base + e] = e_pos[lsrc + s0 + e];
-        sm.aux[base + e] = e_alpha[lsrc + s0 + e];
-        sm.dvl[base + e] = e_d[lsrc + s0 + e];
+        const int4 rec = srec[lsrc + s0 + e];
+        sm.rows[base + e] = rec.x;
+        sm.aux[base + e] = __int_as_float(rec.y);
+        sm.dvl[base + e] = __int_as_float(rec.z);
       }
       __syncthreads();
       int e0 = kTileRows * w;
@@ -1071,7 +1069,7 @@ bool bwd_plan(const Dims& dm, BPlan* p) {
   p->nblk = (dm.Tq + kLBlk - 1) / kLBlk;
   p->cnt_bytes = (size_t)dm.B * dm.H * p->nct * p->nblk * sizeof(int);
   p->ls_bytes = (size_t)dm.B * dm.H * p->nct * sizeof(int);
-  p->ent_bytes = (size_t)dm.B * dm.H * dm.Tq * dm.K * sizeof(int);
+  p->ent_bytes = (size_t)dm.B * dm.H * dm.Tq * dm.K * sizeof(int4);
   p->fill_smem = (size_t)p->nct * (kLBlk / 32 + 1) * sizeof(int);
   if (p->fill_smem > 160 * 1024) return false;
   return true;
@@ -1085,7 +1083,7 @@ size_t backward_mfma_ws_bytes(const Dims& dm) {
   BPlan p;
   if (!bwd_plan(dm, &p)) return 0;
   return up256(p.kt_bytes) + up256(p.bnd_bytes) + up256(p.cnt_bytes) + 2 * up256(p.ls_bytes) +
-         3 * up256(p.ent_bytes);
+         up256(p.ent_bytes);
 }
 
 bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void* V,
@@ -1106,11 +1104,7 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
   base += up256(p.ls_bytes);
   int* llen = reinterpret_cast<int*>(base);
   base += up256(p.ls_bytes);
-  int* e_pos = reinterpret_cast<int*>(base);
-  base += up256(p.ent_bytes);
-  float* e_alpha = reinterpret_cast<float*>(base);
-  base += up256(p.ent_bytes);
-  float* e_d = reinterpret_cast<float*>(base);
+  int4* srec = reinterpret_cast<int4*>(base);
   const auto* Qh = reinterpret_cast<const uint16_t*>(Q);
   const auto* Kh = reinterpret_cast<const uint16_t*>(K);
   const auto* Vh = reinterpret_cast<const uint16_t*>(V);
@@ -1136,7 +1130,7 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
     return true;
   }
   hipLaunchKernelGGL(k_sel_fill, dim3(p.nblk, dm.H, dm.B), dim3(256), p.fill_smem, st, dm, p.nblk,
-                     idx, score, lse_tot, ws_D, cnt, e_pos, e_alpha, e_d);
+                     idx, score, lse_tot, ws_D, cnt, srec);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_kv_mfma),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(KSmem));
   if (e != hipSuccess) {
@@ -1145,8 +1139,7 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
   }
   hipLaunchKernelGGL(k_bwd_kv_mfma, dim3(p.nct, dm.Hkv, dm.B), dim3(kKThreads), sizeof(KSmem), st, dm, Qh, Kh,
                      Vh, reinterpret_cast<const uint16_t*>(Ql), ksum, ent, lse_l, idx, score,
-                     lse_tot, reinterpret_cast<const uint16_t*>(dO), ws_D, lstart, llen, e_pos,
-                     e_alpha, e_d,
+                     lse_tot, reinterpret_cast<const uint16_t*>(dO), ws_D, lstart, llen, srec,
                      reinterpret_cast<uint16_t*>(dK), reinterpret_cast<uint16_t*>(dV),
                      reinterpret_cast<uint16_t*>(dQl));
   *err = hipGetLastError();
