@@ -173,6 +173,31 @@ __device__ __forceinline__ void load_qfrag(QFrag& f, const uint16_t* K, const ui
           Kt + kt_base + (long long)(16 * db + c) * kChunk + 32 * ks + 8 * g);
 }
 
+// K and V rows of a chunk (the A operands of S^T and U^T)
+__device__ __forceinline__ void load_kvfrag(uint4* k, uint4* v, const uint16_t* K, const uint16_t* V,
+                                            long long kv_base, long long kv_stride, int chunk,
+                                            long long Tkv) {
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      const long long row = min((long long)chunk * kChunk + 16 * kb + c, Tkv - 1);
+      const long long off = kv_base + row * kv_stride + 32 * ds + 8 * g;
+      k[kb * 2 + ds] = *reinterpret_cast<const uint4*>(K + off);
+      v[kb * 2 + ds] = *reinterpret_cast<const uint4*>(V + off);
+    }
+}
+__device__ __forceinline__ void load_ktfrag(uint4* kt, const uint16_t* Kt, long long kt_base) {
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      kt[db * 2 + ks] = *reinterpret_cast<const uint4*>(Kt + kt_base + (long long)(16 * db + c) * kChunk +
+                                                        32 * ks + 8 * g);
+}
+
 // S^T (scaled, log2 units) and U^T of one 16-row tile: lane l holds keys
 // 16 kb + 4g + r of tile row c in s[kb][r], u[kb][r].
 __device__ __forceinline__ void tile_su(const QFrag& f, const uint4* q, const uint4* o,
@@ -217,6 +242,7 @@ struct QSmem {
   uint16_t* qs;   // [R][QP] query rows
   uint16_t* os;   // [R][QP] dO rows
   uint32_t* ent;  // chunk-major entries rho | k << 16
+  float* eal;     // alpha of each entry
   int* cnt;
   int* off;
   int* cur;
@@ -227,7 +253,7 @@ struct QSmem {
 };
 
 __host__ __device__ inline size_t q_smem_bytes(int R, int K, int ncr) {
-  return (size_t)R * AP * 4 + 2 * (size_t)R * QP * 2 + (size_t)R * K * 4 +
+  return (size_t)R * AP * 4 + 2 * (size_t)R * QP * 2 + 2 * (size_t)R * K * 4 +
          4 * (size_t)(ncr + 1) * 4 + 2 * (size_t)R * 4 + 64 * 4;
 }
 
@@ -237,6 +263,7 @@ __device__ __forceinline__ QSmem q_carve(char* p, int R, int K, int ncr) {
   s.qs = reinterpret_cast<uint16_t*>(p); p += (size_t)R * QP * 2;
   s.os = reinterpret_cast<uint16_t*>(p); p += (size_t)R * QP * 2;
   s.ent = reinterpret_cast<uint32_t*>(p); p += (size_t)R * K * 4;
+  s.eal = reinterpret_cast<float*>(p); p += (size_t)R * K * 4;
   s.cnt = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
   s.off = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
   s.cur = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
@@ -389,10 +416,13 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
   for (int x = t; x < Rv * Ksel; x += kQThreads) {
     const int rho = x / Ksel, k = x % Ksel;
     const int own = (int)((p0 + rho / G) / S);
-    const int c = idx[row_of(rho) * Ksel + k];
+    const long long r = row_of(rho);
+    const int c = idx[r * Ksel + k];
+    const float sc = score[r * Ksel + k];
     if (c >= 0 && c < own) {
       const int p = atomicAdd(&sm.cur[c], 1);
       sm.ent[p] = (uint32_t)rho | ((uint32_t)k << 16);
+      sm.eal[p] = expf(sc - sm.lam[rho]);
     }
   }
   // bound of every partial sum of dQ / scale (see the file comment): with
@@ -421,6 +451,7 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
   const float fx_scale = ldexpf(1.0f, 29 - ex);
   const float fx_inv = ldexpf(1.0f, ex - 29);
   for (int x = t; x < R * AP; x += kQThreads) sm.acc[x] = 0;
+  if (t == 0) sm.misc[40] = 0;  // selected-chunk queue
   __syncthreads();
 
   const int n_own = [&]() {
@@ -464,28 +495,47 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
     if (valid) q_accumulate(sm.acc + rho * AP, dq, fx_scale);
   }
 
-  // ---- selected chunks (chunk u belongs to wave u mod 8):
+  // ---- selected chunks:
   //      ds_j = alpha P_j (u_j - r), plus ds^ = alpha (r - D) times the summary key
-  for (int uu = w; uu < nnz; uu += kQWaves) {
+  // wavefronts take chunks from a queue; the next chunk's K and V are loaded
+  // while the current one is processed
+  auto grab = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&sm.misc[40], 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  int uu = grab();
+  uint4 kn[KF], vnx[KF];
+  if (uu < nnz) load_kvfrag(kn, vnx, K, V, kv_base, kv_stride, sm.cur[uu], dm.Tkv);
+  while (uu < nnz) {
     const int c = sm.cur[uu];
     QFrag f;
-    load_qfrag(f, K, V, Kt, kv_base, kv_stride, c, kt_base + (long long)c * D * kChunk, dm.Tkv);
+#pragma unroll
+    for (int i = 0; i < KF; ++i) f.k[i] = kn[i], f.v[i] = vnx[i];
+    load_ktfrag(f.kt, Kt, kt_base + (long long)c * D * kChunk);
+    const int nu = grab();
+    load_kvfrag(kn, vnx, K, V, kv_base, kv_stride, sm.cur[min(nu, nnz - 1)], dm.Tkv);
+    // summary key of the chunk (one head per kv head: loaded with the chunk)
+    const float* kbar0 = ksum + (((long long)b * dm.NCcap + c) * dm.H + (long long)g * G) * D + 4 * gl;
+    float4 kb4[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) kb4[db] = *reinterpret_cast<const float4*>(kbar0 + 16 * db);
     const int e0 = sm.off[c], n = sm.cnt[c];
     for (int tl = 0; tl < (n + 15) / 16; ++tl) {
       const int e = 16 * tl + col;
       const bool valid = e < n;
       const uint32_t en = sm.ent[e0 + min(e, n - 1)];
-      const int rho = (int)(en & 0xFFFFu), k = (int)(en >> 16);
-      const long long r = row_of(rho);
-      const float sc = score[r * Ksel + k];
-      const float* kbar = ksum + (((long long)b * dm.NCcap + c) * dm.H + (long long)g * G + rho % G) * D + 4 * gl;
-      float4 kb4[D / 16];
+      const float eal = sm.eal[e0 + min(e, n - 1)];
+      const int rho = (int)(en & 0xFFFFu);
+      if (G > 1) {  // rows of a tile belong to different query heads
+        const float* kbar = kbar0 + (long long)(rho % G) * D;
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) kb4[db] = *reinterpret_cast<const float4*>(kbar + 16 * db);
+        for (int db = 0; db < D / 16; ++db) kb4[db] = *reinterpret_cast<const float4*>(kbar + 16 * db);
+      }
       uint4 q[2], o[2];
       lds_frag2(q, sm.qs, rho, true);
       lds_frag2(o, sm.os, rho, true);
-      const float lam = sm.lam[rho], Dr = sm.dv[rho];
+      const float Dr = sm.dv[rho];
       floatx4 s[4], u[4];
       tile_su(f, q, o, s, u);
       float m = -INFINITY;
@@ -508,7 +558,7 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
         }
       z = xsum_16_32(z);
       zu = xsum_16_32(zu);
-      const float alpha = valid ? expf(sc - lam) : 0.f;
+      const float alpha = valid ? eal : 0.f;
       const float iz = 1.0f / z, rcv = zu * iz;
       floatx4 ds[4];
 #pragma unroll
@@ -527,6 +577,7 @@ __global__ __launch_bounds__(kQThreads) void k_bwd_q(
       }
       if (valid) q_accumulate(sm.acc + rho * AP, dq, fx_scale);
     }
+    uu = nu;
   }
   __syncthreads();
 
