@@ -14,23 +14,20 @@
 //   ds'_j = p'_j [dk'.(k_j - k'_c) + db' (L' - s'_j - b'_c)],
 //   dQl = scale sum_j ds'_j k_j,  dK_j += p'_j dk'_c + scale ds'_j Ql.
 //
-// Kernels (no floating-point atomics; integer or fixed-order sums, so the
+// Kernels (no floating-point atomics; every sum has a fixed order, so the
 // gradients are bitwise reproducible):
-//   k_bwd_prep   : per (chunk, kv head) K^T in MFMA k-slot order and bounds
-//                  (max |k|, max ||v||) for the fixed-point dQ accumulator
-//   k_bwd_q      : query side, one workgroup per (kv head, block of rows), the
-//                  rows' selections counting-sorted by chunk as in the forward;
-//                  D = dO.O from the forward output; per 16-row tile
-//                  S^T = K Q^T and U^T = V dO^T on MFMA, then dQ^T += K^T dS^T
-//                  on MFMA (plus ds^ k') into integer LDS accumulators; writes
-//                  dQ and D per row
-//   k_sel_bitmap : (k_backward.hip) rows that selected each chunk
-//   k_bwd_kv_mfma: key side, one workgroup per (chunk, kv head); the rows that
-//                  selected the chunk (ascending) and the chunk's own rows in
-//                  32-row tiles: S^T, U^T on MFMA, weights and dS written
-//                  transposed to LDS, dK += dS^T Q and dV += A^T dO on MFMA,
-//                  ds^ = alpha (r - D) into dk' and db'; then the summary and
-//                  landmark backward; writes dK, dV, dQl.
+//   k_bwd_rowd   : D = dO.O per row from the forward output
+//   k_sel_count, k_sel_scan, k_sel_fill: per (b, h, chunk) the rows that
+//                  selected the chunk (ascending) as records (position, alpha,
+//                  D, slot)
+//   k_bwd_kv_mfma: one workgroup per (chunk, kv head); the chunk's own rows and
+//                  the rows that selected it in 32-row tiles: S^T, U^T on MFMA,
+//                  weights and dS through LDS, dK += dS^T Q and dV += A^T dO on
+//                  MFMA, ds^ = alpha (r - D) into dk' and db', and each row's
+//                  dQ contribution K^T dS^T (+ ds^ k') on MFMA into the row's
+//                  slot of a bf16 partial buffer; then the summary and landmark
+//                  backward; writes dK, dV, dQl.
+//   k_dq_reduce  : dQ = scale * sum of a row's slots in slot order.
 #include "hils_internal.h"
 
 namespace hils {
@@ -43,7 +40,6 @@ constexpr int D = 64;
 constexpr int kLanes = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int KF = 4 * (D / 32);  // row fragments (uint4) of a 64-key chunk per lane
-constexpr int VF = (D / 16) * 2;  // transposed-chunk fragments per lane
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
   bf16x8 r;
@@ -75,525 +71,75 @@ __device__ __forceinline__ float bf(uint16_t h) { return __uint_as_float((uint32
 // S^T block kb of a chunk gives lane l keys 16 kb + 4g + r of tile row c. For a
 // product whose k dimension is the chunk's keys, k-slot 8g + j of step ks holds
 // key 32 ks + 4g + j (j < 4) or 32 ks + 16 + 4g + (j - 4) (j >= 4): exactly the
-// S^T values the lane holds, so weights need no data movement; K^T is stored in
-// that key order (k_bwd_prep).
+// S^T values the lane holds, so weights need no data movement; K^T is read in
+// that key order from LDS (lds_ktfrag).
 
-// ------------------------------------------------------------------ prep
-// Kt[b][g][c][e][p] = K[key(p)][e] (k-slot order, zero beyond Tkv);
-// bnd[b][g][c] = (max |k|, max_j ||v_j||).
-__global__ __launch_bounds__(256) void k_bwd_prep(Dims dm, int nct, const uint16_t* __restrict__ K,
-                                                  const uint16_t* __restrict__ V,
-                                                  uint16_t* __restrict__ Kt,
-                                                  float2* __restrict__ bnd) {
-  __shared__ uint16_t ks[kChunk][D + 8];
-  __shared__ float red[2][4];
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
-  const long long kv_stride = (long long)dm.Hkv * D;
-  const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
-  float km = 0.f, vn = 0.f;
-  for (int u = t; u < kChunk * D / 8; u += 256) {
-    const int j = u / (D / 8), c8 = u % (D / 8);
-    const long long row = (long long)c * kChunk + j;
-    const bool in = row < dm.Tkv;
-    const uint4 kv = in ? *reinterpret_cast<const uint4*>(K + kv_base + row * kv_stride + c8 * 8)
-                        : make_uint4(0, 0, 0, 0);
-    const uint4 vv = in ? *reinterpret_cast<const uint4*>(V + kv_base + row * kv_stride + c8 * 8)
-                        : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(&ks[j][c8 * 8]) = kv;
-    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
-    float v2 = 0.f;
+// ------------------------------------------------------------------ rows
+// D = dO . O per row (eight lanes per row, 16-byte loads).
+__global__ __launch_bounds__(256) void k_bwd_rowd(long long rows, const uint16_t* __restrict__ O,
+                                                  const uint16_t* __restrict__ dO,
+                                                  float* __restrict__ ws_D) {
+  const long long r = (long long)blockIdx.x * 32 + threadIdx.x / 8;
+  const int c8 = threadIdx.x % 8;
+  const long long rr = min(r, rows - 1);
+  const uint4 ov = *reinterpret_cast<const uint4*>(dO + rr * D + c8 * 8);
+  const uint4 yv = *reinterpret_cast<const uint4*>(O + rr * D + c8 * 8);
+  const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w}, yw[4] = {yv.x, yv.y, yv.z, yv.w};
+  float dd = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      km = fmaxf(km, fmaxf(fabsf(__uint_as_float(kw[q] << 16)), fabsf(__uint_as_float(kw[q] & 0xFFFF0000u))));
-      const float a = __uint_as_float(vw[q] << 16), bb = __uint_as_float(vw[q] & 0xFFFF0000u);
-      v2 = fmaf(a, a, fmaf(bb, bb, v2));
-    }
-    // squared norm of row j: the D / 8 pieces of a row sit in consecutive lanes
+  for (int q = 0; q < 4; ++q)
+    dd = fmaf(__uint_as_float(ow[q] << 16), __uint_as_float(yw[q] << 16),
+              fmaf(__uint_as_float(ow[q] & 0xFFFF0000u), __uint_as_float(yw[q] & 0xFFFF0000u), dd));
 #pragma unroll
-    for (int o = 1; o < D / 8; o <<= 1) v2 += __shfl_xor(v2, o, kLanes);
-    vn = fmaxf(vn, v2);
-  }
-  km = wave_max(km);
-  vn = wave_max(vn);
-  if ((t & 63) == 0) red[0][t >> 6] = km, red[1][t >> 6] = vn;
-  __syncthreads();
-  const long long cbase = (((long long)b * dm.Hkv + g) * nct + c) * (long long)D * kChunk;
-  for (int u = t; u < D * 8; u += 256) {
-    const int e = u / 8, p8 = u % 8;  // feature e, k-slots 8 p8 .. 8 p8 + 7
-    const int kstep = p8 / 4, gg = p8 % 4;
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j0 = 2 * q, j1 = 2 * q + 1;
-      const int k0 = 32 * kstep + (j0 < 4 ? 4 * gg + j0 : 16 + 4 * gg + j0 - 4);
-      const int k1 = 32 * kstep + (j1 < 4 ? 4 * gg + j1 : 16 + 4 * gg + j1 - 4);
-      w[q] = (uint32_t)ks[k0][e] | ((uint32_t)ks[k1][e] << 16);
-    }
-    *reinterpret_cast<uint4*>(Kt + cbase + (long long)e * kChunk + p8 * 8) =
-        make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  if (t == 0)
-    bnd[((long long)b * dm.Hkv + g) * nct + c] =
-        make_float2(fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3])),
-                    sqrtf(fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]))));
+  for (int o = 1; o < 8; o <<= 1) dd += __shfl_xor(dd, o, kLanes);
+  if (c8 == 0 && r < rows) ws_D[r] = dd;
 }
 
-// ------------------------------------------------------------------ query side
-constexpr int kQThreads = 512;
-constexpr int kQWaves = kQThreads / 64;
-constexpr int kQRows = 128;  // rows per workgroup (positions x heads of one kv head)
-constexpr int QP = D + 8;    // LDS row pitch of query / dO rows (bf16)
-constexpr int AP = D + 1;    // accumulator row pitch (words)
-
-struct QFrag {
-  uint4 k[KF];   // K rows:  k[kb * 2 + ds] = K[16 kb + c][32 ds + 8g .. +8]
-  uint4 v[KF];   // V rows, same layout
-  uint4 kt[VF];  // K^T:     kt[db * 2 + ks] = K^T[16 db + c][k-slots 32 ks + 8g .. +8]
-};
-
-__device__ __forceinline__ void load_qfrag(QFrag& f, const uint16_t* K, const uint16_t* V,
-                                           const uint16_t* Kt, long long kv_base,
-                                           long long kv_stride, int chunk, long long kt_base,
-                                           long long Tkv) {
-  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+// dQ = scale * (sum over the row's slots of its dQ partials, fixed slot order):
+// slot k < K holds selected chunk idx[k] (written only for valid selections),
+// slot K the own chunk. Eight lanes per row, 16-byte loads issued together.
+template <int KM>
+__global__ __launch_bounds__(256) void k_dq_reduce(Dims dm, long long rows,
+                                                   const int32_t* __restrict__ idx,
+                                                   const uint16_t* __restrict__ part,
+                                                   uint16_t* __restrict__ dQ) {
+  const long long r0 = (long long)blockIdx.x * 32 + threadIdx.x / 8;
+  const long long r = min(r0, rows - 1);
+  const int c8 = threadIdx.x % 8;
+  const int Ksel = dm.K, NC = dm.Tkv / dm.S;
+  const int pos = (int)((r / dm.H) % dm.Tq);
+  const int own = (int)((dm.q_pos0 + pos) / dm.S);
+  const uint16_t* pr = part + r * (long long)(Ksel + 1) * D + c8 * 8;
+  float acc[8];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  for (int k0 = 0; k0 <= Ksel; k0 += KM) {
+    uint4 v[KM];
+    bool ok[KM];
 #pragma unroll
-    for (int ds = 0; ds < 2; ++ds) {
-      const long long row = min((long long)chunk * kChunk + 16 * kb + c, Tkv - 1);
-      const long long off = kv_base + row * kv_stride + 32 * ds + 8 * g;
-      f.k[kb * 2 + ds] = *reinterpret_cast<const uint4*>(K + off);
-      f.v[kb * 2 + ds] = *reinterpret_cast<const uint4*>(V + off);
+    for (int q = 0; q < KM; ++q) {
+      const int k = min(k0 + q, Ksel);
+      const int c = k < Ksel ? idx[r * Ksel + k] : own;
+      ok[q] = k0 + q <= Ksel && (k == Ksel || (c >= 0 && c < own && c < NC));
+      v[q] = *reinterpret_cast<const uint4*>(pr + (long long)k * D);
     }
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
+    for (int q = 0; q < KM; ++q) {
+      const uint32_t wv[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      f.kt[db * 2 + ks] = *reinterpret_cast<const uint4*>(
-          Kt + kt_base + (long long)(16 * db + c) * kChunk + 32 * ks + 8 * g);
-}
-
-// K and V rows of a chunk (the A operands of S^T and U^T)
-__device__ __forceinline__ void load_kvfrag(uint4* k, uint4* v, const uint16_t* K, const uint16_t* V,
-                                            long long kv_base, long long kv_stride, int chunk,
-                                            long long Tkv) {
-  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int ds = 0; ds < 2; ++ds) {
-      const long long row = min((long long)chunk * kChunk + 16 * kb + c, Tkv - 1);
-      const long long off = kv_base + row * kv_stride + 32 * ds + 8 * g;
-      k[kb * 2 + ds] = *reinterpret_cast<const uint4*>(K + off);
-      v[kb * 2 + ds] = *reinterpret_cast<const uint4*>(V + off);
-    }
-}
-__device__ __forceinline__ void load_ktfrag(uint4* kt, const uint16_t* Kt, long long kt_base) {
-  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      kt[db * 2 + ks] = *reinterpret_cast<const uint4*>(Kt + kt_base + (long long)(16 * db + c) * kChunk +
-                                                        32 * ks + 8 * g);
-}
-
-// S^T (scaled, log2 units) and U^T of one 16-row tile: lane l holds keys
-// 16 kb + 4g + r of tile row c in s[kb][r], u[kb][r].
-__device__ __forceinline__ void tile_su(const QFrag& f, const uint4* q, const uint4* o,
-                                        floatx4* s, floatx4* u) {
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    u[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ds = 0; ds < 2; ++ds) {
-      s[kb] = mfma(f.k[kb * 2 + ds], q[ds], s[kb]);
-      u[kb] = mfma(f.v[kb * 2 + ds], o[ds], u[kb]);
-    }
-  }
-}
-
-// dQ^T partial of a tile: sum_j ds_j k_j, with ds given in S^T layout.
-__device__ __forceinline__ void tile_dq(const QFrag& f, const floatx4* ds, floatx4* dq) {
-  bf16x8 pf[2];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pf[kb >> 1][(kb & 1) * 4 + r] = (__bf16)ds[kb][r];
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db) {
-    dq[db] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) dq[db] = mfma(f.kt[db * 2 + ks], pf[ks], dq[db]);
-  }
-}
-
-__device__ __forceinline__ void lds_frag2(uint4* x, const uint16_t* base, int rho, bool valid) {
-  const int g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int ds = 0; ds < 2; ++ds)
-    x[ds] = valid ? *reinterpret_cast<const uint4*>(base + rho * QP + 32 * ds + 8 * g)
-                  : make_uint4(0, 0, 0, 0);
-}
-
-struct QSmem {
-  int* acc;       // [R][AP] dQ / scale in fixed point
-  uint16_t* qs;   // [R][QP] query rows
-  uint16_t* os;   // [R][QP] dO rows
-  uint32_t* ent;  // chunk-major entries rho | k << 16
-  float* eal;     // alpha of each entry
-  int* cnt;
-  int* off;
-  int* cur;
-  int* nz;
-  float* lam;     // Lambda (natural log)
-  float* dv;      // D = dO . O
-  int* misc;
-};
-
-__host__ __device__ inline size_t q_smem_bytes(int R, int K, int ncr) {
-  return (size_t)R * AP * 4 + 2 * (size_t)R * QP * 2 + 2 * (size_t)R * K * 4 +
-         4 * (size_t)(ncr + 1) * 4 + 2 * (size_t)R * 4 + 64 * 4;
-}
-
-__device__ __forceinline__ QSmem q_carve(char* p, int R, int K, int ncr) {
-  QSmem s;
-  s.acc = reinterpret_cast<int*>(p); p += (size_t)R * AP * 4;
-  s.qs = reinterpret_cast<uint16_t*>(p); p += (size_t)R * QP * 2;
-  s.os = reinterpret_cast<uint16_t*>(p); p += (size_t)R * QP * 2;
-  s.ent = reinterpret_cast<uint32_t*>(p); p += (size_t)R * K * 4;
-  s.eal = reinterpret_cast<float*>(p); p += (size_t)R * K * 4;
-  s.cnt = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
-  s.off = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
-  s.cur = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
-  s.nz = reinterpret_cast<int*>(p); p += (ncr + 1) * 4;
-  s.lam = reinterpret_cast<float*>(p); p += R * 4;
-  s.dv = reinterpret_cast<float*>(p); p += R * 4;
-  s.misc = reinterpret_cast<int*>(p);
-  return s;
-}
-
-// In-place exclusive scan of n ints by the workgroup; returns the total.
-__device__ __forceinline__ int q_scan(int* a, int n, int* scratch) {
-  const int t = threadIdx.x;
-  const int seg = (n + kQThreads - 1) / kQThreads;
-  const int lo = min(n, t * seg), hi = min(n, lo + seg);
-  int s = 0;
-  for (int x = lo; x < hi; ++x) s += a[x];
-  const int lane = t & 63, w = t >> 6;
-  int incl = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) scratch[w] = incl;
-  __syncthreads();
-  int before = 0, total = 0;
-#pragma unroll
-  for (int x = 0; x < kQWaves; ++x) {
-    const int v = scratch[x];
-    before += x < w ? v : 0;
-    total += v;
-  }
-  int run = before + incl - s;
-  for (int x = lo; x < hi; ++x) {
-    const int v = a[x];
-    a[x] = run;
-    run += v;
-  }
-  __syncthreads();
-  return total;
-}
-
-// Own-chunk tile items: (own chunk, 16-row tile) pairs in chunk order.
-__device__ __forceinline__ bool q_own_item(int item, long long p0, int S, int G, int Rv,
-                                           int own_first, int own_last, int* oc, int* ra, int* rb,
-                                           int* tl) {
-  for (int c = own_first; c <= own_last; ++c) {
-    const int a = (int)max(0LL, (long long)c * S - p0) * G;
-    const int bnd = (int)min((long long)Rv, ((long long)c * S + S - p0) * G);
-    const int nt = (bnd - a + 15) / 16;
-    if (item < nt) {
-      *oc = c, *ra = a, *rb = bnd, *tl = item;
-      return true;
-    }
-    item -= nt;
-  }
-  return false;
-}
-
-// Add a tile's dQ^T (lane: features 16 db + 4g + r of tile row c) to the row's
-// fixed-point accumulator.
-__device__ __forceinline__ void q_accumulate(int* acc_row, const floatx4* dq, float fx_scale) {
-  const int gl = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) atomicAdd(acc_row + 16 * db + 4 * gl + r, (int)(dq[db][r] * fx_scale));
-}
-
-__global__ __launch_bounds__(kQThreads) void k_bwd_q(
-    Dims dm, int R, int Rq, int ncr_cap, int nqb, int nct, const uint16_t* __restrict__ Q,
-    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ Kt, const float2* __restrict__ bnd,
-    const float* __restrict__ ksum, const int32_t* __restrict__ idx,
-    const float* __restrict__ score, const float* __restrict__ lse_tot,
-    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, uint16_t* __restrict__ dQ,
-    float* __restrict__ ws_D) {
-  extern __shared__ __align__(16) char smem_raw[];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 15, gl = lane >> 4;
-  const int G = dm.G, Ksel = dm.K, S = dm.S;
-  const int L = blockIdx.x;
-  const int g = L % dm.Hkv, qb = (L / dm.Hkv) % nqb, b = L / (dm.Hkv * nqb);
-  const int qi0 = qb * Rq;
-  const int nq = min(Rq, dm.Tq - qi0);
-  const int Rv = nq * G;
-  const long long p0 = dm.q_pos0 + qi0;
-  const int own_first = (int)(p0 / S), own_last = (int)((p0 + nq - 1) / S);
-  const int ncr = own_last;
-  QSmem sm = q_carve(smem_raw, R, Ksel, ncr_cap);
-  const long long kv_stride = (long long)dm.Hkv * D;
-  const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
-  const long long kt_base = ((long long)b * dm.Hkv + g) * nct * (long long)D * kChunk;
-  const float2* bd = bnd + ((long long)b * dm.Hkv + g) * nct;
-  const float scale2 = dm.scale * kLog2e;
-  auto row_of = [&](int rho) -> long long {
-    return ((long long)b * dm.Tq + qi0 + rho / G) * dm.H + (long long)g * G + rho % G;
-  };
-
-  // ---- set-up: query and dO rows, D = dO . O, Lambda, counting sort of the selections
-  for (int c = t; c <= ncr; c += kQThreads) sm.cnt[c] = 0;
-  float dn = 0.f;  // max ||dO||^2 over the rows
-  for (int x = t; x < Rv * (D / 8); x += kQThreads) {
-    const int rho = x / (D / 8), c8 = x % (D / 8);
-    const long long r = row_of(rho);
-    const uint4 qv = *reinterpret_cast<const uint4*>(Q + r * D + c8 * 8);
-    const uint4 ov = *reinterpret_cast<const uint4*>(dO + r * D + c8 * 8);
-    const uint4 yv = *reinterpret_cast<const uint4*>(O + r * D + c8 * 8);
-    *reinterpret_cast<uint4*>(sm.qs + rho * QP + c8 * 8) = qv;
-    *reinterpret_cast<uint4*>(sm.os + rho * QP + c8 * 8) = ov;
-    const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w}, yw[4] = {yv.x, yv.y, yv.z, yv.w};
-    float dd = 0.f, n2 = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float o0 = __uint_as_float(ow[q] << 16), o1 = __uint_as_float(ow[q] & 0xFFFF0000u);
-      const float y0 = __uint_as_float(yw[q] << 16), y1 = __uint_as_float(yw[q] & 0xFFFF0000u);
-      dd = fmaf(o0, y0, fmaf(o1, y1, dd));
-      n2 = fmaf(o0, o0, fmaf(o1, o1, n2));
-    }
-    // the D / 8 pieces of a row sit in consecutive lanes
-#pragma unroll
-    for (int o = 1; o < D / 8; o <<= 1) {
-      dd += __shfl_xor(dd, o, kLanes);
-      n2 += __shfl_xor(n2, o, kLanes);
-    }
-    if (c8 == 0) {
-      sm.dv[rho] = dd;
-      ws_D[r] = dd;
-    }
-    dn = fmaxf(dn, n2);
-  }
-  for (int rho = t; rho < Rv; rho += kQThreads) sm.lam[rho] = lse_tot[row_of(rho)];
-  __syncthreads();
-  for (int x = t; x < Rv * Ksel; x += kQThreads) {
-    const int rho = x / Ksel, k = x % Ksel;
-    const int own = (int)((p0 + rho / G) / S);
-    const int c = idx[row_of(rho) * Ksel + k];
-    if (c >= 0 && c < own) atomicAdd(&sm.cnt[c], 1);
-  }
-  __syncthreads();
-  for (int c = t; c < ncr; c += kQThreads) {
-    sm.off[c] = sm.cnt[c];
-    sm.nz[c] = sm.cnt[c] > 0 ? 1 : 0;
-  }
-  __syncthreads();
-  q_scan(sm.off, ncr, sm.misc);
-  const int nnz = q_scan(sm.nz, ncr, sm.misc + 8);
-  for (int c = t; c < ncr; c += kQThreads) sm.cur[c] = sm.off[c];
-  __syncthreads();
-  for (int x = t; x < Rv * Ksel; x += kQThreads) {
-    const int rho = x / Ksel, k = x % Ksel;
-    const int own = (int)((p0 + rho / G) / S);
-    const long long r = row_of(rho);
-    const int c = idx[r * Ksel + k];
-    const float sc = score[r * Ksel + k];
-    if (c >= 0 && c < own) {
-      const int p = atomicAdd(&sm.cur[c], 1);
-      sm.ent[p] = (uint32_t)rho | ((uint32_t)k << 16);
-      sm.eal[p] = expf(sc - sm.lam[rho]);
-    }
-  }
-  // bound of every partial sum of dQ / scale (see the file comment): with
-  // |u| <= ||dO|| max||v||, sum_j |ds_j| <= 2 alpha max|u| per chunk and
-  // |ds^_c| <= 2 alpha_c max|u|, |dQ / scale| <= 4 max||dO|| max||v|| max|k|
-  __syncthreads();
-  float km = 0.f, vn = 0.f;
-  for (int c = t; c <= own_last; c += kQThreads)
-    if (c >= own_first || (c < ncr && sm.cnt[c] > 0)) {
-      const float2 bb = bd[c];
-      km = fmaxf(km, bb.x);
-      vn = fmaxf(vn, bb.y);
-    }
-  for (int c = t; c < ncr; c += kQThreads)
-    if (sm.cnt[c] > 0) sm.cur[sm.nz[c]] = c;
-  dn = wave_max(dn), km = wave_max(km), vn = wave_max(vn);
-  float* redf = reinterpret_cast<float*>(sm.misc) + 16;
-  if (lane == 0) redf[w] = dn, redf[8 + w] = km, redf[16 + w] = vn;
-  __syncthreads();
-  float dnw = 0.f, kmw = 0.f, vnw = 0.f;
-#pragma unroll
-  for (int x = 0; x < kQWaves; ++x)
-    dnw = fmaxf(dnw, redf[x]), kmw = fmaxf(kmw, redf[8 + x]), vnw = fmaxf(vnw, redf[16 + x]);
-  int ex = 0;
-  frexpf(fmaxf(4.f * sqrtf(dnw) * vnw * kmw, 1e-30f), &ex);
-  const float fx_scale = ldexpf(1.0f, 29 - ex);
-  const float fx_inv = ldexpf(1.0f, ex - 29);
-  for (int x = t; x < R * AP; x += kQThreads) sm.acc[x] = 0;
-  if (t == 0) sm.misc[40] = 0;  // selected-chunk queue
-  __syncthreads();
-
-  const int n_own = [&]() {
-    int n = 0;
-    for (int c = own_first; c <= own_last; ++c) {
-      const int a = (int)max(0LL, (long long)c * S - p0) * G;
-      const int e = (int)min((long long)Rv, ((long long)c * S + S - p0) * G);
-      n += (e - a + 15) / 16;
-    }
-    return n;
-  }();
-
-  // ---- own chunks: ds_j = w_j (u_j - D), w_j = exp(s_j - Lambda)
-  for (int item = w; item < n_own; item += kQWaves) {
-    int oc, ra, rb, tl;
-    q_own_item(item, p0, S, G, Rv, own_first, own_last, &oc, &ra, &rb, &tl);
-    QFrag f;
-    load_qfrag(f, K, V, Kt, kv_base, kv_stride, oc, kt_base + (long long)oc * D * kChunk, dm.Tkv);
-    const int rho = ra + 16 * tl + col;
-    const bool valid = rho < rb;
-    const int rc = valid ? rho : ra;
-    const int nk = valid ? (int)(p0 + rho / G - (long long)oc * S) + 1 : 0;
-    uint4 q[2], o[2];
-    lds_frag2(q, sm.qs, rc, true);
-    lds_frag2(o, sm.os, rc, true);
-    const float lam2 = sm.lam[rc] * kLog2e;
-    const float Dr = sm.dv[rc];
-    floatx4 s[4], u[4];
-    tile_su(f, q, o, s, u);
-    floatx4 ds[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * kb + 4 * gl + r;
-        const float wj = j < nk ? exp2f(s[kb][r] * scale2 - lam2) : 0.f;
-        ds[kb][r] = wj * (u[kb][r] - Dr);
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += ok[q] ? __uint_as_float(wv[j] << 16) : 0.f;
+        acc[2 * j + 1] += ok[q] ? __uint_as_float(wv[j] & 0xFFFF0000u) : 0.f;
       }
-    floatx4 dq[D / 16];
-    tile_dq(f, ds, dq);
-    if (valid) q_accumulate(sm.acc + rho * AP, dq, fx_scale);
-  }
-
-  // ---- selected chunks:
-  //      ds_j = alpha P_j (u_j - r), plus ds^ = alpha (r - D) times the summary key
-  // wavefronts take chunks from a queue; the next chunk's K and V are loaded
-  // while the current one is processed
-  auto grab = [&]() -> int {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&sm.misc[40], 1);
-    return __builtin_amdgcn_readfirstlane(v);
-  };
-  int uu = grab();
-  uint4 kn[KF], vnx[KF];
-  if (uu < nnz) load_kvfrag(kn, vnx, K, V, kv_base, kv_stride, sm.cur[uu], dm.Tkv);
-  while (uu < nnz) {
-    const int c = sm.cur[uu];
-    QFrag f;
-#pragma unroll
-    for (int i = 0; i < KF; ++i) f.k[i] = kn[i], f.v[i] = vnx[i];
-    load_ktfrag(f.kt, Kt, kt_base + (long long)c * D * kChunk);
-    const int nu = grab();
-    load_kvfrag(kn, vnx, K, V, kv_base, kv_stride, sm.cur[min(nu, nnz - 1)], dm.Tkv);
-    // summary key of the chunk (one head per kv head: loaded with the chunk)
-    const float* kbar0 = ksum + (((long long)b * dm.NCcap + c) * dm.H + (long long)g * G) * D + 4 * gl;
-    float4 kb4[D / 16];
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) kb4[db] = *reinterpret_cast<const float4*>(kbar0 + 16 * db);
-    const int e0 = sm.off[c], n = sm.cnt[c];
-    for (int tl = 0; tl < (n + 15) / 16; ++tl) {
-      const int e = 16 * tl + col;
-      const bool valid = e < n;
-      const uint32_t en = sm.ent[e0 + min(e, n - 1)];
-      const float eal = sm.eal[e0 + min(e, n - 1)];
-      const int rho = (int)(en & 0xFFFFu);
-      if (G > 1) {  // rows of a tile belong to different query heads
-        const float* kbar = kbar0 + (long long)(rho % G) * D;
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) kb4[db] = *reinterpret_cast<const float4*>(kbar + 16 * db);
-      }
-      uint4 q[2], o[2];
-      lds_frag2(q, sm.qs, rho, true);
-      lds_frag2(o, sm.os, rho, true);
-      const float Dr = sm.dv[rho];
-      floatx4 s[4], u[4];
-      tile_su(f, q, o, s, u);
-      float m = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r2 = 0; r2 < 4; ++r2) {
-          s[kb][r2] *= scale2;
-          m = fmaxf(m, s[kb][r2]);
-        }
-      m = xmax_16_32(m);
-      float z = 0.f, zu = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r2 = 0; r2 < 4; ++r2) {
-          s[kb][r2] = exp2f(s[kb][r2] - m);
-          z += s[kb][r2];
-          zu = fmaf(s[kb][r2], u[kb][r2], zu);
-        }
-      z = xsum_16_32(z);
-      zu = xsum_16_32(zu);
-      const float alpha = valid ? eal : 0.f;
-      const float iz = 1.0f / z, rcv = zu * iz;
-      floatx4 ds[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r2 = 0; r2 < 4; ++r2) ds[kb][r2] = alpha * s[kb][r2] * iz * (u[kb][r2] - rcv);
-      floatx4 dq[D / 16];
-      tile_dq(f, ds, dq);
-      const float dsh = alpha * (rcv - Dr);
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        dq[db][0] = fmaf(dsh, kb4[db].x, dq[db][0]);
-        dq[db][1] = fmaf(dsh, kb4[db].y, dq[db][1]);
-        dq[db][2] = fmaf(dsh, kb4[db].z, dq[db][2]);
-        dq[db][3] = fmaf(dsh, kb4[db].w, dq[db][3]);
-      }
-      if (valid) q_accumulate(sm.acc + rho * AP, dq, fx_scale);
     }
-    uu = nu;
   }
-  __syncthreads();
-
-  // ---- dQ = scale * accumulator (bf16, round to nearest even)
-  const float out_scale = fx_inv * dm.scale;
-  for (int x = t; x < Rv * (D / 8); x += kQThreads) {
-    const int rho = x / (D / 8), c8 = x % (D / 8);
-    uint32_t ow[4];
+  if (r0 >= rows) return;
+  uint32_t ow[4];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int e0 = 8 * c8 + 2 * y;
-      ow[y] = (uint32_t)f32_to_bf16_bits((float)sm.acc[rho * AP + e0] * out_scale) |
-              ((uint32_t)f32_to_bf16_bits((float)sm.acc[rho * AP + e0 + 1] * out_scale) << 16);
-    }
-    *reinterpret_cast<uint4*>(dQ + row_of(rho) * D + c8 * 8) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-  }
+  for (int j = 0; j < 4; ++j)
+    ow[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * dm.scale) |
+            ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * dm.scale) << 16);
+  *reinterpret_cast<uint4*>(dQ + r * D + c8 * 8) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
 }
 
 // ------------------------------------------------------------------ selection lists
@@ -699,9 +245,9 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
     const int wd = ii / 32;
     int rank = __popc(lb[c * W + wd] & ((1u << (ii % 32)) - 1u));
     for (int ww = 0; ww < wd; ++ww) rank += __popc(lb[c * W + ww]);
-    // one 16-byte record: position, alpha, D
+    // one 16-byte record: position, alpha, D, slot
     srec[ebase + lo[c] + rank] = make_int4(i, __float_as_int(expf(score[r * dm.K + k] - lse_tot[r])),
-                                          __float_as_int(ws_D[r]), 0);
+                                          __float_as_int(ws_D[r]), k);
   }
 }
 
@@ -744,6 +290,16 @@ __device__ __forceinline__ uint4 lds_kfrag(const uint16_t* m, int n0) {
 }
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // four floats to bf16, round to nearest even (packed hardware conversion)
+// A operand K^T of a product whose k dimension is the chunk's keys in the
+// lane-held order (k-slot 8g + j of step ks = key 32 ks + 4g + j for j < 4,
+// 32 ks + 16 + 4g + j - 4 otherwise), from the row-major key tile kc: lane
+// (c, g) gets kc[key][n0 + c].
+__device__ __forceinline__ uint4 lds_ktfrag(const uint16_t* kc, int ks, int n0) {
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+  const uint16_t* p = kc + (32 * ks + 4 * g + (c >> 2)) * TP + n0 + 4 * (c & 3);
+  const uint2 lo = lds_tr16(p), hi = lds_tr16(p + 16 * TP);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
 __device__ __forceinline__ uint2 pack4_bf16(const floatx4& v) {
   const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
   uint2 u;
@@ -763,6 +319,7 @@ struct KSmem {
   int rows[kListMax];       // list segment: position of the row
   float aux[kListMax];      // own rows: D; selecting rows: alpha
   float dvl[kListMax];      // own rows: Lambda; selecting rows: D
+  int slotv[kListMax];      // dQ partial slot: selection slot, or K for own rows
   float dkb[kKWaves][D];    // per-wave dk' partials, then the total
   float dql[kKWaves][D];
   float dbw[kKWaves];
@@ -776,18 +333,19 @@ static_assert(sizeof(KWave) >= kChunk * D * sizeof(float), "final reduction buff
 struct KTile {
   uint4 qf[2][2], of[2][2];  // B operands: Q / dO of rows 16 hf + c, features 32 ds + 8g ..
   float aux[2], dvr[2];
-  int rpos[2];
+  int rpos[2];   // position of the row, -1 beyond the tile's rows
+  int slot[2];
 };
 
 __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ Ql,
     const float* __restrict__ ksum, const float* __restrict__ ent,
-    const float* __restrict__ lse_l, const int32_t* __restrict__ idx,
-    const float* __restrict__ score, const float* __restrict__ lse_tot,
+    const float* __restrict__ lse_l, const float* __restrict__ lse_tot,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws_D,
     const int* __restrict__ lstart, const int* __restrict__ llen, const int4* __restrict__ srec,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, uint16_t* __restrict__ dQl) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, uint16_t* __restrict__ dQl,
+    uint16_t* __restrict__ part) {
   extern __shared__ __align__(16) char smem_raw[];
   KSmem& sm = *reinterpret_cast<KSmem*>(smem_raw);
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -841,6 +399,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
       T.aux[hf] = v ? sm.aux[e] : 0.f;
       T.dvr[hf] = sm.dvl[e];
       T.rpos[hf] = v ? pos : -1;
+      T.slot[hf] = sm.slotv[e];
     }
     (void)own_rows;
     return T;
@@ -917,6 +476,29 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         *reinterpret_cast<uint2*>(&wv.as[16 * hf + col][16 * kb + 4 * gl]) = pack4_bf16(a[kb]);
         *reinterpret_cast<uint2*>(&wv.dsm[16 * hf + col][16 * kb + 4 * gl]) = pack4_bf16(d[kb]);
       }
+      // dQ^T / scale of the row from this chunk: K^T dS^T (+ ds^ k' for a
+      // selecting row), to the row's partial slot (lane: features 16 db + 4 gl + r)
+      bf16x8 pf[2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pf[kb >> 1][(kb & 1) * 4 + r] = (__bf16)d[kb][r];
+      const long long prow = (row_base + (long long)max(T.rpos[hf], 0) * dm.H) * (dm.K + 1) + T.slot[hf];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        floatx4 dq = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) dq = mfma(lds_ktfrag(&sm.kc[0][0], ks, 16 * db), pf[ks], dq);
+        if (!own_rows) {
+          const float4 kb4 = *reinterpret_cast<const float4*>(&sm.kbv[16 * db + 4 * gl]);
+          dq[0] = fmaf(dsh, kb4.x, dq[0]);
+          dq[1] = fmaf(dsh, kb4.y, dq[1]);
+          dq[2] = fmaf(dsh, kb4.z, dq[2]);
+          dq[3] = fmaf(dsh, kb4.w, dq[3]);
+        }
+        if (T.rpos[hf] >= 0)
+          *reinterpret_cast<uint2*>(part + prow * D + 16 * db + 4 * gl) = pack4_bf16(dq);
+      }
     }
     __builtin_amdgcn_wave_barrier();
     // dV += A^T dO, dK += dS^T Q over the tile's 32 rows (k dimension = rows)
@@ -955,6 +537,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     for (int fb = 0; fb < 4; ++fb) dkq[fb] = floatx4{0.f, 0.f, 0.f, 0.f};
     float dbp = 0.f;
     const long long bh = (long long)b * dm.H + h;
+    const long long sidx = ((long long)b * dm.NCcap + c) * dm.H + h;
     const int LN = llen[bh * NC + c];
     const long long lsrc = bh * (long long)dm.Tq * dm.K + lstart[bh * NC + c];
     constexpr int kSeg = kListMax - kChunk;
@@ -969,12 +552,15 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         sm.rows[t] = (int)key0 + t;
         sm.aux[t] = ws_D[r];
         sm.dvl[t] = lse_tot[r];
+        sm.slotv[t] = dm.K;
+        sm.kbv[t] = ksum[sidx * D + t];
       }
       for (int e = t; e < ns; e += kKThreads) {
         const int4 rec = srec[lsrc + s0 + e];
         sm.rows[base + e] = rec.x;
         sm.aux[base + e] = __int_as_float(rec.y);
         sm.dvl[base + e] = __int_as_float(rec.z);
+        sm.slotv[base + e] = rec.w;
       }
       __syncthreads();
       int e0 = kTileRows * w;
@@ -1005,11 +591,9 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     }
     if (lane == 0) sm.dbw[w] = dbp;
     __syncthreads();
-    const long long sidx = ((long long)b * dm.NCcap + c) * dm.H + h;
     if (t < D) {  // fixed order over the wavefronts
       sm.dkb[0][t] = (((sm.dkb[0][t] + sm.dkb[1][t]) + sm.dkb[2][t]) + sm.dkb[3][t]) * dm.scale;
       sm.qlv[t] = bf(Ql[sidx * D + t]);
-      sm.kbv[t] = ksum[sidx * D + t];
     }
     __syncthreads();
     if (w == 0) {  // lane j: key j of the chunk
@@ -1095,35 +679,21 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
 }
 
 struct BPlan {
-  int R, Rq, ncr, nqb, nct, nblk;
-  size_t smem, kt_bytes, bnd_bytes, cnt_bytes, ls_bytes, ent_bytes, fill_smem;
+  int nct, nblk;
+  size_t cnt_bytes, ls_bytes, rec_bytes, part_bytes, fill_smem;
 };
 
 bool bwd_plan(const Dims& dm, BPlan* p) {
-  if (!dm.bf16 || dm.d != 64 || dm.Tq < 64 || dm.q_pos0 != 0) return false;
-  int r = kQRows;
-  while (r > 16 && r * dm.K > 2048) r /= 2;
-  int rq = r / dm.G;
-  if (rq < 1) return false;
-  const int ncr = (dm.Tq - 1) / dm.S + 1;
-  while (rq > 1 && q_smem_bytes(rq * dm.G, dm.K, ncr) > 160 * 1024) rq -= max(1, rq / 8);
-  r = rq * dm.G;
-  p->smem = q_smem_bytes(r, dm.K, ncr);
-  if (p->smem > 160 * 1024) return false;
-  p->R = r;
-  p->Rq = rq;
-  p->ncr = ncr;
-  p->nqb = (dm.Tq + rq - 1) / rq;
+  if (!dm.bf16 || dm.d != 64 || dm.Tq < 64 || dm.q_pos0 != 0 || dm.Tq != dm.Tkv) return false;
   p->nct = dm.Tkv / dm.S;
-  p->kt_bytes = (size_t)dm.B * dm.Hkv * p->nct * D * kChunk * 2;
-  p->bnd_bytes = (size_t)dm.B * dm.Hkv * p->nct * sizeof(float2);
   p->nblk = (dm.Tq + kLBlk - 1) / kLBlk;
+  const size_t rows = (size_t)dm.B * dm.Tq * dm.H;
   p->cnt_bytes = (size_t)dm.B * dm.H * p->nct * p->nblk * sizeof(int);
   p->ls_bytes = (size_t)dm.B * dm.H * p->nct * sizeof(int);
-  p->ent_bytes = (size_t)dm.B * dm.H * dm.Tq * dm.K * sizeof(int4);
+  p->rec_bytes = rows * dm.K * sizeof(int4);
+  p->part_bytes = rows * (dm.K + 1) * D * sizeof(uint16_t);
   p->fill_smem = (size_t)p->nct * (kLBlk / 32 + 1) * sizeof(int);
-  if (p->fill_smem > 160 * 1024) return false;
-  return true;
+  return p->fill_smem <= 160 * 1024;
 }
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1133,8 +703,7 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t backward_mfma_ws_bytes(const Dims& dm) {
   BPlan p;
   if (!bwd_plan(dm, &p)) return 0;
-  return up256(p.kt_bytes) + up256(p.bnd_bytes) + up256(p.cnt_bytes) + 2 * up256(p.ls_bytes) +
-         up256(p.ent_bytes);
+  return up256(p.cnt_bytes) + 2 * up256(p.ls_bytes) + up256(p.rec_bytes) + up256(p.part_bytes);
 }
 
 bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void* V,
@@ -1145,10 +714,6 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
   BPlan p;
   if (!bwd_plan(dm, &p)) return false;
   char* base = reinterpret_cast<char*>(ws_mfma);
-  uint16_t* Kt = reinterpret_cast<uint16_t*>(base);
-  base += up256(p.kt_bytes);
-  float2* bnd = reinterpret_cast<float2*>(base);
-  base += up256(p.bnd_bytes);
   int* cnt = reinterpret_cast<int*>(base);
   base += up256(p.cnt_bytes);
   int* lstart = reinterpret_cast<int*>(base);
@@ -1156,26 +721,18 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
   int* llen = reinterpret_cast<int*>(base);
   base += up256(p.ls_bytes);
   int4* srec = reinterpret_cast<int4*>(base);
-  const auto* Qh = reinterpret_cast<const uint16_t*>(Q);
-  const auto* Kh = reinterpret_cast<const uint16_t*>(K);
-  const auto* Vh = reinterpret_cast<const uint16_t*>(V);
-  hipLaunchKernelGGL(k_bwd_prep, dim3(p.nct, dm.Hkv, dm.B), dim3(256), 0, st, dm, p.nct, Kh, Vh,
-                     Kt, bnd);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_q),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.smem);
-  if (e != hipSuccess) {
-    *err = e;
-    return true;
-  }
-  hipLaunchKernelGGL(k_bwd_q, dim3(dm.B * p.nqb * dm.Hkv), dim3(kQThreads), p.smem, st, dm, p.R,
-                     p.Rq, p.ncr, p.nqb, p.nct, Qh, Kh, Vh, Kt, bnd, ksum, idx, score, lse_tot,
-                     reinterpret_cast<const uint16_t*>(O), reinterpret_cast<const uint16_t*>(dO),
-                     reinterpret_cast<uint16_t*>(dQ), ws_D);
+  base += up256(p.rec_bytes);
+  uint16_t* part = reinterpret_cast<uint16_t*>(base);
+  const long long rows = (long long)dm.B * dm.Tq * dm.H;
+  const unsigned rblocks = (unsigned)((rows + 31) / 32);
+  const auto* dOh = reinterpret_cast<const uint16_t*>(dO);
+  hipLaunchKernelGGL(k_bwd_rowd, dim3(rblocks), dim3(256), 0, st, rows,
+                     reinterpret_cast<const uint16_t*>(O), dOh, ws_D);
   hipLaunchKernelGGL(k_sel_count, dim3(p.nblk, dm.H, dm.B), dim3(256), (size_t)p.nct * sizeof(int),
                      st, dm, p.nblk, idx, cnt);
   hipLaunchKernelGGL(k_sel_scan, dim3(dm.H, dm.B), dim3(256), 0, st, dm, p.nblk, cnt, lstart, llen);
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sel_fill),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.fill_smem);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sel_fill),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.fill_smem);
   if (e != hipSuccess) {
     *err = e;
     return true;
@@ -1188,11 +745,18 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
     *err = e;
     return true;
   }
-  hipLaunchKernelGGL(k_bwd_kv_mfma, dim3(p.nct, dm.Hkv, dm.B), dim3(kKThreads), sizeof(KSmem), st, dm, Qh, Kh,
-                     Vh, reinterpret_cast<const uint16_t*>(Ql), ksum, ent, lse_l, idx, score,
-                     lse_tot, reinterpret_cast<const uint16_t*>(dO), ws_D, lstart, llen, srec,
+  hipLaunchKernelGGL(k_bwd_kv_mfma, dim3(p.nct, dm.Hkv, dm.B), dim3(kKThreads), sizeof(KSmem), st, dm,
+                     reinterpret_cast<const uint16_t*>(Q), reinterpret_cast<const uint16_t*>(K),
+                     reinterpret_cast<const uint16_t*>(V), reinterpret_cast<const uint16_t*>(Ql),
+                     ksum, ent, lse_l, lse_tot, dOh, ws_D, lstart, llen, srec,
                      reinterpret_cast<uint16_t*>(dK), reinterpret_cast<uint16_t*>(dV),
-                     reinterpret_cast<uint16_t*>(dQl));
+                     reinterpret_cast<uint16_t*>(dQl), part);
+  if (dm.K + 1 <= 17)
+    hipLaunchKernelGGL(k_dq_reduce<17>, dim3(rblocks), dim3(256), 0, st, dm, rows, idx, part,
+                       reinterpret_cast<uint16_t*>(dQ));
+  else
+    hipLaunchKernelGGL(k_dq_reduce<13>, dim3(rblocks), dim3(256), 0, st, dm, rows, idx, part,
+                       reinterpret_cast<uint16_t*>(dQ));
   *err = hipGetLastError();
   return true;
 }
