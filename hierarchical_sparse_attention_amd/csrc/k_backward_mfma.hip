@@ -471,18 +471,17 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         dbp += dsh;
       }
       if (gl == 0) wv.dsm[16 * hf + col][D] = __builtin_bit_cast(uint16_t, (__bf16)dsh);
+      uint2 dpk[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
+        dpk[kb] = pack4_bf16(d[kb]);
         *reinterpret_cast<uint2*>(&wv.as[16 * hf + col][16 * kb + 4 * gl]) = pack4_bf16(a[kb]);
-        *reinterpret_cast<uint2*>(&wv.dsm[16 * hf + col][16 * kb + 4 * gl]) = pack4_bf16(d[kb]);
+        *reinterpret_cast<uint2*>(&wv.dsm[16 * hf + col][16 * kb + 4 * gl]) = dpk[kb];
       }
       // dQ^T / scale of the row from this chunk: K^T dS^T (+ ds^ k' for a
       // selecting row), to the row's partial slot (lane: features 16 db + 4 gl + r)
-      bf16x8 pf[2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pf[kb >> 1][(kb & 1) * 4 + r] = (__bf16)d[kb][r];
+      const uint4 pf[2] = {make_uint4(dpk[0].x, dpk[0].y, dpk[1].x, dpk[1].y),
+                           make_uint4(dpk[2].x, dpk[2].y, dpk[3].x, dpk[3].y)};
       const long long prow = (row_base + (long long)max(T.rpos[hf], 0) * dm.H) * (dm.K + 1) + T.slot[hf];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
