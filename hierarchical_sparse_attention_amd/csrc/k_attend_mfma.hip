@@ -499,9 +499,11 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   extern __shared__ __align__(16) char smem_raw[];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 15, gl = lane >> 4;
   const int G = dm.G, Ksel = dm.K, S = dm.S;
-  // kv head fastest: neighbouring workgroups (spread over XCDs) share few kv heads
+  // kv head fastest: neighbouring workgroups (spread over XCDs) share few kv heads;
+  // query blocks from the last one down, so the blocks with the most candidate
+  // chunks (the latest positions) start first and the cheap ones fill in
   const int L = blockIdx.x;
-  const int g = L % dm.Hkv, qb = (L / dm.Hkv) % nqb, b = L / (dm.Hkv * nqb);
+  const int g = L % dm.Hkv, qb = nqb - 1 - (L / dm.Hkv) % nqb, b = L / (dm.Hkv * nqb);
   const int qi0 = qb * Rq;
   const int nq = min(Rq, dm.Tq - qi0);
   const int Rv = nq * G;

@@ -348,9 +348,12 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     uint16_t* __restrict__ part) {
   extern __shared__ __align__(16) char smem_raw[];
   KSmem& sm = *reinterpret_cast<KSmem*>(smem_raw);
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 15, gl = lane >> 4;
+  // chunk slowest, from chunk 0 up: the early chunks, which most rows can
+  // select, start first and the cheap late ones fill in
   const int NC = dm.Tkv / dm.S, G = dm.G;
+  const int g = blockIdx.x % dm.Hkv, b = (blockIdx.x / dm.Hkv) % dm.B,
+            c = blockIdx.x / (dm.Hkv * dm.B);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 15, gl = lane >> 4;
   const float scale2 = dm.scale * kLog2e;
   const float inv_scale = 1.0f / dm.scale;
   const long long kv_stride = (long long)dm.Hkv * D;
@@ -744,7 +747,7 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
     *err = e;
     return true;
   }
-  hipLaunchKernelGGL(k_bwd_kv_mfma, dim3(p.nct, dm.Hkv, dm.B), dim3(kKThreads), sizeof(KSmem), st, dm,
+  hipLaunchKernelGGL(k_bwd_kv_mfma, dim3(p.nct * dm.Hkv * dm.B), dim3(kKThreads), sizeof(KSmem), st, dm,
                      reinterpret_cast<const uint16_t*>(Q), reinterpret_cast<const uint16_t*>(K),
                      reinterpret_cast<const uint16_t*>(V), reinterpret_cast<const uint16_t*>(Ql),
                      ksum, ent, lse_l, lse_tot, dOh, ws_D, lstart, llen, srec,
