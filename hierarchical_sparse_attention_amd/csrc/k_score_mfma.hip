@@ -83,9 +83,11 @@ __global__ __launch_bounds__(256) void k_ksplit(Dims dm, int nc, const float* __
 }
 
 // Running top-KM list of one row in registers, sorted by (score desc, chunk asc).
-// Inserting is a fixed compare-exchange pass (no dynamic indexing); a candidate
-// that loses every comparison falls off the end. Candidates arrive in ascending
-// chunk order and compare strictly, so equal scores keep the lower chunk first.
+// Inserting is one pass with no dependency chain (no dynamic indexing): entry k
+// becomes entry k-1 when the candidate beats entry k-1, else the candidate when
+// it beats entry k, else stays; a candidate that beats nothing falls off the end.
+// Candidates arrive in ascending chunk order and compare strictly, so equal
+// scores keep the lower chunk first.
 template <int KM>
 struct TopList {
   float s[KM];
@@ -95,18 +97,47 @@ struct TopList {
     for (int k = 0; k < KM; ++k) { s[k] = -INFINITY; c[k] = 0x7fffffff; }
   }
   __device__ __forceinline__ void insert(float x, int xc) {
+    float ns[KM];
+    int nc[KM];
+    bool gprev = false;
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
-      const bool take = x > s[k];
-      const float ts = s[k];
-      const int tc = c[k];
-      s[k] = take ? x : ts;
-      c[k] = take ? xc : tc;
-      x = take ? ts : x;
-      xc = take ? tc : xc;
+      const bool gk = x > s[k];
+      const float ts = gk ? x : s[k];
+      const int tc = gk ? xc : c[k];
+      ns[k] = gprev ? s[k - (k > 0)] : ts;
+      nc[k] = gprev ? c[k - (k > 0)] : tc;
+      gprev = gk;
     }
+#pragma unroll
+    for (int k = 0; k < KM; ++k) s[k] = ns[k], c[k] = nc[k];
   }
 };
+
+// Sorts 16 (score, chunk) pairs by (score desc, chunk asc) in registers with a
+// bitonic network (80 compare-exchanges at fixed positions).
+__device__ __forceinline__ void sort16(float* x, int* xc) {
+#pragma unroll
+  for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          // first = the one that belongs earlier in (score desc, chunk asc)
+          const bool desc = (i & k) == 0;
+          const bool lbefore = x[l] > x[i] || (x[l] == x[i] && xc[l] < xc[i]);
+          const bool sw = desc ? lbefore : !lbefore;
+          const float a = x[i], bb = x[l];
+          const int ca = xc[i], cb = xc[l];
+          x[i] = sw ? bb : a;
+          x[l] = sw ? a : bb;
+          xc[i] = sw ? cb : ca;
+          xc[l] = sw ? ca : cb;
+        }
+      }
+}
 
 template <int D, int KM>
 __global__ __launch_bounds__(64) void k_score_mfma(Dims dm, int nc, const uint16_t* __restrict__ Q,
@@ -161,8 +192,24 @@ __global__ __launch_bounds__(64) void k_score_mfma(Dims dm, int nc, const uint16
     // lane = row. In sub-blocks of 16 candidates: mark the ones that beat the
     // row's current KM-th score, then insert them (all lanes step together).
     const int lim = min(64, my_n - c0);
+    int sb0 = 0;
+    if (c0 == 0) {
+      // the row's first 16 candidates fill its empty list in one sort
+      float xs[16];
+      int xc[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const bool ok = jj < lim;
+        xs[jj] = ok ? sS[lane][jj] : -INFINITY;
+        xc[jj] = ok ? jj : 0x7fffffff;
+      }
+      sort16(xs, xc);
+#pragma unroll
+      for (int k = 0; k < 16 && k < KM; ++k) top.s[k] = xs[k], top.c[k] = xc[k];
+      sb0 = 1;
+    }
 #pragma unroll 1
-    for (int sb = 0; sb < 4; ++sb) {
+    for (int sb = sb0; sb < 4; ++sb) {
       const float theta = top.s[KM - 1];
       uint32_t mask = 0;
 #pragma unroll
