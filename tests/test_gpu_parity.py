@@ -271,10 +271,15 @@ BWD = {
                                n_planted=2, need_dO=True),
     "bwd_bf16_gqa4": synth.small("bwd_bf16_gqa4", B=1, T=768, H=8, Hkv=2, d=64, K=5,
                                  dtype="bf16", n_planted=1, need_dO=True),
+    # K above the candidate count of every row (padded selections) and above 16
+    "bwd_bf16_k20": synth.small("bwd_bf16_k20", B=1, T=1024, H=2, Hkv=1, d=64, K=20,
+                                dtype="bf16", need_dO=True),
     "bwd_f32": synth.small("bwd_f32", B=1, T=640, H=2, Hkv=1, d=64, K=4, dtype="f32",
                            need_dO=True),
     "bwd_f32_d128": synth.small("bwd_f32_d128", B=1, T=256, H=2, Hkv=1, d=128, K=2,
                                 dtype="f32", need_dO=True),
+    "bwd_bf16_d128": synth.small("bwd_bf16_d128", B=1, T=512, H=4, Hkv=1, d=128, K=3,
+                                 dtype="bf16", need_dO=True),
 }
 
 
