@@ -42,14 +42,16 @@ def lib():
         L.oracle_summarize.argtypes = [ci, ci, ci, ci, ci, ci, ci, cd, _D, _D, ci, ci, _D, _D, _D]
         L.oracle_score_topk.argtypes = [ci, ci, cl, ci, ci, ci, ci, ci, cd, _D, _D, _D, cl, _L,
                                         _I, _D, _D]
+        L.oracle_score_topk_group.argtypes = [ci, ci, cl, ci, ci, ci, ci, ci, ci, cd, _D, _D,
+                                              _D, cl, _L, _I, _D, _D]
         L.oracle_exact_chunk_lse.argtypes = [ci, ci, ci, cl, ci, ci, ci, ci, ci, cd, _D, _D, cl,
                                              _L, _D]
         L.oracle_attend_fuse.argtypes = [ci, ci, ci, cl, ci, ci, ci, ci, ci, cd, _D, _D, _D, _I,
                                          _D, cl, _L, _D, _D, _D]
         L.oracle_backward.argtypes = [ci, ci, ci, cl, ci, ci, ci, ci, ci, ci, cd, _D, _D, _D, _D,
                                       _I, _D, _U8, _U8, _D, _D, _D, _D]
-        for f in (L.oracle_summarize, L.oracle_score_topk, L.oracle_exact_chunk_lse,
-                  L.oracle_attend_fuse, L.oracle_backward):
+        for f in (L.oracle_summarize, L.oracle_score_topk, L.oracle_score_topk_group,
+                  L.oracle_exact_chunk_lse, L.oracle_attend_fuse, L.oracle_backward):
             f.restype = None
         _lib = L
     return _lib
@@ -84,8 +86,11 @@ def summarize(K, Ql, S, scale=0.0, c_begin=0, c_end=None):
     return ksum, ent, lse
 
 
-def score_topk(Q, ksum, ent, S, Ksel, q_pos0=0, scale=0.0, rows=None):
-    """Top-K chunk selection -> (idx [B,Tq,H,K] int32, score [B,Tq,H,K], gap [B,Tq,H])."""
+def score_topk(Q, ksum, ent, S, Ksel, q_pos0=0, scale=0.0, rows=None, group_hkv=None):
+    """Top-K chunk selection -> (idx [B,Tq,H,K] int32, score [B,Tq,H,K], gap [B,Tq,H]).
+
+    group_hkv=Hkv selects one chunk set per kv head by the maximum of the group's
+    head scores (GQA group-max selection); None selects per query head."""
     Q, ksum, ent = _d(Q), _d(ksum), _d(ent)
     B, Tq, H, d = Q.shape
     NC = ksum.shape[1]
@@ -93,8 +98,14 @@ def score_topk(Q, ksum, ent, S, Ksel, q_pos0=0, scale=0.0, rows=None):
     score = np.full((B, Tq, H, Ksel), -np.inf)
     gap = np.full((B, Tq, H), np.nan)
     n, r = _rows(rows)
-    lib().oracle_score_topk(B, Tq, q_pos0, H, d, S, NC, Ksel, scale, _p(Q, _D), _p(ksum, _D),
-                            _p(ent, _D), n, _p(r, _L), _p(idx, _I), _p(score, _D), _p(gap, _D))
+    if group_hkv is None:
+        lib().oracle_score_topk(B, Tq, q_pos0, H, d, S, NC, Ksel, scale, _p(Q, _D),
+                                _p(ksum, _D), _p(ent, _D), n, _p(r, _L), _p(idx, _I),
+                                _p(score, _D), _p(gap, _D))
+    else:
+        lib().oracle_score_topk_group(B, Tq, q_pos0, H, group_hkv, d, S, NC, Ksel, scale,
+                                      _p(Q, _D), _p(ksum, _D), _p(ent, _D), n, _p(r, _L),
+                                      _p(idx, _I), _p(score, _D), _p(gap, _D))
     return idx, score, gap
 
 
@@ -127,10 +138,12 @@ def attend_fuse(Q, K, V, idx, score, S, q_pos0=0, scale=0.0, rows=None):
     return O, lo, lt
 
 
-def forward(Q, K, V, Ql, S, Ksel, q_pos0=0, scale=0.0, rows=None):
-    """Whole forward: summaries, scores/top-K, attend+fuse. Returns a dict."""
+def forward(Q, K, V, Ql, S, Ksel, q_pos0=0, scale=0.0, rows=None, group=False):
+    """Whole forward: summaries, scores/top-K, attend+fuse. Returns a dict.
+    group=True selects one chunk set per kv head (GQA group-max selection)."""
     ksum, ent, lse_l = summarize(K, Ql, S, scale)
-    idx, score, gap = score_topk(Q, ksum, ent, S, Ksel, q_pos0, scale, rows)
+    idx, score, gap = score_topk(Q, ksum, ent, S, Ksel, q_pos0, scale, rows,
+                                 group_hkv=K.shape[2] if group else None)
     O, lo, lt = attend_fuse(Q, K, V, idx, score, S, q_pos0, scale, rows)
     return dict(ksum=ksum, ent=ent, lse_l=lse_l, idx=idx, score=score, gap=gap, O=O,
                 lse_own=lo, lse_tot=lt)

@@ -245,6 +245,51 @@ void oracle_score_topk(int B, int Tq, long q_pos0, int H, int d, int S, int NC, 
   }
 }
 
+// Group-max selection for GQA (page 2 §5.4): the chunk scores of every query
+// head of a kv head are computed as above and aggregated by their maximum over
+// the G heads of the group; the top-K of the aggregated scores (equal scores to
+// the lower chunk) is the one index set of every head of the group. idx is that
+// set in ascending order for each listed row; score is the row's own head score
+// of each selected chunk; gap is taken on the aggregated scores.
+void oracle_score_topk_group(int B, int Tq, long q_pos0, int H, int Hkv, int d, int S, int NC,
+                             int Ksel, double scale, const double* Q, const double* ksum,
+                             const double* ent, long nrows, const long* rows, int* idx,
+                             double* score, double* gap) {
+  Shape sh{B, Tq, 0, H, Hkv, d, S, NC, Ksel, q_pos0, resolve_scale(scale, d)};
+  const int G = H / Hkv;
+  std::vector<long> rl;
+  list_rows(sh, nrows, rows, rl);
+  std::vector<double> own, other, agg;
+  std::vector<int> order;
+  for (long r : rl) {
+    const int h = (int)(r % H);
+    const int i = (int)((r / H) % Tq);
+    const int b = (int)(r / ((long)H * Tq));
+    const int g = h / G;
+    row_scores(sh, Q, ksum, ent, b, i, h, own);
+    agg = own;
+    for (int hh = g * G; hh < g * G + G; ++hh) {
+      row_scores(sh, Q, ksum, ent, b, i, hh, other);
+      for (size_t c = 0; c < agg.size(); ++c) agg[c] = std::max(agg[c], other[c]);
+    }
+    const int n = (int)agg.size();
+    order.resize(n);
+    for (int c = 0; c < n; ++c) order[c] = c;
+    std::sort(order.begin(), order.end(), [&](int a, int c) {
+      if (agg[a] != agg[c]) return agg[a] > agg[c];
+      return a < c;
+    });
+    const int take = std::min(n, Ksel);
+    std::vector<int> sel(order.begin(), order.begin() + take);
+    std::sort(sel.begin(), sel.end());
+    for (int k = 0; k < Ksel; ++k) {
+      idx[r * Ksel + k] = k < take ? sel[k] : -1;
+      score[r * Ksel + k] = k < take ? own[sel[k]] : -INFINITY;
+    }
+    if (gap) gap[r] = n > Ksel ? agg[order[Ksel - 1]] - agg[order[Ksel]] : INFINITY;
+  }
+}
+
 // Exact log chunk masses log Z_{i,c} (page 2 §3, naive block sparse attention)
 // of every candidate chunk c < c_i; entries c >= c_i are -inf. out is [rows][NC].
 void oracle_exact_chunk_lse(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d, int S,

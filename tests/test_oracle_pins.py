@@ -188,6 +188,63 @@ def test_topk_exact_tie_goes_to_lower_chunk():
     assert idx[0, row, 0, 0] == 1 and gap[0, row, 0] == 0.0
 
 
+# ---------------------------------------------------------------- GQA group-max top-K
+def _gqa_case(seed, T=512, S=16, H=8, Hkv=2, d=16):
+    Q, K, V, Ql = _small(seed, T=T, S=S, H=H, Hkv=Hkv, d=d)
+    ksum, ent, _ = oracle.summarize(K, Ql, S)
+    return Q, ksum, ent, S
+
+
+def test_group_topk_brute_force():
+    """Group-max selection (page 2 §5.4): per kv head, the top-K of the maximum over the
+    group's query-head scores (ties to the lower id) is every head's index set, and
+    each head keeps its own score; checked by a full sort of the aggregated scores."""
+    Q, ksum, ent, S = _gqa_case(61)
+    B, T, H, d = Q.shape
+    Hkv, G, Ksel = 2, 4, 5
+    idx_all, sc_all = all_scores(Q, ksum, ent, S)
+    idx, score, gap = oracle.score_topk(Q, ksum, ent, S, Ksel, group_hkv=Hkv)
+    for i in range(0, T, 7):
+        n = i // S
+        for g in range(Hkv):
+            heads = range(g * G, g * G + G)
+            agg = [max(sc_all[0, i, h, c] for h in heads) for c in range(n)]
+            cand = sorted(range(n), key=lambda c: (-agg[c], c))
+            take = sorted(cand[:Ksel])
+            want = take + [-1] * (Ksel - len(take))
+            for h in heads:
+                assert list(idx[0, i, h]) == want
+                np.testing.assert_array_equal(score[0, i, h, : len(take)], sc_all[0, i, h, take])
+                assert np.all(np.isneginf(score[0, i, h, len(take):]))
+                if n > Ksel:
+                    assert gap[0, i, h] == agg[cand[Ksel - 1]] - agg[cand[Ksel]]
+
+
+def test_group_topk_one_head_per_group_is_per_head_selection():
+    """G = 1: the group maximum is the head's own score, so both modes agree exactly."""
+    Q, ksum, ent, S = _gqa_case(71, H=2, Hkv=2)
+    a = oracle.score_topk(Q, ksum, ent, S, 4)
+    b = oracle.score_topk(Q, ksum, ent, S, 4, group_hkv=2)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_group_topk_identical_heads():
+    """Heads of a group with the same query and landmark queries have equal scores, so
+    the group selection is each head's own selection."""
+    S, d, H, Hkv = 16, 16, 4, 2
+    Q, K, V, Ql = _small(81, T=384, S=S, H=H, Hkv=Hkv, d=d)
+    for g in range(Hkv):
+        for h in range(g * 2 + 1, g * 2 + 2):
+            Q[:, :, h] = Q[:, :, g * 2]
+            Ql[:, :, h] = Ql[:, :, g * 2]
+    ksum, ent, _ = oracle.summarize(K, Ql, S)
+    a = oracle.score_topk(Q, ksum, ent, S, 3)
+    b = oracle.score_topk(Q, ksum, ent, S, 3, group_hkv=Hkv)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
 # ---------------------------------------------------------------- attend + fuse
 @pytest.mark.parametrize("H,Hkv", [(2, 1), (4, 2)])
 def test_full_attention_equivalence(H, Hkv):
