@@ -316,46 +316,52 @@ def main():
         return ev[0].elapsed_time(ev[1]) / reps
 
     if not args.no_extra_configs:
-        for name in ("prefill_7b_gqa", "train_345m"):
+        # the 7B-class GQA prefill also with group-max selection (one chunk set per kv head)
+        for name, modes in (("prefill_7b_gqa", (False, True)), ("train_345m", (False,))):
             wx = synth.workloads()[name]
             log(f"generating {name} inputs")
             xx = synth.make_inputs(wx)
             keys = ("Q", "K", "V", "Ql") + (("dO",) if wx.need_dO else ())
             tx = {k: torch.from_numpy(xx[k]).to(dev, torch.bfloat16) for k in keys}
             del xx
-            fw = hsa.forward(tx["Q"], tx["K"], tx["V"], tx["Ql"], wx.K, wx.S)
-            ksx, enx, llx, ix, scx = (fw[k] for k in ("ksum", "ent", "lse_l", "idx", "score"))
-            Ox, lox, ltx = fw["O"], fw["lse_own"], fw["lse_tot"]
-            calls = {
-                "summarize": lambda: hsa.summarize(tx["K"], tx["Ql"], wx.S, ksum=ksx, ent=enx,
-                                                   lse_l=llx),
-                "score_topk": lambda: hsa.score_topk(tx["Q"], ksx, enx, wx.K, wx.S, 0, wx.T,
-                                                     Hkv=wx.Hkv, idx=ix, score=scx),
-                "attend_fuse": lambda: hsa.attend_fuse(tx["Q"], tx["K"], tx["V"], ix, scx, wx.S,
-                                                       O=Ox, lse_own=lox, lse_tot=ltx),
-            }
-            if wx.need_dO:
-                calls["backward"] = lambda: hsa.backward(tx["Q"], tx["K"], tx["V"], tx["Ql"], ksx,
-                                                         enx, llx, ix, scx, ltx, Ox, tx["dO"],
-                                                         wx.S)
-            for fn in calls.values():
-                fn()
-            torch.cuda.synchronize()
-            km = {k: ev_ms(fn, 5) for k, fn in calls.items()}
-            cx = algorithmic_counts(wx, ix.cpu().numpy())
-            fwd_ms = km["summarize"] + km["score_topk"] + km["attend_fuse"]
-            rec = {"kernels_ms": km, "forward_ms": fwd_ms,
-                   "attend_tflops": cx["attend_fuse"]["flops"] / (km["attend_fuse"] * 1e-3) / 1e12,
-                   "score_topk_tflops": cx["score_topk"]["flops"] / (km["score_topk"] * 1e-3) / 1e12,
-                   "summarize_gbs": cx["summarize"]["bytes"] / (km["summarize"] * 1e-3) / 1e9}
-            if wx.need_dO:
-                bwd_flops = 10 * wx.d * cx["key_visits"]
-                rec["backward_tflops"] = bwd_flops / (km["backward"] * 1e-3) / 1e12
-                rec["train_tokens_per_s"] = wx.B * wx.T / ((fwd_ms + km["backward"]) * 1e-3)
-            else:
-                rec["prefill_tokens_per_s"] = wx.B * wx.T / (fwd_ms * 1e-3)
-            extra[name] = rec
-            del tx, fw, calls
+            for group in modes:
+                fw = hsa.forward(tx["Q"], tx["K"], tx["V"], tx["Ql"], wx.K, wx.S, group=group)
+                ksx, enx, llx, ix, scx = (fw[k] for k in ("ksum", "ent", "lse_l", "idx", "score"))
+                Ox, lox, ltx = fw["O"], fw["lse_own"], fw["lse_tot"]
+                calls = {
+                    "summarize": lambda: hsa.summarize(tx["K"], tx["Ql"], wx.S, ksum=ksx,
+                                                       ent=enx, lse_l=llx),
+                    "score_topk": lambda: hsa.score_topk(tx["Q"], ksx, enx, wx.K, wx.S, 0, wx.T,
+                                                         Hkv=wx.Hkv, idx=ix, score=scx,
+                                                         group=group),
+                    "attend_fuse": lambda: hsa.attend_fuse(tx["Q"], tx["K"], tx["V"], ix, scx,
+                                                           wx.S, O=Ox, lse_own=lox, lse_tot=ltx),
+                }
+                if wx.need_dO:
+                    calls["backward"] = lambda: hsa.backward(tx["Q"], tx["K"], tx["V"], tx["Ql"],
+                                                             ksx, enx, llx, ix, scx, ltx, Ox,
+                                                             tx["dO"], wx.S)
+                for fn in calls.values():
+                    fn()
+                torch.cuda.synchronize()
+                km = {k: ev_ms(fn, 5) for k, fn in calls.items()}
+                cx = algorithmic_counts(wx, ix.cpu().numpy())
+                fwd_ms = km["summarize"] + km["score_topk"] + km["attend_fuse"]
+                rec = {"kernels_ms": km, "forward_ms": fwd_ms,
+                       "attend_tflops": cx["attend_fuse"]["flops"] / (km["attend_fuse"] * 1e-3) / 1e12,
+                       "score_topk_tflops": cx["score_topk"]["flops"] / (km["score_topk"] * 1e-3) / 1e12,
+                       "summarize_gbs": cx["summarize"]["bytes"] / (km["summarize"] * 1e-3) / 1e9}
+                if wx.need_dO:
+                    bwd_flops = 10 * wx.d * cx["key_visits"]
+                    rec["backward_tflops"] = bwd_flops / (km["backward"] * 1e-3) / 1e12
+                    rec["train_tokens_per_s"] = wx.B * wx.T / ((fwd_ms + km["backward"]) * 1e-3)
+                else:
+                    rec["prefill_tokens_per_s"] = wx.B * wx.T / (fwd_ms * 1e-3)
+                if group:
+                    rec["selection"] = "group max over the 4 query heads of each kv head"
+                extra[name + ("_group_max" if group else "")] = rec
+                del fw, calls
+            del tx
             torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU baseline

@@ -29,7 +29,7 @@ class hils_dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Tq", ctypes.c_int32), ("Tkv", ctypes.c_int32),
                 ("Tkv_cap", ctypes.c_int32), ("NC_cap", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32), ("S", ctypes.c_int32),
-                ("K", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("dtype", ctypes.c_int32), ("select_mode", ctypes.c_int32),
                 ("q_pos0", ctypes.c_int64), ("scale", ctypes.c_float),
                 ("reserved2", ctypes.c_float)]
 
@@ -77,8 +77,9 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def make_dims(B, Tq, Tkv, H, Hkv, d, S, K, dtype, q_pos0=0, scale=0.0, Tkv_cap=0,
-              NC_cap=0) -> hils_dims:
-    return hils_dims(B, Tq, Tkv, Tkv_cap, NC_cap, H, Hkv, d, S, K, dtype, 0, q_pos0, scale, 0.0)
+              NC_cap=0, select_mode=0) -> hils_dims:
+    return hils_dims(B, Tq, Tkv, Tkv_cap, NC_cap, H, Hkv, d, S, K, dtype, select_mode, q_pos0,
+                     scale, 0.0)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -144,8 +145,9 @@ def summarize(K: torch.Tensor, Ql: torch.Tensor, S: int = 64, c_begin: int = 0,
 
 def score_topk(Q: torch.Tensor, ksum: torch.Tensor, ent: torch.Tensor, K_sel: int, S: int = 64,
                q_pos0: int = 0, Tkv: Optional[int] = None, scale: float = 0.0, Hkv: int = 1,
-               idx=None, score=None):
-    """Top-K chunk selection for query rows at positions q_pos0.. -> (idx int32, score f32)."""
+               idx=None, score=None, group: bool = False):
+    """Top-K chunk selection for query rows at positions q_pos0.. -> (idx int32, score f32).
+    group=True selects one chunk set per kv head by the group maximum of the scores."""
     B, Tq, H, d = Q.shape
     NCcap = ksum.shape[1]
     Tkv = q_pos0 + Tq if Tkv is None else Tkv
@@ -157,7 +159,7 @@ def score_topk(Q: torch.Tensor, ksum: torch.Tensor, ent: torch.Tensor, K_sel: in
     _need(idx, "idx", (B, Tq, H, K_sel), torch.int32)
     _need(score, "score", (B, Tq, H, K_sel), torch.float32)
     dims = make_dims(B, Tq, Tkv, H, Hkv, d, S, K_sel, _dtype_code(Q), q_pos0, scale,
-                     max(Tkv, NCcap * S), NCcap)
+                     max(Tkv, NCcap * S), NCcap, 1 if group else 0)
     ws, n = _workspace(dims, OP_SCORE_TOPK, dev)
     _check("hils_score_topk", lib().hils_score_topk(
         ctypes.byref(dims), _ptr(Q), _ptr(ksum), _ptr(ent), _ptr(idx), _ptr(score), _ptr(ws), n,
@@ -189,10 +191,11 @@ def attend_fuse(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Te
     return O, lse_own, lse_tot
 
 
-def forward(Q, K, V, Ql, K_sel: int, S: int = 64, scale: float = 0.0):
+def forward(Q, K, V, Ql, K_sel: int, S: int = 64, scale: float = 0.0, group: bool = False):
     """Prefill forward: summaries, selection, attention. Returns a dict of tensors."""
     ksum, ent, lse_l = summarize(K, Ql, S, scale=scale)
-    idx, score = score_topk(Q, ksum, ent, K_sel, S, 0, K.shape[1], scale, Hkv=K.shape[2])
+    idx, score = score_topk(Q, ksum, ent, K_sel, S, 0, K.shape[1], scale, Hkv=K.shape[2],
+                            group=group)
     O, lse_own, lse_tot = attend_fuse(Q, K, V, idx, score, S, 0, scale=scale)
     return dict(ksum=ksum, ent=ent, lse_l=lse_l, idx=idx, score=score, O=O, lse_own=lse_own,
                 lse_tot=lse_tot)

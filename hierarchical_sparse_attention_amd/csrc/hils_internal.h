@@ -14,6 +14,7 @@ constexpr int kMaxSel = 64;  // largest supported top-K
 struct Dims {
   int B, Tq, Tkv, Tcap, NCcap, H, Hkv, G, d, S, K;
   bool bf16;
+  bool group_sel;  // one chunk set per kv head by the group maximum of the scores
   long long q_pos0;
   float scale;
 };
@@ -235,6 +236,11 @@ hipError_t launch_summarize(const Dims& dm, const void* K, const void* Ql, int c
 
 size_t score_topk_ws_bytes(const Dims& dm);
 size_t score_mfma_prefill_ws_bytes(const Dims& dm);
+// bf16 group-max selection on matrix cores (G = 2 or 4); same workspace as prefill
+bool score_mfma_group_applies(const Dims& dm);
+hipError_t launch_score_mfma_group(const Dims& dm, const void* Q, const float* ksum,
+                                   const float* ent, int32_t* idx, float* score, void* ws,
+                                   hipStream_t st);
 hipError_t launch_score_mfma_prefill(const Dims& dm, const void* Q, const float* ksum,
                                      const float* ent, int32_t* idx, float* score, void* ws,
                                      hipStream_t st);

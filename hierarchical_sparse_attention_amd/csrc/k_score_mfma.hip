@@ -248,6 +248,169 @@ __global__ __launch_bounds__(64) void k_score_mfma(Dims dm, int nc, const uint16
   }
 }
 
+// GQA group-max selection on matrix cores (note §5.4), G = 2 or 4. A wavefront
+// owns P = 64 / G positions of one kv head; its 64 MFMA rows are (head hh,
+// position p) in head-major order, so every 16-row block belongs to one head and
+// is scored against that head's summary keys (the same block sequence as the
+// per-head kernel). Lanes p < P rank the candidates by the maximum of the G head
+// scores with the same register top-K; a second pass scores the blocks again and
+// writes each head's own score of the selected chunks.
+template <int D, int KM, int G>
+__global__ __launch_bounds__(64) void k_score_mfma_group(Dims dm, int nc,
+                                                         const uint16_t* __restrict__ Q,
+                                                         const uint16_t* __restrict__ ks,
+                                                         const float* __restrict__ ent,
+                                                         int32_t* __restrict__ idx,
+                                                         float* __restrict__ score) {
+  constexpr int P = 64 / G;    // positions per wavefront
+  constexpr int MBH = P / 16;  // 16-row blocks per head
+  static_assert(G == 2 || G == 4, "group size");
+  __shared__ float sS[64][65];
+  __shared__ float gS[P][65];  // group maximum per (position, candidate)
+  const int lane = threadIdx.x, c = lane & 15, g = lane >> 4;
+  const int gk = blockIdx.y, b = blockIdx.z, K = dm.K;
+  const int i0 = blockIdx.x * P;
+  const int npos = min(P, dm.Tq - i0);
+  const int p_me = min(lane, P - 1);  // clamped: lanes >= P only read in-bounds rows
+  const int my_n = lane < npos ? (int)((dm.q_pos0 + i0 + lane) / dm.S) : 0;
+  const int nmax = (int)((dm.q_pos0 + i0 + npos - 1) / dm.S);
+
+  // A fragments: row m = hh P + p (head gk G + hh, position i0 + p)
+  uint4 qa[4][D / 32];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = 16 * mb + c, hh = m / P, p = m % P;
+    const bool v = p < npos;
+    const long long off = (((long long)b * dm.Tq + i0 + p) * dm.H + (long long)gk * G + hh) * D;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+      qa[mb][ds] = v ? *reinterpret_cast<const uint4*>(Q + off + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
+  }
+  // scores of candidates c0 .. c0 + 63 for all 64 rows into sS
+  auto score_blocks = [&](int c0) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int chunk = c0 + 16 * nb + c;
+      const bool cv = chunk < nmax;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const long long hrow = ((long long)b * nc + (cv ? chunk : 0)) * dm.H + (long long)gk * G + hh;
+        bf16x8 hi[D / 32], lo[D / 32];
+#pragma unroll
+        for (int ds = 0; ds < D / 32; ++ds) {
+          const uint4 uh = cv ? *reinterpret_cast<const uint4*>(ks + hrow * 2 * D + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
+          const uint4 ul = cv ? *reinterpret_cast<const uint4*>(ks + hrow * 2 * D + D + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
+          hi[ds] = as_bf16x8(uh);
+          lo[ds] = as_bf16x8(ul);
+        }
+        const float e = cv ? ent[((long long)b * dm.NCcap + chunk) * dm.H + (long long)gk * G + hh] : 0.f;
+#pragma unroll
+        for (int mbh = 0; mbh < MBH; ++mbh) {
+          const int mb = hh * MBH + mbh;
+          const floatx4 acc = score_block<D>(qa[mb], hi, lo);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sS[16 * mb + 4 * g + r][16 * nb + c] = fmaf(acc[r], dm.scale, e);
+        }
+      }
+    }
+  };
+  auto gscore = [&](int j) -> float { return gS[p_me][j]; };
+
+  TopList<KM> top;
+  top.init();
+  for (int c0 = 0; c0 < nmax; c0 += 64) {
+    score_blocks(c0);
+    __syncthreads();
+    // group maxima, all lanes: element x = (position x / 64, candidate x % 64)
+#pragma unroll
+    for (int x = lane; x < P * 64; x += 64) {
+      const int p = x / 64, j = x % 64;
+      float v = sS[p][j];
+#pragma unroll
+      for (int hh = 1; hh < G; ++hh) v = fmaxf(v, sS[hh * P + p][j]);
+      gS[p][j] = v;
+    }
+    __syncthreads();
+    const int lim = min(64, my_n - c0);
+    int sb0 = 0;
+    if (c0 == 0) {
+      float xs[16];
+      int xc[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const bool ok = jj < lim;
+        xs[jj] = ok ? gscore(jj) : -INFINITY;
+        xc[jj] = ok ? jj : 0x7fffffff;
+      }
+      sort16(xs, xc);
+#pragma unroll
+      for (int k = 0; k < 16 && k < KM; ++k) top.s[k] = xs[k], top.c[k] = xc[k];
+      sb0 = 1;
+    }
+#pragma unroll 1
+    for (int sb = sb0; sb < 4; ++sb) {
+      const float theta = top.s[KM - 1];
+      uint32_t mask = 0;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int j = 16 * sb + jj;
+        mask |= (j < lim && gscore(j) > theta) ? (1u << jj) : 0u;
+      }
+      int todo = __popc(mask);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) todo = max(todo, __shfl_xor(todo, o, 64));
+      for (int q = 0; q < todo; ++q) {
+        const int jj = mask ? __ffs(mask) - 1 : 0;
+        const float x = mask ? gscore(16 * sb + jj) : -INFINITY;
+        mask &= mask - 1;
+        top.insert(x, c0 + 16 * sb + jj);
+      }
+    }
+    __syncthreads();
+  }
+  // ranks in ascending chunk order, index sets of the G heads
+  const int cnt = min(K, my_n);
+  int rk[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    int rank = 0;
+#pragma unroll
+    for (int k2 = 0; k2 < KM; ++k2) rank += (k2 < cnt && top.c[k2] < top.c[k]) ? 1 : 0;
+    rk[k] = rank;
+  }
+  const bool own = lane < npos;
+  const long long orow = ((long long)b * dm.Tq + i0 + p_me) * dm.H + (long long)gk * G;
+  if (own) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const long long o = (orow + hh) * K;
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (k < cnt) idx[o + rk[k]] = top.c[k];
+      for (int k = cnt; k < K; ++k) {
+        idx[o + k] = -1;
+        score[o + k] = -INFINITY;
+      }
+    }
+  }
+  // second pass: each head's own score of the selected chunks
+  for (int c0 = 0; c0 < nmax; c0 += 64) {
+    score_blocks(c0);
+    __syncthreads();
+    if (own) {
+#pragma unroll
+      for (int k = 0; k < KM; ++k) {
+        const int ch = top.c[k];
+        if (k < cnt && ch >= c0 && ch < c0 + 64) {
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) score[(orow + hh) * K + rk[k]] = sS[hh * P + p_me][ch - c0];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Decode split: grid (splits, rows); a workgroup of 4 wavefronts scores the
 // kSplitM candidates of one row, 32 per wavefront (the row sits in M position 0
 // of each 16x16 block; other positions are zero), and writes the split's local
@@ -454,6 +617,39 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_score_row_mfma(
 }
 
 }  // namespace
+
+bool score_mfma_group_applies(const Dims& dm) { return dm.bf16 && (dm.G == 2 || dm.G == 4); }
+
+hipError_t launch_score_mfma_group(const Dims& dm, const void* Q, const float* ksum,
+                                   const float* ent, int32_t* idx, float* score, void* ws,
+                                   hipStream_t st) {
+  const int nc = max(1, (int)((dm.q_pos0 + dm.Tq - 1) / dm.S));
+  uint16_t* ks = reinterpret_cast<uint16_t*>(ws);
+  const long long n8 = (long long)dm.B * nc * dm.H * (dm.d / 8);
+  const int grid = (int)std::min<long long>((n8 + 255) / 256, 4096);
+  const int P = 64 / dm.G;
+  dim3 g3((dm.Tq + P - 1) / P, dm.Hkv, dm.B);
+  const auto* Qh = reinterpret_cast<const uint16_t*>(Q);
+#define HILS_GRP(DD, KMM, GG) \
+  hipLaunchKernelGGL((k_score_mfma_group<DD, KMM, GG>), g3, dim3(64), 0, st, dm, nc, Qh, ks, ent, idx, score)
+  if (dm.d == 64) {
+    hipLaunchKernelGGL((k_ksplit<64>), dim3(grid), dim3(256), 0, st, dm, nc, ksum, ks);
+    if (dm.K <= 16) {
+      if (dm.G == 2) HILS_GRP(64, 16, 2); else HILS_GRP(64, 16, 4);
+    } else {
+      if (dm.G == 2) HILS_GRP(64, 64, 2); else HILS_GRP(64, 64, 4);
+    }
+  } else {
+    hipLaunchKernelGGL((k_ksplit<128>), dim3(grid), dim3(256), 0, st, dm, nc, ksum, ks);
+    if (dm.K <= 16) {
+      if (dm.G == 2) HILS_GRP(128, 16, 2); else HILS_GRP(128, 16, 4);
+    } else {
+      if (dm.G == 2) HILS_GRP(128, 64, 2); else HILS_GRP(128, 64, 4);
+    }
+  }
+#undef HILS_GRP
+  return hipGetLastError();
+}
 
 size_t score_mfma_prefill_ws_bytes(const Dims& dm) {
   const int nc = (int)((dm.q_pos0 + dm.Tq - 1) / dm.S);

@@ -12,6 +12,7 @@
 //    local top-K to the workspace, and a merge kernel ranks the union. The global
 //    top-K is a subset of the union of local top-Ks, so the merge is exact.
 // The order key is total: (score descending, chunk id ascending).
+#include <algorithm>
 #include <cfloat>
 #include <climits>
 
@@ -98,6 +99,98 @@ __global__ __launch_bounds__(256) void k_score_rows(Dims dm, const void* __restr
     idx[o + k] = -1;
     score[o + k] = -INFINITY;
   }
+}
+
+// Group-max selection (note §5.4, GQA): the chunk scores of the G query heads of
+// a kv head are aggregated by their maximum and the top K of that is the chunk
+// set of the whole group. Thread t owns query head g G + t % G of position
+// blockIdx.x * (R / G) + t / G, so the G heads of a position sit in neighbouring
+// lanes: they take the group maximum with lane shuffles and keep identical lists
+// ordered by (group score desc, chunk asc), each carrying its own head's score
+// per entry. Summaries of the G heads are staged in LDS in blocks of cpb chunks.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void k_score_group(Dims dm, int cpb, const void* __restrict__ Q,
+                                                     const float* __restrict__ ksum,
+                                                     const float* __restrict__ ent,
+                                                     int32_t* __restrict__ idx,
+                                                     float* __restrict__ score) {
+  extern __shared__ __align__(16) float gsm[];
+  const int R = blockDim.x, t = threadIdx.x, G = dm.G, K = dm.K;
+  float* kb = gsm;                                   // [cpb][G][D]
+  float* eb = kb + cpb * G * D;                      // [cpb][G]
+  float* ls = eb + cpb * G;                          // [K][R] group scores
+  float* lh = ls + K * R;                            // [K][R] own head scores
+  int* li = reinterpret_cast<int*>(lh + K * R);      // [K][R] chunk ids
+  const int g = blockIdx.y, b = blockIdx.z, hh = t % G;
+  const int P = R / G;
+  const int i = blockIdx.x * P + t / G;
+  const bool valid = i < dm.Tq;
+  const int h = g * G + hh;
+  const int last = min(dm.Tq, (int)(blockIdx.x + 1) * P) - 1;
+  const int n = valid ? (int)((dm.q_pos0 + i) / dm.S) : 0;
+  const int nmax = (int)((dm.q_pos0 + last) / dm.S);
+  float q[D];
+  if (valid) {
+    load_row<BF16, D>(Q, (((long long)b * dm.Tq + i) * dm.H + h) * D, q);
+  } else {
+#pragma unroll
+    for (int e = 0; e < D; ++e) q[e] = 0.0f;
+  }
+  int cnt = 0;
+  for (int c0 = 0; c0 < nmax; c0 += cpb) {
+    const int nb = min(cpb, nmax - c0);
+    for (int x = t; x < nb * G * D; x += R) {
+      const int cc = x / (G * D), hx = (x / D) % G, e = x % D;
+      kb[x] = ksum[(((long long)b * dm.NCcap + c0 + cc) * dm.H + g * G + hx) * D + e];
+    }
+    for (int x = t; x < nb * G; x += R)
+      eb[x] = ent[((long long)b * dm.NCcap + c0 + x / G) * dm.H + g * G + x % G];
+    __syncthreads();
+    const int lim = min(nb, n - c0);  // equal for the G heads of a position
+    for (int cc = 0; cc < lim; ++cc) {
+      const float s = chunk_score<D>(q, kb + (cc * G + hh) * D, dm.scale, eb[cc * G + hh]);
+      float gs = s;
+      for (int o = 1; o < G; o <<= 1) gs = fmaxf(gs, __shfl_xor(gs, o, 64));
+      const int c = c0 + cc;
+      if (cnt < K || gs > ls[(K - 1) * R + t]) {
+        int pos = cnt < K ? cnt : K - 1;
+        while (pos > 0) {
+          const float prev = ls[(pos - 1) * R + t];
+          if (!(prev < gs)) break;  // equal scores keep the earlier (lower) chunk first
+          ls[pos * R + t] = prev;
+          lh[pos * R + t] = lh[(pos - 1) * R + t];
+          li[pos * R + t] = li[(pos - 1) * R + t];
+          --pos;
+        }
+        ls[pos * R + t] = gs;
+        lh[pos * R + t] = s;
+        li[pos * R + t] = c;
+        if (cnt < K) ++cnt;
+      }
+    }
+    __syncthreads();
+  }
+  if (!valid) return;
+  const long long o = (((long long)b * dm.Tq + i) * dm.H + h) * K;
+  for (int k = 0; k < cnt; ++k) {
+    const int c = li[k * R + t];
+    int rank = 0;
+    for (int k2 = 0; k2 < cnt; ++k2) rank += li[k2 * R + t] < c;
+    idx[o + rank] = c;
+    score[o + rank] = lh[k * R + t];
+  }
+  for (int k = cnt; k < K; ++k) {
+    idx[o + k] = -1;
+    score[o + k] = -INFINITY;
+  }
+}
+
+// chunks per LDS block of the group kernel: as many as 32 KiB hold, 1 to 8
+int group_cpb(const Dims& dm) {
+  return std::max(1, std::min(8, 32768 / (dm.G * (dm.d + 1) * (int)sizeof(float))));
+}
+size_t group_smem_bytes(const Dims& dm, int R) {
+  return ((size_t)group_cpb(dm) * dm.G * (dm.d + 1) + 3 * (size_t)dm.K * R) * sizeof(float);
 }
 
 // Split path, stage 1: grid (splits, rows); thread t scores candidate split*256+t.
@@ -209,6 +302,19 @@ bool use_split(const Dims& dm) {
 template <bool BF16, int D>
 hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const float* ent,
                     int32_t* idx, float* score, void* ws, hipStream_t st) {
+  if (dm.group_sel && score_mfma_group_applies(dm))
+    return launch_score_mfma_group(dm, Q, ksum, ent, idx, score, ws, st);
+  if (dm.group_sel && dm.G > 1) {
+    const int R = rows_per_wg(dm.K);  // a multiple of every supported G (powers of two <= 64)
+    const int P = R / dm.G;
+    const size_t smem = group_smem_bytes(dm, R);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_score_group<BF16, D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_score_group<BF16, D>), dim3((dm.Tq + P - 1) / P, dm.Hkv, dm.B),
+                       dim3(R), smem, st, dm, group_cpb(dm), Q, ksum, ent, idx, score);
+    return hipGetLastError();
+  }
   if (use_split(dm)) {
     hipError_t err = hipSuccess;
     if (score_row_mfma_try(dm, Q, ksum, ent, idx, score, st, &err)) return err;
@@ -252,6 +358,8 @@ hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const floa
 }  // namespace
 
 size_t score_topk_ws_bytes(const Dims& dm) {
+  if (dm.group_sel && score_mfma_group_applies(dm)) return score_mfma_prefill_ws_bytes(dm);
+  if (dm.group_sel && dm.G > 1) return 0;
   if (!use_split(dm)) return dm.bf16 ? score_mfma_prefill_ws_bytes(dm) : 0;
   const long long rows = (long long)dm.B * dm.Tq * dm.H;
   return (size_t)rows * split_count(dm) * dm.K * (sizeof(float) + sizeof(int));

@@ -54,6 +54,12 @@ typedef enum {
 
 typedef enum { HILS_F32 = 0, HILS_BF16 = 1 } hils_dtype;
 
+/* Chunk selection of hils_score_topk. PER_HEAD: every query head selects its own
+ * chunks. GROUP_MAX (note §5.4, GQA): the chunk scores of the G = H/Hkv query
+ * heads of a kv head are aggregated by their maximum and the top K of that is
+ * the one chunk set of all G heads; requires G to be a power of two. */
+typedef enum { HILS_SELECT_PER_HEAD = 0, HILS_SELECT_GROUP_MAX = 1 } hils_select;
+
 /* A hipStream_t passed as an opaque pointer; NULL means the default stream. */
 typedef void* hils_stream;
 
@@ -69,7 +75,7 @@ typedef struct {
   int32_t S;        /* chunk size (64) */
   int32_t K;        /* selected past chunks per (query, head), 1..64 */
   int32_t dtype;    /* hils_dtype of Q, K, V, Ql, O, dO, dQ, dK, dV, dQl */
-  int32_t reserved; /* must be 0 */
+  int32_t select_mode; /* hils_select of hils_score_topk; 0 for the other calls */
   int64_t q_pos0;   /* absolute position of query row 0; q_pos0 + Tq <= Tkv */
   float scale;      /* softmax scale; 0 => 1/sqrt(d) */
   float reserved2;  /* must be 0 */
@@ -108,7 +114,10 @@ hils_status hils_summarize(const hils_dims* dims, const void* K, const void* Ql,
  * The min(K, n_i) best candidates (score descending, equal scores to the
  * lower chunk id) are written to idx in ascending chunk id, padded with -1,
  * and their scores to score, padded with -inf. ksum/ent must hold every
- * chunk below floor((q_pos0+Tq-1)/S).
+ * chunk below floor((q_pos0+Tq-1)/S). With dims->select_mode ==
+ * HILS_SELECT_GROUP_MAX the ranking uses max over the kv group's query heads
+ * of s^ (same order key); idx is then equal for the heads of a group and each
+ * head's score holds its own s^ of the selected chunks.
  */
 hils_status hils_score_topk(const hils_dims* dims, const void* Q, const float* ksum,
                             const float* ent, int32_t* idx, float* score, void* ws,

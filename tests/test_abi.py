@@ -58,13 +58,19 @@ def test_dims_validation(kw, status):
     assert st == status
 
 
-def test_reserved_fields_must_be_zero():
-    d = base()
-    d.reserved = 1
-    assert ws_size(d, hsa.OP_SUMMARIZE)[0] == 1
+def test_reserved_field_and_select_mode():
     d = base()
     d.reserved2 = 1.0
     assert ws_size(d, hsa.OP_SUMMARIZE)[0] == 1
+    d = base()
+    d.select_mode = 2                                    # no such selection
+    assert ws_size(d, hsa.OP_SCORE_TOPK)[0] == 1
+    d = base(H=8, Hkv=2)
+    d.select_mode = 1                                    # group max, G = 4
+    assert ws_size(d, hsa.OP_SCORE_TOPK)[0] == 0
+    d = base(H=6, Hkv=2)
+    d.select_mode = 1                                    # G = 3: not a power of two
+    assert ws_size(d, hsa.OP_SCORE_TOPK)[0] == 2
 
 
 def test_workspace_sizes():

@@ -263,6 +263,87 @@ def test_full_size_decode_sampled_steps():
         assert_close(host(lt)[eq], olt[eq], TOL_F32, f"lse_tot step {step}")
 
 
+# ------------------------------------------------------------------ GQA group-max selection
+GROUP = {
+    "grp_bf16_g2": synth.small("grp_bf16_g2", B=1, T=704, H=4, Hkv=2, d=64, K=5, dtype="bf16",
+                               n_planted=2),
+    "grp_bf16_d128_g4": synth.small("grp_bf16_d128_g4", B=1, T=1024, H=8, Hkv=2, d=128, K=6,
+                                    dtype="bf16", n_planted=1, n_uniform=2),
+    "grp_f32_g8_k20": synth.small("grp_f32_g8_k20", B=2, T=640, H=8, Hkv=1, d=64, K=20,
+                                  dtype="f32"),
+    "grp_f32_g1": synth.small("grp_f32_g1", B=1, T=512, H=2, Hkv=2, d=64, K=4, dtype="f32"),
+}
+
+
+def check_group_forward(w, x, f, rows=None):
+    o = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K, group=True)
+    gi = host(f["idx"])
+    G = w.H // w.Hkv
+    # one chunk set per kv group, on every row
+    grp = gi.reshape(w.B, w.T, w.Hkv, G, w.K)
+    assert np.all(grp == grp[:, :, :, :1])
+    excl, eq = compare_selection(gi, o["idx"], o["gap"], w.K)
+    say(f"  near-tie rows excluded: {int(excl.sum())}/{excl.size}")
+    sel = eq[..., None].repeat(w.K, -1) & (o["idx"] >= 0)
+    assert_close(host(f["score"])[sel], o["score"][sel], TOL_F32, "score")
+    assert np.all(host(f["score"])[eq[..., None].repeat(w.K, -1) & (o["idx"] < 0)] == -np.inf)
+    assert_close(host(f["O"])[eq], o["O"][eq], out_tol(w), "O")
+    assert_close(host(f["lse_tot"])[eq], o["lse_tot"][eq], TOL_F32, "lse_tot")
+    return o
+
+
+@pytest.mark.parametrize("name", list(GROUP))
+def test_forward_group_max(name):
+    w = GROUP[name]
+    x = synth.make_inputs(w)
+    say(f"[forward group-max] {name}")
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
+    f = hsa.forward(t["Q"], t["K"], t["V"], t["Ql"], w.K, w.S, group=True)
+    torch.cuda.synchronize()
+    check_group_forward(w, x, f)
+
+
+def test_backward_with_group_selection():
+    """The backward takes any fixed selection: here a group-max one (bf16, G = 4)."""
+    w = synth.small("bwd_grp", B=1, T=768, H=8, Hkv=2, d=64, K=5, dtype="bf16", need_dO=True)
+    x = synth.make_inputs(w)
+    say("[backward group-max] bwd_grp")
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql", "dO")}
+    f = hsa.forward(t["Q"], t["K"], t["V"], t["Ql"], w.K, w.S, group=True)
+    g = hsa.backward(t["Q"], t["K"], t["V"], t["Ql"], f["ksum"], f["ent"], f["lse_l"], f["idx"],
+                     f["score"], f["lse_tot"], f["O"], t["dO"], w.S)
+    torch.cuda.synchronize()
+    o = check_group_forward(w, x, f)
+    excl, eq = compare_selection(host(f["idx"]), o["idx"], o["gap"], w.K)
+    assert eq.all(), "this case needs identical selections"
+    og = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], o["idx"], x["dO"], w.S)
+    for nm, a, b in zip(("dQ", "dK", "dV", "dQl"), g, og):
+        assert_close(host(a), b, TOL_GRAD_BF16, nm)
+
+
+def test_full_size_group_max_7b_sampled():
+    w, x = case("prefill_7b_gqa")
+    say(f"[full group-max] B{w.B} T{w.T} H{w.H}/{w.Hkv} d{w.d} K{w.K}")
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
+    f = hsa.forward(t["Q"], t["K"], t["V"], t["Ql"], w.K, w.S, group=True)
+    torch.cuda.synchronize()
+    ksum, ent, _ = oracle.summarize(x["K"], x["Ql"], w.S)
+    rows = sampled_rows(w, 256, 13)
+    idx, score, gap = oracle.score_topk(x["Q"], ksum, ent, w.S, w.K, rows=rows,
+                                        group_hkv=w.Hkv)
+    O, lo, lt = oracle.attend_fuse(x["Q"], x["K"], x["V"], idx, score, w.S, rows=rows)
+    flat = lambda a: a.reshape(-1, *a.shape[3:])  # noqa: E731
+    gi, gs = flat(host(f["idx"]))[rows], flat(host(f["score"]))[rows]
+    excl, eq = compare_selection(gi, flat(idx)[rows], flat(gap)[rows], w.K)
+    say(f"  sampled rows {len(rows)}, near-tie excluded {int(excl.sum())}")
+    m = eq[:, None].repeat(w.K, 1) & (flat(idx)[rows] >= 0)
+    assert_close(gs[m], flat(score)[rows][m], TOL_F32, "score")
+    assert_close(flat(host(f["O"]))[rows][eq], flat(O)[rows][eq], out_tol(w), "O")
+    G = w.H // w.Hkv
+    grp = host(f["idx"]).reshape(w.B, w.T, w.Hkv, G, w.K)
+    assert np.all(grp == grp[:, :, :, :1])
+
+
 # ------------------------------------------------------------------ backward
 BWD = {
     "bwd_bf16_gqa": synth.small("bwd_bf16_gqa", B=2, T=512, H=4, Hkv=2, d=64, K=3, dtype="bf16",
