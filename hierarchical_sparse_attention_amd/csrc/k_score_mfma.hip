@@ -147,8 +147,10 @@ __global__ __launch_bounds__(64) void k_score_mfma(Dims dm, int nc, const uint16
                                                    float* __restrict__ score) {
   __shared__ float sS[64][65];
   const int lane = threadIdx.x, c = lane & 15, g = lane >> 4;
-  const int h = blockIdx.y, b = blockIdx.z, K = dm.K;
-  const int i0 = blockIdx.x * 64;
+  // 1-D grid, position blocks slowest and longest (latest) first
+  const int nqb = (dm.Tq + 63) / 64, L = blockIdx.x;
+  const int h = L % dm.H, b = (L / dm.H) % dm.B, K = dm.K;
+  const int i0 = (nqb - 1 - L / (dm.H * dm.B)) * 64;
   const int nrows = min(64, dm.Tq - i0);
   const int my_n = lane < nrows ? (int)((dm.q_pos0 + i0 + lane) / dm.S) : 0;
   const int nmax = (int)((dm.q_pos0 + i0 + nrows - 1) / dm.S);
@@ -248,88 +250,89 @@ __global__ __launch_bounds__(64) void k_score_mfma(Dims dm, int nc, const uint16
   }
 }
 
-// GQA group-max selection on matrix cores (note §5.4), G = 2 or 4. A wavefront
-// owns P = 64 / G positions of one kv head; its 64 MFMA rows are (head hh,
-// position p) in head-major order, so every 16-row block belongs to one head and
-// is scored against that head's summary keys (the same block sequence as the
-// per-head kernel). Lanes p < P rank the candidates by the maximum of the G head
-// scores with the same register top-K; a second pass scores the blocks again and
-// writes each head's own score of the selected chunks.
+// GQA group-max selection on matrix cores (note §5.4), G = 2 or 4. A workgroup
+// of G wavefronts owns 64 positions of one kv head; wavefront hh scores them for
+// query head gk G + hh exactly as the per-head kernel does (same blocks, same
+// summary-key reuse) into its own LDS region. The G wavefronts then split the 64
+// positions (64 / G each) and rank the candidates by the maximum over the G
+// regions with the per-head kernel's register top-K. The selected chunks go to a
+// per-position bitmask; a second pass scores the blocks again and every lane
+// writes the scores of the (position, chunk) elements it holds whose bit is set.
 template <int D, int KM, int G>
-__global__ __launch_bounds__(64) void k_score_mfma_group(Dims dm, int nc,
-                                                         const uint16_t* __restrict__ Q,
-                                                         const uint16_t* __restrict__ ks,
-                                                         const float* __restrict__ ent,
-                                                         int32_t* __restrict__ idx,
-                                                         float* __restrict__ score) {
-  constexpr int P = 64 / G;    // positions per wavefront
-  constexpr int MBH = P / 16;  // 16-row blocks per head
+__global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
+                                                             const uint16_t* __restrict__ Q,
+                                                             const uint16_t* __restrict__ ks,
+                                                             const float* __restrict__ ent,
+                                                             int32_t* __restrict__ idx,
+                                                             float* __restrict__ score) {
+  constexpr int PS = 64 / G;  // positions each wavefront selects for
   static_assert(G == 2 || G == 4, "group size");
-  __shared__ float sS[64][65];
-  __shared__ float gS[P][65];  // group maximum per (position, candidate)
-  const int lane = threadIdx.x, c = lane & 15, g = lane >> 4;
-  const int gk = blockIdx.y, b = blockIdx.z, K = dm.K;
-  const int i0 = blockIdx.x * P;
-  const int npos = min(P, dm.Tq - i0);
-  const int p_me = min(lane, P - 1);  // clamped: lanes >= P only read in-bounds rows
-  const int my_n = lane < npos ? (int)((dm.q_pos0 + i0 + lane) / dm.S) : 0;
+  extern __shared__ __align__(16) float gsm2[];
+  float (*sS)[64][65] = reinterpret_cast<float (*)[64][65]>(gsm2);              // [G]
+  uint32_t* selb = reinterpret_cast<uint32_t*>(gsm2 + G * 64 * 65);              // [64][words]
+  const int t = threadIdx.x, lane = t & 63, hh = t >> 6, c = lane & 15, g = lane >> 4;
+  const int nqb = (dm.Tq + 63) / 64, L = blockIdx.x;
+  const int gk = L % dm.Hkv, b = (L / dm.Hkv) % dm.B, K = dm.K;
+  const int h = gk * G + hh;
+  const int i0 = (nqb - 1 - L / (dm.Hkv * dm.B)) * 64;
+  const int npos = min(64, dm.Tq - i0);
   const int nmax = (int)((dm.q_pos0 + i0 + npos - 1) / dm.S);
+  const int words = (nmax + 31) / 32;
+  // selecting lane: position sp = hh PS + lane of the block
+  const int sp = hh * PS + min(lane, PS - 1);
+  const bool sel_lane = lane < PS && sp < npos;
+  const int my_n = sel_lane ? (int)((dm.q_pos0 + i0 + sp) / dm.S) : 0;
 
-  // A fragments: row m = hh P + p (head gk G + hh, position i0 + p)
   uint4 qa[4][D / 32];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const int m = 16 * mb + c, hh = m / P, p = m % P;
-    const bool v = p < npos;
-    const long long off = (((long long)b * dm.Tq + i0 + p) * dm.H + (long long)gk * G + hh) * D;
+    const int m = 16 * mb + c;
+    const long long off = (((long long)b * dm.Tq + i0 + m) * dm.H + h) * D;
 #pragma unroll
     for (int ds = 0; ds < D / 32; ++ds)
-      qa[mb][ds] = v ? *reinterpret_cast<const uint4*>(Q + off + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
+      qa[mb][ds] = m < npos ? *reinterpret_cast<const uint4*>(Q + off + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
   }
-  // scores of candidates c0 .. c0 + 63 for all 64 rows into sS
-  auto score_blocks = [&](int c0) {
+  // this wavefront's head: scores of candidates c0 .. c0 + 63 for the 64 positions
+  // scores of candidates c0 + 16 nb + c for rows 16 mb + 4 g + r, handed per block to f
+  auto score_blocks = [&](int c0, auto&& f) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int chunk = c0 + 16 * nb + c;
       const bool cv = chunk < nmax;
+      const long long hrow = ((long long)b * nc + (cv ? chunk : 0)) * dm.H + h;
+      bf16x8 hi[D / 32], lo[D / 32];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const long long hrow = ((long long)b * nc + (cv ? chunk : 0)) * dm.H + (long long)gk * G + hh;
-        bf16x8 hi[D / 32], lo[D / 32];
+      for (int ds = 0; ds < D / 32; ++ds) {
+        const uint4 uh = cv ? *reinterpret_cast<const uint4*>(ks + hrow * 2 * D + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
+        const uint4 ul = cv ? *reinterpret_cast<const uint4*>(ks + hrow * 2 * D + D + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
+        hi[ds] = as_bf16x8(uh);
+        lo[ds] = as_bf16x8(ul);
+      }
+      const float e = cv ? ent[((long long)b * dm.NCcap + chunk) * dm.H + h] : 0.f;
 #pragma unroll
-        for (int ds = 0; ds < D / 32; ++ds) {
-          const uint4 uh = cv ? *reinterpret_cast<const uint4*>(ks + hrow * 2 * D + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
-          const uint4 ul = cv ? *reinterpret_cast<const uint4*>(ks + hrow * 2 * D + D + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
-          hi[ds] = as_bf16x8(uh);
-          lo[ds] = as_bf16x8(ul);
-        }
-        const float e = cv ? ent[((long long)b * dm.NCcap + chunk) * dm.H + (long long)gk * G + hh] : 0.f;
+      for (int mb = 0; mb < 4; ++mb) {
+        const floatx4 a = score_block<D>(qa[mb], hi, lo);
+        floatx4 v;
 #pragma unroll
-        for (int mbh = 0; mbh < MBH; ++mbh) {
-          const int mb = hh * MBH + mbh;
-          const floatx4 acc = score_block<D>(qa[mb], hi, lo);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sS[16 * mb + 4 * g + r][16 * nb + c] = fmaf(acc[r], dm.scale, e);
-        }
+        for (int r = 0; r < 4; ++r) v[r] = fmaf(a[r], dm.scale, e);
+        f(mb, nb, v);
       }
     }
   };
-  auto gscore = [&](int j) -> float { return gS[p_me][j]; };
+  auto gscore = [&](int j) -> float {
+    float v = sS[0][sp][j];
+#pragma unroll
+    for (int x = 1; x < G; ++x) v = fmaxf(v, sS[x][sp][j]);
+    return v;
+  };
 
   TopList<KM> top;
   top.init();
   for (int c0 = 0; c0 < nmax; c0 += 64) {
-    score_blocks(c0);
-    __syncthreads();
-    // group maxima, all lanes: element x = (position x / 64, candidate x % 64)
+    score_blocks(c0, [&](int mb, int nb, const floatx4& v) {
 #pragma unroll
-    for (int x = lane; x < P * 64; x += 64) {
-      const int p = x / 64, j = x % 64;
-      float v = sS[p][j];
-#pragma unroll
-      for (int hh = 1; hh < G; ++hh) v = fmaxf(v, sS[hh * P + p][j]);
-      gS[p][j] = v;
-    }
+      for (int r = 0; r < 4; ++r) sS[hh][16 * mb + 4 * g + r][16 * nb + c] = v[r];
+    });
     __syncthreads();
     const int lim = min(64, my_n - c0);
     int sb0 = 0;
@@ -368,47 +371,52 @@ __global__ __launch_bounds__(64) void k_score_mfma_group(Dims dm, int nc,
     }
     __syncthreads();
   }
-  // ranks in ascending chunk order, index sets of the G heads
+  // selected sets: index output for the G heads and the position's bitmask
   const int cnt = min(K, my_n);
-  int rk[KM];
+  for (int x = t; x < 64 * words; x += 64 * G) selb[x] = 0u;
+  __syncthreads();
+  if (sel_lane) {
+    const long long orow = ((long long)b * dm.Tq + i0 + sp) * dm.H + (long long)gk * G;
 #pragma unroll
-  for (int k = 0; k < KM; ++k) {
-    int rank = 0;
+    for (int k = 0; k < KM; ++k) {
+      int rank = 0;
 #pragma unroll
-    for (int k2 = 0; k2 < KM; ++k2) rank += (k2 < cnt && top.c[k2] < top.c[k]) ? 1 : 0;
-    rk[k] = rank;
-  }
-  const bool own = lane < npos;
-  const long long orow = ((long long)b * dm.Tq + i0 + p_me) * dm.H + (long long)gk * G;
-  if (own) {
+      for (int k2 = 0; k2 < KM; ++k2) rank += (k2 < cnt && top.c[k2] < top.c[k]) ? 1 : 0;
+      if (k < cnt) {
+        atomicOr(&selb[sp * words + top.c[k] / 32], 1u << (top.c[k] % 32));
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const long long o = (orow + hh) * K;
-#pragma unroll
-      for (int k = 0; k < KM; ++k)
-        if (k < cnt) idx[o + rk[k]] = top.c[k];
-      for (int k = cnt; k < K; ++k) {
-        idx[o + k] = -1;
-        score[o + k] = -INFINITY;
+        for (int x = 0; x < G; ++x) idx[(orow + x) * K + rank] = top.c[k];
       }
     }
+    for (int k = cnt; k < K; ++k)
+#pragma unroll
+      for (int x = 0; x < G; ++x) {
+        idx[(orow + x) * K + k] = -1;
+        score[(orow + x) * K + k] = -INFINITY;
+      }
   }
-  // second pass: each head's own score of the selected chunks
+  __syncthreads();
+  // second pass: this head's score of every selected (position, chunk)
   for (int c0 = 0; c0 < nmax; c0 += 64) {
-    score_blocks(c0);
-    __syncthreads();
-    if (own) {
+    score_blocks(c0, [&](int mb, int nb, const floatx4& v) {
+      const int ch = c0 + 16 * nb + c;
 #pragma unroll
-      for (int k = 0; k < KM; ++k) {
-        const int ch = top.c[k];
-        if (k < cnt && ch >= c0 && ch < c0 + 64) {
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) score[(orow + hh) * K + rk[k]] = sS[hh * P + p_me][ch - c0];
+      for (int r = 0; r < 4; ++r) {
+        const int pos = 16 * mb + 4 * g + r;
+        if (pos >= npos || ch >= nmax) continue;
+        const uint32_t wv = selb[pos * words + ch / 32];
+        if ((wv >> (ch % 32)) & 1u) {
+          int rank = __popc(wv & ((1u << (ch % 32)) - 1u));
+          for (int x = 0; x < ch / 32; ++x) rank += __popc(selb[pos * words + x]);
+          score[(((long long)b * dm.Tq + i0 + pos) * dm.H + h) * K + rank] = v[r];
         }
       }
-    }
-    __syncthreads();
+    });
   }
+}
+
+size_t group_mfma_smem(int G, int nmax) {
+  return (size_t)G * 64 * 65 * sizeof(float) + (size_t)64 * ((nmax + 31) / 32) * sizeof(uint32_t);
 }
 
 // Decode split: grid (splits, rows); a workgroup of 4 wavefronts scores the
@@ -618,7 +626,10 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_score_row_mfma(
 
 }  // namespace
 
-bool score_mfma_group_applies(const Dims& dm) { return dm.bf16 && (dm.G == 2 || dm.G == 4); }
+bool score_mfma_group_applies(const Dims& dm) {
+  const int nmax = (int)((dm.q_pos0 + dm.Tq - 1) / dm.S);
+  return dm.bf16 && (dm.G == 2 || dm.G == 4) && group_mfma_smem(dm.G, nmax) <= 160 * 1024;
+}
 
 hipError_t launch_score_mfma_group(const Dims& dm, const void* Q, const float* ksum,
                                    const float* ent, int32_t* idx, float* score, void* ws,
@@ -627,11 +638,18 @@ hipError_t launch_score_mfma_group(const Dims& dm, const void* Q, const float* k
   uint16_t* ks = reinterpret_cast<uint16_t*>(ws);
   const long long n8 = (long long)dm.B * nc * dm.H * (dm.d / 8);
   const int grid = (int)std::min<long long>((n8 + 255) / 256, 4096);
-  const int P = 64 / dm.G;
-  dim3 g3((dm.Tq + P - 1) / P, dm.Hkv, dm.B);
+  const size_t smem = group_mfma_smem(dm.G, nc);
+  dim3 g3((unsigned)((dm.Tq + 63) / 64) * dm.Hkv * dm.B);
   const auto* Qh = reinterpret_cast<const uint16_t*>(Q);
-#define HILS_GRP(DD, KMM, GG) \
-  hipLaunchKernelGGL((k_score_mfma_group<DD, KMM, GG>), g3, dim3(64), 0, st, dm, nc, Qh, ks, ent, idx, score)
+  hipError_t e = hipSuccess;
+#define HILS_GRP(DD, KMM, GG)                                                                  \
+  do {                                                                                         \
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_score_mfma_group<DD, KMM, GG>),     \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);             \
+    if (e != hipSuccess) return e;                                                             \
+    hipLaunchKernelGGL((k_score_mfma_group<DD, KMM, GG>), g3, dim3(64 * GG), smem, st, dm, nc, \
+                       Qh, ks, ent, idx, score);                                               \
+  } while (0)
   if (dm.d == 64) {
     hipLaunchKernelGGL((k_ksplit<64>), dim3(grid), dim3(256), 0, st, dm, nc, ksum, ks);
     if (dm.K <= 16) {
@@ -663,7 +681,7 @@ hipError_t launch_score_mfma_prefill(const Dims& dm, const void* Q, const float*
   uint16_t* ks = reinterpret_cast<uint16_t*>(ws);
   const long long n8 = (long long)dm.B * nc * dm.H * (dm.d / 8);
   const int grid = (int)std::min<long long>((n8 + 255) / 256, 4096);
-  dim3 g3((dm.Tq + 63) / 64, dm.H, dm.B);
+  dim3 g3((unsigned)((dm.Tq + 63) / 64) * dm.H * dm.B);
   if (dm.d == 64) {
     hipLaunchKernelGGL((k_ksplit<64>), dim3(grid), dim3(256), 0, st, dm, nc, ksum, ks);
     if (dm.K <= 16)
