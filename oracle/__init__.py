@@ -49,7 +49,7 @@ def lib():
         L.oracle_attend_fuse.argtypes = [ci, ci, ci, cl, ci, ci, ci, ci, ci, cd, _D, _D, _D, _I,
                                          _D, cl, _L, _D, _D, _D]
         L.oracle_backward.argtypes = [ci, ci, ci, cl, ci, ci, ci, ci, ci, ci, cd, _D, _D, _D, _D,
-                                      _I, _D, _U8, _U8, _D, _D, _D, _D]
+                                      _I, _D, _U8, _U8, _D, _D, _D, _D, _D, _D]
         for f in (L.oracle_summarize, L.oracle_score_topk, L.oracle_score_topk_group,
                   L.oracle_exact_chunk_lse, L.oracle_attend_fuse, L.oracle_backward):
             f.restype = None
@@ -138,19 +138,23 @@ def attend_fuse(Q, K, V, idx, score, S, q_pos0=0, scale=0.0, rows=None):
     return O, lo, lt
 
 
-def forward(Q, K, V, Ql, S, Ksel, q_pos0=0, scale=0.0, rows=None, group=False):
+def forward(Q, K, V, Ql, S, Ksel, q_pos0=0, scale=0.0, rows=None, group=False, Qs=None):
     """Whole forward: summaries, scores/top-K, attend+fuse. Returns a dict.
-    group=True selects one chunk set per kv head (GQA group-max selection)."""
+    group=True selects one chunk set per kv head (GQA group-max selection);
+    Qs is the Q-Cal scoring query (the chunk scores use it, the attention uses Q)."""
     ksum, ent, lse_l = summarize(K, Ql, S, scale)
-    idx, score, gap = score_topk(Q, ksum, ent, S, Ksel, q_pos0, scale, rows,
+    idx, score, gap = score_topk(Q if Qs is None else Qs, ksum, ent, S, Ksel, q_pos0, scale, rows,
                                  group_hkv=K.shape[2] if group else None)
     O, lo, lt = attend_fuse(Q, K, V, idx, score, S, q_pos0, scale, rows)
     return dict(ksum=ksum, ent=ent, lse_l=lse_l, idx=idx, score=score, gap=gap, O=O,
                 lse_own=lo, lse_tot=lt)
 
 
-def backward(Q, K, V, Ql, idx, dO, S, q_pos0=0, scale=0.0, row_mask=None, kv_mask=None):
-    """Gradients (dQ, dK, dV, dQl) of sum(dO*O) with idx held fixed; NaN outside the masks."""
+def backward(Q, K, V, Ql, idx, dO, S, q_pos0=0, scale=0.0, row_mask=None, kv_mask=None,
+             Qs=None):
+    """Gradients (dQ, dK, dV, dQl) of sum(dO*O) with idx held fixed; NaN outside the masks.
+    With a Q-Cal scoring query Qs the result is (dQ, dK, dV, dQl, dQs): dQs is the
+    gradient through the chunk scores, dQ the one through the token attention."""
     Q, K, V, Ql, dO = _d(Q), _d(K), _d(V), _d(Ql), _d(dO)
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     B, Tq, H, d = Q.shape
@@ -161,9 +165,12 @@ def backward(Q, K, V, Ql, idx, dO, S, q_pos0=0, scale=0.0, row_mask=None, kv_mas
     dK = np.full(K.shape, np.nan)
     dV = np.full(V.shape, np.nan)
     dQl = np.full(Ql.shape, np.nan)
+    Qs = None if Qs is None else _d(Qs)
+    dQs = None if Qs is None else np.full(Q.shape, np.nan)
     rm = None if row_mask is None else np.ascontiguousarray(row_mask, dtype=np.uint8)
     km = None if kv_mask is None else np.ascontiguousarray(kv_mask, dtype=np.uint8)
     lib().oracle_backward(B, Tq, Tkv, q_pos0, H, Hkv, d, S, NC, Ksel, scale, _p(Q, _D), _p(K, _D),
                           _p(V, _D), _p(Ql, _D), _p(idx, _I), _p(dO, _D), _p(rm, _U8),
-                          _p(km, _U8), _p(dQ, _D), _p(dK, _D), _p(dV, _D), _p(dQl, _D))
-    return dQ, dK, dV, dQl
+                          _p(km, _U8), _p(dQ, _D), _p(dK, _D), _p(dV, _D), _p(dQl, _D),
+                          _p(Qs, _D), _p(dQs, _D))
+    return (dQ, dK, dV, dQl) if Qs is None else (dQ, dK, dV, dQl, dQs)

@@ -341,7 +341,11 @@ void oracle_attend_fuse(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int
 }
 
 // Gradients of sum(dO * O) with the selected indices held fixed. The forward is
-// recomputed from Q, K, V, Ql (summaries and scores included). row_mask
+// recomputed from Q, K, V, Ql (summaries and scores included). With Q-Cal
+// (page 2 §5.4) the chunk scores use a separate scoring query Qs (the
+// calibrated q^ = q + W_up W_down h, formed by the caller): the scores' part
+// of the query gradient then goes to dQs and dQ keeps the token-attention
+// part; Qs == NULL means the scores use Q and dQs is not written. row_mask
 // [B*Tq*H] selects the rows whose dQ is produced; kv_mask [B*NC*Hkv] selects the
 // (chunk, kv head) pairs whose dK, dV rows and whose dQl rows (heads of that
 // group) are produced. NULL masks mean everything. Entries outside the masks are
@@ -350,7 +354,7 @@ void oracle_backward(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d,
                      int Ksel, double scale, const double* Q, const double* K, const double* V,
                      const double* Ql, const int* idx, const double* dO,
                      const unsigned char* row_mask, const unsigned char* kv_mask, double* dQ,
-                     double* dK, double* dV, double* dQl) {
+                     double* dK, double* dV, double* dQl, const double* Qs, double* dQs) {
   Shape sh{B, Tq, Tkv, H, Hkv, d, S, NC, Ksel, q_pos0, resolve_scale(scale, d)};
   const double tau = sh.scale;
   const int G = H / Hkv;
@@ -365,7 +369,7 @@ void oracle_backward(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d,
   // gradient accumulators for the summaries (k' and b')
   std::vector<double> dks((long)B * NC * H * d, 0.0), db((long)B * NC * H, 0.0);
   std::vector<double> gK((long)B * Tkv * Hkv * d, 0.0), gV((long)B * Tkv * Hkv * d, 0.0);
-  std::vector<double> dq(d);
+  std::vector<double> dq(d), dqs(d);
   RowFwd f;
   for (int b = 0; b < B; ++b)
     for (int i = 0; i < Tq; ++i)
@@ -381,19 +385,22 @@ void oracle_backward(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d,
           if (c >= 0 && kv_on(b, c, g)) need = true;
         }
         if (!need) continue;
-        // scores of the selected chunks from the summaries (page 2 §5.2)
+        // scores of the selected chunks from the summaries (page 2 §5.2), with
+        // the scoring query (Q-Cal) when one is given
         const double* q = sh.q(Q, b, i, h);
+        const double* qs = Qs ? sh.q(Qs, b, i, h) : q;
         std::vector<double> sc(Ksel);
         for (int k = 0; k < Ksel; ++k) {
           const int c = idx[r * Ksel + k];
           if (c < 0) { sc[k] = -INFINITY; continue; }
           const long sidx = ((long)b * NC + c) * H + h;
-          sc[k] = tau * dot(q, ksum.data() + sidx * d, d) + ent[sidx];
+          sc[k] = tau * dot(qs, ksum.data() + sidx * d, d) + ent[sidx];
         }
         row_forward(sh, Q, K, V, idx + r * Ksel, sc.data(), b, i, h, f);
         const double* go = dO + r * d;
         const double D = dot(go, f.O.data(), d);
-        for (int e = 0; e < d; ++e) dq[e] = 0.0;
+        for (int e = 0; e < d; ++e) dq[e] = dqs[e] = 0.0;
+        double* dq_score = Qs ? dqs.data() : dq.data();  // where the score's query gradient goes
         // selected chunks
         for (size_t k = 0; k < f.chunks.size(); ++k) {
           const int c = f.chunks[k];
@@ -402,8 +409,8 @@ void oracle_backward(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d,
           const double dsh = a * (rc - D);  // gradient of the fusion logit s^_{i,c}
           const long sidx = ((long)b * NC + c) * H + h;
           const double* kb = ksum.data() + sidx * d;
-          for (int e = 0; e < d; ++e) dq[e] += tau * dsh * kb[e];
-          for (int e = 0; e < d; ++e) dks[sidx * d + e] += tau * dsh * q[e];
+          for (int e = 0; e < d; ++e) dq_score[e] += tau * dsh * kb[e];
+          for (int e = 0; e < d; ++e) dks[sidx * d + e] += tau * dsh * qs[e];
           db[sidx] += dsh;
           for (int j = 0; j < S; ++j) {
             const long key = (long)c * S + j;
@@ -434,8 +441,11 @@ void oracle_backward(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d,
             for (int e = 0; e < d; ++e) gv[e] += w * go[e];
           }
         }
-        if (!row_mask || row_mask[r])
+        if (!row_mask || row_mask[r]) {
           for (int e = 0; e < d; ++e) dQ[r * d + e] = dq[e];
+          if (Qs)
+            for (int e = 0; e < d; ++e) dQs[r * d + e] = dqs[e];
+        }
       }
   // landmark summaries: k' = sum p'_j k_j, b' = L' - sum p'_j s'_j with p' = softmax(s')
   for (int b = 0; b < B; ++b)

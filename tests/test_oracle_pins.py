@@ -307,8 +307,9 @@ def test_decode_equals_prefill_row():
 
 
 # ---------------------------------------------------------------- backward
-def torch_hils(Q, K, V, Ql, idx, S):
-    """Dense, differentiable restatement of the forward with fixed idx (torch fp64)."""
+def torch_hils(Q, K, V, Ql, idx, S, Qs=None):
+    """Dense, differentiable restatement of the forward with fixed idx (torch fp64);
+    Qs, when given, is the scoring query of the chunk scores (Q-Cal)."""
     B, T, H, d = Q.shape
     Hkv = K.shape[2]
     G, NC, tau = H // Hkv, Ql.shape[1], 1.0 / math.sqrt(d)
@@ -324,9 +325,10 @@ def torch_hils(Q, K, V, Ql, idx, S):
         for i in range(T):
             for h in range(H):
                 q = Q[b, i, h]
+                qs = q if Qs is None else Qs[b, i, h]
                 logits, outs = [], []
                 for c in [int(c) for c in idx[b, i, h] if c >= 0]:
-                    logits.append(tau * (ksum[b, c, h] @ q) + ent[b, c, h])
+                    logits.append(tau * (ksum[b, c, h] @ qs) + ent[b, c, h])
                     s = tau * (Kh[b, c * S:(c + 1) * S, h] @ q)
                     outs.append(torch.softmax(s, 0) @ Vh[b, c * S:(c + 1) * S, h])
                 own = (i // S) * S
@@ -379,6 +381,70 @@ def test_backward_finite_differences():
                 vals.append(np.sum(g["O"] * dO))
             fd = (vals[0] - vals[1]) / (2 * h)
             assert fd == pytest.approx(grads[name][pos], rel=1e-5, abs=1e-7), (name, pos)
+
+
+def _qcal_case():
+    """Backward case with a Q-Cal scoring query: Qs = Q + a low-rank update of
+    seeded hidden states (the caller's W_up W_down h of page 2 §5.4)."""
+    w, x, _ = _bwd_case()
+    rng = np.random.default_rng(11)
+    hdim, rank = 24, 4
+    hid = rng.standard_normal((w.B, w.T, hdim))
+    Wd = rng.standard_normal((rank, hdim)) / np.sqrt(hdim)
+    Wu = rng.standard_normal((w.H, w.d, rank)) / np.sqrt(rank)
+    Qs = x["Q"].astype(np.float64) + np.einsum("hdr,rk,btk->bthd", Wu, Wd, hid)
+    f = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K, Qs=Qs)
+    return w, x, Qs, f
+
+
+def test_qcal_backward_matches_autograd():
+    w, x, Qs, f = _qcal_case()
+    dQ, dK, dV, dQl, dQs = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], f["idx"], x["dO"],
+                                           w.S, Qs=Qs)
+    t = {k: torch.from_numpy(x[k].astype(np.float64)).requires_grad_(True)
+         for k in ("Q", "K", "V", "Ql")}
+    t["Qs"] = torch.from_numpy(Qs).requires_grad_(True)
+    O = torch_hils(t["Q"], t["K"], t["V"], t["Ql"], f["idx"], w.S, Qs=t["Qs"])
+    np.testing.assert_allclose(O.detach().numpy(), f["O"], rtol=1e-11, atol=1e-12)
+    (O * torch.from_numpy(x["dO"].astype(np.float64))).sum().backward()
+    for name, g in (("Q", dQ), ("Qs", dQs), ("K", dK), ("V", dV), ("Ql", dQl)):
+        np.testing.assert_allclose(g, t[name].grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
+
+
+def test_qcal_backward_finite_differences():
+    """Central differences in the scoring query and the token query (selection unchanged)."""
+    w, x, Qs, f = _qcal_case()
+    assert np.nanmin(f["gap"]) > 1e-5   # a step of 1e-6 moves a score by far less
+    dQ, _, _, _, dQs = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], f["idx"], x["dO"], w.S,
+                                       Qs=Qs)
+    dO = x["dO"].astype(np.float64)
+    Q0 = x["Q"].astype(np.float64)
+    rng = np.random.default_rng(6)
+    h = 1e-6
+    for which, grad in (("Qs", dQs), ("Q", dQ)):
+        for _ in range(6):
+            pos = tuple(rng.integers(0, s) for s in Q0.shape)
+            vals = []
+            for sgn in (1, -1):
+                q, qs = Q0.copy(), Qs.copy()
+                (qs if which == "Qs" else q)[pos] += sgn * h
+                g = oracle.forward(q, x["K"], x["V"], x["Ql"], w.S, w.K, Qs=qs)
+                assert np.array_equal(g["idx"], f["idx"])
+                vals.append(np.sum(g["O"] * dO))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            assert fd == pytest.approx(grad[pos], rel=1e-5, abs=1e-7), (which, pos)
+
+
+def test_qcal_with_token_query_splits_the_plain_gradient():
+    """Qs = Q: the scoring and token parts add up to the plain query gradient and
+    every other gradient is unchanged."""
+    w, x, f = _bwd_case()
+    plain = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], f["idx"], x["dO"], w.S)
+    split = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], f["idx"], x["dO"], w.S, Qs=x["Q"])
+    np.testing.assert_allclose(split[0] + split[4], plain[0], rtol=1e-12, atol=1e-13)
+    assert np.abs(split[4]).max() > 1e-3 * np.abs(plain[0]).max()
+    for a, b in zip(split[1:4], plain[1:4]):
+        np.testing.assert_array_equal(a, b)
 
 
 def test_backward_masks_restrict_work():
