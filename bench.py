@@ -316,22 +316,30 @@ def main():
         return ev[0].elapsed_time(ev[1]) / reps
 
     if not args.no_extra_configs:
-        # the 7B-class GQA prefill also with group-max selection (one chunk set per kv head)
-        for name, modes in (("prefill_7b_gqa", (False, True)), ("train_345m", (False,))):
+        # the 7B-class GQA prefill also with group-max selection (one chunk set per kv
+        # head); the training step also with a Q-Cal scoring query
+        for name, modes in (("prefill_7b_gqa", ("per_head", "group_max")),
+                            ("train_345m", ("per_head", "qcal"))):
             wx = synth.workloads()[name]
             log(f"generating {name} inputs")
             xx = synth.make_inputs(wx)
             keys = ("Q", "K", "V", "Ql") + (("dO",) if wx.need_dO else ())
             tx = {k: torch.from_numpy(xx[k]).to(dev, torch.bfloat16) for k in keys}
+            if "qcal" in modes:
+                tx["Qs"] = torch.from_numpy(synth.scoring_query(wx, xx)).to(dev, torch.bfloat16)
             del xx
-            for group in modes:
-                fw = hsa.forward(tx["Q"], tx["K"], tx["V"], tx["Ql"], wx.K, wx.S, group=group)
+            for mode in modes:
+                group = mode == "group_max"
+                Qsx = tx["Qs"] if mode == "qcal" else None
+                Qsel = tx["Q"] if Qsx is None else Qsx   # the query the chunk scores use
+                fw = hsa.forward(tx["Q"], tx["K"], tx["V"], tx["Ql"], wx.K, wx.S, group=group,
+                                 Qs=Qsx)
                 ksx, enx, llx, ix, scx = (fw[k] for k in ("ksum", "ent", "lse_l", "idx", "score"))
                 Ox, lox, ltx = fw["O"], fw["lse_own"], fw["lse_tot"]
                 calls = {
                     "summarize": lambda: hsa.summarize(tx["K"], tx["Ql"], wx.S, ksum=ksx,
                                                        ent=enx, lse_l=llx),
-                    "score_topk": lambda: hsa.score_topk(tx["Q"], ksx, enx, wx.K, wx.S, 0, wx.T,
+                    "score_topk": lambda: hsa.score_topk(Qsel, ksx, enx, wx.K, wx.S, 0, wx.T,
                                                          Hkv=wx.Hkv, idx=ix, score=scx,
                                                          group=group),
                     "attend_fuse": lambda: hsa.attend_fuse(tx["Q"], tx["K"], tx["V"], ix, scx,
@@ -340,7 +348,7 @@ def main():
                 if wx.need_dO:
                     calls["backward"] = lambda: hsa.backward(tx["Q"], tx["K"], tx["V"], tx["Ql"],
                                                              ksx, enx, llx, ix, scx, ltx, Ox,
-                                                             tx["dO"], wx.S)
+                                                             tx["dO"], wx.S, Qs=Qsx)
                 for fn in calls.values():
                     fn()
                 torch.cuda.synchronize()
@@ -359,7 +367,9 @@ def main():
                     rec["prefill_tokens_per_s"] = wx.B * wx.T / (fwd_ms * 1e-3)
                 if group:
                     rec["selection"] = "group max over the 4 query heads of each kv head"
-                extra[name + ("_group_max" if group else "")] = rec
+                if Qsx is not None:
+                    rec["scoring_query"] = "Q-Cal: separate scoring query, dQs returned apart"
+                extra[name + ("" if mode == "per_head" else "_" + mode)] = rec
                 del fw, calls
             del tx
             torch.cuda.empty_cache()

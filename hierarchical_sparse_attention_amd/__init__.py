@@ -57,7 +57,7 @@ def lib():
         L.hils_summarize.argtypes = [P, VP, VP, i32, i32, VP, VP, VP, VP, SZ, VP]
         L.hils_score_topk.argtypes = [P, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.hils_attend_fuse.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
-        L.hils_backward.argtypes = [P] + [VP] * 16 + [VP, SZ, VP]
+        L.hils_backward.argtypes = [P] + [VP] * 18 + [VP, SZ, VP]
         L.hils_status_string.argtypes = [ctypes.c_int]
         L.hils_status_string.restype = ctypes.c_char_p
         L.hils_version.restype = i32
@@ -191,34 +191,41 @@ def attend_fuse(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Te
     return O, lse_own, lse_tot
 
 
-def forward(Q, K, V, Ql, K_sel: int, S: int = 64, scale: float = 0.0, group: bool = False):
-    """Prefill forward: summaries, selection, attention. Returns a dict of tensors."""
+def forward(Q, K, V, Ql, K_sel: int, S: int = 64, scale: float = 0.0, group: bool = False,
+            Qs=None):
+    """Prefill forward: summaries, selection, attention. Returns a dict of tensors.
+    Qs is an optional Q-Cal scoring query (the chunk scores use it, the attention Q)."""
     ksum, ent, lse_l = summarize(K, Ql, S, scale=scale)
-    idx, score = score_topk(Q, ksum, ent, K_sel, S, 0, K.shape[1], scale, Hkv=K.shape[2],
-                            group=group)
+    idx, score = score_topk(Q if Qs is None else Qs, ksum, ent, K_sel, S, 0, K.shape[1], scale,
+                            Hkv=K.shape[2], group=group)
     O, lse_own, lse_tot = attend_fuse(Q, K, V, idx, score, S, 0, scale=scale)
     return dict(ksum=ksum, ent=ent, lse_l=lse_l, idx=idx, score=score, O=O, lse_own=lse_own,
                 lse_tot=lse_tot)
 
 
 def backward(Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, S: int = 64,
-             scale: float = 0.0):
+             scale: float = 0.0, Qs=None):
     """Gradients (dQ, dK, dV, dQl) of sum(dO * O) with the selection held fixed; O is the
-    forward's output."""
+    forward's output. With a Q-Cal scoring query Qs (the query the chunk scores were
+    computed from) the result is (dQ, dK, dV, dQl, dQs): dQs through the scores, dQ
+    through the token attention."""
     B, T, H, d = Q.shape
     Hkv = K.shape[2]
     K_sel = idx.shape[-1]
     NC = Ql.shape[1]
     for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (Ql, "Ql"), (O, "O"), (dO, "dO")):
         _need(t, n, dtype=Q.dtype)
+    if Qs is not None:
+        _need(Qs, "Qs", tuple(Q.shape), Q.dtype)
     _need(ksum, "ksum", (B, NC, H, d), torch.float32)
     _need(idx, "idx", (B, T, H, K_sel), torch.int32)
     dev = Q.device
     dQ, dK, dV, dQl = (torch.empty_like(x) for x in (Q, K, V, Ql))
+    dQs = None if Qs is None else torch.empty_like(Q)
     dims = make_dims(B, T, T, H, Hkv, d, S, K_sel, _dtype_code(Q), 0, scale, T, NC)
     ws, n = _workspace(dims, OP_BACKWARD, dev)
     _check("hils_backward", lib().hils_backward(
         ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(Ql), _ptr(ksum), _ptr(ent),
         _ptr(lse_l), _ptr(idx), _ptr(score), _ptr(lse_tot), _ptr(O), _ptr(dO), _ptr(dQ), _ptr(dK),
-        _ptr(dV), _ptr(dQl), _ptr(ws), n, _stream(dev)))
-    return dQ, dK, dV, dQl
+        _ptr(dV), _ptr(dQl), _ptr(Qs), _ptr(dQs), _ptr(ws), n, _stream(dev)))
+    return (dQ, dK, dV, dQl) if Qs is None else (dQ, dK, dV, dQl, dQs)

@@ -137,8 +137,8 @@ hils_status hils_backward(const hils_dims* dims, const void* Q, const void* K, c
                           const void* Ql, const float* ksum, const float* ent,
                           const float* lse_l, const int32_t* idx, const float* score,
                           const float* lse_tot, const void* O, const void* dO, void* dQ,
-                          void* dK, void* dV, void* dQl, void* ws, size_t ws_bytes,
-                          hils_stream stream) {
+                          void* dK, void* dV, void* dQl, const void* Qs, void* dQs, void* ws,
+                          size_t ws_bytes, hils_stream stream) {
   hils::Dims dm;
   hils_status st = resolve(dims, &dm);
   if (st != HILS_OK) return st;
@@ -147,10 +147,12 @@ hils_status hils_backward(const hils_dims* dims, const void* Q, const void* K, c
   const void* in[] = {Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, dQ, dK, dV, dQl};
   for (const void* p : in)
     if (!aligned16(p)) return HILS_ERR_INVALID_ARG;
+  if ((Qs == nullptr) != (dQs == nullptr)) return HILS_ERR_INVALID_ARG;
+  if (Qs != nullptr && (!aligned16(Qs) || !aligned16(dQs))) return HILS_ERR_INVALID_ARG;
   st = check_ws(hils::backward_ws_bytes(dm), ws, ws_bytes);
   if (st != HILS_OK) return st;
   return from_hip(hils::launch_backward(dm, Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O,
-                                        dO, dQ, dK, dV, dQl, ws,
+                                        dO, dQ, dK, dV, dQl, Qs, dQs, ws,
                                         reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -271,11 +271,12 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
                        const void* Ql, const float* ksum, const float* ent, const float* lse_l,
                        const int32_t* idx, const float* score, const float* lse_tot,
                        const void* O, const void* dO, void* dQ, void* dK, void* dV, void* dQl,
-                       float* ws_D, void* ws_mfma, hipStream_t st, hipError_t* err);
+                       const void* Qs, void* dQs, float* ws_D, float* ws_dsh, void* ws_mfma,
+                       hipStream_t st, hipError_t* err);
 hipError_t launch_backward(const Dims& dm, const void* Q, const void* K, const void* V,
                            const void* Ql, const float* ksum, const float* ent, const float* lse_l,
                            const int32_t* idx, const float* score, const float* lse_tot,
                            const void* O, const void* dO, void* dQ, void* dK, void* dV,
-                           void* dQl, void* ws, hipStream_t st);
+                           void* dQl, const void* Qs, void* dQs, void* ws, hipStream_t st);
 
 }  // namespace hils

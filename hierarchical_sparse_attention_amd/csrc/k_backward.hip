@@ -71,7 +71,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(Dims dm, const void* __restric
                                                   const float* __restrict__ score,
                                                   const float* __restrict__ lse_tot,
                                                   const void* __restrict__ dO,
-                                                  void* __restrict__ dQ, float* __restrict__ ws_dsh,
+                                                  void* __restrict__ dQ, void* __restrict__ dQs,
+                                                  float* __restrict__ ws_dsh,
                                                   float* __restrict__ ws_D) {
   constexpr int X = D / kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -129,10 +130,11 @@ __global__ __launch_bounds__(256) void k_bwd_rows(Dims dm, const void* __restric
     if (lane == k) { rk = rc; ak = a; mk = lz; }
   }
 
-  // pass 2: gradients of the logits and of the query
-  float dq[X];
+  // pass 2: gradients of the logits and of the query; with a scoring query
+  // (Q-Cal) the chunk scores' part goes to dQs
+  float dq[X], dqs[X];
 #pragma unroll
-  for (int x = 0; x < X; ++x) dq[x] = 0.0f;
+  for (int x = 0; x < X; ++x) dq[x] = dqs[x] = 0.0f;
   auto add_keys = [&](long long c0, int nk, float ds) {
     for (int j = 0; j < nk; ++j) {
       const float dj = bcast(ds, j);
@@ -155,8 +157,15 @@ __global__ __launch_bounds__(256) void k_bwd_rows(Dims dm, const void* __restric
     const float dsh = a * (rc - Dsum);
     const long long sidx = (((long long)b * dm.NCcap + c) * dm.H + h) * D;
 #pragma unroll
-    for (int x = 0; x < X; ++x) dq[x] = fmaf(tau * dsh, ksum[sidx + lane + kWave * x], dq[x]);
+    for (int x = 0; x < X; ++x) dqs[x] = fmaf(tau * dsh, ksum[sidx + lane + kWave * x], dqs[x]);
     if (lane == 0) ws_dsh[r * Ksel + k] = dsh;
+  }
+  if (dQs) {
+#pragma unroll
+    for (int x = 0; x < X; ++x) store_elem<BF16>(dQs, r * D + lane + kWave * x, dqs[x]);
+  } else {
+#pragma unroll
+    for (int x = 0; x < X; ++x) dq[x] += dqs[x];
   }
 #pragma unroll
   for (int x = 0; x < X; ++x) store_elem<BF16>(dQ, r * D + lane + kWave * x, dq[x]);
@@ -214,6 +223,7 @@ __global__ __launch_bounds__(256) void k_sel_bitmap_lds(Dims dm, const int32_t* 
 
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, const void* __restrict__ Q,
+                                                const void* __restrict__ Qsc,
                                                 const void* __restrict__ K,
                                                 const void* __restrict__ V,
                                                 const void* __restrict__ Ql,
@@ -342,7 +352,7 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, const void* __restrict_
         row_pass(r, false, kChunk, score[r * Ksel + slot]);
 #pragma unroll
         for (int x = 0; x < X; ++x)
-          dkb[x] = fmaf(tau * dsh, load_elem<BF16>(Q, r * D + lane + kWave * x), dkb[x]);
+          dkb[x] = fmaf(tau * dsh, load_elem<BF16>(Qsc, r * D + lane + kWave * x), dkb[x]);
         dbs += dsh;
       }
       __syncthreads();
@@ -420,7 +430,8 @@ template <bool BF16, int D>
 hipError_t launch_t(const Dims& dm, const void* Q, const void* K, const void* V, const void* Ql,
                     const float* ksum, const float* ent, const float* lse_l, const int32_t* idx,
                     const float* score, const float* lse_tot, const void* O, const void* dO,
-                    void* dQ, void* dK, void* dV, void* dQl, void* ws, hipStream_t st) {
+                    void* dQ, void* dK, void* dV, void* dQl, const void* Qs, void* dQs, void* ws,
+                    hipStream_t st) {
   const WsLayout L = ws_layout(dm);
   char* base = reinterpret_cast<char*>(ws);
   float* dsh = reinterpret_cast<float*>(base + L.dsh);
@@ -429,7 +440,7 @@ hipError_t launch_t(const Dims& dm, const void* Q, const void* K, const void* V,
   const int NC = dm.Tkv / dm.S;
   hipError_t err = hipSuccess;
   if (backward_mfma_try(dm, Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, dQ, dK,
-                        dV, dQl, Dr, base + L.mfma, st, &err))
+                        dV, dQl, Qs, dQs, Dr, dsh, base + L.mfma, st, &err))
     return err;
   // words per bitmap block: as many as 64 KiB of LDS holds, at most 16
   int wpw = 16;
@@ -443,8 +454,9 @@ hipError_t launch_t(const Dims& dm, const void* Q, const void* K, const void* V,
     hipLaunchKernelGGL(k_sel_bitmap, dim3(1024), dim3(256), 0, st, dm, idx, bm, L.words);
   }
   hipLaunchKernelGGL((k_bwd_rows<BF16, D>), dim3((dm.Tq + 3) / 4, dm.H, dm.B), dim3(256), 0, st,
-                     dm, Q, K, V, ksum, idx, score, lse_tot, dO, dQ, dsh, Dr);
-  hipLaunchKernelGGL((k_bwd_kv<BF16, D>), dim3(NC, dm.Hkv, dm.B), dim3(256), 0, st, dm, Q, K, V,
+                     dm, Q, K, V, ksum, idx, score, lse_tot, dO, dQ, dQs, dsh, Dr);
+  hipLaunchKernelGGL((k_bwd_kv<BF16, D>), dim3(NC, dm.Hkv, dm.B), dim3(256), 0, st, dm, Q,
+                     Qs ? Qs : Q, K, V,
                      Ql, ksum, ent, lse_l, idx, score, lse_tot, dO, dsh, Dr, bm, L.words, dK, dV,
                      dQl);
   return hipGetLastError();
@@ -458,11 +470,11 @@ hipError_t launch_backward(const Dims& dm, const void* Q, const void* K, const v
                            const void* Ql, const float* ksum, const float* ent, const float* lse_l,
                            const int32_t* idx, const float* score, const float* lse_tot,
                            const void* O, const void* dO, void* dQ, void* dK, void* dV,
-                           void* dQl, void* ws, hipStream_t st) {
+                           void* dQl, const void* Qs, void* dQs, void* ws, hipStream_t st) {
   if ((long long)dm.B * dm.Tq * dm.H == 0) return hipSuccess;
 #define HILS_BWD(BF, DD)                                                                      \
   return launch_t<BF, DD>(dm, Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, dQ, \
-                          dK, dV, dQl, ws, st)
+                          dK, dV, dQl, Qs, dQs, ws, st)
   if (dm.bf16) {
     if (dm.d == 64) HILS_BWD(true, 64);
     HILS_BWD(true, 128);

@@ -28,6 +28,10 @@
 //                  slot of a bf16 partial buffer; then the summary and landmark
 //                  backward; writes dK, dV, dQl.
 //   k_dq_reduce  : dQ = scale * sum of a row's slots in slot order.
+// With a Q-Cal scoring query Qs (note §5.4) the chunk scores were computed
+// from Qs: dk'_c sums ds^ Qs instead of ds^ q, the partial slots leave out
+// ds^ k', and k_dq_reduce forms dQs = scale sum_c ds^_c k'_c from the ds^
+// values the key side wrote per (row, slot).
 #include "hils_internal.h"
 
 namespace hils {
@@ -98,11 +102,14 @@ __global__ __launch_bounds__(256) void k_bwd_rowd(long long rows, const uint16_t
 // dQ = scale * (sum over the row's slots of its dQ partials, fixed slot order):
 // slot k < K holds selected chunk idx[k] (written only for valid selections),
 // slot K the own chunk. Eight lanes per row, 16-byte loads issued together.
-template <int KM>
+template <int KM, bool QCAL>
 __global__ __launch_bounds__(256) void k_dq_reduce(Dims dm, long long rows,
                                                    const int32_t* __restrict__ idx,
                                                    const uint16_t* __restrict__ part,
-                                                   uint16_t* __restrict__ dQ) {
+                                                   uint16_t* __restrict__ dQ,
+                                                   const float* __restrict__ ws_dsh,
+                                                   const float* __restrict__ ksum,
+                                                   uint16_t* __restrict__ dQs) {
   const long long r0 = (long long)blockIdx.x * 32 + threadIdx.x / 8;
   const long long r = min(r0, rows - 1);
   const int c8 = threadIdx.x % 8;
@@ -133,6 +140,40 @@ __global__ __launch_bounds__(256) void k_dq_reduce(Dims dm, long long rows,
       }
     }
   }
+  float accs[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) accs[j] = 0.f;
+  if constexpr (QCAL) {
+    // dQs: ds^ k' over the selected slots in slot order, eight slots' loads at a time
+    const long long b = r / ((long long)dm.Tq * dm.H);
+    const int h = (int)(r % dm.H);
+    constexpr int KS = 8;
+    for (int k0 = 0; k0 < Ksel; k0 += KS) {
+      float dsv[KS];
+      float4 ka[KS], kb[KS];
+#pragma unroll
+      for (int q = 0; q < KS; ++q) {
+        const int k = min(k0 + q, Ksel - 1);
+        const int c = idx[r * Ksel + k];
+        const bool okq = k0 + q < Ksel && c >= 0 && c < own && c < NC;
+        dsv[q] = okq ? ws_dsh[r * Ksel + k] : 0.f;
+        const float* kp = ksum + (((b * dm.NCcap + (okq ? c : 0)) * dm.H + h) * D + c8 * 8);
+        ka[q] = *reinterpret_cast<const float4*>(kp);
+        kb[q] = *reinterpret_cast<const float4*>(kp + 4);
+      }
+#pragma unroll
+      for (int q = 0; q < KS; ++q) {
+        accs[0] = fmaf(dsv[q], ka[q].x, accs[0]);
+        accs[1] = fmaf(dsv[q], ka[q].y, accs[1]);
+        accs[2] = fmaf(dsv[q], ka[q].z, accs[2]);
+        accs[3] = fmaf(dsv[q], ka[q].w, accs[3]);
+        accs[4] = fmaf(dsv[q], kb[q].x, accs[4]);
+        accs[5] = fmaf(dsv[q], kb[q].y, accs[5]);
+        accs[6] = fmaf(dsv[q], kb[q].z, accs[6]);
+        accs[7] = fmaf(dsv[q], kb[q].w, accs[7]);
+      }
+    }
+  }
   if (r0 >= rows) return;
   uint32_t ow[4];
 #pragma unroll
@@ -140,6 +181,13 @@ __global__ __launch_bounds__(256) void k_dq_reduce(Dims dm, long long rows,
     ow[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * dm.scale) |
             ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * dm.scale) << 16);
   *reinterpret_cast<uint4*>(dQ + r * D + c8 * 8) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  if constexpr (QCAL) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      ow[j] = (uint32_t)f32_to_bf16_bits(accs[2 * j] * dm.scale) |
+              ((uint32_t)f32_to_bf16_bits(accs[2 * j + 1] * dm.scale) << 16);
+    *reinterpret_cast<uint4*>(dQs + r * D + c8 * 8) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  }
 }
 
 // ------------------------------------------------------------------ selection lists
@@ -312,6 +360,7 @@ struct KWave {
   uint16_t os[kTileRows][TP];   // dO rows of the tile
   uint16_t as[kTileRows][TP];   // value weights [row][key]
   uint16_t dsm[kTileRows][TPD]; // dS [row][key], ds^ of the row in column D
+  uint16_t ss[kTileRows][TP];   // scoring-query (Q-Cal) rows of the tile
 };
 struct KSmem {
   KWave wv[kKWaves];
@@ -332,13 +381,16 @@ static_assert(sizeof(KWave) >= kChunk * D * sizeof(float), "final reduction buff
 
 struct KTile {
   uint4 qf[2][2], of[2][2];  // B operands: Q / dO of rows 16 hf + c, features 32 ds + 8g ..
+  uint4 sf[2][2];            // the scoring query's rows (Q-Cal; zero for own rows)
   float aux[2], dvr[2];
   int rpos[2];   // position of the row, -1 beyond the tile's rows
   int slot[2];
 };
 
+template <bool QCAL>
 __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
-    Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Qs,
+    float* __restrict__ ws_dsh, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ Ql,
     const float* __restrict__ ksum, const float* __restrict__ ent,
     const float* __restrict__ lse_l, const float* __restrict__ lse_tot,
@@ -398,18 +450,30 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
       for (int ds = 0; ds < 2; ++ds) {
         T.qf[hf][ds] = *reinterpret_cast<const uint4*>(Q + r * D + 32 * ds + 8 * gl);
         T.of[hf][ds] = *reinterpret_cast<const uint4*>(dO + r * D + 32 * ds + 8 * gl);
+        if constexpr (QCAL)
+          T.sf[hf][ds] = own_rows ? make_uint4(0, 0, 0, 0)
+                                  : *reinterpret_cast<const uint4*>(Qs + r * D + 32 * ds + 8 * gl);
       }
       T.aux[hf] = v ? sm.aux[e] : 0.f;
       T.dvr[hf] = sm.dvl[e];
       T.rpos[hf] = v ? pos : -1;
       T.slot[hf] = sm.slotv[e];
     }
-    (void)own_rows;
     return T;
   };
 
   // one 32-row tile; rows beyond nr get zero weights (their Q / dO are a valid row's)
   auto compute_tile = [&](const KTile& T, bool own_rows, floatx4 (&dkq)[4], float& dbp) {
+    if constexpr (QCAL) {
+      // the scoring query's rows (prefetched with the tile), needed for dk'
+      if (!own_rows) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int ds = 0; ds < 2; ++ds)
+            *reinterpret_cast<uint4*>(&wv.ss[16 * hf + col][32 * ds + 8 * gl]) = T.sf[hf][ds];
+      }
+    }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -472,6 +536,10 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         // ds^ = alpha (r - D) of the row: db' here, dk' through the dS tile
         dsh = al * (rc - T.dvr[hf]);
         dbp += dsh;
+        if constexpr (QCAL) {
+          if (gl == 0 && T.rpos[hf] >= 0)
+            ws_dsh[(row_base + (long long)T.rpos[hf] * dm.H) * dm.K + T.slot[hf]] = dsh;
+        }
       }
       if (gl == 0) wv.dsm[16 * hf + col][D] = __builtin_bit_cast(uint16_t, (__bf16)dsh);
       uint2 dpk[4];
@@ -491,7 +559,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         floatx4 dq = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) dq = mfma(lds_ktfrag(&sm.kc[0][0], ks, 16 * db), pf[ks], dq);
-        if (!own_rows) {
+        if (!QCAL && !own_rows) {
           const float4 kb4 = *reinterpret_cast<const float4*>(&sm.kbv[16 * db + 4 * gl]);
           dq[0] = fmaf(dsh, kb4.x, dq[0]);
           dq[1] = fmaf(dsh, kb4.y, dq[1]);
@@ -520,11 +588,16 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         dka[kb][fb] = mfma(df, qbf[fb], dka[kb][fb]);
       }
     }
-    // dk' / scale += sum over the rows of ds^ q (row 0 of this product)
+    // dk' / scale += sum over the rows of ds^ q, or of ds^ times the scoring
+    // query with Q-Cal (row 0 of this product)
     {
       const uint4 hf5 = lds_kfrag<TPD>(&wv.dsm[0][0], D);
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb) dkq[fb] = mfma(hf5, qbf[fb], dkq[fb]);
+      for (int fb = 0; fb < 4; ++fb) {
+        // own rows have ds^ = 0: their scoring-query rows are not loaded
+        const uint4 qb = QCAL && !own_rows ? lds_kfrag<TP>(&wv.ss[0][0], 16 * fb) : qbf[fb];
+        dkq[fb] = mfma(hf5, qb, dkq[fb]);
+      }
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -712,7 +785,8 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
                        const void* Ql, const float* ksum, const float* ent, const float* lse_l,
                        const int32_t* idx, const float* score, const float* lse_tot,
                        const void* O, const void* dO, void* dQ, void* dK, void* dV, void* dQl,
-                       float* ws_D, void* ws_mfma, hipStream_t st, hipError_t* err) {
+                       const void* Qs, void* dQs, float* ws_D, float* ws_dsh, void* ws_mfma,
+                       hipStream_t st, hipError_t* err) {
   BPlan p;
   if (!bwd_plan(dm, &p)) return false;
   char* base = reinterpret_cast<char*>(ws_mfma);
@@ -741,24 +815,36 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
   }
   hipLaunchKernelGGL(k_sel_fill, dim3(p.nblk, dm.H, dm.B), dim3(256), p.fill_smem, st, dm, p.nblk,
                      idx, score, lse_tot, ws_D, cnt, srec);
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_kv_mfma),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(KSmem));
+  const bool qcal = Qs != nullptr;
+  const void* kvk = qcal ? reinterpret_cast<const void*>(k_bwd_kv_mfma<true>)
+                         : reinterpret_cast<const void*>(k_bwd_kv_mfma<false>);
+  e = hipFuncSetAttribute(kvk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(KSmem));
   if (e != hipSuccess) {
     *err = e;
     return true;
   }
-  hipLaunchKernelGGL(k_bwd_kv_mfma, dim3(p.nct * dm.Hkv * dm.B), dim3(kKThreads), sizeof(KSmem), st, dm,
-                     reinterpret_cast<const uint16_t*>(Q), reinterpret_cast<const uint16_t*>(K),
-                     reinterpret_cast<const uint16_t*>(V), reinterpret_cast<const uint16_t*>(Ql),
-                     ksum, ent, lse_l, lse_tot, dOh, ws_D, lstart, llen, srec,
-                     reinterpret_cast<uint16_t*>(dK), reinterpret_cast<uint16_t*>(dV),
-                     reinterpret_cast<uint16_t*>(dQl), part);
-  if (dm.K + 1 <= 17)
-    hipLaunchKernelGGL(k_dq_reduce<17>, dim3(rblocks), dim3(256), 0, st, dm, rows, idx, part,
-                       reinterpret_cast<uint16_t*>(dQ));
-  else
-    hipLaunchKernelGGL(k_dq_reduce<13>, dim3(rblocks), dim3(256), 0, st, dm, rows, idx, part,
-                       reinterpret_cast<uint16_t*>(dQ));
+  const auto* Qh = reinterpret_cast<const uint16_t*>(Q);
+  const auto* Qsh = qcal ? reinterpret_cast<const uint16_t*>(Qs) : Qh;
+#define HILS_KV(QC)                                                                                 \
+  hipLaunchKernelGGL(k_bwd_kv_mfma<QC>, dim3(p.nct * dm.Hkv * dm.B), dim3(kKThreads), sizeof(KSmem), \
+                     st, dm, Qh, Qsh, ws_dsh, reinterpret_cast<const uint16_t*>(K),                 \
+                     reinterpret_cast<const uint16_t*>(V), reinterpret_cast<const uint16_t*>(Ql),   \
+                     ksum, ent, lse_l, lse_tot, dOh, ws_D, lstart, llen, srec,                      \
+                     reinterpret_cast<uint16_t*>(dK), reinterpret_cast<uint16_t*>(dV),              \
+                     reinterpret_cast<uint16_t*>(dQl), part)
+  if (qcal) HILS_KV(true); else HILS_KV(false);
+#undef HILS_KV
+  auto* dQh = reinterpret_cast<uint16_t*>(dQ);
+  auto* dQsh = reinterpret_cast<uint16_t*>(dQs);
+#define HILS_DQ(KM, QC)                                                                          \
+  hipLaunchKernelGGL((k_dq_reduce<KM, QC>), dim3(rblocks), dim3(256), 0, st, dm, rows, idx, part, \
+                     dQh, ws_dsh, ksum, dQsh)
+  if (dm.K + 1 <= 17) {
+    if (qcal) HILS_DQ(17, true); else HILS_DQ(17, false);
+  } else {
+    if (qcal) HILS_DQ(13, true); else HILS_DQ(13, false);
+  }
+#undef HILS_DQ
   *err = hipGetLastError();
   return true;
 }

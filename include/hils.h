@@ -108,6 +108,9 @@ hils_status hils_summarize(const hils_dims* dims, const void* K, const void* Ql,
 
 /*
  * Chunk scoring and top-K selection (note §5.2, score and top-K equations).
+ * Q here is the query the scores use: with Q-Cal (note §5.4) pass the
+ * calibrated scoring query q^ = q + W_up W_down h (formed by the caller), and
+ * the token query q to hils_attend_fuse.
  * Row (b,i,h) at position p = q_pos0+i has candidates c < floor(p/S) (complete
  * chunks before its own chunk) with score
  *   s^_{i,c} = scale * Q[b,i,h] . ksum[b,c,h] + ent[b,c,h]   (float32).
@@ -147,16 +150,21 @@ hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K
  * (Ql, K). dK/dV sum over the query heads of each kv head. Inputs are the
  * forward's: Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot and its
  * output O, which gives each row's D = dO . O (the weighted mean of dO . v
- * over everything the row attends to). Requires a
- * prefill layout (q_pos0 == 0, Tq == Tkv, Tkv % S == 0). Deterministic: no
- * floating-point atomics.
+ * over everything the row attends to). Q-Cal (note §5.4): when the scores were
+ * computed from a separate scoring query, pass it as Qs [B, Tq, H, d]; the
+ * summary-key gradient then uses Qs, dQs [B, Tq, H, d] receives the gradient
+ * through the chunk scores and dQ only the one through the token attention
+ * (the caller back-propagates dQs into its calibration weights and adds it to
+ * the query's gradient). Qs and dQs are both NULL (scores from Q, dQ holds
+ * both parts) or both set. Requires a prefill layout (q_pos0 == 0,
+ * Tq == Tkv, Tkv % S == 0). Deterministic: no floating-point atomics.
  */
 hils_status hils_backward(const hils_dims* dims, const void* Q, const void* K, const void* V,
                           const void* Ql, const float* ksum, const float* ent,
                           const float* lse_l, const int32_t* idx, const float* score,
                           const float* lse_tot, const void* O, const void* dO, void* dQ,
-                          void* dK, void* dV, void* dQl, void* ws, size_t ws_bytes,
-                          hils_stream stream);
+                          void* dK, void* dV, void* dQl, const void* Qs, void* dQs, void* ws,
+                          size_t ws_bytes, hils_stream stream);
 
 /* Static description of a status code. */
 const char* hils_status_string(hils_status status);

@@ -38,6 +38,7 @@ _M2 = np.uint64(0x94D049BB133111EB)
 # stream ids, one per drawn tensor
 ST_Q, ST_K, ST_V, ST_QL, ST_DO = 1, 2, 3, 4, 5
 ST_CHUNK_PICK, ST_KEY_PICK, ST_NU_SHARED, ST_NU_NOISE = 6, 7, 9, 10
+ST_QS = 11
 
 
 def _fmix(z: np.ndarray) -> np.ndarray:
@@ -201,6 +202,14 @@ def make_inputs(w: Workload) -> Dict[str, np.ndarray]:
     out["planted_chunks"] = np.array(planted, dtype=np.int64)
     out["uniform_chunks"] = np.array(uniform_chunks, dtype=np.int64)
     return out
+
+
+def scoring_query(w: Workload, x: Dict[str, np.ndarray], spread: float = 0.5) -> np.ndarray:
+    """A stand-in for a calibrated scoring query (Q-Cal): the workload's Q plus
+    seeded N(0, spread^2) noise from a stream of its own, rounded to the dtype."""
+    q = x["Q"]
+    noise = normal(w.seed, ST_QS, q.size).reshape(q.shape)
+    return to_dtype(q.astype(np.float64) + spread * noise, w.dtype)
 
 
 def small(name: str, B=1, T=512, H=2, Hkv=1, d=64, S=64, K=4, dtype="f32", n_planted=1,

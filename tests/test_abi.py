@@ -98,7 +98,15 @@ def test_entry_points_reject_bad_pointers_without_launching():
     assert L.hils_summarize(ctypes.byref(d), p, p, 1, 1, p, p, p, nul, 0, nul) == 0  # empty range
     assert L.hils_score_topk(ctypes.byref(d), mis, p, p, p, p, nul, 0, nul) == 1
     assert L.hils_attend_fuse(ctypes.byref(d), p, p, p, p, p, nul, p, p, nul, 0, nul) == 1
-    assert L.hils_backward(ctypes.byref(d), *([p] * 15), nul, nul, 0, nul) == 1
+    assert L.hils_backward(ctypes.byref(d), *([p] * 15), nul, nul, nul, nul, 0, nul) == 1
+    d2 = base(Tq=4096, Tkv=4096)
+    n = ws_size(d2, hsa.OP_BACKWARD)[1]
+    big = ctypes.c_void_p(1 << 40)
+    # the Q-Cal pair is both NULL or both set, 16-byte aligned
+    assert L.hils_backward(ctypes.byref(d2), *([p] * 16), p, nul, big, n, nul) == 1
+    assert L.hils_backward(ctypes.byref(d2), *([p] * 16), nul, p, big, n, nul) == 1
+    assert L.hils_backward(ctypes.byref(d2), *([p] * 16), mis, p, big, n, nul) == 1
+    assert L.hils_backward(ctypes.byref(d2), *([p] * 16), p, p, big, n - 1, nul) == 3
     dd = base(Tq=1, Tkv=131073, q_pos0=131072, H=16, Hkv=16, K=16)
     assert L.hils_score_topk(ctypes.byref(dd), p, p, p, p, p, p, 8, nul) == 3   # workspace short
     assert L.hils_score_topk(None, p, p, p, p, p, nul, 0, nul) == 1

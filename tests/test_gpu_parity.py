@@ -388,6 +388,30 @@ def test_backward_small(name):
         assert_close(host(a), b, tol, nm)
 
 
+@pytest.mark.parametrize("name", ["bwd_bf16_gqa", "bwd_bf16_k20", "bwd_f32", "bwd_bf16_d128"])
+def test_backward_qcal(name):
+    """Q-Cal: the chunk scores use a separate scoring query Qs; the backward
+    returns its gradient dQs apart from dQ (matrix-core and vector paths)."""
+    w = BWD[name]
+    x = synth.make_inputs(w)
+    qs = synth.scoring_query(w, x)
+    say(f"[backward q-cal] {name}")
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql", "dO")}
+    tqs = dev(qs, w.dtype)
+    f = hsa.forward(t["Q"], t["K"], t["V"], t["Ql"], w.K, w.S, Qs=tqs)
+    g = hsa.backward(t["Q"], t["K"], t["V"], t["Ql"], f["ksum"], f["ent"], f["lse_l"], f["idx"],
+                     f["score"], f["lse_tot"], f["O"], t["dO"], w.S, Qs=tqs)
+    torch.cuda.synchronize()
+    o = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K, Qs=qs)
+    excl, eq = compare_selection(host(f["idx"]), o["idx"], o["gap"], w.K)
+    assert eq.all(), "small backward cases need identical selections"
+    tol = TOL_GRAD_BF16 if w.dtype == "bf16" else TOL_F32
+    assert_close(host(f["O"]), o["O"], out_tol(w), "O")
+    og = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], o["idx"], x["dO"], w.S, Qs=qs)
+    for nm, a, b in zip(("dQ", "dK", "dV", "dQl", "dQs"), g, og):
+        assert_close(host(a), b, tol, nm)
+
+
 def test_backward_deterministic():
     w = BWD["bwd_bf16_gqa"]
     x = synth.make_inputs(w)
