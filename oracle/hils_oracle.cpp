@@ -20,9 +20,14 @@
 //     the local branch.
 //
 // Readings taken where the pages are silent (each is restated in the tests):
-//   * candidates C_i are the complete chunks strictly before the query's own
-//     chunk; the own chunk is the local branch, attended causally with its
-//     exact log-sum-exp entering Z^_i;
+//   * the local branch is, by default (window 0), the query's own chunk up to
+//     the query, attended causally with its exact log-sum-exp entering Z^_i;
+//     candidates C_i are the complete chunks strictly before it;
+//   * with a sliding window of W > 0 tokens (page 2 §5.2 main setting: W = 512)
+//     the local branch is the last W keys [max(0, pos - W + 1), pos] and the
+//     candidates are the chunks lying wholly before the window's first key
+//     (a chunk the window cuts is not a candidate; its keys before the window
+//     are not attended);
 //   * the landmark query is per query head and attends the S keys of its
 //     chunk (not itself); landmark tokens hold no key/value;
 //   * ties in the score rank go to the lower chunk index; rows with fewer
@@ -70,6 +75,13 @@ struct Shape {
   int B, Tq, Tkv, H, Hkv, d, S, NC, Ksel;
   long q_pos0;
   double scale;
+  long window;  // local branch: 0 = own chunk, W > 0 = the last W keys
+  // first key of the local branch of the query at absolute position pos
+  long local_start(long pos) const {
+    return window > 0 ? std::max(0L, pos - window + 1) : (pos / S) * S;
+  }
+  // candidate chunks: 0 .. n_cand(pos) - 1, the chunks wholly before the local branch
+  long n_cand(long pos) const { return local_start(pos) / S; }
   const double* q(const double* Q, int b, int i, int h) const {
     return Q + (((long)b * Tq + i) * H + h) * d;
   }
@@ -102,11 +114,11 @@ void summary_one(const Shape& sh, const double* K, const double* ql, int b, int 
   if (lse) *lse = L;
 }
 
-// Scores of every candidate chunk c < c_i for one row (page 2 §5.2).
+// Scores of every candidate chunk for one row (page 2 §5.2).
 void row_scores(const Shape& sh, const double* Q, const double* ksum, const double* ent, int b,
                 int i, int h, std::vector<double>& out) {
   const long pos = sh.q_pos0 + i;
-  const int n = (int)(pos / sh.S);
+  const int n = (int)sh.n_cand(pos);
   out.resize(n);
   const double* q = sh.q(Q, b, i, h);
   for (int c = 0; c < n; ++c) {
@@ -135,8 +147,9 @@ double chunk_attend(const Shape& sh, const double* q, const double* K, const dou
 }
 
 // Forward of one row given its selected set: per selected chunk the intra-chunk
-// softmax output o_c and log-mass m_c; own chunk output and log-mass; fusion
-// logits (selected scores plus the own log-mass), their log-sum-exp and O.
+// softmax output o_c and log-mass m_c; the local branch's output and log-mass
+// (l_own); fusion logits (selected scores plus the local log-mass), their
+// log-sum-exp and O.
 struct RowFwd {
   std::vector<int> chunks;        // selected chunk ids (pads dropped)
   std::vector<double> logit;      // s^_{i,c} for selected chunks
@@ -151,7 +164,6 @@ void row_forward(const Shape& sh, const double* Q, const double* K, const double
                  const int* idx_row, const double* score_row, int b, int i, int h, RowFwd& f) {
   const int d = sh.d, S = sh.S, g = h / (sh.H / sh.Hkv);
   const long pos = sh.q_pos0 + i;
-  const long own = pos / S;
   const double* q = sh.q(Q, b, i, h);
   f.chunks.clear(); f.logit.clear(); f.m.clear(); f.o.clear();
   for (int k = 0; k < sh.Ksel; ++k) {
@@ -164,7 +176,7 @@ void row_forward(const Shape& sh, const double* Q, const double* K, const double
     f.o.push_back(oc);
   }
   f.o_own.assign(d, 0.0);
-  f.l_own = chunk_attend(sh, q, K, V, b, own * S, pos, g, f.o_own.data());
+  f.l_own = chunk_attend(sh, q, K, V, b, sh.local_start(pos), pos, g, f.o_own.data());
   std::vector<double> all(f.logit);
   all.push_back(f.l_own);
   f.Lambda = logsumexp(all);
@@ -197,7 +209,7 @@ extern "C" {
 void oracle_summarize(int B, int Tkv, int H, int Hkv, int d, int S, int NC, double scale,
                       const double* K, const double* Ql, int c_begin, int c_end, double* ksum,
                       double* ent, double* lse_l) {
-  Shape sh{B, 0, Tkv, H, Hkv, d, S, NC, 0, 0, resolve_scale(scale, d)};
+  Shape sh{B, 0, Tkv, H, Hkv, d, S, NC, 0, 0, resolve_scale(scale, d), 0};
   const int G = H / Hkv;
   for (int b = 0; b < B; ++b)
     for (int c = c_begin; c < c_end; ++c)
@@ -214,9 +226,10 @@ void oracle_summarize(int B, int Tkv, int H, int Hkv, int d, int S, int NC, doub
 // with -inf, gap the difference between the K-th and (K+1)-th largest score
 // (+inf when the row has at most K candidates).
 void oracle_score_topk(int B, int Tq, long q_pos0, int H, int d, int S, int NC, int Ksel,
-                       double scale, const double* Q, const double* ksum, const double* ent,
+                       double scale, long window, const double* Q, const double* ksum,
+                       const double* ent,
                        long nrows, const long* rows, int* idx, double* score, double* gap) {
-  Shape sh{B, Tq, 0, H, 0, d, S, NC, Ksel, q_pos0, resolve_scale(scale, d)};
+  Shape sh{B, Tq, 0, H, 0, d, S, NC, Ksel, q_pos0, resolve_scale(scale, d), window};
   std::vector<long> rl;
   list_rows(sh, nrows, rows, rl);
   std::vector<double> s;
@@ -252,10 +265,11 @@ void oracle_score_topk(int B, int Tq, long q_pos0, int H, int d, int S, int NC, 
 // set in ascending order for each listed row; score is the row's own head score
 // of each selected chunk; gap is taken on the aggregated scores.
 void oracle_score_topk_group(int B, int Tq, long q_pos0, int H, int Hkv, int d, int S, int NC,
-                             int Ksel, double scale, const double* Q, const double* ksum,
+                             int Ksel, double scale, long window, const double* Q,
+                             const double* ksum,
                              const double* ent, long nrows, const long* rows, int* idx,
                              double* score, double* gap) {
-  Shape sh{B, Tq, 0, H, Hkv, d, S, NC, Ksel, q_pos0, resolve_scale(scale, d)};
+  Shape sh{B, Tq, 0, H, Hkv, d, S, NC, Ksel, q_pos0, resolve_scale(scale, d), window};
   const int G = H / Hkv;
   std::vector<long> rl;
   list_rows(sh, nrows, rows, rl);
@@ -291,11 +305,12 @@ void oracle_score_topk_group(int B, int Tq, long q_pos0, int H, int Hkv, int d, 
 }
 
 // Exact log chunk masses log Z_{i,c} (page 2 §3, naive block sparse attention)
-// of every candidate chunk c < c_i; entries c >= c_i are -inf. out is [rows][NC].
+// of every candidate chunk; entries of other chunks are -inf. out is [rows][NC].
 void oracle_exact_chunk_lse(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d, int S,
-                            int NC, double scale, const double* Q, const double* K, long nrows,
+                            int NC, double scale, long window, const double* Q, const double* K,
+                            long nrows,
                             const long* rows, double* out) {
-  Shape sh{B, Tq, Tkv, H, Hkv, d, S, NC, 0, q_pos0, resolve_scale(scale, d)};
+  Shape sh{B, Tq, Tkv, H, Hkv, d, S, NC, 0, q_pos0, resolve_scale(scale, d), window};
   std::vector<long> rl;
   list_rows(sh, nrows, rows, rl);
   std::vector<double> tmp(d);
@@ -303,7 +318,7 @@ void oracle_exact_chunk_lse(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv,
     const int h = (int)(r % H);
     const int i = (int)((r / H) % Tq);
     const int b = (int)(r / ((long)H * Tq));
-    const long n = (q_pos0 + i) / S;
+    const long n = sh.n_cand(q_pos0 + i);
     for (int c = 0; c < NC; ++c) {
       double v = -INFINITY;
       if (c < n) {
@@ -318,14 +333,15 @@ void oracle_exact_chunk_lse(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv,
   }
 }
 
-// Intra-chunk attention over each selected chunk plus the causal own chunk,
-// fused by the inter-chunk softmax (page 2 §5.3, page 4 Fig. 3). lse_own and
-// lse_tot may be NULL.
+// Intra-chunk attention over each selected chunk plus the local branch (the
+// causal own chunk, or the last `window` keys), fused by the inter-chunk
+// softmax (page 2 §5.3, page 4 Fig. 3). lse_own (the local branch's log-mass)
+// and lse_tot may be NULL.
 void oracle_attend_fuse(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d, int S,
-                        int Ksel, double scale, const double* Q, const double* K,
+                        int Ksel, double scale, long window, const double* Q, const double* K,
                         const double* V, const int* idx, const double* score, long nrows,
                         const long* rows, double* O, double* lse_own, double* lse_tot) {
-  Shape sh{B, Tq, Tkv, H, Hkv, d, S, 0, Ksel, q_pos0, resolve_scale(scale, d)};
+  Shape sh{B, Tq, Tkv, H, Hkv, d, S, 0, Ksel, q_pos0, resolve_scale(scale, d), window};
   std::vector<long> rl;
   list_rows(sh, nrows, rows, rl);
   RowFwd f;
@@ -351,11 +367,12 @@ void oracle_attend_fuse(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int
 // group) are produced. NULL masks mean everything. Entries outside the masks are
 // left untouched. idx must be the selection made from these inputs.
 void oracle_backward(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d, int S, int NC,
-                     int Ksel, double scale, const double* Q, const double* K, const double* V,
+                     int Ksel, double scale, long window, const double* Q, const double* K,
+                     const double* V,
                      const double* Ql, const int* idx, const double* dO,
                      const unsigned char* row_mask, const unsigned char* kv_mask, double* dQ,
                      double* dK, double* dV, double* dQl, const double* Qs, double* dQs) {
-  Shape sh{B, Tq, Tkv, H, Hkv, d, S, NC, Ksel, q_pos0, resolve_scale(scale, d)};
+  Shape sh{B, Tq, Tkv, H, Hkv, d, S, NC, Ksel, q_pos0, resolve_scale(scale, d), window};
   const double tau = sh.scale;
   const int G = H / Hkv;
   auto kv_on = [&](int b, long c, int g) {
@@ -377,9 +394,9 @@ void oracle_backward(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d,
         const long r = sh.row(b, i, h);
         const int g = h / G;
         const long pos = q_pos0 + i;
-        const long own = pos / S;
+        const long l0 = sh.local_start(pos);
         bool need = !row_mask || row_mask[r];
-        if (!need) need = kv_on(b, own, g);
+        for (long c = l0 / S; c <= pos / S && !need; ++c) need = kv_on(b, c, g);
         for (int k = 0; k < Ksel && !need; ++k) {
           const int c = idx[r * Ksel + k];
           if (c >= 0 && kv_on(b, c, g)) need = true;
@@ -427,14 +444,14 @@ void oracle_backward(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d,
             }
           }
         }
-        // own chunk: weights w_j = exp(s_j - Lambda); its log-mass is also a fusion logit
-        for (long key = own * S; key <= pos; ++key) {
+        // local branch: weights w_j = exp(s_j - Lambda); its log-mass is also a fusion logit
+        for (long key = l0; key <= pos; ++key) {
           const double* kj = sh.kv(K, b, key, g);
           const double* vj = sh.kv(V, b, key, g);
           const double w = std::exp(tau * dot(q, kj, d) - f.Lambda);
           const double ds = w * (dot(go, vj, d) - D);
           for (int e = 0; e < d; ++e) dq[e] += tau * ds * kj[e];
-          if (kv_on(b, own, g)) {
+          if (kv_on(b, key / S, g)) {
             double* gk = gK.data() + (((long)b * Tkv + key) * Hkv + g) * d;
             double* gv = gV.data() + (((long)b * Tkv + key) * Hkv + g) * d;
             for (int e = 0; e < d; ++e) gk[e] += tau * ds * q[e];
@@ -481,7 +498,7 @@ void oracle_backward(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d,
           for (int e = 0; e < d; ++e) { dK[off + e] = gK[off + e]; dV[off + e] = gV[off + e]; }
         }
       }
-  // keys of an incomplete trailing chunk (decode caches) only receive own-chunk terms
+  // keys of an incomplete trailing chunk (decode caches) only receive local-branch terms
   const long tail0 = (long)NC * S;
   for (int b = 0; b < B; ++b)
     for (long key = tail0; key < Tkv; ++key)

@@ -32,8 +32,9 @@ def all_scores(Q, ksum, ent, S, q_pos0=0):
     return idx, score
 
 
-def dense_causal(Q, K, V, q_pos0=0):
-    """torch fp64 scaled-dot-product attention, causal over absolute positions."""
+def dense_causal(Q, K, V, q_pos0=0, keep=None):
+    """torch fp64 scaled-dot-product attention, causal over absolute positions;
+    keep [Tq, Tkv] (bool), when given, further restricts the keys each row sees."""
     Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
     B, Tq, H, d = Q.shape
     Tkv, Hkv = K.shape[1], K.shape[2]
@@ -42,7 +43,8 @@ def dense_causal(Q, K, V, q_pos0=0):
     k = torch.from_numpy(np.ascontiguousarray(np.repeat(K, G, axis=2).transpose(0, 2, 1, 3)))
     v = torch.from_numpy(np.ascontiguousarray(np.repeat(V, G, axis=2).transpose(0, 2, 1, 3)))
     pos = q_pos0 + np.arange(Tq)[:, None]
-    mask = torch.from_numpy(np.arange(Tkv)[None, :] <= pos)
+    m = np.arange(Tkv)[None, :] <= pos
+    mask = torch.from_numpy(m if keep is None else m & keep)
     o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
     logits = (q @ k.transpose(-1, -2)) / math.sqrt(d)
     lse = torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=-1)
@@ -268,6 +270,65 @@ def test_full_attention_equivalence(H, Hkv):
     np.testing.assert_allclose(lt, lse, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("W", [64, 96, 128])
+def test_window_full_attention_equivalence(W):
+    """Sliding-window local branch (page 2 §5.2: SWA with chunk selection): with exact
+    chunk masses as scores and every candidate selected, each row attends exactly to
+    the chunks wholly before its window plus the window's keys, as one softmax."""
+    S, d, T, H, Hkv = 32, 32, 512, 2, 1
+    Q = normals((1, T, H, d), 81)
+    K = normals((1, T, Hkv, d), 82)
+    V = normals((1, T, Hkv, d), 83)
+    NC = T // S
+    lz = oracle.exact_chunk_lse(Q, K, S, NC, window=W)
+    idx = np.full((1, T, H, NC), -1, dtype=np.int32)
+    score = np.full((1, T, H, NC), -np.inf)
+    keep = np.zeros((T, T), dtype=bool)
+    for i in range(T):
+        first = max(0, i - W + 1)              # the window: the last W keys
+        n = first // S                          # chunks ending before the window
+        assert np.all(np.isinf(lz[0, i, :, n:])) and np.all(np.isfinite(lz[0, i, :, :n]))
+        idx[0, i, :, :n] = np.arange(n)
+        score[0, i, :, :n] = lz[0, i, :, :n]
+        keep[i, :n * S] = True
+        keep[i, first:i + 1] = True
+    O, lo, lt = oracle.attend_fuse(Q, K, V, idx, score, S, window=W)
+    Od, lse = dense_causal(Q, K, V, keep=keep)
+    np.testing.assert_allclose(O, Od, rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(lt, lse, rtol=1e-12, atol=1e-12)
+    # the window's own log-mass is the dense LSE over the window alone
+    wonly = np.zeros((T, T), dtype=bool)
+    for i in range(T):
+        wonly[i, max(0, i - W + 1):i + 1] = True
+    np.testing.assert_allclose(lo, dense_causal(Q, K, V, keep=wonly)[1], rtol=1e-12, atol=1e-12)
+
+
+def test_window_covering_the_prefix_is_causal_attention():
+    """A window at least as long as the sequence leaves no candidate chunk: every row
+    is plain causal attention, whatever K."""
+    w = synth.small("wfull", T=384, H=2, Hkv=1, d=32, S=64, K=3)
+    x = synth.make_inputs(w)
+    f = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K, window=512)
+    Od, lse = dense_causal(x["Q"], x["K"], x["V"])
+    np.testing.assert_allclose(f["O"], Od, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(f["lse_tot"], lse, rtol=1e-12, atol=1e-12)
+    assert np.all(f["idx"] == -1)
+
+
+def test_window_candidates_lie_wholly_before_the_window():
+    """With W = 2S the candidate chunks are exactly those whose last key precedes the
+    window's first key: a chunk the window cuts is never scored."""
+    w = synth.small("wcand", T=640, H=2, Hkv=1, d=32, S=64, K=20)
+    x = synth.make_inputs(w)
+    ksum, ent, _ = oracle.summarize(x["K"], x["Ql"], w.S)
+    idx, score, _ = oracle.score_topk(x["Q"], ksum, ent, w.S, w.NC, window=128)
+    for i in (0, 126, 127, 128, 190, 191, 192, 255, 256, 639):
+        first = max(0, i - 127)
+        got = set(int(c) for c in idx[0, i, 0] if c >= 0)
+        want = {c for c in range(w.NC) if (c + 1) * w.S - 1 < first}
+        assert got == want, (i, sorted(got))
+
+
 def test_first_chunk_rows_are_causal_attention():
     """Rows in chunk 0 have no candidates: plain causal attention over positions <= i."""
     w = synth.small("c0", T=256, H=2, Hkv=1, d=32, S=64, K=2)
@@ -307,9 +368,10 @@ def test_decode_equals_prefill_row():
 
 
 # ---------------------------------------------------------------- backward
-def torch_hils(Q, K, V, Ql, idx, S, Qs=None):
+def torch_hils(Q, K, V, Ql, idx, S, Qs=None, window=0):
     """Dense, differentiable restatement of the forward with fixed idx (torch fp64);
-    Qs, when given, is the scoring query of the chunk scores (Q-Cal)."""
+    Qs, when given, is the scoring query of the chunk scores (Q-Cal); window > 0
+    makes the local branch the last `window` keys instead of the own chunk."""
     B, T, H, d = Q.shape
     Hkv = K.shape[2]
     G, NC, tau = H // Hkv, Ql.shape[1], 1.0 / math.sqrt(d)
@@ -331,7 +393,7 @@ def torch_hils(Q, K, V, Ql, idx, S, Qs=None):
                     logits.append(tau * (ksum[b, c, h] @ qs) + ent[b, c, h])
                     s = tau * (Kh[b, c * S:(c + 1) * S, h] @ q)
                     outs.append(torch.softmax(s, 0) @ Vh[b, c * S:(c + 1) * S, h])
-                own = (i // S) * S
+                own = (i // S) * S if window == 0 else max(0, i - window + 1)
                 s = tau * (Kh[b, own:i + 1, h] @ q)
                 logits.append(torch.logsumexp(s, 0))
                 outs.append(torch.softmax(s, 0) @ Vh[b, own:i + 1, h])
@@ -445,6 +507,58 @@ def test_qcal_with_token_query_splits_the_plain_gradient():
     assert np.abs(split[4]).max() > 1e-3 * np.abs(plain[0]).max()
     for a, b in zip(split[1:4], plain[1:4]):
         np.testing.assert_array_equal(a, b)
+
+
+def test_window_backward_matches_autograd_and_differences():
+    """Sliding-window local branch (W = 40 keys, S = 16): the backward equals autograd
+    of the dense restatement and central differences of the oracle's own forward."""
+    w = synth.small("bwdw", B=1, T=256, H=4, Hkv=2, d=16, S=16, K=3, n_planted=1,
+                    need_dO=True)
+    x = synth.make_inputs(w)
+    W = 40
+    f = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K, window=W)
+    grads = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], f["idx"], x["dO"], w.S, window=W)
+    t = {k: torch.from_numpy(x[k].astype(np.float64)).requires_grad_(True)
+         for k in ("Q", "K", "V", "Ql")}
+    O = torch_hils(t["Q"], t["K"], t["V"], t["Ql"], f["idx"], w.S, window=W)
+    np.testing.assert_allclose(O.detach().numpy(), f["O"], rtol=1e-11, atol=1e-12)
+    (O * torch.from_numpy(x["dO"].astype(np.float64))).sum().backward()
+    for name, g in zip(("Q", "K", "V", "Ql"), grads):
+        np.testing.assert_allclose(g, t[name].grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
+    base = {k: x[k].astype(np.float64) for k in ("Q", "K", "V", "Ql")}
+    dO = x["dO"].astype(np.float64)
+    rng = np.random.default_rng(7)
+    h = 1e-6
+    for gi, name in enumerate(("Q", "K", "V", "Ql")):
+        for _ in range(3):
+            pos = tuple(rng.integers(0, sz) for sz in base[name].shape)
+            vals = []
+            for sgn in (1, -1):
+                arrs = {k: v.copy() for k, v in base.items()}
+                arrs[name][pos] += sgn * h
+                g = oracle.forward(arrs["Q"], arrs["K"], arrs["V"], arrs["Ql"], w.S, w.K, window=W)
+                assert np.array_equal(g["idx"], f["idx"])
+                vals.append(np.sum(g["O"] * dO))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            assert fd == pytest.approx(grads[gi][pos], rel=1e-5, abs=1e-7), (name, pos)
+
+
+def test_window_decode_equals_prefill_row():
+    """Decode with a sliding window: position p over a cache of p+1 keys = prefill row p."""
+    w = synth.small("decw", T=1024, H=2, Hkv=1, d=32, S=64, K=4)
+    x = synth.make_inputs(w)
+    W = 256
+    f = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K, window=W)
+    for p in (63, 255, 256, 319, 320, 700, 1023):
+        nc = (p + 1) // w.S
+        Kc, Vc = x["K"][:, : p + 1], x["V"][:, : p + 1]
+        ksum, ent, _ = oracle.summarize(Kc, x["Ql"][:, :nc], w.S)
+        q = x["Q"][:, p:p + 1]
+        idx, score, _ = oracle.score_topk(q, ksum, ent, w.S, w.K, q_pos0=p, window=W)
+        O, lo, lt = oracle.attend_fuse(q, Kc, Vc, idx, score, w.S, q_pos0=p, window=W)
+        np.testing.assert_array_equal(idx[:, 0], f["idx"][:, p])
+        np.testing.assert_allclose(O[:, 0], f["O"][:, p], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lt[:, 0], f["lse_tot"][:, p], rtol=1e-13)
 
 
 def test_backward_masks_restrict_work():
