@@ -31,7 +31,7 @@ class hils_dims(ctypes.Structure):
                 ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32), ("S", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("dtype", ctypes.c_int32), ("select_mode", ctypes.c_int32),
                 ("q_pos0", ctypes.c_int64), ("scale", ctypes.c_float),
-                ("reserved2", ctypes.c_float)]
+                ("window", ctypes.c_int32)]
 
 
 class HilsError(RuntimeError):
@@ -77,9 +77,9 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def make_dims(B, Tq, Tkv, H, Hkv, d, S, K, dtype, q_pos0=0, scale=0.0, Tkv_cap=0,
-              NC_cap=0, select_mode=0) -> hils_dims:
+              NC_cap=0, select_mode=0, window=0) -> hils_dims:
     return hils_dims(B, Tq, Tkv, Tkv_cap, NC_cap, H, Hkv, d, S, K, dtype, select_mode, q_pos0,
-                     scale, 0.0)
+                     scale, window)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -145,9 +145,10 @@ def summarize(K: torch.Tensor, Ql: torch.Tensor, S: int = 64, c_begin: int = 0,
 
 def score_topk(Q: torch.Tensor, ksum: torch.Tensor, ent: torch.Tensor, K_sel: int, S: int = 64,
                q_pos0: int = 0, Tkv: Optional[int] = None, scale: float = 0.0, Hkv: int = 1,
-               idx=None, score=None, group: bool = False):
+               idx=None, score=None, group: bool = False, window: int = 0):
     """Top-K chunk selection for query rows at positions q_pos0.. -> (idx int32, score f32).
-    group=True selects one chunk set per kv head by the group maximum of the scores."""
+    group=True selects one chunk set per kv head by the group maximum of the scores;
+    window is the local branch (0: own chunk; W > 0: the last W keys)."""
     B, Tq, H, d = Q.shape
     NCcap = ksum.shape[1]
     Tkv = q_pos0 + Tq if Tkv is None else Tkv
@@ -159,7 +160,7 @@ def score_topk(Q: torch.Tensor, ksum: torch.Tensor, ent: torch.Tensor, K_sel: in
     _need(idx, "idx", (B, Tq, H, K_sel), torch.int32)
     _need(score, "score", (B, Tq, H, K_sel), torch.float32)
     dims = make_dims(B, Tq, Tkv, H, Hkv, d, S, K_sel, _dtype_code(Q), q_pos0, scale,
-                     max(Tkv, NCcap * S), NCcap, 1 if group else 0)
+                     max(Tkv, NCcap * S), NCcap, 1 if group else 0, window)
     ws, n = _workspace(dims, OP_SCORE_TOPK, dev)
     _check("hils_score_topk", lib().hils_score_topk(
         ctypes.byref(dims), _ptr(Q), _ptr(ksum), _ptr(ent), _ptr(idx), _ptr(score), _ptr(ws), n,
@@ -169,8 +170,9 @@ def score_topk(Q: torch.Tensor, ksum: torch.Tensor, ent: torch.Tensor, K_sel: in
 
 def attend_fuse(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor,
                 score: torch.Tensor, S: int = 64, q_pos0: int = 0, Tkv: Optional[int] = None,
-                scale: float = 0.0, O=None, lse_own=None, lse_tot=None):
-    """Hierarchical attention -> (O [B,Tq,H,d], lse_own [B,Tq,H], lse_tot [B,Tq,H])."""
+                scale: float = 0.0, O=None, lse_own=None, lse_tot=None, window: int = 0):
+    """Hierarchical attention -> (O [B,Tq,H,d], lse_own [B,Tq,H], lse_tot [B,Tq,H]);
+    lse_own is the local branch's log-mass (own chunk, or the last `window` keys)."""
     B, Tq, H, d = Q.shape
     Tcap, Hkv = K.shape[1], K.shape[2]
     K_sel = idx.shape[-1]
@@ -183,7 +185,8 @@ def attend_fuse(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Te
     lse_own = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if lse_own is None else lse_own
     lse_tot = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if lse_tot is None else lse_tot
     _need(O, "O", Q.shape, Q.dtype)
-    dims = make_dims(B, Tq, Tkv, H, Hkv, d, S, K_sel, _dtype_code(Q), q_pos0, scale, Tcap, 0)
+    dims = make_dims(B, Tq, Tkv, H, Hkv, d, S, K_sel, _dtype_code(Q), q_pos0, scale, Tcap, 0,
+                     window=window)
     ws, n = _workspace(dims, OP_ATTEND_FUSE, dev)
     _check("hils_attend_fuse", lib().hils_attend_fuse(
         ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(score), _ptr(O),
@@ -192,19 +195,20 @@ def attend_fuse(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Te
 
 
 def forward(Q, K, V, Ql, K_sel: int, S: int = 64, scale: float = 0.0, group: bool = False,
-            Qs=None):
+            Qs=None, window: int = 0):
     """Prefill forward: summaries, selection, attention. Returns a dict of tensors.
-    Qs is an optional Q-Cal scoring query (the chunk scores use it, the attention Q)."""
+    Qs is an optional Q-Cal scoring query (the chunk scores use it, the attention Q);
+    window is the local branch (0: own chunk; W > 0: sliding window of W keys)."""
     ksum, ent, lse_l = summarize(K, Ql, S, scale=scale)
     idx, score = score_topk(Q if Qs is None else Qs, ksum, ent, K_sel, S, 0, K.shape[1], scale,
-                            Hkv=K.shape[2], group=group)
-    O, lse_own, lse_tot = attend_fuse(Q, K, V, idx, score, S, 0, scale=scale)
+                            Hkv=K.shape[2], group=group, window=window)
+    O, lse_own, lse_tot = attend_fuse(Q, K, V, idx, score, S, 0, scale=scale, window=window)
     return dict(ksum=ksum, ent=ent, lse_l=lse_l, idx=idx, score=score, O=O, lse_own=lse_own,
                 lse_tot=lse_tot)
 
 
 def backward(Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, S: int = 64,
-             scale: float = 0.0, Qs=None):
+             scale: float = 0.0, Qs=None, window: int = 0):
     """Gradients (dQ, dK, dV, dQl) of sum(dO * O) with the selection held fixed; O is the
     forward's output. With a Q-Cal scoring query Qs (the query the chunk scores were
     computed from) the result is (dQ, dK, dV, dQl, dQs): dQs through the scores, dQ
@@ -222,7 +226,8 @@ def backward(Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, S: int =
     dev = Q.device
     dQ, dK, dV, dQl = (torch.empty_like(x) for x in (Q, K, V, Ql))
     dQs = None if Qs is None else torch.empty_like(Q)
-    dims = make_dims(B, T, T, H, Hkv, d, S, K_sel, _dtype_code(Q), 0, scale, T, NC)
+    dims = make_dims(B, T, T, H, Hkv, d, S, K_sel, _dtype_code(Q), 0, scale, T, NC,
+                     window=window)
     ws, n = _workspace(dims, OP_BACKWARD, dev)
     _check("hils_backward", lib().hils_backward(
         ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(Ql), _ptr(ksum), _ptr(ent),

@@ -13,7 +13,7 @@ bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr
 hils_status resolve(const hils_dims* in, hils::Dims* out) {
   if (in == nullptr || out == nullptr) return HILS_ERR_INVALID_ARG;
   const hils_dims& d = *in;
-  if (d.reserved2 != 0.0f) return HILS_ERR_INVALID_ARG;
+  if (d.window < 0) return HILS_ERR_INVALID_ARG;
   if (d.select_mode != HILS_SELECT_PER_HEAD && d.select_mode != HILS_SELECT_GROUP_MAX)
     return HILS_ERR_INVALID_ARG;
   if (d.B < 1 || d.Tq < 0 || d.Tkv < 1 || d.H < 1 || d.Hkv < 1 || d.H % d.Hkv != 0)
@@ -21,6 +21,7 @@ hils_status resolve(const hils_dims* in, hils::Dims* out) {
   if (d.dtype != HILS_F32 && d.dtype != HILS_BF16) return HILS_ERR_INVALID_ARG;
   if (d.S < 1 || d.d < 1 || d.K < 1) return HILS_ERR_INVALID_ARG;
   if (d.S != hils::kChunk || (d.d != 64 && d.d != 128) || d.K > hils::kMaxSel) return HILS_ERR_UNSUPPORTED;
+  if (d.window % d.S != 0 || d.window > hils::kMaxWinChunks * d.S) return HILS_ERR_UNSUPPORTED;
   if (d.q_pos0 < 0 || d.q_pos0 + d.Tq > d.Tkv) return HILS_ERR_INVALID_ARG;
   if (d.Tkv_cap < 0 || d.NC_cap < 0) return HILS_ERR_INVALID_ARG;
   const int Tcap = d.Tkv_cap ? d.Tkv_cap : d.Tkv;
@@ -43,6 +44,7 @@ hils_status resolve(const hils_dims* in, hils::Dims* out) {
   out->q_pos0 = d.q_pos0;
   out->scale = d.scale != 0.0f ? d.scale : 1.0f / std::sqrt((float)d.d);
   out->group_sel = d.select_mode == HILS_SELECT_GROUP_MAX;
+  out->window = d.window;
   if (out->group_sel && ((out->G & (out->G - 1)) != 0 || out->G > 64)) return HILS_ERR_UNSUPPORTED;
   return HILS_OK;
 }

@@ -9,6 +9,7 @@ namespace hils {
 constexpr int kWave = 64;   // CDNA wavefront width
 constexpr int kChunk = 64;  // supported chunk size S (one key per lane)
 constexpr int kMaxSel = 64;  // largest supported top-K
+constexpr int kMaxWinChunks = 32;  // largest sliding window, in chunks (2048 keys)
 
 // Dimensions after validation and defaulting (see hils_dims in hils.h).
 struct Dims {
@@ -17,6 +18,23 @@ struct Dims {
   bool group_sel;  // one chunk set per kv head by the group maximum of the scores
   long long q_pos0;
   float scale;
+  int window;  // local branch: 0 = the query's own chunk; W > 0 = the last W keys
+  // first key of the local branch of the query at absolute position pos
+  __host__ __device__ __forceinline__ long long lstart(long long pos) const {
+    return window > 0 ? (pos >= window ? pos - window + 1 : 0) : pos - pos % S;
+  }
+  // candidates are the chunks 0 .. ncand(pos) - 1, wholly before the local branch
+  __host__ __device__ __forceinline__ int ncand(long long pos) const {
+    return (int)(lstart(pos) / S);
+  }
+  // chunks the local branch of pos touches: lstart(pos) / S .. pos / S
+  __host__ __device__ __forceinline__ int nlocal(long long pos) const {
+    return (int)(pos / S - lstart(pos) / S) + 1;
+  }
+  // most local chunks of any query (partial slots per row in the decode and backward paths)
+  __host__ __device__ __forceinline__ int nlocal_max() const {
+    return window > 0 ? window / S + 1 : 1;
+  }
 };
 
 // ---------------------------------------------------------------- numerics

@@ -1,11 +1,13 @@
-// Intra-chunk attention over the selected chunks plus the causal own chunk,
-// fused with the inter-chunk softmax (note §5.3 hierarchical softmax; Tide
-// Fig. 3: intra-chunk weight exp(s_ij)/Z_{i,c(j)} times inter-chunk share
-// exp(s^_{i,c})/Z^_i, with the own chunk's exact mass inside Z^_i).
+// Intra-chunk attention over the selected chunks plus the local branch (the
+// causal own chunk, or a sliding window of the last W keys), fused with the
+// inter-chunk softmax (note §5.3 hierarchical softmax; Tide Fig. 3:
+// intra-chunk weight exp(s_ij)/Z_{i,c(j)} times inter-chunk share
+// exp(s^_{i,c})/Z^_i, with the local branch's exact mass inside Z^_i).
 //
 // Each (query, chunk) pair is an independent softmax over at most S = 64 keys,
-// so the fusion weight of every chunk is known once the own chunk's log-mass
-// is: w_ij = exp(s_ij - m_ic + s^_ic - Lambda_i). No online rescaling is needed.
+// so the fusion weight of every chunk is known once the local branch's
+// log-mass is: w_ij = exp(s_ij - m_ic + s^_ic - Lambda_i); a local key gets
+// exp(s_ij - Lambda_i). No online rescaling of outputs is needed.
 //
 // Rows kernel: one wavefront per (b, i, h). Lane j owns key j for the logits;
 // lane e owns output features e (and e+64) for the value sum, with the weights
@@ -60,20 +62,31 @@ __global__ __launch_bounds__(256) void k_attend_rows(Dims dm, const void* __rest
   const int g = h / dm.G;
   const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
   const long long pos = dm.q_pos0 + i;
-  const long long own = pos / dm.S;
+  const int ncand = dm.ncand(pos);
   const long long kv_stride = (long long)dm.Hkv * D;                 // elements between key rows
   const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;  // row 0 of (b, g)
 
   float q[D];
   load_row<BF16, D>(Q, r * D, q);
 
-  // own chunk: keys own*S .. pos (causal)
-  const long long j_own = own * dm.S + lane;
-  const bool own_valid = j_own <= pos;
-  float s_own = -INFINITY;
-  if (own_valid) s_own = key_logit<BF16, D>(K, kv_base + j_own * kv_stride, q, dm.scale);
-  const float m_own = wave_max(s_own);
-  const float l_own = m_own + logf(wave_sum(own_valid ? expf(s_own - m_own) : 0.0f));
+  // local branch: keys l0 .. pos, chunk by chunk (one chunk for the own-chunk branch)
+  const long long l0 = dm.lstart(pos), c_lo = l0 / dm.S, c_hi = pos / dm.S;
+  auto local_logit = [&](long long cc, bool* v) {
+    const long long j = cc * dm.S + lane;
+    *v = j >= l0 && j <= pos;
+    return *v ? key_logit<BF16, D>(K, kv_base + j * kv_stride, q, dm.scale) : -INFINITY;
+  };
+  float m_loc = -INFINITY, z_loc = 0.0f;  // running max and sum over the local chunks
+  for (long long cc = c_lo; cc <= c_hi; ++cc) {
+    bool v;
+    const float s = local_logit(cc, &v);
+    const float m = wave_max(s);
+    const float z = wave_sum(v ? expf(s - m) : 0.0f);
+    const float mn = fmaxf(m_loc, m);
+    z_loc = z_loc * expf(m_loc - mn) + z * expf(m - mn);
+    m_loc = mn;
+  }
+  const float l_own = m_loc + logf(z_loc);
 
   // inter-chunk normaliser over the selected scores and the own log-mass
   const int Ksel = dm.K;
@@ -85,13 +98,17 @@ __global__ __launch_bounds__(256) void k_attend_rows(Dims dm, const void* __rest
   float acc[D / kWave];
 #pragma unroll
   for (int x = 0; x < D / kWave; ++x) acc[x] = 0.0f;
-  const float w_own = own_valid ? expf(s_own - Lambda) : 0.0f;
-  accumulate_values<BF16, D>(V, kv_base + own * dm.S * kv_stride, kv_stride, w_own,
-                             (int)(pos - own * dm.S) + 1, lane, acc);
+  for (long long cc = c_lo; cc <= c_hi; ++cc) {
+    bool v;
+    const float s = local_logit(cc, &v);
+    accumulate_values<BF16, D>(V, kv_base + cc * dm.S * kv_stride, kv_stride,
+                               v ? expf(s - Lambda) : 0.0f,
+                               (int)min((long long)kChunk, pos - cc * dm.S + 1), lane, acc);
+  }
 
   for (int k = 0; k < Ksel; ++k) {
     const int c = idx[r * Ksel + k];  // wave-uniform
-    if (c < 0 || c >= own) continue;  // pads; ids outside the candidate range are ignored
+    if (c < 0 || c >= ncand) continue;  // pads; ids outside the candidate range are ignored
     const float sh = score[r * Ksel + k];
     const long long j = (long long)c * dm.S + lane;
     const float s = key_logit<BF16, D>(K, kv_base + j * kv_stride, q, dm.scale);
@@ -111,9 +128,11 @@ __global__ __launch_bounds__(256) void k_attend_rows(Dims dm, const void* __rest
 
 // ---------------------------------------------------------------- decode
 // Few query rows (decode): one wavefront per (slot, row): slot k < K attends
-// selected chunk idx[k], slot K the causal own chunk. Each writes its normalised
-// output and log-mass to the workspace; a combine kernel then applies the
-// inter-chunk softmax per row in a fixed slot order.
+// selected chunk idx[k], slots K .. K + NL - 1 the local branch's chunks (its
+// keys inside each chunk). Each writes its normalised output and log-mass to
+// the workspace; a combine kernel then applies the inter-chunk softmax per row
+// in a fixed slot order (a local chunk enters with its exact log-mass, which
+// sums to the local branch's).
 // bf16 key and value rows are read with 16-byte loads in one layout: the wave's
 // lanes form NG = 64 / LP groups of LP = d / 8 lanes; group q holds rows
 // NV q .. NV q + NV - 1 (NV = d / 8) and lane l % LP of the group the features
@@ -274,7 +293,7 @@ __device__ __forceinline__ void decode_slot_f32(const Dims& dm, const float* qs,
   if (lane == 0) *l_out = L;
 }
 
-// Slot kernel: grid (K + 1, rows), one wavefront per (slot, row); writes the
+// Slot kernel: grid (K + NL, rows), one wavefront per (slot, row); writes the
 // slot's normalised output and log-mass (-inf for padding) to the workspace.
 // Spreading the slots over workgroups keeps many chunk reads in flight at once.
 template <bool BF16, int D>
@@ -291,8 +310,9 @@ __global__ __launch_bounds__(64) void k_decode_partial(Dims dm, const void* __re
   const int h = (int)(r % dm.H), i = (int)((r / dm.H) % dm.Tq);
   const int b = (int)(r / ((long long)dm.H * dm.Tq));
   const int g = h / dm.G;
-  const long long pos = dm.q_pos0 + i, own = pos / dm.S;
-  const long long po = r * (dm.K + 1) + slot;
+  const long long pos = dm.q_pos0 + i;
+  const int ncand = dm.ncand(pos);
+  const long long po = r * (dm.K + dm.nlocal_max()) + slot;
   const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
   const long long kv_stride = (long long)dm.Hkv * D;
   // query and selection read together (unconditionally, indices in bounds)
@@ -305,15 +325,20 @@ __global__ __launch_bounds__(64) void k_decode_partial(Dims dm, const void* __re
   long long key0;
   int nk;
   if (slot < dm.K) {
-    if (c < 0 || c >= own) {  // padding slot: no mass
+    if (c < 0 || c >= ncand) {  // padding slot: no mass
       if (lane == 0) part_l[po] = -INFINITY;
       return;
     }
     key0 = (long long)c * dm.S;
     nk = kChunk;
-  } else {
-    key0 = own * dm.S;
-    nk = (int)(pos - key0) + 1;
+  } else {  // local chunk l0 / S + slot - K, keys from max(l0, its start) to min(pos, its end)
+    const long long l0 = dm.lstart(pos), cc = l0 / dm.S + (slot - dm.K);
+    if (cc > pos / dm.S) {
+      if (lane == 0) part_l[po] = -INFINITY;
+      return;
+    }
+    key0 = cc * dm.S > l0 ? cc * dm.S : l0;
+    nk = (int)(min(pos, cc * dm.S + dm.S - 1) - key0) + 1;
   }
   if (BF16) {
     SlotRegs<D> rg;
@@ -329,8 +354,8 @@ __global__ __launch_bounds__(64) void k_decode_partial(Dims dm, const void* __re
 }
 
 // Combine kernel: one wavefront per row applies the inter-chunk softmax to the
-// slots in a fixed order (selected slots by their chunk score, the own slot by
-// its exact log-mass).
+// slots in a fixed order (selected slots by their chunk score, local slots by
+// their exact log-mass). Lane k holds slots k and 64 + k.
 template <bool BF16, int D>
 __global__ __launch_bounds__(64) void k_decode_combine(Dims dm, const float* __restrict__ score,
                                                        const float* __restrict__ part_o,
@@ -341,49 +366,49 @@ __global__ __launch_bounds__(64) void k_decode_combine(Dims dm, const float* __r
   constexpr int X = D / kWave;
   constexpr int KF = 16;  // slots whose partials are read in the first round trip
   const long long r = blockIdx.x;
-  const int lane = threadIdx.x, Ks = dm.K;
-  const long long pb = r * (Ks + 1);
-  const int kl = min(lane, Ks - 1);
+  const int lane = threadIdx.x, Ks = dm.K, NS = Ks + dm.nlocal_max();
+  const long long pb = r * NS;
   // every read is issued before any is used; rows of padding slots were not
   // written and are read only to keep the loads unconditional (weight 0)
-  const float l_own = part_l[pb + Ks];
-  const float pl = part_l[pb + kl];
-  const float sc = score[r * Ks + kl];
-  float po_own[X], pv[KF][X];
+  float lg[2], loc[2];
 #pragma unroll
-  for (int x = 0; x < X; ++x) po_own[x] = part_o[(pb + Ks) * D + lane + kWave * x];
+  for (int u = 0; u < 2; ++u) {
+    const int k = lane + 64 * u, kc = min(k, NS - 1);
+    const float pl = part_l[pb + kc];
+    const float sc = score[r * Ks + min(k, Ks - 1)];
+    lg[u] = k >= NS ? -INFINITY : k < Ks ? (pl != -INFINITY ? sc : -INFINITY) : pl;
+    loc[u] = k >= Ks && k < NS ? pl : -INFINITY;
+  }
+  float pv[KF][X];
 #pragma unroll
   for (int k = 0; k < KF; ++k)
 #pragma unroll
-    for (int x = 0; x < X; ++x) pv[k][x] = part_o[(pb + min(k, Ks)) * D + lane + kWave * x];
-  const float lg = (lane < Ks && pl != -INFINITY) ? sc : -INFINITY;
-  const float mx = fmaxf(wave_max(lg), l_own);
-  const float Lambda = mx + logf(wave_sum(lane < Ks ? expf(lg - mx) : 0.0f) + expf(l_own - mx));
-  const float a = lane < Ks ? expf(lg - Lambda) : 0.0f;
-  const float a_own = expf(l_own - Lambda);
+    for (int x = 0; x < X; ++x) pv[k][x] = part_o[(pb + min(k, NS - 1)) * D + lane + kWave * x];
+  const float ml = wave_max(fmaxf(loc[0], loc[1]));
+  const float l_own = ml + logf(wave_sum(expf(loc[0] - ml) + expf(loc[1] - ml)));
+  const float mx = wave_max(fmaxf(lg[0], lg[1]));
+  const float Lambda = mx + logf(wave_sum(expf(lg[0] - mx) + expf(lg[1] - mx)));
+  const float a0 = expf(lg[0] - Lambda), a1 = expf(lg[1] - Lambda);
   float acc[X];
 #pragma unroll
   for (int x = 0; x < X; ++x) acc[x] = 0.0f;
 #pragma unroll
   for (int k = 0; k < KF; ++k) {
-    const float ak = k < Ks ? lane_bcast(a, k) : 0.0f;
+    const float ak = k < NS ? lane_bcast(a0, k) : 0.0f;
     if (ak != 0.0f) {  // wave-uniform; padding and absent slots are skipped
 #pragma unroll
       for (int x = 0; x < X; ++x) acc[x] = fmaf(ak, pv[k][x], acc[x]);
     }
   }
-  for (int k = KF; k < Ks; ++k) {  // K > 16
-    const float ak = lane_bcast(a, k);
+  for (int k = KF; k < NS; ++k) {
+    const float ak = k < 64 ? lane_bcast(a0, k) : lane_bcast(a1, k - 64);
     if (ak != 0.0f) {
 #pragma unroll
       for (int x = 0; x < X; ++x) acc[x] = fmaf(ak, part_o[(pb + k) * D + lane + kWave * x], acc[x]);
     }
   }
 #pragma unroll
-  for (int x = 0; x < X; ++x) {
-    acc[x] = fmaf(a_own, po_own[x], acc[x]);
-    store_elem<BF16>(O, r * D + lane + kWave * x, acc[x]);
-  }
+  for (int x = 0; x < X; ++x) store_elem<BF16>(O, r * D + lane + kWave * x, acc[x]);
   if (lane == 0) {
     if (lse_own) lse_own[r] = l_own;
     if (lse_tot) lse_tot[r] = Lambda;
@@ -394,7 +419,7 @@ bool use_decode(const Dims& dm) { return dm.Tq < 64; }
 
 size_t decode_ws_bytes(const Dims& dm) {
   const size_t rows = (size_t)dm.B * dm.Tq * dm.H;
-  const size_t n = rows * (dm.K + 1);
+  const size_t n = rows * (dm.K + dm.nlocal_max());
   return ((n * dm.d * sizeof(float) + 255) & ~(size_t)255) + n * sizeof(float);
 }
 
@@ -403,11 +428,12 @@ hipError_t launch_decode(const Dims& dm, const void* Q, const void* K, const voi
                          const int32_t* idx, const float* score, void* O, float* lse_own,
                          float* lse_tot, void* ws, hipStream_t st) {
   const long long rows = (long long)dm.B * dm.Tq * dm.H;
-  const size_t n = (size_t)rows * (dm.K + 1);
+  const size_t n = (size_t)rows * (dm.K + dm.nlocal_max());
   float* part_o = reinterpret_cast<float*>(ws);
   float* part_l = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
                                            ((n * D * sizeof(float) + 255) & ~(size_t)255));
-  hipLaunchKernelGGL((k_decode_partial<BF16, D>), dim3(dm.K + 1, rows), dim3(64), 0, st, dm, Q, K,
+  hipLaunchKernelGGL((k_decode_partial<BF16, D>), dim3(dm.K + dm.nlocal_max(), rows), dim3(64), 0,
+                     st, dm, Q, K,
                      V, idx, part_o, part_l);
   hipLaunchKernelGGL((k_decode_combine<BF16, D>), dim3(rows), dim3(64), 0, st, dm, score, part_o,
                      part_l, O, lse_own, lse_tot);

@@ -13,6 +13,12 @@
 //    LDS staging and no workgroup barrier in the main loop) and runs every tile
 //    of the chunk: S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys on M, rows on N),
 //    a column softmax, O^T = V^T P^T.
+//  * The local branch is the own chunk (one causal tile per row, normalised in
+//    place) or, with a sliding window of W keys, the W/S + 1 chunks the window
+//    touches: a first pass over (local chunk, 16-row tile) items records each
+//    row's per-chunk maximum and sum, which give the window's log-mass; after
+//    Lambda is known a second pass adds exp(s_j - Lambda) v_j of every window
+//    key into the row's accumulator.
 //  * Contributions are added into the LDS row accumulators with integer atomics
 //    in a fixed-point format scaled from max|V| over the workgroup's chunks.
 //    Integer addition is associative, so the result does not depend on which
@@ -256,6 +262,76 @@ __device__ __forceinline__ void tile_ref(const Frag<D>& f, const uint4* qv, floa
   *z = zz[0];
 }
 
+// Sliding-window pass 1: column max (log2 domain, 0 for an empty column) and sum
+// of 2^(s scale2 - m2) over the keys klo <= j < khi of the tile's chunk.
+template <int D>
+__device__ __forceinline__ void tile_stats(const Frag<D>& f, const uint4* qv, int klo, int khi,
+                                           float scale2, float* m2, float* z) {
+  const int g = (threadIdx.x & 63) >> 4;
+  floatx4 s[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.k[kb * (D / 32) + ds]),
+                                                      as_bf16x8(qv[ds]), s[kb], 0, 0, 0);
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * kb + 4 * g + r;
+      if (j < klo || j >= khi) s[kb][r] = -INFINITY;
+      m = fmaxf(m, s[kb][r]);
+    }
+  m = xmax_16_32(m);
+  if (m == -INFINITY) m = 0.f;
+  const float nb = -scale2 * m;
+  float zz = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) zz += fast_exp2(fmaf(s[kb][r], scale2, nb));
+  *z = xsum_16_32(zz);
+  *m2 = m * scale2;
+}
+
+// Sliding-window pass 2: o = sum over the keys klo <= j < khi of
+// 2^(s_j scale2 - lam2) V_j (lam2 = Lambda log2 e, so every weight is at most 1).
+template <int D>
+__device__ __forceinline__ void tile_abs(const Frag<D>& f, const uint4* qv, int klo, int khi,
+                                         float scale2, float lam2, floatx4* o) {
+  const int g = (threadIdx.x & 63) >> 4;
+  floatx4 s[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.k[kb * (D / 32) + ds]),
+                                                      as_bf16x8(qv[ds]), s[kb], 0, 0, 0);
+  }
+  bf16x8 pf[2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * kb + 4 * g + r;
+      const float e = fast_exp2(fmaf(s[kb][r], scale2, -lam2));
+      pf[kb >> 1][(kb & 1) * 4 + r] = (__bf16)(j >= klo && j < khi ? e : 0.f);
+    }
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    o[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.v[db * 2 + ks]), pf[ks], o[db],
+                                                      0, 0, 0);
+  }
+}
+
 // ------------------------------------------------------------------ main kernel
 // Accumulator column of feature 16 db + 4 g + r (the O^T fragment element r of
 // block db held by lane group g). The four lane groups of one LDS atomic land 16
@@ -278,33 +354,39 @@ struct Smem {
   float* lam;     // Lambda times log2(e)
   float* pm;      // per (row, group of 8 slots): max score and sum of exp(score - max)
   float* pz;
-  int* nsel;      // per row: number of selected-chunk terms added to its accumulator
+  int* nsel;      // per row: number of terms added to its fixed-point accumulator
+  float2* lpart;  // sliding window: per (row, local chunk) max (log2 domain) and sum
   int* misc;
 };
 
+// LDS regions, each starting on a 16-byte boundary; nloc = local chunks per row
+// kept by the sliding-window pass (0 without a window).
+__host__ __device__ inline size_t up16(size_t x) { return (x + 15) & ~(size_t)15; }
+
 template <int D>
-__host__ __device__ inline size_t smem_bytes(int R, int K, int ncr) {
-  return (size_t)R * Cfg<D>::AP * 4 + (size_t)R * Cfg<D>::QP * 2 + (size_t)R * K * 8 +
-         4 * (size_t)(ncr + 1) * 4 + 3 * (size_t)R * 4 + 2 * (size_t)R * ((K + 7) / 8) * 4 +
-         32 * 4;
+__host__ __device__ inline size_t smem_bytes(int R, int K, int ncr, int nloc) {
+  return up16((size_t)R * Cfg<D>::AP * 4) + up16((size_t)R * Cfg<D>::QP * 2) +
+         2 * up16((size_t)R * K * 4) + 4 * up16((size_t)(ncr + 1) * 4) + 3 * up16((size_t)R * 4) +
+         2 * up16((size_t)R * ((K + 7) / 8) * 4) + up16((size_t)R * nloc * 8) + 32 * 4;
 }
 
 template <int D>
-__device__ __forceinline__ Smem carve(char* base, int R, int K, int ncr) {
+__device__ __forceinline__ Smem carve(char* base, int R, int K, int ncr, int nloc) {
   Smem s;
-  s.acc = reinterpret_cast<int*>(base); base += (size_t)R * Cfg<D>::AP * 4;
-  s.qs = reinterpret_cast<uint16_t*>(base); base += (size_t)R * Cfg<D>::QP * 2;
-  s.ent = reinterpret_cast<uint32_t*>(base); base += (size_t)R * K * 4;
-  s.lw = reinterpret_cast<float*>(base); base += (size_t)R * K * 4;
-  s.cnt = reinterpret_cast<int*>(base); base += (ncr + 1) * 4;
-  s.off = reinterpret_cast<int*>(base); base += (ncr + 1) * 4;
-  s.cur = reinterpret_cast<int*>(base); base += (ncr + 1) * 4;
-  s.nz = reinterpret_cast<int*>(base); base += (ncr + 1) * 4;
-  s.lown = reinterpret_cast<float*>(base); base += R * 4;
-  s.lam = reinterpret_cast<float*>(base); base += R * 4;
-  s.pm = reinterpret_cast<float*>(base); base += (size_t)R * ((K + 7) / 8) * 4;
-  s.pz = reinterpret_cast<float*>(base); base += (size_t)R * ((K + 7) / 8) * 4;
-  s.nsel = reinterpret_cast<int*>(base); base += R * 4;
+  s.acc = reinterpret_cast<int*>(base); base += up16((size_t)R * Cfg<D>::AP * 4);
+  s.qs = reinterpret_cast<uint16_t*>(base); base += up16((size_t)R * Cfg<D>::QP * 2);
+  s.ent = reinterpret_cast<uint32_t*>(base); base += up16((size_t)R * K * 4);
+  s.lw = reinterpret_cast<float*>(base); base += up16((size_t)R * K * 4);
+  s.cnt = reinterpret_cast<int*>(base); base += up16((ncr + 1) * 4);
+  s.off = reinterpret_cast<int*>(base); base += up16((ncr + 1) * 4);
+  s.cur = reinterpret_cast<int*>(base); base += up16((ncr + 1) * 4);
+  s.nz = reinterpret_cast<int*>(base); base += up16((ncr + 1) * 4);
+  s.lown = reinterpret_cast<float*>(base); base += up16(R * 4);
+  s.lam = reinterpret_cast<float*>(base); base += up16(R * 4);
+  s.pm = reinterpret_cast<float*>(base); base += up16((size_t)R * ((K + 7) / 8) * 4);
+  s.pz = reinterpret_cast<float*>(base); base += up16((size_t)R * ((K + 7) / 8) * 4);
+  s.nsel = reinterpret_cast<int*>(base); base += up16(R * 4);
+  s.lpart = reinterpret_cast<float2*>(base); base += up16((size_t)R * nloc * 8);
   s.misc = reinterpret_cast<int*>(base);
   return s;
 }
@@ -352,15 +434,17 @@ __device__ __forceinline__ void lds_q(uint4* qv, const uint16_t* qs, int rho, bo
                    : make_uint4(0, 0, 0, 0);
 }
 
-// Own-chunk work items are the (own chunk, 16-row tile) pairs in chunk order;
-// each wave takes a contiguous run of them so it mostly stays on one chunk.
+// Local-branch work items are the (local chunk, 16-row tile) pairs in chunk
+// order; the rows of chunk oc are the positions oc S .. oc S + span - 1 of the
+// block (span = S for the own chunk, S + W - 1 for a window of W keys). Each
+// wave takes a contiguous run of items so it mostly stays on one chunk.
 // Returns false when `item` is past the last one.
-__device__ __forceinline__ bool own_item(int item, long long p0, int S, int G, int Rv,
+__device__ __forceinline__ bool own_item(int item, long long p0, int S, int span, int G, int Rv,
                                          int own_first, int own_last, int* oc_out, int* ra_out,
                                          int* rb_out, int* tl_out) {
   for (int oc = own_first; oc <= own_last; ++oc) {
     const int ra = (int)max(0LL, (long long)oc * S - p0) * G;
-    const int rb = (int)min((long long)Rv, ((long long)oc * S + S - p0) * G);
+    const int rb = (int)min((long long)Rv, ((long long)oc * S + span - p0) * G);
     const int ntile = (rb - ra + 15) / 16;
     if (item < ntile) {
       *oc_out = oc, *ra_out = ra, *rb_out = rb, *tl_out = item;
@@ -371,12 +455,12 @@ __device__ __forceinline__ bool own_item(int item, long long p0, int S, int G, i
   return false;
 }
 
-__device__ __forceinline__ int own_item_count(long long p0, int S, int G, int Rv, int own_first,
-                                              int own_last) {
+__device__ __forceinline__ int own_item_count(long long p0, int S, int span, int G, int Rv,
+                                              int own_first, int own_last) {
   int n = 0;
   for (int oc = own_first; oc <= own_last; ++oc) {
     const int ra = (int)max(0LL, (long long)oc * S - p0) * G;
-    const int rb = (int)min((long long)Rv, ((long long)oc * S + S - p0) * G);
+    const int rb = (int)min((long long)Rv, ((long long)oc * S + span - p0) * G);
     n += (rb - ra + 15) / 16;
   }
   return n;
@@ -393,12 +477,10 @@ constexpr float kMagicF = 12582912.0f;  // 1.5 * 2^23
 constexpr uint32_t kMagic = 0x4B400000u;
 
 template <int D>
-__device__ __forceinline__ void accumulate_tile(const Smem& sm, const floatx4* o, float z,
-                                                uint32_t en, float lw2, float lam2,
-                                                float fx_scale) {
+__device__ __forceinline__ void accumulate_fw(const Smem& sm, const floatx4* o, int rho,
+                                              float fw) {
   const int gl = (threadIdx.x & 63) >> 4;
-  const float fw = fast_exp2(lw2 - lam2) * __builtin_amdgcn_rcpf(z) * fx_scale;
-  int* ar = sm.acc + (int)(en & 0xFFFFu) * Cfg<D>::AP;
+  int* ar = sm.acc + rho * Cfg<D>::AP;
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
 #pragma unroll
@@ -408,6 +490,14 @@ __device__ __forceinline__ void accumulate_tile(const Smem& sm, const floatx4* o
       atomicAdd(reinterpret_cast<unsigned long long*>(ar + acc_col(db, gl, q)),
                 (unsigned long long)((hi << 32) | lo));
     }
+}
+
+template <int D>
+__device__ __forceinline__ void accumulate_tile(const Smem& sm, const floatx4* o, float z,
+                                                uint32_t en, float lw2, float lam2,
+                                                float fx_scale) {
+  const float fw = fast_exp2(lw2 - lam2) * __builtin_amdgcn_rcpf(z) * fx_scale;
+  accumulate_fw<D>(sm, o, (int)(en & 0xFFFFu), fw);
 }
 
 // Weight sums of the fast path that are safe to use (see tile_ref).
@@ -488,7 +578,7 @@ __device__ __forceinline__ void run_chunk(const Frag<D>& f, const Smem& sm, int 
   }
 }
 
-template <int D>
+template <int D, bool SWA>
 __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     Dims dm, int R, int Rq, int ncr_cap, int nqb, int nct, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Vt,
@@ -509,8 +599,12 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   const int Rv = nq * G;
   const long long p0 = dm.q_pos0 + qi0;
   const int own_first = (int)(p0 / S), own_last = (int)((p0 + nq - 1) / S);
-  const int ncr = own_last;  // selectable chunks: [0, own_last)
-  Smem sm = carve<D>(smem_raw, R, Ksel, ncr_cap);
+  const int ncr = own_last;  // selectable chunks lie in [0, own_last)
+  // local chunks of the block and the rows each one serves (see own_item)
+  const int span = SWA ? S + dm.window - 1 : S;
+  const int loc_first = SWA ? (int)(dm.lstart(p0) / S) : own_first;
+  const int nloc = SWA ? dm.nlocal_max() : 0;
+  Smem sm = carve<D>(smem_raw, R, Ksel, ncr_cap, nloc);
   const long long kv_stride = (long long)dm.Hkv * D;
   const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
   const long long vt_base = ((long long)b * dm.Hkv + g) * nct * (long long)D * kChunk;
@@ -523,13 +617,13 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
 
   // own-chunk items of this wave; for d = 64 the first fragment is requested now
   // and lands during the set-up
-  const int n_own = own_item_count(p0, S, G, Rv, own_first, own_last);
+  const int n_own = own_item_count(p0, S, span, G, Rv, loc_first, own_last);
   const int per_wave = (n_own + kWaves - 1) / kWaves;
   const int item0 = w * per_wave, item_end = min(n_own, item0 + per_wave);
   Frag<D> f, f2;
   int o_oc = 0, o_ra = 0, o_rb = 0, o_tl = 0;
-  bool o_have = item0 < item_end &&
-                own_item(item0, p0, S, G, Rv, own_first, own_last, &o_oc, &o_ra, &o_rb, &o_tl);
+  bool o_have = item0 < item_end && own_item(item0, p0, S, span, G, Rv, loc_first, own_last,
+                                             &o_oc, &o_ra, &o_rb, &o_tl);
   if (C::PREFETCH && o_have)
     load_frag<D>(f, K, Vt, kv_base, kv_stride, o_oc, vt_base + (long long)o_oc * D * kChunk, dm.Tkv);
 
@@ -537,7 +631,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   const int kgroups = (Ksel + 7) / 8;  // Rv * kgroups <= kThreads (see plan)
   const bool has_item = t < Rv * kgroups;
   const int it_rho = t / kgroups, it_k0 = (t % kgroups) * 8;
-  const int it_own = (int)((p0 + it_rho / G) / S);
+  const int it_own = dm.ncand(p0 + it_rho / G);  // the row's candidates: chunks below this
   int cs[8];
   float ss[8];
   {
@@ -607,7 +701,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   // max|V| over every chunk this workgroup reads
   float vm = 0.f;
   for (int c = t; c <= own_last; c += kThreads) {
-    const bool used = c >= own_first || sm.cnt[c] > 0;
+    const bool used = c >= loc_first || sm.cnt[c] > 0;
     if (c < ncr && sm.cnt[c] > 0) sm.cur[sm.nz[c]] = c;
     if (used) vm = fmaxf(vm, c == t ? vpre : vmx[c]);
   }
@@ -629,8 +723,33 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   // product of the PV step finite
   const bool fast = vmax_wg < 0x1p50f;
 
+  // ---- sliding window, pass 1: per (row, local chunk) maximum and sum
+  if constexpr (SWA) {
+    int fc = C::PREFETCH && o_have ? o_oc : -1;  // chunk whose fragments f holds
+    for (int item = item0; o_have;) {
+      if (o_oc != fc) {
+        load_frag<D>(f, K, Vt, kv_base, kv_stride, o_oc, vt_base + (long long)o_oc * D * kChunk,
+                     dm.Tkv);
+        fc = o_oc;
+      }
+      const int rho = o_ra + 16 * o_tl + col;
+      const bool valid = rho < o_rb;
+      const long long pos = p0 + (valid ? rho : o_ra) / G, cb = (long long)o_oc * S;
+      const long long l0 = dm.lstart(pos);
+      const int klo = valid ? (int)max(0LL, l0 - cb) : 0;
+      const int khi = valid ? (int)min((long long)S, pos - cb + 1) : 0;
+      uint4 qo[D / 32];
+      lds_q<D>(qo, sm.qs, rho, valid);
+      float m2, z;
+      tile_stats<D>(f, qo, klo, khi, scale2, &m2, &z);
+      if (valid && gl == 0) sm.lpart[rho * nloc + (o_oc - (int)(l0 / S))] = make_float2(m2, z);
+      ++item;
+      o_have = item < item_end && own_item(item, p0, S, span, G, Rv, loc_first, own_last, &o_oc,
+                                           &o_ra, &o_rb, &o_tl);
+    }
+  }
   // ---- own chunks: causal, normalised (float accumulators for now)
-  for (int item = item0; o_have; ) {
+  for (int item = item0; !SWA && o_have; ) {
     if (!C::PREFETCH)
       load_frag<D>(f, K, Vt, kv_base, kv_stride, o_oc, vt_base + (long long)o_oc * D * kChunk,
                    dm.Tkv);
@@ -653,21 +772,33 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     }
     const int prev = o_oc;
     ++item;
-    o_have = item < item_end &&
-             own_item(item, p0, S, G, Rv, own_first, own_last, &o_oc, &o_ra, &o_rb, &o_tl);
+    o_have = item < item_end && own_item(item, p0, S, span, G, Rv, loc_first, own_last, &o_oc,
+                                         &o_ra, &o_rb, &o_tl);
     if (C::PREFETCH && o_have && o_oc != prev)
       load_frag<D>(f, K, Vt, kv_base, kv_stride, o_oc, vt_base + (long long)o_oc * D * kChunk,
                    dm.Tkv);
   }
   // the first selected chunk's fragment is requested before the fusion set-up
-  if (C::PREFETCH && w < nnz)
+  if (!SWA && C::PREFETCH && w < nnz)
     load_frag<D>(f, K, Vt, kv_base, kv_stride, sm.cur[w],
                  vt_base + (long long)sm.cur[w] * D * kChunk, dm.Tkv);
   __syncthreads();
 
-  // ---- fusion normaliser per row from the own log-mass and the score partials
+  // ---- fusion normaliser per row from the local log-mass and the score partials
   for (int rho = t; rho < Rv; rho += kThreads) {
-    const float lo = sm.lown[rho];
+    float lo;
+    if constexpr (SWA) {  // the window's log-mass from its chunks' partials, in chunk order
+      const int nl = dm.nlocal(p0 + rho / G);
+      const float2* lp = sm.lpart + rho * nloc;
+      float m2 = -INFINITY;
+      for (int k = 0; k < nl; ++k) m2 = fmaxf(m2, lp[k].x);
+      float z = 0.f;
+      for (int k = 0; k < nl; ++k) z += lp[k].y * exp2f(lp[k].x - m2);
+      lo = (m2 + log2f(z)) * kLn2;
+      sm.nsel[rho] += nl;  // one term per local chunk in pass 2
+    } else {
+      lo = sm.lown[rho];
+    }
     float mx = lo;
     for (int kg = 0; kg < kgroups; ++kg) mx = fmaxf(mx, sm.pm[rho * kgroups + kg]);
     float z = expf(lo - mx);
@@ -688,11 +819,47 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   for (int x = t; x < Rv * (D / 2); x += kThreads) {
     const int rho = x / (D / 2), e = 2 * (x % (D / 2));
     int64_t* a = reinterpret_cast<int64_t*>(sm.acc + rho * C::AP + e);
-    const float2 v = *reinterpret_cast<const float2*>(a);
-    const float w = sm.lown[rho];
-    *a = (int64_t)(int)(v.y * w) * 4294967296LL + (int64_t)(int)(v.x * w);
+    if constexpr (SWA) {
+      *a = 0;
+    } else {
+      const float2 v = *reinterpret_cast<const float2*>(a);
+      const float w = sm.lown[rho];
+      *a = (int64_t)(int)(v.y * w) * 4294967296LL + (int64_t)(int)(v.x * w);
+    }
   }
   __syncthreads();
+
+  // ---- sliding window, pass 2: exp(s_j - Lambda) v_j of every window key
+  if constexpr (SWA) {
+    int oc = 0, ra = 0, rb = 0, tl = 0, fc = -1;
+    bool have = item0 < item_end &&
+                own_item(item0, p0, S, span, G, Rv, loc_first, own_last, &oc, &ra, &rb, &tl);
+    for (int item = item0; have;) {
+      if (oc != fc) {
+        load_frag<D>(f, K, Vt, kv_base, kv_stride, oc, vt_base + (long long)oc * D * kChunk,
+                     dm.Tkv);
+        fc = oc;
+      }
+      const int rho = ra + 16 * tl + col;
+      const bool valid = rho < rb;
+      const long long pos = p0 + (valid ? rho : ra) / G, cb = (long long)oc * S;
+      const long long l0 = dm.lstart(pos);
+      const int klo = valid ? (int)max(0LL, l0 - cb) : 0;
+      const int khi = valid ? (int)min((long long)S, pos - cb + 1) : 0;
+      const float lam2 = valid ? sm.lam[rho] : 0.f;
+      uint4 qo[D / 32];
+      lds_q<D>(qo, sm.qs, rho, valid);
+      floatx4 o[D / 16];
+      tile_abs<D>(f, qo, klo, khi, scale2, lam2, o);
+      if (valid) accumulate_fw<D>(sm, o, rho, fx_scale);
+      ++item;
+      have = item < item_end &&
+             own_item(item, p0, S, span, G, Rv, loc_first, own_last, &oc, &ra, &rb, &tl);
+    }
+    if (C::PREFETCH && w < nnz)
+      load_frag<D>(f, K, Vt, kv_base, kv_stride, sm.cur[w],
+                   vt_base + (long long)sm.cur[w] * D * kChunk, dm.Tkv);
+  }
 
   // ---- selected chunks: chunk u belongs to wavefront u mod 8; no barriers.
   if (!C::PREFETCH) {
@@ -752,10 +919,11 @@ bool plan(const Dims& dm, Plan* p) {
   if (rq < 1) return false;
   const long long last = dm.q_pos0 + dm.Tq - 1;
   const int ncr = (int)(last / dm.S) + 1;
+  const int nloc = dm.window > 0 ? dm.nlocal_max() : 0;
   const size_t limit = 160 * 1024;
-  while (rq > 1 && smem_bytes<D>(rq * dm.G, dm.K, ncr) > limit) rq -= max(1, rq / 8);
+  while (rq > 1 && smem_bytes<D>(rq * dm.G, dm.K, ncr, nloc) > limit) rq -= max(1, rq / 8);
   r = rq * dm.G;
-  const size_t b = smem_bytes<D>(r, dm.K, ncr);
+  const size_t b = smem_bytes<D>(r, dm.K, ncr, nloc);
   if (b > limit) return false;
   // the set-up gives each thread at most one (row, 8 selections) item and four
   // 16-byte pieces of the query rows
@@ -780,7 +948,7 @@ hipError_t launch_t(const Dims& dm, const Plan& p, const void* Q, const void* K,
                                          ((p.vt_bytes + 255) & ~(size_t)255));
   hipLaunchKernelGGL((k_vt_prep<D>), dim3(p.nct, dm.Hkv, dm.B), dim3(256), 0, st, dm, p.nct,
                      reinterpret_cast<const uint16_t*>(V), vt, vmax);
-  auto kfn = k_attend_mfma<D>;
+  auto kfn = dm.window > 0 ? k_attend_mfma<D, true> : k_attend_mfma<D, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.bytes);
   if (e != hipSuccess) return e;

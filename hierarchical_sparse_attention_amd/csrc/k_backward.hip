@@ -7,10 +7,11 @@
 // the forward by the chain rule. Per row (b,i,h) with dO_i, fused weight
 // alpha_c = exp(s^_c - Lambda), intra-chunk softmax P_cj, u_j = dO_i.v_j and
 // r_c = sum_j P_cj u_j:
-//   D_i     = sum_c alpha_c r_c + alpha_own r_own  (= dO_i . O_i)
+//   D_i     = sum_c alpha_c r_c + sum_local w_j u_j  (= dO_i . O_i)
 //   ds^_c   = alpha_c (r_c - D_i)                  (gradient of the chunk score)
 //   ds_cj   = alpha_c P_cj (u_j - r_c)             (selected chunk logits)
-//   ds_j    = w_j (u_j - D_i), w_j = exp(s_j - Lambda)  (own chunk, incl. its log-mass)
+//   ds_j    = w_j (u_j - D_i), w_j = exp(s_j - Lambda)  (local branch: the own
+//             chunk up to the row, or the last W keys; incl. its log-mass)
 //   dQ_i    = scale (sum ds k_j + sum_c ds^_c k'_c)
 //   dK_j   += scale ds q_i,  dV_j += (alpha P or w) dO_i
 //   dk'_c   = scale sum_i ds^_ic q_i,  db'_c = sum_i ds^_ic
@@ -23,7 +24,8 @@
 //                 commutes, so the bitmap does not depend on thread order);
 //                 k_sel_bitmap_lds builds blocks of it in LDS and writes them once
 //   k_bwd_kv   : one workgroup per (chunk, kv head, batch) -> dK, dV, dQl, walking
-//                the rows that selected the chunk in ascending order.
+//                the rows whose local branch covers the chunk's keys and the
+//                rows that selected the chunk in ascending order.
 #include "hils_internal.h"
 
 namespace hils {
@@ -81,7 +83,9 @@ __global__ __launch_bounds__(256) void k_bwd_rows(Dims dm, const void* __restric
   if (i >= dm.Tq) return;
   const int g = h / dm.G, Ksel = dm.K;
   const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
-  const long long pos = dm.q_pos0 + i, own = pos / dm.S;
+  const long long pos = dm.q_pos0 + i;
+  const int ncand = dm.ncand(pos);
+  const long long l0 = dm.lstart(pos), c_lo = l0 / dm.S, c_hi = pos / dm.S;
   const long long kv_stride = (long long)dm.Hkv * D;
   const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
   const float tau = dm.scale, Lambda = lse_tot[r];
@@ -108,19 +112,25 @@ __global__ __launch_bounds__(256) void k_bwd_rows(Dims dm, const void* __restric
     }
   };
 
-  // pass 1: per-chunk r, alpha and intra-chunk log-sum-exp
-  const int n_own = (int)(pos - own * dm.S) + 1;
-  float s, u;
-  logits(own * dm.S, n_own, s, u);
-  float m = wave_max(s);
-  const float l_own = m + logf(wave_sum(lane < n_own ? expf(s - m) : 0.0f));
-  const float r_own = wave_sum(lane < n_own ? expf(s - l_own) * u : 0.0f);
-  const float a_own = expf(l_own - Lambda);
-  float Dsum = a_own * r_own;
+  // the local branch's keys of chunk cc: logits, dO.v and whether the lane's key is one
+  auto local_logits = [&](long long cc, float& s, float& u) {
+    const int nk = (int)min((long long)kChunk, pos - cc * dm.S + 1);
+    logits(cc * dm.S, nk, s, u);
+    if (cc * dm.S + lane < l0) s = -INFINITY;
+    return nk;
+  };
+  // pass 1: the local branch's share of D (sum of exp(s_j - Lambda) u_j over its
+  // keys), per selected chunk r, alpha and intra-chunk log-sum-exp
+  float s, u, m;
+  float Dsum = 0.0f;
+  for (long long cc = c_lo; cc <= c_hi; ++cc) {
+    local_logits(cc, s, u);
+    Dsum += wave_sum(s > -INFINITY ? expf(s - Lambda) * u : 0.0f);
+  }
   float rk = 0.0f, ak = 0.0f, mk = 0.0f;  // lane k holds slot k's values
   for (int k = 0; k < Ksel; ++k) {
     const int c = idx[r * Ksel + k];
-    if (c < 0 || c >= own) continue;
+    if (c < 0 || c >= ncand) continue;
     logits((long long)c * dm.S, kChunk, s, u);
     m = wave_max(s);
     const float lz = m + logf(wave_sum(expf(s - m)));
@@ -143,11 +153,13 @@ __global__ __launch_bounds__(256) void k_bwd_rows(Dims dm, const void* __restric
       for (int x = 0; x < X; ++x) dq[x] = fmaf(tau * dj, load_elem<BF16>(K, off + lane + kWave * x), dq[x]);
     }
   };
-  logits(own * dm.S, n_own, s, u);
-  add_keys(own * dm.S, n_own, lane < n_own ? expf(s - Lambda) * (u - Dsum) : 0.0f);
+  for (long long cc = c_lo; cc <= c_hi; ++cc) {
+    const int nk = local_logits(cc, s, u);
+    add_keys(cc * dm.S, nk, s > -INFINITY ? expf(s - Lambda) * (u - Dsum) : 0.0f);
+  }
   for (int k = 0; k < Ksel; ++k) {
     const int c = idx[r * Ksel + k];
-    if (c < 0 || c >= own) {
+    if (c < 0 || c >= ncand) {
       if (lane == 0) ws_dsh[r * Ksel + k] = 0.0f;
       continue;
     }
@@ -189,7 +201,7 @@ __global__ void k_sel_bitmap(Dims dm, const int32_t* __restrict__ idx, uint32_t*
     const int h = (int)(r % dm.H);
     const int i = (int)((r / dm.H) % dm.Tq);
     const int b = (int)(r / ((long long)dm.H * dm.Tq));
-    if (c < 0 || c >= (dm.q_pos0 + i) / dm.S || c >= NC) continue;
+    if (c < 0 || c >= dm.ncand(dm.q_pos0 + i) || c >= NC) continue;
     atomicOr(&bm[(((long long)b * dm.H + h) * NC + c) * words + i / 32], 1u << (i % 32));
   }
 }
@@ -211,7 +223,7 @@ __global__ __launch_bounds__(256) void k_sel_bitmap_lds(Dims dm, const int32_t* 
     const int ii = x / dm.K, k = x % dm.K;
     const int i = i0 + ii;
     const int c = idx[(((long long)b * dm.Tq + i) * dm.H + h) * dm.K + k];
-    if (c < 0 || c >= (dm.q_pos0 + i) / dm.S || c >= NC) continue;
+    if (c < 0 || c >= dm.ncand(dm.q_pos0 + i) || c >= NC) continue;
     atomicOr(&lb[c * wpw + ii / 32], 1u << (ii % 32));
   }
   __syncthreads();
@@ -267,7 +279,8 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, const void* __restrict_
   for (int y = 0; y < kChunk * X; ++y) { dk[y] = 0.0f; dv[y] = 0.0f; }
 
   // one query row against this chunk's keys; ds and the value weight a per lane j
-  auto row_pass = [&](long long r, bool own_row, int nvalid, float sh) {
+  // (keys klo <= j < khi of the chunk take part)
+  auto row_pass = [&](long long r, bool own_row, int klo, int khi, float sh) {
     float qx[X], gx[X];
 #pragma unroll
     for (int x = 0; x < X; ++x) {
@@ -280,7 +293,7 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, const void* __restrict_
       sacc = fmaf(bcast(qx[e / kWave], e % kWave), kt[lane][e], sacc);
       uacc = fmaf(bcast(gx[e / kWave], e % kWave), vt[lane][e], uacc);
     }
-    const bool valid = lane < nvalid;
+    const bool valid = lane >= klo && lane < khi;
     const float s = valid ? sacc * tau : -INFINITY;
     const float Lambda = lse_tot[r];
     float ds, a;
@@ -313,10 +326,14 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, const void* __restrict_
 #pragma unroll
     for (int x = 0; x < X; ++x) dkb[x] = 0.0f;
     float dbs = 0.0f;
-    // rows of this chunk (own-chunk branch, causal)
-    for (int i = (int)key0 + w; i < (int)key0 + kChunk && i < dm.Tq; i += 4) {
+    // rows whose local branch covers keys of this chunk: its own rows, or with a
+    // window of W keys the positions key0 .. key0 + S + W - 2
+    const int span = dm.window > 0 ? kChunk + dm.window - 1 : kChunk;
+    for (int i = (int)key0 + w; i < (int)key0 + span && i < dm.Tq; i += 4) {
       const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
-      row_pass(r, true, i - (int)key0 + 1, 0.0f);
+      const long long l0 = dm.lstart(dm.q_pos0 + i);
+      row_pass(r, true, (int)max(0LL, l0 - key0),
+               (int)min((long long)kChunk, dm.q_pos0 + i - key0 + 1), 0.0f);
     }
     // rows that selected this chunk, ascending, in segments of 64 bitmap words
     const uint32_t* bmw = bm + (((long long)b * dm.H + h) * NC + c) * words;
@@ -349,7 +366,7 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, const void* __restrict_
         if (hit == 0) continue;  // wave-uniform; cannot happen for a consistent bitmap
         const int slot = __ffsll((long long)hit) - 1;
         const float dsh = ws_dsh[r * Ksel + slot];
-        row_pass(r, false, kChunk, score[r * Ksel + slot]);
+        row_pass(r, false, 0, kChunk, score[r * Ksel + slot]);
 #pragma unroll
         for (int x = 0; x < X; ++x)
           dkb[x] = fmaf(tau * dsh, load_elem<BF16>(Qsc, r * D + lane + kWave * x), dkb[x]);

@@ -8,7 +8,8 @@
 // r_c = sum_j P_j u_j and D = sum_c alpha_c r_c + sum_own w_j u_j = dO.O:
 //   selected chunk: ds_j = alpha_c P_j (u_j - r_c), value weight alpha_c P_j,
 //                   ds^_c = alpha_c (r_c - D)
-//   own chunk:      ds_j = w_j (u_j - D), w_j = exp(s_j - Lambda)
+//   local branch:   ds_j = w_j (u_j - D), w_j = exp(s_j - Lambda) over its keys
+//                   (the own chunk up to the row, or the last W keys)
 //   dQ = scale (sum ds_j k_j + sum_c ds^_c k'_c),  dK_j += scale ds_j q,
 //   dV_j += weight dO,  dk'_c = scale sum_i ds^_ic q_i,  db'_c = sum_i ds^_ic,
 //   ds'_j = p'_j [dk'.(k_j - k'_c) + db' (L' - s'_j - b'_c)],
@@ -20,8 +21,10 @@
 //   k_sel_count, k_sel_scan, k_sel_fill: per (b, h, chunk) the rows that
 //                  selected the chunk (ascending) as records (position, alpha,
 //                  D, slot)
-//   k_bwd_kv_mfma: one workgroup per (chunk, kv head); the chunk's own rows and
-//                  the rows that selected it in 32-row tiles: S^T, U^T on MFMA,
+//   k_bwd_kv_mfma: one workgroup per (chunk, kv head); the rows whose local
+//                  branch covers keys of the chunk (its own 64 rows, or with a
+//                  window of W keys the next S + W - 1 positions) and the rows
+//                  that selected it, in 32-row tiles: S^T, U^T on MFMA,
 //                  weights and dS through LDS, dK += dS^T Q and dV += A^T dO on
 //                  MFMA, ds^ = alpha (r - D) into dk' and db', and each row's
 //                  dQ contribution K^T dS^T (+ ds^ k') on MFMA into the row's
@@ -101,7 +104,8 @@ __global__ __launch_bounds__(256) void k_bwd_rowd(long long rows, const uint16_t
 
 // dQ = scale * (sum over the row's slots of its dQ partials, fixed slot order):
 // slot k < K holds selected chunk idx[k] (written only for valid selections),
-// slot K the own chunk. Eight lanes per row, 16-byte loads issued together.
+// slots K .. K + NL - 1 the local branch's chunks (the first nlocal of them are
+// written). Eight lanes per row, 16-byte loads issued together.
 template <int KM, bool QCAL>
 __global__ __launch_bounds__(256) void k_dq_reduce(Dims dm, long long rows,
                                                    const int32_t* __restrict__ idx,
@@ -113,21 +117,22 @@ __global__ __launch_bounds__(256) void k_dq_reduce(Dims dm, long long rows,
   const long long r0 = (long long)blockIdx.x * 32 + threadIdx.x / 8;
   const long long r = min(r0, rows - 1);
   const int c8 = threadIdx.x % 8;
-  const int Ksel = dm.K, NC = dm.Tkv / dm.S;
+  const int Ksel = dm.K, NC = dm.Tkv / dm.S, NS = Ksel + dm.nlocal_max();
   const int pos = (int)((r / dm.H) % dm.Tq);
-  const int own = (int)((dm.q_pos0 + pos) / dm.S);
-  const uint16_t* pr = part + r * (long long)(Ksel + 1) * D + c8 * 8;
+  const int own = dm.ncand(dm.q_pos0 + pos);           // candidates: chunks below this
+  const int nloc = dm.nlocal(dm.q_pos0 + pos);         // written local slots
+  const uint16_t* pr = part + r * (long long)NS * D + c8 * 8;
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  for (int k0 = 0; k0 <= Ksel; k0 += KM) {
+  for (int k0 = 0; k0 < NS; k0 += KM) {
     uint4 v[KM];
     bool ok[KM];
 #pragma unroll
     for (int q = 0; q < KM; ++q) {
-      const int k = min(k0 + q, Ksel);
-      const int c = k < Ksel ? idx[r * Ksel + k] : own;
-      ok[q] = k0 + q <= Ksel && (k == Ksel || (c >= 0 && c < own && c < NC));
+      const int k = min(k0 + q, NS - 1);
+      const int c = k < Ksel ? idx[r * Ksel + k] : -1;
+      ok[q] = k0 + q < NS && (k < Ksel ? (c >= 0 && c < own && c < NC) : k - Ksel < nloc);
       v[q] = *reinterpret_cast<const uint4*>(pr + (long long)k * D);
     }
 #pragma unroll
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(256) void k_sel_count(Dims dm, int nblk, const int3
   for (int x = threadIdx.x; x < ni * dm.K; x += blockDim.x) {
     const int i = i0 + x / dm.K, k = x % dm.K;
     const int c = idx[(((long long)b * dm.Tq + i) * dm.H + h) * dm.K + k];
-    if (c >= 0 && c < (int)((dm.q_pos0 + i) / dm.S) && c < NC) atomicAdd(&lcnt[c], 1);
+    if (c >= 0 && c < dm.ncand(dm.q_pos0 + i) && c < NC) atomicAdd(&lcnt[c], 1);
   }
   __syncthreads();
   int* out = cnt + ((long long)b * dm.H + h) * NC * nblk;
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
   for (int x = threadIdx.x; x < ni * dm.K; x += blockDim.x) {
     const int ii = x / dm.K, k = x % dm.K, i = i0 + ii;
     const int c = idx[(((long long)b * dm.Tq + i) * dm.H + h) * dm.K + k];
-    if (c >= 0 && c < (int)((dm.q_pos0 + i) / dm.S) && c < NC)
+    if (c >= 0 && c < dm.ncand(dm.q_pos0 + i) && c < NC)
       atomicOr(&lb[c * W + ii / 32], 1u << (ii % 32));
   }
   __syncthreads();
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
     const int ii = x / dm.K, k = x % dm.K, i = i0 + ii;
     const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
     const int c = idx[r * dm.K + k];
-    if (c < 0 || c >= (int)((dm.q_pos0 + i) / dm.S) || c >= NC) continue;
+    if (c < 0 || c >= dm.ncand(dm.q_pos0 + i) || c >= NC) continue;
     const int wd = ii / 32;
     int rank = __popc(lb[c * W + wd] & ((1u << (ii % 32)) - 1u));
     for (int ww = 0; ww < wd; ++ww) rank += __popc(lb[c * W + ww]);
@@ -366,9 +371,10 @@ struct KSmem {
   KWave wv[kKWaves];
   uint16_t kc[kChunk][TP];  // the chunk's keys
   int rows[kListMax];       // list segment: position of the row
-  float aux[kListMax];      // own rows: D; selecting rows: alpha
-  float dvl[kListMax];      // own rows: Lambda; selecting rows: D
-  int slotv[kListMax];      // dQ partial slot: selection slot, or K for own rows
+  float aux[kListMax];      // local rows: D; selecting rows: alpha
+  float dvl[kListMax];      // local rows: Lambda; selecting rows: D
+  int slotv[kListMax];      // dQ partial slot: selection slot, or K + local chunk
+                            // index for local rows; -1 for padding entries
   float dkb[kKWaves][D];    // per-wave dk' partials, then the total
   float dql[kKWaves][D];
   float dbw[kKWaves];
@@ -456,8 +462,8 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
       }
       T.aux[hf] = v ? sm.aux[e] : 0.f;
       T.dvr[hf] = sm.dvl[e];
-      T.rpos[hf] = v ? pos : -1;
       T.slot[hf] = sm.slotv[e];
+      T.rpos[hf] = v && T.slot[hf] >= 0 ? pos : -1;
     }
     return T;
   };
@@ -496,14 +502,16 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
       floatx4 a[4], d[4];
       float dsh = 0.f;
       if (own_rows) {
-        // w_j = exp(s_j - Lambda) over keys up to the row's position
+        // w_j = exp(s_j - Lambda) over the row's local keys lstart .. position
         const float lam2 = T.dvr[hf] * kLog2e, Dr = T.aux[hf];
+        const int klo = (int)dm.lstart(max(T.rpos[hf], 0));
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int kp = (int)key0 + 16 * kb + 4 * gl + r;
-            const float wj = kp <= T.rpos[hf] ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale2, -lam2)) : 0.f;
+            const float wj = kp <= T.rpos[hf] && kp >= klo
+                                 ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale2, -lam2)) : 0.f;
             a[kb][r] = wj;
             d[kb][r] = wj * (u[kb][r] - Dr);
           }
@@ -553,7 +561,8 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
       // selecting row), to the row's partial slot (lane: features 16 db + 4 gl + r)
       const uint4 pf[2] = {make_uint4(dpk[0].x, dpk[0].y, dpk[1].x, dpk[1].y),
                            make_uint4(dpk[2].x, dpk[2].y, dpk[3].x, dpk[3].y)};
-      const long long prow = (row_base + (long long)max(T.rpos[hf], 0) * dm.H) * (dm.K + 1) + T.slot[hf];
+      const long long prow = (row_base + (long long)max(T.rpos[hf], 0) * dm.H) *
+                                 (dm.K + dm.nlocal_max()) + max(T.slot[hf], 0);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         floatx4 dq = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -615,20 +624,26 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     const long long sidx = ((long long)b * dm.NCcap + c) * dm.H + h;
     const int LN = llen[bh * NC + c];
     const long long lsrc = bh * (long long)dm.Tq * dm.K + lstart[bh * NC + c];
-    constexpr int kSeg = kListMax - kChunk;
+    // local rows: positions key0 .. key0 + span - 1 (span = S, or S + W - 1 with a
+    // window), padded to whole tiles with entries of slot -1
+    const int nown = (int)min((long long)(dm.window > 0 ? kChunk + dm.window - 1 : kChunk),
+                              (long long)dm.Tq - key0);
+    const int nown_pad = (nown + kTileRows - 1) / kTileRows * kTileRows;
+    const int kSeg = kListMax - nown_pad;  // > 0: the plan bounds the window
     for (int s0 = 0;; s0 += kSeg) {
-      // list segment: the chunk's own rows first (first segment only), then
+      // list segment: the local rows first (first segment only), then
       // selecting rows s0 .. s0 + kSeg of the chunk's list
-      const int base = s0 == 0 ? kChunk : 0;
+      const int base = s0 == 0 ? nown_pad : 0;
       const int ns = min(kSeg, LN - s0);
       const int n = base + ns;
-      if (base > 0 && t < kChunk) {
-        const long long r = row_base + (key0 + t) * dm.H;
-        sm.rows[t] = (int)key0 + t;
-        sm.aux[t] = ws_D[r];
-        sm.dvl[t] = lse_tot[r];
-        sm.slotv[t] = dm.K;
-        sm.kbv[t] = ksum[sidx * D + t];
+      if (s0 == 0 && t < D) sm.kbv[t] = ksum[sidx * D + t];
+      for (int e = t; e < base; e += kKThreads) {
+        const long long pos = key0 + min(e, nown - 1);
+        const long long r = row_base + pos * dm.H;
+        sm.rows[e] = (int)pos;
+        sm.aux[e] = ws_D[r];
+        sm.dvl[e] = lse_tot[r];
+        sm.slotv[e] = e < nown ? dm.K + (c - (int)(dm.lstart(pos) / dm.S)) : -1;
       }
       for (int e = t; e < ns; e += kKThreads) {
         const int4 rec = srec[lsrc + s0 + e];
@@ -760,13 +775,15 @@ struct BPlan {
 
 bool bwd_plan(const Dims& dm, BPlan* p) {
   if (!dm.bf16 || dm.d != 64 || dm.Tq < 64 || dm.q_pos0 != 0 || dm.Tq != dm.Tkv) return false;
+  // the local rows of a chunk and at least one tile of selecting rows fit a list segment
+  if (dm.window > 16 * kChunk) return false;
   p->nct = dm.Tkv / dm.S;
   p->nblk = (dm.Tq + kLBlk - 1) / kLBlk;
   const size_t rows = (size_t)dm.B * dm.Tq * dm.H;
   p->cnt_bytes = (size_t)dm.B * dm.H * p->nct * p->nblk * sizeof(int);
   p->ls_bytes = (size_t)dm.B * dm.H * p->nct * sizeof(int);
   p->rec_bytes = rows * dm.K * sizeof(int4);
-  p->part_bytes = rows * (dm.K + 1) * D * sizeof(uint16_t);
+  p->part_bytes = rows * (dm.K + dm.nlocal_max()) * D * sizeof(uint16_t);
   p->fill_smem = (size_t)p->nct * (kLBlk / 32 + 1) * sizeof(int);
   return p->fill_smem <= 160 * 1024;
 }

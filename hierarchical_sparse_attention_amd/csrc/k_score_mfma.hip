@@ -152,8 +152,8 @@ __global__ __launch_bounds__(64) void k_score_mfma(Dims dm, int nc, const uint16
   const int h = L % dm.H, b = (L / dm.H) % dm.B, K = dm.K;
   const int i0 = (nqb - 1 - L / (dm.H * dm.B)) * 64;
   const int nrows = min(64, dm.Tq - i0);
-  const int my_n = lane < nrows ? (int)((dm.q_pos0 + i0 + lane) / dm.S) : 0;
-  const int nmax = (int)((dm.q_pos0 + i0 + nrows - 1) / dm.S);
+  const int my_n = lane < nrows ? dm.ncand(dm.q_pos0 + i0 + lane) : 0;
+  const int nmax = dm.ncand(dm.q_pos0 + i0 + nrows - 1);
 
   // A fragments: rows 16mb + c, features 32ds + 8g .. +8
   uint4 qa[4][D / 32];
@@ -276,12 +276,12 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
   const int h = gk * G + hh;
   const int i0 = (nqb - 1 - L / (dm.Hkv * dm.B)) * 64;
   const int npos = min(64, dm.Tq - i0);
-  const int nmax = (int)((dm.q_pos0 + i0 + npos - 1) / dm.S);
+  const int nmax = dm.ncand(dm.q_pos0 + i0 + npos - 1);
   const int words = (nmax + 31) / 32;
   // selecting lane: position sp = hh PS + lane of the block
   const int sp = hh * PS + min(lane, PS - 1);
   const bool sel_lane = lane < PS && sp < npos;
-  const int my_n = sel_lane ? (int)((dm.q_pos0 + i0 + sp) / dm.S) : 0;
+  const int my_n = sel_lane ? dm.ncand(dm.q_pos0 + i0 + sp) : 0;
 
   uint4 qa[4][D / 32];
 #pragma unroll
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(256) void k_score_split_mfma(Dims dm, const uint16_
   const int split = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, c = lane & 15, g = lane >> 4;
   const int h = r % dm.H, i = (r / dm.H) % dm.Tq, b = r / (dm.H * dm.Tq);
-  const int n = (int)((dm.q_pos0 + i) / dm.S);
+  const int n = dm.ncand(dm.q_pos0 + i);
   const int cbase = split * kSplitM;
   // every global read is issued up front and unconditionally (invalid chunks
   // read chunk 0 and are discarded), so they share one round trip
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_score_row_mfma(
   const int r = blockIdx.x, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, c = lane & 15, g = lane >> 4;
   const int h = r % dm.H, i = (r / dm.H) % dm.Tq, b = r / (dm.H * dm.Tq);
-  const int n = (int)((dm.q_pos0 + i) / dm.S);
+  const int n = dm.ncand(dm.q_pos0 + i);
   const int K = dm.K;
   uint4 qa[D / 32];
 #pragma unroll
@@ -627,14 +627,14 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_score_row_mfma(
 }  // namespace
 
 bool score_mfma_group_applies(const Dims& dm) {
-  const int nmax = (int)((dm.q_pos0 + dm.Tq - 1) / dm.S);
+  const int nmax = dm.ncand(dm.q_pos0 + dm.Tq - 1);
   return dm.bf16 && (dm.G == 2 || dm.G == 4) && group_mfma_smem(dm.G, nmax) <= 160 * 1024;
 }
 
 hipError_t launch_score_mfma_group(const Dims& dm, const void* Q, const float* ksum,
                                    const float* ent, int32_t* idx, float* score, void* ws,
                                    hipStream_t st) {
-  const int nc = max(1, (int)((dm.q_pos0 + dm.Tq - 1) / dm.S));
+  const int nc = max(1, dm.ncand(dm.q_pos0 + dm.Tq - 1));
   uint16_t* ks = reinterpret_cast<uint16_t*>(ws);
   const long long n8 = (long long)dm.B * nc * dm.H * (dm.d / 8);
   const int grid = (int)std::min<long long>((n8 + 255) / 256, 4096);
@@ -670,14 +670,14 @@ hipError_t launch_score_mfma_group(const Dims& dm, const void* Q, const float* k
 }
 
 size_t score_mfma_prefill_ws_bytes(const Dims& dm) {
-  const int nc = (int)((dm.q_pos0 + dm.Tq - 1) / dm.S);
+  const int nc = dm.ncand(dm.q_pos0 + dm.Tq - 1);
   return (size_t)dm.B * (size_t)(nc > 0 ? nc : 1) * dm.H * 2 * dm.d * sizeof(uint16_t);
 }
 
 hipError_t launch_score_mfma_prefill(const Dims& dm, const void* Q, const float* ksum,
                                      const float* ent, int32_t* idx, float* score, void* ws,
                                      hipStream_t st) {
-  const int nc = max(1, (int)((dm.q_pos0 + dm.Tq - 1) / dm.S));
+  const int nc = max(1, dm.ncand(dm.q_pos0 + dm.Tq - 1));
   uint16_t* ks = reinterpret_cast<uint16_t*>(ws);
   const long long n8 = (long long)dm.B * nc * dm.H * (dm.d / 8);
   const int grid = (int)std::min<long long>((n8 + 255) / 256, 4096);
@@ -720,7 +720,7 @@ bool score_row_mfma_try(const Dims& dm, const void* Q, const float* ksum, const 
   // worth it only with enough rows to spread over the chip: a single row's
   // summaries read by one compute unit are latency-bound
   const long long rows = (long long)dm.B * dm.Tq * dm.H;
-  const long long ncand = dm.Tq > 0 ? (dm.q_pos0 + dm.Tq - 1) / dm.S : 0;
+  const long long ncand = dm.Tq > 0 ? dm.ncand(dm.q_pos0 + dm.Tq - 1) : 0;
   if (!dm.bf16 || ncand > kRowCand || ncand < 1 || rows < 256 || rows > 65535) return false;
   if (dm.d == 64)
     hipLaunchKernelGGL((k_score_row_mfma<64>), dim3(rows), dim3(kRowWaves * 64), 0, st, dm,

@@ -47,8 +47,8 @@ __global__ __launch_bounds__(256) void k_score_rows(Dims dm, const void* __restr
   const int i = blockIdx.x * R + t;
   const bool valid = i < dm.Tq;
   const int last = min(dm.Tq, (int)(blockIdx.x + 1) * R) - 1;
-  const int n = valid ? (int)((dm.q_pos0 + i) / dm.S) : 0;
-  const int nmax = (int)((dm.q_pos0 + last) / dm.S);
+  const int n = valid ? dm.ncand(dm.q_pos0 + i) : 0;
+  const int nmax = dm.ncand(dm.q_pos0 + last);
 
   float q[D];
   if (valid) {
@@ -127,8 +127,8 @@ __global__ __launch_bounds__(256) void k_score_group(Dims dm, int cpb, const voi
   const bool valid = i < dm.Tq;
   const int h = g * G + hh;
   const int last = min(dm.Tq, (int)(blockIdx.x + 1) * P) - 1;
-  const int n = valid ? (int)((dm.q_pos0 + i) / dm.S) : 0;
-  const int nmax = (int)((dm.q_pos0 + last) / dm.S);
+  const int n = valid ? dm.ncand(dm.q_pos0 + i) : 0;
+  const int nmax = dm.ncand(dm.q_pos0 + last);
   float q[D];
   if (valid) {
     load_row<BF16, D>(Q, (((long long)b * dm.Tq + i) * dm.H + h) * D, q);
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kSplit) void k_score_split(Dims dm, const void* __r
   __shared__ float ss[kSplit];
   const int split = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
   const int h = r % dm.H, i = (r / dm.H) % dm.Tq, b = r / (dm.H * dm.Tq);
-  const int n = (int)((dm.q_pos0 + i) / dm.S);
+  const int n = dm.ncand(dm.q_pos0 + i);
   const int c = split * kSplit + t;
   for (int e = t; e < D; e += kSplit) qs[e] = load_elem<BF16>(Q, (long long)r * D + e);
   __syncthreads();
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(1024) void k_topk_merge(Dims dm, const float* __res
   __shared__ int sel_c[64];
   const int r = blockIdx.x;
   const int i = (r / dm.H) % dm.Tq;
-  const int n = (int)((dm.q_pos0 + i) / dm.S);
+  const int n = dm.ncand(dm.q_pos0 + i);
   topk_merge_row(dm, r, n, ws_s, ws_i, nsplit, kSplit, idx, score, es, ec, sel_s, sel_c);
 }
 
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(64) void k_topk_merge_wave(Dims dm, const float* __
   __shared__ int sel_c[64];
   const int r = blockIdx.x, lane = threadIdx.x, K = dm.K;
   const int i = (r / dm.H) % dm.Tq;
-  const int n = (int)((dm.q_pos0 + i) / dm.S);
+  const int n = dm.ncand(dm.q_pos0 + i);
   const int nv = lane < nsplit ? min(K, max(0, min(kSplit, n - lane * kSplit))) : 0;
   const long long base = ((long long)r * nsplit + min(lane, nsplit - 1)) * K;
   uint32_t lh[KM], ll[KM];
@@ -286,9 +286,20 @@ __global__ __launch_bounds__(64) void k_topk_merge_wave(Dims dm, const float* __
   }
 }
 
+// No row has a candidate (every query's local branch reaches back to key 0):
+// the selection is empty.
+__global__ __launch_bounds__(256) void k_sel_empty(long long n, int32_t* __restrict__ idx,
+                                                   float* __restrict__ score) {
+  for (long long x = (long long)blockIdx.x * 256 + threadIdx.x; x < n;
+       x += (long long)gridDim.x * 256) {
+    idx[x] = -1;
+    score[x] = -INFINITY;
+  }
+}
+
 int max_candidates(const Dims& dm) {
   if (dm.Tq <= 0) return 0;
-  return (int)((dm.q_pos0 + dm.Tq - 1) / dm.S);
+  return dm.ncand(dm.q_pos0 + dm.Tq - 1);
 }
 
 int split_count(const Dims& dm) { return (max_candidates(dm) + kSplit - 1) / kSplit; }
@@ -358,6 +369,7 @@ hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const floa
 }  // namespace
 
 size_t score_topk_ws_bytes(const Dims& dm) {
+  if (max_candidates(dm) == 0) return 0;
   if (dm.group_sel && score_mfma_group_applies(dm)) return score_mfma_prefill_ws_bytes(dm);
   if (dm.group_sel && dm.G > 1) return 0;
   if (!use_split(dm)) return dm.bf16 ? score_mfma_prefill_ws_bytes(dm) : 0;
@@ -368,6 +380,12 @@ size_t score_topk_ws_bytes(const Dims& dm) {
 hipError_t launch_score_topk(const Dims& dm, const void* Q, const float* ksum, const float* ent,
                              int32_t* idx, float* score, void* ws, hipStream_t st) {
   if ((long long)dm.B * dm.Tq * dm.H == 0) return hipSuccess;
+  if (max_candidates(dm) == 0) {
+    const long long n = (long long)dm.B * dm.Tq * dm.H * dm.K;
+    hipLaunchKernelGGL(k_sel_empty, dim3((unsigned)std::min<long long>((n + 255) / 256, 4096)),
+                       dim3(256), 0, st, n, idx, score);
+    return hipGetLastError();
+  }
   if (dm.bf16) {
     return dm.d == 64 ? launch_t<true, 64>(dm, Q, ksum, ent, idx, score, ws, st)
                       : launch_t<true, 128>(dm, Q, ksum, ent, idx, score, ws, st);

@@ -78,7 +78,11 @@ typedef struct {
   int32_t select_mode; /* hils_select of hils_score_topk; 0 for the other calls */
   int64_t q_pos0;   /* absolute position of query row 0; q_pos0 + Tq <= Tkv */
   float scale;      /* softmax scale; 0 => 1/sqrt(d) */
-  float reserved2;  /* must be 0 */
+  int32_t window;   /* local branch: 0 = the query's own chunk (keys from its start
+                       up to the query); W > 0 = a sliding window of the last W keys
+                       (note §5.2 main setting: 512), W a multiple of S, <= 32 S.
+                       The same value must be passed to every call of a forward
+                       and its backward. */
 } hils_dims;
 
 enum {
@@ -111,13 +115,15 @@ hils_status hils_summarize(const hils_dims* dims, const void* K, const void* Ql,
  * Q here is the query the scores use: with Q-Cal (note §5.4) pass the
  * calibrated scoring query q^ = q + W_up W_down h (formed by the caller), and
  * the token query q to hils_attend_fuse.
- * Row (b,i,h) at position p = q_pos0+i has candidates c < floor(p/S) (complete
- * chunks before its own chunk) with score
+ * Row (b,i,h) at position p = q_pos0+i has candidates c < floor(l_p/S), the
+ * complete chunks before its local branch, whose first key l_p is the start of
+ * its own chunk floor(p/S)*S (window 0) or max(0, p - W + 1) (window W > 0; a
+ * chunk the window cuts is not a candidate), with score
  *   s^_{i,c} = scale * Q[b,i,h] . ksum[b,c,h] + ent[b,c,h]   (float32).
  * The min(K, n_i) best candidates (score descending, equal scores to the
  * lower chunk id) are written to idx in ascending chunk id, padded with -1,
  * and their scores to score, padded with -inf. ksum/ent must hold every
- * chunk below floor((q_pos0+Tq-1)/S). With dims->select_mode ==
+ * candidate chunk of the last row. With dims->select_mode ==
  * HILS_SELECT_GROUP_MAX the ranking uses max over the kv group's query heads
  * of s^ (same order key); idx is then equal for the heads of a group and each
  * head's score holds its own s^ of the selected chunks.
@@ -130,9 +136,12 @@ hils_status hils_score_topk(const hils_dims* dims, const void* Q, const float* k
  * Intra-chunk attention and inter-chunk fusion (note §5.3 hierarchical
  * softmax; Tide Fig. 3). For row (b,i,h) at position p:
  *   each selected chunk c (idx >= 0): o_c = softmax_j(scale q.k_j) V over its S keys;
- *   own chunk floor(p/S), keys floor(p/S)*S .. p:  o_own and its log-mass l_own;
+ *   local branch, keys l_p .. p (l_p as in hils_score_topk: the own chunk's
+ *   start, or the sliding window's first key): o_own = softmax over those keys
+ *   and its log-mass l_own;
  *   Lambda = log(sum_c exp(score_c) + exp(l_own));
  *   O = sum_c exp(score_c - Lambda) o_c + exp(l_own - Lambda) o_own.
+ * Selected ids outside the row's candidates are ignored.
  * lse_own (l_own) and lse_tot (Lambda) may be NULL; hils_backward needs them.
  */
 hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K,
@@ -145,7 +154,7 @@ hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K
  * score enters the forward weights, so the loss gradient reaches the summary
  * key, the entropy bias and the landmark query; unselected chunks get none).
  * Given dO, writes (overwrites) dQ, dK, dV and dQl: the gradients of
- * sum(dO * O) through the inter-chunk softmax (scores and own log-mass), the
+ * sum(dO * O) through the inter-chunk softmax (scores and local log-mass), the
  * intra-chunk softmaxes, the scores (Q, ksum, ent) and the landmark softmax
  * (Ql, K). dK/dV sum over the query heads of each kv head. Inputs are the
  * forward's: Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot and its

@@ -58,10 +58,9 @@ def test_dims_validation(kw, status):
     assert st == status
 
 
-def test_reserved_field_and_select_mode():
-    d = base()
-    d.reserved2 = 1.0
-    assert ws_size(d, hsa.OP_SUMMARIZE)[0] == 1
+def test_window_field_and_select_mode():
+    for wnd, status in ((-64, 1), (32, 2), (96, 2), (64 * 33, 2), (64, 0), (512, 0), (2048, 0)):
+        assert ws_size(base(window=wnd), hsa.OP_ATTEND_FUSE)[0] == status, wnd
     d = base()
     d.select_mode = 2                                    # no such selection
     assert ws_size(d, hsa.OP_SCORE_TOPK)[0] == 1
