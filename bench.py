@@ -13,6 +13,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -113,15 +114,20 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_counts(w, idx_host):
-    """Per-step algorithmic work of each kernel (bytes that must move / flops)."""
+def algorithmic_counts(w, idx_host, window=0):
+    """Per-step algorithmic work of each kernel (bytes that must move / flops). The
+    local branch is the own chunk (window 0) or the last `window` keys."""
     B, T, H, Hkv, d, S, K = w.B, w.T, w.H, w.Hkv, w.d, w.S, w.K
     NC = T // S
     esz = 2  # bf16
+
+    def lstart(i):
+        return max(0, i - window + 1) if window > 0 else i - i % S
+
     sel_pairs = int((idx_host >= 0).sum())                 # (row, selected chunk) pairs
-    own_keys = B * H * sum(i % S + 1 for i in range(T))    # causal own-chunk key visits
+    own_keys = B * H * sum(i - lstart(i) + 1 for i in range(T))  # local-branch key visits
     key_visits = sel_pairs * S + own_keys
-    cand = B * H * sum(i // S for i in range(T))           # scored candidates
+    cand = B * H * sum(lstart(i) // S for i in range(T))   # scored candidates
     summ_bytes = B * T * Hkv * d * esz + B * NC * H * d * esz + B * NC * H * (d + 2) * 4
     score_flops = 2 * d * cand
     score_bytes = B * T * H * d * esz + B * NC * H * (d + 1) * 4 + B * T * H * K * 8
@@ -246,64 +252,78 @@ def main():
         td = {k: torch.from_numpy(xd[k]).to(dev, torch.bfloat16) for k in ("Q", "K", "V", "Ql")}
         del xd
         NCd = wd.T // wd.S
-        dk = torch.empty(1, NCd, wd.H, wd.d, device=dev)
-        de = torch.empty(1, NCd, wd.H, device=dev)
-        dl = torch.empty(1, NCd, wd.H, device=dev)
         p0 = wd.q_pos0
-        hsa.summarize(td["K"], td["Ql"], wd.S, 0, p0 // wd.S, Tkv=p0, ksum=dk, ent=de, lse_l=dl)
-        didx = torch.empty(1, 1, wd.H, wd.K, dtype=torch.int32, device=dev)
-        dsc = torch.empty(1, 1, wd.H, wd.K, device=dev)
-        dO = torch.empty(1, 1, wd.H, wd.d, dtype=torch.bfloat16, device=dev)
-        dlo = torch.empty(1, 1, wd.H, device=dev)
-        dlt = torch.empty(1, 1, wd.H, device=dev)
         nsteps = min(args.decode_steps, wd.rows_q)
 
-        def dstep(s):
-            p = p0 + s
-            if (p % wd.S) == 0 and p > p0:  # chunk p/S - 1 just completed
-                c = p // wd.S - 1
-                hsa.summarize(td["K"], td["Ql"], wd.S, c, c + 1, Tkv=p, ksum=dk, ent=de,
-                              lse_l=dl)
-            q = td["Q"][:, s:s + 1]
-            hsa.score_topk(q, dk, de, wd.K, wd.S, p, p + 1, Hkv=wd.Hkv, idx=didx, score=dsc)
-            hsa.attend_fuse(q, td["K"], td["V"], didx, dsc, wd.S, p, p + 1, O=dO, lse_own=dlo,
-                            lse_tot=dlt)
+        def decode_run(Kd, wnd):
+            """(eager us/step, HIP-graph us/step) of the decode sequence with top-Kd and
+            local branch `wnd` (0: own chunk)."""
+            dk = torch.empty(1, NCd, wd.H, wd.d, device=dev)
+            de = torch.empty(1, NCd, wd.H, device=dev)
+            dl = torch.empty(1, NCd, wd.H, device=dev)
+            hsa.summarize(td["K"], td["Ql"], wd.S, 0, p0 // wd.S, Tkv=p0, ksum=dk, ent=de,
+                          lse_l=dl)
+            didx = torch.empty(1, 1, wd.H, Kd, dtype=torch.int32, device=dev)
+            dsc = torch.empty(1, 1, wd.H, Kd, device=dev)
+            dO = torch.empty(1, 1, wd.H, wd.d, dtype=torch.bfloat16, device=dev)
+            dlo = torch.empty(1, 1, wd.H, device=dev)
+            dlt = torch.empty(1, 1, wd.H, device=dev)
 
-        for s in range(8):
-            dstep(s)
-        torch.cuda.synchronize()
-        # eager (one host call per kernel launch)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        for s in range(nsteps):
-            dstep(s)
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        extra["decode_us_per_token_eager"] = ev[0].elapsed_time(ev[1]) * 1e3 / nsteps
-        # HIP graph: the whole sequence of decode steps captured once and replayed
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graph, stream=cap):
-                for s in range(nsteps):
-                    dstep(s)
-        stream.wait_stream(cap)
-        graph.replay()
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        reps = 3
-        ev[0].record(stream)
-        for _ in range(reps):
+            def dstep(s):
+                p = p0 + s
+                if (p % wd.S) == 0 and p > p0:  # chunk p/S - 1 just completed
+                    c = p // wd.S - 1
+                    hsa.summarize(td["K"], td["Ql"], wd.S, c, c + 1, Tkv=p, ksum=dk, ent=de,
+                                  lse_l=dl)
+                q = td["Q"][:, s:s + 1]
+                hsa.score_topk(q, dk, de, Kd, wd.S, p, p + 1, Hkv=wd.Hkv, idx=didx, score=dsc,
+                               window=wnd)
+                hsa.attend_fuse(q, td["K"], td["V"], didx, dsc, wd.S, p, p + 1, O=dO,
+                                lse_own=dlo, lse_tot=dlt, window=wnd)
+
+            for s in range(8):
+                dstep(s)
+            torch.cuda.synchronize()
+            # eager (one host call per kernel launch)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for s in range(nsteps):
+                dstep(s)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            eager = ev[0].elapsed_time(ev[1]) * 1e3 / nsteps
+            # HIP graph: the whole sequence of decode steps captured once and replayed
+            graph = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(graph, stream=cap):
+                    for s in range(nsteps):
+                        dstep(s)
+            stream.wait_stream(cap)
             graph.replay()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        dec_us = ev[0].elapsed_time(ev[1]) * 1e3 / (nsteps * reps)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            reps = 3
+            ev[0].record(stream)
+            for _ in range(reps):
+                graph.replay()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            return eager, ev[0].elapsed_time(ev[1]) * 1e3 / (nsteps * reps)
+
+        eager_us, dec_us = decode_run(wd.K, 0)
         dec_bytes = (NCd * wd.H * (wd.d + 1) * 4 + wd.K * wd.S * wd.H * wd.d * 2 * 2
                      + 32 * wd.H * wd.d * 2 * 2)
+        extra["decode_us_per_token_eager"] = eager_us
         extra["decode_us_per_token"] = dec_us
         extra["decode_gbs_wallclock"] = dec_bytes / (dec_us * 1e-6) / 1e9
         extra["decode_steps"] = nsteps
+        # the pages' main setting: top-32 and a sliding window of 512 keys
+        eager_m, dec_m = decode_run(32, 512)
+        extra["decode_main_us_per_token"] = dec_m
+        extra["decode_main_us_per_token_eager"] = eager_m
+        extra["decode_main"] = "K=32, sliding window of 512 keys, same cache and steps"
 
     # ------------------------------------------- 7B-class GQA prefill, training step
     def ev_ms(fn, reps):
@@ -317,23 +337,32 @@ def main():
 
     if not args.no_extra_configs:
         # the 7B-class GQA prefill also with group-max selection (one chunk set per kv
-        # head); the training step also with a Q-Cal scoring query
-        for name, modes in (("prefill_7b_gqa", ("per_head", "group_max")),
-                            ("train_345m", ("per_head", "qcal"))):
-            wx = synth.workloads()[name]
-            log(f"generating {name} inputs")
-            xx = synth.make_inputs(wx)
-            keys = ("Q", "K", "V", "Ql") + (("dO",) if wx.need_dO else ())
+        # head); the 345M prefill and the training step in the pages' main setting
+        # (K = 32, a sliding window of 512 keys); the training step with a Q-Cal
+        # scoring query
+        groups = (
+            ("prefill_7b_gqa", (("prefill_7b_gqa", {}),
+                                ("prefill_7b_gqa_group_max", {"group": True}))),
+            ("prefill_345m", (("prefill_345m_main", {"K": 32, "window": 512}),)),
+            ("train_345m", (("train_345m", {}), ("train_345m_qcal", {"qcal": True}),
+                            ("train_345m_main", {"K": 32, "window": 512}))),
+        )
+        for wname, recs in groups:
+            w0 = synth.workloads()[wname]
+            log(f"generating {wname} inputs")
+            xx = synth.make_inputs(w0)
+            keys = ("Q", "K", "V", "Ql") + (("dO",) if w0.need_dO else ())
             tx = {k: torch.from_numpy(xx[k]).to(dev, torch.bfloat16) for k in keys}
-            if "qcal" in modes:
-                tx["Qs"] = torch.from_numpy(synth.scoring_query(wx, xx)).to(dev, torch.bfloat16)
+            if any(o.get("qcal") for _, o in recs):
+                tx["Qs"] = torch.from_numpy(synth.scoring_query(w0, xx)).to(dev, torch.bfloat16)
             del xx
-            for mode in modes:
-                group = mode == "group_max"
-                Qsx = tx["Qs"] if mode == "qcal" else None
+            for rname, opt in recs:
+                wx = dataclasses.replace(w0, K=opt.get("K", w0.K))
+                group, wnd = opt.get("group", False), opt.get("window", 0)
+                Qsx = tx["Qs"] if opt.get("qcal") else None
                 Qsel = tx["Q"] if Qsx is None else Qsx   # the query the chunk scores use
                 fw = hsa.forward(tx["Q"], tx["K"], tx["V"], tx["Ql"], wx.K, wx.S, group=group,
-                                 Qs=Qsx)
+                                 Qs=Qsx, window=wnd)
                 ksx, enx, llx, ix, scx = (fw[k] for k in ("ksum", "ent", "lse_l", "idx", "score"))
                 Ox, lox, ltx = fw["O"], fw["lse_own"], fw["lse_tot"]
                 calls = {
@@ -341,24 +370,26 @@ def main():
                                                        ent=enx, lse_l=llx),
                     "score_topk": lambda: hsa.score_topk(Qsel, ksx, enx, wx.K, wx.S, 0, wx.T,
                                                          Hkv=wx.Hkv, idx=ix, score=scx,
-                                                         group=group),
+                                                         group=group, window=wnd),
                     "attend_fuse": lambda: hsa.attend_fuse(tx["Q"], tx["K"], tx["V"], ix, scx,
-                                                           wx.S, O=Ox, lse_own=lox, lse_tot=ltx),
+                                                           wx.S, O=Ox, lse_own=lox, lse_tot=ltx,
+                                                           window=wnd),
                 }
                 if wx.need_dO:
                     calls["backward"] = lambda: hsa.backward(tx["Q"], tx["K"], tx["V"], tx["Ql"],
                                                              ksx, enx, llx, ix, scx, ltx, Ox,
-                                                             tx["dO"], wx.S, Qs=Qsx)
+                                                             tx["dO"], wx.S, Qs=Qsx, window=wnd)
                 for fn in calls.values():
                     fn()
                 torch.cuda.synchronize()
                 km = {k: ev_ms(fn, 5) for k, fn in calls.items()}
-                cx = algorithmic_counts(wx, ix.cpu().numpy())
+                cx = algorithmic_counts(wx, ix.cpu().numpy(), wnd)
                 fwd_ms = km["summarize"] + km["score_topk"] + km["attend_fuse"]
                 rec = {"kernels_ms": km, "forward_ms": fwd_ms,
                        "attend_tflops": cx["attend_fuse"]["flops"] / (km["attend_fuse"] * 1e-3) / 1e12,
                        "score_topk_tflops": cx["score_topk"]["flops"] / (km["score_topk"] * 1e-3) / 1e12,
-                       "summarize_gbs": cx["summarize"]["bytes"] / (km["summarize"] * 1e-3) / 1e9}
+                       "summarize_gbs": cx["summarize"]["bytes"] / (km["summarize"] * 1e-3) / 1e9,
+                       "K": wx.K}
                 if wx.need_dO:
                     bwd_flops = 10 * wx.d * cx["key_visits"]
                     rec["backward_tflops"] = bwd_flops / (km["backward"] * 1e-3) / 1e12
@@ -369,7 +400,9 @@ def main():
                     rec["selection"] = "group max over the 4 query heads of each kv head"
                 if Qsx is not None:
                     rec["scoring_query"] = "Q-Cal: separate scoring query, dQs returned apart"
-                extra[name + ("" if mode == "per_head" else "_" + mode)] = rec
+                if wnd:
+                    rec["local_branch"] = f"sliding window of {wnd} keys"
+                extra[rname] = rec
                 del fw, calls
             del tx
             torch.cuda.empty_cache()

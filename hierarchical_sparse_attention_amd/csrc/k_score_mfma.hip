@@ -650,21 +650,24 @@ hipError_t launch_score_mfma_group(const Dims& dm, const void* Q, const float* k
     hipLaunchKernelGGL((k_score_mfma_group<DD, KMM, GG>), g3, dim3(64 * GG), smem, st, dm, nc, \
                        Qh, ks, ent, idx, score);                                               \
   } while (0)
+#define HILS_GRP_K(DD)                                                                       \
+  do {                                                                                         \
+    if (dm.K <= 16) {                                                                          \
+      if (dm.G == 2) HILS_GRP(DD, 16, 2); else HILS_GRP(DD, 16, 4);                             \
+    } else if (dm.K <= 32) {                                                                   \
+      if (dm.G == 2) HILS_GRP(DD, 32, 2); else HILS_GRP(DD, 32, 4);                             \
+    } else {                                                                                   \
+      if (dm.G == 2) HILS_GRP(DD, 64, 2); else HILS_GRP(DD, 64, 4);                             \
+    }                                                                                          \
+  } while (0)
   if (dm.d == 64) {
     hipLaunchKernelGGL((k_ksplit<64>), dim3(grid), dim3(256), 0, st, dm, nc, ksum, ks);
-    if (dm.K <= 16) {
-      if (dm.G == 2) HILS_GRP(64, 16, 2); else HILS_GRP(64, 16, 4);
-    } else {
-      if (dm.G == 2) HILS_GRP(64, 64, 2); else HILS_GRP(64, 64, 4);
-    }
+    HILS_GRP_K(64);
   } else {
     hipLaunchKernelGGL((k_ksplit<128>), dim3(grid), dim3(256), 0, st, dm, nc, ksum, ks);
-    if (dm.K <= 16) {
-      if (dm.G == 2) HILS_GRP(128, 16, 2); else HILS_GRP(128, 16, 4);
-    } else {
-      if (dm.G == 2) HILS_GRP(128, 64, 2); else HILS_GRP(128, 64, 4);
-    }
+    HILS_GRP_K(128);
   }
+#undef HILS_GRP_K
 #undef HILS_GRP
   return hipGetLastError();
 }
@@ -682,23 +685,28 @@ hipError_t launch_score_mfma_prefill(const Dims& dm, const void* Q, const float*
   const long long n8 = (long long)dm.B * nc * dm.H * (dm.d / 8);
   const int grid = (int)std::min<long long>((n8 + 255) / 256, 4096);
   dim3 g3((unsigned)((dm.Tq + 63) / 64) * dm.H * dm.B);
+  const auto* Qh = reinterpret_cast<const uint16_t*>(Q);
+  // the register list holds 16, 32 or 64 entries: the smallest that holds K
+#define HILS_ROW(DD)                                                                             \
+  do {                                                                                           \
+    if (dm.K <= 16)                                                                              \
+      hipLaunchKernelGGL((k_score_mfma<DD, 16>), g3, dim3(64), 0, st, dm, nc, Qh, ks, ent, idx,   \
+                         score);                                                                 \
+    else if (dm.K <= 32)                                                                         \
+      hipLaunchKernelGGL((k_score_mfma<DD, 32>), g3, dim3(64), 0, st, dm, nc, Qh, ks, ent, idx,   \
+                         score);                                                                 \
+    else                                                                                         \
+      hipLaunchKernelGGL((k_score_mfma<DD, 64>), g3, dim3(64), 0, st, dm, nc, Qh, ks, ent, idx,   \
+                         score);                                                                 \
+  } while (0)
   if (dm.d == 64) {
     hipLaunchKernelGGL((k_ksplit<64>), dim3(grid), dim3(256), 0, st, dm, nc, ksum, ks);
-    if (dm.K <= 16)
-      hipLaunchKernelGGL((k_score_mfma<64, 16>), g3, dim3(64), 0, st, dm, nc,
-                         reinterpret_cast<const uint16_t*>(Q), ks, ent, idx, score);
-    else
-      hipLaunchKernelGGL((k_score_mfma<64, 64>), g3, dim3(64), 0, st, dm, nc,
-                         reinterpret_cast<const uint16_t*>(Q), ks, ent, idx, score);
+    HILS_ROW(64);
   } else {
     hipLaunchKernelGGL((k_ksplit<128>), dim3(grid), dim3(256), 0, st, dm, nc, ksum, ks);
-    if (dm.K <= 16)
-      hipLaunchKernelGGL((k_score_mfma<128, 16>), g3, dim3(64), 0, st, dm, nc,
-                         reinterpret_cast<const uint16_t*>(Q), ks, ent, idx, score);
-    else
-      hipLaunchKernelGGL((k_score_mfma<128, 64>), g3, dim3(64), 0, st, dm, nc,
-                         reinterpret_cast<const uint16_t*>(Q), ks, ent, idx, score);
+    HILS_ROW(128);
   }
+#undef HILS_ROW
   return hipGetLastError();
 }
 

@@ -346,6 +346,9 @@ hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const floa
       if (dm.K <= 16)
         hipLaunchKernelGGL(k_topk_merge_wave<16>, dim3(rows), dim3(64), 0, st, dm, ws_s, ws_i, ns,
                            idx, score);
+      else if (dm.K <= 32)
+        hipLaunchKernelGGL(k_topk_merge_wave<32>, dim3(rows), dim3(64), 0, st, dm, ws_s, ws_i, ns,
+                           idx, score);
       else
         hipLaunchKernelGGL(k_topk_merge_wave<64>, dim3(rows), dim3(64), 0, st, dm, ws_s, ws_i, ns,
                            idx, score);
