@@ -255,13 +255,13 @@ def main():
         p0 = wd.q_pos0
         nsteps = min(args.decode_steps, wd.rows_q)
 
-        def decode_run(Kd, wnd):
-            """(eager us/step, HIP-graph us/step) of the decode sequence with top-Kd and
-            local branch `wnd` (0: own chunk)."""
+        def decode_run(Kd, wnd, Kc, Vc):
+            """(eager us/step, HIP-graph us/step) of the decode sequence with top-Kd,
+            local branch `wnd` (0: own chunk) and the cache Kc, Vc (device or pinned host)."""
             dk = torch.empty(1, NCd, wd.H, wd.d, device=dev)
             de = torch.empty(1, NCd, wd.H, device=dev)
             dl = torch.empty(1, NCd, wd.H, device=dev)
-            hsa.summarize(td["K"], td["Ql"], wd.S, 0, p0 // wd.S, Tkv=p0, ksum=dk, ent=de,
+            hsa.summarize(Kc, td["Ql"], wd.S, 0, p0 // wd.S, Tkv=p0, ksum=dk, ent=de,
                           lse_l=dl)
             didx = torch.empty(1, 1, wd.H, Kd, dtype=torch.int32, device=dev)
             dsc = torch.empty(1, 1, wd.H, Kd, device=dev)
@@ -273,12 +273,12 @@ def main():
                 p = p0 + s
                 if (p % wd.S) == 0 and p > p0:  # chunk p/S - 1 just completed
                     c = p // wd.S - 1
-                    hsa.summarize(td["K"], td["Ql"], wd.S, c, c + 1, Tkv=p, ksum=dk, ent=de,
+                    hsa.summarize(Kc, td["Ql"], wd.S, c, c + 1, Tkv=p, ksum=dk, ent=de,
                                   lse_l=dl)
                 q = td["Q"][:, s:s + 1]
                 hsa.score_topk(q, dk, de, Kd, wd.S, p, p + 1, Hkv=wd.Hkv, idx=didx, score=dsc,
                                window=wnd)
-                hsa.attend_fuse(q, td["K"], td["V"], didx, dsc, wd.S, p, p + 1, O=dO,
+                hsa.attend_fuse(q, Kc, Vc, didx, dsc, wd.S, p, p + 1, O=dO,
                                 lse_own=dlo, lse_tot=dlt, window=wnd)
 
             for s in range(8):
@@ -312,7 +312,7 @@ def main():
             torch.cuda.synchronize()
             return eager, ev[0].elapsed_time(ev[1]) * 1e3 / (nsteps * reps)
 
-        eager_us, dec_us = decode_run(wd.K, 0)
+        eager_us, dec_us = decode_run(wd.K, 0, td["K"], td["V"])
         dec_bytes = (NCd * wd.H * (wd.d + 1) * 4 + wd.K * wd.S * wd.H * wd.d * 2 * 2
                      + 32 * wd.H * wd.d * 2 * 2)
         extra["decode_us_per_token_eager"] = eager_us
@@ -320,10 +320,22 @@ def main():
         extra["decode_gbs_wallclock"] = dec_bytes / (dec_us * 1e-6) / 1e9
         extra["decode_steps"] = nsteps
         # the pages' main setting: top-32 and a sliding window of 512 keys
-        eager_m, dec_m = decode_run(32, 512)
+        eager_m, dec_m = decode_run(32, 512, td["K"], td["V"])
         extra["decode_main_us_per_token"] = dec_m
         extra["decode_main_us_per_token_eager"] = eager_m
         extra["decode_main"] = "K=32, sliding window of 512 keys, same cache and steps"
+        # the cache in pinned host memory: each step reads its selected chunks and its
+        # own chunk over the host link; summaries and outputs stay on the GPU
+        Kh = torch.empty(td["K"].shape, dtype=torch.bfloat16, pin_memory=True)
+        Vh = torch.empty(td["V"].shape, dtype=torch.bfloat16, pin_memory=True)
+        Kh.copy_(td["K"])
+        Vh.copy_(td["V"])
+        torch.cuda.synchronize()
+        eager_h, dec_h = decode_run(wd.K, 0, Kh, Vh)
+        extra["decode_host_cache_us_per_token"] = dec_h
+        extra["decode_host_cache_us_per_token_eager"] = eager_h
+        extra["decode_host_cache_gbs"] = (wd.K + 1) * wd.S * wd.H * wd.d * 2 * 2 / (dec_h * 1e-6) / 1e9
+        del Kh, Vh
 
     # ------------------------------------------- 7B-class GQA prefill, training step
     def ev_ms(fn, reps):

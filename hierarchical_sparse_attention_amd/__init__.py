@@ -95,9 +95,11 @@ def _check(fn: str, st: int):
         raise HilsError(fn, st)
 
 
-def _need(t: torch.Tensor, name: str, shape=None, dtype=None):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+def _need(t: torch.Tensor, name: str, shape=None, dtype=None, host_ok=False):
+    """host_ok: the tensor may also live in pinned host memory (a decode cache's K/V)."""
+    if not (t.is_cuda or (host_ok and t.is_pinned())):
+        raise ValueError(f"{name} must be a GPU tensor" + (" or pinned host memory" if host_ok
+                                                          else ""))
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
@@ -121,6 +123,7 @@ def summarize(K: torch.Tensor, Ql: torch.Tensor, S: int = 64, c_begin: int = 0,
               c_end: Optional[int] = None, Tkv: Optional[int] = None, scale: float = 0.0,
               ksum=None, ent=None, lse_l=None):
     """Landmark summaries of chunks [c_begin, c_end). K [B,Tcap,Hkv,d], Ql [B,NCcap,H,d].
+    K may be in pinned host memory (an offloaded cache).
 
     Returns (ksum [B,NCcap,H,d] f32, ent [B,NCcap,H] f32, lse_l [B,NCcap,H] f32).
     """
@@ -128,8 +131,8 @@ def summarize(K: torch.Tensor, Ql: torch.Tensor, S: int = 64, c_begin: int = 0,
     NCcap, H = Ql.shape[1], Ql.shape[2]
     Tkv = Tcap if Tkv is None else Tkv
     c_end = Tkv // S if c_end is None else c_end
-    _need(K, "K"), _need(Ql, "Ql", (B, NCcap, H, d), K.dtype)
-    dev = K.device
+    _need(K, "K", host_ok=True), _need(Ql, "Ql", (B, NCcap, H, d), K.dtype)
+    dev = Ql.device
     ksum = torch.empty(B, NCcap, H, d, dtype=torch.float32, device=dev) if ksum is None else ksum
     ent = torch.empty(B, NCcap, H, dtype=torch.float32, device=dev) if ent is None else ent
     lse_l = torch.empty(B, NCcap, H, dtype=torch.float32, device=dev) if lse_l is None else lse_l
@@ -172,12 +175,15 @@ def attend_fuse(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Te
                 score: torch.Tensor, S: int = 64, q_pos0: int = 0, Tkv: Optional[int] = None,
                 scale: float = 0.0, O=None, lse_own=None, lse_tot=None, window: int = 0):
     """Hierarchical attention -> (O [B,Tq,H,d], lse_own [B,Tq,H], lse_tot [B,Tq,H]);
-    lse_own is the local branch's log-mass (own chunk, or the last `window` keys)."""
+    lse_own is the local branch's log-mass (own chunk, or the last `window` keys).
+    K and V may be in pinned host memory (an offloaded decode cache): the kernels
+    then read only the chunks the rows select and their local branch."""
     B, Tq, H, d = Q.shape
     Tcap, Hkv = K.shape[1], K.shape[2]
     K_sel = idx.shape[-1]
     Tkv = Tcap if Tkv is None else Tkv
-    _need(Q, "Q"), _need(K, "K", (B, Tcap, Hkv, d), Q.dtype), _need(V, "V", (B, Tcap, Hkv, d), Q.dtype)
+    _need(Q, "Q"), _need(K, "K", (B, Tcap, Hkv, d), Q.dtype, host_ok=True)
+    _need(V, "V", (B, Tcap, Hkv, d), Q.dtype, host_ok=True)
     _need(idx, "idx", (B, Tq, H, K_sel), torch.int32)
     _need(score, "score", (B, Tq, H, K_sel), torch.float32)
     dev = Q.device

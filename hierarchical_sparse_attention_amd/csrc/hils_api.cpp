@@ -49,6 +49,27 @@ hils_status resolve(const hils_dims* in, hils::Dims* out) {
   return HILS_OK;
 }
 
+// K and V of a decode cache may live in pinned host memory (hipHostMalloc): the
+// kernels then read through its device mapping, so only the chunks a call
+// touches cross the host link. Device memory passes unchanged; memory no
+// kernel can read (pageable host memory) is rejected.
+hils_status kv_view(const void* p, const void** out) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return HILS_ERR_INVALID_ARG;
+  }
+  if (a.type == hipMemoryTypeHost) {
+    if (a.devicePointer == nullptr) return HILS_ERR_INVALID_ARG;
+    *out = a.devicePointer;
+  } else if (a.type == hipMemoryTypeDevice) {
+    *out = p;
+  } else {
+    return HILS_ERR_INVALID_ARG;  // unregistered (pageable) or other memory kinds
+  }
+  return HILS_OK;
+}
+
 hils_status backward_shape_ok(const hils::Dims& dm) {
   if (dm.q_pos0 != 0 || dm.Tq != dm.Tkv || dm.Tkv % dm.S != 0) return HILS_ERR_UNSUPPORTED;
   return HILS_OK;
@@ -98,7 +119,10 @@ hils_status hils_summarize(const hils_dims* dims, const void* K, const void* Ql,
   if (c_end == c_begin) return HILS_OK;
   if (!aligned16(K) || !aligned16(Ql) || !aligned16(ksum) || !aligned16(ent)) return HILS_ERR_INVALID_ARG;
   if (lse_l != nullptr && !aligned16(lse_l)) return HILS_ERR_INVALID_ARG;
-  return from_hip(hils::launch_summarize(dm, K, Ql, c_begin, c_end, ksum, ent, lse_l,
+  const void* Kd = nullptr;
+  st = kv_view(K, &Kd);
+  if (st != HILS_OK) return st;
+  return from_hip(hils::launch_summarize(dm, Kd, Ql, c_begin, c_end, ksum, ent, lse_l,
                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -131,7 +155,9 @@ hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K
     return HILS_ERR_INVALID_ARG;
   st = check_ws(hils::attend_ws_bytes(dm), ws, ws_bytes);
   if (st != HILS_OK) return st;
-  return from_hip(hils::launch_attend_fuse(dm, Q, K, V, idx, score, O, lse_own, lse_tot, ws,
+  const void *Kd = nullptr, *Vd = nullptr;
+  if ((st = kv_view(K, &Kd)) != HILS_OK || (st = kv_view(V, &Vd)) != HILS_OK) return st;
+  return from_hip(hils::launch_attend_fuse(dm, Q, Kd, Vd, idx, score, O, lse_own, lse_tot, ws,
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -133,6 +133,16 @@ hils_status hils_score_topk(const hils_dims* dims, const void* Q, const float* k
                             size_t ws_bytes, hils_stream stream);
 
 /*
+ * K and V may also be pinned host memory (hipHostMalloc) in hils_summarize and
+ * hils_attend_fuse: a decode cache kept off the GPU (the youleyou.com news
+ * article on HiLS-Attention, its first section and Q&A: the KV cache of the
+ * chunks a query does not select sits in CPU memory). The kernels read it through
+ * its device mapping, so a decode step moves only the chunks it selected and
+ * its local branch over the host link; the summaries stay in device memory.
+ * Pageable host memory returns HILS_ERR_INVALID_ARG.
+ */
+
+/*
  * Intra-chunk attention and inter-chunk fusion (note §5.3 hierarchical
  * softmax; Tide Fig. 3). For row (b,i,h) at position p:
  *   each selected chunk c (idx >= 0): o_c = softmax_j(scale q.k_j) V over its S keys;
