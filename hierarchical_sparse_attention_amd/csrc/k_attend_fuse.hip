@@ -364,7 +364,7 @@ __global__ __launch_bounds__(64) void k_decode_combine(Dims dm, const float* __r
                                                        float* __restrict__ lse_own,
                                                        float* __restrict__ lse_tot) {
   constexpr int X = D / kWave;
-  constexpr int KF = 16;  // slots whose partials are read in the first round trip
+  constexpr int KF = 48 / X;  // slots whose partials are read in the first round trip
   const long long r = blockIdx.x;
   const int lane = threadIdx.x, Ks = dm.K, NS = Ks + dm.nlocal_max();
   const long long pb = r * NS;
@@ -400,11 +400,22 @@ __global__ __launch_bounds__(64) void k_decode_combine(Dims dm, const float* __r
       for (int x = 0; x < X; ++x) acc[x] = fmaf(ak, pv[k][x], acc[x]);
     }
   }
-  for (int k = KF; k < NS; ++k) {
-    const float ak = k < 64 ? lane_bcast(a0, k) : lane_bcast(a1, k - 64);
-    if (ak != 0.0f) {
+  // the remaining slots (more than KF: K > 32 or a long window), eight loads at a time
+  for (int k0 = KF; k0 < NS; k0 += 8) {
+    float pw[8][X];
 #pragma unroll
-      for (int x = 0; x < X; ++x) acc[x] = fmaf(ak, part_o[(pb + k) * D + lane + kWave * x], acc[x]);
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int x = 0; x < X; ++x)
+        pw[u][x] = part_o[(pb + min(k0 + u, NS - 1)) * D + lane + kWave * x];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u;
+      const float ak = k >= NS ? 0.0f : k < 64 ? lane_bcast(a0, k) : lane_bcast(a1, k - 64);
+      if (ak != 0.0f) {
+#pragma unroll
+        for (int x = 0; x < X; ++x) acc[x] = fmaf(ak, pw[u][x], acc[x]);
+      }
     }
   }
 #pragma unroll
