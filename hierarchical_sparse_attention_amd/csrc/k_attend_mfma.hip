@@ -723,29 +723,56 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   // product of the PV step finite
   const bool fast = vmax_wg < 0x1p50f;
 
-  // ---- sliding window, pass 1: per (row, local chunk) maximum and sum
+  // ---- sliding window, pass 1: per (row, local chunk) maximum and sum. Items are
+  // taken two at a time when they share a chunk, so two independent tiles run
+  // per step (every chunk in loc_first .. own_last has rows, see own_item).
+  auto win_next = [&](int& oc, int& ra, int& rb, int& tl) {
+    if (16 * ++tl >= rb - ra) {
+      ++oc;
+      tl = 0;
+      ra = (int)max(0LL, (long long)oc * S - p0) * G;
+      rb = (int)min((long long)Rv, ((long long)oc * S + span - p0) * G);
+    }
+  };
+  // rows, key bounds and query fragments of the tile (oc, ra, rb, tl); `on` false
+  // gives an empty tile
+  auto win_tile = [&](bool on, int oc, int ra, int rb, int tl, int* rho, bool* valid, int* klo,
+                      int* khi, int* lofs, uint4* qo) {
+    *rho = ra + 16 * tl + col;
+    *valid = on && *rho < rb;
+    const long long pos = p0 + (*valid ? *rho : ra) / G, cb = (long long)oc * S;
+    const long long l0 = dm.lstart(pos);
+    *klo = *valid ? (int)max(0LL, l0 - cb) : 0;
+    *khi = *valid ? (int)min((long long)S, pos - cb + 1) : 0;
+    *lofs = oc - (int)(l0 / S);
+    lds_q<D>(qo, sm.qs, *rho, *valid);
+  };
   if constexpr (SWA) {
     int fc = C::PREFETCH && o_have ? o_oc : -1;  // chunk whose fragments f holds
-    for (int item = item0; o_have;) {
-      if (o_oc != fc) {
-        load_frag<D>(f, K, Vt, kv_base, kv_stride, o_oc, vt_base + (long long)o_oc * D * kChunk,
+    int oc = o_oc, ra = o_ra, rb = o_rb, tl = o_tl;
+    for (int left = o_have ? item_end - item0 : 0; left > 0;) {
+      int oc2 = oc, ra2 = ra, rb2 = rb, tl2 = tl;
+      win_next(oc2, ra2, rb2, tl2);
+      const bool two = left >= 2 && oc2 == oc;
+      if (oc != fc) {
+        load_frag<D>(f, K, Vt, kv_base, kv_stride, oc, vt_base + (long long)oc * D * kChunk,
                      dm.Tkv);
-        fc = o_oc;
+        fc = oc;
       }
-      const int rho = o_ra + 16 * o_tl + col;
-      const bool valid = rho < o_rb;
-      const long long pos = p0 + (valid ? rho : o_ra) / G, cb = (long long)o_oc * S;
-      const long long l0 = dm.lstart(pos);
-      const int klo = valid ? (int)max(0LL, l0 - cb) : 0;
-      const int khi = valid ? (int)min((long long)S, pos - cb + 1) : 0;
-      uint4 qo[D / 32];
-      lds_q<D>(qo, sm.qs, rho, valid);
-      float m2, z;
-      tile_stats<D>(f, qo, klo, khi, scale2, &m2, &z);
-      if (valid && gl == 0) sm.lpart[rho * nloc + (o_oc - (int)(l0 / S))] = make_float2(m2, z);
-      ++item;
-      o_have = item < item_end && own_item(item, p0, S, span, G, Rv, loc_first, own_last, &o_oc,
-                                           &o_ra, &o_rb, &o_tl);
+      int rho[2], klo[2], khi[2], lofs[2];
+      bool valid[2];
+      uint4 qo[2][D / 32];
+      win_tile(true, oc, ra, rb, tl, &rho[0], &valid[0], &klo[0], &khi[0], &lofs[0], qo[0]);
+      win_tile(two, oc2, ra2, rb2, tl2, &rho[1], &valid[1], &klo[1], &khi[1], &lofs[1], qo[1]);
+      float m2[2], z[2];
+      tile_stats<D>(f, qo[0], klo[0], khi[0], scale2, &m2[0], &z[0]);
+      tile_stats<D>(f, qo[1], klo[1], khi[1], scale2, &m2[1], &z[1]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (valid[i] && gl == 0) sm.lpart[rho[i] * nloc + lofs[i]] = make_float2(m2[i], z[i]);
+      oc = oc2, ra = ra2, rb = rb2, tl = tl2;
+      if (two) win_next(oc, ra, rb, tl);
+      left -= two ? 2 : 1;
     }
   }
   // ---- own chunks: causal, normalised (float accumulators for now)
@@ -829,32 +856,36 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   }
   __syncthreads();
 
-  // ---- sliding window, pass 2: exp(s_j - Lambda) v_j of every window key
+  // ---- sliding window, pass 2: exp(s_j - Lambda) v_j of every window key,
+  // two tiles per step as in pass 1
   if constexpr (SWA) {
     int oc = 0, ra = 0, rb = 0, tl = 0, fc = -1;
-    bool have = item0 < item_end &&
-                own_item(item0, p0, S, span, G, Rv, loc_first, own_last, &oc, &ra, &rb, &tl);
-    for (int item = item0; have;) {
+    const bool have = item0 < item_end &&
+                      own_item(item0, p0, S, span, G, Rv, loc_first, own_last, &oc, &ra, &rb, &tl);
+    for (int left = have ? item_end - item0 : 0; left > 0;) {
+      int oc2 = oc, ra2 = ra, rb2 = rb, tl2 = tl;
+      win_next(oc2, ra2, rb2, tl2);
+      const bool two = left >= 2 && oc2 == oc;
       if (oc != fc) {
         load_frag<D>(f, K, Vt, kv_base, kv_stride, oc, vt_base + (long long)oc * D * kChunk,
                      dm.Tkv);
         fc = oc;
       }
-      const int rho = ra + 16 * tl + col;
-      const bool valid = rho < rb;
-      const long long pos = p0 + (valid ? rho : ra) / G, cb = (long long)oc * S;
-      const long long l0 = dm.lstart(pos);
-      const int klo = valid ? (int)max(0LL, l0 - cb) : 0;
-      const int khi = valid ? (int)min((long long)S, pos - cb + 1) : 0;
-      const float lam2 = valid ? sm.lam[rho] : 0.f;
-      uint4 qo[D / 32];
-      lds_q<D>(qo, sm.qs, rho, valid);
-      floatx4 o[D / 16];
-      tile_abs<D>(f, qo, klo, khi, scale2, lam2, o);
-      if (valid) accumulate_fw<D>(sm, o, rho, fx_scale);
-      ++item;
-      have = item < item_end &&
-             own_item(item, p0, S, span, G, Rv, loc_first, own_last, &oc, &ra, &rb, &tl);
+      int rho[2], klo[2], khi[2], lofs[2];
+      bool valid[2];
+      uint4 qo[2][D / 32];
+      win_tile(true, oc, ra, rb, tl, &rho[0], &valid[0], &klo[0], &khi[0], &lofs[0], qo[0]);
+      win_tile(two, oc2, ra2, rb2, tl2, &rho[1], &valid[1], &klo[1], &khi[1], &lofs[1], qo[1]);
+      floatx4 o[2][D / 16];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        tile_abs<D>(f, qo[i], klo[i], khi[i], scale2, valid[i] ? sm.lam[rho[i]] : 0.f, o[i]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (valid[i]) accumulate_fw<D>(sm, o[i], rho[i], fx_scale);
+      oc = oc2, ra = ra2, rb = rb2, tl = tl2;
+      if (two) win_next(oc, ra, rb, tl);
+      left -= two ? 2 : 1;
     }
     if (C::PREFETCH && w < nnz)
       load_frag<D>(f, K, Vt, kv_base, kv_stride, sm.cur[w],
