@@ -40,6 +40,7 @@ SMALL = {
                                   dtype="bf16", n_planted=1, n_uniform=2),
     "f32_d128": synth.small("f32_d128", B=1, T=512, H=2, Hkv=2, d=128, K=3, dtype="f32"),
     "f32_kmax": synth.small("f32_kmax", B=1, T=4224, H=1, Hkv=1, d=64, K=64, dtype="f32"),
+    "bf16_kmax": synth.small("bf16_kmax", B=1, T=4224, H=2, Hkv=1, d=64, K=64, dtype="bf16"),
     "single_chunk": synth.small("single_chunk", B=1, T=64, H=2, Hkv=1, d=64, K=2, dtype="bf16"),
 }
 _cache = {}
@@ -360,6 +361,9 @@ BWD = {
     "bwd_f32_d128": synth.small("bwd_f32_d128", B=1, T=256, H=2, Hkv=1, d=128, K=2,
                                 dtype="f32", need_dO=True),
     "bwd_bf16_d128": synth.small("bwd_bf16_d128", B=1, T=512, H=4, Hkv=1, d=128, K=3,
+                                 dtype="bf16", need_dO=True),
+    # the largest top-K with real selections (up to 65 candidates per row)
+    "bwd_bf16_kmax": synth.small("bwd_bf16_kmax", B=1, T=4224, H=2, Hkv=1, d=64, K=64,
                                  dtype="bf16", need_dO=True),
 }
 

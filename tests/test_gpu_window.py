@@ -46,6 +46,9 @@ WIN = {
                                dtype="f32"), 64),
     # the window covers every row's prefix: no candidates anywhere
     "w_cover": (synth.small("w_cover", B=1, T=384, H=2, Hkv=1, d=64, K=3, dtype="bf16"), 512),
+    # the largest top-K and the largest window
+    "w_bf16_kmax_wmax": (synth.small("w_bf16_kmax_wmax", B=1, T=3072, H=2, Hkv=1, d=64, K=64,
+                                     dtype="bf16"), 2048),
 }
 _cache = {}
 
@@ -108,7 +111,7 @@ def test_forward_window_group_max(name):
     check_forward(w, x, f, o)
 
 
-@pytest.mark.parametrize("name", ["w_bf16_gqa_k32", "w_bf16_d128_g4", "w_f32"])
+@pytest.mark.parametrize("name", ["w_bf16_gqa_k32", "w_bf16_d128_g4", "w_f32", "w_bf16_kmax_wmax"])
 def test_decode_window_rows_equal_prefill_rows(name):
     """Single rows (split scoring, slot-parallel decode attention with one slot per
     local chunk) select and attend as the prefill pass does."""
@@ -142,6 +145,12 @@ BWD = {
                            need_dO=True), 128),
     "bw_bf16_d128": (synth.small("bw_bf16_d128", B=1, T=512, H=4, Hkv=1, d=128, K=3,
                                  dtype="bf16", need_dO=True), 192),
+    # the largest window of the matrix-core backward (1024 keys) and, past it, the
+    # vector path with the largest window and top-K
+    "bw_bf16_w1024": (synth.small("bw_bf16_w1024", B=1, T=2048, H=2, Hkv=1, d=64, K=8,
+                                  dtype="bf16", need_dO=True), 1024),
+    "bw_bf16_kmax_wmax": (synth.small("bw_bf16_kmax_wmax", B=1, T=3072, H=2, Hkv=1, d=64,
+                                      K=64, dtype="bf16", need_dO=True), 2048),
 }
 
 
