@@ -9,10 +9,11 @@
 //    into one row list per chunk, so the work is exactly the (row, chunk) pairs
 //    the selection asks for, packed into 16-row MFMA tiles.
 //  * Chunk u of the workgroup's union is owned by wavefront u mod 8, which loads
-//    that chunk's K and V^T MFMA fragments straight into registers (from L2; no
-//    LDS staging and no workgroup barrier in the main loop) and runs every tile
-//    of the chunk: S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys on M, rows on N),
-//    a column softmax, O^T = V^T P^T.
+//    that chunk's K and V^T MFMA fragments straight into registers (from the
+//    fragment copy through L2; no LDS staging and no workgroup barrier in the
+//    main loop) and runs every tile of the chunk: S^T = K Q^T
+//    (v_mfma_f32_16x16x32_bf16, keys on M, rows on N), a column softmax,
+//    O^T = V^T P^T.
 //  * The local branch is the own chunk (one causal tile per row, normalised in
 //    place) or, with a sliding window of W keys, the W/S + 1 chunks the window
 //    touches: a first pass over (local chunk, 16-row tile) items records each
@@ -23,9 +24,10 @@
 //    in a fixed-point format scaled from max|V| over the workgroup's chunks.
 //    Integer addition is associative, so the result does not depend on which
 //    wavefront finishes first: the output is bitwise deterministic.
-//  * V is first rewritten (k_vt_prep) chunk by chunk as V^T with the key order of
-//    the MFMA k-slots, so each V^T fragment is one 16-byte load; the same pass
-//    records max|V| per chunk.
+//  * K and V are first rewritten (k_kv_prep), chunk by chunk, as the MFMA
+//    fragments of each lane in lane order (V as V^T with the key order of the
+//    MFMA k-slots), so every fragment load of a wavefront is 1 KiB of contiguous
+//    memory; the same pass records max|V| per chunk.
 //  * Workgroups are numbered kv-head-fastest, so consecutive workgroups (which
 //    the dispatcher spreads over the 8 XCDs) give each XCD's L2 a small set of kv
 //    heads whose K/V it keeps resident.
@@ -57,6 +59,7 @@ struct Cfg {
   static constexpr int KF = 4 * (D / 32);           // K fragments (uint4) per lane per chunk
   static constexpr int VF = (D / 16) * 2;           // V^T fragments per lane per chunk
   static constexpr bool PREFETCH = D == 64;         // second fragment set, LDS reads ahead
+  static constexpr int CH = (KF + VF) * 64;         // 16-byte words per chunk in the fragment copy
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
@@ -81,13 +84,23 @@ __device__ __forceinline__ float xsum_16_32(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// ------------------------------------------------------------------ V^T prepass
-// Vt[b][g][c][e][p]: feature e of chunk c in k-slot order p (see above), zero for
-// keys at or beyond Tkv; vmax[b][g][c] = max |V| over the chunk.
+// ------------------------------------------------------------------ fragment copy
+// Per chunk, the K and V^T MFMA fragments of every lane, in the order the main
+// kernel reads them: fragment i of lane l is the 16-byte word i * 64 + l of the
+// chunk's block, so one fragment load of a wavefront reads 1 KiB of contiguous
+// memory (a direct load of K rows would put the 16 lanes of each quarter-wave on
+// 16 different rows and cache lines, and the L1 tag rate would bound the kernel).
+// Fragment kb (D/32) + ds of lane (c, g) holds K[16 kb + c][32 ds + 8 g .. + 8];
+// fragment KF + 2 db + ks holds feature 16 db + c of the keys in k-slots
+// 32 ks + 8 g .. + 8 (the k-slot key order above). Keys at or beyond Tkv are zero.
+// vmax[b][g][c] = max |V| over the chunk.
 template <int D>
-__global__ __launch_bounds__(256) void k_vt_prep(Dims dm, int nct, const uint16_t* __restrict__ V,
-                                                 uint16_t* __restrict__ Vt,
+__global__ __launch_bounds__(256) void k_kv_prep(Dims dm, int nct, const uint16_t* __restrict__ K,
+                                                 const uint16_t* __restrict__ V,
+                                                 uint4* __restrict__ KVf,
                                                  float* __restrict__ vmax) {
+  using C = Cfg<D>;
+  __shared__ uint16_t ks[kChunk][D + 8];
   __shared__ uint16_t vs[kChunk][D + 8];
   __shared__ float red[4];
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
@@ -97,8 +110,11 @@ __global__ __launch_bounds__(256) void k_vt_prep(Dims dm, int nct, const uint16_
   for (int u = t; u < kChunk * D / 8; u += 256) {
     const int j = u / (D / 8), c8 = u % (D / 8);
     const long long row = (long long)c * kChunk + j;
-    uint4 v = row < dm.Tkv ? *reinterpret_cast<const uint4*>(V + kv_base + row * kv_stride + c8 * 8)
-                           : make_uint4(0, 0, 0, 0);
+    const long long off = kv_base + row * kv_stride + c8 * 8;
+    const bool in = row < dm.Tkv;
+    const uint4 kk = in ? *reinterpret_cast<const uint4*>(K + off) : make_uint4(0, 0, 0, 0);
+    const uint4 v = in ? *reinterpret_cast<const uint4*>(V + off) : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&ks[j][c8 * 8]) = kk;
     *reinterpret_cast<uint4*>(&vs[j][c8 * 8]) = v;
     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -110,20 +126,24 @@ __global__ __launch_bounds__(256) void k_vt_prep(Dims dm, int nct, const uint16_
   mx = wave_max(mx);
   if ((t & 63) == 0) red[t >> 6] = mx;
   __syncthreads();
-  const long long cbase = (((long long)b * dm.Hkv + g) * nct + c) * (long long)D * kChunk;
-  for (int u = t; u < D * 8; u += 256) {
-    const int e = u / 8, p8 = u % 8;  // feature e, k-slot run p8*8..p8*8+7
-    const int ks = p8 / 4, gg = p8 % 4;
+  uint4* out = KVf + (((long long)b * dm.Hkv + g) * nct + c) * C::CH;
+  for (int u = t; u < C::KF * 64; u += 256) {
+    const int i = u >> 6, lc = u & 15, lg = (u >> 4) & 3;
+    const int kb = i / (D / 32), ds = i % (D / 32);
+    out[u] = *reinterpret_cast<const uint4*>(&ks[16 * kb + lc][32 * ds + 8 * lg]);
+  }
+  for (int u = t; u < C::VF * 64; u += 256) {
+    const int i = u >> 6, lg = (u >> 4) & 3, kslot = i & 1;
+    const int e = 16 * (i >> 1) + (u & 15);
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int j0 = 2 * q, j1 = 2 * q + 1;
-      const int k0 = 32 * ks + (j0 < 4 ? 4 * gg + j0 : 16 + 4 * gg + j0 - 4);
-      const int k1 = 32 * ks + (j1 < 4 ? 4 * gg + j1 : 16 + 4 * gg + j1 - 4);
+      const int k0 = 32 * kslot + (j0 < 4 ? 4 * lg + j0 : 16 + 4 * lg + j0 - 4);
+      const int k1 = 32 * kslot + (j1 < 4 ? 4 * lg + j1 : 16 + 4 * lg + j1 - 4);
       w[q] = (uint32_t)vs[k0][e] | ((uint32_t)vs[k1][e] << 16);
     }
-    *reinterpret_cast<uint4*>(Vt + cbase + (long long)e * kChunk + p8 * 8) =
-        make_uint4(w[0], w[1], w[2], w[3]);
+    out[C::KF * 64 + u] = make_uint4(w[0], w[1], w[2], w[3]);
   }
   if (t == 0)
     vmax[((long long)b * dm.Hkv + g) * nct + c] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -136,27 +156,15 @@ struct Frag {
   uint4 v[Cfg<D>::VF];  // v[db * 2 + ks]: V^T[16db + c][k-slots 32ks + 8g .. +8]
 };
 
-// Key rows at or beyond Tkv (a partial trailing own chunk) are clamped to the last
-// key: they are masked out of the softmax, so only the read must stay in bounds.
+// Fragments of one chunk from its block of the fragment copy (word `base`).
 template <int D>
-__device__ __forceinline__ void load_frag(Frag<D>& f, const uint16_t* K, const uint16_t* Vt,
-                                          long long kv_base, long long kv_stride, int chunk,
-                                          long long vt_chunk_base, long long Tkv) {
-  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+__device__ __forceinline__ void load_frag(Frag<D>& f, const uint4* __restrict__ KVf,
+                                          long long base) {
+  const uint4* p = KVf + base + (threadIdx.x & 63);
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int i = 0; i < Cfg<D>::KF; ++i) f.k[i] = p[i * 64];
 #pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-      const long long row = min((long long)chunk * kChunk + 16 * kb + c, Tkv - 1);
-      f.k[kb * (D / 32) + ds] =
-          *reinterpret_cast<const uint4*>(K + kv_base + row * kv_stride + 32 * ds + 8 * g);
-    }
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      f.v[db * 2 + ks] = *reinterpret_cast<const uint4*>(
-          Vt + vt_chunk_base + (long long)(16 * db + c) * kChunk + 32 * ks + 8 * g);
+  for (int i = 0; i < Cfg<D>::VF; ++i) f.v[i] = p[(Cfg<D>::KF + i) * 64];
 }
 
 template <int D>
@@ -581,8 +589,7 @@ __device__ __forceinline__ void run_chunk(const Frag<D>& f, const Smem& sm, int 
 template <int D, bool SWA>
 __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     Dims dm, int R, int Rq, int ncr_cap, int nqb, int nct, const uint16_t* __restrict__ Q,
-    const uint16_t* __restrict__ K, const uint16_t* __restrict__ Vt,
-    const float* __restrict__ vmax, const int32_t* __restrict__ idx,
+    const uint4* __restrict__ KVf, const float* __restrict__ vmax, const int32_t* __restrict__ idx,
     const float* __restrict__ score, uint16_t* __restrict__ O, float* __restrict__ lse_own,
     float* __restrict__ lse_tot) {
   using C = Cfg<D>;
@@ -605,9 +612,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   const int loc_first = SWA ? (int)(dm.lstart(p0) / S) : own_first;
   const int nloc = SWA ? dm.nlocal_max() : 0;
   Smem sm = carve<D>(smem_raw, R, Ksel, ncr_cap, nloc);
-  const long long kv_stride = (long long)dm.Hkv * D;
-  const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
-  const long long vt_base = ((long long)b * dm.Hkv + g) * nct * (long long)D * kChunk;
+  const long long kvf_base = ((long long)b * dm.Hkv + g) * nct * (long long)C::CH;
   const float* vmx = vmax + ((long long)b * dm.Hkv + g) * nct;
   const float scale2 = dm.scale * kLog2e;
   // global row of workgroup row rho (query position qi0 + rho / G, head g G + rho % G)
@@ -625,7 +630,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   bool o_have = item0 < item_end && own_item(item0, p0, S, span, G, Rv, loc_first, own_last,
                                              &o_oc, &o_ra, &o_rb, &o_tl);
   if (C::PREFETCH && o_have)
-    load_frag<D>(f, K, Vt, kv_base, kv_stride, o_oc, vt_base + (long long)o_oc * D * kChunk, dm.Tkv);
+    load_frag<D>(f, KVf, kvf_base + (long long)(o_oc) * C::CH);
 
   // ---- set-up: every global read of the set-up is issued first
   const int kgroups = (Ksel + 7) / 8;  // Rv * kgroups <= kThreads (see plan)
@@ -755,8 +760,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
       win_next(oc2, ra2, rb2, tl2);
       const bool two = left >= 2 && oc2 == oc;
       if (oc != fc) {
-        load_frag<D>(f, K, Vt, kv_base, kv_stride, oc, vt_base + (long long)oc * D * kChunk,
-                     dm.Tkv);
+        load_frag<D>(f, KVf, kvf_base + (long long)(oc) * C::CH);
         fc = oc;
       }
       int rho[2], klo[2], khi[2], lofs[2];
@@ -778,8 +782,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   // ---- own chunks: causal, normalised (float accumulators for now)
   for (int item = item0; !SWA && o_have; ) {
     if (!C::PREFETCH)
-      load_frag<D>(f, K, Vt, kv_base, kv_stride, o_oc, vt_base + (long long)o_oc * D * kChunk,
-                   dm.Tkv);
+      load_frag<D>(f, KVf, kvf_base + (long long)(o_oc) * C::CH);
     const int rho = o_ra + 16 * o_tl + col;
     const bool valid = rho < o_rb;
     const int nk = valid ? (int)(p0 + rho / G - (long long)o_oc * S) + 1 : 0;
@@ -802,13 +805,11 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     o_have = item < item_end && own_item(item, p0, S, span, G, Rv, loc_first, own_last, &o_oc,
                                          &o_ra, &o_rb, &o_tl);
     if (C::PREFETCH && o_have && o_oc != prev)
-      load_frag<D>(f, K, Vt, kv_base, kv_stride, o_oc, vt_base + (long long)o_oc * D * kChunk,
-                   dm.Tkv);
+      load_frag<D>(f, KVf, kvf_base + (long long)(o_oc) * C::CH);
   }
   // the first selected chunk's fragment is requested before the fusion set-up
   if (!SWA && C::PREFETCH && w < nnz)
-    load_frag<D>(f, K, Vt, kv_base, kv_stride, sm.cur[w],
-                 vt_base + (long long)sm.cur[w] * D * kChunk, dm.Tkv);
+    load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[w]) * C::CH);
   __syncthreads();
 
   // ---- fusion normaliser per row from the local log-mass and the score partials
@@ -867,8 +868,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
       win_next(oc2, ra2, rb2, tl2);
       const bool two = left >= 2 && oc2 == oc;
       if (oc != fc) {
-        load_frag<D>(f, K, Vt, kv_base, kv_stride, oc, vt_base + (long long)oc * D * kChunk,
-                     dm.Tkv);
+        load_frag<D>(f, KVf, kvf_base + (long long)(oc) * C::CH);
         fc = oc;
       }
       int rho[2], klo[2], khi[2], lofs[2];
@@ -888,15 +888,13 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
       left -= two ? 2 : 1;
     }
     if (C::PREFETCH && w < nnz)
-      load_frag<D>(f, K, Vt, kv_base, kv_stride, sm.cur[w],
-                   vt_base + (long long)sm.cur[w] * D * kChunk, dm.Tkv);
+      load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[w]) * C::CH);
   }
 
   // ---- selected chunks: chunk u belongs to wavefront u mod 8; no barriers.
   if (!C::PREFETCH) {
     for (int u = w; u < nnz; u += kWaves) {
-      load_frag<D>(f, K, Vt, kv_base, kv_stride, sm.cur[u],
-                   vt_base + (long long)sm.cur[u] * D * kChunk, dm.Tkv);
+      load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[u]) * C::CH);
       run_chunk<D, 1>(f, sm, sm.cur[u], scale2, fast, fx_scale);
     }
   }
@@ -906,10 +904,10 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   // waiting for the current set never waits for the one behind it.
   for (int u = w; C::PREFETCH && u < nnz; u += 2 * kWaves) {
     const int ua = sm.cur[min(u + kWaves, nnz - 1)], ub = sm.cur[min(u + 2 * kWaves, nnz - 1)];
-    load_frag<D>(f2, K, Vt, kv_base, kv_stride, ua, vt_base + (long long)ua * D * kChunk, dm.Tkv);
+    load_frag<D>(f2, KVf, kvf_base + (long long)(ua) * C::CH);
     run_chunk<D, 2>(f, sm, sm.cur[u], scale2, fast, fx_scale);
     if (u + kWaves >= nnz) break;
-    load_frag<D>(f, K, Vt, kv_base, kv_stride, ub, vt_base + (long long)ub * D * kChunk, dm.Tkv);
+    load_frag<D>(f, KVf, kvf_base + (long long)(ub) * C::CH);
     run_chunk<D, 2>(f2, sm, ua, scale2, fast, fx_scale);
   }
   __syncthreads();
@@ -938,7 +936,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
 
 struct Plan {
   int R, Rq, ncr, nqb, nct;
-  size_t bytes, vt_bytes, vmax_bytes;
+  size_t bytes, kvf_bytes, vmax_bytes;
 };
 
 template <int D>
@@ -965,7 +963,7 @@ bool plan(const Dims& dm, Plan* p) {
   p->nqb = (dm.Tq + rq - 1) / rq;
   p->nct = (int)((last + dm.S) / dm.S);  // chunks holding keys 0..last
   p->bytes = b;
-  p->vt_bytes = (size_t)dm.B * dm.Hkv * p->nct * D * kChunk * 2;
+  p->kvf_bytes = (size_t)dm.B * dm.Hkv * p->nct * Cfg<D>::CH * 16;
   p->vmax_bytes = (size_t)dm.B * dm.Hkv * p->nct * 4;
   return true;
 }
@@ -974,18 +972,19 @@ template <int D>
 hipError_t launch_t(const Dims& dm, const Plan& p, const void* Q, const void* K, const void* V,
                     const int32_t* idx, const float* score, void* O, float* lse_own,
                     float* lse_tot, void* ws, hipStream_t st) {
-  uint16_t* vt = reinterpret_cast<uint16_t*>(ws);
+  uint4* kvf = reinterpret_cast<uint4*>(ws);
   float* vmax = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                         ((p.vt_bytes + 255) & ~(size_t)255));
-  hipLaunchKernelGGL((k_vt_prep<D>), dim3(p.nct, dm.Hkv, dm.B), dim3(256), 0, st, dm, p.nct,
-                     reinterpret_cast<const uint16_t*>(V), vt, vmax);
+                                         ((p.kvf_bytes + 255) & ~(size_t)255));
+  hipLaunchKernelGGL((k_kv_prep<D>), dim3(p.nct, dm.Hkv, dm.B), dim3(256), 0, st, dm, p.nct,
+                     reinterpret_cast<const uint16_t*>(K), reinterpret_cast<const uint16_t*>(V),
+                     kvf, vmax);
   auto kfn = dm.window > 0 ? k_attend_mfma<D, true> : k_attend_mfma<D, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.bytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kfn, dim3(dm.B * p.nqb * dm.Hkv), dim3(kThreads), p.bytes, st, dm, p.R, p.Rq,
                      p.ncr, p.nqb, p.nct, reinterpret_cast<const uint16_t*>(Q),
-                     reinterpret_cast<const uint16_t*>(K), vt, vmax, idx, score,
+                     kvf, vmax, idx, score,
                      reinterpret_cast<uint16_t*>(O), lse_own, lse_tot);
   return hipGetLastError();
 }
@@ -1000,7 +999,7 @@ bool plan_any(const Dims& dm, Plan* p) {
 size_t attend_mfma_ws_bytes(const Dims& dm) {
   Plan p;
   if (!plan_any(dm, &p)) return 0;
-  return ((p.vt_bytes + 255) & ~(size_t)255) + p.vmax_bytes;
+  return ((p.kvf_bytes + 255) & ~(size_t)255) + p.vmax_bytes;
 }
 
 // Launches and returns true when the MFMA path applies (bf16, prefill-sized,
