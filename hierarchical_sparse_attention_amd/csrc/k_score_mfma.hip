@@ -58,27 +58,41 @@ __device__ __forceinline__ floatx4 score_block(const uint4* qa, const bf16x8* hi
   return acc;
 }
 
-// Split copy of the summary keys: ks[b][c][h][0:D] = hi, [D:2D] = lo.
+// Split copy of the summary keys in MFMA fragment order. Per (b, h) the chunks
+// come in blocks of 16; block blk holds D/16 fragments of 64 lanes, fragment
+// 2 ds + x of lane (c, g) being the hi (x = 0) or lo (x = 1) part of
+// k'[16 blk + c][32 ds + 8 g .. + 8] (16 bytes). One fragment load of a
+// wavefront is then 1 KiB of contiguous memory. Chunks at or beyond nc are zero.
+template <int D>
+__device__ __forceinline__ long long ks_frag(const Dims& dm, int nc, int b, int h, int blk) {
+  return ((((long long)b * dm.H + h) * ((nc + 15) / 16) + blk) * (D / 16)) * 64;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_ksplit(Dims dm, int nc, const float* __restrict__ ksum,
-                                                uint16_t* __restrict__ ks) {
-  const long long n8 = (long long)dm.B * nc * dm.H * (D / 8);
-  for (long long x = blockIdx.x * 256LL + threadIdx.x; x < n8; x += (long long)gridDim.x * 256) {
-    const long long rowi = x / (D / 8);
-    const int c8 = (int)(x % (D / 8));
-    const int h = (int)(rowi % dm.H);
-    const long long bc = rowi / dm.H;
-    const int c = (int)(bc % nc), b = (int)(bc / nc);
-    const float* src = ksum + (((long long)b * dm.NCcap + c) * dm.H + h) * D + c8 * 8;
-    float v[8];
-    const float4 a = *reinterpret_cast<const float4*>(src);
-    const float4 bb = *reinterpret_cast<const float4*>(src + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = bb.x; v[5] = bb.y; v[6] = bb.z; v[7] = bb.w;
+                                                uint4* __restrict__ ks) {
+  const int nblk = (nc + 15) / 16;
+  const long long n = (long long)dm.B * dm.H * nblk * (D / 16) * 64;
+  for (long long x = blockIdx.x * 256LL + threadIdx.x; x < n; x += (long long)gridDim.x * 256) {
+    const int lane = (int)(x & 63), i = (int)((x >> 6) % (D / 16));
+    const long long bhb = (x >> 6) / (D / 16);
+    const int blk = (int)(bhb % nblk);
+    const long long bh = bhb / nblk;
+    const int h = (int)(bh % dm.H), b = (int)(bh / dm.H);
+    const int chunk = 16 * blk + (lane & 15), ds = i >> 1;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (chunk < nc) {
+      const float* src = ksum + (((long long)b * dm.NCcap + chunk) * dm.H + h) * D + 32 * ds +
+                         8 * (lane >> 4);
+      const float4 a = *reinterpret_cast<const float4*>(src);
+      const float4 bb = *reinterpret_cast<const float4*>(src + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = bb.x; v[5] = bb.y; v[6] = bb.z; v[7] = bb.w;
+    }
     bf16x8 hi, lo;
     split8(v, hi, lo);
-    uint16_t* dst = ks + rowi * 2 * D + c8 * 8;
-    __builtin_memcpy(dst, &hi, 16);
-    __builtin_memcpy(dst + D, &lo, 16);
+    uint4 w;
+    __builtin_memcpy(&w, (i & 1) ? &lo : &hi, 16);
+    ks[x] = w;
   }
 }
 
@@ -139,12 +153,12 @@ __device__ __forceinline__ void sort16(float* x, int* xc) {
       }
 }
 
+// d = 128 with a 16-entry list is held to 3 wavefronts per SIMD (it fits in 168
+// registers; left alone the compiler takes 174 and only 2 fit).
 template <int D, int KM>
-__global__ __launch_bounds__(64) void k_score_mfma(Dims dm, int nc, const uint16_t* __restrict__ Q,
-                                                   const uint16_t* __restrict__ ks,
-                                                   const float* __restrict__ ent,
-                                                   int32_t* __restrict__ idx,
-                                                   float* __restrict__ score) {
+__global__ __launch_bounds__(64, (D == 128 && KM == 16) ? 3 : 1) void k_score_mfma(
+    Dims dm, int nc, const uint16_t* __restrict__ Q, const uint4* __restrict__ ks,
+    const float* __restrict__ ent, int32_t* __restrict__ idx, float* __restrict__ score) {
   __shared__ float sS[64][65];
   const int lane = threadIdx.x, c = lane & 15, g = lane >> 4;
   // 1-D grid, position blocks slowest and longest (latest) first
@@ -174,11 +188,11 @@ __global__ __launch_bounds__(64) void k_score_mfma(Dims dm, int nc, const uint16
       const int chunk = c0 + 16 * nb + c;
       const bool cv = chunk < nmax;
       bf16x8 hi[D / 32], lo[D / 32];
-      const uint16_t* src = ks + (((long long)b * nc + (cv ? chunk : 0)) * dm.H + h) * 2 * D;
+      const uint4* src = ks + ks_frag<D>(dm, nc, b, h, cv ? (c0 >> 4) + nb : 0) + lane;
 #pragma unroll
       for (int ds = 0; ds < D / 32; ++ds) {
-        const uint4 uh = cv ? *reinterpret_cast<const uint4*>(src + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
-        const uint4 ul = cv ? *reinterpret_cast<const uint4*>(src + D + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
+        const uint4 uh = cv ? src[(2 * ds) * 64] : make_uint4(0, 0, 0, 0);
+        const uint4 ul = cv ? src[(2 * ds + 1) * 64] : make_uint4(0, 0, 0, 0);
         hi[ds] = as_bf16x8(uh);
         lo[ds] = as_bf16x8(ul);
       }
@@ -261,7 +275,7 @@ __global__ __launch_bounds__(64) void k_score_mfma(Dims dm, int nc, const uint16
 template <int D, int KM, int G>
 __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
                                                              const uint16_t* __restrict__ Q,
-                                                             const uint16_t* __restrict__ ks,
+                                                             const uint4* __restrict__ ks,
                                                              const float* __restrict__ ent,
                                                              int32_t* __restrict__ idx,
                                                              float* __restrict__ score) {
@@ -299,12 +313,12 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
     for (int nb = 0; nb < 4; ++nb) {
       const int chunk = c0 + 16 * nb + c;
       const bool cv = chunk < nmax;
-      const long long hrow = ((long long)b * nc + (cv ? chunk : 0)) * dm.H + h;
+      const uint4* src = ks + ks_frag<D>(dm, nc, b, h, cv ? (c0 >> 4) + nb : 0) + lane;
       bf16x8 hi[D / 32], lo[D / 32];
 #pragma unroll
       for (int ds = 0; ds < D / 32; ++ds) {
-        const uint4 uh = cv ? *reinterpret_cast<const uint4*>(ks + hrow * 2 * D + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
-        const uint4 ul = cv ? *reinterpret_cast<const uint4*>(ks + hrow * 2 * D + D + 32 * ds + 8 * g) : make_uint4(0, 0, 0, 0);
+        const uint4 uh = cv ? src[(2 * ds) * 64] : make_uint4(0, 0, 0, 0);
+        const uint4 ul = cv ? src[(2 * ds + 1) * 64] : make_uint4(0, 0, 0, 0);
         hi[ds] = as_bf16x8(uh);
         lo[ds] = as_bf16x8(ul);
       }
@@ -635,9 +649,9 @@ hipError_t launch_score_mfma_group(const Dims& dm, const void* Q, const float* k
                                    const float* ent, int32_t* idx, float* score, void* ws,
                                    hipStream_t st) {
   const int nc = max(1, dm.ncand(dm.q_pos0 + dm.Tq - 1));
-  uint16_t* ks = reinterpret_cast<uint16_t*>(ws);
-  const long long n8 = (long long)dm.B * nc * dm.H * (dm.d / 8);
-  const int grid = (int)std::min<long long>((n8 + 255) / 256, 4096);
+  uint4* ks = reinterpret_cast<uint4*>(ws);
+  const long long n16 = (long long)dm.B * dm.H * ((nc + 15) / 16) * (dm.d / 16) * 64;
+  const int grid = (int)std::min<long long>((n16 + 255) / 256, 4096);
   const size_t smem = group_mfma_smem(dm.G, nc);
   dim3 g3((unsigned)((dm.Tq + 63) / 64) * dm.Hkv * dm.B);
   const auto* Qh = reinterpret_cast<const uint16_t*>(Q);
@@ -673,17 +687,17 @@ hipError_t launch_score_mfma_group(const Dims& dm, const void* Q, const float* k
 }
 
 size_t score_mfma_prefill_ws_bytes(const Dims& dm) {
-  const int nc = dm.ncand(dm.q_pos0 + dm.Tq - 1);
-  return (size_t)dm.B * (size_t)(nc > 0 ? nc : 1) * dm.H * 2 * dm.d * sizeof(uint16_t);
+  const int nc = max(1, dm.ncand(dm.q_pos0 + dm.Tq - 1));
+  return (size_t)dm.B * dm.H * ((nc + 15) / 16) * 16 * 2 * dm.d * sizeof(uint16_t);
 }
 
 hipError_t launch_score_mfma_prefill(const Dims& dm, const void* Q, const float* ksum,
                                      const float* ent, int32_t* idx, float* score, void* ws,
                                      hipStream_t st) {
   const int nc = max(1, dm.ncand(dm.q_pos0 + dm.Tq - 1));
-  uint16_t* ks = reinterpret_cast<uint16_t*>(ws);
-  const long long n8 = (long long)dm.B * nc * dm.H * (dm.d / 8);
-  const int grid = (int)std::min<long long>((n8 + 255) / 256, 4096);
+  uint4* ks = reinterpret_cast<uint4*>(ws);
+  const long long n16 = (long long)dm.B * dm.H * ((nc + 15) / 16) * (dm.d / 16) * 64;
+  const int grid = (int)std::min<long long>((n16 + 255) / 256, 4096);
   dim3 g3((unsigned)((dm.Tq + 63) / 64) * dm.H * dm.B);
   const auto* Qh = reinterpret_cast<const uint16_t*>(Q);
   // the register list holds 16, 32 or 64 entries: the smallest that holds K
