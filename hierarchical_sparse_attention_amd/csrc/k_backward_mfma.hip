@@ -322,6 +322,9 @@ constexpr int TPD = D + 16;     // dS tile: keys, then ds^ in column D, zeros up
 constexpr int kListMax = kChunk + 64 * 32;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
+// 16 bytes as a native vector, so that copies of a tile's rows stay in registers
+// (copies of HIP's uint4, a struct, went through scratch memory here)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // LDS transpose read (ds_read_b64_tr_b16): in each group of 16 lanes, lane
 // 4j + a gives the address of four consecutive 16-bit elements and lane 4a + b
@@ -385,9 +388,11 @@ struct KSmem {
 static_assert(sizeof(KSmem) <= 160 * 1024, "key-side LDS");
 static_assert(sizeof(KWave) >= kChunk * D * sizeof(float), "final reduction buffer");
 
+// A tile's rows are read 8 lanes to a row (one 128-byte line each), so every
+// quarter-wave touches two lines; they reach the MFMA operand layout through LDS.
 struct KTile {
-  uint4 qf[2][2], of[2][2];  // B operands: Q / dO of rows 16 hf + c, features 32 ds + 8g ..
-  uint4 sf[2][2];            // the scoring query's rows (Q-Cal; zero for own rows)
+  u32x4 qc[4], oc[4];  // Q / dO of tile rows 8 i + lane / 8, features 8 (lane % 8) .. + 8
+  u32x4 sc[4];         // the scoring query's rows (Q-Cal; zero for own rows)
   float aux[2], dvr[2];
   int rpos[2];   // position of the row, -1 beyond the tile's rows
   int slot[2];
@@ -447,19 +452,20 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
   auto load_tile = [&](int e0, int nr, bool own_rows) {
     KTile T;
 #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + min(8 * i + (lane >> 3), nr - 1);
+      const long long r = row_base + (long long)sm.rows[e] * dm.H;
+      const long long off = r * D + 8 * (lane & 7);
+      T.qc[i] = *reinterpret_cast<const u32x4*>(Q + off);
+      T.oc[i] = *reinterpret_cast<const u32x4*>(dO + off);
+      if constexpr (QCAL)
+        T.sc[i] = own_rows ? u32x4{0, 0, 0, 0} : *reinterpret_cast<const u32x4*>(Qs + off);
+    }
+#pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const bool v = 16 * hf + col < nr;
       const int e = e0 + min(16 * hf + col, nr - 1);
       const int pos = sm.rows[e];
-      const long long r = row_base + (long long)pos * dm.H;
-#pragma unroll
-      for (int ds = 0; ds < 2; ++ds) {
-        T.qf[hf][ds] = *reinterpret_cast<const uint4*>(Q + r * D + 32 * ds + 8 * gl);
-        T.of[hf][ds] = *reinterpret_cast<const uint4*>(dO + r * D + 32 * ds + 8 * gl);
-        if constexpr (QCAL)
-          T.sf[hf][ds] = own_rows ? make_uint4(0, 0, 0, 0)
-                                  : *reinterpret_cast<const uint4*>(Qs + r * D + 32 * ds + 8 * gl);
-      }
       T.aux[hf] = v ? sm.aux[e] : 0.f;
       T.dvr[hf] = sm.dvl[e];
       T.slot[hf] = sm.slotv[e];
@@ -470,33 +476,33 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
 
   // one 32-row tile; rows beyond nr get zero weights (their Q / dO are a valid row's)
   auto compute_tile = [&](const KTile& T, bool own_rows, floatx4 (&dkq)[4], float& dbp) {
-    if constexpr (QCAL) {
-      // the scoring query's rows (prefetched with the tile), needed for dk'
-      if (!own_rows) {
+    // the tile's rows to LDS (the scoring query's only for dk'), then the B
+    // operands Q / dO of rows 16 hf + c, features 32 ds + 8g .. back from there
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int ds = 0; ds < 2; ++ds)
-            *reinterpret_cast<uint4*>(&wv.ss[16 * hf + col][32 * ds + 8 * gl]) = T.sf[hf][ds];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 8 * i + (lane >> 3), c8 = 8 * (lane & 7);
+      *reinterpret_cast<u32x4*>(&wv.qs[rr][c8]) = T.qc[i];
+      *reinterpret_cast<u32x4*>(&wv.os[rr][c8]) = T.oc[i];
+      if constexpr (QCAL)
+        if (!own_rows) *reinterpret_cast<u32x4*>(&wv.ss[rr][c8]) = T.sc[i];
     }
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int ds = 0; ds < 2; ++ds) {
-        *reinterpret_cast<uint4*>(&wv.qs[16 * hf + col][32 * ds + 8 * gl]) = T.qf[hf][ds];
-        *reinterpret_cast<uint4*>(&wv.os[16 * hf + col][32 * ds + 8 * gl]) = T.of[hf][ds];
-      }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
+      uint4 qf[2], of[2];
+#pragma unroll
+      for (int ds = 0; ds < 2; ++ds) {
+        qf[ds] = *reinterpret_cast<const uint4*>(&wv.qs[16 * hf + col][32 * ds + 8 * gl]);
+        of[ds] = *reinterpret_cast<const uint4*>(&wv.os[16 * hf + col][32 * ds + 8 * gl]);
+      }
       floatx4 s[4], u[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         s[kb] = u[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ds = 0; ds < 2; ++ds) {
-          s[kb] = mfma(kf[kb * 2 + ds], T.qf[hf][ds], s[kb]);
-          u[kb] = mfma(vf[kb * 2 + ds], T.of[hf][ds], u[kb]);
+          s[kb] = mfma(kf[kb * 2 + ds], qf[ds], s[kb]);
+          u[kb] = mfma(vf[kb * 2 + ds], of[ds], u[kb]);
         }
       }
       floatx4 a[4], d[4];
