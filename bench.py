@@ -90,7 +90,7 @@ def write_traffic_record(fetch_csv, write_csv):
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     rec = {"sources_hash": sources_hash(), "copy_bytes": COPY_BYTES,
            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
-    for pat in ("k_vt_prep", "k_attend_mfma"):
+    for pat in ("k_kv_prep", "k_attend_mfma"):
         fb, wb = pick(fetch, pat), pick(write, pat)
         if fb is not None:
             rec["kernels"][pat] = {"fetch_bytes": fb * f_scale, "write_bytes": wb * w_scale}
@@ -234,7 +234,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     rec = read_traffic_record() if dominant == "attend_fuse" else None
     roof["traffic"] = rec["attend_call_bytes"] if rec else None
-    roof["kernel"] = ("hils_attend_fuse (k_vt_prep + k_attend_mfma)" if dominant == "attend_fuse"
+    roof["kernel"] = ("hils_attend_fuse (k_kv_prep + k_attend_mfma)" if dominant == "attend_fuse"
                       else dominant)
     roof["ms_per_launch"] = kern[dominant]
     roof["algorithmic"] = (cnt["attend_fuse"] if dominant == "attend_fuse"
