@@ -4,11 +4,12 @@
 // Fig. 3): for each selected chunk an independent softmax over its 64 keys,
 // weighted by exp(s^ - Lambda); the causal own chunk enters with its exact
 // log-mass. Organisation for CDNA4:
-//  * A workgroup (8 wavefronts) owns R query rows: Rq consecutive positions x the
-//    G query heads of one kv head. Their selections are counting-sorted in LDS
-//    into one row list per chunk, so the work is exactly the (row, chunk) pairs
-//    the selection asks for, packed into 16-row MFMA tiles.
-//  * Chunk u of the workgroup's union is owned by wavefront u mod 8, which loads
+//  * A workgroup of W wavefronts (12 for d = 64, 8 for d = 128) owns R query rows:
+//    Rq consecutive positions x the G query heads of one kv head. Their
+//    selections are counting-sorted in LDS into one row list per chunk, so the
+//    work is exactly the (row, chunk) pairs the selection asks for, packed into
+//    16-row MFMA tiles.
+//  * Chunk u of the workgroup's union is owned by wavefront u mod W, which loads
 //    that chunk's K and V^T MFMA fragments straight into registers (from the
 //    fragment copy through L2; no LDS staging and no workgroup barrier in the
 //    main loop) and runs every tile of the chunk: S^T = K Q^T
@@ -46,8 +47,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;  // 8 wavefronts: two per SIMD
-constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -58,7 +57,10 @@ struct Cfg {
   static constexpr int QP = D + 8;                  // LDS query row pitch (bf16)
   static constexpr int KF = 4 * (D / 32);           // K fragments (uint4) per lane per chunk
   static constexpr int VF = (D / 16) * 2;           // V^T fragments per lane per chunk
-  static constexpr bool PREFETCH = D == 64;         // second fragment set, LDS reads ahead
+  // wavefronts per workgroup: 12 for d = 64 (three per SIMD, in 168 registers),
+  // 8 for d = 128 (two per SIMD; its fragments alone take 128 registers)
+  static constexpr int THREADS = D == 64 ? 768 : 512;
+  static constexpr int WAVES = THREADS / 64;
   static constexpr int CH = (KF + VF) * 64;         // 16-byte words per chunk in the fragment copy
 };
 
@@ -400,7 +402,9 @@ __device__ __forceinline__ Smem carve(char* base, int R, int K, int ncr, int nlo
 }
 
 // In-place exclusive scan of n ints with kThreads threads; returns the total.
+template <int kThreads>
 __device__ __forceinline__ int block_exclusive_scan(int* a, int n, int* scratch) {
+  constexpr int kWaves = kThreads / 64;
   const int t = threadIdx.x;
   const int seg = (n + kThreads - 1) / kThreads;
   const int lo = min(n, t * seg), hi = min(n, lo + seg);
@@ -530,8 +534,9 @@ __device__ __forceinline__ void read_entry(const Smem& sm, int e0, int n, int e,
 }
 
 // All tiles of one selected chunk (fragments in f) for the rows that picked it,
-// NT independent tiles per step (two for d = 64, so their matrix-core and vector
-// work interleave). The next step's entries, query fragments and row normalisers
+// NT independent tiles per step (NT > 1 lets their matrix-core and vector work
+// interleave within a wave; the kernel runs NT = 1 and leaves that to the other
+// waves of the SIMD). The next step's entries, query fragments and row normalisers
 // are read from LDS while the current step runs. When the fast path's weight sum
 // is out of range on any lane (or `fast` is off) the step is redone with the
 // running-maximum tile.
@@ -587,12 +592,13 @@ __device__ __forceinline__ void run_chunk(const Frag<D>& f, const Smem& sm, int 
 }
 
 template <int D, bool SWA>
-__global__ __launch_bounds__(kThreads) void k_attend_mfma(
+__global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
     Dims dm, int R, int Rq, int ncr_cap, int nqb, int nct, const uint16_t* __restrict__ Q,
     const uint4* __restrict__ KVf, const float* __restrict__ vmax, const int32_t* __restrict__ idx,
     const float* __restrict__ score, uint16_t* __restrict__ O, float* __restrict__ lse_own,
     float* __restrict__ lse_tot) {
   using C = Cfg<D>;
+  constexpr int kThreads = C::THREADS, kWaves = C::WAVES;
   extern __shared__ __align__(16) char smem_raw[];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 15, gl = lane >> 4;
   const int G = dm.G, Ksel = dm.K, S = dm.S;
@@ -620,17 +626,14 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     return ((long long)b * dm.Tq + qi0 + rho / G) * dm.H + (long long)g * G + rho % G;
   };
 
-  // own-chunk items of this wave; for d = 64 the first fragment is requested now
-  // and lands during the set-up
+  // own-chunk items of this wave
   const int n_own = own_item_count(p0, S, span, G, Rv, loc_first, own_last);
   const int per_wave = (n_own + kWaves - 1) / kWaves;
   const int item0 = w * per_wave, item_end = min(n_own, item0 + per_wave);
-  Frag<D> f, f2;
+  Frag<D> f;
   int o_oc = 0, o_ra = 0, o_rb = 0, o_tl = 0;
   bool o_have = item0 < item_end && own_item(item0, p0, S, span, G, Rv, loc_first, own_last,
                                              &o_oc, &o_ra, &o_rb, &o_tl);
-  if (C::PREFETCH && o_have)
-    load_frag<D>(f, KVf, kvf_base + (long long)(o_oc) * C::CH);
 
   // ---- set-up: every global read of the set-up is issued first
   const int kgroups = (Ksel + 7) / 8;  // Rv * kgroups <= kThreads (see plan)
@@ -678,8 +681,8 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     sm.nz[c] = sm.cnt[c] > 0 ? 1 : 0;
   }
   __syncthreads();
-  block_exclusive_scan(sm.off, ncr, sm.misc);
-  const int nnz = block_exclusive_scan(sm.nz, ncr, sm.misc + 8);
+  block_exclusive_scan<kThreads>(sm.off, ncr, sm.misc);
+  const int nnz = block_exclusive_scan<kThreads>(sm.nz, ncr, sm.misc + 12);
   for (int c = t; c < ncr; c += kThreads) sm.cur[c] = sm.off[c];
   __syncthreads();
 #pragma unroll
@@ -753,7 +756,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     lds_q<D>(qo, sm.qs, *rho, *valid);
   };
   if constexpr (SWA) {
-    int fc = C::PREFETCH && o_have ? o_oc : -1;  // chunk whose fragments f holds
+    int fc = -1;  // chunk whose fragments f holds
     int oc = o_oc, ra = o_ra, rb = o_rb, tl = o_tl;
     for (int left = o_have ? item_end - item0 : 0; left > 0;) {
       int oc2 = oc, ra2 = ra, rb2 = rb, tl2 = tl;
@@ -780,9 +783,11 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     }
   }
   // ---- own chunks: causal, normalised (float accumulators for now)
-  for (int item = item0; !SWA && o_have; ) {
-    if (!C::PREFETCH)
+  for (int item = item0, fc = -1; !SWA && o_have; ) {
+    if (o_oc != fc) {
       load_frag<D>(f, KVf, kvf_base + (long long)(o_oc) * C::CH);
+      fc = o_oc;
+    }
     const int rho = o_ra + 16 * o_tl + col;
     const bool valid = rho < o_rb;
     const int nk = valid ? (int)(p0 + rho / G - (long long)o_oc * S) + 1 : 0;
@@ -800,16 +805,10 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
         for (int q = 0; q < 4; ++q) ar[acc_col(db, gl, q)] = o[db][q] * inv;
       if (gl == 0) sm.lown[rho] = (m2 + __log2f(z)) * kLn2;
     }
-    const int prev = o_oc;
     ++item;
     o_have = item < item_end && own_item(item, p0, S, span, G, Rv, loc_first, own_last, &o_oc,
                                          &o_ra, &o_rb, &o_tl);
-    if (C::PREFETCH && o_have && o_oc != prev)
-      load_frag<D>(f, KVf, kvf_base + (long long)(o_oc) * C::CH);
   }
-  // the first selected chunk's fragment is requested before the fusion set-up
-  if (!SWA && C::PREFETCH && w < nnz)
-    load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[w]) * C::CH);
   __syncthreads();
 
   // ---- fusion normaliser per row from the local log-mass and the score partials
@@ -887,28 +886,14 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
       if (two) win_next(oc, ra, rb, tl);
       left -= two ? 2 : 1;
     }
-    if (C::PREFETCH && w < nnz)
-      load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[w]) * C::CH);
   }
 
-  // ---- selected chunks: chunk u belongs to wavefront u mod 8; no barriers.
-  if (!C::PREFETCH) {
-    for (int u = w; u < nnz; u += kWaves) {
-      load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[u]) * C::CH);
-      run_chunk<D, 1>(f, sm, sm.cur[u], scale2, fast, fx_scale);
-    }
-  }
-  // d = 64: two fragment sets alternate, one consumed while the next chunk's lands
-  // in the other. The prefetches are unconditional (the chunk index is clamped at
-  // the end of the list) so that every path has the same loads in flight and
-  // waiting for the current set never waits for the one behind it.
-  for (int u = w; C::PREFETCH && u < nnz; u += 2 * kWaves) {
-    const int ua = sm.cur[min(u + kWaves, nnz - 1)], ub = sm.cur[min(u + 2 * kWaves, nnz - 1)];
-    load_frag<D>(f2, KVf, kvf_base + (long long)(ua) * C::CH);
-    run_chunk<D, 2>(f, sm, sm.cur[u], scale2, fast, fx_scale);
-    if (u + kWaves >= nnz) break;
-    load_frag<D>(f, KVf, kvf_base + (long long)(ub) * C::CH);
-    run_chunk<D, 2>(f2, sm, ua, scale2, fast, fx_scale);
+  // ---- selected chunks: chunk u belongs to wavefront u mod kWaves; no barriers.
+  // A wave waiting for its chunk's fragments is covered by the other waves of
+  // its SIMD (more waves per SIMD measured faster than a second fragment set).
+  for (int u = w; u < nnz; u += kWaves) {
+    load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[u]) * C::CH);
+    run_chunk<D, 1>(f, sm, sm.cur[u], scale2, fast, fx_scale);
   }
   __syncthreads();
 
@@ -956,7 +941,7 @@ bool plan(const Dims& dm, Plan* p) {
   if (b > limit) return false;
   // the set-up gives each thread at most one (row, 8 selections) item and four
   // 16-byte pieces of the query rows
-  if (r * ((dm.K + 7) / 8) > kThreads || r * (D / 8) > 4 * kThreads) return false;
+  if (r * ((dm.K + 7) / 8) > Cfg<D>::THREADS || r * (D / 8) > 4 * Cfg<D>::THREADS) return false;
   p->R = r;
   p->Rq = rq;
   p->ncr = ncr;
@@ -982,7 +967,8 @@ hipError_t launch_t(const Dims& dm, const Plan& p, const void* Q, const void* K,
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kfn, dim3(dm.B * p.nqb * dm.Hkv), dim3(kThreads), p.bytes, st, dm, p.R, p.Rq,
+  hipLaunchKernelGGL(kfn, dim3(dm.B * p.nqb * dm.Hkv), dim3(Cfg<D>::THREADS), p.bytes, st, dm,
+                     p.R, p.Rq,
                      p.ncr, p.nqb, p.nct, reinterpret_cast<const uint16_t*>(Q),
                      kvf, vmax, idx, score,
                      reinterpret_cast<uint16_t*>(O), lse_own, lse_tot);
