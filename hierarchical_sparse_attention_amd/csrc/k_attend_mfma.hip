@@ -231,15 +231,20 @@ __device__ __forceinline__ void tile_core(const Frag<D>& f, const uint4* qv, int
   }
 }
 
-// Scores, weights and values of one 16-row tile of a selected chunk, fast path:
-// u_j = 2^(s_j scale2) with no running maximum and no reference, since the
-// intra-chunk normalisation divides any common factor out. The caller checks
-// that the weight sum is in [2^-64, 2^64] and otherwise redoes the tile with
-// tile_core. The row sum comes out of the matrix core as a ones row of
-// the PV product, i.e. it is the sum of the bf16-rounded weights that multiply
-// the values.
+// Weight sums of the fast path that are safe to use.
+__device__ __forceinline__ bool z_ok(float z) { return z >= 0x1p-64f && z <= 0x1p64f; }
+
+// Scores, weights and values of one 16-row tile of a selected chunk. Fast path:
+// u_j = 2^(s_j scale2) with no running maximum, since the intra-chunk
+// normalisation divides any common factor out. The column sum z comes from the
+// matrix core as a ones row times the weights, i.e. it is the sum of the bf16
+// weights that multiply the values. A column whose sum falls outside
+// [2^-64, 2^64], or every column when `fast` is off, takes u_j =
+// 2^(s_j scale2 - m2) instead (m2 its log2-domain maximum, so the largest weight
+// is 1) before the values are multiplied. The choice is made per column: a row's
+// result does not depend on which other rows share its tile.
 template <int D>
-__device__ __forceinline__ void tile_ref(const Frag<D>& f, const uint4* qv, float scale2,
+__device__ __forceinline__ void tile_sel(const Frag<D>& f, const uint4* qv, float scale2, bool fast,
                                          floatx4* o, float* z) {
   floatx4 s[4];
 #pragma unroll
@@ -256,6 +261,29 @@ __device__ __forceinline__ void tile_ref(const Frag<D>& f, const uint4* qv, floa
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       pf[kb >> 1][(kb & 1) * 4 + r] = (__bf16)fast_exp2(s[kb][r] * scale2);
+  const __bf16 one = (__bf16)1.0f;
+  const bf16x8 ones = {one, one, one, one, one, one, one, one};
+  floatx4 zz = floatx4{0.f, 0.f, 0.f, 0.f};
+  zz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[0], zz, 0, 0, 0);
+  zz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[1], zz, 0, 0, 0);
+  const bool colbad = !fast || !z_ok(zz[0]);
+  if (__builtin_amdgcn_ballot_w64(colbad) != 0) {
+    float m = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    m = fmaxf(m, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                       fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
+    m = xmax_16_32(m);
+    const float nb = -scale2 * m;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (colbad) pf[kb >> 1][(kb & 1) * 4 + r] = (__bf16)fast_exp2(fmaf(s[kb][r], scale2, nb));
+    zz = floatx4{0.f, 0.f, 0.f, 0.f};
+    zz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[0], zz, 0, 0, 0);
+    zz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[1], zz, 0, 0, 0);
+  }
+  *z = zz[0];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
     o[db] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -264,12 +292,6 @@ __device__ __forceinline__ void tile_ref(const Frag<D>& f, const uint4* qv, floa
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.v[db * 2 + ks]), pf[ks], o[db],
                                                       0, 0, 0);
   }
-  const __bf16 one = (__bf16)1.0f;
-  const bf16x8 ones = {one, one, one, one, one, one, one, one};
-  floatx4 zz = floatx4{0.f, 0.f, 0.f, 0.f};
-  zz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[0], zz, 0, 0, 0);
-  zz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[1], zz, 0, 0, 0);
-  *z = zz[0];
 }
 
 // Sliding-window pass 1: column max (log2 domain, 0 for an empty column) and sum
@@ -512,8 +534,6 @@ __device__ __forceinline__ void accumulate_tile(const Smem& sm, const floatx4* o
   accumulate_fw<D>(sm, o, (int)(en & 0xFFFFu), fw);
 }
 
-// Weight sums of the fast path that are safe to use (see tile_ref).
-__device__ __forceinline__ bool z_ok(float z) { return z >= 0x1p-64f && z <= 0x1p64f; }
 
 // Row-list entry e of a chunk, clamped to the last entry so every LDS read is of
 // real data (a lane past the end computes a copy of the last row and does not
@@ -534,60 +554,32 @@ __device__ __forceinline__ void read_entry(const Smem& sm, int e0, int n, int e,
 }
 
 // All tiles of one selected chunk (fragments in f) for the rows that picked it,
-// NT independent tiles per step (NT > 1 lets their matrix-core and vector work
-// interleave within a wave; the kernel runs NT = 1 and leaves that to the other
-// waves of the SIMD). The next step's entries, query fragments and row normalisers
-// are read from LDS while the current step runs. When the fast path's weight sum
-// is out of range on any lane (or `fast` is off) the step is redone with the
-// running-maximum tile.
-template <int D, int NT>
+// one 16-row tile per step; the next step's entry, query fragments and row
+// normaliser are read from LDS while the current step runs.
+template <int D>
 __device__ __forceinline__ void run_chunk(const Frag<D>& f, const Smem& sm, int c, float scale2,
                                           bool fast, float fx_scale) {
   const int col = threadIdx.x & 15;
   const int e0 = sm.off[c], n = sm.cnt[c];
-  const int nstep = (n + 16 * NT - 1) / (16 * NT);
-  bool v[NT];
-  uint32_t en[NT];
-  float lw[NT], lm[NT];
-  uint4 q[NT][D / 32];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) read_entry<D>(sm, e0, n, 16 * i + col, &v[i], &en[i], &lw[i], &lm[i], q[i]);
+  const int nstep = (n + 15) / 16;
+  bool v;
+  uint32_t en;
+  float lw, lm;
+  uint4 q[D / 32];
+  read_entry<D>(sm, e0, n, col, &v, &en, &lw, &lm, q);
   for (int st = 0; st < nstep; ++st) {
-    bool vn[NT];
-    uint32_t enn[NT];
-    float lwn[NT], lmn[NT];
-    uint4 qn[NT][D / 32];
+    bool vn;
+    uint32_t enn;
+    float lwn, lmn;
+    uint4 qn[D / 32];
+    read_entry<D>(sm, e0, n, 16 * (st + 1) + col, &vn, &enn, &lwn, &lmn, qn);
+    floatx4 o[D / 16];
+    float z;
+    tile_sel<D>(f, q, scale2, fast, o, &z);
+    if (v) accumulate_tile<D>(sm, o, z, en, lw, lm, fx_scale);
+    v = vn, en = enn, lw = lwn, lm = lmn;
 #pragma unroll
-    for (int i = 0; i < NT; ++i)
-      read_entry<D>(sm, e0, n, 16 * NT * (st + 1) + 16 * i + col, &vn[i], &enn[i], &lwn[i],
-                    &lmn[i], qn[i]);
-    floatx4 o[NT][D / 16];
-    float z[NT];
-    bool bad = !fast;
-    if (fast) {
-#pragma unroll
-      for (int i = 0; i < NT; ++i) tile_ref<D>(f, q[i], scale2, o[i], &z[i]);
-      bool b = false;
-#pragma unroll
-      for (int i = 0; i < NT; ++i) b |= !z_ok(z[i]);
-      bad = __builtin_amdgcn_ballot_w64(b) != 0;
-    }
-    if (bad) {
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        float m2;
-        tile_core<D, false>(f, q[i], kChunk, scale2, o[i], &z[i], &m2);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-      if (v[i]) accumulate_tile<D>(sm, o[i], z[i], en[i], lw[i], lm[i], fx_scale);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      v[i] = vn[i], en[i] = enn[i], lw[i] = lwn[i], lm[i] = lmn[i];
-#pragma unroll
-      for (int ds = 0; ds < D / 32; ++ds) q[i][ds] = qn[i][ds];
-    }
+    for (int ds = 0; ds < D / 32; ++ds) q[ds] = qn[ds];
   }
 }
 
@@ -893,7 +885,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
   // its SIMD (more waves per SIMD measured faster than a second fragment set).
   for (int u = w; u < nnz; u += kWaves) {
     load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[u]) * C::CH);
-    run_chunk<D, 1>(f, sm, sm.cur[u], scale2, fast, fx_scale);
+    run_chunk<D>(f, sm, sm.cur[u], scale2, fast, fx_scale);
   }
   __syncthreads();
 

@@ -147,6 +147,32 @@ def test_attend_stage_large_logits(name):
     assert_close(host(lt), o["lse_tot"], TOL_F32, "lse_tot")
 
 
+@pytest.mark.parametrize("name", ["bf16_gqa_ragged", "bf16_d128_gqa4"])
+def test_attend_rows_independent_of_tile_mates(name):
+    """A row's output does not depend on the rows that share its MFMA tiles. With
+    every other query position scaled by 32 (logits of several hundred: those rows'
+    weight sums leave the no-maximum fast path), the unscaled rows equal a run
+    without scaling bit for bit (selection and scores held fixed), and the scaled
+    rows match the oracle."""
+    w, x = case(name)
+    say(f"[attend stage, tile mates] {name}")
+    o = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K)
+    Q2 = x["Q"].copy()
+    Q2[:, 1::2] *= 32.0                      # exact in bf16
+    idx = torch.from_numpy(o["idx"]).to(DEV)
+    score = torch.from_numpy(o["score"].astype(np.float32)).to(DEV)
+    K, V = dev(x["K"], w.dtype), dev(x["V"], w.dtype)
+    Oa, loa, _ = hsa.attend_fuse(dev(x["Q"], w.dtype), K, V, idx, score, w.S)
+    Ob, lob, ltb = hsa.attend_fuse(dev(Q2, w.dtype), K, V, idx, score, w.S)
+    torch.cuda.synchronize()
+    assert torch.equal(Oa[:, 0::2], Ob[:, 0::2])
+    assert torch.equal(loa[:, 0::2], lob[:, 0::2])
+    O_ref, lo_ref, lt_ref = oracle.attend_fuse(Q2, x["K"], x["V"], o["idx"], o["score"], w.S)
+    assert_close(host(Ob), O_ref, out_tol(w), "O")
+    assert_close(host(lob), lo_ref, TOL_F32, "lse_own")
+    assert_close(host(ltb), lt_ref, TOL_F32, "lse_tot")
+
+
 @pytest.mark.parametrize("name", ["bf16_gqa_ragged", "bf16_d128_gqa4", "f32_kmax"])
 def test_decode_rows_equal_prefill_rows(name):
     """A query scored alone (split path) selects what the prefill pass selected, bit for bit,
