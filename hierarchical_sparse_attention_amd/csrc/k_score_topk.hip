@@ -259,15 +259,26 @@ __global__ __launch_bounds__(64) void k_topk_merge_wave(Dims dm, const float* __
   const int n = dm.ncand(dm.q_pos0 + i);
   const int nv = lane < nsplit ? min(K, max(0, min(kSplit, n - lane * kSplit))) : 0;
   const long long base = ((long long)r * nsplit + min(lane, nsplit - 1)) * K;
+  // every load is issued before any is used (in bounds, masked after); the empty
+  // asm statements consume each value unconditionally, which keeps the compiler
+  // from moving a load into the branch of its select, where each one would wait
+  // for the previous
+  float sv[KM];
+  int cv[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const int jj = min(j, K - 1);
+    sv[j] = ws_s[base + jj];
+    cv[j] = ws_i[base + jj];
+  }
+#pragma unroll
+  for (int j = 0; j < KM; ++j) asm volatile("" ::"v"(sv[j]), "v"(cv[j]));
   uint32_t lh[KM], ll[KM];
 #pragma unroll
-  for (int j = 0; j < KM; ++j) {  // all loads in flight together (in bounds, masked after)
-    const int jj = min(j, K - 1);
-    const float sv = ws_s[base + jj];
-    const int cv = ws_i[base + jj];
+  for (int j = 0; j < KM; ++j) {
     const bool v = j < nv;
-    lh[j] = v ? order_bits(sv) : 0u;
-    ll[j] = v ? ~(uint32_t)cv : 0u;
+    lh[j] = v ? order_bits(sv[j]) : 0u;
+    ll[j] = v ? ~(uint32_t)cv[j] : 0u;
   }
   uint32_t wh = 0, wl = 0;
   const int cnt = wave_merge_lists<KM>(lh, ll, K, &wh, &wl);
