@@ -178,11 +178,11 @@ __device__ __forceinline__ void load_q(uint4* qv, const uint16_t* Q, long long r
                    : make_uint4(0, 0, 0, 0);
 }
 
-// Scores, softmax weights and values of one 16-row tile. keys >= nk are masked
-// (causal own chunk; nk = 64 for selected chunks). On return o[db] holds the
-// unnormalised O^T block, *z the column sum of the weights and *m2 the column max
-// of the log2-domain logits.
-template <int D, bool MASK>
+// Scores, softmax weights and values of one 16-row tile of the causal own chunk:
+// keys >= nk (per column) are masked. On return o[db] holds the unnormalised O^T
+// block, *z the column sum of the weights and *m2 the column max of the
+// log2-domain logits.
+template <int D>
 __device__ __forceinline__ void tile_core(const Frag<D>& f, const uint4* qv, int nk, float scale2,
                                           floatx4* o, float* z, float* m2) {
   const int g = (threadIdx.x & 63) >> 4;
@@ -195,19 +195,17 @@ __device__ __forceinline__ void tile_core(const Frag<D>& f, const uint4* qv, int
       s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.k[kb * (D / 32) + ds]),
                                                       as_bf16x8(qv[ds]), s[kb], 0, 0, 0);
   }
-  if (MASK) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * kb + 4 * g + r >= nk) s[kb][r] = -INFINITY;
-  }
+    for (int r = 0; r < 4; ++r)
+      if (16 * kb + 4 * g + r >= nk) s[kb][r] = -INFINITY;
   float m = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
   m = fmaxf(m, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
                      fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
   m = xmax_16_32(m);
-  if (MASK && m == -INFINITY) m = 0.f;  // padding lane: keeps every value finite
+  if (m == -INFINITY) m = 0.f;  // padding lane: keeps every value finite
   const float nb = -scale2 * m;
   float zz = 0.f;
   bf16x8 pf[2];
@@ -787,7 +785,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
     lds_q<D>(qo, sm.qs, rho, valid);
     floatx4 o[D / 16];
     float z, m2;
-    tile_core<D, true>(f, qo, nk, scale2, o, &z, &m2);
+    tile_core<D>(f, qo, nk, scale2, o, &z, &m2);
     if (valid) {
       const float inv = __builtin_amdgcn_rcpf(z);
       float* ar = reinterpret_cast<float*>(sm.acc + rho * C::AP);

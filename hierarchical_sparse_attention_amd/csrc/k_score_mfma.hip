@@ -185,18 +185,19 @@ __global__ __launch_bounds__(64, (D == 128 && KM == 16) ? 3 : 1) void k_score_mf
   for (int c0 = 0; c0 < nmax; c0 += 64) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
+      // a column past the candidates reads block 0 (in bounds): its score is
+      // never looked at, so the loads need no condition and stay in flight
+      // together
       const int chunk = c0 + 16 * nb + c;
       const bool cv = chunk < nmax;
       bf16x8 hi[D / 32], lo[D / 32];
       const uint4* src = ks + ks_frag<D>(dm, nc, b, h, cv ? (c0 >> 4) + nb : 0) + lane;
 #pragma unroll
       for (int ds = 0; ds < D / 32; ++ds) {
-        const uint4 uh = cv ? src[(2 * ds) * 64] : make_uint4(0, 0, 0, 0);
-        const uint4 ul = cv ? src[(2 * ds + 1) * 64] : make_uint4(0, 0, 0, 0);
-        hi[ds] = as_bf16x8(uh);
-        lo[ds] = as_bf16x8(ul);
+        hi[ds] = as_bf16x8(src[(2 * ds) * 64]);
+        lo[ds] = as_bf16x8(src[(2 * ds + 1) * 64]);
       }
-      const float e = cv ? ent[((long long)b * dm.NCcap + chunk) * dm.H + h] : 0.f;
+      const float e = ent[((long long)b * dm.NCcap + (cv ? chunk : 0)) * dm.H + h];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const floatx4 acc = score_block<D>(qa[mb], hi, lo);
@@ -227,20 +228,29 @@ __global__ __launch_bounds__(64, (D == 128 && KM == 16) ? 3 : 1) void k_score_mf
 #pragma unroll 1
     for (int sb = sb0; sb < 4; ++sb) {
       const float theta = top.s[KM - 1];
+      // the 16 reads are unconditional and combined without short-circuit, so
+      // they are all in flight together
+      float xv[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) xv[jj] = sS[lane][16 * sb + jj];
       uint32_t mask = 0;
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int j = 16 * sb + jj;
-        mask |= (j < lim && sS[lane][j] > theta) ? (1u << jj) : 0u;
-      }
+      for (int jj = 0; jj < 16; ++jj)
+        mask |= ((16 * sb + jj < lim) & (xv[jj] > theta)) ? (1u << jj) : 0u;
       int todo = __popc(mask);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) todo = max(todo, __shfl_xor(todo, o, 64));
+      // each insert's candidate is read one insert ahead
+      int jj = mask ? __ffs(mask) - 1 : 0;
+      float x = sS[lane][16 * sb + jj];
       for (int p = 0; p < todo; ++p) {
-        const int jj = mask ? __ffs(mask) - 1 : 0;
-        const float x = mask ? sS[lane][16 * sb + jj] : -INFINITY;
+        const bool have = mask != 0;
+        const int cj = jj;
         mask &= mask - 1;
-        top.insert(x, c0 + 16 * sb + jj);
+        jj = mask ? __ffs(mask) - 1 : 0;
+        const float xn = sS[lane][16 * sb + jj];
+        top.insert(have ? x : -INFINITY, c0 + 16 * sb + cj);
+        x = xn;
       }
     }
     __syncthreads();
@@ -313,16 +323,16 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
     for (int nb = 0; nb < 4; ++nb) {
       const int chunk = c0 + 16 * nb + c;
       const bool cv = chunk < nmax;
+      // a column past the candidates reads block 0 (in bounds); its score is
+      // never selected, so the loads need no condition
       const uint4* src = ks + ks_frag<D>(dm, nc, b, h, cv ? (c0 >> 4) + nb : 0) + lane;
       bf16x8 hi[D / 32], lo[D / 32];
 #pragma unroll
       for (int ds = 0; ds < D / 32; ++ds) {
-        const uint4 uh = cv ? src[(2 * ds) * 64] : make_uint4(0, 0, 0, 0);
-        const uint4 ul = cv ? src[(2 * ds + 1) * 64] : make_uint4(0, 0, 0, 0);
-        hi[ds] = as_bf16x8(uh);
-        lo[ds] = as_bf16x8(ul);
+        hi[ds] = as_bf16x8(src[(2 * ds) * 64]);
+        lo[ds] = as_bf16x8(src[(2 * ds + 1) * 64]);
       }
-      const float e = cv ? ent[((long long)b * dm.NCcap + chunk) * dm.H + h] : 0.f;
+      const float e = ent[((long long)b * dm.NCcap + (cv ? chunk : 0)) * dm.H + h];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const floatx4 a = score_block<D>(qa[mb], hi, lo);
@@ -367,20 +377,28 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
 #pragma unroll 1
     for (int sb = sb0; sb < 4; ++sb) {
       const float theta = top.s[KM - 1];
+      // unconditional reads, combined without short-circuit (all in flight together)
+      float xv[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) xv[jj] = gscore(16 * sb + jj);
       uint32_t mask = 0;
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int j = 16 * sb + jj;
-        mask |= (j < lim && gscore(j) > theta) ? (1u << jj) : 0u;
-      }
+      for (int jj = 0; jj < 16; ++jj)
+        mask |= ((16 * sb + jj < lim) & (xv[jj] > theta)) ? (1u << jj) : 0u;
       int todo = __popc(mask);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) todo = max(todo, __shfl_xor(todo, o, 64));
+      // each insert's candidate is read one insert ahead
+      int jj = mask ? __ffs(mask) - 1 : 0;
+      float x = gscore(16 * sb + jj);
       for (int q = 0; q < todo; ++q) {
-        const int jj = mask ? __ffs(mask) - 1 : 0;
-        const float x = mask ? gscore(16 * sb + jj) : -INFINITY;
+        const bool have = mask != 0;
+        const int cj = jj;
         mask &= mask - 1;
-        top.insert(x, c0 + 16 * sb + jj);
+        jj = mask ? __ffs(mask) - 1 : 0;
+        const float xn = gscore(16 * sb + jj);
+        top.insert(have ? x : -INFINITY, c0 + 16 * sb + cj);
+        x = xn;
       }
     }
     __syncthreads();
