@@ -574,7 +574,9 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         floatx4 dq = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) dq = mfma(lds_ktfrag(&sm.kc[0][0], ks, 16 * db), pf[ks], dq);
-        if (!QCAL && !own_rows) {
+        if constexpr (!QCAL) {
+          // unconditional (a local row has ds^ = 0, and 0 k' + dq = dq exactly), so
+          // the read needs no branch and wait of its own
           const float4 kb4 = *reinterpret_cast<const float4*>(&sm.kbv[16 * db + 4 * gl]);
           dq[0] = fmaf(dsh, kb4.x, dq[0]);
           dq[1] = fmaf(dsh, kb4.y, dq[1]);

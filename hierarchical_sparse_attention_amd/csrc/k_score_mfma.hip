@@ -364,9 +364,11 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
       float xs[16];
       int xc[16];
 #pragma unroll
+      for (int jj = 0; jj < 16; ++jj) xs[jj] = gscore(jj);  // unconditional: in flight together
+#pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const bool ok = jj < lim;
-        xs[jj] = ok ? gscore(jj) : -INFINITY;
+        xs[jj] = ok ? xs[jj] : -INFINITY;
         xc[jj] = ok ? jj : 0x7fffffff;
       }
       sort16(xs, xc);
@@ -428,20 +430,38 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
       }
   }
   __syncthreads();
-  // second pass: this head's score of every selected (position, chunk)
+  // per (position, bitmask word): selected chunks in the words before it, kept
+  // where the first pass's scores were
+  int* selp = reinterpret_cast<int*>(gsm2);  // [64][words]
+  for (int p = t; p < 64; p += 64 * G) {
+    int run = 0;
+    for (int x = 0; x < words; ++x) {
+      selp[p * words + x] = run;
+      run += __popc(selb[p * words + x]);
+    }
+  }
+  __syncthreads();
+  // second pass: this head's score of every selected (position, chunk); the
+  // bitmask and prefix reads are unconditional, so they are in flight together
   for (int c0 = 0; c0 < nmax; c0 += 64) {
     score_blocks(c0, [&](int mb, int nb, const floatx4& v) {
       const int ch = c0 + 16 * nb + c;
+      const int wi = min(ch / 32, words - 1);
+      uint32_t wv[4];
+      int pre[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int pos = 16 * mb + 4 * g + r;
-        if (pos >= npos || ch >= nmax) continue;
-        const uint32_t wv = selb[pos * words + ch / 32];
-        if ((wv >> (ch % 32)) & 1u) {
-          int rank = __popc(wv & ((1u << (ch % 32)) - 1u));
-          for (int x = 0; x < ch / 32; ++x) rank += __popc(selb[pos * words + x]);
-          score[(((long long)b * dm.Tq + i0 + pos) * dm.H + h) * K + rank] = v[r];
-        }
+        wv[r] = selb[pos * words + wi];
+        pre[r] = selp[pos * words + wi];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pos = 16 * mb + 4 * g + r;
+        const bool hit = (pos < npos) & (ch < nmax) & (((wv[r] >> (ch % 32)) & 1u) != 0u);
+        if (hit)
+          score[(((long long)b * dm.Tq + i0 + pos) * dm.H + h) * K + pre[r] +
+                __popc(wv[r] & ((1u << (ch % 32)) - 1u))] = v[r];
       }
     });
   }
