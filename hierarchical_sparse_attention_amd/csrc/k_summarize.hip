@@ -22,21 +22,57 @@ __global__ __launch_bounds__(kWave) void k_summarize(Dims dm, const void* __rest
 
   constexpr int VE = BF16 ? 8 : 4;  // elements per 16-byte vector
   constexpr int VPR = D / VE;       // vectors per key row
-  for (int v = lane; v < kChunk * VPR; v += kWave) {
+  constexpr int NV = kChunk * VPR / kWave;  // vectors per lane
+  static_assert(kChunk * VPR % kWave == 0 && D % kWave == 0, "tile shape");
+  // the landmark query of the first head is requested with the keys; each later
+  // head's while the previous head is being summarised (the head index is
+  // clamped, so the load needs no branch)
+  constexpr int QE = D / kWave;
+  auto ldql = [&](int hh, float* q) {
+    const long long sidx = ((long long)b * dm.NCcap + c) * dm.H + g * dm.G + hh;
+#pragma unroll
+    for (int k = 0; k < QE; ++k) q[k] = load_elem<BF16>(Ql, sidx * D + lane + k * kWave);
+  };
+  float qn[QE];
+  ldql(0, qn);
+  // every 16-byte load of the chunk's keys is issued before any is used
+  uint4 raw[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + i * kWave;
     const int j = v / VPR, col = (v % VPR) * VE;
     const long long off =
         (((long long)b * dm.Tcap + (long long)c * kChunk + j) * dm.Hkv + g) * D + col;
-    float tmp[VE];
-    load_row<BF16, VE>(K, off, tmp);
-#pragma unroll
-    for (int k = 0; k < VE; ++k) kt[j][col + k] = tmp[k];
+    raw[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(K) +
+                                             off * (BF16 ? 2 : 4));
   }
-  __syncthreads();
+  // consumed here, after every key load (nothing is scheduled across the
+  // barrier), so the compiler cannot sink the first query load below the keys
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < QE; ++k) asm volatile("" ::"v"(qn[k]));
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + i * kWave;
+    const int j = v / VPR, col = (v % VPR) * VE;
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (BF16) {
+        kt[j][col + 2 * k] = __uint_as_float(w[k] << 16);
+        kt[j][col + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      } else {
+        kt[j][col + k] = __uint_as_float(w[k]);
+      }
+    }
+  }
 
   for (int hh = 0; hh < dm.G; ++hh) {
     const int h = g * dm.G + hh;
     const long long sidx = ((long long)b * dm.NCcap + c) * dm.H + h;
-    for (int e = lane; e < D; e += kWave) qs[e] = load_elem<BF16>(Ql, sidx * D + e);
+#pragma unroll
+    for (int k = 0; k < QE; ++k) qs[lane + k * kWave] = qn[k];
+    ldql(min(hh + 1, dm.G - 1), qn);
     __syncthreads();
     float acc = 0.0f;
 #pragma unroll 16
