@@ -9,6 +9,23 @@
 namespace hils {
 namespace {
 
+// Sum or maximum over the 64 lanes with DPP row permutations (quad swaps, then
+// the half-row and row mirrors) and the permlane swaps between rows and halves,
+// with no LDS round trip. Every lane ends with the same value: each step
+// combines a lane's value with its partner's by a commutative operation.
+template <bool MAX>
+__device__ __forceinline__ float wave_all(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
 template <bool BF16, int D>
 __global__ __launch_bounds__(kWave) void k_summarize(Dims dm, const void* __restrict__ K,
                                                       const void* __restrict__ Ql, int c_begin,
@@ -74,21 +91,26 @@ __global__ __launch_bounds__(kWave) void k_summarize(Dims dm, const void* __rest
     for (int k = 0; k < QE; ++k) qs[lane + k * kWave] = qn[k];
     ldql(min(hh + 1, dm.G - 1), qn);
     __syncthreads();
-    float acc = 0.0f;
-#pragma unroll 16
-    for (int e = 0; e < D; ++e) acc = fmaf(qs[e], kt[lane][e], acc);
-    const float s = acc * dm.scale;             // landmark logit s'_j
-    const float m = wave_max(s);
-    const float L = m + logf(wave_sum(expf(s - m)));  // log-sum-exp
-    const float p = expf(s - L);                // p'_j
-    const float H = wave_sum(p * (L - s));      // -sum p log p, each term >= 0
+    // four interleaved partial sums keep the dependent chains short
+    float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int e = 0; e < D; e += 4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a4[u] = fmaf(qs[e + u], kt[lane][e + u], a4[u]);
+    const float s = ((a4[0] + a4[1]) + (a4[2] + a4[3])) * dm.scale;  // landmark logit s'_j
+    const float m = wave_all<true>(s);
+    const float L = m + logf(wave_all<false>(expf(s - m)));  // log-sum-exp
+    const float p = expf(s - L);                              // p'_j
+    const float H = wave_all<false>(p * (L - s));             // -sum p log p, terms >= 0
     pw[lane] = p;
     __syncthreads();
     for (int e = lane; e < D; e += kWave) {
-      float a = 0.0f;
-#pragma unroll 16
-      for (int j = 0; j < kChunk; ++j) a = fmaf(pw[j], kt[j][e], a);
-      ksum[sidx * D + e] = a;
+      float b4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int j = 0; j < kChunk; j += 4)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) b4[u] = fmaf(pw[j + u], kt[j + u][e], b4[u]);
+      ksum[sidx * D + e] = (b4[0] + b4[1]) + (b4[2] + b4[3]);
     }
     if (lane == 0) {
       ent[sidx] = H;
