@@ -19,21 +19,24 @@ struct Dims {
   long long q_pos0;
   float scale;
   int window;  // local branch: 0 = the query's own chunk; W > 0 = the last W keys
+  // The helpers below divide by the constant kChunk: the entry points reject any
+  // other S, and a constant divisor is a shift where a run-time 64-bit one is a
+  // long emulated division. Positions are never negative.
   // first key of the local branch of the query at absolute position pos
   __host__ __device__ __forceinline__ long long lstart(long long pos) const {
-    return window > 0 ? (pos >= window ? pos - window + 1 : 0) : pos - pos % S;
+    return window > 0 ? (pos >= window ? pos - window + 1 : 0) : pos - pos % kChunk;
   }
   // candidates are the chunks 0 .. ncand(pos) - 1, wholly before the local branch
   __host__ __device__ __forceinline__ int ncand(long long pos) const {
-    return (int)(lstart(pos) / S);
+    return (int)(lstart(pos) / kChunk);
   }
   // chunks the local branch of pos touches: lstart(pos) / S .. pos / S
   __host__ __device__ __forceinline__ int nlocal(long long pos) const {
-    return (int)(pos / S - lstart(pos) / S) + 1;
+    return (int)(pos / kChunk - lstart(pos) / kChunk) + 1;
   }
   // most local chunks of any query (partial slots per row in the decode and backward paths)
   __host__ __device__ __forceinline__ int nlocal_max() const {
-    return window > 0 ? window / S + 1 : 1;
+    return window > 0 ? window / kChunk + 1 : 1;
   }
 };
 

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void k_attend_rows(Dims dm, const void* __rest
   load_row<BF16, D>(Q, r * D, q);
 
   // local branch: keys l0 .. pos, chunk by chunk (one chunk for the own-chunk branch)
-  const long long l0 = dm.lstart(pos), c_lo = l0 / dm.S, c_hi = pos / dm.S;
+  const long long l0 = dm.lstart(pos), c_lo = l0 / kChunk, c_hi = pos / kChunk;
   auto local_logit = [&](long long cc, bool* v) {
     const long long j = cc * dm.S + lane;
     *v = j >= l0 && j <= pos;
@@ -332,8 +332,8 @@ __global__ __launch_bounds__(64) void k_decode_partial(Dims dm, const void* __re
     key0 = (long long)c * dm.S;
     nk = kChunk;
   } else {  // local chunk l0 / S + slot - K, keys from max(l0, its start) to min(pos, its end)
-    const long long l0 = dm.lstart(pos), cc = l0 / dm.S + (slot - dm.K);
-    if (cc > pos / dm.S) {
+    const long long l0 = dm.lstart(pos), cc = l0 / kChunk + (slot - dm.K);
+    if (cc > pos / kChunk) {
       if (lane == 0) part_l[po] = -INFINITY;
       return;
     }

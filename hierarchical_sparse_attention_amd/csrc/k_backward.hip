@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows(Dims dm, const void* __restric
   const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
   const long long pos = dm.q_pos0 + i;
   const int ncand = dm.ncand(pos);
-  const long long l0 = dm.lstart(pos), c_lo = l0 / dm.S, c_hi = pos / dm.S;
+  const long long l0 = dm.lstart(pos), c_lo = l0 / kChunk, c_hi = pos / kChunk;
   const long long kv_stride = (long long)dm.Hkv * D;
   const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
   const float tau = dm.scale, Lambda = lse_tot[r];

@@ -651,7 +651,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         sm.rows[e] = (int)pos;
         sm.aux[e] = ws_D[r];
         sm.dvl[e] = lse_tot[r];
-        sm.slotv[e] = e < nown ? dm.K + (c - (int)(dm.lstart(pos) / dm.S)) : -1;
+        sm.slotv[e] = e < nown ? dm.K + (c - (int)(dm.lstart(pos) / kChunk)) : -1;
       }
       for (int e = t; e < ns; e += kKThreads) {
         const int4 rec = srec[lsrc + s0 + e];
