@@ -271,9 +271,10 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
                                                   const float* __restrict__ ws_D,
                                                   const int* __restrict__ off,
                                                   int4* __restrict__ srec) {
-  extern __shared__ uint32_t lfill[];
+  extern __shared__ __align__(16) uint32_t lfill[];
   const int NC = dm.Tkv / dm.S;
   constexpr int W = kLBlk / 32;
+  static_assert(W % 4 == 0, "bitmap rows are read 16 bytes at a time");
   uint32_t* lb = lfill;                                   // [NC][W] bitmap of the block
   int* lo = reinterpret_cast<int*>(lfill + (size_t)NC * W);  // [NC] entry offsets
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -295,9 +296,20 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
     const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
     const int c = idx[r * dm.K + k];
     if (c < 0 || c >= dm.ncand(dm.q_pos0 + i) || c >= NC) continue;
+    // the chunk's bitmap row in four 16-byte reads (all in flight), then the
+    // selected positions before ii counted in registers
     const int wd = ii / 32;
-    int rank = __popc(lb[c * W + wd] & ((1u << (ii % 32)) - 1u));
-    for (int ww = 0; ww < wd; ++ww) rank += __popc(lb[c * W + ww]);
+    const uint4* row4 = reinterpret_cast<const uint4*>(lb + c * W);
+    uint32_t wv[W];
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const uint4 u = row4[q];
+      wv[4 * q] = u.x, wv[4 * q + 1] = u.y, wv[4 * q + 2] = u.z, wv[4 * q + 3] = u.w;
+    }
+    int rank = 0;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww)
+      rank += ww < wd ? __popc(wv[ww]) : (ww == wd ? __popc(wv[ww] & ((1u << (ii % 32)) - 1u)) : 0);
     // one 16-byte record: position, alpha, D, slot
     srec[ebase + lo[c] + rank] = make_int4(i, __float_as_int(expf(score[r * dm.K + k] - lse_tot[r])),
                                           __float_as_int(ws_D[r]), k);
