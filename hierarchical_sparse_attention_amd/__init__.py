@@ -191,6 +191,8 @@ def attend_fuse(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Te
     lse_own = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if lse_own is None else lse_own
     lse_tot = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if lse_tot is None else lse_tot
     _need(O, "O", Q.shape, Q.dtype)
+    _need(lse_own, "lse_own", (B, Tq, H), torch.float32)
+    _need(lse_tot, "lse_tot", (B, Tq, H), torch.float32)
     dims = make_dims(B, Tq, Tkv, H, Hkv, d, S, K_sel, _dtype_code(Q), q_pos0, scale, Tcap, 0,
                      window=window)
     ws, n = _workspace(dims, OP_ATTEND_FUSE, dev)
@@ -223,12 +225,23 @@ def backward(Q, K, V, Ql, ksum, ent, lse_l, idx, score, lse_tot, O, dO, S: int =
     Hkv = K.shape[2]
     K_sel = idx.shape[-1]
     NC = Ql.shape[1]
-    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (Ql, "Ql"), (O, "O"), (dO, "dO")):
-        _need(t, n, dtype=Q.dtype)
+    _dtype_code(Q)
+    _need(Q, "Q")
+    _need(K, "K", (B, T, Hkv, d), Q.dtype)
+    _need(V, "V", (B, T, Hkv, d), Q.dtype)
+    if NC < T // S:
+        raise ValueError(f"Ql holds {NC} chunks, fewer than the {T // S} of the sequence")
+    _need(Ql, "Ql", (B, NC, H, d), Q.dtype)
+    _need(O, "O", tuple(Q.shape), Q.dtype)
+    _need(dO, "dO", tuple(Q.shape), Q.dtype)
     if Qs is not None:
         _need(Qs, "Qs", tuple(Q.shape), Q.dtype)
     _need(ksum, "ksum", (B, NC, H, d), torch.float32)
+    _need(ent, "ent", (B, NC, H), torch.float32)
+    _need(lse_l, "lse_l", (B, NC, H), torch.float32)
     _need(idx, "idx", (B, T, H, K_sel), torch.int32)
+    _need(score, "score", (B, T, H, K_sel), torch.float32)
+    _need(lse_tot, "lse_tot", (B, T, H), torch.float32)
     dev = Q.device
     dQ, dK, dV, dQl = (torch.empty_like(x) for x in (Q, K, V, Ql))
     dQs = None if Qs is None else torch.empty_like(Q)

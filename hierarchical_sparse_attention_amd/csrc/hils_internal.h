@@ -122,6 +122,37 @@ __device__ __forceinline__ float chunk_score(const float* q, const float* kbar, 
   return fmaf(acc, scale, ent);
 }
 
+// Whether entry k of a row's selection list counts: its id c is a candidate of
+// the row (0 <= c < ncand) and larger than every earlier entry of the row
+// (prev_max, the largest earlier id; -1 before the first). Padding, ids outside
+// the candidates and repeated or out-of-order ids contribute nothing, neither
+// output nor score; a list made by the selection (ascending, padding last)
+// counts every real entry. Counted entries are distinct, so per-chunk row lists
+// built from them hold a row at most once.
+__host__ __device__ __forceinline__ bool entry_counts(int c, int ncand, int prev_max) {
+  return c >= 0 && c < ncand && c > prev_max;
+}
+
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Largest value held by the lanes below this one (exclusive prefix maximum
+// across the wavefront; `lo` for lane 0).
+__device__ __forceinline__ int wave_excl_max(int v, int lo) {
+  const int lane = threadIdx.x & 63;
+  int x = __shfl_up(v, 1, 64);
+  x = lane == 0 ? lo : x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x = max(x, y);
+  }
+  return x;
+}
+
 // Top-K order key: (score descending, chunk id ascending). Branch-free, so rank
 // loops keep their loads in flight.
 __device__ __forceinline__ bool topk_before(float sa, int ca, float sb, int cb) {

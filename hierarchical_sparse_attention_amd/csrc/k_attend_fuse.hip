@@ -88,10 +88,14 @@ __global__ __launch_bounds__(256) void k_attend_rows(Dims dm, const void* __rest
   }
   const float l_own = m_loc + logf(z_loc);
 
-  // inter-chunk normaliser over the selected scores and the own log-mass
+  // inter-chunk normaliser over the counted entries' scores and the own log-mass
+  // (lane k holds entry k; see entry_counts)
   const int Ksel = dm.K;
+  const int cl = lane < Ksel ? idx[r * Ksel + lane] : -1;
+  const bool counted = lane < Ksel && entry_counts(cl, ncand, wave_excl_max(cl, -1));
+  const uint64_t cmask = __ballot(counted);
   float sc = -INFINITY;
-  if (lane < Ksel) sc = score[r * Ksel + lane];
+  if (counted) sc = score[r * Ksel + lane];
   const float mx = fmaxf(wave_max(sc), l_own);
   const float Lambda = mx + logf(wave_sum(lane < Ksel ? expf(sc - mx) : 0.0f) + expf(l_own - mx));
 
@@ -107,9 +111,9 @@ __global__ __launch_bounds__(256) void k_attend_rows(Dims dm, const void* __rest
   }
 
   for (int k = 0; k < Ksel; ++k) {
-    const int c = idx[r * Ksel + k];  // wave-uniform
-    if (c < 0 || c >= ncand) continue;  // pads; ids outside the candidate range are ignored
-    const float sh = score[r * Ksel + k];
+    if (((cmask >> k) & 1ull) == 0ull) continue;  // wave-uniform: entries that do not count
+    const int c = __builtin_amdgcn_readlane(cl, k);
+    const float sh = lane_bcast(sc, k);
     const long long j = (long long)c * dm.S + lane;
     const float s = key_logit<BF16, D>(K, kv_base + j * kv_stride, q, dm.scale);
     const float m = wave_max(s);
@@ -315,8 +319,10 @@ __global__ __launch_bounds__(64) void k_decode_partial(Dims dm, const void* __re
   const long long po = r * (dm.K + dm.nlocal_max()) + slot;
   const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
   const long long kv_stride = (long long)dm.Hkv * D;
-  // query and selection read together (unconditionally, indices in bounds)
+  // query and selection read together (unconditionally, indices in bounds); lane
+  // l < slot holds the row's earlier entry l, which decides whether this one counts
   const int c = idx[r * dm.K + min(slot, dm.K - 1)];
+  const int cprev = lane < min(slot, dm.K) ? idx[r * dm.K + lane] : -1;
 #pragma unroll
   for (int x = 0; x < D / kWave; ++x) {
     if (BF16) qh[lane + kWave * x] = reinterpret_cast<const uint16_t*>(Q)[r * D + lane + kWave * x];
@@ -324,8 +330,9 @@ __global__ __launch_bounds__(64) void k_decode_partial(Dims dm, const void* __re
   }
   long long key0;
   int nk;
+  const int prev_max = wave_max_int(cprev);
   if (slot < dm.K) {
-    if (c < 0 || c >= ncand) {  // padding slot: no mass
+    if (!entry_counts(c, ncand, prev_max)) {  // padding or an entry that does not count: no mass
       if (lane == 0) part_l[po] = -INFINITY;
       return;
     }

@@ -22,7 +22,8 @@
 //    Lambda is known a second pass adds exp(s_j - Lambda) v_j of every window
 //    key into the row's accumulator.
 //  * Contributions are added into the LDS row accumulators with integer atomics
-//    in a fixed-point format scaled from max|V| over the workgroup's chunks.
+//    in a fixed-point format scaled, row by row, from max|V| over the chunks that
+//    row reads (its counted selections and its local chunks).
 //    Integer addition is associative, so the result does not depend on which
 //    wavefront finishes first: the output is bitwise deterministic.
 //  * K and V are first rewritten (k_kv_prep), chunk by chunk, as the MFMA
@@ -382,6 +383,11 @@ struct Smem {
   int* nz;
   float* lown;    // own-chunk log-mass, then the own weight in fixed-point units
   float* lam;     // Lambda times log2(e)
+  float* lamx;    // Lambda times log2(e) minus the row's fixed-point shift
+  int* fsh;       // per row: fixed-point shift (the row's units are 2^-fsh)
+  uint32_t* rvm;  // per row: max |V| over the chunks it reads (float bits)
+  float* vx;      // per chunk: max |V|
+  int* gmx;       // per (row, group of 8 entries): largest id of the group
   float* pm;      // per (row, group of 8 slots): max score and sum of exp(score - max)
   float* pz;
   int* nsel;      // per row: number of terms added to its fixed-point accumulator
@@ -396,8 +402,8 @@ __host__ __device__ inline size_t up16(size_t x) { return (x + 15) & ~(size_t)15
 template <int D>
 __host__ __device__ inline size_t smem_bytes(int R, int K, int ncr, int nloc) {
   return up16((size_t)R * Cfg<D>::AP * 4) + up16((size_t)R * Cfg<D>::QP * 2) +
-         2 * up16((size_t)R * K * 4) + 4 * up16((size_t)(ncr + 1) * 4) + 3 * up16((size_t)R * 4) +
-         2 * up16((size_t)R * ((K + 7) / 8) * 4) + up16((size_t)R * nloc * 8) + 32 * 4;
+         2 * up16((size_t)R * K * 4) + 5 * up16((size_t)(ncr + 1) * 4) + 6 * up16((size_t)R * 4) +
+         3 * up16((size_t)R * ((K + 7) / 8) * 4) + up16((size_t)R * nloc * 8) + 32 * 4;
 }
 
 template <int D>
@@ -413,6 +419,11 @@ __device__ __forceinline__ Smem carve(char* base, int R, int K, int ncr, int nlo
   s.nz = reinterpret_cast<int*>(base); base += up16((ncr + 1) * 4);
   s.lown = reinterpret_cast<float*>(base); base += up16(R * 4);
   s.lam = reinterpret_cast<float*>(base); base += up16(R * 4);
+  s.lamx = reinterpret_cast<float*>(base); base += up16(R * 4);
+  s.fsh = reinterpret_cast<int*>(base); base += up16(R * 4);
+  s.rvm = reinterpret_cast<uint32_t*>(base); base += up16(R * 4);
+  s.vx = reinterpret_cast<float*>(base); base += up16((ncr + 1) * 4);
+  s.gmx = reinterpret_cast<int*>(base); base += up16((size_t)R * ((K + 7) / 8) * 4);
   s.pm = reinterpret_cast<float*>(base); base += up16((size_t)R * ((K + 7) / 8) * 4);
   s.pz = reinterpret_cast<float*>(base); base += up16((size_t)R * ((K + 7) / 8) * 4);
   s.nsel = reinterpret_cast<int*>(base); base += up16(R * 4);
@@ -499,7 +510,8 @@ __device__ __forceinline__ int own_item_count(long long p0, int S, int span, int
 }
 
 // Adds one tile's normalised, fused-weighted output to its rows' fixed-point
-// accumulators: weight 2^(lw2 - lam2) / z (lw2 = s^ log2 e, lam2 = Lambda log2 e).
+// accumulators: weight 2^(lw2 - lamx) / z (lw2 = s^ log2 e, lamx = Lambda log2 e
+// minus the row's fixed-point shift, so the weight is alpha in the row's units).
 // The conversion to an integer is one fma: for |v| < 2^22, v + 1.5 2^23 is a
 // float whose bit pattern is 0x4B400000 + round(v). Two neighbouring columns a, b
 // share one 64-bit word and one 64-bit integer atomic: the word gains
@@ -526,11 +538,15 @@ __device__ __forceinline__ void accumulate_fw(const Smem& sm, const floatx4* o, 
 
 template <int D>
 __device__ __forceinline__ void accumulate_tile(const Smem& sm, const floatx4* o, float z,
-                                                uint32_t en, float lw2, float lam2,
-                                                float fx_scale) {
-  const float fw = fast_exp2(lw2 - lam2) * __builtin_amdgcn_rcpf(z) * fx_scale;
+                                                uint32_t en, float lw2, float lamx) {
+  const float fw = fast_exp2(lw2 - lamx) * __builtin_amdgcn_rcpf(z);
   accumulate_fw<D>(sm, o, (int)(en & 0xFFFFu), fw);
 }
+
+// Entry word of a chunk's row list: workgroup row (bits 0-15), selection slot
+// (bits 16-21), and bit 30 set when the row's values are too large for the
+// fast-path weights (max |V| >= 2^50).
+constexpr uint32_t kEntrySlow = 1u << 30;
 
 
 // Row-list entry e of a chunk, clamped to the last entry so every LDS read is of
@@ -544,7 +560,7 @@ __device__ __forceinline__ void read_entry(const Smem& sm, int e0, int n, int e,
   *en = sm.ent[ec];
   *lw = sm.lw[ec];
   const int rho = (int)(*en & 0xFFFFu);
-  *lm = sm.lam[rho];
+  *lm = sm.lamx[rho];
   const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds)
@@ -555,8 +571,7 @@ __device__ __forceinline__ void read_entry(const Smem& sm, int e0, int n, int e,
 // one 16-row tile per step; the next step's entry, query fragments and row
 // normaliser are read from LDS while the current step runs.
 template <int D>
-__device__ __forceinline__ void run_chunk(const Frag<D>& f, const Smem& sm, int c, float scale2,
-                                          bool fast, float fx_scale) {
+__device__ __forceinline__ void run_chunk(const Frag<D>& f, const Smem& sm, int c, float scale2) {
   const int col = threadIdx.x & 15;
   const int e0 = sm.off[c], n = sm.cnt[c];
   const int nstep = (n + 15) / 16;
@@ -573,8 +588,8 @@ __device__ __forceinline__ void run_chunk(const Frag<D>& f, const Smem& sm, int 
     read_entry<D>(sm, e0, n, 16 * (st + 1) + col, &vn, &enn, &lwn, &lmn, qn);
     floatx4 o[D / 16];
     float z;
-    tile_sel<D>(f, q, scale2, fast, o, &z);
-    if (v) accumulate_tile<D>(sm, o, z, en, lw, lm, fx_scale);
+    tile_sel<D>(f, q, scale2, (en & kEntrySlow) == 0u, o, &z);
+    if (v) accumulate_tile<D>(sm, o, z, en, lw, lm);
     v = vn, en = enn, lw = lwn, lm = lmn;
 #pragma unroll
     for (int ds = 0; ds < D / 32; ++ds) q[ds] = qn[ds];
@@ -628,8 +643,9 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
   // ---- set-up: every global read of the set-up is issued first
   const int kgroups = (Ksel + 7) / 8;  // Rv * kgroups <= kThreads (see plan)
   const bool has_item = t < Rv * kgroups;
-  const int it_rho = t / kgroups, it_k0 = (t % kgroups) * 8;
-  const int it_own = dm.ncand(p0 + it_rho / G);  // the row's candidates: chunks below this
+  const int it_rho = t / kgroups, it_kg = t % kgroups, it_k0 = it_kg * 8;
+  const long long it_pos = p0 + it_rho / G;
+  const int it_own = dm.ncand(it_pos);  // the row's candidates: chunks below this
   int cs[8];
   float ss[8];
   {
@@ -654,17 +670,49 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
   const float vpre = t <= own_last ? vmx[t] : 0.f;
 
   for (int c = t; c <= ncr; c += kThreads) sm.cnt[c] = 0;
-  for (int rho = t; rho < Rv; rho += kThreads) sm.nsel[rho] = 0;
+  for (int c = t; c <= own_last; c += kThreads) sm.vx[c] = c == t ? vpre : vmx[c];
+  for (int rho = t; rho < Rv; rho += kThreads) {
+    sm.nsel[rho] = 0;
+    sm.rvm[rho] = 0u;
+  }
+  if (has_item) {
+    int m8 = -1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m8 = max(m8, cs[j]);
+    sm.gmx[t] = m8;  // t = it_rho * kgroups + it_kg
+  }
   __syncthreads();
   stq(0, qv0), stq(1, qv1), stq(2, qv2), stq(3, qv3);
+  // the entries that count (entry_counts: a candidate above every earlier entry
+  // of the row); the others lose their score too, so they leave Lambda alone
+  uint32_t okm = 0u;
+  float rv = 0.f;  // max |V| over the chunks of the row this thread sees
+  if (has_item) {
+    int prev = -1;
+    for (int x = 0; x < it_kg; ++x) prev = max(prev, sm.gmx[it_rho * kgroups + x]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      okm |= entry_counts(cs[j], it_own, prev) ? 1u << j : 0u;
+      prev = max(prev, cs[j]);
+    }
+    if (it_kg == 0)  // the row's local chunks
+      for (int c = (int)(dm.lstart(it_pos) / S); c <= (int)(it_pos / S); ++c) rv = fmaxf(rv, sm.vx[c]);
+  }
   int nmine = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (cs[j] >= 0 && cs[j] < it_own) {
+  for (int j = 0; j < 8; ++j) {
+    if ((okm >> j) & 1u) {
       atomicAdd(&sm.cnt[cs[j]], 1);
+      rv = fmaxf(rv, sm.vx[cs[j]]);
       ++nmine;
+    } else {
+      ss[j] = -INFINITY;
     }
-  if (nmine) atomicAdd(&sm.nsel[it_rho], nmine);
+  }
+  if (has_item) {
+    if (nmine) atomicAdd(&sm.nsel[it_rho], nmine);
+    atomicMax(&sm.rvm[it_rho], __float_as_uint(rv));  // non-negative floats order as their bits
+  }
   __syncthreads();
   for (int c = t; c < ncr; c += kThreads) {
     sm.off[c] = sm.cnt[c];
@@ -675,13 +723,18 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
   const int nnz = block_exclusive_scan<kThreads>(sm.nz, ncr, sm.misc + 12);
   for (int c = t; c < ncr; c += kThreads) sm.cur[c] = sm.off[c];
   __syncthreads();
+  {
+    // fast path: weight sums below 2^64 and values below 2^50 keep every partial
+    // product of the PV step finite; the row's flag travels in its entries
+    const uint32_t slow = has_item && __uint_as_float(sm.rvm[it_rho]) >= 0x1p50f ? kEntrySlow : 0u;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (cs[j] >= 0 && cs[j] < it_own) {
-      const int p = atomicAdd(&sm.cur[cs[j]], 1);
-      sm.ent[p] = (uint32_t)it_rho | ((uint32_t)(it_k0 + j) << 16);
-      sm.lw[p] = ss[j] * kLog2e;
-    }
+    for (int j = 0; j < 8; ++j)
+      if ((okm >> j) & 1u) {
+        const int p = atomicAdd(&sm.cur[cs[j]], 1);
+        sm.ent[p] = (uint32_t)it_rho | ((uint32_t)(it_k0 + j) << 16) | slow;
+        sm.lw[p] = ss[j] * kLog2e;
+      }
+  }
   if (has_item) {  // partial log-sum-exp of this group of scores (padding holds -inf)
     float m8 = -INFINITY;
 #pragma unroll
@@ -695,31 +748,18 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
     sm.pz[t] = z8;
   }
   __syncthreads();
-  // compacted list of non-empty chunks (chunk c goes to slot nz[c]) and the bound
-  // max|V| over every chunk this workgroup reads
-  float vm = 0.f;
-  for (int c = t; c <= own_last; c += kThreads) {
-    const bool used = c >= loc_first || sm.cnt[c] > 0;
-    if (c < ncr && sm.cnt[c] > 0) sm.cur[sm.nz[c]] = c;
-    if (used) vm = fmaxf(vm, c == t ? vpre : vmx[c]);
+  // compacted list of non-empty chunks (chunk c goes to slot nz[c])
+  for (int c = t; c < ncr; c += kThreads)
+    if (sm.cnt[c] > 0) sm.cur[sm.nz[c]] = c;
+  // per-row fixed point: every partial sum of a row is a sub-convex combination
+  // of the values of the chunks it reads, so its magnitude is at most that
+  // row's max|V| < 2^ex, mapped below 2^21 (each term then fits the one-fma
+  // conversion of accumulate_fw); the row's units are 2^-(21 - ex)
+  for (int rho = t; rho < Rv; rho += kThreads) {
+    int ex = 0;
+    frexpf(fmaxf(__uint_as_float(sm.rvm[rho]), 1e-30f), &ex);
+    sm.fsh[rho] = 21 - ex;
   }
-  vm = wave_max(vm);
-  if (lane == 0) reinterpret_cast<float*>(sm.misc)[16 + w] = vm;
-  __syncthreads();
-  float vmax_wg = 0.f;
-#pragma unroll
-  for (int x = 0; x < kWaves; ++x)
-    vmax_wg = fmaxf(vmax_wg, reinterpret_cast<float*>(sm.misc)[16 + x]);
-  // fixed point: every partial sum is a sub-convex combination of values, so its
-  // magnitude is at most max|V| < 2^ex, mapped below 2^21 (each term then fits
-  // the one-fma conversion of accumulate_tile)
-  int ex = 0;
-  frexpf(fmaxf(vmax_wg, 1e-30f), &ex);
-  const float fx_scale = ldexpf(1.0f, 21 - ex);
-  const float fx_inv = ldexpf(1.0f, ex - 21);
-  // fast path: weight sums below 2^64 and values below 2^50 keep every partial
-  // product of the PV step finite
-  const bool fast = vmax_wg < 0x1p50f;
 
   // ---- sliding window, pass 1: per (row, local chunk) maximum and sum. Items are
   // taken two at a time when they share a chunk, so two independent tiles run
@@ -824,8 +864,10 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
       if (zg > 0.f) z += zg * expf(sm.pm[rho * kgroups + kg] - mx);
     }
     const float lam = mx + logf(z);
+    const int sh = sm.fsh[rho];
     sm.lam[rho] = lam * kLog2e;
-    sm.lown[rho] = expf(lo - lam) * fx_scale;
+    sm.lamx[rho] = lam * kLog2e - (float)sh;
+    sm.lown[rho] = ldexpf(expf(lo - lam), sh);
     const long long r = row_of(rho);
     if (lse_own) lse_own[r] = lo;
     if (lse_tot) lse_tot[r] = lam;
@@ -840,8 +882,8 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
       *a = 0;
     } else {
       const float2 v = *reinterpret_cast<const float2*>(a);
-      const float w = sm.lown[rho];
-      *a = (int64_t)(int)(v.y * w) * 4294967296LL + (int64_t)(int)(v.x * w);
+      const float w = sm.lown[rho];  // rounded to the nearest unit, as the other terms are
+      *a = (int64_t)__float2int_rn(v.y * w) * 4294967296LL + (int64_t)__float2int_rn(v.x * w);
     }
   }
   __syncthreads();
@@ -871,7 +913,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
         tile_abs<D>(f, qo[i], klo[i], khi[i], scale2, valid[i] ? sm.lam[rho[i]] : 0.f, o[i]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (valid[i]) accumulate_fw<D>(sm, o[i], rho[i], fx_scale);
+        if (valid[i]) accumulate_fw<D>(sm, o[i], rho[i], ldexpf(1.0f, sm.fsh[rho[i]]));
       oc = oc2, ra = ra2, rb = rb2, tl = tl2;
       if (two) win_next(oc, ra, rb, tl);
       left -= two ? 2 : 1;
@@ -883,7 +925,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
   // its SIMD (more waves per SIMD measured faster than a second fragment set).
   for (int u = w; u < nnz; u += kWaves) {
     load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[u]) * C::CH);
-    run_chunk<D>(f, sm, sm.cur[u], scale2, fast, fx_scale);
+    run_chunk<D>(f, sm, sm.cur[u], scale2);
   }
   __syncthreads();
 
@@ -892,6 +934,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
     const int rho = x / (D / 8), c8 = x % (D / 8);
     const int* ar = sm.acc + rho * C::AP;
     const uint64_t off = (uint64_t)sm.nsel[rho] * ((uint64_t)kMagic * 4294967297ull);
+    const int sh = sm.fsh[rho];
     // features 8 c8 .. 8 c8 + 7 are columns acc_col(db, g, 0..3) for g = 2 (c8 & 1),
     // 2 (c8 & 1) + 1 and db = c8 / 2; each pair of columns is one 64-bit word
     const int db = c8 >> 1, g0 = 2 * (c8 & 1);
@@ -902,8 +945,8 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
       const int64_t xw = (int64_t)(*reinterpret_cast<const uint64_t*>(ar + acc_col(db, g, r)) - off);
       const int a = (int)(uint32_t)xw;
       const int b = (int)((xw - a) >> 32);
-      ow[y] = (uint32_t)f32_to_bf16_bits((float)a * fx_inv) |
-              ((uint32_t)f32_to_bf16_bits((float)b * fx_inv) << 16);
+      ow[y] = (uint32_t)f32_to_bf16_bits(ldexpf((float)a, -sh)) |
+              ((uint32_t)f32_to_bf16_bits(ldexpf((float)b, -sh)) << 16);
     }
     *reinterpret_cast<uint4*>(O + row_of(rho) * D + c8 * 8) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
   }

@@ -128,9 +128,13 @@ __global__ __launch_bounds__(256) void k_bwd_rows(Dims dm, const void* __restric
     Dsum += wave_sum(s > -INFINITY ? expf(s - Lambda) * u : 0.0f);
   }
   float rk = 0.0f, ak = 0.0f, mk = 0.0f;  // lane k holds slot k's values
+  // lane k holds entry k and whether it counts (entry_counts)
+  const int cl = lane < Ksel ? idx[r * Ksel + lane] : -1;
+  const uint64_t cmask =
+      __ballot(lane < Ksel && entry_counts(cl, ncand, wave_excl_max(cl, -1)));
   for (int k = 0; k < Ksel; ++k) {
-    const int c = idx[r * Ksel + k];
-    if (c < 0 || c >= ncand) continue;
+    if (((cmask >> k) & 1ull) == 0ull) continue;  // wave-uniform
+    const int c = __builtin_amdgcn_readlane(cl, k);
     logits((long long)c * dm.S, kChunk, s, u);
     m = wave_max(s);
     const float lz = m + logf(wave_sum(expf(s - m)));
@@ -158,8 +162,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(Dims dm, const void* __restric
     add_keys(cc * dm.S, nk, s > -INFINITY ? expf(s - Lambda) * (u - Dsum) : 0.0f);
   }
   for (int k = 0; k < Ksel; ++k) {
-    const int c = idx[r * Ksel + k];
-    if (c < 0 || c >= ncand) {
+    const int c = __builtin_amdgcn_readlane(cl, k);
+    if (((cmask >> k) & 1ull) == 0ull) {  // wave-uniform
       if (lane == 0) ws_dsh[r * Ksel + k] = 0.0f;
       continue;
     }
@@ -192,17 +196,22 @@ __global__ void k_fill_zero(uint32_t* __restrict__ p, long long n) {
 
 __global__ void k_sel_bitmap(Dims dm, const int32_t* __restrict__ idx, uint32_t* __restrict__ bm,
                              int words) {
-  const long long n = (long long)dm.B * dm.Tq * dm.H * dm.K;
+  const long long n = (long long)dm.B * dm.Tq * dm.H;
   const int NC = dm.Tkv / dm.S;
-  for (long long x = blockIdx.x * (long long)blockDim.x + threadIdx.x; x < n;
-       x += (long long)gridDim.x * blockDim.x) {
-    const int c = idx[x];
-    const long long r = x / dm.K;
+  // one thread per row: its entries in order, so entry_counts sees the earlier ids
+  for (long long r = blockIdx.x * (long long)blockDim.x + threadIdx.x; r < n;
+       r += (long long)gridDim.x * blockDim.x) {
     const int h = (int)(r % dm.H);
     const int i = (int)((r / dm.H) % dm.Tq);
     const int b = (int)(r / ((long long)dm.H * dm.Tq));
-    if (c < 0 || c >= dm.ncand(dm.q_pos0 + i) || c >= NC) continue;
-    atomicOr(&bm[(((long long)b * dm.H + h) * NC + c) * words + i / 32], 1u << (i % 32));
+    const int nc = min(dm.ncand(dm.q_pos0 + i), NC);
+    int seen = -1;
+    for (int k = 0; k < dm.K; ++k) {
+      const int c = idx[r * dm.K + k];
+      if (entry_counts(c, nc, seen))
+        atomicOr(&bm[(((long long)b * dm.H + h) * NC + c) * words + i / 32], 1u << (i % 32));
+      seen = max(seen, c);
+    }
   }
 }
 
@@ -219,12 +228,16 @@ __global__ __launch_bounds__(256) void k_sel_bitmap_lds(Dims dm, const int32_t* 
   for (int x = threadIdx.x; x < NC * wpw; x += blockDim.x) lb[x] = 0u;
   __syncthreads();
   const int i0 = w0 * 32, ni = min(nw * 32, dm.Tq - i0);
-  for (int x = threadIdx.x; x < ni * dm.K; x += blockDim.x) {
-    const int ii = x / dm.K, k = x % dm.K;
+  for (int ii = threadIdx.x; ii < ni; ii += blockDim.x) {  // one thread per row
     const int i = i0 + ii;
-    const int c = idx[(((long long)b * dm.Tq + i) * dm.H + h) * dm.K + k];
-    if (c < 0 || c >= dm.ncand(dm.q_pos0 + i) || c >= NC) continue;
-    atomicOr(&lb[c * wpw + ii / 32], 1u << (ii % 32));
+    const int nc = min(dm.ncand(dm.q_pos0 + i), NC);
+    const int32_t* ir = idx + (((long long)b * dm.Tq + i) * dm.H + h) * dm.K;
+    int seen = -1;
+    for (int k = 0; k < dm.K; ++k) {
+      const int c = ir[k];
+      if (entry_counts(c, nc, seen)) atomicOr(&lb[c * wpw + ii / 32], 1u << (ii % 32));
+      seen = max(seen, c);
+    }
   }
   __syncthreads();
   for (int x = threadIdx.x; x < NC * nw; x += blockDim.x) {

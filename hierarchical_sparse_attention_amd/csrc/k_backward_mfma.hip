@@ -125,15 +125,23 @@ __global__ __launch_bounds__(256) void k_dq_reduce(Dims dm, long long rows,
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  int seen = -1;  // largest selection id so far (entry_counts)
   for (int k0 = 0; k0 < NS; k0 += KM) {
     uint4 v[KM];
     bool ok[KM];
+    int cq[KM];
 #pragma unroll
     for (int q = 0; q < KM; ++q) {
       const int k = min(k0 + q, NS - 1);
-      const int c = k < Ksel ? idx[r * Ksel + k] : -1;
-      ok[q] = k0 + q < NS && (k < Ksel ? (c >= 0 && c < own && c < NC) : k - Ksel < nloc);
+      cq[q] = k < Ksel ? idx[r * Ksel + k] : -1;
       v[q] = *reinterpret_cast<const uint4*>(pr + (long long)k * D);
+    }
+#pragma unroll
+    for (int q = 0; q < KM; ++q) {
+      const int k = min(k0 + q, NS - 1);
+      ok[q] = k0 + q < NS &&
+              (k < Ksel ? entry_counts(cq[q], min(own, NC), seen) : k - Ksel < nloc);
+      if (k0 + q < NS && k < Ksel) seen = max(seen, cq[q]);
     }
 #pragma unroll
     for (int q = 0; q < KM; ++q) {
@@ -153,6 +161,7 @@ __global__ __launch_bounds__(256) void k_dq_reduce(Dims dm, long long rows,
     const long long b = r / ((long long)dm.Tq * dm.H);
     const int h = (int)(r % dm.H);
     constexpr int KS = 8;
+    int seen_s = -1;
     for (int k0 = 0; k0 < Ksel; k0 += KS) {
       float dsv[KS];
       float4 ka[KS], kb[KS];
@@ -160,7 +169,8 @@ __global__ __launch_bounds__(256) void k_dq_reduce(Dims dm, long long rows,
       for (int q = 0; q < KS; ++q) {
         const int k = min(k0 + q, Ksel - 1);
         const int c = idx[r * Ksel + k];
-        const bool okq = k0 + q < Ksel && c >= 0 && c < own && c < NC;
+        const bool okq = k0 + q < Ksel && entry_counts(c, min(own, NC), seen_s);
+        if (k0 + q < Ksel) seen_s = max(seen_s, c);
         dsv[q] = okq ? ws_dsh[r * Ksel + k] : 0.f;
         const float* kp = ksum + (((b * dm.NCcap + (okq ? c : 0)) * dm.H + h) * D + c8 * 8);
         ka[q] = *reinterpret_cast<const float4*>(kp);
@@ -212,10 +222,17 @@ __global__ __launch_bounds__(256) void k_sel_count(Dims dm, int nblk, const int3
   for (int x = threadIdx.x; x < NC; x += blockDim.x) lcnt[x] = 0;
   __syncthreads();
   const int i0 = blk * kLBlk, ni = min(kLBlk, dm.Tq - i0);
-  for (int x = threadIdx.x; x < ni * dm.K; x += blockDim.x) {
-    const int i = i0 + x / dm.K, k = x % dm.K;
-    const int c = idx[(((long long)b * dm.Tq + i) * dm.H + h) * dm.K + k];
-    if (c >= 0 && c < dm.ncand(dm.q_pos0 + i) && c < NC) atomicAdd(&lcnt[c], 1);
+  // one thread per row: its entries in order, so entry_counts sees the earlier ids
+  for (int ii = threadIdx.x; ii < ni; ii += blockDim.x) {
+    const int i = i0 + ii;
+    const int n = min(dm.ncand(dm.q_pos0 + i), NC);
+    const int32_t* ir = idx + (((long long)b * dm.Tq + i) * dm.H + h) * dm.K;
+    int seen = -1;
+    for (int k = 0; k < dm.K; ++k) {
+      const int c = ir[k];
+      if (entry_counts(c, n, seen)) atomicAdd(&lcnt[c], 1);
+      seen = max(seen, c);
+    }
   }
   __syncthreads();
   int* out = cnt + ((long long)b * dm.H + h) * NC * nblk;
@@ -283,36 +300,49 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
   for (int c = threadIdx.x; c < NC; c += blockDim.x) lo[c] = off[(bh * NC + c) * nblk + blk];
   __syncthreads();
   const int i0 = blk * kLBlk, ni = min(kLBlk, dm.Tq - i0);
-  for (int x = threadIdx.x; x < ni * dm.K; x += blockDim.x) {
-    const int ii = x / dm.K, k = x % dm.K, i = i0 + ii;
-    const int c = idx[(((long long)b * dm.Tq + i) * dm.H + h) * dm.K + k];
-    if (c >= 0 && c < dm.ncand(dm.q_pos0 + i) && c < NC)
-      atomicOr(&lb[c * W + ii / 32], 1u << (ii % 32));
+  // one thread per row: its entries in order, so entry_counts sees the earlier ids
+  for (int ii = threadIdx.x; ii < ni; ii += blockDim.x) {
+    const int i = i0 + ii;
+    const int n = min(dm.ncand(dm.q_pos0 + i), NC);
+    const int32_t* ir = idx + (((long long)b * dm.Tq + i) * dm.H + h) * dm.K;
+    int seen = -1;
+    for (int k = 0; k < dm.K; ++k) {
+      const int c = ir[k];
+      if (entry_counts(c, n, seen)) atomicOr(&lb[c * W + ii / 32], 1u << (ii % 32));
+      seen = max(seen, c);
+    }
   }
   __syncthreads();
   const long long ebase = bh * (long long)dm.Tq * dm.K;
-  for (int x = threadIdx.x; x < ni * dm.K; x += blockDim.x) {
-    const int ii = x / dm.K, k = x % dm.K, i = i0 + ii;
+  for (int ii = threadIdx.x; ii < ni; ii += blockDim.x) {
+    const int i = i0 + ii;
     const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
-    const int c = idx[r * dm.K + k];
-    if (c < 0 || c >= dm.ncand(dm.q_pos0 + i) || c >= NC) continue;
-    // the chunk's bitmap row in four 16-byte reads (all in flight), then the
-    // selected positions before ii counted in registers
+    const int n = min(dm.ncand(dm.q_pos0 + i), NC);
+    const float lt = lse_tot[r], Dr = ws_D[r];
     const int wd = ii / 32;
-    const uint4* row4 = reinterpret_cast<const uint4*>(lb + c * W);
-    uint32_t wv[W];
+    int seen = -1;
+    for (int k = 0; k < dm.K; ++k) {
+      const int c = idx[r * dm.K + k];
+      const bool ok = entry_counts(c, n, seen);
+      seen = max(seen, c);
+      if (!ok) continue;
+      // the chunk's bitmap row in four 16-byte reads (all in flight), then the
+      // selected positions before ii counted in registers
+      const uint4* row4 = reinterpret_cast<const uint4*>(lb + c * W);
+      uint32_t wv[W];
 #pragma unroll
-    for (int q = 0; q < W / 4; ++q) {
-      const uint4 u = row4[q];
-      wv[4 * q] = u.x, wv[4 * q + 1] = u.y, wv[4 * q + 2] = u.z, wv[4 * q + 3] = u.w;
+      for (int q = 0; q < W / 4; ++q) {
+        const uint4 u = row4[q];
+        wv[4 * q] = u.x, wv[4 * q + 1] = u.y, wv[4 * q + 2] = u.z, wv[4 * q + 3] = u.w;
+      }
+      int rank = 0;
+#pragma unroll
+      for (int ww = 0; ww < W; ++ww)
+        rank += ww < wd ? __popc(wv[ww]) : (ww == wd ? __popc(wv[ww] & ((1u << (ii % 32)) - 1u)) : 0);
+      // one 16-byte record: position, alpha, D, slot
+      srec[ebase + lo[c] + rank] = make_int4(i, __float_as_int(expf(score[r * dm.K + k] - lt)),
+                                            __float_as_int(Dr), k);
     }
-    int rank = 0;
-#pragma unroll
-    for (int ww = 0; ww < W; ++ww)
-      rank += ww < wd ? __popc(wv[ww]) : (ww == wd ? __popc(wv[ww] & ((1u << (ii % 32)) - 1u)) : 0);
-    // one 16-byte record: position, alpha, D, slot
-    srec[ebase + lo[c] + rank] = make_int4(i, __float_as_int(expf(score[r * dm.K + k] - lse_tot[r])),
-                                          __float_as_int(ws_D[r]), k);
   }
 }
 

@@ -143,15 +143,26 @@ hils_status hils_score_topk(const hils_dims* dims, const void* Q, const float* k
  */
 
 /*
+ * Selection lists passed to hils_attend_fuse and hils_backward. Entry k of a
+ * row's list (idx[b,i,h,k], with its score) counts only when its id c is a
+ * candidate of the row (0 <= c < n_i, the candidates of hils_score_topk) and
+ * is larger than every earlier entry k' < k of the same row. Any other entry
+ * (padding -1, an id outside the candidates, a repeated or out-of-order id)
+ * contributes nothing: neither its chunk's output nor its score. The lists
+ * hils_score_topk writes (ascending, padding last) count every real entry.
+ * No input makes a kernel read outside its buffers.
+ */
+
+/*
  * Intra-chunk attention and inter-chunk fusion (note §5.3 hierarchical
  * softmax; Tide Fig. 3). For row (b,i,h) at position p:
- *   each selected chunk c (idx >= 0): o_c = softmax_j(scale q.k_j) V over its S keys;
+ *   each counted entry c (see above): o_c = softmax_j(scale q.k_j) V over its S keys;
  *   local branch, keys l_p .. p (l_p as in hils_score_topk: the own chunk's
  *   start, or the sliding window's first key): o_own = softmax over those keys
  *   and its log-mass l_own;
  *   Lambda = log(sum_c exp(score_c) + exp(l_own));
  *   O = sum_c exp(score_c - Lambda) o_c + exp(l_own - Lambda) o_own.
- * Selected ids outside the row's candidates are ignored.
+ * Sums over c run over the counted entries.
  * lse_own (l_own) and lse_tot (Lambda) may be NULL; hils_backward needs them.
  */
 hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K,
@@ -176,7 +187,8 @@ hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K
  * (the caller back-propagates dQs into its calibration weights and adds it to
  * the query's gradient). Qs and dQs are both NULL (scores from Q, dQ holds
  * both parts) or both set. Requires a prefill layout (q_pos0 == 0,
- * Tq == Tkv, Tkv % S == 0). Deterministic: no floating-point atomics.
+ * Tq == Tkv, Tkv % S == 0). idx entries count by the rule above, as in the
+ * forward. Deterministic: no floating-point atomics.
  */
 hils_status hils_backward(const hils_dims* dims, const void* Q, const void* K, const void* V,
                           const void* Ql, const float* ksum, const float* ent,

@@ -32,6 +32,12 @@
 //     chunk (not itself); landmark tokens hold no key/value;
 //   * ties in the score rank go to the lower chunk index; rows with fewer
 //     than K candidates select all of them (idx padded with -1);
+//   * a selection list handed to the attention or the backward counts entry k
+//     only when its id is a candidate of the row (0 <= c < n_cand) and larger
+//     than every earlier entry of the row; any other entry (padding, an id
+//     outside the candidates, a repeated or out-of-order id) contributes
+//     nothing, neither its output nor its score. Lists made by the selection
+//     (ascending, padded last) count every real entry;
 //   * the scale 1/sqrt(d) is applied in all three softmaxes (page 4 Fig. 3
 //     caption says it is only omitted there for readability).
 //
@@ -159,16 +165,31 @@ struct RowFwd {
   std::vector<double> o_own, O;
 };
 
+// Entries of a selection list that count (see the readings above): a candidate
+// id above every earlier entry of the row. counted[k] says whether entry k does.
+void counted_entries(const Shape& sh, const int* idx_row, long pos, std::vector<bool>& counted) {
+  counted.assign(sh.Ksel, false);
+  const long n = sh.n_cand(pos);
+  long seen = -1;  // largest id among the earlier entries
+  for (int k = 0; k < sh.Ksel; ++k) {
+    const long c = idx_row[k];
+    counted[k] = c >= 0 && c < n && c > seen;
+    seen = std::max(seen, c);
+  }
+}
+
 // idx_row / score_row: the row's Ksel selected ids (-1 = pad) and their scores.
 void row_forward(const Shape& sh, const double* Q, const double* K, const double* V,
                  const int* idx_row, const double* score_row, int b, int i, int h, RowFwd& f) {
   const int d = sh.d, S = sh.S, g = h / (sh.H / sh.Hkv);
   const long pos = sh.q_pos0 + i;
   const double* q = sh.q(Q, b, i, h);
+  std::vector<bool> counted;
+  counted_entries(sh, idx_row, pos, counted);
   f.chunks.clear(); f.logit.clear(); f.m.clear(); f.o.clear();
   for (int k = 0; k < sh.Ksel; ++k) {
     const int c = idx_row[k];
-    if (c < 0) continue;
+    if (!counted[k]) continue;
     f.chunks.push_back(c);
     f.logit.push_back(score_row[k]);
     std::vector<double> oc(d);
@@ -407,9 +428,11 @@ void oracle_backward(int B, int Tq, int Tkv, long q_pos0, int H, int Hkv, int d,
         const double* q = sh.q(Q, b, i, h);
         const double* qs = Qs ? sh.q(Qs, b, i, h) : q;
         std::vector<double> sc(Ksel);
+        std::vector<bool> counted;
+        counted_entries(sh, idx + r * Ksel, pos, counted);
         for (int k = 0; k < Ksel; ++k) {
           const int c = idx[r * Ksel + k];
-          if (c < 0) { sc[k] = -INFINITY; continue; }
+          if (!counted[k]) { sc[k] = -INFINITY; continue; }
           const long sidx = ((long)b * NC + c) * H + h;
           sc[k] = tau * dot(qs, ksum.data() + sidx * d, d) + ent[sidx];
         }

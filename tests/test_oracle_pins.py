@@ -581,3 +581,56 @@ def test_backward_masks_restrict_work():
         G = w.H // w.Hkv
         np.testing.assert_allclose(part[3][0, c, g * G:(g + 1) * G],
                                    full[3][0, c, g * G:(g + 1) * G], rtol=1e-12, atol=1e-14)
+
+
+def test_selection_lists_count_only_ascending_candidates():
+    """A selection list handed to the attention or the backward counts entry k only
+    when its id is a candidate of the row and above every earlier entry; the others
+    (a repeated id, an out-of-order id, an id past the candidates, a negative id)
+    contribute nothing. Pinned against the same lists with those entries replaced by
+    padding: the oracle's forward, and the dense autograd restatement for the
+    gradients."""
+    w, x, f = _bwd_case()
+    rng = np.random.default_rng(3)
+    idx = f["idx"].copy()
+    score = f["score"].copy()
+    fi, fs = idx.reshape(-1, w.K), score.reshape(-1, w.K)
+    H = w.H
+    ncand = ((np.arange(fi.shape[0]) // H) % w.T) // w.S
+    for r in range(fi.shape[0]):
+        nv = int((fi[r] >= 0).sum())
+        if nv < 2:
+            continue
+        kind = r % 5
+        k = int(rng.integers(0, nv - 1))
+        if kind == 1:
+            fi[r, k + 1], fs[r, k + 1] = fi[r, k], fs[r, k]
+        elif kind == 2:
+            fi[r, [k, k + 1]] = fi[r, [k + 1, k]]
+            fs[r, [k, k + 1]] = fs[r, [k + 1, k]]
+        elif kind == 3:
+            fi[r, k] = ncand[r]
+        elif kind == 4:
+            fi[r, k] = -3
+    clean = idx.copy()
+    fc = clean.reshape(-1, w.K)
+    for r in range(fc.shape[0]):
+        seen = -1
+        for k in range(w.K):
+            c = int(fi[r, k])
+            if not (0 <= c < ncand[r] and c > seen):
+                fc[r, k] = -1
+            seen = max(seen, c)
+    assert (clean != idx).any()
+    O1, lo1, lt1 = oracle.attend_fuse(x["Q"], x["K"], x["V"], idx, score, w.S)
+    sc_clean = np.where(clean >= 0, score, -np.inf)
+    O2, lo2, lt2 = oracle.attend_fuse(x["Q"], x["K"], x["V"], clean, sc_clean, w.S)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(lt1, lt2)
+    g = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], idx, x["dO"], w.S)
+    t = {k: torch.from_numpy(x[k].astype(np.float64)).requires_grad_(True)
+         for k in ("Q", "K", "V", "Ql")}
+    O = torch_hils(t["Q"], t["K"], t["V"], t["Ql"], clean, w.S)
+    (O * torch.from_numpy(x["dO"].astype(np.float64))).sum().backward()
+    for name, gg in zip(("Q", "K", "V", "Ql"), g):
+        np.testing.assert_allclose(gg, t[name].grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
