@@ -12,7 +12,7 @@ import torch
 import hierarchical_sparse_attention_amd as hsa
 import oracle
 import synth
-from hils_testutil import TOL_BF16, TOL_F32, assert_close, compare_selection, say
+from hils_testutil import TOL_BF16, TOL_F32, assert_close, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -65,7 +65,7 @@ def test_decode_with_host_resident_cache(K_sel, window):
     q = x["Q"][:, s:s + 1]
     oidx, osc, ogap = oracle.score_topk(q, oks, oent, w.S, K_sel, q_pos0=p, window=window)
     oO, _, olt = oracle.attend_fuse(q, Kc, Vc, oidx, osc, w.S, q_pos0=p, window=window)
-    excl, eq = compare_selection(host_run[-1][0].numpy(), oidx, ogap, K_sel)
+    eq = np.all(host_run[-1][0].numpy() == oidx, axis=-1)
     assert eq.all()
     assert_close(host_run[-1][2].float().numpy(), oO, TOL_BF16, "O")
     assert_close(host_run[-1][3].numpy(), olt, TOL_F32, "lse_tot")

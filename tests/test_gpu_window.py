@@ -11,7 +11,8 @@ import torch
 import hierarchical_sparse_attention_amd as hsa
 import oracle
 import synth
-from hils_testutil import (TOL_BF16, TOL_F32, TOL_GRAD_BF16, assert_close, compare_selection,
+from hils_testutil import (TOL_BF16, TOL_F32, TOL_GRAD_BF16, all_scores, assert_close,
+                           compare_selection,
                            say)
 
 pytestmark = pytest.mark.gpu
@@ -60,8 +61,11 @@ def case(name):
     return _cache[name]
 
 
-def check_forward(w, x, f, o):
-    excl, eq = compare_selection(host(f["idx"]), o["idx"], o["gap"], w.K)
+def check_forward(w, x, f, o, W, group=False):
+    excl, eq = compare_selection(host(f["idx"]), o["idx"], o["gap"], w.K,
+                                 lambda d: all_scores(x["Q"], o["ksum"], o["ent"], w.S, d,
+                                                      group_hkv=w.Hkv if group else None,
+                                                      window=W))
     say(f"  near-tie rows excluded: {int(excl.sum())}/{excl.size}")
     sel = eq[..., None].repeat(w.K, -1) & (o["idx"] >= 0)
     assert_close(host(f["score"])[sel], o["score"][sel], TOL_F32, "score")
@@ -79,7 +83,7 @@ def test_forward_window(name):
     f = hsa.forward(t["Q"], t["K"], t["V"], t["Ql"], w.K, w.S, window=W)
     torch.cuda.synchronize()
     o = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K, window=W)
-    check_forward(w, x, f, o)
+    check_forward(w, x, f, o, W)
     if name == "w_cover":
         assert np.all(host(f["idx"]) == -1)
 
@@ -108,7 +112,7 @@ def test_forward_window_group_max(name):
     f = hsa.forward(t["Q"], t["K"], t["V"], t["Ql"], w.K, w.S, group=True, window=W)
     torch.cuda.synchronize()
     o = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K, group=True, window=W)
-    check_forward(w, x, f, o)
+    check_forward(w, x, f, o, W, group=True)
 
 
 @pytest.mark.parametrize("name", ["w_bf16_gqa_k32", "w_bf16_d128_g4", "w_f32", "w_bf16_kmax_wmax"])
@@ -165,7 +169,7 @@ def test_backward_window(name):
                      f["score"], f["lse_tot"], f["O"], t["dO"], w.S, window=W)
     torch.cuda.synchronize()
     o = oracle.forward(x["Q"], x["K"], x["V"], x["Ql"], w.S, w.K, window=W)
-    excl, eq = compare_selection(host(f["idx"]), o["idx"], o["gap"], w.K)
+    eq = np.all(host(f["idx"]) == o["idx"], axis=-1)
     assert eq.all(), "small backward cases need identical selections"
     og = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], o["idx"], x["dO"], w.S, window=W)
     tol = TOL_GRAD_BF16 if w.dtype == "bf16" else TOL_F32
@@ -199,7 +203,8 @@ def test_full_size_main_config_sampled():
     O, lo, lt = oracle.attend_fuse(x["Q"], x["K"], x["V"], idx, score, w.S, rows=rows, window=W)
     flat = lambda a: a.reshape(-1, *a.shape[3:])  # noqa: E731
     gi, gs = flat(host(f["idx"]))[rows], flat(host(f["score"]))[rows]
-    excl, eq = compare_selection(gi, flat(idx)[rows], flat(gap)[rows], w.K)
+    excl, eq = compare_selection(gi, flat(idx)[rows], flat(gap)[rows], w.K,
+                                 lambda d: all_scores(x["Q"], ksum, ent, w.S, rows[d], window=W))
     say(f"  sampled rows {len(rows)}, near-tie excluded {int(excl.sum())}")
     m = eq[:, None].repeat(w.K, 1) & (flat(idx)[rows] >= 0)
     assert_close(gs[m], flat(score)[rows][m], TOL_F32, "score")
