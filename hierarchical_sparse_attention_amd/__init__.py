@@ -12,7 +12,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["HilsError", "lib", "make_dims", "summarize", "score_topk", "attend_fuse", "backward",
+__all__ = ["HilsError", "lib", "make_dims", "summarize", "score_topk", "score_topk_noalloc",
+           "attend_fuse", "backward",
            "forward", "workspace_size", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhils.so")
@@ -20,9 +21,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhils.so"
 HILS_F32, HILS_BF16 = 0, 1
 OP_SUMMARIZE, OP_SCORE_TOPK, OP_ATTEND_FUSE, OP_BACKWARD = 0, 1, 2, 3
 STATUS = {0: "HILS_OK", 1: "HILS_ERR_INVALID_ARG", 2: "HILS_ERR_UNSUPPORTED",
-          3: "HILS_ERR_WORKSPACE", 4: "HILS_ERR_HIP"}
-EXPORTS = ("hils_workspace_size", "hils_summarize", "hils_score_topk", "hils_attend_fuse",
-           "hils_backward", "hils_status_string", "hils_version")
+          3: "HILS_ERR_WORKSPACE", 4: "HILS_ERR_HIP", 5: "HILS_ERR_SCRATCH"}
+EXPORTS = ("hils_workspace_size", "hils_summarize", "hils_score_topk", "hils_score_topk_noalloc",
+           "hils_attend_fuse", "hils_backward", "hils_status_string", "hils_version")
 
 
 class hils_dims(ctypes.Structure):
@@ -56,13 +57,14 @@ def lib():
         L.hils_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(SZ)]
         L.hils_summarize.argtypes = [P, VP, VP, i32, i32, VP, VP, VP, VP, SZ, VP]
         L.hils_score_topk.argtypes = [P, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.hils_score_topk_noalloc.argtypes = [P, VP, VP, VP, VP, VP, VP]
         L.hils_attend_fuse.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.hils_backward.argtypes = [P] + [VP] * 18 + [VP, SZ, VP]
         L.hils_status_string.argtypes = [ctypes.c_int]
         L.hils_status_string.restype = ctypes.c_char_p
         L.hils_version.restype = i32
-        for f in ("hils_workspace_size", "hils_summarize", "hils_score_topk", "hils_attend_fuse",
-                  "hils_backward"):
+        for f in ("hils_workspace_size", "hils_summarize", "hils_score_topk",
+                  "hils_score_topk_noalloc", "hils_attend_fuse", "hils_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -168,6 +170,29 @@ def score_topk(Q: torch.Tensor, ksum: torch.Tensor, ent: torch.Tensor, K_sel: in
     _check("hils_score_topk", lib().hils_score_topk(
         ctypes.byref(dims), _ptr(Q), _ptr(ksum), _ptr(ent), _ptr(idx), _ptr(score), _ptr(ws), n,
         _stream(dev)))
+    return idx, score
+
+
+def score_topk_noalloc(Q: torch.Tensor, ksum: torch.Tensor, ent: torch.Tensor, K_sel: int,
+                       S: int = 64, q_pos0: int = 0, Tkv: Optional[int] = None,
+                       scale: float = 0.0, Hkv: int = 1, idx=None, score=None,
+                       group: bool = False, window: int = 0):
+    """score_topk through the entry point that takes no workspace (the library's static
+    scratch); for callers that cannot allocate, pass idx and score."""
+    B, Tq, H, d = Q.shape
+    NCcap = ksum.shape[1]
+    Tkv = q_pos0 + Tq if Tkv is None else Tkv
+    _need(Q, "Q"), _need(ksum, "ksum", (B, NCcap, H, d), torch.float32)
+    _need(ent, "ent", (B, NCcap, H), torch.float32)
+    dev = Q.device
+    idx = torch.empty(B, Tq, H, K_sel, dtype=torch.int32, device=dev) if idx is None else idx
+    score = torch.empty(B, Tq, H, K_sel, dtype=torch.float32, device=dev) if score is None else score
+    _need(idx, "idx", (B, Tq, H, K_sel), torch.int32)
+    _need(score, "score", (B, Tq, H, K_sel), torch.float32)
+    dims = make_dims(B, Tq, Tkv, H, Hkv, d, S, K_sel, _dtype_code(Q), q_pos0, scale,
+                     max(Tkv, NCcap * S), NCcap, 1 if group else 0, window)
+    _check("hils_score_topk_noalloc", lib().hils_score_topk_noalloc(
+        ctypes.byref(dims), _ptr(Q), _ptr(ksum), _ptr(ent), _ptr(idx), _ptr(score), _stream(dev)))
     return idx, score
 
 

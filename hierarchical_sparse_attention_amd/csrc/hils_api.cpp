@@ -2,11 +2,45 @@
 // kernel dispatch. Every check happens before anything is enqueued.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "hils.h"
 #include "hils_internal.h"
 
 namespace {
+// Static scratch of hils_score_topk_noalloc: one copy per GPU, held until the
+// process ends. Host code never uses the name below as an address; it uses the
+// device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// Device address of the current device's scratch, looked up once per device.
+hils_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return HILS_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return HILS_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HILS_OK;
+}
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -141,6 +175,23 @@ hils_status hils_score_topk(const hils_dims* dims, const void* Q, const float* k
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
+hils_status hils_score_topk_noalloc(const hils_dims* dims, const void* Q, const float* ksum,
+                                    const float* ent, int32_t* idx, float* score,
+                                    hils_stream stream) {
+  hils::Dims dm;
+  hils_status st = resolve(dims, &dm);
+  if (st != HILS_OK) return st;
+  if (dm.Tq == 0) return HILS_OK;
+  if (!aligned16(Q) || !aligned16(ksum) || !aligned16(ent) || !aligned16(idx) || !aligned16(score))
+    return HILS_ERR_INVALID_ARG;
+  const size_t need = hils::score_topk_ws_bytes(dm);
+  if (need > kScratchBytes) return HILS_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_of_current_device(&ws)) != HILS_OK) return st;
+  return from_hip(hils::launch_score_topk(dm, Q, ksum, ent, idx, score, ws,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
 hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K, const void* V,
                              const int32_t* idx, const float* score, void* O, float* lse_own,
                              float* lse_tot, void* ws, size_t ws_bytes, hils_stream stream) {
@@ -191,6 +242,8 @@ const char* hils_status_string(hils_status status) {
     case HILS_ERR_UNSUPPORTED: return "HILS_ERR_UNSUPPORTED: shape outside S=64, d in {64,128}, K<=64";
     case HILS_ERR_WORKSPACE: return "HILS_ERR_WORKSPACE: workspace smaller than hils_workspace_size";
     case HILS_ERR_HIP: return "HILS_ERR_HIP: kernel launch failed";
+    case HILS_ERR_SCRATCH:
+      return "HILS_ERR_SCRATCH: the call needs more scratch than the library's static 16 MiB";
     default: return "unknown hils_status";
   }
 }

@@ -49,7 +49,8 @@ typedef enum {
   HILS_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, inconsistent sizes */
   HILS_ERR_UNSUPPORTED = 2,  /* valid but unsupported shape (S, d, K) */
   HILS_ERR_WORKSPACE = 3,    /* ws smaller than hils_workspace_size */
-  HILS_ERR_HIP = 4           /* a kernel launch failed */
+  HILS_ERR_HIP = 4,          /* a kernel launch failed */
+  HILS_ERR_SCRATCH = 5       /* hils_score_topk_noalloc: more scratch than the library holds */
 } hils_status;
 
 typedef enum { HILS_F32 = 0, HILS_BF16 = 1 } hils_dtype;
@@ -131,6 +132,23 @@ hils_status hils_summarize(const hils_dims* dims, const void* K, const void* Ql,
 hils_status hils_score_topk(const hils_dims* dims, const void* Q, const float* ksum,
                             const float* ent, int32_t* idx, float* score, void* ws,
                             size_t ws_bytes, hils_stream stream);
+
+/*
+ * hils_score_topk without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Same arguments, semantics and results (bit for bit) as
+ * hils_score_topk; its scratch is a static 16 MiB device buffer of the library,
+ * one per GPU, held until the process ends (16 MiB covers every shape whose
+ * hils_workspace_size(.., HILS_OP_SCORE_TOPK, ..) is at most 16 MiB; larger ones
+ * return HILS_ERR_SCRATCH before anything is enqueued). The copy of the current
+ * device is used: make the stream's device current. All calls on one GPU share
+ * that buffer, so calls that overlap on one GPU (concurrent streams, or host
+ * threads) race and must be serialised by the caller; nothing in it needs to
+ * start at zero. The call itself allocates nothing.
+ */
+hils_status hils_score_topk_noalloc(const hils_dims* dims, const void* Q, const float* ksum,
+                                    const float* ent, int32_t* idx, float* score,
+                                    hils_stream stream);
 
 /*
  * K and V may also be pinned host memory (hipHostMalloc) in hils_summarize and
