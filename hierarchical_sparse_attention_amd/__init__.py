@@ -13,17 +13,18 @@ from typing import Optional
 import torch
 
 __all__ = ["HilsError", "lib", "make_dims", "summarize", "score_topk", "score_topk_noalloc",
-           "attend_fuse", "backward",
+           "attend_fuse", "decode", "decode_workspace", "backward",
            "forward", "workspace_size", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhils.so")
 
 HILS_F32, HILS_BF16 = 0, 1
-OP_SUMMARIZE, OP_SCORE_TOPK, OP_ATTEND_FUSE, OP_BACKWARD = 0, 1, 2, 3
+OP_SUMMARIZE, OP_SCORE_TOPK, OP_ATTEND_FUSE, OP_BACKWARD, OP_DECODE = 0, 1, 2, 3, 4
 STATUS = {0: "HILS_OK", 1: "HILS_ERR_INVALID_ARG", 2: "HILS_ERR_UNSUPPORTED",
           3: "HILS_ERR_WORKSPACE", 4: "HILS_ERR_HIP", 5: "HILS_ERR_SCRATCH"}
 EXPORTS = ("hils_workspace_size", "hils_summarize", "hils_score_topk", "hils_score_topk_noalloc",
-           "hils_attend_fuse", "hils_backward", "hils_status_string", "hils_version")
+           "hils_attend_fuse", "hils_decode", "hils_backward", "hils_status_string",
+           "hils_version")
 
 
 class hils_dims(ctypes.Structure):
@@ -59,12 +60,14 @@ def lib():
         L.hils_score_topk.argtypes = [P, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.hils_score_topk_noalloc.argtypes = [P, VP, VP, VP, VP, VP, VP]
         L.hils_attend_fuse.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.hils_decode.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.hils_backward.argtypes = [P] + [VP] * 18 + [VP, SZ, VP]
         L.hils_status_string.argtypes = [ctypes.c_int]
         L.hils_status_string.restype = ctypes.c_char_p
         L.hils_version.restype = i32
         for f in ("hils_workspace_size", "hils_summarize", "hils_score_topk",
-                  "hils_score_topk_noalloc", "hils_attend_fuse", "hils_backward"):
+                  "hils_score_topk_noalloc", "hils_attend_fuse", "hils_decode",
+                  "hils_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -225,6 +228,58 @@ def attend_fuse(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Te
         ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(score), _ptr(O),
         _ptr(lse_own), _ptr(lse_tot), _ptr(ws), n, _stream(dev)))
     return O, lse_own, lse_tot
+
+
+def decode_workspace(Q: torch.Tensor, K: torch.Tensor, ksum: torch.Tensor, K_sel: int,
+                     S: int = 64, q_pos0: int = 0, Tkv: Optional[int] = None,
+                     window: int = 0) -> torch.Tensor:
+    """A zeroed workspace for decode() calls of these shapes (allocate it once, outside
+    any captured graph, and pass it to every call)."""
+    B, Tq, H, d = Q.shape
+    Tcap, Hkv = K.shape[1], K.shape[2]
+    Tkv = q_pos0 + Tq if Tkv is None else Tkv
+    dims = make_dims(B, Tq, Tkv, H, Hkv, d, S, K_sel, _dtype_code(Q), q_pos0, 0.0, Tcap,
+                     ksum.shape[1], window=window)
+    return torch.zeros(max(workspace_size(dims, OP_DECODE), 256), dtype=torch.uint8,
+                       device=Q.device)
+
+
+def decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, ksum: torch.Tensor,
+           ent: torch.Tensor, K_sel: int, S: int = 64, q_pos0: int = 0, Tkv: Optional[int] = None,
+           scale: float = 0.0, idx=None, score=None, O=None, lse_own=None, lse_tot=None,
+           ws: Optional[torch.Tensor] = None, window: int = 0):
+    """One decode step of the query rows at q_pos0.. over the cache K, V (selection and
+    attention in one call) -> (idx, score, O, lse_own, lse_tot). ws: a workspace from
+    decode_workspace() (a zeroed one is made when it is None)."""
+    B, Tq, H, d = Q.shape
+    Tcap, Hkv = K.shape[1], K.shape[2]
+    NCcap = ksum.shape[1]
+    Tkv = q_pos0 + Tq if Tkv is None else Tkv
+    _need(Q, "Q"), _need(K, "K", (B, Tcap, Hkv, d), Q.dtype, host_ok=True)
+    _need(V, "V", (B, Tcap, Hkv, d), Q.dtype, host_ok=True)
+    _need(ksum, "ksum", (B, NCcap, H, d), torch.float32)
+    _need(ent, "ent", (B, NCcap, H), torch.float32)
+    dev = Q.device
+    idx = torch.empty(B, Tq, H, K_sel, dtype=torch.int32, device=dev) if idx is None else idx
+    score = torch.empty(B, Tq, H, K_sel, dtype=torch.float32, device=dev) if score is None else score
+    O = torch.empty_like(Q) if O is None else O
+    lse_own = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if lse_own is None else lse_own
+    lse_tot = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if lse_tot is None else lse_tot
+    _need(idx, "idx", (B, Tq, H, K_sel), torch.int32)
+    _need(score, "score", (B, Tq, H, K_sel), torch.float32)
+    _need(O, "O", Q.shape, Q.dtype)
+    _need(lse_own, "lse_own", (B, Tq, H), torch.float32)
+    _need(lse_tot, "lse_tot", (B, Tq, H), torch.float32)
+    dims = make_dims(B, Tq, Tkv, H, Hkv, d, S, K_sel, _dtype_code(Q), q_pos0, scale, Tcap, NCcap,
+                     window=window)
+    need = workspace_size(dims, OP_DECODE)
+    if ws is None:
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(ws, "ws", dtype=torch.uint8)
+    _check("hils_decode", lib().hils_decode(
+        ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(ksum), _ptr(ent), _ptr(idx),
+        _ptr(score), _ptr(O), _ptr(lse_own), _ptr(lse_tot), _ptr(ws), ws.numel(), _stream(dev)))
+    return idx, score, O, lse_own, lse_tot
 
 
 def forward(Q, K, V, Ql, K_sel: int, S: int = 64, scale: float = 0.0, group: bool = False,

@@ -111,6 +111,15 @@ hils_status backward_shape_ok(const hils::Dims& dm) {
 
 hils_status from_hip(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_ERR_HIP; }
 
+// Workspace of hils_decode: the fused kernel's counters and lists, or else the
+// larger of the two calls it is made of (they run one after the other on the stream).
+size_t decode_ws(const hils::Dims& dm) {
+  const size_t f = hils::decode_fused_ws_bytes(dm);
+  if (f > 0) return f;
+  const size_t a = hils::score_topk_ws_bytes(dm), b = hils::attend_ws_bytes(dm);
+  return a > b ? a : b;
+}
+
 hils_status check_ws(size_t need, const void* ws, size_t ws_bytes) {
   if (need == 0) return HILS_OK;
   if (ws_bytes < need) return HILS_ERR_WORKSPACE;
@@ -131,6 +140,7 @@ hils_status hils_workspace_size(const hils_dims* dims, int op, size_t* bytes) {
     case HILS_OP_SUMMARIZE: *bytes = 0; return HILS_OK;
     case HILS_OP_SCORE_TOPK: *bytes = hils::score_topk_ws_bytes(dm); return HILS_OK;
     case HILS_OP_ATTEND_FUSE: *bytes = hils::attend_ws_bytes(dm); return HILS_OK;
+    case HILS_OP_DECODE: *bytes = decode_ws(dm); return HILS_OK;
     case HILS_OP_BACKWARD:
       st = backward_shape_ok(dm);
       if (st != HILS_OK) return st;
@@ -210,6 +220,33 @@ hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K
   if ((st = kv_view(K, &Kd)) != HILS_OK || (st = kv_view(V, &Vd)) != HILS_OK) return st;
   return from_hip(hils::launch_attend_fuse(dm, Q, Kd, Vd, idx, score, O, lse_own, lse_tot, ws,
                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+hils_status hils_decode(const hils_dims* dims, const void* Q, const void* K, const void* V,
+                        const float* ksum, const float* ent, int32_t* idx, float* score, void* O,
+                        float* lse_own, float* lse_tot, void* ws, size_t ws_bytes,
+                        hils_stream stream) {
+  hils::Dims dm;
+  hils_status st = resolve(dims, &dm);
+  if (st != HILS_OK) return st;
+  if (dm.Tq == 0) return HILS_OK;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(ksum) || !aligned16(ent) ||
+      !aligned16(idx) || !aligned16(score) || !aligned16(O))
+    return HILS_ERR_INVALID_ARG;
+  if ((lse_own != nullptr && !aligned16(lse_own)) || (lse_tot != nullptr && !aligned16(lse_tot)))
+    return HILS_ERR_INVALID_ARG;
+  st = check_ws(decode_ws(dm), ws, ws_bytes);
+  if (st != HILS_OK) return st;
+  const void *Kd = nullptr, *Vd = nullptr;
+  if ((st = kv_view(K, &Kd)) != HILS_OK || (st = kv_view(V, &Vd)) != HILS_OK) return st;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (hils::decode_fused_try(dm, Q, Kd, Vd, ksum, ent, idx, score, O, lse_own, lse_tot, ws, hs,
+                             &err))
+    return from_hip(err);
+  if ((err = hils::launch_score_topk(dm, Q, ksum, ent, idx, score, ws, hs)) != hipSuccess)
+    return HILS_ERR_HIP;
+  return from_hip(hils::launch_attend_fuse(dm, Q, Kd, Vd, idx, score, O, lse_own, lse_tot, ws, hs));
 }
 
 hils_status hils_backward(const hils_dims* dims, const void* Q, const void* K, const void* V,

@@ -21,42 +21,18 @@
 // Decode: candidates of a row are split over workgroups; each writes its local
 // top-K (rank counting) and the merge kernel of the float32 path ranks the union.
 #include "hils_internal.h"
+#include "mfma_common.h"
 
 namespace hils {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
 constexpr int kSplitM = kSplitMfma;  // candidates per decode workgroup
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &u, 16);
-  return r;
-}
-
-// hi/lo split of 8 float32 values into two bf16x8 fragments (round to nearest even).
-__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = (__bf16)x[j];
-    hi[j] = h;
-    lo[j] = (__bf16)(x[j] - (float)h);
-  }
-}
-
-// Score accumulation for one 16x16 block: sum_ds q.hi + q.lo, fixed order.
-template <int D>
-__device__ __forceinline__ floatx4 score_block(const uint4* qa, const bf16x8* hi, const bf16x8* lo) {
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ds]), hi[ds], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ds]), lo[ds], acc, 0, 0, 0);
-  }
-  return acc;
-}
+using mf::as_bf16x8;
+using mf::bf16x8;
+using mf::floatx4;
+using mf::score_block;
+using mf::split8;
 
 // Split copy of the summary keys in MFMA fragment order. Per (b, h) the chunks
 // come in blocks of 16; block blk holds D/16 fragments of 64 lanes, fragment
@@ -481,80 +457,19 @@ __global__ __launch_bounds__(256) void k_score_split_mfma(Dims dm, const uint16_
                                                           const float* __restrict__ ent,
                                                           float* __restrict__ ws_s,
                                                           int* __restrict__ ws_i, int nsplit) {
+  static_assert(kSplitM == 128, "four wavefronts of 32 candidates");
   __shared__ __align__(16) float ss[kSplitM];
-  const int split = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6, c = lane & 15, g = lane >> 4;
-  const int h = r % dm.H, i = (r / dm.H) % dm.Tq, b = r / (dm.H * dm.Tq);
+  const int split = blockIdx.x, r = blockIdx.y;
+  const int i = (r / dm.H) % dm.Tq;
   const int n = dm.ncand(dm.q_pos0 + i);
   const int cbase = split * kSplitM;
-  // every global read is issued up front and unconditionally (invalid chunks
-  // read chunk 0 and are discarded), so they share one round trip
-  constexpr int NBW = kSplitM / 16 / 4;
-  uint4 qraw[D / 32];
-#pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds)
-    qraw[ds] = *reinterpret_cast<const uint4*>(Q + (long long)r * D + 32 * ds + 8 * g);
-  float4 raw[NBW][D / 32][2];
-  float ev[NBW];
-#pragma unroll
-  for (int q = 0; q < NBW; ++q) {
-    const int chunk = cbase + 16 * (NBW * w + q) + c;
-    const long long row = ((long long)b * dm.NCcap + (chunk < n ? chunk : 0)) * dm.H + h;
-    const float* src = ksum + row * D;
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-      raw[q][ds][0] = *reinterpret_cast<const float4*>(src + 32 * ds + 8 * g);
-      raw[q][ds][1] = *reinterpret_cast<const float4*>(src + 32 * ds + 8 * g + 4);
-    }
-    ev[q] = ent[row];
-  }
-  uint4 qa[D / 32];  // the row sits in M position 0 (lanes with c == 0)
-#pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds) qa[ds] = c == 0 ? qraw[ds] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int q = 0; q < NBW; ++q) {
-    const int nb = NBW * w + q;
-    const int chunk = cbase + 16 * nb + c;
-    const bool cv = chunk < n;
-    bf16x8 hi[D / 32], lo[D / 32];
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-      const float4 a = raw[q][ds][0], bb = raw[q][ds][1];
-      float v[8] = {a.x, a.y, a.z, a.w, bb.x, bb.y, bb.z, bb.w};
-      if (!cv) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = 0.f;
-      }
-      split8(v, hi[ds], lo[ds]);
-    }
-    const floatx4 acc = score_block<D>(qa, hi, lo);
-    if (g == 0) ss[16 * nb + c] = cv ? fmaf(acc[0], dm.scale, ev[q]) : -INFINITY;
-  }
+  mf::split_scores<D, 4>(dm, Q, ksum, ent, r, n, cbase, ss);
   __syncthreads();
   // local rank: invalid candidates hold -inf and sort after every valid one
   // (a valid candidate's rank counts only valid candidates before it)
-  const int nvalid = max(0, min(kSplitM, n - cbase));
-  if (t < nvalid) {
-    const float sv = ss[t];
-    int rank = 0;
-    const float4* s4 = reinterpret_cast<const float4*>(ss);
-    for (int y0 = 0; y0 < kSplitM / 4; y0 += 16) {  // 16 LDS reads in flight per step
-      float4 v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = s4[y0 + j];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int y = 4 * (y0 + j);
-        rank += topk_before(v[j].x, y, sv, t) + topk_before(v[j].y, y + 1, sv, t) +
-                topk_before(v[j].z, y + 2, sv, t) + topk_before(v[j].w, y + 3, sv, t);
-      }
-    }
-    if (rank < dm.K) {
-      const long long o = ((long long)r * nsplit + split) * dm.K + rank;
-      ws_s[o] = sv;
-      ws_i[o] = cbase + t;
-    }
-  }
+  const long long o = ((long long)r * nsplit + split) * dm.K;
+  mf::split_local_topk<kSplitM>(ss, max(0, min(kSplitM, n - cbase)), cbase, dm.K, ws_s + o,
+                                ws_i + o);
 }
 
 // Decode scoring, one workgroup (16 wavefronts) per query row when the row has

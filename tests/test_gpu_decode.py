@@ -1,0 +1,164 @@
+"""hils_decode (one decode step in one call) through the C ABI.
+
+Its results are those of hils_score_topk followed by hils_attend_fuse: the
+selection and scores bit for bit, and for bf16 per-head selection (the fused
+single-launch kernel) the outputs and log-masses bit for bit too (same slot and
+fusion arithmetic in the same order). Also checked against the oracle, over many
+steps in a row on one workspace (the per-row counters reset themselves), with
+windows, K = 64, several rows per call, rows with no candidates, d = 128, float32
+(two-call fallback) and a host-resident cache.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_amd as hsa
+import oracle
+import synth
+from hils_testutil import TOL_BF16, TOL_F32, all_scores, assert_close, compare_selection, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(device=DEV, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+def host(t):
+    return t.detach().float().cpu().numpy() if t.dtype != torch.int32 else t.cpu().numpy()
+
+
+CASES = {
+    # name: workload, window, query rows per call
+    "bf16_d64": (synth.small("dec_d64", B=1, T=8192, H=4, Hkv=2, d=64, K=16, dtype="bf16",
+                             n_planted=2), 0, 1),
+    "bf16_d64_rows4_b2": (synth.small("dec_rows", B=2, T=4096, H=2, Hkv=1, d=64, K=8,
+                                      dtype="bf16"), 0, 4),
+    "bf16_d128_g4": (synth.small("dec_d128", B=1, T=8192, H=8, Hkv=2, d=128, K=16, dtype="bf16",
+                                 n_uniform=3), 0, 1),
+    "bf16_window_k32": (synth.small("dec_win", B=1, T=8192, H=4, Hkv=4, d=64, K=32,
+                                    dtype="bf16"), 512, 1),
+    "bf16_k64_window2048": (synth.small("dec_k64", B=1, T=12288, H=2, Hkv=1, d=64, K=64,
+                                        dtype="bf16"), 2048, 2),
+    "f32_d64": (synth.small("dec_f32", B=1, T=4096, H=2, Hkv=1, d=64, K=8, dtype="f32"), 0, 1),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_steps_match_two_calls_and_oracle(name):
+    w, W, nq = CASES[name]
+    x = synth.make_inputs(w)
+    say(f"[decode] {name}")
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
+    ksum, ent, _ = hsa.summarize(t["K"], t["Ql"], w.S)
+    oks, oent, _ = oracle.summarize(x["K"], x["Ql"], w.S)
+    # positions: the first chunk (no candidates), chunk edges, late rows
+    starts = [0, 63, 64, 1000, w.T // 2 + 5, w.T - 64, w.T - nq]
+    ws = None
+    fused_bitwise = w.dtype == "bf16"
+    for p in starts:
+        q = t["Q"][:, p:p + nq].contiguous()
+        if ws is None:
+            ws = hsa.decode_workspace(t["Q"][:, :nq], t["K"], ksum, w.K, w.S, w.T - nq, w.T,
+                                      window=W)
+        got = hsa.decode(q, t["K"], t["V"], ksum, ent, w.K, w.S, q_pos0=p, Tkv=p + nq, ws=ws,
+                         window=W)
+        idx, sc = hsa.score_topk(q, ksum, ent, w.K, w.S, q_pos0=p, Tkv=p + nq, Hkv=w.Hkv,
+                                 window=W)
+        O, lo, lt = hsa.attend_fuse(q, t["K"], t["V"], idx, sc, w.S, q_pos0=p, Tkv=p + nq,
+                                    window=W)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], idx), p
+        assert torch.equal(got[1], sc), p
+        if fused_bitwise:
+            assert torch.equal(got[2], O), p
+            assert torch.equal(got[4], lt), p
+            assert torch.equal(got[3], lo), p
+        qn = x["Q"][:, p:p + nq]
+        oidx, osc, ogap = oracle.score_topk(qn, oks, oent, w.S, w.K, q_pos0=p, window=W)
+        oO, olo, olt = oracle.attend_fuse(qn, x["K"][:, :p + nq], x["V"][:, :p + nq], oidx, osc,
+                                          w.S, q_pos0=p, window=W)
+        excl, eq = compare_selection(host(got[0]), oidx, ogap, w.K,
+                                     lambda d: all_scores(qn, oks, oent, w.S, d, q_pos0=p,
+                                                          window=W))
+        tol = TOL_BF16 if w.dtype == "bf16" else TOL_F32
+        assert_close(host(got[2])[eq], oO[eq], tol, f"O {p}")
+        assert_close(host(got[4])[eq], olt[eq], TOL_F32, f"lse_tot {p}")
+        assert_close(host(got[3])[eq], olo[eq], TOL_F32, f"lse_own {p}")
+
+
+def test_decode_workspace_counters_stay_zero():
+    """The per-row counters at the start of the workspace are zero after every call."""
+    w, W, nq = CASES["bf16_d64"]
+    x = synth.make_inputs(w)
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
+    ksum, ent, _ = hsa.summarize(t["K"], t["Ql"], w.S)
+    ws = hsa.decode_workspace(t["Q"][:, :1], t["K"], ksum, w.K, w.S, w.T - 1, w.T)
+    for p in range(w.T - 40, w.T):
+        hsa.decode(t["Q"][:, p:p + 1].contiguous(), t["K"], t["V"], ksum, ent, w.K, w.S,
+                   q_pos0=p, Tkv=p + 1, ws=ws)
+    torch.cuda.synchronize()
+    rows = w.B * w.H
+    assert int(ws[:4 * rows].view(torch.int32).abs().sum()) == 0
+
+
+def test_decode_full_size_cache_steps():
+    """The 128K-token cache, 256 steps with incremental summaries; sampled steps
+    against the oracle and the two-call path."""
+    w = synth.workloads()["decode_128k"]
+    x = synth.make_inputs(w)
+    say(f"[decode full] cache {w.T} H{w.H} d{w.d} K{w.K}")
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
+    p0 = w.q_pos0
+    NC = w.T // w.S
+    ksum = torch.empty(1, NC, w.H, w.d, device=DEV)
+    ent = torch.empty(1, NC, w.H, device=DEV)
+    hsa.summarize(t["K"], t["Ql"], w.S, 0, p0 // w.S, Tkv=p0, ksum=ksum, ent=ent)
+    oks, oent, _ = oracle.summarize(x["K"], x["Ql"], w.S)
+    ws = hsa.decode_workspace(t["Q"][:, :1], t["K"], ksum, w.K, w.S, w.T - 1, w.T)
+    check = {0, 63, 64, 65, 128, 200, 255}
+    for s in range(w.rows_q):
+        p = p0 + s
+        if p % w.S == 0 and p > p0:
+            c = p // w.S - 1
+            hsa.summarize(t["K"], t["Ql"], w.S, c, c + 1, Tkv=p, ksum=ksum, ent=ent)
+        q = t["Q"][:, s:s + 1].contiguous()
+        got = hsa.decode(q, t["K"], t["V"], ksum, ent, w.K, w.S, q_pos0=p, Tkv=p + 1, ws=ws)
+        if s not in check:
+            continue
+        idx, sc = hsa.score_topk(q, ksum, ent, w.K, w.S, q_pos0=p, Tkv=p + 1, Hkv=w.Hkv)
+        O, lo, lt = hsa.attend_fuse(q, t["K"], t["V"], idx, sc, w.S, q_pos0=p, Tkv=p + 1)
+        torch.cuda.synchronize()
+        for a, b, nm in zip(got, (idx, sc, O, lo, lt), ("idx", "score", "O", "lse_own", "lse_tot")):
+            assert torch.equal(a, b), (s, nm)
+        qn = x["Q"][:, s:s + 1]
+        oidx, osc, ogap = oracle.score_topk(qn, oks, oent, w.S, w.K, q_pos0=p)
+        oO, _, olt = oracle.attend_fuse(qn, x["K"][:, :p + 1], x["V"][:, :p + 1], oidx, osc, w.S,
+                                        q_pos0=p)
+        excl, eq = compare_selection(host(got[0]), oidx, ogap, w.K,
+                                     lambda d: all_scores(qn, oks, oent, w.S, d, q_pos0=p))
+        assert_close(host(got[2])[eq], oO[eq], TOL_BF16, f"O step {s}")
+        assert_close(host(got[4])[eq], olt[eq], TOL_F32, f"lse_tot step {s}")
+
+
+def test_decode_host_resident_cache():
+    """K and V in pinned host memory: the fused step reads the selected chunks and the
+    local branch through the device mapping; results equal the device-resident cache."""
+    w, W, nq = CASES["bf16_d64"]
+    x = synth.make_inputs(w)
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
+    Kh = torch.empty(t["K"].shape, dtype=torch.bfloat16, pin_memory=True)
+    Vh = torch.empty(t["V"].shape, dtype=torch.bfloat16, pin_memory=True)
+    Kh.copy_(t["K"])
+    Vh.copy_(t["V"])
+    ksum, ent, _ = hsa.summarize(t["K"], t["Ql"], w.S)
+    ws = hsa.decode_workspace(t["Q"][:, :1], t["K"], ksum, w.K, w.S, w.T - 1, w.T)
+    for p in (w.T - 1, w.T // 2):
+        q = t["Q"][:, p:p + 1].contiguous()
+        a = hsa.decode(q, t["K"], t["V"], ksum, ent, w.K, w.S, q_pos0=p, Tkv=p + 1, ws=ws)
+        b = hsa.decode(q, Kh, Vh, ksum, ent, w.K, w.S, q_pos0=p, Tkv=p + 1, ws=ws)
+        torch.cuda.synchronize()
+        for u, v in zip(a, b):
+            assert torch.equal(u, v), p
