@@ -1,37 +1,60 @@
 """Benchmark of the HiLS attention hot path on one MI355X.
 
-One step = the whole prefill forward (landmark summaries, chunk scoring + top-K,
-intra-chunk attention + inter-chunk fusion) over the 345M-class workload
-(B=1, H=16, d=64, T=8192, S=64, K=16, bf16 storage, float32 accumulation),
-inputs resident in HBM. Also reported: 128K-context decode (256 steps, one query
-per step, incremental summaries), per-kernel roofline fractions measured with
-HIP events on the stream the kernels run on, and the CPU oracle timed on a
-bounded sample of the same workload.
+Headline: the 7B-class GQA prefill (B=1, H=32 query heads over 8 kv heads,
+d=128, T=32768, S=64, K=16, bf16 storage, float32 accumulation), the largest
+prefill workload that fits one GPU. One step is the whole forward: landmark
+summaries, chunk scoring + top-K, intra-chunk attention + inter-chunk fusion,
+with inputs resident in HBM.
+
+Also measured, each with a roofline block for its kernels: the 345M-class
+prefill (B=1, H=16, d=64, T=8192), 128K-context decode (256 steps of
+hils_decode under a HIP graph, with incremental summaries), the training step
+(B=2, T=16384: forward + backward), and variants (group-max selection, the
+pages' main setting K=32 with a 512-key window, Q-Cal, a host-resident decode
+cache, 16 query rows per decode call).
+
+Kernel durations come from HIP events recorded on the stream the kernels run
+on. The CPU oracle (one thread, -O3 -march=native, compiled on the machine that
+runs it) is timed on bounded samples of each workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --pmc-run WORKLOAD            (a short run for rocprofv3 --pmc)
+       python bench.py --traffic WORKLOAD FETCH_CSV WRITE_CSV   (counter CSVs -> record)
 """
 from __future__ import annotations
 
 import argparse
 import dataclasses
+import hashlib
 import json
 import os
 import sys
+import tempfile
 import time
 
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attend_fuse_prefill_345m_traffic.json")
-# sources of the kernels behind hils_attend_fuse on the prefill path
-ATTEND_SOURCES = ["hierarchical_sparse_attention_amd/csrc/k_attend_mfma.hip",
-                  "hierarchical_sparse_attention_amd/csrc/k_attend_fuse.hip",
-                  "hierarchical_sparse_attention_amd/csrc/hils_internal.h"]
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = "hierarchical_sparse_attention_amd/csrc/"
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
+
+# kernels behind each measured call, and the sources they are built from (a
+# counter record is used only while those sources are unchanged)
+CALL_KERNELS = {
+    "attend_fuse": (("k_kv_prep", "k_attend_mfma"),
+                    ("k_attend_mfma.hip", "k_attend_fuse.hip", "hils_internal.h")),
+    "decode": (("k_score_split_mfma", "k_topk_merge_rank", "k_decode_partial", "k_decode_combine"),
+               ("k_score_mfma.hip", "k_score_topk.hip", "k_attend_fuse.hip", "decode_slot.h",
+                "mfma_common.h", "hils_internal.h")),
+    "backward": (("k_bwd_rowd", "k_sel_count", "k_sel_scan", "k_sel_fill", "k_bwd_kv_mfma",
+                  "k_dq_reduce"), ("k_backward_mfma.hip", "k_backward.hip", "hils_internal.h")),
+}
+PMC_WORKLOADS = ("prefill_7b_gqa", "prefill_345m", "decode_128k", "train_345m")
 
 
 def parse():
@@ -41,29 +64,36 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra-configs", action="store_true",
-                    help="skip the 7B-class GQA prefill and the training-step timings")
-    ap.add_argument("--pmc-run", action="store_true",
-                    help="run 3 prefill steps and one calibration copy, for counter collection")
-    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc counter CSVs into the traffic record")
+                    help="only the headline workload and the 128K decode")
+    ap.add_argument("--pmc-run", choices=PMC_WORKLOADS,
+                    help="run 3 steps of one workload and a calibration copy, for counters")
+    ap.add_argument("--traffic", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs into the workload's record")
     return ap.parse_args()
 
 
-def sources_hash():
-    import hashlib
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- counter records
+def sources_hash(call):
     h = hashlib.sha256()
-    for rel in ATTEND_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    for rel in CALL_KERNELS[call][1]:
+        with open(os.path.join(ROOT, CSRC, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def write_traffic_record(fetch_csv, write_csv):
-    """HBM bytes per attend launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
-    each scaled by the same counter's reading for an elementwise copy (neg) of
-    COPY_BYTES."""
+def traffic_path(workload):
+    return os.path.join(PROFILES, f"traffic_{workload}.json")
+
+
+def write_traffic_record(workload, fetch_csv, write_csv):
+    """HBM bytes per dispatch of every kernel from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for an elementwise copy
+    (neg) of COPY_BYTES."""
     import csv
 
     def per_kernel(path, counter):
@@ -75,70 +105,313 @@ def write_traffic_record(fetch_csv, write_csv):
             acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
         out = {}
         for (name, _), v in acc.items():
-            out.setdefault(name, []).append(v)
-        return out
+            out.setdefault(name, []).append(v * 1024.0)
+        return {k: sum(v) / len(v) for k, v in out.items()}
 
-    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
-    write = per_kernel(write_csv, "WRITE_SIZE")
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
 
-    def pick(d, pat):
-        ks = [k for k in d if pat in k]
-        vals = [v for k in ks for v in d[k]]
-        return sum(vals) / len(vals) * 1024.0 if vals else None  # bytes per dispatch
+    def copy_reading(d):
+        vals = [v for k, v in d.items() if "neg" in k]
+        return vals[0] if vals else None
 
-    f_copy, w_copy = pick(fetch, "neg"), pick(write, "neg")
-    f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
-    rec = {"sources_hash": sources_hash(), "copy_bytes": COPY_BYTES,
-           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
-    for pat in ("k_kv_prep", "k_attend_mfma"):
-        fb, wb = pick(fetch, pat), pick(write, pat)
-        if fb is not None:
-            rec["kernels"][pat] = {"fetch_bytes": fb * f_scale, "write_bytes": wb * w_scale}
-    rec["attend_call_bytes"] = sum(v["fetch_bytes"] + v["write_bytes"]
-                                   for v in rec["kernels"].values())
-    os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
-    with open(TRAFFIC_RECORD, "w") as f:
+    f_scale, w_scale = COPY_BYTES / copy_reading(fetch), COPY_BYTES / copy_reading(write)
+    rec = {"workload": workload, "copy_bytes": COPY_BYTES, "fetch_scale": f_scale,
+           "write_scale": w_scale, "sources_hash": {c: sources_hash(c) for c in CALL_KERNELS},
+           "kernels": {}}
+    for name in sorted(set(fetch) | set(write)):
+        if "neg" in name:
+            continue
+        short = name.split("(")[0].split("<")[0].split("::")[-1].strip()
+        rec["kernels"][name] = {"short": short,
+                                "fetch_bytes": fetch.get(name, 0.0) * f_scale,
+                                "write_bytes": write.get(name, 0.0) * w_scale}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_path(workload), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
 
-def read_traffic_record():
+def call_traffic(workload, call):
+    """HBM bytes per call from the committed counter record, or None when there is
+    none or the call's kernel sources changed since it was taken."""
     try:
-        rec = json.load(open(TRAFFIC_RECORD))
+        rec = json.load(open(traffic_path(workload)))
     except (OSError, ValueError):
         return None
-    return rec if rec.get("sources_hash") == sources_hash() else None
+    if rec.get("sources_hash", {}).get(call) != sources_hash(call):
+        return None
+    pats = CALL_KERNELS[call][0]
+    tot = [v["fetch_bytes"] + v["write_bytes"] for v in rec["kernels"].values()
+           if any(p in v["short"] for p in pats)]
+    return sum(tot) if tot else None
 
 
-def log(msg):
-    print(msg, file=sys.stderr, flush=True)
+# ---------------------------------------------------------------- algorithmic work
+def lstart_of(i, S, window):
+    return max(0, i - window + 1) if window > 0 else i - i % S
 
 
-def algorithmic_counts(w, idx_host, window=0):
-    """Per-step algorithmic work of each kernel (bytes that must move / flops). The
-    local branch is the own chunk (window 0) or the last `window` keys."""
+def prefill_counts(w, idx_host, window=0):
+    """Per-step algorithmic work of each prefill kernel (bytes the method must move,
+    flops it must do; never the dense work it avoids)."""
     B, T, H, Hkv, d, S, K = w.B, w.T, w.H, w.Hkv, w.d, w.S, w.K
     NC = T // S
     esz = 2  # bf16
-
-    def lstart(i):
-        return max(0, i - window + 1) if window > 0 else i - i % S
-
     sel_pairs = int((idx_host >= 0).sum())                 # (row, selected chunk) pairs
-    own_keys = B * H * sum(i - lstart(i) + 1 for i in range(T))  # local-branch key visits
+    own_keys = B * H * sum(i - lstart_of(i, S, window) + 1 for i in range(T))
     key_visits = sel_pairs * S + own_keys
-    cand = B * H * sum(lstart(i) // S for i in range(T))   # scored candidates
+    cand = B * H * sum(lstart_of(i, S, window) // S for i in range(T))
     summ_bytes = B * T * Hkv * d * esz + B * NC * H * d * esz + B * NC * H * (d + 2) * 4
-    score_flops = 2 * d * cand
-    score_bytes = B * T * H * d * esz + B * NC * H * (d + 1) * 4 + B * T * H * K * 8
-    attend_flops = 4 * d * key_visits
     attend_bytes = (2 * B * T * H * d * esz + 2 * B * T * Hkv * d * esz + B * T * H * K * 8
                     + B * T * H * 8)
-    return dict(summarize=dict(bytes=summ_bytes), score_topk=dict(flops=score_flops,
-                bytes=score_bytes), attend_fuse=dict(flops=attend_flops, bytes=attend_bytes),
-                key_visits=key_visits, sel_pairs=sel_pairs, candidates=cand)
+    return dict(summarize_bytes=summ_bytes, score_flops=2 * d * cand,
+                attend_flops=4 * d * key_visits, attend_bytes=attend_bytes,
+                backward_flops=10 * d * key_visits, key_visits=key_visits, sel_pairs=sel_pairs,
+                candidates=cand)
 
 
+def decode_step_bytes(wd, K_sel, window, p):
+    """Algorithmic HBM bytes of one decode step at position p: the candidates'
+    summaries and entropies, the selected chunks' keys and values, the local
+    branch's keys and values, the query, output and selection."""
+    H, Hkv, d, S = wd.H, wd.Hkv, wd.d, wd.S
+    n = lstart_of(p, S, window) // S
+    nloc = p - lstart_of(p, S, window) + 1
+    return (n * H * (d + 1) * 4 + H * min(K_sel, n) * S * d * 2 * 2 + H * nloc * d * 2 * 2
+            + 2 * H * d * 2 + H * K_sel * 8)
+
+
+def roofline(kernel, bound, work, ms, traffic=None, note=None):
+    """Roofline block: achieved = algorithmic work per launch / launch duration."""
+    if bound == "mfma":
+        achieved, peak, unit = work / (ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+    elif bound == "hbm":
+        achieved, peak, unit = work / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:  # "alu": float32 vector arithmetic
+        achieved, peak, unit = work / (ms * 1e-3) / 1e12, FP32_VECTOR_PEAK_TFLOPS, "TFLOP/s"
+    b = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+         "traffic": traffic, "kernel": kernel, "ms_per_launch": ms, "work_per_launch": work}
+    if note:
+        b["note"] = note
+    return b
+
+
+# ---------------------------------------------------------------- timing helpers
+def make_timers(torch, stream):
+    def ev_ms(fn, reps):
+        """Average duration of fn over reps calls, HIP events on the kernels' stream."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    def wall_ms(fn, reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / reps
+
+    return ev_ms, wall_ms
+
+
+def prefill_setup(torch, hsa, synth, dev, wname, K=None, group=False, window=0, qcal=False):
+    w = synth.workloads()[wname]
+    w = dataclasses.replace(w, K=K or w.K)
+    log(f"generating {wname} inputs")
+    x = synth.make_inputs(w)
+    keys = ("Q", "K", "V", "Ql") + (("dO",) if w.need_dO else ())
+    t = {k: torch.from_numpy(x[k]).to(dev, torch.bfloat16) for k in keys}
+    if qcal:
+        t["Qs"] = torch.from_numpy(synth.scoring_query(w, x)).to(dev, torch.bfloat16)
+    Qs = t.get("Qs")
+    f = hsa.forward(t["Q"], t["K"], t["V"], t["Ql"], w.K, w.S, group=group, Qs=Qs, window=window)
+    calls = {
+        "summarize": lambda: hsa.summarize(t["K"], t["Ql"], w.S, ksum=f["ksum"], ent=f["ent"],
+                                           lse_l=f["lse_l"]),
+        "score_topk": lambda: hsa.score_topk(t["Q"] if Qs is None else Qs, f["ksum"], f["ent"],
+                                             w.K, w.S, 0, w.T, Hkv=w.Hkv, idx=f["idx"],
+                                             score=f["score"], group=group, window=window),
+        "attend_fuse": lambda: hsa.attend_fuse(t["Q"], t["K"], t["V"], f["idx"], f["score"],
+                                               w.S, O=f["O"], lse_own=f["lse_own"],
+                                               lse_tot=f["lse_tot"], window=window),
+    }
+    if w.need_dO:
+        calls["backward"] = lambda: hsa.backward(t["Q"], t["K"], t["V"], t["Ql"], f["ksum"],
+                                                 f["ent"], f["lse_l"], f["idx"], f["score"],
+                                                 f["lse_tot"], f["O"], t["dO"], w.S, Qs=Qs,
+                                                 window=window)
+    return w, x, t, f, calls
+
+
+def measure_prefill(torch, ev_ms, w, f, calls, reps, workload, window=0):
+    for fn in calls.values():
+        fn()
+    torch.cuda.synchronize()
+    km = {k: ev_ms(fn, reps) for k, fn in calls.items()}
+    cnt = prefill_counts(w, f["idx"].cpu().numpy(), window)
+    fwd_ms = km["summarize"] + km["score_topk"] + km["attend_fuse"]
+    blocks = {
+        "summarize": roofline("hils_summarize (k_summarize)", "hbm", cnt["summarize_bytes"],
+                              km["summarize"]),
+        "score_topk": roofline("hils_score_topk", "alu", cnt["score_flops"], km["score_topk"],
+                               note="float32-accurate products on bf16 MFMAs over a hi/lo split "
+                                    "of the summary key, against the float32 vector peak"),
+        "attend_fuse": roofline("hils_attend_fuse (k_kv_prep + k_attend_mfma)", "mfma",
+                                cnt["attend_flops"], km["attend_fuse"],
+                                call_traffic(workload, "attend_fuse")),
+    }
+    rec = {"kernels_ms": km, "forward_ms": fwd_ms, "roofline": blocks,
+           "key_visits": cnt["key_visits"], "candidates": cnt["candidates"],
+           "attend_algorithmic_bytes": cnt["attend_bytes"], "K": w.K}
+    if "backward" in km:
+        blocks["backward"] = roofline("hils_backward", "mfma", cnt["backward_flops"],
+                                      km["backward"], call_traffic(workload, "backward"))
+        rec["train_tokens_per_s"] = w.B * w.T / ((fwd_ms + km["backward"]) * 1e-3)
+    else:
+        rec["prefill_tokens_per_s"] = w.B * w.T / (fwd_ms * 1e-3)
+    return rec
+
+
+def measure_decode(torch, hsa, stream, td, wd, K_sel, window, Kc, Vc, nsteps, dev, nb=1):
+    """(record, idx of every step) for a sequence of decode steps: step s queries the
+    nb positions p0 + nb s .. over a cache that ends with them; a chunk's summary is
+    made when it completes. Timed eagerly and as one captured HIP graph. nb > 1
+    stands in for nb sequences decoding together (each row its own position)."""
+    p0, S = wd.q_pos0, wd.S
+    NCd = wd.T // S
+    nsteps = nsteps // nb
+    dk = torch.empty(1, NCd, wd.H, wd.d, device=dev)
+    de = torch.empty(1, NCd, wd.H, device=dev)
+    dl = torch.empty(1, NCd, wd.H, device=dev)
+    hsa.summarize(Kc, td["Ql"], S, 0, p0 // S, Tkv=p0, ksum=dk, ent=de, lse_l=dl)
+    didx = torch.empty(nsteps, 1, nb, wd.H, K_sel, dtype=torch.int32, device=dev)
+    dsc = torch.empty(nsteps, 1, nb, wd.H, K_sel, device=dev)
+    dO = torch.empty(1, nb, wd.H, wd.d, dtype=torch.bfloat16, device=dev)
+    dlo = torch.empty(1, nb, wd.H, device=dev)
+    dlt = torch.empty(1, nb, wd.H, device=dev)
+    ws = hsa.decode_workspace(td["Q"][:, :nb], Kc, dk, K_sel, S, wd.T - nb, wd.T, window=window)
+    qs = [td["Q"][:, nb * s:nb * s + nb].contiguous() for s in range(nsteps)]
+
+    def dstep(s):
+        p = p0 + nb * s
+        if p % S == 0 and p > p0:  # chunk p/S - 1 just completed
+            c = p // S - 1
+            hsa.summarize(Kc, td["Ql"], S, c, c + 1, Tkv=p, ksum=dk, ent=de, lse_l=dl)
+        hsa.decode(qs[s], Kc, Vc, dk, de, K_sel, S, p, p + nb, idx=didx[s], score=dsc[s], O=dO,
+                   lse_own=dlo, lse_tot=dlt, ws=ws, window=window)
+
+    for s in range(8):
+        dstep(s)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for s in range(nsteps):
+        dstep(s)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    eager = ev[0].elapsed_time(ev[1]) * 1e3 / nsteps
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for s in range(nsteps):
+                dstep(s)
+    stream.wait_stream(cap)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 3
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        graph.replay()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / (nsteps * reps)
+    mean_bytes = float(np.mean([sum(decode_step_bytes(wd, K_sel, window, p0 + nb * s + j)
+                                    for j in range(nb)) for s in range(nsteps)]))
+    rec = {"us_per_token": us / nb, "us_per_step": us, "us_per_token_eager": eager / nb,
+           "steps": nsteps, "rows_per_step": nb * wd.H, "bytes_per_step": mean_bytes,
+           "roofline": roofline("hils_decode (split scoring, list merge, slot attention, slot "
+                                "fusion: four launches; a k_summarize every 64 positions)",
+                                "hbm", mean_bytes, us * 1e-3),
+           "K": K_sel}
+    if window:
+        rec["local_branch"] = f"sliding window of {window} keys"
+    del graph
+    return rec, didx
+
+
+# ---------------------------------------------------------------- CPU baselines
+def cpu_prefill(oracle, x, w, nrows, seed):
+    """All landmark summaries, then nrows sampled (row, head) queries scored, selected
+    and attended; scaled to the full step."""
+    rng = np.random.default_rng(seed)
+    rows_total = w.B * w.T * w.H
+    rows = np.sort(rng.choice(rows_total, size=nrows, replace=False))
+    X = {k: x[k].astype(np.float64) for k in ("Q", "K", "V", "Ql")}
+    t0 = time.perf_counter()
+    oks, oent, _ = oracle.summarize(X["K"], X["Ql"], w.S)
+    t_sum = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oidx, osc, _ = oracle.score_topk(X["Q"], oks, oent, w.S, w.K, rows=rows)
+    oracle.attend_fuse(X["Q"], X["K"], X["V"], oidx, osc, w.S, rows=rows)
+    t_rows = time.perf_counter() - t0
+    t_full = t_sum + t_rows * rows_total / nrows
+    return {"value": w.B * w.T / t_full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {w.B * w.NC * w.H} landmark summaries ({t_sum:.2f} s) + {nrows} of "
+                      f"{rows_total} (row, head) queries scored, selected and attended "
+                      f"({t_rows:.2f} s), scaled to the full step"}
+
+
+def cpu_decode(oracle, xd, wd, K_sel, nsteps):
+    """Every step of the decode sequence: scoring, selection and attention of the
+    step's query, plus the summary of each chunk that completes (the initial
+    summaries of the cache are made before the timed region, as on the GPU)."""
+    p0, S = wd.q_pos0, wd.S
+    K64, V64 = xd["K"].astype(np.float64), xd["V"].astype(np.float64)
+    Ql64 = xd["Ql"].astype(np.float64)
+    oks, oent, _ = oracle.summarize(K64[:, :p0], Ql64[:, :p0 // S], S)
+    NC = wd.T // S
+    ks = np.zeros((1, NC, wd.H, wd.d))
+    en = np.zeros((1, NC, wd.H))
+    ks[:, :p0 // S], en[:, :p0 // S] = oks, oent
+    t0 = time.perf_counter()
+    for s in range(nsteps):
+        p = p0 + s
+        if p % S == 0 and p > p0:
+            c = p // S - 1
+            a, b_, _ = oracle.summarize(K64[:, c * S:(c + 1) * S], Ql64[:, c:c + 1], S)
+            ks[:, c], en[:, c] = a[:, 0], b_[:, 0]
+        q = xd["Q"][:, s:s + 1].astype(np.float64)
+        oidx, osc, _ = oracle.score_topk(q, ks, en, S, K_sel, q_pos0=p)
+        oracle.attend_fuse(q, K64[:, :p + 1], V64[:, :p + 1], oidx, osc, S, q_pos0=p)
+    t = time.perf_counter() - t0
+    return {"value": t / nsteps * 1e6, "unit": "us/token", "cores": 1, "kind": "oracle",
+            "sample": f"all {nsteps} decode steps on the {wd.T}-token cache ({t:.2f} s)"}
+
+
+def cpu_train(oracle, x, w):
+    """Forward and backward of batch element 0, head 0 in full (heads and batch
+    elements are independent at G = 1), scaled by B * H."""
+    assert w.H == w.Hkv
+    sl = {k: x[k][:1, :, :1].astype(np.float64) for k in ("Q", "K", "V", "Ql", "dO")}
+    t0 = time.perf_counter()
+    f = oracle.forward(sl["Q"], sl["K"], sl["V"], sl["Ql"], w.S, w.K)
+    oracle.backward(sl["Q"], sl["K"], sl["V"], sl["Ql"], f["idx"], sl["dO"], w.S)
+    t = time.perf_counter() - t0
+    t_full = t * w.B * w.H
+    return {"value": w.B * w.T / t_full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"forward + backward of one (batch element, head) of {w.B * w.H} in full "
+                      f"({t:.2f} s), scaled by {w.B * w.H}"}
+
+
+# ---------------------------------------------------------------- main
 def main():
     args = parse()
     if args.traffic:
@@ -154,42 +427,22 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    w = synth.workloads()["prefill_345m"]
-    log(f"generating {w.name} inputs")
-    x = synth.make_inputs(w)
-    t = {k: torch.from_numpy(x[k]).to(dev, torch.bfloat16) for k in ("Q", "K", "V", "Ql")}
-    B, T, H, Hkv, d, S, K = w.B, w.T, w.H, w.Hkv, w.d, w.S, w.K
-    NC = T // S
     stream = torch.cuda.current_stream()
-
-    # persistent outputs so the timed region allocates only workspaces (cached by torch)
-    ksum = torch.empty(B, NC, H, d, device=dev)
-    ent = torch.empty(B, NC, H, device=dev)
-    lse_l = torch.empty(B, NC, H, device=dev)
-    idx = torch.empty(B, T, H, K, dtype=torch.int32, device=dev)
-    score = torch.empty(B, T, H, K, device=dev)
-    O = torch.empty_like(t["Q"])
-    lse_own = torch.empty(B, T, H, device=dev)
-    lse_tot = torch.empty(B, T, H, device=dev)
-
-    def k_sum():
-        hsa.summarize(t["K"], t["Ql"], S, ksum=ksum, ent=ent, lse_l=lse_l)
-
-    def k_score():
-        hsa.score_topk(t["Q"], ksum, ent, K, S, 0, T, Hkv=Hkv, idx=idx, score=score)
-
-    def k_attend():
-        hsa.attend_fuse(t["Q"], t["K"], t["V"], idx, score, S, O=O, lse_own=lse_own,
-                        lse_tot=lse_tot)
-
-    def step():
-        k_sum()
-        k_score()
-        k_attend()
+    ev_ms, wall_ms = make_timers(torch, stream)
 
     if args.pmc_run:
-        for _ in range(3):
-            step()
+        wname = args.pmc_run
+        if wname == "decode_128k":
+            wd = synth.workloads()[wname]
+            xd = synth.make_inputs(wd)
+            td = {k: torch.from_numpy(xd[k]).to(dev, torch.bfloat16) for k in ("Q", "K", "V", "Ql")}
+            del xd
+            measure_decode(torch, hsa, stream, td, wd, wd.K, 0, td["K"], td["V"], 16, dev)
+        else:
+            w, x, t, f, calls = prefill_setup(torch, hsa, synth, dev, wname)
+            for _ in range(3):
+                for fn in calls.values():
+                    fn()
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -198,251 +451,110 @@ def main():
         log("pmc run done")
         return
 
+    extra = {}
+    cpu_extra = {}
+    oracle = None
+    if not args.no_cpu_baseline:
+        import oracle as oracle_mod
+        oracle = oracle_mod
+        path = oracle.use_native_build(tempfile.mkdtemp(prefix="hils_oracle_"))
+        extra["cpu_host"] = {"nproc": os.cpu_count(), "oracle_build": "g++ -O3 -march=native, "
+                             "one thread", "library": os.path.basename(path)}
+
+    # ---------------------------------------------- headline: the 7B-class GQA prefill
+    hw, hx, ht, hf, hcalls = prefill_setup(torch, hsa, synth, dev, "prefill_7b_gqa")
+
+    def step():
+        hcalls["summarize"]()
+        hcalls["score_topk"]()
+        hcalls["attend_fuse"]()
+
     log("warmup")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = wall_ms(step, args.steps)
+    head = measure_prefill(torch, ev_ms, hw, hf, {k: hcalls[k] for k in
+                                                   ("summarize", "score_topk", "attend_fuse")},
+                           args.steps, "prefill_7b_gqa")
+    head["step_ms_wallclock"] = ms
+    dominant = max(head["kernels_ms"], key=head["kernels_ms"].get)
+    roof = dict(head["roofline"][dominant])
+    extra["prefill_7b_gqa"] = head
+    cpu = None
+    if oracle is not None:
+        log("cpu baseline: 7B GQA prefill")
+        cpu = cpu_prefill(oracle, hx, hw, 8192, 0)
+    del hx, ht, hf, hcalls
+    torch.cuda.empty_cache()
 
-    # per-kernel durations with HIP events on the stream the kernels run on
-    kern = {}
-    for name, fn in (("summarize", k_sum), ("score_topk", k_score), ("attend_fuse", k_attend)):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        for _ in range(args.steps):
-            fn()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        kern[name] = ev[0].elapsed_time(ev[1]) / args.steps  # ms per launch
-    idx_host = idx.cpu().numpy()
-    cnt = algorithmic_counts(w, idx_host)
-    ach_attend = cnt["attend_fuse"]["flops"] / (kern["attend_fuse"] * 1e-3) / 1e12
-    ach_score_bw = cnt["score_topk"]["bytes"] / (kern["score_topk"] * 1e-3) / 1e9
-    ach_sum = cnt["summarize"]["bytes"] / (kern["summarize"] * 1e-3) / 1e9
-    dominant = max(kern, key=kern.get)
-    if dominant == "summarize":
-        roof = dict(bound="hbm", achieved=ach_sum, peak=HBM_PEAK_GBS, unit="GB/s")
-    elif dominant == "score_topk":
-        roof = dict(bound="hbm", achieved=ach_score_bw, peak=HBM_PEAK_GBS, unit="GB/s")
-    else:
-        roof = dict(bound="mfma", achieved=ach_attend, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    rec = read_traffic_record() if dominant == "attend_fuse" else None
-    roof["traffic"] = rec["attend_call_bytes"] if rec else None
-    roof["kernel"] = ("hils_attend_fuse (k_kv_prep + k_attend_mfma)" if dominant == "attend_fuse"
-                      else dominant)
-    roof["ms_per_launch"] = kern[dominant]
-    roof["algorithmic"] = (cnt["attend_fuse"] if dominant == "attend_fuse"
-                           else cnt[dominant])
-
-    extra = {"kernels_ms": kern,
-             "attend_tflops": ach_attend, "summarize_gbs": ach_sum, "score_topk_gbs": ach_score_bw,
-             "key_visits": cnt["key_visits"], "candidates": cnt["candidates"]}
-
-    # ---------------------------------------------------------------- decode
-    if not args.no_decode:
-        wd = synth.workloads()["decode_128k"]
-        log("generating decode_128k inputs")
-        xd = synth.make_inputs(wd)
-        td = {k: torch.from_numpy(xd[k]).to(dev, torch.bfloat16) for k in ("Q", "K", "V", "Ql")}
-        del xd
-        NCd = wd.T // wd.S
-        p0 = wd.q_pos0
-        nsteps = min(args.decode_steps, wd.rows_q)
-
-        def decode_run(Kd, wnd, Kc, Vc):
-            """(eager us/step, HIP-graph us/step) of the decode sequence with top-Kd,
-            local branch `wnd` (0: own chunk) and the cache Kc, Vc (device or pinned host)."""
-            dk = torch.empty(1, NCd, wd.H, wd.d, device=dev)
-            de = torch.empty(1, NCd, wd.H, device=dev)
-            dl = torch.empty(1, NCd, wd.H, device=dev)
-            hsa.summarize(Kc, td["Ql"], wd.S, 0, p0 // wd.S, Tkv=p0, ksum=dk, ent=de,
-                          lse_l=dl)
-            didx = torch.empty(1, 1, wd.H, Kd, dtype=torch.int32, device=dev)
-            dsc = torch.empty(1, 1, wd.H, Kd, device=dev)
-            dO = torch.empty(1, 1, wd.H, wd.d, dtype=torch.bfloat16, device=dev)
-            dlo = torch.empty(1, 1, wd.H, device=dev)
-            dlt = torch.empty(1, 1, wd.H, device=dev)
-
-            def dstep(s):
-                p = p0 + s
-                if (p % wd.S) == 0 and p > p0:  # chunk p/S - 1 just completed
-                    c = p // wd.S - 1
-                    hsa.summarize(Kc, td["Ql"], wd.S, c, c + 1, Tkv=p, ksum=dk, ent=de,
-                                  lse_l=dl)
-                q = td["Q"][:, s:s + 1]
-                hsa.score_topk(q, dk, de, Kd, wd.S, p, p + 1, Hkv=wd.Hkv, idx=didx, score=dsc,
-                               window=wnd)
-                hsa.attend_fuse(q, Kc, Vc, didx, dsc, wd.S, p, p + 1, O=dO,
-                                lse_own=dlo, lse_tot=dlt, window=wnd)
-
-            for s in range(8):
-                dstep(s)
-            torch.cuda.synchronize()
-            # eager (one host call per kernel launch)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            ev[0].record(stream)
-            for s in range(nsteps):
-                dstep(s)
-            ev[1].record(stream)
-            torch.cuda.synchronize()
-            eager = ev[0].elapsed_time(ev[1]) * 1e3 / nsteps
-            # HIP graph: the whole sequence of decode steps captured once and replayed
-            graph = torch.cuda.CUDAGraph()
-            cap = torch.cuda.Stream()
-            cap.wait_stream(stream)
-            with torch.cuda.stream(cap):
-                with torch.cuda.graph(graph, stream=cap):
-                    for s in range(nsteps):
-                        dstep(s)
-            stream.wait_stream(cap)
-            graph.replay()
-            torch.cuda.synchronize()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            reps = 3
-            ev[0].record(stream)
-            for _ in range(reps):
-                graph.replay()
-            ev[1].record(stream)
-            torch.cuda.synchronize()
-            return eager, ev[0].elapsed_time(ev[1]) * 1e3 / (nsteps * reps)
-
-        eager_us, dec_us = decode_run(wd.K, 0, td["K"], td["V"])
-        dec_bytes = (NCd * wd.H * (wd.d + 1) * 4 + wd.K * wd.S * wd.H * wd.d * 2 * 2
-                     + 32 * wd.H * wd.d * 2 * 2)
-        extra["decode_us_per_token_eager"] = eager_us
-        extra["decode_us_per_token"] = dec_us
-        extra["decode_gbs_wallclock"] = dec_bytes / (dec_us * 1e-6) / 1e9
-        extra["decode_steps"] = nsteps
-        # the pages' main setting: top-32 and a sliding window of 512 keys
-        eager_m, dec_m = decode_run(32, 512, td["K"], td["V"])
-        extra["decode_main_us_per_token"] = dec_m
-        extra["decode_main_us_per_token_eager"] = eager_m
-        extra["decode_main"] = "K=32, sliding window of 512 keys, same cache and steps"
-        # the cache in pinned host memory: each step reads its selected chunks and its
-        # own chunk over the host link; summaries and outputs stay on the GPU
+    # ---------------------------------------------- 128K decode
+    wd = synth.workloads()["decode_128k"]
+    log("generating decode_128k inputs")
+    xd = synth.make_inputs(wd)
+    td = {k: torch.from_numpy(xd[k]).to(dev, torch.bfloat16) for k in ("Q", "K", "V", "Ql")}
+    nsteps = min(args.decode_steps, wd.rows_q)
+    rec, didx = measure_decode(torch, hsa, stream, td, wd, wd.K, 0, td["K"], td["V"], nsteps, dev)
+    extra["decode_128k"] = rec
+    if not args.no_extra_configs:
+        rec, _ = measure_decode(torch, hsa, stream, td, wd, 32, 512, td["K"], td["V"], nsteps, dev)
+        extra["decode_128k_main"] = rec
         Kh = torch.empty(td["K"].shape, dtype=torch.bfloat16, pin_memory=True)
         Vh = torch.empty(td["V"].shape, dtype=torch.bfloat16, pin_memory=True)
         Kh.copy_(td["K"])
         Vh.copy_(td["V"])
         torch.cuda.synchronize()
-        eager_h, dec_h = decode_run(wd.K, 0, Kh, Vh)
-        extra["decode_host_cache_us_per_token"] = dec_h
-        extra["decode_host_cache_us_per_token_eager"] = eager_h
-        extra["decode_host_cache_gbs"] = (wd.K + 1) * wd.S * wd.H * wd.d * 2 * 2 / (dec_h * 1e-6) / 1e9
+        rec, _ = measure_decode(torch, hsa, stream, td, wd, wd.K, 0, Kh, Vh, nsteps, dev)
+        rec["cache"] = "K and V in pinned host memory, read through their device mapping"
+        rec["host_link_gbs"] = ((wd.K + 1) * wd.S * wd.H * wd.d * 2 * 2
+                                / (rec["us_per_token"] * 1e-6) / 1e9)
+        extra["decode_128k_host_cache"] = rec
         del Kh, Vh
+        rec, _ = measure_decode(torch, hsa, stream, td, wd, wd.K, 0, td["K"], td["V"], nsteps,
+                                dev, nb=16)
+        rec["rows"] = ("16 query positions per call, a stand-in for 16 sequences decoding "
+                       "together: per-row work and bytes are a sequence's")
+        extra["decode_128k_16_rows"] = rec
+    if oracle is not None:
+        log("cpu baseline: 128K decode")
+        cpu_extra["decode_128k"] = cpu_decode(oracle, xd, wd, wd.K, nsteps)
+    del xd, td
+    torch.cuda.empty_cache()
 
-    # ------------------------------------------- 7B-class GQA prefill, training step
-    def ev_ms(fn, reps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        for _ in range(reps):
-            fn()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) / reps
-
+    # ---------------------------------------------- the other prefill and training workloads
+    runs = [("prefill_345m", "prefill_345m", {})]
     if not args.no_extra_configs:
-        # the 7B-class GQA prefill also with group-max selection (one chunk set per kv
-        # head); the 345M prefill and the training step in the pages' main setting
-        # (K = 32, a sliding window of 512 keys); the training step with a Q-Cal
-        # scoring query
-        groups = (
-            ("prefill_7b_gqa", (("prefill_7b_gqa", {}),
-                                ("prefill_7b_gqa_group_max", {"group": True}))),
-            ("prefill_345m", (("prefill_345m_main", {"K": 32, "window": 512}),)),
-            ("train_345m", (("train_345m", {}), ("train_345m_qcal", {"qcal": True}),
-                            ("train_345m_main", {"K": 32, "window": 512}))),
-        )
-        for wname, recs in groups:
-            w0 = synth.workloads()[wname]
-            log(f"generating {wname} inputs")
-            xx = synth.make_inputs(w0)
-            keys = ("Q", "K", "V", "Ql") + (("dO",) if w0.need_dO else ())
-            tx = {k: torch.from_numpy(xx[k]).to(dev, torch.bfloat16) for k in keys}
-            if any(o.get("qcal") for _, o in recs):
-                tx["Qs"] = torch.from_numpy(synth.scoring_query(w0, xx)).to(dev, torch.bfloat16)
-            del xx
-            for rname, opt in recs:
-                wx = dataclasses.replace(w0, K=opt.get("K", w0.K))
-                group, wnd = opt.get("group", False), opt.get("window", 0)
-                Qsx = tx["Qs"] if opt.get("qcal") else None
-                Qsel = tx["Q"] if Qsx is None else Qsx   # the query the chunk scores use
-                fw = hsa.forward(tx["Q"], tx["K"], tx["V"], tx["Ql"], wx.K, wx.S, group=group,
-                                 Qs=Qsx, window=wnd)
-                ksx, enx, llx, ix, scx = (fw[k] for k in ("ksum", "ent", "lse_l", "idx", "score"))
-                Ox, lox, ltx = fw["O"], fw["lse_own"], fw["lse_tot"]
-                calls = {
-                    "summarize": lambda: hsa.summarize(tx["K"], tx["Ql"], wx.S, ksum=ksx,
-                                                       ent=enx, lse_l=llx),
-                    "score_topk": lambda: hsa.score_topk(Qsel, ksx, enx, wx.K, wx.S, 0, wx.T,
-                                                         Hkv=wx.Hkv, idx=ix, score=scx,
-                                                         group=group, window=wnd),
-                    "attend_fuse": lambda: hsa.attend_fuse(tx["Q"], tx["K"], tx["V"], ix, scx,
-                                                           wx.S, O=Ox, lse_own=lox, lse_tot=ltx,
-                                                           window=wnd),
-                }
-                if wx.need_dO:
-                    calls["backward"] = lambda: hsa.backward(tx["Q"], tx["K"], tx["V"], tx["Ql"],
-                                                             ksx, enx, llx, ix, scx, ltx, Ox,
-                                                             tx["dO"], wx.S, Qs=Qsx, window=wnd)
-                for fn in calls.values():
-                    fn()
-                torch.cuda.synchronize()
-                km = {k: ev_ms(fn, 5) for k, fn in calls.items()}
-                cx = algorithmic_counts(wx, ix.cpu().numpy(), wnd)
-                fwd_ms = km["summarize"] + km["score_topk"] + km["attend_fuse"]
-                rec = {"kernels_ms": km, "forward_ms": fwd_ms,
-                       "attend_tflops": cx["attend_fuse"]["flops"] / (km["attend_fuse"] * 1e-3) / 1e12,
-                       "score_topk_tflops": cx["score_topk"]["flops"] / (km["score_topk"] * 1e-3) / 1e12,
-                       "summarize_gbs": cx["summarize"]["bytes"] / (km["summarize"] * 1e-3) / 1e9,
-                       "K": wx.K}
-                if wx.need_dO:
-                    bwd_flops = 10 * wx.d * cx["key_visits"]
-                    rec["backward_tflops"] = bwd_flops / (km["backward"] * 1e-3) / 1e12
-                    rec["train_tokens_per_s"] = wx.B * wx.T / ((fwd_ms + km["backward"]) * 1e-3)
-                else:
-                    rec["prefill_tokens_per_s"] = wx.B * wx.T / (fwd_ms * 1e-3)
-                if group:
-                    rec["selection"] = "group max over the 4 query heads of each kv head"
-                if Qsx is not None:
-                    rec["scoring_query"] = "Q-Cal: separate scoring query, dQs returned apart"
-                if wnd:
-                    rec["local_branch"] = f"sliding window of {wnd} keys"
-                extra[rname] = rec
-                del fw, calls
-            del tx
-            torch.cuda.empty_cache()
-
-    # ---------------------------------------------------------------- CPU baseline
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        rng = np.random.default_rng(0)
-        nrows = 4096
-        rows = np.sort(rng.choice(B * T * H, size=nrows, replace=False))
-        log(f"cpu baseline: oracle on {nrows} sampled rows")
-        t0 = time.perf_counter()
-        oks, oent, _ = oracle.summarize(x["K"], x["Ql"], S)
-        t_sum = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        oidx, osc, _ = oracle.score_topk(x["Q"], oks, oent, S, K, rows=rows)
-        oracle.attend_fuse(x["Q"], x["K"], x["V"], oidx, osc, S, rows=rows)
-        t_rows = time.perf_counter() - t0
-        t_full = t_sum + t_rows * (B * T * H) / nrows
-        cpu = {"value": B * T / t_full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"all {NC * H} landmark summaries + {nrows} of {B * T * H} (row, head) "
-                         f"queries scored/selected/attended, scaled to the full step "
-                         f"({t_sum:.2f}s + {t_rows:.2f}s measured)"}
+        runs += [("prefill_7b_gqa_group_max", "prefill_7b_gqa", {"group": True}),
+                 ("prefill_345m_main", "prefill_345m", {"K": 32, "window": 512}),
+                 ("train_345m", "train_345m", {}),
+                 ("train_345m_qcal", "train_345m", {"qcal": True}),
+                 ("train_345m_main", "train_345m", {"K": 32, "window": 512})]
+    for rname, wname, opt in runs:
+        w, x, t, f, calls = prefill_setup(torch, hsa, synth, dev, wname, **opt)
+        rec = measure_prefill(torch, ev_ms, w, f, calls, 5, rname if not opt else "-",
+                              opt.get("window", 0))
+        if opt.get("group"):
+            rec["selection"] = "group max over the 4 query heads of each kv head"
+        if opt.get("qcal"):
+            rec["scoring_query"] = "Q-Cal: separate scoring query, dQs returned apart"
+        if opt.get("window"):
+            rec["local_branch"] = f"sliding window of {opt['window']} keys"
+        extra[rname] = rec
+        if oracle is not None and rname == "prefill_345m":
+            log("cpu baseline: 345M prefill")
+            cpu_extra["prefill_345m"] = cpu_prefill(oracle, x, w, 4096, 1)
+        if oracle is not None and rname == "train_345m":
+            log("cpu baseline: training step")
+            cpu_extra["train_345m"] = cpu_train(oracle, x, w)
+        del x, t, f, calls
+        torch.cuda.empty_cache()
+    if cpu_extra:
+        extra["cpu_baselines"] = cpu_extra
 
     out = {
         "metric": "HiLS prefill tokens/s + 128K decode us/token; % of HBM BW / bf16 MFMA peak",
-        "value": B * T / (ms * 1e-3),
+        "value": hw.B * hw.T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -453,9 +565,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "prefill_345m: B=1 H=16 Hkv=16 d=64 T=8192 S=64 K=16, N(0,1) "
-                               "+ 1 planted-peak chunk", "global_batch": B, "seq_len": T,
-                   "parallelism": "single GPU"},
+        "config": {"workload": "prefill_7b_gqa: B=1 H=32 Hkv=8 d=128 T=32768 S=64 K=16, N(0,1) "
+                               "+ 3 planted-peak and 26 near-uniform chunks, per-head selection",
+                   "global_batch": hw.B, "seq_len": hw.T, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "extra": extra,

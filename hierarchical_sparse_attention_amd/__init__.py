@@ -233,14 +233,14 @@ def attend_fuse(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Te
 def decode_workspace(Q: torch.Tensor, K: torch.Tensor, ksum: torch.Tensor, K_sel: int,
                      S: int = 64, q_pos0: int = 0, Tkv: Optional[int] = None,
                      window: int = 0) -> torch.Tensor:
-    """A zeroed workspace for decode() calls of these shapes (allocate it once, outside
-    any captured graph, and pass it to every call)."""
+    """A workspace for decode() calls of these shapes (allocate it once, outside any
+    captured graph, and pass it to every call)."""
     B, Tq, H, d = Q.shape
     Tcap, Hkv = K.shape[1], K.shape[2]
     Tkv = q_pos0 + Tq if Tkv is None else Tkv
     dims = make_dims(B, Tq, Tkv, H, Hkv, d, S, K_sel, _dtype_code(Q), q_pos0, 0.0, Tcap,
                      ksum.shape[1], window=window)
-    return torch.zeros(max(workspace_size(dims, OP_DECODE), 256), dtype=torch.uint8,
+    return torch.empty(max(workspace_size(dims, OP_DECODE), 256), dtype=torch.uint8,
                        device=Q.device)
 
 
@@ -274,7 +274,7 @@ def decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, ksum: torch.Tensor
                      window=window)
     need = workspace_size(dims, OP_DECODE)
     if ws is None:
-        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _need(ws, "ws", dtype=torch.uint8)
     _check("hils_decode", lib().hils_decode(
         ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(ksum), _ptr(ent), _ptr(idx),

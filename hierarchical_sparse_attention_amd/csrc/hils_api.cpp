@@ -111,11 +111,9 @@ hils_status backward_shape_ok(const hils::Dims& dm) {
 
 hils_status from_hip(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_ERR_HIP; }
 
-// Workspace of hils_decode: the fused kernel's counters and lists, or else the
-// larger of the two calls it is made of (they run one after the other on the stream).
+// Workspace of hils_decode: the larger of the two calls it is made of (they run
+// one after the other on the stream, so they can share it).
 size_t decode_ws(const hils::Dims& dm) {
-  const size_t f = hils::decode_fused_ws_bytes(dm);
-  if (f > 0) return f;
   const size_t a = hils::score_topk_ws_bytes(dm), b = hils::attend_ws_bytes(dm);
   return a > b ? a : b;
 }
@@ -240,11 +238,8 @@ hils_status hils_decode(const hils_dims* dims, const void* Q, const void* K, con
   const void *Kd = nullptr, *Vd = nullptr;
   if ((st = kv_view(K, &Kd)) != HILS_OK || (st = kv_view(V, &Vd)) != HILS_OK) return st;
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  hipError_t err = hipSuccess;
-  if (hils::decode_fused_try(dm, Q, Kd, Vd, ksum, ent, idx, score, O, lse_own, lse_tot, ws, hs,
-                             &err))
-    return from_hip(err);
-  if ((err = hils::launch_score_topk(dm, Q, ksum, ent, idx, score, ws, hs)) != hipSuccess)
+  hipError_t err = hils::launch_score_topk(dm, Q, ksum, ent, idx, score, ws, hs);
+  if (err != hipSuccess)
     return HILS_ERR_HIP;
   return from_hip(hils::launch_attend_fuse(dm, Q, Kd, Vd, idx, score, O, lse_own, lse_tot, ws, hs));
 }

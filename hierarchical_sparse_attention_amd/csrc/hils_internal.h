@@ -316,14 +316,6 @@ hipError_t launch_attend_fuse(const Dims& dm, const void* Q, const void* K, cons
                               const int32_t* idx, const float* score, void* O, float* lse_own,
                               float* lse_tot, void* ws, hipStream_t st);
 
-// Fused decode step (scoring, selection, attention, fusion in one launch) for bf16
-// per-head selection; returns false when it does not apply.
-size_t decode_fused_ws_bytes(const Dims& dm);
-size_t decode_fused_counter_bytes(const Dims& dm);
-bool decode_fused_try(const Dims& dm, const void* Q, const void* K, const void* V,
-                      const float* ksum, const float* ent, int32_t* idx, float* score, void* O,
-                      float* lse_own, float* lse_tot, void* ws, hipStream_t st, hipError_t* err);
-
 size_t backward_ws_bytes(const Dims& dm);
 size_t backward_mfma_ws_bytes(const Dims& dm);
 // bf16, d = 64 prefill backward on matrix cores; returns false when it does not apply.

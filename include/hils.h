@@ -193,17 +193,12 @@ hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K
  * One decode step of the query rows at positions q_pos0 .. q_pos0 + Tq - 1 (note
  * §5.2 chunk scores and top-K; note §5.3 hierarchical softmax; the note's key
  * result 5 times HiLS decode per token): the selection of hils_score_topk and the
- * attention of hils_attend_fuse in one call, with the same results (idx and score
- * bit for bit; O, lse_own, lse_tot as hils_attend_fuse computes them from that
- * selection). For bf16 with per-head selection it runs as one kernel launch:
- * workgroups score candidate splits and write local top-K lists, the last
- * workgroup of each row merges them and attends the selected chunks and the
- * local branch. Otherwise it enqueues the two calls' kernels in turn.
- * The workspace (hils_workspace_size with HILS_OP_DECODE) begins with per-row
- * counters that must be zero when a call starts; every call leaves them zero.
- * Zero the workspace once when it is allocated; calls with the same workspace
- * may then follow one another (also inside a captured graph) as long as no other
- * call writes into it in between. K and V may be pinned host memory as for
+ * attention of hils_attend_fuse in one call, with the same results: it enqueues
+ * the selection's kernels (for a few rows: candidate splits scored into local
+ * top-K lists, then a merge of the lists) and the decode attention's kernels (one
+ * wavefront per selected or local chunk of a row, then the fusion of the slots).
+ * ws is one workspace of hils_workspace_size(.., HILS_OP_DECODE, ..) bytes for
+ * both; its contents do not matter. K and V may be pinned host memory as for
  * hils_attend_fuse; lse_own and lse_tot may be NULL.
  */
 hils_status hils_decode(const hils_dims* dims, const void* Q, const void* K, const void* V,

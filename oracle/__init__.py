@@ -33,11 +33,26 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
-def lib():
+def use_native_build(directory: str) -> str:
+    """Compile the oracle with -O3 -march=native (vectorisation allowed, still one
+    thread) into `directory` on the machine that will run it, and load that build
+    in place of the portable one. Used by the benchmark's CPU baseline."""
+    global _lib
+    os.makedirs(directory, exist_ok=True)
+    path = os.path.join(directory, "libhils_oracle_native.so")
+    subprocess.check_call(["g++", "-O3", "-march=native", "-std=c++17", "-shared", "-fPIC", "-o",
+                           path, _SRC])
+    _lib = None
+    lib(path)
+    return path
+
+
+def lib(path: Optional[str] = None):
     global _lib
     if _lib is None:
-        build(force=False)
-        L = ctypes.CDLL(_LIB)
+        if path is None:
+            build(force=False)
+        L = ctypes.CDLL(path or _LIB)
         ci, cl, cd = ctypes.c_int, ctypes.c_long, ctypes.c_double
         L.oracle_summarize.argtypes = [ci, ci, ci, ci, ci, ci, ci, cd, _D, _D, ci, ci, _D, _D, _D]
         L.oracle_score_topk.argtypes = [ci, ci, cl, ci, ci, ci, ci, ci, cd, cl, _D, _D, _D, cl,

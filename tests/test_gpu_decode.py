@@ -1,10 +1,8 @@
 """hils_decode (one decode step in one call) through the C ABI.
 
-Its results are those of hils_score_topk followed by hils_attend_fuse: the
-selection and scores bit for bit, and for bf16 per-head selection (the fused
-single-launch kernel) the outputs and log-masses bit for bit too (same slot and
-fusion arithmetic in the same order). Also checked against the oracle, over many
-steps in a row on one workspace (the per-row counters reset themselves), with
+Its results are those of hils_score_topk followed by hils_attend_fuse, bit for
+bit (selection, scores, outputs, log-masses). Also checked against the oracle, over many
+steps in a row on one workspace (whose contents do not matter), with
 windows, K = 64, several rows per call, rows with no candidates, d = 128, float32
 (two-call fallback) and a host-resident cache.
 """
@@ -57,7 +55,6 @@ def test_decode_steps_match_two_calls_and_oracle(name):
     # positions: the first chunk (no candidates), chunk edges, late rows
     starts = [0, 63, 64, 1000, w.T // 2 + 5, w.T - 64, w.T - nq]
     ws = None
-    fused_bitwise = w.dtype == "bf16"
     for p in starts:
         q = t["Q"][:, p:p + nq].contiguous()
         if ws is None:
@@ -72,10 +69,9 @@ def test_decode_steps_match_two_calls_and_oracle(name):
         torch.cuda.synchronize()
         assert torch.equal(got[0], idx), p
         assert torch.equal(got[1], sc), p
-        if fused_bitwise:
-            assert torch.equal(got[2], O), p
-            assert torch.equal(got[4], lt), p
-            assert torch.equal(got[3], lo), p
+        assert torch.equal(got[2], O), p
+        assert torch.equal(got[4], lt), p
+        assert torch.equal(got[3], lo), p
         qn = x["Q"][:, p:p + nq]
         oidx, osc, ogap = oracle.score_topk(qn, oks, oent, w.S, w.K, q_pos0=p, window=W)
         oO, olo, olt = oracle.attend_fuse(qn, x["K"][:, :p + nq], x["V"][:, :p + nq], oidx, osc,
@@ -89,19 +85,22 @@ def test_decode_steps_match_two_calls_and_oracle(name):
         assert_close(host(got[3])[eq], olo[eq], TOL_F32, f"lse_own {p}")
 
 
-def test_decode_workspace_counters_stay_zero():
-    """The per-row counters at the start of the workspace are zero after every call."""
+def test_decode_workspace_contents_do_not_matter():
+    """A workspace full of arbitrary bytes gives the same results as a fresh one."""
     w, W, nq = CASES["bf16_d64"]
     x = synth.make_inputs(w)
     t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
     ksum, ent, _ = hsa.summarize(t["K"], t["Ql"], w.S)
     ws = hsa.decode_workspace(t["Q"][:, :1], t["K"], ksum, w.K, w.S, w.T - 1, w.T)
-    for p in range(w.T - 40, w.T):
-        hsa.decode(t["Q"][:, p:p + 1].contiguous(), t["K"], t["V"], ksum, ent, w.K, w.S,
-                   q_pos0=p, Tkv=p + 1, ws=ws)
-    torch.cuda.synchronize()
-    rows = w.B * w.H
-    assert int(ws[:4 * rows].view(torch.int32).abs().sum()) == 0
+    for p in range(w.T - 40, w.T, 7):
+        q = t["Q"][:, p:p + 1].contiguous()
+        ws.fill_(0xA5)
+        a = hsa.decode(q, t["K"], t["V"], ksum, ent, w.K, w.S, q_pos0=p, Tkv=p + 1, ws=ws)
+        ws.fill_(0xFF)
+        b = hsa.decode(q, t["K"], t["V"], ksum, ent, w.K, w.S, q_pos0=p, Tkv=p + 1, ws=ws)
+        torch.cuda.synchronize()
+        for u, v in zip(a, b):
+            assert torch.equal(u, v), p
 
 
 def test_decode_full_size_cache_steps():
@@ -144,8 +143,8 @@ def test_decode_full_size_cache_steps():
 
 
 def test_decode_host_resident_cache():
-    """K and V in pinned host memory: the fused step reads the selected chunks and the
-    local branch through the device mapping; results equal the device-resident cache."""
+    """K and V in pinned host memory: the step reads the selected chunks and the local
+    branch through the device mapping; results equal the device-resident cache."""
     w, W, nq = CASES["bf16_d64"]
     x = synth.make_inputs(w)
     t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
