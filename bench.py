@@ -70,6 +70,9 @@ def parse():
                     help="run 3 steps of one workload and a calibration copy, for counters")
     ap.add_argument("--traffic", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs into the workload's record")
+    ap.add_argument("--counters", nargs=2, metavar=("WORKLOAD", "DIR"),
+                    help="summarise the counter passes DIR/p1..p4 of a --pmc-run of WORKLOAD "
+                         "(FETCH_SIZE, WRITE_SIZE, SQ and TCC counters) into profiles/")
     return ap.parse_args()
 
 
@@ -121,7 +124,8 @@ def write_traffic_record(workload, fetch_csv, write_csv):
     for name in sorted(set(fetch) | set(write)):
         if "neg" in name:
             continue
-        short = name.split("(")[0].split("<")[0].split("::")[-1].strip()
+        short = (name.replace("void ", "").replace("hils::(anonymous namespace)::", "")
+                 .split("(")[0].split("<")[0].split("::")[-1].strip())
         rec["kernels"][name] = {"short": short,
                                 "fetch_bytes": fetch.get(name, 0.0) * f_scale,
                                 "write_bytes": write.get(name, 0.0) * w_scale}
@@ -129,6 +133,87 @@ def write_traffic_record(workload, fetch_csv, write_csv):
     with open(traffic_path(workload), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+PMC_PASSES = ("FETCH_SIZE", "WRITE_SIZE",
+              "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 "
+              "SQ_BUSY_CYCLES SQ_WAVES GRBM_GUI_ACTIVE",
+              "TCC_HIT_sum TCC_MISS_sum SQ_WAIT_INST_ANY SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT")
+
+
+def write_counter_summary(workload, directory):
+    """profiles/counters_<workload>.txt: per kernel of a --pmc-run, the average per
+    dispatch of every counter of the four passes, the dispatch duration and derived
+    figures; and the traffic record from passes 1 and 2."""
+    import csv
+    import glob
+
+    def load(i):
+        path = glob.glob(os.path.join(directory, f"p{i}", "*counter_collection.csv"))[0]
+        return path, list(csv.DictReader(open(path)))
+
+    per = {}   # kernel -> counter -> [values]
+    dur = {}
+    for i in range(1, 5):
+        _, rows = load(i)
+        acc = {}
+        for r in rows:
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            acc.setdefault(key, {"name": r["Kernel_Name"], "c": {}, "t": (int(r["Start_Timestamp"]), int(r["End_Timestamp"])), "vgpr": r["VGPR_Count"], "lds": r["LDS_Block_Size"]})
+            acc[key]["c"][r["Counter_Name"]] = acc[key]["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for v in acc.values():
+            d = per.setdefault(v["name"], {})
+            for cn, cv in v["c"].items():
+                d.setdefault(cn, []).append(cv)
+            if i == 3:
+                dur.setdefault(v["name"], []).append((v["t"][1] - v["t"][0]) / 1e3)
+            d.setdefault("_vgpr", [v["vgpr"]])
+            d.setdefault("_lds", [v["lds"]])
+    write_traffic_record(workload, load(1)[0], load(2)[0])
+    rec = json.load(open(traffic_path(workload)))
+    scale = {"FETCH_SIZE": rec["fetch_scale"], "WRITE_SIZE": rec["write_scale"]}
+    lines = [f"rocprofv3 counters per kernel, {workload} (bench.py --pmc-run {workload}: the "
+             f"workload's inputs, 3 steps, then a 256 MiB elementwise copy for calibration), MI355X",
+             "commands, one pass each (cd /tmp && export TMPDIR=/tmp first):"]
+    for i, c in enumerate(PMC_PASSES, 1):
+        lines.append(f"  timeout -s KILL 240 rocprofv3 --pmc {c} --output-format csv -d <dir>/p{i} "
+                     f"-o pmc -- python3 bench.py --pmc-run {workload}")
+    lines.append(f"  python3 bench.py --counters {workload} <dir>   (writes this file and "
+                 f"traffic_{workload}.json)")
+    lines.append(f"FETCH_SIZE / WRITE_SIZE are scaled to bytes by the calibration copy "
+                 f"(fetch x{rec['fetch_scale']:.3f}, write x{rec['write_scale']:.3f}); other "
+                 "counters are raw sums over the GPU per dispatch, averaged over dispatches.")
+    lines.append("mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs); "
+                 "l2_hit = TCC_HIT / (TCC_HIT + TCC_MISS); us = dispatch duration in pass 3.")
+    lines.append("")
+    hdr = (f"{'kernel':44s} {'calls':>5s} {'us':>9s} {'fetch MB':>9s} {'write MB':>9s} "
+           f"{'mfma_busy':>9s} {'MFMA inst':>10s} {'VALU inst':>11s} {'TRANS':>10s} {'l2_hit':>7s} "
+           f"{'LDS inst':>10s} {'LDS bkcf':>10s} {'vgpr':>5s}")
+    lines.append(hdr)
+    avg = lambda xs: sum(xs) / len(xs) if xs else float("nan")  # noqa: E731
+    order = sorted(per, key=lambda k: -avg(dur.get(k, [0])) * len(dur.get(k, [0])))
+    for name in order:
+        if "neg" in name:
+            continue
+        d = per[name]
+        short = (name.replace("void ", "").replace("hils::(anonymous namespace)::", "")
+                 .replace("at::native::", "").split("(")[0])
+        g = avg(d.get("GRBM_GUI_ACTIVE", []))
+        busy = avg(d.get("SQ_VALU_MFMA_BUSY_CYCLES", [])) / (g * 256 * 4) if g else float("nan")
+        hit, miss = avg(d.get("TCC_HIT_sum", [])), avg(d.get("TCC_MISS_sum", []))
+        l2 = hit / (hit + miss) if hit + miss else float("nan")
+        lines.append(
+            f"{short[:44]:44s} {len(dur.get(name, [])):5d} {avg(dur.get(name, [])):9.2f} "
+            f"{avg(d.get('FETCH_SIZE', [])) * 1024 * scale['FETCH_SIZE'] / 1e6:9.2f} "
+            f"{avg(d.get('WRITE_SIZE', [])) * 1024 * scale['WRITE_SIZE'] / 1e6:9.2f} "
+            f"{busy:9.3f} {avg(d.get('SQ_INSTS_MFMA', [])):10.3g} "
+            f"{avg(d.get('SQ_INSTS_VALU', [])):11.4g} {avg(d.get('SQ_INSTS_VALU_TRANS_F32', [])):10.3g} "
+            f"{l2:7.3f} {avg(d.get('SQ_INSTS_LDS', [])):10.3g} "
+            f"{avg(d.get('SQ_LDS_BANK_CONFLICT', [])):10.3g} {d['_vgpr'][0]:>5s}")
+    out = os.path.join(PROFILES, f"counters_{workload}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def call_traffic(workload, call):
@@ -416,6 +501,9 @@ def main():
     args = parse()
     if args.traffic:
         write_traffic_record(*args.traffic)
+        return
+    if args.counters:
+        write_counter_summary(*args.counters)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
