@@ -53,7 +53,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 template <int D>
 struct Cfg {
-  static constexpr int RMAX = D == 64 ? 256 : 128;  // rows per workgroup
+  static constexpr int RMAX = 256;                  // rows per workgroup
+  // d = 128: the query rows are read from global memory at tile time and the row
+  // lists hold 16-bit entries (the score is read again with the row), so that
+  // 256 rows' accumulators fit in LDS: twice the rows per chunk load of 128
+  static constexpr bool QG = D == 128;
   static constexpr int AP = D + 2;                  // accumulator row pitch (words, even)
   static constexpr int QP = D + 8;                  // LDS query row pitch (bf16)
   static constexpr int KF = 4 * (D / 32);           // K fragments (uint4) per lane per chunk
@@ -374,9 +378,11 @@ __host__ __device__ __forceinline__ int acc_col(int db, int g, int r) {
 
 struct Smem {
   int* acc;       // [R][AP] fixed point (float during the own-chunk phase)
-  uint16_t* qs;   // [R][QP] the workgroup's query rows (bf16)
-  uint32_t* ent;  // row-list entries, chunk-major: rho | k << 16
-  float* lw;      // per entry: its chunk score times log2(e)
+  uint16_t* qs;   // [R][QP] the workgroup's query rows (bf16; none with QG)
+  uint32_t* ent;  // row-list entries, chunk-major: rho | k << 16 (16-bit with QG)
+  uint16_t* ent16;
+  float* lw;      // per entry: its chunk score times log2(e) (none with QG)
+  int* rowoff;    // per row: its global row index relative to workgroup row 0
   int* cnt;
   int* off;
   int* cur;
@@ -386,8 +392,9 @@ struct Smem {
   float* lamx;    // Lambda times log2(e) minus the row's fixed-point shift
   int* fsh;       // per row: fixed-point shift (the row's units are 2^-fsh)
   uint32_t* rvm;  // per row: max |V| over the chunks it reads (float bits)
-  float* vx;      // per chunk: max |V|
-  int* gmx;       // per (row, group of 8 entries): largest id of the group
+  float* vx;      // per chunk: max |V| (set-up only; shares off's space)
+  int* gmx;       // per (row, group of 8 entries): largest id of the group (set-up
+                  // only; shares pm's space)
   float* pm;      // per (row, group of 8 slots): max score and sum of exp(score - max)
   float* pz;
   int* nsel;      // per row: number of terms added to its fixed-point accumulator
@@ -401,20 +408,26 @@ __host__ __device__ inline size_t up16(size_t x) { return (x + 15) & ~(size_t)15
 
 template <int D>
 __host__ __device__ inline size_t smem_bytes(int R, int K, int ncr, int nloc) {
-  return up16((size_t)R * Cfg<D>::AP * 4) + up16((size_t)R * Cfg<D>::QP * 2) +
-         2 * up16((size_t)R * K * 4) + 5 * up16((size_t)(ncr + 1) * 4) + 6 * up16((size_t)R * 4) +
-         3 * up16((size_t)R * ((K + 7) / 8) * 4) + up16((size_t)R * nloc * 8) + 32 * 4;
+  constexpr bool QG = Cfg<D>::QG;
+  return up16((size_t)R * Cfg<D>::AP * 4) + (QG ? 0 : up16((size_t)R * Cfg<D>::QP * 2)) +
+         (QG ? up16((size_t)R * K * 2) : 2 * up16((size_t)R * K * 4)) +
+         4 * up16((size_t)(ncr + 1) * 4) + 7 * up16((size_t)R * 4) +
+         2 * up16((size_t)R * ((K + 7) / 8) * 4) + up16((size_t)R * nloc * 8) + 32 * 4;
 }
 
 template <int D>
 __device__ __forceinline__ Smem carve(char* base, int R, int K, int ncr, int nloc) {
+  constexpr bool QG = Cfg<D>::QG;
   Smem s;
   s.acc = reinterpret_cast<int*>(base); base += up16((size_t)R * Cfg<D>::AP * 4);
-  s.qs = reinterpret_cast<uint16_t*>(base); base += up16((size_t)R * Cfg<D>::QP * 2);
-  s.ent = reinterpret_cast<uint32_t*>(base); base += up16((size_t)R * K * 4);
-  s.lw = reinterpret_cast<float*>(base); base += up16((size_t)R * K * 4);
+  s.qs = reinterpret_cast<uint16_t*>(base); base += QG ? 0 : up16((size_t)R * Cfg<D>::QP * 2);
+  s.ent = reinterpret_cast<uint32_t*>(base);
+  s.ent16 = reinterpret_cast<uint16_t*>(base);
+  base += QG ? up16((size_t)R * K * 2) : up16((size_t)R * K * 4);
+  s.lw = reinterpret_cast<float*>(base); base += QG ? 0 : up16((size_t)R * K * 4);
   s.cnt = reinterpret_cast<int*>(base); base += up16((ncr + 1) * 4);
-  s.off = reinterpret_cast<int*>(base); base += up16((ncr + 1) * 4);
+  s.off = reinterpret_cast<int*>(base);
+  s.vx = reinterpret_cast<float*>(base); base += up16((ncr + 1) * 4);
   s.cur = reinterpret_cast<int*>(base); base += up16((ncr + 1) * 4);
   s.nz = reinterpret_cast<int*>(base); base += up16((ncr + 1) * 4);
   s.lown = reinterpret_cast<float*>(base); base += up16(R * 4);
@@ -422,9 +435,9 @@ __device__ __forceinline__ Smem carve(char* base, int R, int K, int ncr, int nlo
   s.lamx = reinterpret_cast<float*>(base); base += up16(R * 4);
   s.fsh = reinterpret_cast<int*>(base); base += up16(R * 4);
   s.rvm = reinterpret_cast<uint32_t*>(base); base += up16(R * 4);
-  s.vx = reinterpret_cast<float*>(base); base += up16((ncr + 1) * 4);
+  s.rowoff = reinterpret_cast<int*>(base); base += up16(R * 4);
+  s.pm = reinterpret_cast<float*>(base);
   s.gmx = reinterpret_cast<int*>(base); base += up16((size_t)R * ((K + 7) / 8) * 4);
-  s.pm = reinterpret_cast<float*>(base); base += up16((size_t)R * ((K + 7) / 8) * 4);
   s.pz = reinterpret_cast<float*>(base); base += up16((size_t)R * ((K + 7) / 8) * 4);
   s.nsel = reinterpret_cast<int*>(base); base += up16(R * 4);
   s.lpart = reinterpret_cast<float2*>(base); base += up16((size_t)R * nloc * 8);
@@ -467,14 +480,32 @@ __device__ __forceinline__ int block_exclusive_scan(int* a, int n, int* scratch)
   return total;
 }
 
-// Query fragment of workgroup row rho from LDS (zero for an empty tile column).
+// Where the workgroup's query rows and scores are read: Q and score point at
+// workgroup row 0 (position qi0, head g G); rowoff holds each row's offset in rows.
+struct RowSrc {
+  const uint16_t* Q;
+  const float* score;
+};
+
+// Query fragment of workgroup row rho (zero for an empty tile column): from LDS,
+// or with QG from global memory (read unconditionally, at a clamped row).
 template <int D>
-__device__ __forceinline__ void lds_q(uint4* qv, const uint16_t* qs, int rho, bool valid) {
+__device__ __forceinline__ void lds_q(uint4* qv, const Smem& sm, const RowSrc& rs, int rho,
+                                      bool valid) {
   const int g = (threadIdx.x & 63) >> 4;
+  if constexpr (Cfg<D>::QG) {
+    const uint16_t* qr = rs.Q + (long long)sm.rowoff[rho] * D + 8 * g;
 #pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds)
-    qv[ds] = valid ? *reinterpret_cast<const uint4*>(qs + rho * Cfg<D>::QP + 32 * ds + 8 * g)
-                   : make_uint4(0, 0, 0, 0);
+    for (int ds = 0; ds < D / 32; ++ds) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qr + 32 * ds);
+      qv[ds] = valid ? v : make_uint4(0, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+      qv[ds] = valid ? *reinterpret_cast<const uint4*>(sm.qs + rho * Cfg<D>::QP + 32 * ds + 8 * g)
+                     : make_uint4(0, 0, 0, 0);
+  }
 }
 
 // Local-branch work items are the (local chunk, 16-row tile) pairs in chunk
@@ -537,60 +568,78 @@ __device__ __forceinline__ void accumulate_fw(const Smem& sm, const floatx4* o, 
 }
 
 template <int D>
-__device__ __forceinline__ void accumulate_tile(const Smem& sm, const floatx4* o, float z,
-                                                uint32_t en, float lw2, float lamx) {
+__device__ __forceinline__ void accumulate_tile(const Smem& sm, const floatx4* o, float z, int rho,
+                                                float lw2, float lamx) {
   const float fw = fast_exp2(lw2 - lamx) * __builtin_amdgcn_rcpf(z);
-  accumulate_fw<D>(sm, o, (int)(en & 0xFFFFu), fw);
+  accumulate_fw<D>(sm, o, rho, fw);
 }
 
 // Entry word of a chunk's row list: workgroup row (bits 0-15), selection slot
 // (bits 16-21), and bit 30 set when the row's values are too large for the
-// fast-path weights (max |V| >= 2^50).
+// fast-path weights (max |V| >= 2^50). With QG the entry is 16 bits: row (bits
+// 0-7), slot (bits 8-13), slow-path flag (bit 14).
 constexpr uint32_t kEntrySlow = 1u << 30;
+constexpr uint32_t kEntrySlow16 = 1u << 14;
 
 
-// Row-list entry e of a chunk, clamped to the last entry so every LDS read is of
-// real data (a lane past the end computes a copy of the last row and does not
-// accumulate it); reads happen without branches, so they stay in flight.
+// Row-list entry e of a chunk, clamped to the last entry so every read is of real
+// data (a lane past the end computes a copy of the last row and does not
+// accumulate it); reads happen without branches, so they stay in flight. Returns
+// the entry's row, its slow-path flag, its chunk score times log2(e) and the
+// row's query fragments.
 template <int D>
-__device__ __forceinline__ void read_entry(const Smem& sm, int e0, int n, int e, bool* v,
-                                           uint32_t* en, float* lw, float* lm, uint4* q) {
+__device__ __forceinline__ void read_entry(const Smem& sm, const RowSrc& rs, int Ksel, int e0,
+                                           int n, int e, bool* v, int* rho, bool* slow, float* lw,
+                                           float* lm, uint4* q) {
   *v = e < n;
   const int ec = e0 + min(e, n - 1);
-  *en = sm.ent[ec];
-  *lw = sm.lw[ec];
-  const int rho = (int)(*en & 0xFFFFu);
-  *lm = sm.lamx[rho];
   const int g = (threadIdx.x & 63) >> 4;
+  if constexpr (Cfg<D>::QG) {
+    const uint32_t en = sm.ent16[ec];
+    *rho = (int)(en & 0xFFu);
+    *slow = (en & 0x4000u) != 0u;
+    const long long ro = sm.rowoff[*rho];
+    *lw = rs.score[ro * Ksel + ((en >> 8) & 63u)] * kLog2e;
+    const uint16_t* qr = rs.Q + ro * D + 8 * g;
 #pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds)
-    q[ds] = *reinterpret_cast<const uint4*>(sm.qs + rho * Cfg<D>::QP + 32 * ds + 8 * g);
+    for (int ds = 0; ds < D / 32; ++ds) q[ds] = *reinterpret_cast<const uint4*>(qr + 32 * ds);
+  } else {
+    const uint32_t en = sm.ent[ec];
+    *rho = (int)(en & 0xFFFFu);
+    *slow = (en & kEntrySlow) != 0u;
+    *lw = sm.lw[ec];
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+      q[ds] = *reinterpret_cast<const uint4*>(sm.qs + *rho * Cfg<D>::QP + 32 * ds + 8 * g);
+  }
+  *lm = sm.lamx[*rho];
 }
 
 // All tiles of one selected chunk (fragments in f) for the rows that picked it,
 // one 16-row tile per step; the next step's entry, query fragments and row
 // normaliser are read from LDS while the current step runs.
 template <int D>
-__device__ __forceinline__ void run_chunk(const Frag<D>& f, const Smem& sm, int c, float scale2) {
+__device__ __forceinline__ void run_chunk(const Frag<D>& f, const Smem& sm, const RowSrc& rs,
+                                          int Ksel, int c, float scale2) {
   const int col = threadIdx.x & 15;
   const int e0 = sm.off[c], n = sm.cnt[c];
   const int nstep = (n + 15) / 16;
-  bool v;
-  uint32_t en;
+  bool v, slow;
+  int rho;
   float lw, lm;
   uint4 q[D / 32];
-  read_entry<D>(sm, e0, n, col, &v, &en, &lw, &lm, q);
+  read_entry<D>(sm, rs, Ksel, e0, n, col, &v, &rho, &slow, &lw, &lm, q);
   for (int st = 0; st < nstep; ++st) {
-    bool vn;
-    uint32_t enn;
+    bool vn, slown;
+    int rhon;
     float lwn, lmn;
     uint4 qn[D / 32];
-    read_entry<D>(sm, e0, n, 16 * (st + 1) + col, &vn, &enn, &lwn, &lmn, qn);
+    read_entry<D>(sm, rs, Ksel, e0, n, 16 * (st + 1) + col, &vn, &rhon, &slown, &lwn, &lmn, qn);
     floatx4 o[D / 16];
     float z;
-    tile_sel<D>(f, q, scale2, (en & kEntrySlow) == 0u, o, &z);
-    if (v) accumulate_tile<D>(sm, o, z, en, lw, lm);
-    v = vn, en = enn, lw = lwn, lm = lmn;
+    tile_sel<D>(f, q, scale2, !slow, o, &z);
+    if (v) accumulate_tile<D>(sm, o, z, rho, lw, lm);
+    v = vn, rho = rhon, slow = slown, lw = lwn, lm = lmn;
 #pragma unroll
     for (int ds = 0; ds < D / 32; ++ds) q[ds] = qn[ds];
   }
@@ -630,6 +679,8 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
   auto row_of = [&](int rho) -> long long {
     return ((long long)b * dm.Tq + qi0 + rho / G) * dm.H + (long long)g * G + rho % G;
   };
+  const long long row0 = row_of(0);
+  const RowSrc rs{Q + row0 * D, score + row0 * Ksel};
 
   // own-chunk items of this wave
   const int n_own = own_item_count(p0, S, span, G, Rv, loc_first, own_last);
@@ -666,7 +717,8 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
     const int x = t + j * kThreads;
     if (x < nqv) *reinterpret_cast<uint4*>(sm.qs + (x / (D / 8)) * C::QP + (x % (D / 8)) * 8) = v;
   };
-  const uint4 qv0 = ldq(0), qv1 = ldq(1), qv2 = ldq(2), qv3 = ldq(3);
+  uint4 qv0 = make_uint4(0, 0, 0, 0), qv1 = qv0, qv2 = qv0, qv3 = qv0;
+  if constexpr (!C::QG) qv0 = ldq(0), qv1 = ldq(1), qv2 = ldq(2), qv3 = ldq(3);
   const float vpre = t <= own_last ? vmx[t] : 0.f;
 
   for (int c = t; c <= ncr; c += kThreads) sm.cnt[c] = 0;
@@ -674,6 +726,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
   for (int rho = t; rho < Rv; rho += kThreads) {
     sm.nsel[rho] = 0;
     sm.rvm[rho] = 0u;
+    sm.rowoff[rho] = (rho / G) * dm.H + rho % G;
   }
   if (has_item) {
     int m8 = -1;
@@ -682,7 +735,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
     sm.gmx[t] = m8;  // t = it_rho * kgroups + it_kg
   }
   __syncthreads();
-  stq(0, qv0), stq(1, qv1), stq(2, qv2), stq(3, qv3);
+  if constexpr (!C::QG) stq(0, qv0), stq(1, qv1), stq(2, qv2), stq(3, qv3);
   // the entries that count (entry_counts: a candidate above every earlier entry
   // of the row); the others lose their score too, so they leave Lambda alone
   uint32_t okm = 0u;
@@ -726,13 +779,18 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
   {
     // fast path: weight sums below 2^64 and values below 2^50 keep every partial
     // product of the PV step finite; the row's flag travels in its entries
-    const uint32_t slow = has_item && __uint_as_float(sm.rvm[it_rho]) >= 0x1p50f ? kEntrySlow : 0u;
+    const bool slow = has_item && __uint_as_float(sm.rvm[it_rho]) >= 0x1p50f;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if ((okm >> j) & 1u) {
         const int p = atomicAdd(&sm.cur[cs[j]], 1);
-        sm.ent[p] = (uint32_t)it_rho | ((uint32_t)(it_k0 + j) << 16) | slow;
-        sm.lw[p] = ss[j] * kLog2e;
+        if constexpr (C::QG) {
+          sm.ent16[p] = (uint16_t)((uint32_t)it_rho | ((uint32_t)(it_k0 + j) << 8) |
+                                   (slow ? kEntrySlow16 : 0u));
+        } else {
+          sm.ent[p] = (uint32_t)it_rho | ((uint32_t)(it_k0 + j) << 16) | (slow ? kEntrySlow : 0u);
+          sm.lw[p] = ss[j] * kLog2e;
+        }
       }
   }
   if (has_item) {  // partial log-sum-exp of this group of scores (padding holds -inf)
@@ -783,7 +841,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
     *klo = *valid ? (int)max(0LL, l0 - cb) : 0;
     *khi = *valid ? (int)min((long long)S, pos - cb + 1) : 0;
     *lofs = oc - (int)(l0 / S);
-    lds_q<D>(qo, sm.qs, *rho, *valid);
+    lds_q<D>(qo, sm, rs, min(*rho, Rv - 1), *valid);
   };
   if constexpr (SWA) {
     int fc = -1;  // chunk whose fragments f holds
@@ -822,7 +880,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
     const bool valid = rho < o_rb;
     const int nk = valid ? (int)(p0 + rho / G - (long long)o_oc * S) + 1 : 0;
     uint4 qo[D / 32];
-    lds_q<D>(qo, sm.qs, rho, valid);
+    lds_q<D>(qo, sm, rs, min(rho, Rv - 1), valid);
     floatx4 o[D / 16];
     float z, m2;
     tile_core<D>(f, qo, nk, scale2, o, &z, &m2);
@@ -925,7 +983,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
   // its SIMD (more waves per SIMD measured faster than a second fragment set).
   for (int u = w; u < nnz; u += kWaves) {
     load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[u]) * C::CH);
-    run_chunk<D>(f, sm, sm.cur[u], scale2);
+    run_chunk<D>(f, sm, rs, Ksel, sm.cur[u], scale2);
   }
   __syncthreads();
 
@@ -974,7 +1032,8 @@ bool plan(const Dims& dm, Plan* p) {
   if (b > limit) return false;
   // the set-up gives each thread at most one (row, 8 selections) item and four
   // 16-byte pieces of the query rows
-  if (r * ((dm.K + 7) / 8) > Cfg<D>::THREADS || r * (D / 8) > 4 * Cfg<D>::THREADS) return false;
+  if (r * ((dm.K + 7) / 8) > Cfg<D>::THREADS) return false;
+  if (!Cfg<D>::QG && r * (D / 8) > 4 * Cfg<D>::THREADS) return false;
   p->R = r;
   p->Rq = rq;
   p->ncr = ncr;
