@@ -183,11 +183,13 @@ def write_counter_summary(workload, directory):
     lines.append(f"FETCH_SIZE / WRITE_SIZE are scaled to bytes by the calibration copy "
                  f"(fetch x{rec['fetch_scale']:.3f}, write x{rec['write_scale']:.3f}); other "
                  "counters are raw sums over the GPU per dispatch, averaged over dispatches.")
-    lines.append("mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs); "
+    lines.append("GRBM_GUI_ACTIVE is summed over the 8 XCDs: cycles = GRBM_GUI_ACTIVE / 8, and "
+                 "MHz = cycles / us (the clock the kernel ran at); mfma_busy = "
+                 "SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (cycles x 256 CUs x 4 SIMDs); "
                  "l2_hit = TCC_HIT / (TCC_HIT + TCC_MISS); us = dispatch duration in pass 3.")
     lines.append("")
     hdr = (f"{'kernel':44s} {'calls':>5s} {'us':>9s} {'fetch MB':>9s} {'write MB':>9s} "
-           f"{'mfma_busy':>9s} {'MFMA inst':>10s} {'VALU inst':>11s} {'TRANS':>10s} {'l2_hit':>7s} "
+           f"{'MHz':>5s} {'mfma_busy':>9s} {'MFMA inst':>10s} {'VALU inst':>11s} {'TRANS':>10s} {'l2_hit':>7s} "
            f"{'LDS inst':>10s} {'LDS bkcf':>10s} {'vgpr':>5s}")
     lines.append(hdr)
     avg = lambda xs: sum(xs) / len(xs) if xs else float("nan")  # noqa: E731
@@ -198,15 +200,16 @@ def write_counter_summary(workload, directory):
         d = per[name]
         short = (name.replace("void ", "").replace("hils::(anonymous namespace)::", "")
                  .replace("at::native::", "").split("(")[0])
-        g = avg(d.get("GRBM_GUI_ACTIVE", []))
+        g = avg(d.get("GRBM_GUI_ACTIVE", [])) / 8  # one instance per XCD
         busy = avg(d.get("SQ_VALU_MFMA_BUSY_CYCLES", [])) / (g * 256 * 4) if g else float("nan")
+        mhz = g / avg(dur.get(name, [])) if g and dur.get(name) else float("nan")
         hit, miss = avg(d.get("TCC_HIT_sum", [])), avg(d.get("TCC_MISS_sum", []))
         l2 = hit / (hit + miss) if hit + miss else float("nan")
         lines.append(
             f"{short[:44]:44s} {len(dur.get(name, [])):5d} {avg(dur.get(name, [])):9.2f} "
             f"{avg(d.get('FETCH_SIZE', [])) * 1024 * scale['FETCH_SIZE'] / 1e6:9.2f} "
             f"{avg(d.get('WRITE_SIZE', [])) * 1024 * scale['WRITE_SIZE'] / 1e6:9.2f} "
-            f"{busy:9.3f} {avg(d.get('SQ_INSTS_MFMA', [])):10.3g} "
+            f"{mhz:5.0f} {busy:9.3f} {avg(d.get('SQ_INSTS_MFMA', [])):10.3g} "
             f"{avg(d.get('SQ_INSTS_VALU', [])):11.4g} {avg(d.get('SQ_INSTS_VALU_TRANS_F32', [])):10.3g} "
             f"{l2:7.3f} {avg(d.get('SQ_INSTS_LDS', [])):10.3g} "
             f"{avg(d.get('SQ_LDS_BANK_CONFLICT', [])):10.3g} {d['_vgpr'][0]:>5s}")
