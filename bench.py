@@ -184,7 +184,9 @@ def write_counter_summary(workload, directory):
                  f"(fetch x{rec['fetch_scale']:.3f}, write x{rec['write_scale']:.3f}); other "
                  "counters are raw sums over the GPU per dispatch, averaged over dispatches.")
     lines.append("GRBM_GUI_ACTIVE is summed over the 8 XCDs: cycles = GRBM_GUI_ACTIVE / 8, and "
-                 "MHz = cycles / us (the clock the kernel ran at); mfma_busy = "
+                 "MHz = cycles / us (the clock the kernel ran at; for kernels of a few tens of us "
+                 "the count also takes in time around the dispatch, so MHz and mfma_busy are only "
+                 "meaningful for the long ones); mfma_busy = "
                  "SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (cycles x 256 CUs x 4 SIMDs); "
                  "l2_hit = TCC_HIT / (TCC_HIT + TCC_MISS); us = dispatch duration in pass 3.")
     lines.append("")
