@@ -412,6 +412,51 @@ def gpu_train(w, x):
     return f, g
 
 
+def test_full_size_training_backward_one_head():
+    """Every dQ row of one (batch element, head) of the training workload, and dK, dV
+    and dQl of every chunk of its kv head (one query head per kv head), against the
+    oracle. Rows whose near-tie selection differs from the oracle's, and the chunks
+    they touch, are left out (their gradients follow a different, equally valid
+    selection)."""
+    w, x = case("train_345m")
+    G = w.H // w.Hkv
+    assert G == 1
+    b0, h0 = 1, 9
+    say(f"[full backward, one head] b{b0} h{h0}: {w.T} rows, {w.NC} chunks")
+    f, g = gpu_train(w, x)
+    ksum, ent, _ = oracle.summarize(x["K"], x["Ql"], w.S)
+    rows = np.array([(b0 * w.T + i) * w.H + h0 for i in range(w.T)])
+    idx, score, gap = oracle.score_topk(x["Q"], ksum, ent, w.S, w.K, rows=rows)
+    gi = host(f["idx"]).reshape(-1, w.K)
+    oi = idx.reshape(-1, w.K)
+    differ = rows[np.any(gi[rows] != oi[rows], axis=1)]
+    assert np.all(gap.reshape(-1)[differ] < NEAR_TIE)
+    if differ.size:  # a valid top-K within the near-tie band
+        check_band(gi[differ], all_scores(x["Q"], ksum, ent, w.S, differ), w.K)
+    row_mask = np.zeros(w.B * w.T * w.H, np.uint8)
+    row_mask[np.setdiff1d(rows, differ)] = 1
+    kv_mask = np.zeros((w.B, w.NC, w.Hkv), np.uint8)
+    kv_mask[b0, :, h0] = 1
+    for r in differ:
+        for c in set(gi[r].tolist()) | set(oi[r].tolist()):
+            if c >= 0:
+                kv_mask[b0, c, h0] = 0
+    say(f"  rows with differing near-tie selections: {len(differ)}; "
+        f"chunks compared {int(kv_mask.sum())} of {w.NC}")
+    oidx_full = np.full((w.B, w.T, w.H, w.K), -1, np.int32)
+    oidx_full.reshape(-1, w.K)[rows] = oi[rows]
+    og = oracle.backward(x["Q"], x["K"], x["V"], x["Ql"], oidx_full, x["dO"], w.S,
+                         row_mask=row_mask.reshape(w.B, w.T, w.H), kv_mask=kv_mask)
+    dQ, dK, dV, dQl = (host(a) for a in g)
+    rm = row_mask.astype(bool)
+    assert_close(dQ.reshape(-1, w.d)[rm], og[0].reshape(-1, w.d)[rm], TOL_GRAD_BF16, "dQ")
+    cs = np.flatnonzero(kv_mask[b0, :, h0])
+    keys = (cs[:, None] * w.S + np.arange(w.S)[None, :]).reshape(-1)
+    assert_close(dK[b0, keys, h0], og[1][b0, keys, h0], TOL_GRAD_BF16, "dK")
+    assert_close(dV[b0, keys, h0], og[2][b0, keys, h0], TOL_GRAD_BF16, "dV")
+    assert_close(dQl[b0, cs, h0], og[3][b0, cs, h0], TOL_GRAD_BF16, "dQl")
+
+
 @pytest.mark.parametrize("name", list(BWD))
 def test_backward_small(name):
     w = BWD[name]
