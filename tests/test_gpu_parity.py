@@ -240,22 +240,29 @@ def sampled_rows(w, n, seed):
 
 @pytest.mark.parametrize("name,nrows", [("prefill_345m", None), ("prefill_7b_gqa", 1024)])
 def test_full_size_prefill(name, nrows):
-    """The full workload on the GPU; every row compared for the 345M prefill, sampled
-    rows (plus the last row and a chunk-0 row) for the 7B GQA prefill."""
+    """The full workload on the GPU; every row compared for the 345M prefill; for the
+    7B GQA prefill every row of kv head 5 (all 32768 positions of its 4 query heads)
+    and sampled rows of the other heads (plus the last row and a chunk-0 row)."""
     w, x = case(name)
     say(f"[full prefill] {name}: B{w.B} T{w.T} H{w.H}/{w.Hkv} d{w.d} K{w.K}")
     t, f = gpu_forward(w, x)
     ksum, ent, lse = oracle.summarize(x["K"], x["Ql"], w.S)
     assert_close(host(f["ksum"]), ksum, TOL_F32, "ksum")
     assert_close(host(f["ent"]), ent, TOL_F32, "ent")
-    rows = np.arange(w.B * w.T * w.H) if nrows is None else sampled_rows(w, nrows, 7)
+    if nrows is None:
+        rows = np.arange(w.B * w.T * w.H)
+    else:
+        G, g0 = w.H // w.Hkv, 5
+        group = np.array([(b * w.T + i) * w.H + g0 * G + hh for b in range(w.B)
+                          for i in range(w.T) for hh in range(G)])
+        rows = np.unique(np.concatenate([group, sampled_rows(w, nrows, 7)]))
     idx, score, gap = oracle.score_topk(x["Q"], ksum, ent, w.S, w.K, rows=rows)
     O, lo, lt = oracle.attend_fuse(x["Q"], x["K"], x["V"], idx, score, w.S, rows=rows)
     flat = lambda a: a.reshape(-1, *a.shape[3:])  # noqa: E731
     gi, gs = flat(host(f["idx"]))[rows], flat(host(f["score"]))[rows]
     excl, eq = compare_selection(gi, flat(idx)[rows], flat(gap)[rows], w.K,
                                  lambda d: all_scores(x["Q"], ksum, ent, w.S, rows[d]))
-    say(f"  sampled rows {len(rows)}, near-tie excluded {int(excl.sum())}")
+    say(f"  rows compared {len(rows)}, near-tie excluded {int(excl.sum())}")
     m = eq[:, None].repeat(w.K, 1) & (flat(idx)[rows] >= 0)
     assert_close(gs[m], flat(score)[rows][m], TOL_F32, "score")
     assert_close(flat(host(f["O"]))[rows][eq], flat(O)[rows][eq], out_tol(w), "O")
@@ -371,7 +378,7 @@ def test_full_size_group_max_7b_sampled():
     excl, eq = compare_selection(gi, flat(idx)[rows], flat(gap)[rows], w.K,
                                  lambda d: all_scores(x["Q"], ksum, ent, w.S, rows[d],
                                                       group_hkv=w.Hkv))
-    say(f"  sampled rows {len(rows)}, near-tie excluded {int(excl.sum())}")
+    say(f"  rows compared {len(rows)}, near-tie excluded {int(excl.sum())}")
     m = eq[:, None].repeat(w.K, 1) & (flat(idx)[rows] >= 0)
     assert_close(gs[m], flat(score)[rows][m], TOL_F32, "score")
     assert_close(flat(host(f["O"]))[rows][eq], flat(O)[rows][eq], out_tol(w), "O")
