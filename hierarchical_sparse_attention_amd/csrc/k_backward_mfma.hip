@@ -282,6 +282,13 @@ __global__ __launch_bounds__(256) void k_sel_scan(Dims dm, int nblk, int* __rest
   }
 }
 
+// STAGED (when the block's entries fit in LDS beside the bitmap): the records are
+// first placed in LDS in list order (chunk, then rank) as packed (position,
+// slot, chunk) words and then written out in that order, so consecutive threads
+// write consecutive 16-byte records: whole cache lines, where writing each row's
+// records from its own thread scatters 16-byte pieces over a line per chunk. The
+// records and their places are the same either way.
+template <bool STAGED>
 __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32_t* __restrict__ idx,
                                                   const float* __restrict__ score,
                                                   const float* __restrict__ lse_tot,
@@ -292,8 +299,12 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
   const int NC = dm.Tkv / dm.S;
   constexpr int W = kLBlk / 32;
   static_assert(W % 4 == 0, "bitmap rows are read 16 bytes at a time");
+  static_assert(kLBlk <= 512, "positions are packed in 9 bits");
   uint32_t* lb = lfill;                                   // [NC][W] bitmap of the block
   int* lo = reinterpret_cast<int*>(lfill + (size_t)NC * W);  // [NC] entry offsets
+  int* lofl = lo + NC;                                    // STAGED: [NC] block-local offsets
+  uint32_t* stage = reinterpret_cast<uint32_t*>(lofl + NC);  // STAGED: [kLBlk * K] entries
+  __shared__ int wtot[4];
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const long long bh = (long long)b * dm.H + h;
   for (int x = threadIdx.x; x < NC * W; x += blockDim.x) lb[x] = 0u;
@@ -313,12 +324,46 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
     }
   }
   __syncthreads();
+  int total = 0;
+  if constexpr (STAGED) {
+    // block-local entries per chunk (bitmap popcounts), exclusive scan in chunk order
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int seg = (NC + 255) / 256;
+    const int c0 = min(NC, t * seg), c1 = min(NC, c0 + seg);
+    int sum = 0;
+    for (int c = c0; c < c1; ++c) {
+      int cn = 0;
+#pragma unroll
+      for (int ww = 0; ww < W; ++ww) cn += __popc(lb[c * W + ww]);
+      lofl[c] = cn;
+      sum += cn;
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wtot[w] = incl;
+    __syncthreads();
+    int run = incl - sum;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      run += x < w ? wtot[x] : 0;
+      total += wtot[x];
+    }
+    for (int c = c0; c < c1; ++c) {
+      const int v = lofl[c];
+      lofl[c] = run;
+      run += v;
+    }
+    __syncthreads();
+  }
   const long long ebase = bh * (long long)dm.Tq * dm.K;
   for (int ii = threadIdx.x; ii < ni; ii += blockDim.x) {
     const int i = i0 + ii;
     const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
     const int n = min(dm.ncand(dm.q_pos0 + i), NC);
-    const float lt = lse_tot[r], Dr = ws_D[r];
     const int wd = ii / 32;
     int seen = -1;
     for (int k = 0; k < dm.K; ++k) {
@@ -339,9 +384,26 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
 #pragma unroll
       for (int ww = 0; ww < W; ++ww)
         rank += ww < wd ? __popc(wv[ww]) : (ww == wd ? __popc(wv[ww] & ((1u << (ii % 32)) - 1u)) : 0);
-      // one 16-byte record: position, alpha, D, slot
-      srec[ebase + lo[c] + rank] = make_int4(i, __float_as_int(expf(score[r * dm.K + k] - lt)),
-                                            __float_as_int(Dr), k);
+      if constexpr (STAGED) {
+        stage[lofl[c] + rank] = (uint32_t)ii | ((uint32_t)k << 9) | ((uint32_t)c << 15);
+      } else {
+        // one 16-byte record: position, alpha, D, slot
+        srec[ebase + lo[c] + rank] = make_int4(i, __float_as_int(expf(score[r * dm.K + k] -
+                                                                         lse_tot[r])),
+                                               __float_as_int(ws_D[r]), k);
+      }
+    }
+  }
+  if constexpr (STAGED) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < total; e += blockDim.x) {
+      const uint32_t v = stage[e];
+      const int ii = (int)(v & 511u), k = (int)((v >> 9) & 63u), c = (int)(v >> 15);
+      const int i = i0 + ii;
+      const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
+      srec[ebase + lo[c] + (e - lofl[c])] =
+          make_int4(i, __float_as_int(expf(score[r * dm.K + k] - lse_tot[r])),
+                    __float_as_int(ws_D[r]), k);
     }
   }
 }
@@ -820,6 +882,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
 
 struct BPlan {
   int nct, nblk;
+  bool staged;  // the list fill stages the block's records in LDS
   size_t cnt_bytes, ls_bytes, rec_bytes, part_bytes, fill_smem;
 };
 
@@ -835,6 +898,10 @@ bool bwd_plan(const Dims& dm, BPlan* p) {
   p->rec_bytes = rows * dm.K * sizeof(int4);
   p->part_bytes = rows * (dm.K + dm.nlocal_max()) * D * sizeof(uint16_t);
   p->fill_smem = (size_t)p->nct * (kLBlk / 32 + 1) * sizeof(int);
+  const size_t staged = p->fill_smem + (size_t)p->nct * sizeof(int) +
+                        (size_t)kLBlk * dm.K * sizeof(uint32_t);
+  p->staged = staged <= 160 * 1024 && p->nct <= (1 << 17);  // chunk ids packed in 17 bits
+  if (p->staged) p->fill_smem = staged;
   return p->fill_smem <= 160 * 1024;
 }
 
@@ -874,14 +941,20 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
   hipLaunchKernelGGL(k_sel_count, dim3(p.nblk, dm.H, dm.B), dim3(256), (size_t)p.nct * sizeof(int),
                      st, dm, p.nblk, idx, cnt);
   hipLaunchKernelGGL(k_sel_scan, dim3(dm.H, dm.B), dim3(256), 0, st, dm, p.nblk, cnt, lstart, llen);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sel_fill),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.fill_smem);
+  const void* fk = p.staged ? reinterpret_cast<const void*>(k_sel_fill<true>)
+                           : reinterpret_cast<const void*>(k_sel_fill<false>);
+  hipError_t e = hipFuncSetAttribute(fk, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)p.fill_smem);
   if (e != hipSuccess) {
     *err = e;
     return true;
   }
-  hipLaunchKernelGGL(k_sel_fill, dim3(p.nblk, dm.H, dm.B), dim3(256), p.fill_smem, st, dm, p.nblk,
-                     idx, score, lse_tot, ws_D, cnt, srec);
+  if (p.staged)
+    hipLaunchKernelGGL(k_sel_fill<true>, dim3(p.nblk, dm.H, dm.B), dim3(256), p.fill_smem, st, dm,
+                       p.nblk, idx, score, lse_tot, ws_D, cnt, srec);
+  else
+    hipLaunchKernelGGL(k_sel_fill<false>, dim3(p.nblk, dm.H, dm.B), dim3(256), p.fill_smem, st, dm,
+                       p.nblk, idx, score, lse_tot, ws_D, cnt, srec);
   const bool qcal = Qs != nullptr;
   const void* kvk = qcal ? reinterpret_cast<const void*>(k_bwd_kv_mfma<true>)
                          : reinterpret_cast<const void*>(k_bwd_kv_mfma<false>);
