@@ -56,9 +56,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
 __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
-__device__ __forceinline__ floatx4 mfma(uint4 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), b, c, 0, 0, 0);
-}
 __device__ __forceinline__ float xmax_16_32(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
