@@ -48,9 +48,9 @@ COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
 CALL_KERNELS = {
     "attend_fuse": (("k_kv_prep", "k_attend_mfma"),
                     ("k_attend_mfma.hip", "k_attend_fuse.hip", "hils_internal.h")),
-    "decode": (("k_score_split_mfma", "k_topk_merge_rank", "k_decode_partial", "k_decode_combine"),
+    "decode": (("k_score_split_mfma", "k_decode_merge_partial", "k_decode_combine"),
                ("k_score_mfma.hip", "k_score_topk.hip", "k_attend_fuse.hip", "decode_slot.h",
-                "mfma_common.h", "hils_internal.h")),
+                "decode_merge.h", "mfma_common.h", "hils_internal.h")),
     "backward": (("k_bwd_rowd", "k_sel_count", "k_sel_scan", "k_sel_fill", "k_bwd_kv_mfma",
                   "k_dq_reduce"), ("k_backward_mfma.hip", "k_backward.hip", "hils_internal.h")),
 }
@@ -427,8 +427,8 @@ def measure_decode(torch, hsa, stream, td, wd, K_sel, window, Kc, Vc, nsteps, de
                                     for j in range(nb)) for s in range(nsteps)]))
     rec = {"us_per_token": us / nb, "us_per_step": us, "us_per_token_eager": eager / nb,
            "steps": nsteps, "rows_per_step": nb * wd.H, "bytes_per_step": mean_bytes,
-           "roofline": roofline("hils_decode (split scoring, list merge, slot attention, slot "
-                                "fusion: four launches; a k_summarize every 64 positions)",
+           "roofline": roofline("hils_decode (split scoring; list merge and slot attention; slot "
+                                "fusion: three launches; a k_summarize every 64 positions)",
                                 "hbm", mean_bytes, us * 1e-3),
            "K": K_sel}
     if window:

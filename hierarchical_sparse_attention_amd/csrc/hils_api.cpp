@@ -111,9 +111,19 @@ hils_status backward_shape_ok(const hils::Dims& dm) {
 
 hils_status from_hip(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_ERR_HIP; }
 
-// Workspace of hils_decode: the larger of the two calls it is made of (they run
-// one after the other on the stream, so they can share it).
+// A decode step of few rows runs as split scoring, then a slot kernel that
+// merges the split lists itself, then the combine: the lists and the slot
+// partials are live together, lists first. Otherwise the step is the two calls
+// one after the other on the stream, which share the larger of their workspaces.
+int decode_merged_plan(const hils::Dims& dm, int* km) {
+  return hils::attend_is_decode(dm) ? hils::decode_lists_plan(dm, km) : 0;
+}
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 size_t decode_ws(const hils::Dims& dm) {
+  int km = 0;
+  const int ns = decode_merged_plan(dm, &km);
+  if (ns > 0) return align256(hils::decode_lists_ws_bytes(dm, ns)) + hils::attend_ws_bytes(dm);
   const size_t a = hils::score_topk_ws_bytes(dm), b = hils::attend_ws_bytes(dm);
   return a > b ? a : b;
 }
@@ -238,6 +248,18 @@ hils_status hils_decode(const hils_dims* dims, const void* Q, const void* K, con
   const void *Kd = nullptr, *Vd = nullptr;
   if ((st = kv_view(K, &Kd)) != HILS_OK || (st = kv_view(V, &Vd)) != HILS_OK) return st;
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  int km = 0;
+  const int ns = decode_merged_plan(dm, &km);
+  if (ns > 0) {
+    const long long nl = (long long)dm.B * dm.Tq * dm.H * ns * dm.K;
+    float* ws_s = reinterpret_cast<float*>(ws);
+    int* ws_i = reinterpret_cast<int*>(ws_s + nl);
+    void* ws_a = reinterpret_cast<char*>(ws) + align256(hils::decode_lists_ws_bytes(dm, ns));
+    hipError_t e = hils::launch_decode_lists(dm, Q, ksum, ent, ws_s, ws_i, ns, hs);
+    if (e != hipSuccess) return HILS_ERR_HIP;
+    return from_hip(hils::launch_decode_merged(dm, Q, Kd, Vd, ws_s, ws_i, ns, km, idx, score, O,
+                                               lse_own, lse_tot, ws_a, hs));
+  }
   hipError_t err = hils::launch_score_topk(dm, Q, ksum, ent, idx, score, ws, hs);
   if (err != hipSuccess)
     return HILS_ERR_HIP;

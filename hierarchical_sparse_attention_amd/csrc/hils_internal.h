@@ -299,6 +299,7 @@ hipError_t launch_score_mfma_prefill(const Dims& dm, const void* Q, const float*
 constexpr int kSplitMfma = 128;  // candidates per workgroup of the bf16 decode scoring
 constexpr int kRowCand = 8192;   // most candidates the one-workgroup-per-row scoring handles
 // One workgroup per query row (bf16, few rows); returns false when it does not apply.
+bool score_row_mfma_applies(const Dims& dm);
 bool score_row_mfma_try(const Dims& dm, const void* Q, const float* ksum, const float* ent,
                         int32_t* idx, float* score, hipStream_t st, hipError_t* err);
 hipError_t launch_score_mfma_split(const Dims& dm, const void* Q, const float* ksum,
@@ -306,6 +307,14 @@ hipError_t launch_score_mfma_split(const Dims& dm, const void* Q, const float* k
                                    hipStream_t st);
 hipError_t launch_score_topk(const Dims& dm, const void* Q, const float* ksum, const float* ent,
                              int32_t* idx, float* score, void* ws, hipStream_t st);
+// Decode step with the list merge inside the slot kernel: the number of
+// candidate splits (and in *km the list capacity, 16, 32 or 64) when the step
+// scores by candidate splits and the rank merge holds every list entry, else 0.
+int decode_lists_plan(const Dims& dm, int* km);
+size_t decode_lists_ws_bytes(const Dims& dm, int nsplit);
+// Split scoring only: each split's local top list (score, chunk) into ws_s / ws_i.
+hipError_t launch_decode_lists(const Dims& dm, const void* Q, const float* ksum, const float* ent,
+                               float* ws_s, int* ws_i, int nsplit, hipStream_t st);
 
 size_t attend_ws_bytes(const Dims& dm);
 size_t attend_mfma_ws_bytes(const Dims& dm);
@@ -315,6 +324,16 @@ bool attend_mfma_try(const Dims& dm, const void* Q, const void* K, const void* V
 hipError_t launch_attend_fuse(const Dims& dm, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* score, void* O, float* lse_own,
                               float* lse_tot, void* ws, hipStream_t st);
+// Whether the attention of these rows runs as decode slots (few query rows).
+bool attend_is_decode(const Dims& dm);
+// Rest of the decode step after launch_decode_lists: per (slot, row) the merge
+// of the row's lists and the slot's attention, then the fixed-order combine.
+// Writes idx and score (as hils_score_topk would) and O / lse_own / lse_tot;
+// ws holds attend_ws_bytes(dm) and must not overlap the lists.
+hipError_t launch_decode_merged(const Dims& dm, const void* Q, const void* K, const void* V,
+                                const float* ws_s, const int* ws_i, int nsplit, int km,
+                                int32_t* idx, float* score, void* O, float* lse_own,
+                                float* lse_tot, void* ws, hipStream_t st);
 
 size_t backward_ws_bytes(const Dims& dm);
 size_t backward_mfma_ws_bytes(const Dims& dm);

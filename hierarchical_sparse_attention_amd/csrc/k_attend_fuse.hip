@@ -12,6 +12,9 @@
 // Rows kernel: one wavefront per (b, i, h). Lane j owns key j for the logits;
 // lane e owns output features e (and e+64) for the value sum, with the weights
 // broadcast lane-to-lane by v_readlane.
+#include <algorithm>
+
+#include "decode_merge.h"
 #include "decode_slot.h"
 #include "hils_internal.h"
 
@@ -239,6 +242,81 @@ __global__ __launch_bounds__(64) void k_decode_partial(Dims dm, const void* __re
   }
 }
 
+// Slot kernel of a decode step that merges the split lists itself: grid
+// (K + NL, rows), one workgroup of nsplit * KM threads (rounded up to whole
+// wavefronts) per (slot, row). A selected slot's workgroup ranks the union of
+// the row's lists (every workgroup of the row finds the same K entries), takes
+// the entry at its place in chunk order, writes it to idx / score and attends
+// to that chunk with its first wavefront, as k_decode_partial does; local slots
+// skip the merge. Same outputs as the merge kernel followed by k_decode_partial.
+template <bool BF16, int D, int KM, int NL>
+__global__ __launch_bounds__(1024) void k_decode_merge_partial(
+    Dims dm, const void* __restrict__ Q, const void* __restrict__ K, const void* __restrict__ V,
+    const float* __restrict__ ws_s, const int* __restrict__ ws_i, int nsplit,
+    int32_t* __restrict__ idx, float* __restrict__ score, float* __restrict__ part_o,
+    float* __restrict__ part_l) {
+  __shared__ dec::MergeSmem<KM> sm;
+  __shared__ __align__(16) uint16_t qh[D];
+  __shared__ __align__(16) float qf[D];
+  __shared__ int sel_c;
+  const int slot = blockIdx.x, t = threadIdx.x, lane = t & (kWave - 1);
+  const long long r = blockIdx.y;
+  const int h = (int)(r % dm.H), i = (int)((r / dm.H) % dm.Tq);
+  const int b = (int)(r / ((long long)dm.H * dm.Tq));
+  const int g = h / dm.G;
+  const long long pos = dm.q_pos0 + i;
+  const int ncand = dm.ncand(pos);
+  const long long po = r * (dm.K + dm.nlocal_max()) + slot;
+  const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
+  const long long kv_stride = (long long)dm.Hkv * D;
+  for (int e = t; e < D; e += blockDim.x) {  // read before any barrier below
+    if (BF16) qh[e] = reinterpret_cast<const uint16_t*>(Q)[r * D + e];
+    else qf[e] = reinterpret_cast<const float*>(Q)[r * D + e];
+  }
+  long long key0 = 0;
+  int nk = 0;
+  bool have = true;
+  if (slot < dm.K) {  // uniform over the workgroup
+    const int cnt = dec::merge_rank<KM, NL>(dm, r, ncand, ws_s, ws_i, nsplit, kSplitMfma, sm);
+    const long long o = r * dm.K;
+    if (t < cnt && dec::merge_place<KM>(sm, t, cnt) == slot) {
+      const int c = dec::merge_chunk(sm.sel[t]);
+      sel_c = c;
+      idx[o + slot] = c;
+      score[o + slot] = dec::merge_score(sm.sel[t]);
+    }
+    if (slot >= cnt && t == 0) {
+      idx[o + slot] = -1;
+      score[o + slot] = -INFINITY;
+    }
+    __syncthreads();
+    // a merged list is ascending with distinct candidate ids: every entry counts
+    have = slot < cnt;
+    key0 = have ? (long long)sel_c * dm.S : 0;
+    nk = kChunk;
+  } else {  // local chunk l0 / S + slot - K, keys from max(l0, its start) to min(pos, its end)
+    __syncthreads();
+    const long long l0 = dm.lstart(pos), cc = l0 / kChunk + (slot - dm.K);
+    have = cc <= pos / kChunk;
+    key0 = cc * dm.S > l0 ? cc * dm.S : l0;
+    nk = (int)(min(pos, cc * dm.S + dm.S - 1) - key0) + 1;
+  }
+  if (t >= kWave) return;
+  if (!have) {
+    if (lane == 0) part_l[po] = -INFINITY;
+    return;
+  }
+  if (BF16) {
+    SlotRegs<D> rg;
+    slot_load<D>(rg, reinterpret_cast<const uint16_t*>(K), reinterpret_cast<const uint16_t*>(V),
+                 kv_base, kv_stride, key0, nk);
+    slot_compute<D>(rg, dm, qh, nk, part_o + po * D, part_l + po);
+  } else {
+    decode_slot_f32<D>(dm, qf, reinterpret_cast<const float*>(K), reinterpret_cast<const float*>(V),
+                       kv_base, key0, nk, part_o + po * D, part_l + po);
+  }
+}
+
 // Combine kernel: one wavefront per row applies the inter-chunk softmax to the
 // slots in a fixed order (selected slots by their chunk score, local slots by
 // their exact log-mass). Lane k holds slots k and 64 + k.
@@ -337,6 +415,50 @@ hipError_t launch_decode(const Dims& dm, const void* Q, const void* K, const voi
   return hipGetLastError();
 }
 
+template <bool BF16, int D, int KM, int NL>
+hipError_t launch_decode_merged_t(const Dims& dm, const void* Q, const void* K, const void* V,
+                                  const float* ws_s, const int* ws_i, int nsplit, int32_t* idx,
+                                  float* score, void* O, float* lse_own, float* lse_tot, void* ws,
+                                  hipStream_t st) {
+  const long long rows = (long long)dm.B * dm.Tq * dm.H;
+  const size_t n = (size_t)rows * (dm.K + dm.nlocal_max());
+  float* part_o = reinterpret_cast<float*>(ws);
+  float* part_l = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                           ((n * D * sizeof(float) + 255) & ~(size_t)255));
+  const int nt = std::max(kWave, (nsplit * KM + kWave - 1) / kWave * kWave);
+  hipLaunchKernelGGL((k_decode_merge_partial<BF16, D, KM, NL>), dim3(dm.K + dm.nlocal_max(), rows),
+                     dim3(nt), 0, st, dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, part_o,
+                     part_l);
+  hipLaunchKernelGGL((k_decode_combine<BF16, D>), dim3(rows), dim3(64), 0, st, dm, score, part_o,
+                     part_l, O, lse_own, lse_tot);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t launch_decode_merged_d(const Dims& dm, const void* Q, const void* K, const void* V,
+                                  const float* ws_s, const int* ws_i, int nsplit, int km,
+                                  int32_t* idx, float* score, void* O, float* lse_own,
+                                  float* lse_tot, void* ws, hipStream_t st) {
+  const bool nl16 = nsplit <= 16;  // km = 64 holds at most 16 lists
+  if (km == 16 && nl16)
+    return launch_decode_merged_t<BF16, D, 16, 16>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                                   lse_own, lse_tot, ws, st);
+  if (km == 16 && nsplit <= 24)
+    return launch_decode_merged_t<BF16, D, 16, 24>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                                   lse_own, lse_tot, ws, st);
+  if (km == 16)
+    return launch_decode_merged_t<BF16, D, 16, 32>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                                   lse_own, lse_tot, ws, st);
+  if (km == 32 && nl16)
+    return launch_decode_merged_t<BF16, D, 32, 16>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                                   lse_own, lse_tot, ws, st);
+  if (km == 32)
+    return launch_decode_merged_t<BF16, D, 32, 32>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                                   lse_own, lse_tot, ws, st);
+  return launch_decode_merged_t<BF16, D, 64, 16>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                                 lse_own, lse_tot, ws, st);
+}
+
 template <bool BF16, int D>
 hipError_t launch_t(const Dims& dm, const void* Q, const void* K, const void* V,
                     const int32_t* idx, const float* score, void* O, float* lse_own,
@@ -349,6 +471,25 @@ hipError_t launch_t(const Dims& dm, const void* Q, const void* K, const void* V,
 }
 
 }  // namespace
+
+bool attend_is_decode(const Dims& dm) { return use_decode(dm); }
+
+hipError_t launch_decode_merged(const Dims& dm, const void* Q, const void* K, const void* V,
+                                const float* ws_s, const int* ws_i, int nsplit, int km,
+                                int32_t* idx, float* score, void* O, float* lse_own,
+                                float* lse_tot, void* ws, hipStream_t st) {
+  if (km != 16 && km != 32 && km != 64) return hipErrorInvalidValue;
+  if (nsplit < 1 || nsplit > 32 || nsplit * km > 1024) return hipErrorInvalidValue;
+  if (dm.bf16)
+    return dm.d == 64 ? launch_decode_merged_d<true, 64>(dm, Q, K, V, ws_s, ws_i, nsplit, km, idx,
+                                                         score, O, lse_own, lse_tot, ws, st)
+                      : launch_decode_merged_d<true, 128>(dm, Q, K, V, ws_s, ws_i, nsplit, km,
+                                                          idx, score, O, lse_own, lse_tot, ws, st);
+  return dm.d == 64 ? launch_decode_merged_d<false, 64>(dm, Q, K, V, ws_s, ws_i, nsplit, km, idx,
+                                                        score, O, lse_own, lse_tot, ws, st)
+                    : launch_decode_merged_d<false, 128>(dm, Q, K, V, ws_s, ws_i, nsplit, km, idx,
+                                                         score, O, lse_own, lse_tot, ws, st);
+}
 
 size_t attend_ws_bytes(const Dims& dm) {
   return use_decode(dm) ? decode_ws_bytes(dm) : attend_mfma_ws_bytes(dm);

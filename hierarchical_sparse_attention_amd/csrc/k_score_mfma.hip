@@ -459,6 +459,7 @@ __global__ __launch_bounds__(256) void k_score_split_mfma(Dims dm, const uint16_
                                                           int* __restrict__ ws_i, int nsplit) {
   static_assert(kSplitM == 128, "four wavefronts of 32 candidates");
   __shared__ __align__(16) float ss[kSplitM];
+  __shared__ int part[kSplitM];
   const int split = blockIdx.x, r = blockIdx.y;
   const int i = (r / dm.H) % dm.Tq;
   const int n = dm.ncand(dm.q_pos0 + i);
@@ -468,8 +469,8 @@ __global__ __launch_bounds__(256) void k_score_split_mfma(Dims dm, const uint16_
   // local rank: invalid candidates hold -inf and sort after every valid one
   // (a valid candidate's rank counts only valid candidates before it)
   const long long o = ((long long)r * nsplit + split) * dm.K;
-  mf::split_local_topk<kSplitM>(ss, max(0, min(kSplitM, n - cbase)), cbase, dm.K, ws_s + o,
-                                ws_i + o);
+  mf::split_local_topk_halves<kSplitM>(ss, part, max(0, min(kSplitM, n - cbase)), cbase, dm.K,
+                                      ws_s + o, ws_i + o);
 }
 
 // Decode scoring, one workgroup (16 wavefronts) per query row when the row has
@@ -690,13 +691,18 @@ hipError_t launch_score_mfma_split(const Dims& dm, const void* Q, const float* k
   return hipGetLastError();
 }
 
-bool score_row_mfma_try(const Dims& dm, const void* Q, const float* ksum, const float* ent,
-                        int32_t* idx, float* score, hipStream_t st, hipError_t* err) {
+bool score_row_mfma_applies(const Dims& dm) {
   // worth it only with enough rows to spread over the chip: a single row's
   // summaries read by one compute unit are latency-bound
   const long long rows = (long long)dm.B * dm.Tq * dm.H;
   const long long ncand = dm.Tq > 0 ? dm.ncand(dm.q_pos0 + dm.Tq - 1) : 0;
-  if (!dm.bf16 || ncand > kRowCand || ncand < 1 || rows < 256 || rows > 65535) return false;
+  return dm.bf16 && ncand <= kRowCand && ncand >= 1 && rows >= 256 && rows <= 65535;
+}
+
+bool score_row_mfma_try(const Dims& dm, const void* Q, const float* ksum, const float* ent,
+                        int32_t* idx, float* score, hipStream_t st, hipError_t* err) {
+  if (!score_row_mfma_applies(dm)) return false;
+  const long long rows = (long long)dm.B * dm.Tq * dm.H;
   if (dm.d == 64)
     hipLaunchKernelGGL((k_score_row_mfma<64>), dim3(rows), dim3(kRowWaves * 64), 0, st, dm,
                        reinterpret_cast<const uint16_t*>(Q), ksum, ent, idx, score);

@@ -16,6 +16,7 @@
 #include <cfloat>
 #include <climits>
 
+#include "decode_merge.h"
 #include "hils_internal.h"
 
 namespace hils {
@@ -298,69 +299,23 @@ __global__ __launch_bounds__(64) void k_topk_merge_wave(Dims dm, const float* __
 }
 
 // Merge of the per-split top lists by rank, one thread per list entry (at most
-// 32 lists of KM slots, ns * KM <= 1024): an entry's key is its (score, chunk) order as one
-// 64-bit integer (order bits of the score high, the complemented chunk low; 0 for
-// an empty slot), each list sorted descending. An entry's rank in the union is
-// its index in its own list plus, for every other list, the number of keys above
-// it, found by a branch-free binary search; the searches of all lists advance
-// together, so their LDS reads are in flight at once. Keys are unique (chunks
-// are), so the ranks below K are the K best entries, the same set the
-// wavefront merge finds; they are written in chunk order.
-template <int KM>
+// 32 lists of KM slots, ns * KM <= 1024; dec::merge_rank); the K best entries
+// are written in chunk order. The same set as the wavefront merge.
+template <int KM, int NL>
 __global__ __launch_bounds__(1024) void k_topk_merge_rank(Dims dm, const float* __restrict__ ws_s,
                                                           const int* __restrict__ ws_i, int nsplit,
                                                           int32_t* __restrict__ idx,
                                                           float* __restrict__ score) {
-  __shared__ unsigned long long keys[1024];  // [split][KM]
-  __shared__ unsigned long long sel[KM];
-  __shared__ int nval;
+  __shared__ dec::MergeSmem<KM> sm;
   const int r = blockIdx.x, t = threadIdx.x, K = dm.K;
   const int i = (r / dm.H) % dm.Tq;
   const int n = dm.ncand(dm.q_pos0 + i);
-  const int sp = t / KM, j = t % KM;
-  const bool in = sp < nsplit;
-  const int nv = in ? min(K, max(0, min(kSplit, n - sp * kSplit))) : 0;
-  const long long src = ((long long)r * nsplit + (in ? sp : 0)) * K + min(j, K - 1);
-  const float sv = ws_s[src];
-  const int cv = ws_i[src];
-  const unsigned long long key =
-      j < nv ? ((unsigned long long)order_bits(sv) << 32) | (uint32_t)~(uint32_t)cv : 0ull;
-  if (in) keys[t] = key;
-  if (t == 0) {
-    int tot = 0;
-    for (int x = 0; x < nsplit; ++x) tot += min(K, max(0, min(kSplit, n - x * kSplit)));
-    nval = tot;
-  }
-  __syncthreads();
-  if (key != 0ull) {
-    int rank = j;
-    int pos[32];  // per list: keys above `key` found so far (nsplit <= 32)
-#pragma unroll
-    for (int x = 0; x < 32; ++x) pos[x] = 0;
-#pragma unroll
-    for (int step = KM / 2; step > 0; step >>= 1)
-#pragma unroll
-      for (int x = 0; x < 32; ++x) {  // lists past nsplit read the last list (no branch)
-        const unsigned long long a = keys[min(x, nsplit - 1) * KM + pos[x] + step - 1];
-        pos[x] += ((x < nsplit) & (a > key)) ? step : 0;
-      }
-#pragma unroll
-    for (int x = 0; x < 32; ++x) {
-      const unsigned long long a = keys[min(x, nsplit - 1) * KM + pos[x]];
-      rank += ((x < nsplit) & (x != sp)) ? pos[x] + (a > key ? 1 : 0) : 0;
-    }
-    if (rank < K) sel[rank] = key;
-  }
-  __syncthreads();
-  const int cnt = min(K, nval);
+  const int cnt = dec::merge_rank<KM, NL>(dm, r, n, ws_s, ws_i, nsplit, kSplit, sm);
   const long long o = (long long)r * K;
   if (t < cnt) {
-    const unsigned long long k0 = sel[t];
-    const int c = (int)~(uint32_t)k0;
-    int p = 0;
-    for (int k2 = 0; k2 < cnt; ++k2) p += (int)~(uint32_t)sel[k2] < c;
-    idx[o + p] = c;
-    score[o + p] = order_float((uint32_t)(k0 >> 32));
+    const int p = dec::merge_place<KM>(sm, t, cnt);
+    idx[o + p] = dec::merge_chunk(sm.sel[t]);
+    score[o + p] = dec::merge_score(sm.sel[t]);
   } else if (t < K) {
     idx[o + t] = -1;
     score[o + t] = -INFINITY;
@@ -426,15 +381,25 @@ hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const floa
     const int KMr = dm.K <= 16 ? 16 : (dm.K <= 32 ? 32 : 64);
     if (ns <= 32 && ns * KMr <= 1024) {  // one thread per list entry, ranks by binary search
       const int nt = (ns * KMr + 63) / 64 * 64;
-      if (KMr == 16)
-        hipLaunchKernelGGL(k_topk_merge_rank<16>, dim3(rows), dim3(nt), 0, st, dm, ws_s, ws_i, ns,
-                           idx, score);
+      const bool nl16 = ns <= 16;  // KM = 64 holds at most 16 lists
+      if (KMr == 16 && nl16)
+        hipLaunchKernelGGL((k_topk_merge_rank<16, 16>), dim3(rows), dim3(nt), 0, st, dm, ws_s,
+                           ws_i, ns, idx, score);
+      else if (KMr == 16 && ns <= 24)
+        hipLaunchKernelGGL((k_topk_merge_rank<16, 24>), dim3(rows), dim3(nt), 0, st, dm, ws_s,
+                           ws_i, ns, idx, score);
+      else if (KMr == 16)
+        hipLaunchKernelGGL((k_topk_merge_rank<16, 32>), dim3(rows), dim3(nt), 0, st, dm, ws_s,
+                           ws_i, ns, idx, score);
+      else if (KMr == 32 && nl16)
+        hipLaunchKernelGGL((k_topk_merge_rank<32, 16>), dim3(rows), dim3(nt), 0, st, dm, ws_s,
+                           ws_i, ns, idx, score);
       else if (KMr == 32)
-        hipLaunchKernelGGL(k_topk_merge_rank<32>, dim3(rows), dim3(nt), 0, st, dm, ws_s, ws_i, ns,
-                           idx, score);
+        hipLaunchKernelGGL((k_topk_merge_rank<32, 32>), dim3(rows), dim3(nt), 0, st, dm, ws_s,
+                           ws_i, ns, idx, score);
       else
-        hipLaunchKernelGGL(k_topk_merge_rank<64>, dim3(rows), dim3(nt), 0, st, dm, ws_s, ws_i, ns,
-                           idx, score);
+        hipLaunchKernelGGL((k_topk_merge_rank<64, 16>), dim3(rows), dim3(nt), 0, st, dm, ws_s,
+                           ws_i, ns, idx, score);
       return hipGetLastError();
     }
     if (ns <= 64) {  // one wavefront per row, lists in registers
@@ -473,6 +438,36 @@ size_t score_topk_ws_bytes(const Dims& dm) {
   if (!use_split(dm)) return dm.bf16 ? score_mfma_prefill_ws_bytes(dm) : 0;
   const long long rows = (long long)dm.B * dm.Tq * dm.H;
   return (size_t)rows * split_count(dm) * dm.K * (sizeof(float) + sizeof(int));
+}
+
+int decode_lists_plan(const Dims& dm, int* km) {
+  const long long rows = (long long)dm.B * dm.Tq * dm.H;
+  if (rows == 0 || max_candidates(dm) == 0) return 0;
+  if (dm.group_sel && dm.G > 1) return 0;
+  if (!use_split(dm) || score_row_mfma_applies(dm)) return 0;
+  const int ns = split_count(dm);
+  const int KMr = dm.K <= 16 ? 16 : (dm.K <= 32 ? 32 : 64);
+  if (ns > 32 || ns * KMr > 1024) return 0;
+  *km = KMr;
+  return ns;
+}
+
+size_t decode_lists_ws_bytes(const Dims& dm, int nsplit) {
+  const long long rows = (long long)dm.B * dm.Tq * dm.H;
+  return (size_t)rows * nsplit * dm.K * (sizeof(float) + sizeof(int));
+}
+
+hipError_t launch_decode_lists(const Dims& dm, const void* Q, const float* ksum, const float* ent,
+                               float* ws_s, int* ws_i, int nsplit, hipStream_t st) {
+  if (dm.bf16) return launch_score_mfma_split(dm, Q, ksum, ent, ws_s, ws_i, nsplit, st);
+  const long long rows = (long long)dm.B * dm.Tq * dm.H;
+  if (dm.d == 64)
+    hipLaunchKernelGGL((k_score_split<false, 64>), dim3(nsplit, rows), dim3(kSplit), 0, st, dm,
+                       Q, ksum, ent, ws_s, ws_i, nsplit);
+  else
+    hipLaunchKernelGGL((k_score_split<false, 128>), dim3(nsplit, rows), dim3(kSplit), 0, st, dm,
+                       Q, ksum, ent, ws_s, ws_i, nsplit);
+  return hipGetLastError();
 }
 
 hipError_t launch_score_topk(const Dims& dm, const void* Q, const float* ksum, const float* ent,

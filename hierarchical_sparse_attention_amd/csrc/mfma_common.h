@@ -99,32 +99,39 @@ __device__ __forceinline__ void split_scores(const Dims& dm, const uint16_t* __r
 }
 
 // Local top-K of the nvalid scores in ss (candidate cbase + x in slot x, 16-byte
-// aligned, SPLIT a multiple of 64): thread x < nvalid ranks its candidate among
-// them by (score desc, chunk asc) and, if the rank is below K, writes it to slot
-// `rank` of the list at ws_s / ws_i. Reads of ss must be ordered after its writes.
+// aligned; slots past nvalid hold -inf), two threads per candidate (2 SPLIT
+// threads, every one calls this; reads of ss ordered after its writes): thread t
+// counts the entries of half t / SPLIT of the split that come before candidate
+// t % SPLIT in (score desc, chunk asc) order, the second half's counts pass
+// through part (SPLIT ints of LDS), and a candidate whose rank is below K is
+// written to slot `rank` of the list at ws_s / ws_i.
 template <int SPLIT>
-__device__ __forceinline__ void split_local_topk(const float* ss, int nvalid, int cbase, int K,
-                                                 float* __restrict__ ws_s,
-                                                 int* __restrict__ ws_i) {
-  const int t = threadIdx.x;
-  if (t >= nvalid) return;
-  const float sv = ss[t];
+__device__ __forceinline__ void split_local_topk_halves(const float* ss, int* part, int nvalid,
+                                                        int cbase, int K,
+                                                        float* __restrict__ ws_s,
+                                                        int* __restrict__ ws_i) {
+  const int t = threadIdx.x, x = t % SPLIT, half = t / SPLIT;
+  const float sv = ss[x];
   int rank = 0;
-  const float4* s4 = reinterpret_cast<const float4*>(ss);
-  for (int y0 = 0; y0 < SPLIT / 4; y0 += 16) {  // 16 LDS reads in flight per step
-    float4 v[16];
+  const int y0 = half * (SPLIT / 2);
+  const float4* s4 = reinterpret_cast<const float4*>(ss + y0);
+  float4 v[SPLIT / 8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = s4[y0 + j];
+  for (int j = 0; j < SPLIT / 8; ++j) v[j] = s4[j];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int y = 4 * (y0 + j);
-      rank += topk_before(v[j].x, y, sv, t) + topk_before(v[j].y, y + 1, sv, t) +
-              topk_before(v[j].z, y + 2, sv, t) + topk_before(v[j].w, y + 3, sv, t);
-    }
+  for (int j = 0; j < SPLIT / 8; ++j) {
+    const int y = y0 + 4 * j;
+    rank += topk_before(v[j].x, y, sv, x) + topk_before(v[j].y, y + 1, sv, x) +
+            topk_before(v[j].z, y + 2, sv, x) + topk_before(v[j].w, y + 3, sv, x);
   }
-  if (rank < K) {
-    ws_s[rank] = sv;
-    ws_i[rank] = cbase + t;
+  if (half == 1) part[x] = rank;
+  __syncthreads();
+  if (half == 0 && x < nvalid) {
+    rank += part[x];
+    if (rank < K) {
+      ws_s[rank] = sv;
+      ws_i[rank] = cbase + x;
+    }
   }
 }
 

@@ -1,10 +1,11 @@
 """hils_decode (one decode step in one call) through the C ABI.
 
 Its results are those of hils_score_topk followed by hils_attend_fuse, bit for
-bit (selection, scores, outputs, log-masses). Also checked against the oracle, over many
-steps in a row on one workspace (whose contents do not matter), with
-windows, K = 64, several rows per call, rows with no candidates, d = 128, float32
-(two-call fallback) and a host-resident cache.
+bit (selection, scores, outputs, log-masses), also where its slot kernel merges
+the candidate splits' lists itself (few rows, at most 32 splits). Also checked
+against the oracle, over many steps in a row on one workspace (whose contents do
+not matter), with windows, K = 64, several rows per call, rows with no
+candidates, d = 128, float32 and a host-resident cache.
 """
 import numpy as np
 import pytest

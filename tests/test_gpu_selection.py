@@ -157,10 +157,15 @@ def test_exact_ties_decode(name):
     w, nq = DECODE[name]
     x = tied_inputs(w)
     say(f"[ties decode] {name}: cache {w.T}, {nq} query positions")
-    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "Ql")}
+    t = {k: dev(x[k], w.dtype) for k in ("Q", "K", "V", "Ql")}
     ksum, ent, _ = hsa.summarize(t["K"], t["Ql"], w.S)
-    idx, _ = hsa.score_topk(t["Q"], ksum, ent, w.K, w.S, q_pos0=w.q_pos0, Tkv=w.T, Hkv=w.Hkv)
+    idx, sc = hsa.score_topk(t["Q"], ksum, ent, w.K, w.S, q_pos0=w.q_pos0, Tkv=w.T, Hkv=w.Hkv)
+    # hils_decode (with fewer than 256 rows its slot kernel merges the split lists
+    # itself) selects the same chunks
+    ws = hsa.decode_workspace(t["Q"], t["K"], ksum, w.K, w.S, w.q_pos0, w.T)
+    got = hsa.decode(t["Q"], t["K"], t["V"], ksum, ent, w.K, w.S, q_pos0=w.q_pos0, Tkv=w.T, ws=ws)
     torch.cuda.synchronize()
+    assert torch.equal(got[0], idx) and torch.equal(got[1], sc)
     oks, oent, _ = oracle.summarize(x["K"], x["Ql"], w.S)
     n_clean, n_tie = check_ties(host(idx), x["Q"], oks, oent, w.S, w.K, q_pos0=w.q_pos0)
     say(f"  clean rows {n_clean}, ties at the K-th place {n_tie}")
