@@ -116,7 +116,13 @@ hils_status from_hip(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_ERR
 // partials are live together, lists first. Otherwise the step is the two calls
 // one after the other on the stream, which share the larger of their workspaces.
 int decode_merged_plan(const hils::Dims& dm, int* km) {
-  return hils::attend_is_decode(dm) ? hils::decode_lists_plan(dm, km) : 0;
+  if (!hils::attend_is_decode(dm)) return 0;
+  // every slot's workgroup repeats its row's merge: worth it while the slots
+  // fill the chip about once (a K = 16 step of 16 heads: 272 workgroups); with
+  // more slots the separate merge launch costs less than the repeated merges
+  const long long slots = (long long)dm.B * dm.Tq * dm.H * (dm.K + dm.nlocal_max());
+  if (slots > 384) return 0;
+  return hils::decode_lists_plan(dm, km);
 }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

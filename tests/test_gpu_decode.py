@@ -42,6 +42,9 @@ CASES = {
     "bf16_k64_window2048": (synth.small("dec_k64", B=1, T=12288, H=2, Hkv=1, d=64, K=64,
                                         dtype="bf16"), 2048, 2),
     "f32_d64": (synth.small("dec_f32", B=1, T=4096, H=2, Hkv=1, d=64, K=8, dtype="f32"), 0, 1),
+    # 8 candidate splits of 64-entry lists merged inside the slot kernel
+    "bf16_k64_splits8": (synth.small("dec_k64s", B=1, T=65536, H=2, Hkv=1, d=64, K=64,
+                                     dtype="bf16"), 0, 1),
 }
 
 
