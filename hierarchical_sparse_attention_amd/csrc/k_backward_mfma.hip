@@ -35,6 +35,8 @@
 // from Qs: dk'_c sums ds^ Qs instead of ds^ q, the partial slots leave out
 // ds^ k', and k_dq_reduce forms dQs = scale sum_c ds^_c k'_c from the ds^
 // values the key side wrote per (row, slot).
+#include <type_traits>
+
 #include "hils_internal.h"
 
 namespace hils {
@@ -550,6 +552,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     for (int fb = 0; fb < 4; ++fb) dka[kb][fb] = dva[kb][fb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   long long row_base = 0;  // row index of position 0 of the current head
+  const long long discard_row = (long long)dm.B * dm.Tq * dm.H * (dm.K + dm.nlocal_max());
   auto load_tile = [&](int e0, int nr, bool own_rows) {
     KTile T;
 #pragma unroll
@@ -576,7 +579,10 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
   };
 
   // one 32-row tile; rows beyond nr get zero weights (their Q / dO are a valid row's)
-  auto compute_tile = [&](const KTile& T, bool own_rows, floatx4 (&dkq)[4], float& dbp) {
+  // own_rows is a compile-time constant (std::true_type / std::false_type), so
+  // that the selecting rows' tiles, nearly all of them, are one branch-free body
+  auto compute_tile = [&](const KTile& T, auto own_c, floatx4 (&dkq)[4], float& dbp) {
+    constexpr bool own_rows = decltype(own_c)::value;
     // the tile's rows to LDS (the scoring query's only for dk'), then the B
     // operands Q / dO of rows 16 hf + c, features 32 ds + 8g .. back from there
 #pragma unroll
@@ -608,7 +614,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
       }
       floatx4 a[4], d[4];
       float dsh = 0.f;
-      if (own_rows) {
+      if constexpr (own_rows) {
         // w_j = exp(s_j - Lambda) over the row's local keys lstart .. position
         const float lam2 = T.dvr[hf] * kLog2e, Dr = T.aux[hf];
         const int klo = (int)dm.lstart(max(T.rpos[hf], 0));
@@ -668,8 +674,12 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
       // selecting row), to the row's partial slot (lane: features 16 db + 4 gl + r)
       const uint4 pf[2] = {make_uint4(dpk[0].x, dpk[0].y, dpk[1].x, dpk[1].y),
                            make_uint4(dpk[2].x, dpk[2].y, dpk[3].x, dpk[3].y)};
-      const long long prow = (row_base + (long long)max(T.rpos[hf], 0) * dm.H) *
-                                 (dm.K + dm.nlocal_max()) + max(T.slot[hf], 0);
+      // a padding row (rpos < 0) stores to the discard row past the partials, so
+      // the stores need no branch
+      const long long prow =
+          T.rpos[hf] >= 0
+              ? (row_base + (long long)T.rpos[hf] * dm.H) * (dm.K + dm.nlocal_max()) + T.slot[hf]
+              : discard_row;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         floatx4 dq = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -684,8 +694,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
           dq[2] = fmaf(dsh, kb4.z, dq[2]);
           dq[3] = fmaf(dsh, kb4.w, dq[3]);
         }
-        if (T.rpos[hf] >= 0)
-          *reinterpret_cast<uint2*>(part + prow * D + 16 * db + 4 * gl) = pack4_bf16(dq);
+        *reinterpret_cast<uint2*>(part + prow * D + 16 * db + 4 * gl) = pack4_bf16(dq);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -770,7 +779,8 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
           const bool more = e1 < n;
           const int ep = more ? e1 : e0;
           const KTile nxt = load_tile(ep, min(kTileRows, n - ep), ep < base);
-          compute_tile(cur, e0 < base, dkq, dbp);
+          if (e0 < base) compute_tile(cur, std::true_type{}, dkq, dbp);
+          else compute_tile(cur, std::false_type{}, dkq, dbp);
           if (!more) break;
           cur = nxt;
           e0 = e1;
@@ -893,7 +903,8 @@ bool bwd_plan(const Dims& dm, BPlan* p) {
   p->cnt_bytes = (size_t)dm.B * dm.H * p->nct * p->nblk * sizeof(int);
   p->ls_bytes = (size_t)dm.B * dm.H * p->nct * sizeof(int);
   p->rec_bytes = rows * dm.K * sizeof(int4);
-  p->part_bytes = rows * (dm.K + dm.nlocal_max()) * D * sizeof(uint16_t);
+  // the dQ partials, then one discard row that padding rows store to
+  p->part_bytes = (rows * (dm.K + dm.nlocal_max()) + 1) * D * sizeof(uint16_t);
   p->fill_smem = (size_t)p->nct * (kLBlk / 32 + 1) * sizeof(int);
   const size_t staged = p->fill_smem + (size_t)p->nct * sizeof(int) +
                         (size_t)kLBlk * dm.K * sizeof(uint32_t);

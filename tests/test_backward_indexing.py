@@ -7,8 +7,9 @@ on the host for the training workload (B=2, T=16384, H=16, K=16) and the main
 setting (K=32, a 512-key window), with selections made by the selection rule and
 with lists holding entries that do not count, and assert that every record slot
 is written exactly once, every list entry a tile (or its prefetch) reads lies
-inside the entries written for the current segment, and every position and
-partial slot is in range. The constants below mirror the kernel's.
+inside the entries written for the current segment, every position and partial
+slot is in range, and every dQ partial store lands on a (position, slot) of the
+partials or, for a padding row, on the one discard row past them. The constants below mirror the kernel's.
 """
 import numpy as np
 import pytest
@@ -134,6 +135,17 @@ def emulate_head(idx, n, T, K, W, NC):
                         reads += [ep + np.minimum(16 * hf + (lanes & 15), nr - 1) for hf in range(2)]
                         for rd in reads:
                             assert rd.min() >= 0 and rd.max() < nn
+                    # the tile's dQ partial stores: a row that counts writes its
+                    # (position, slot), a padding row the discard row past them
+                    nr = min(TILE, nn - e0)
+                    for hf in range(2):
+                        lr = 16 * hf + (np.arange(64) & 15)
+                        e = e0 + np.minimum(lr, nr - 1)
+                        slot = seg_slot[e]
+                        rpos = np.where((lr < nr) & (slot >= 0), seg_pos[e], -1)
+                        dst = np.where(rpos >= 0, rpos * (K + NL) + slot, T * (K + NL))
+                        assert dst.min() >= 0 and dst.max() <= T * (K + NL)
+                        assert np.all((rpos < 0) | (slot < K + NL))
                     e0 = e1
             if s0 + kseg >= LN:
                 break
