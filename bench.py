@@ -367,11 +367,14 @@ def measure_prefill(torch, ev_ms, w, f, calls, reps, workload, window=0):
     return rec
 
 
-def measure_decode(torch, hsa, stream, td, wd, K_sel, window, Kc, Vc, nsteps, dev, nb=1):
+def measure_decode(torch, hsa, stream, td, wd, K_sel, window, Kc, Vc, nsteps, dev, nb=1,
+                   traffic=None):
     """(record, idx of every step) for a sequence of decode steps: step s queries the
     nb positions p0 + nb s .. over a cache that ends with them; a chunk's summary is
     made when it completes. Timed eagerly and as one captured HIP graph. nb > 1
-    stands in for nb sequences decoding together (each row its own position)."""
+    stands in for nb sequences decoding together (each row its own position).
+    traffic: the counter record's HBM bytes per step, for the configuration it
+    was taken on."""
     p0, S = wd.q_pos0, wd.S
     NCd = wd.T // S
     nsteps = nsteps // nb
@@ -429,7 +432,7 @@ def measure_decode(torch, hsa, stream, td, wd, K_sel, window, Kc, Vc, nsteps, de
            "steps": nsteps, "rows_per_step": nb * wd.H, "bytes_per_step": mean_bytes,
            "roofline": roofline("hils_decode (split scoring; list merge and slot attention; slot "
                                 "fusion: three launches; a k_summarize every 64 positions)",
-                                "hbm", mean_bytes, us * 1e-3),
+                                "hbm", mean_bytes, us * 1e-3, traffic),
            "K": K_sel}
     if window:
         rec["local_branch"] = f"sliding window of {window} keys"
@@ -588,7 +591,8 @@ def main():
     xd = synth.make_inputs(wd)
     td = {k: torch.from_numpy(xd[k]).to(dev, torch.bfloat16) for k in ("Q", "K", "V", "Ql")}
     nsteps = min(args.decode_steps, wd.rows_q)
-    rec, didx = measure_decode(torch, hsa, stream, td, wd, wd.K, 0, td["K"], td["V"], nsteps, dev)
+    rec, didx = measure_decode(torch, hsa, stream, td, wd, wd.K, 0, td["K"], td["V"], nsteps, dev,
+                               traffic=call_traffic("decode_128k", "decode"))
     extra["decode_128k"] = rec
     if not args.no_extra_configs:
         rec, _ = measure_decode(torch, hsa, stream, td, wd, 32, 512, td["K"], td["V"], nsteps, dev)
