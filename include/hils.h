@@ -193,13 +193,15 @@ hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K
  * One decode step of the query rows at positions q_pos0 .. q_pos0 + Tq - 1 (note
  * §5.2 chunk scores and top-K; note §5.3 hierarchical softmax; the note's key
  * result 5 times HiLS decode per token): the selection of hils_score_topk and the
- * attention of hils_attend_fuse in one call, with the same results: it enqueues
- * the selection's kernels (for a few rows: candidate splits scored into local
- * top-K lists, then a merge of the lists) and the decode attention's kernels (one
- * wavefront per selected or local chunk of a row, then the fusion of the slots).
- * ws is one workspace of hils_workspace_size(.., HILS_OP_DECODE, ..) bytes for
- * both; its contents do not matter. K and V may be pinned host memory as for
- * hils_attend_fuse; lse_own and lse_tot may be NULL.
+ * attention of hils_attend_fuse in one call, with the same results (bit for
+ * bit, idx and score included). For a few rows it enqueues the candidate splits
+ * scored into local top-K lists, then one workgroup per (selected or local
+ * chunk, row) that merges the row's lists itself and attends to its chunk, then
+ * the fusion of the slots; with many slots the merge runs once per row as its
+ * own kernel before the slots. ws is one workspace of
+ * hils_workspace_size(.., HILS_OP_DECODE, ..) bytes for all of it (it may be
+ * larger than either call's alone); its contents do not matter. K and V may be
+ * pinned host memory as for hils_attend_fuse; lse_own and lse_tot may be NULL.
  */
 hils_status hils_decode(const hils_dims* dims, const void* Q, const void* K, const void* V,
                         const float* ksum, const float* ent, int32_t* idx, float* score, void* O,
