@@ -213,6 +213,15 @@ __global__ __launch_bounds__(256) void k_dq_reduce(Dims dm, long long rows,
 // selecting position within its block by popcounts of a block bitmap.
 constexpr int kLBlk = 512;  // positions per block (16 bitmap words)
 
+// A row's K selection entries into registers (KM >= K slots, all reads issued
+// together; slots past K repeat entry K - 1 and are never used).
+template <int KM>
+__device__ __forceinline__ void load_row_ids(const int32_t* __restrict__ ir, int K, int (&cv)[KM]) {
+#pragma unroll
+  for (int k = 0; k < KM; ++k) cv[k] = ir[min(k, K - 1)];
+}
+
+template <int KM>
 __global__ __launch_bounds__(256) void k_sel_count(Dims dm, int nblk, const int32_t* __restrict__ idx,
                                                    int* __restrict__ cnt) {
   extern __shared__ int lcnt[];  // [NC]
@@ -225,12 +234,13 @@ __global__ __launch_bounds__(256) void k_sel_count(Dims dm, int nblk, const int3
   for (int ii = threadIdx.x; ii < ni; ii += blockDim.x) {
     const int i = i0 + ii;
     const int n = min(dm.ncand(dm.q_pos0 + i), NC);
-    const int32_t* ir = idx + (((long long)b * dm.Tq + i) * dm.H + h) * dm.K;
+    int cv[KM];
+    load_row_ids<KM>(idx + (((long long)b * dm.Tq + i) * dm.H + h) * dm.K, dm.K, cv);
     int seen = -1;
-    for (int k = 0; k < dm.K; ++k) {
-      const int c = ir[k];
-      if (entry_counts(c, n, seen)) atomicAdd(&lcnt[c], 1);
-      seen = max(seen, c);
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (k < dm.K && entry_counts(cv[k], n, seen)) atomicAdd(&lcnt[cv[k]], 1);
+      seen = max(seen, cv[k]);
     }
   }
   __syncthreads();
@@ -283,12 +293,15 @@ __global__ __launch_bounds__(256) void k_sel_scan(Dims dm, int nblk, int* __rest
 
 // STAGED (when the block's entries fit in LDS beside the bitmap): the records are
 // first placed in LDS in list order (chunk, then rank) as packed (position,
-// slot, chunk) words and then written out in that order, so consecutive threads
-// write consecutive 16-byte records: whole cache lines, where writing each row's
-// records from its own thread scatters 16-byte pieces over a line per chunk. The
-// records and their places are the same either way.
-template <bool STAGED>
-__global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32_t* __restrict__ idx,
+// slot, chunk) words with their weights alpha, and the rows' D, and then written
+// out in that order from LDS alone, so consecutive threads write consecutive
+// 16-byte records: whole cache lines, where writing each row's records from its
+// own thread scatters 16-byte pieces over a line per chunk. Each row's entries
+// and scores are read once, all at a time. The records and their places are the
+// same either way.
+constexpr int kFillThreads = 512;  // one row of the block per thread
+template <bool STAGED, int KM>
+__global__ __launch_bounds__(kFillThreads) void k_sel_fill(Dims dm, int nblk, const int32_t* __restrict__ idx,
                                                   const float* __restrict__ score,
                                                   const float* __restrict__ lse_tot,
                                                   const float* __restrict__ ws_D,
@@ -303,7 +316,10 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
   int* lo = reinterpret_cast<int*>(lfill + (size_t)NC * W);  // [NC] entry offsets
   int* lofl = lo + NC;                                    // STAGED: [NC] block-local offsets
   uint32_t* stage = reinterpret_cast<uint32_t*>(lofl + NC);  // STAGED: [kLBlk * K] entries
-  __shared__ int wtot[4];
+  float* salpha = reinterpret_cast<float*>(stage + kLBlk * dm.K);  // STAGED: their alpha
+  float* sdr = salpha + kLBlk * dm.K;                     // STAGED: [kLBlk] each row's D
+  constexpr int kWv = kFillThreads / 64;
+  __shared__ int wtot[kWv];
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const long long bh = (long long)b * dm.H + h;
   for (int x = threadIdx.x; x < NC * W; x += blockDim.x) lb[x] = 0u;
@@ -314,12 +330,14 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
   for (int ii = threadIdx.x; ii < ni; ii += blockDim.x) {
     const int i = i0 + ii;
     const int n = min(dm.ncand(dm.q_pos0 + i), NC);
-    const int32_t* ir = idx + (((long long)b * dm.Tq + i) * dm.H + h) * dm.K;
+    int cv[KM];
+    load_row_ids<KM>(idx + (((long long)b * dm.Tq + i) * dm.H + h) * dm.K, dm.K, cv);
     int seen = -1;
-    for (int k = 0; k < dm.K; ++k) {
-      const int c = ir[k];
-      if (entry_counts(c, n, seen)) atomicOr(&lb[c * W + ii / 32], 1u << (ii % 32));
-      seen = max(seen, c);
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (k < dm.K && entry_counts(cv[k], n, seen))
+        atomicOr(&lb[cv[k] * W + ii / 32], 1u << (ii % 32));
+      seen = max(seen, cv[k]);
     }
   }
   __syncthreads();
@@ -327,7 +345,7 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
   if constexpr (STAGED) {
     // block-local entries per chunk (bitmap popcounts), exclusive scan in chunk order
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int seg = (NC + 255) / 256;
+    const int seg = (NC + kFillThreads - 1) / kFillThreads;
     const int c0 = min(NC, t * seg), c1 = min(NC, c0 + seg);
     int sum = 0;
     for (int c = c0; c < c1; ++c) {
@@ -347,7 +365,7 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
     __syncthreads();
     int run = incl - sum;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < kWv; ++x) {
       run += x < w ? wtot[x] : 0;
       total += wtot[x];
     }
@@ -364,10 +382,19 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
     const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
     const int n = min(dm.ncand(dm.q_pos0 + i), NC);
     const int wd = ii / 32;
+    // the row's entries, scores, Lambda and D, all reads in flight together
+    int cv[KM];
+    float sv[KM];
+    load_row_ids<KM>(idx + r * dm.K, dm.K, cv);
+#pragma unroll
+    for (int k = 0; k < KM; ++k) sv[k] = score[r * dm.K + min(k, dm.K - 1)];
+    const float lt = lse_tot[r], dr = ws_D[r];
+    if constexpr (STAGED) sdr[ii] = dr;
     int seen = -1;
-    for (int k = 0; k < dm.K; ++k) {
-      const int c = idx[r * dm.K + k];
-      const bool ok = entry_counts(c, n, seen);
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      const int c = cv[k];
+      const bool ok = k < dm.K && entry_counts(c, n, seen);
       seen = max(seen, c);
       if (!ok) continue;
       // the chunk's bitmap row in four 16-byte reads (all in flight), then the
@@ -383,13 +410,13 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
 #pragma unroll
       for (int ww = 0; ww < W; ++ww)
         rank += ww < wd ? __popc(wv[ww]) : (ww == wd ? __popc(wv[ww] & ((1u << (ii % 32)) - 1u)) : 0);
+      const float alpha = expf(sv[k] - lt);
       if constexpr (STAGED) {
         stage[lofl[c] + rank] = (uint32_t)ii | ((uint32_t)k << 9) | ((uint32_t)c << 15);
+        salpha[lofl[c] + rank] = alpha;
       } else {
         // one 16-byte record: position, alpha, D, slot
-        srec[ebase + lo[c] + rank] = make_int4(i, __float_as_int(expf(score[r * dm.K + k] -
-                                                                         lse_tot[r])),
-                                               __float_as_int(ws_D[r]), k);
+        srec[ebase + lo[c] + rank] = make_int4(i, __float_as_int(alpha), __float_as_int(dr), k);
       }
     }
   }
@@ -398,11 +425,8 @@ __global__ __launch_bounds__(256) void k_sel_fill(Dims dm, int nblk, const int32
     for (int e = threadIdx.x; e < total; e += blockDim.x) {
       const uint32_t v = stage[e];
       const int ii = (int)(v & 511u), k = (int)((v >> 9) & 63u), c = (int)(v >> 15);
-      const int i = i0 + ii;
-      const long long r = ((long long)b * dm.Tq + i) * dm.H + h;
       srec[ebase + lo[c] + (e - lofl[c])] =
-          make_int4(i, __float_as_int(expf(score[r * dm.K + k] - lse_tot[r])),
-                    __float_as_int(ws_D[r]), k);
+          make_int4(i0 + ii, __float_as_int(salpha[e]), __float_as_int(sdr[ii]), k);
     }
   }
 }
@@ -907,13 +931,36 @@ bool bwd_plan(const Dims& dm, BPlan* p) {
   p->part_bytes = (rows * (dm.K + dm.nlocal_max()) + 1) * D * sizeof(uint16_t);
   p->fill_smem = (size_t)p->nct * (kLBlk / 32 + 1) * sizeof(int);
   const size_t staged = p->fill_smem + (size_t)p->nct * sizeof(int) +
-                        (size_t)kLBlk * dm.K * sizeof(uint32_t);
+                        (size_t)kLBlk * dm.K * (sizeof(uint32_t) + sizeof(float)) +
+                        (size_t)kLBlk * sizeof(float);
   p->staged = staged <= 160 * 1024 && p->nct <= (1 << 17);  // chunk ids packed in 17 bits
   if (p->staged) p->fill_smem = staged;
   return p->fill_smem <= 160 * 1024;
 }
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The three list passes, with KM >= K register slots per row.
+template <int KM>
+hipError_t launch_lists(const Dims& dm, const BPlan& p, const int32_t* idx, const float* score,
+                        const float* lse_tot, const float* ws_D, int* cnt, int* lstart, int* llen,
+                        int4* srec, hipStream_t st) {
+  hipLaunchKernelGGL(k_sel_count<KM>, dim3(p.nblk, dm.H, dm.B), dim3(256),
+                     (size_t)p.nct * sizeof(int), st, dm, p.nblk, idx, cnt);
+  hipLaunchKernelGGL(k_sel_scan, dim3(dm.H, dm.B), dim3(256), 0, st, dm, p.nblk, cnt, lstart, llen);
+  const void* fk = p.staged ? reinterpret_cast<const void*>(k_sel_fill<true, KM>)
+                            : reinterpret_cast<const void*>(k_sel_fill<false, KM>);
+  hipError_t e = hipFuncSetAttribute(fk, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)p.fill_smem);
+  if (e != hipSuccess) return e;
+  if (p.staged)
+    hipLaunchKernelGGL((k_sel_fill<true, KM>), dim3(p.nblk, dm.H, dm.B), dim3(kFillThreads),
+                       p.fill_smem, st, dm, p.nblk, idx, score, lse_tot, ws_D, cnt, srec);
+  else
+    hipLaunchKernelGGL((k_sel_fill<false, KM>), dim3(p.nblk, dm.H, dm.B), dim3(kFillThreads),
+                       p.fill_smem, st, dm, p.nblk, idx, score, lse_tot, ws_D, cnt, srec);
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -946,23 +993,16 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
   const auto* dOh = reinterpret_cast<const uint16_t*>(dO);
   hipLaunchKernelGGL(k_bwd_rowd, dim3(rblocks), dim3(256), 0, st, rows,
                      reinterpret_cast<const uint16_t*>(O), dOh, ws_D);
-  hipLaunchKernelGGL(k_sel_count, dim3(p.nblk, dm.H, dm.B), dim3(256), (size_t)p.nct * sizeof(int),
-                     st, dm, p.nblk, idx, cnt);
-  hipLaunchKernelGGL(k_sel_scan, dim3(dm.H, dm.B), dim3(256), 0, st, dm, p.nblk, cnt, lstart, llen);
-  const void* fk = p.staged ? reinterpret_cast<const void*>(k_sel_fill<true>)
-                           : reinterpret_cast<const void*>(k_sel_fill<false>);
-  hipError_t e = hipFuncSetAttribute(fk, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)p.fill_smem);
+  hipError_t e = dm.K <= 16 ? launch_lists<16>(dm, p, idx, score, lse_tot, ws_D, cnt, lstart,
+                                                llen, srec, st)
+                 : dm.K <= 32 ? launch_lists<32>(dm, p, idx, score, lse_tot, ws_D, cnt, lstart,
+                                                 llen, srec, st)
+                              : launch_lists<64>(dm, p, idx, score, lse_tot, ws_D, cnt, lstart,
+                                                 llen, srec, st);
   if (e != hipSuccess) {
     *err = e;
     return true;
   }
-  if (p.staged)
-    hipLaunchKernelGGL(k_sel_fill<true>, dim3(p.nblk, dm.H, dm.B), dim3(256), p.fill_smem, st, dm,
-                       p.nblk, idx, score, lse_tot, ws_D, cnt, srec);
-  else
-    hipLaunchKernelGGL(k_sel_fill<false>, dim3(p.nblk, dm.H, dm.B), dim3(256), p.fill_smem, st, dm,
-                       p.nblk, idx, score, lse_tot, ws_D, cnt, srec);
   const bool qcal = Qs != nullptr;
   const void* kvk = qcal ? reinterpret_cast<const void*>(k_bwd_kv_mfma<true>)
                          : reinterpret_cast<const void*>(k_bwd_kv_mfma<false>);
