@@ -764,6 +764,8 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     float dbp = 0.f;
     const long long bh = (long long)b * dm.H + h;
     const long long sidx = ((long long)b * dm.NCcap + c) * dm.H + h;
+    // the summary backward's per-(chunk, head) inputs, read while the tiles run
+    const float lp_h = lse_l[sidx], ent_h = ent[sidx];
     const int LN = llen[bh * NC + c];
     const long long lsrc = bh * (long long)dm.Tq * dm.K + lstart[bh * NC + c];
     // local rows: positions key0 .. key0 + span - 1 (span = S, or S + W - 1 with a
@@ -778,21 +780,50 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
       const int base = s0 == 0 ? nown_pad : 0;
       const int ns = min(kSeg, LN - s0);
       const int n = base + ns;
-      if (s0 == 0 && t < D) sm.kbv[t] = ksum[sidx * D + t];
-      for (int e = t; e < base; e += kKThreads) {
-        const long long pos = key0 + min(e, nown - 1);
-        const long long r = row_base + pos * dm.H;
-        sm.rows[e] = (int)pos;
-        sm.aux[e] = ws_D[r];
-        sm.dvl[e] = lse_tot[r];
-        sm.slotv[e] = e < nown ? dm.K + (c - (int)(dm.lstart(pos) / kChunk)) : -1;
+      if (s0 == 0 && t < D) {
+        sm.kbv[t] = ksum[sidx * D + t];
+        sm.qlv[t] = bf(Ql[sidx * D + t]);  // for the summary backward after the tiles
       }
-      for (int e = t; e < ns; e += kKThreads) {
-        const int4 rec = srec[lsrc + s0 + e];
-        sm.rows[base + e] = rec.x;
-        sm.aux[base + e] = __int_as_float(rec.y);
-        sm.dvl[base + e] = __int_as_float(rec.z);
-        sm.slotv[base + e] = rec.w;
+      // the segment's rows into LDS: a round of reads (kSegU per thread for the
+      // local rows, kSegR for the selecting rows' records) is issued before any
+      // of it is stored, so a segment takes one or two memory round trips
+      constexpr int kSegU = 3, kSegR = 8;
+      for (int e0 = t; e0 < base; e0 += kKThreads * kSegU) {
+        int pp[kSegU];
+        float dr[kSegU], lt[kSegU];
+#pragma unroll
+        for (int u = 0; u < kSegU; ++u) {
+          const long long pos = key0 + min(min(e0 + u * kKThreads, base - 1), nown - 1);
+          const long long r = row_base + pos * dm.H;
+          pp[u] = (int)pos;
+          dr[u] = ws_D[r];
+          lt[u] = lse_tot[r];
+        }
+#pragma unroll
+        for (int u = 0; u < kSegU; ++u) {
+          const int e = e0 + u * kKThreads;
+          if (e < base) {
+            sm.rows[e] = pp[u];
+            sm.aux[e] = dr[u];
+            sm.dvl[e] = lt[u];
+            sm.slotv[e] = e < nown ? dm.K + (c - (int)(dm.lstart(pp[u]) / kChunk)) : -1;
+          }
+        }
+      }
+      for (int e0 = t; e0 < ns; e0 += kKThreads * kSegR) {
+        int4 rec[kSegR];
+#pragma unroll
+        for (int u = 0; u < kSegR; ++u) rec[u] = srec[lsrc + s0 + min(e0 + u * kKThreads, ns - 1)];
+#pragma unroll
+        for (int u = 0; u < kSegR; ++u) {
+          const int e = e0 + u * kKThreads;
+          if (e < ns) {
+            sm.rows[base + e] = rec[u].x;
+            sm.aux[base + e] = __int_as_float(rec[u].y);
+            sm.dvl[base + e] = __int_as_float(rec[u].z);
+            sm.slotv[base + e] = rec[u].w;
+          }
+        }
       }
       __syncthreads();
       int e0 = kTileRows * w;
@@ -824,10 +855,8 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     }
     if (lane == 0) sm.dbw[w] = dbp;
     __syncthreads();
-    if (t < D) {  // fixed order over the wavefronts
+    if (t < D)  // fixed order over the wavefronts
       sm.dkb[0][t] = (((sm.dkb[0][t] + sm.dkb[1][t]) + sm.dkb[2][t]) + sm.dkb[3][t]) * dm.scale;
-      sm.qlv[t] = bf(Ql[sidx * D + t]);
-    }
     __syncthreads();
     if (w == 0) {  // lane j: key j of the chunk
       float s1 = 0.f, t1 = 0.f;
@@ -844,7 +873,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
         }
       }
       s1 *= dm.scale;
-      const float Lp = lse_l[sidx], bias = ent[sidx];
+      const float Lp = lp_h, bias = ent_h;
       const float dbv = ((sm.dbw[0] + sm.dbw[1]) + sm.dbw[2]) + sm.dbw[3];
       const float p1 = expf(s1 - Lp);
       sm.sp[lane] = p1;
