@@ -74,6 +74,29 @@ def test_summarize(name):
     assert_close(host(lse), olse, TOL_F32, "lse_l")
 
 
+# groups of 3 and 8 query heads per kv head: the summaries run a round with an
+# idle wavefront (3 heads on 2) and two rounds of 4
+GROUPS = {
+    "bf16_g3": synth.small("sum_g3", B=1, T=640, H=3, Hkv=1, d=64, K=4, dtype="bf16"),
+    "bf16_d128_g8": synth.small("sum_g8", B=2, T=512, H=16, Hkv=2, d=128, K=4, dtype="bf16"),
+    "f32_g3": synth.small("sum_g3f", B=1, T=384, H=6, Hkv=2, d=64, K=4, dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUPS))
+def test_summarize_head_groups(name):
+    w = GROUPS[name]
+    x = synth.make_inputs(w)
+    say(f"[summarize groups] {name}")
+    t = {k: dev(x[k], w.dtype) for k in ("K", "Ql")}
+    ksum, ent, lse = hsa.summarize(t["K"], t["Ql"], w.S)
+    torch.cuda.synchronize()
+    oks, oent, olse = oracle.summarize(x["K"], x["Ql"], w.S)
+    assert_close(host(ksum), oks, TOL_F32, "ksum")
+    assert_close(host(ent), oent, TOL_F32, "ent")
+    assert_close(host(lse), olse, TOL_F32, "lse_l")
+
+
 @pytest.mark.parametrize("name", list(SMALL) + ["tiny_f32"])
 def test_forward_end_to_end(name):
     w, x = case(name)
