@@ -297,11 +297,6 @@ hipError_t launch_score_mfma_prefill(const Dims& dm, const void* Q, const float*
                                      const float* ent, int32_t* idx, float* score, void* ws,
                                      hipStream_t st);
 constexpr int kSplitMfma = 128;  // candidates per workgroup of the bf16 decode scoring
-constexpr int kRowCand = 8192;   // most candidates the one-workgroup-per-row scoring handles
-// One workgroup per query row (bf16, few rows); returns false when it does not apply.
-bool score_row_mfma_applies(const Dims& dm);
-bool score_row_mfma_try(const Dims& dm, const void* Q, const float* ksum, const float* ent,
-                        int32_t* idx, float* score, hipStream_t st, hipError_t* err);
 hipError_t launch_score_mfma_split(const Dims& dm, const void* Q, const float* ksum,
                                    const float* ent, float* ws_s, int* ws_i, int nsplit,
                                    hipStream_t st);

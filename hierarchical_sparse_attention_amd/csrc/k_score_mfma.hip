@@ -19,7 +19,8 @@
 // 16 candidates, a compare against the list's last score marks the few that can
 // enter, and those are inserted with a compare-exchange pass.
 // Decode: candidates of a row are split over workgroups; each writes its local
-// top-K (rank counting) and the merge kernel of the float32 path ranks the union.
+// top-K (rank counting), and the union is ranked by the merge kernel shared with
+// the float32 path or by the decode step's slot kernel itself.
 #include "hils_internal.h"
 #include "mfma_common.h"
 
@@ -473,125 +474,6 @@ __global__ __launch_bounds__(256) void k_score_split_mfma(Dims dm, const uint16_
                                       ws_s + o, ws_i + o);
 }
 
-// Decode scoring, one workgroup (16 wavefronts) per query row when the row has
-// at most kRowCand candidates: the same per-block scoring as the split kernel
-// (so the scores are bit-identical to the prefill ones), all scores kept in
-// LDS, a local top-K per wavefront over a contiguous candidate range, then the
-// union of the 16 local lists ranked. No workspace and no second kernel.
-constexpr int kRowWaves = 16;
-template <int D>
-__global__ __launch_bounds__(kRowWaves * 64) void k_score_row_mfma(
-    Dims dm, const uint16_t* __restrict__ Q, const float* __restrict__ ksum,
-    const float* __restrict__ ent, int32_t* __restrict__ idx, float* __restrict__ score) {
-  __shared__ __align__(16) float ss[kRowCand];
-  __shared__ __align__(16) float fs[kRowWaves * 64];
-  __shared__ __align__(16) int fc[kRowWaves * 64];
-  __shared__ float sel_s[64];
-  __shared__ int sel_c[64];
-  const int r = blockIdx.x, t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6, c = lane & 15, g = lane >> 4;
-  const int h = r % dm.H, i = (r / dm.H) % dm.Tq, b = r / (dm.H * dm.Tq);
-  const int n = dm.ncand(dm.q_pos0 + i);
-  const int K = dm.K;
-  uint4 qa[D / 32];
-#pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds)
-    qa[ds] = c == 0 ? *reinterpret_cast<const uint4*>(Q + (long long)r * D + 32 * ds + 8 * g)
-                    : make_uint4(0, 0, 0, 0);
-  // scores: wavefront w takes 16-candidate blocks w, w + 16, ..., NB at a time
-  constexpr int NB = D == 64 ? 2 : 1;
-  const int nblk = (n + 15) / 16;
-  for (int blk0 = w; blk0 < nblk; blk0 += kRowWaves * NB) {
-    float4 raw[NB][D / 32][2];
-    float ev[NB];
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int chunk = 16 * (blk0 + kRowWaves * q) + c;
-      const bool cv = chunk < n;
-      const float* src = ksum + (((long long)b * dm.NCcap + (cv ? chunk : 0)) * dm.H + h) * D;
-#pragma unroll
-      for (int ds = 0; ds < D / 32; ++ds) {
-        raw[q][ds][0] = *reinterpret_cast<const float4*>(src + 32 * ds + 8 * g);
-        raw[q][ds][1] = *reinterpret_cast<const float4*>(src + 32 * ds + 8 * g + 4);
-      }
-      ev[q] = ent[((long long)b * dm.NCcap + (cv ? chunk : 0)) * dm.H + h];
-    }
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int blk = blk0 + kRowWaves * q;
-      const int chunk = 16 * blk + c;
-      const bool cv = chunk < n;
-      bf16x8 hi[D / 32], lo[D / 32];
-#pragma unroll
-      for (int ds = 0; ds < D / 32; ++ds) {
-        const float4 a = raw[q][ds][0], bb = raw[q][ds][1];
-        float v[8] = {a.x, a.y, a.z, a.w, bb.x, bb.y, bb.z, bb.w};
-        if (!cv) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = 0.f;
-        }
-        split8(v, hi[ds], lo[ds]);
-      }
-      const floatx4 acc = score_block<D>(qa, hi, lo);
-      if (g == 0 && blk < nblk) ss[chunk] = cv ? fmaf(acc[0], dm.scale, ev[q]) : -INFINITY;
-    }
-  }
-  __syncthreads();
-  // local top-K of wavefront w over candidates [lo, hi) (a multiple of 4 wide)
-  const int per = (((n + kRowWaves - 1) / kRowWaves) + 3) & ~3;
-  const int lo = min(n, w * per), hi = min(n, lo + per);
-  for (int x = lo + lane; x < lo + per; x += 64)  // pad the range tail
-    if (x >= hi && x < kRowCand) ss[x] = -INFINITY;
-  __builtin_amdgcn_wave_barrier();
-  const int nloc = hi - lo, kloc = min(K, nloc);
-  for (int x = lo + lane; x < hi; x += 64) {
-    const float sv = ss[x];
-    int rank = 0;
-    const float4* s4 = reinterpret_cast<const float4*>(ss + lo);
-    for (int y4 = 0; y4 < per / 4; ++y4) {
-      const float4 v = s4[y4];
-      const int y = lo + 4 * y4;
-      rank += topk_before(v.x, y, sv, x) + topk_before(v.y, y + 1, sv, x) +
-              topk_before(v.z, y + 2, sv, x) + topk_before(v.w, y + 3, sv, x);
-    }
-    if (rank < K) {
-      fs[w * K + rank] = sv;
-      fc[w * K + rank] = x;
-    }
-  }
-  for (int k = kloc + lane; k < K; k += 64) {
-    fs[w * K + k] = -INFINITY;
-    fc[w * K + k] = 0x7fffffff;
-  }
-  __syncthreads();
-  // union of the local lists (the global top-K is a subset of it)
-  const int E = kRowWaves * K, cnt = min(K, n);
-  if (t < E) {
-    const float sv = fs[t];
-    const int cx = fc[t];
-    int rank = 0;
-    for (int y = 0; y < E; ++y) rank += topk_before(fs[y], fc[y], sv, cx);
-    if (cx != 0x7fffffff && rank < cnt) {
-      sel_s[rank] = sv;
-      sel_c[rank] = cx;
-    }
-  }
-  __syncthreads();
-  const long long o = (long long)r * K;
-  if (t < K) {
-    if (t < cnt) {
-      const int cx = sel_c[t];
-      int pos = 0;
-      for (int k2 = 0; k2 < cnt; ++k2) pos += sel_c[k2] < cx;
-      idx[o + pos] = cx;
-      score[o + pos] = sel_s[t];
-    } else {
-      idx[o + t] = -1;
-      score[o + t] = -INFINITY;
-    }
-  }
-}
-
 }  // namespace
 
 bool score_mfma_group_applies(const Dims& dm) {
@@ -689,28 +571,6 @@ hipError_t launch_score_mfma_split(const Dims& dm, const void* Q, const float* k
     hipLaunchKernelGGL((k_score_split_mfma<128>), dim3(nsplit, rows), dim3(256), 0, st, dm,
                        reinterpret_cast<const uint16_t*>(Q), ksum, ent, ws_s, ws_i, nsplit);
   return hipGetLastError();
-}
-
-bool score_row_mfma_applies(const Dims& dm) {
-  // worth it only with enough rows to spread over the chip: a single row's
-  // summaries read by one compute unit are latency-bound
-  const long long rows = (long long)dm.B * dm.Tq * dm.H;
-  const long long ncand = dm.Tq > 0 ? dm.ncand(dm.q_pos0 + dm.Tq - 1) : 0;
-  return dm.bf16 && ncand <= kRowCand && ncand >= 1 && rows >= 256 && rows <= 65535;
-}
-
-bool score_row_mfma_try(const Dims& dm, const void* Q, const float* ksum, const float* ent,
-                        int32_t* idx, float* score, hipStream_t st, hipError_t* err) {
-  if (!score_row_mfma_applies(dm)) return false;
-  const long long rows = (long long)dm.B * dm.Tq * dm.H;
-  if (dm.d == 64)
-    hipLaunchKernelGGL((k_score_row_mfma<64>), dim3(rows), dim3(kRowWaves * 64), 0, st, dm,
-                       reinterpret_cast<const uint16_t*>(Q), ksum, ent, idx, score);
-  else
-    hipLaunchKernelGGL((k_score_row_mfma<128>), dim3(rows), dim3(kRowWaves * 64), 0, st, dm,
-                       reinterpret_cast<const uint16_t*>(Q), ksum, ent, idx, score);
-  *err = hipGetLastError();
-  return true;
 }
 
 }  // namespace hils

@@ -363,8 +363,6 @@ hipError_t launch_t(const Dims& dm, const void* Q, const float* ksum, const floa
     return hipGetLastError();
   }
   if (use_split(dm)) {
-    hipError_t err = hipSuccess;
-    if (score_row_mfma_try(dm, Q, ksum, ent, idx, score, st, &err)) return err;
     const int ns = split_count(dm);
     const long long rows = (long long)dm.B * dm.Tq * dm.H;
     float* ws_s = reinterpret_cast<float*>(ws);
@@ -444,7 +442,7 @@ int decode_lists_plan(const Dims& dm, int* km) {
   const long long rows = (long long)dm.B * dm.Tq * dm.H;
   if (rows == 0 || max_candidates(dm) == 0) return 0;
   if (dm.group_sel && dm.G > 1) return 0;
-  if (!use_split(dm) || score_row_mfma_applies(dm)) return 0;
+  if (!use_split(dm)) return 0;
   const int ns = split_count(dm);
   const int KMr = dm.K <= 16 ? 16 : (dm.K <= 32 ? 32 : 64);
   if (ns > 32 || ns * KMr > 1024) return 0;

@@ -45,6 +45,10 @@ CASES = {
     # 8 candidate splits of 64-entry lists merged inside the slot kernel
     "bf16_k64_splits8": (synth.small("dec_k64s", B=1, T=65536, H=2, Hkv=1, d=64, K=64,
                                      dtype="bf16"), 0, 1),
+    # 64 query positions per call: over the long cache the slot kernels serve
+    # them (at the first positions the matrix-core kernel does)
+    "bf16_64pos": (synth.small("dec_64pos", B=1, T=65536, H=2, Hkv=1, d=64, K=8,
+                               dtype="bf16"), 0, 64),
     # 17 splits of 32-entry lists at the last positions (the 24-list merge)
     "bf16_k32_splits17": (synth.small("dec_k32s", B=1, T=17 * 128 * 64 + 128, H=4, Hkv=2,
                                       d=64, K=32, dtype="bf16"), 0, 1),

@@ -131,9 +131,8 @@ def test_exact_ties_group_max(name):
     assert n_tie > 100
 
 
-# decode: the query rows sit at the end of the cache (q_pos0 = T - Tq); the row count
-# picks the kernel (below 256 rows: candidate splits of 128 and a merge whose kind
-# follows the list count; 256 or more: one workgroup per row)
+# decode: the query rows sit at the end of the cache (q_pos0 = T - Tq); candidate
+# splits of 128 and a merge whose kind follows the list count
 DECODE = {
     # 128 splits x 16 entries: rank merge
     "bf16_rank_k16": (synth.small("tie_dec_rank", B=1, T=16384, H=2, Hkv=1, d=64, K=16,
@@ -146,7 +145,7 @@ DECODE = {
                                 dtype="bf16", Tq=4, q_pos0=8256 * 64 - 4), 4),
     "f32_rank_k16": (synth.small("tie_dec_f32", B=1, T=16384, H=2, Hkv=1, d=64, K=16,
                                  dtype="f32", Tq=8, q_pos0=16384 - 8), 8),
-    # 128 positions x 2 heads = 256 rows: one workgroup per row
+    # 128 positions x 2 heads = 256 rows
     "bf16_rowwg_k16": (synth.small("tie_dec_row", B=1, T=8192, H=2, Hkv=1, d=64, K=16,
                                    dtype="bf16", Tq=128, q_pos0=8192 - 128), 128),
 }
