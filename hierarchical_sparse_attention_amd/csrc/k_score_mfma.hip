@@ -14,10 +14,10 @@
 // therefore identical selections.
 //
 // Prefill: one wavefront owns 64 query rows of one head. Candidates are scored
-// 64 at a time into LDS (16 x 16 MFMA blocks, rows on M, chunks on N); then each
-// lane takes one row and keeps its running top list in registers: in groups of
-// 16 candidates, a compare against the list's last score marks the few that can
-// enter, and those are inserted with a compare-exchange pass.
+// 64 (d = 128: 32) at a time into LDS (16 x 16 MFMA blocks, rows on M, chunks on
+// N); then each lane takes one row and keeps its running top list in registers:
+// in groups of 16 candidates, a compare against the list's last score marks the
+// few that can enter, and those are inserted with a compare-exchange pass.
 // Decode: candidates of a row are split over workgroups; each writes its local
 // top-K (rank counting), and the union is ranked by the merge kernel shared with
 // the float32 path or by the decode step's slot kernel itself.
@@ -136,7 +136,11 @@ template <int D, int KM>
 __global__ __launch_bounds__(64, (D == 128 && KM == 16) ? 3 : 1) void k_score_mfma(
     Dims dm, int nc, const uint16_t* __restrict__ Q, const uint4* __restrict__ ks,
     const float* __restrict__ ent, int32_t* __restrict__ idx, float* __restrict__ score) {
-  __shared__ float sS[64][65];
+  // candidates per block: 32 at d = 128 (a smaller LDS block lets more
+  // wavefronts share a compute unit: 0.51 against 0.57 ms at the 7B shape), 64 at
+  // d = 64 (where 32 measured 3% slower)
+  constexpr int CB = D == 128 ? 32 : 64;
+  __shared__ float sS[64][CB + 1];
   const int lane = threadIdx.x, c = lane & 15, g = lane >> 4;
   // 1-D grid, position blocks slowest and longest (latest) first
   const int nqb = (dm.Tq + 63) / 64, L = blockIdx.x;
@@ -159,9 +163,9 @@ __global__ __launch_bounds__(64, (D == 128 && KM == 16) ? 3 : 1) void k_score_mf
   }
   TopList<KM> top;
   top.init();
-  for (int c0 = 0; c0 < nmax; c0 += 64) {
+  for (int c0 = 0; c0 < nmax; c0 += CB) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < CB / 16; ++nb) {
       // a column past the candidates reads block 0 (in bounds): its score is
       // never looked at, so the loads need no condition and stay in flight
       // together
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(64, (D == 128 && KM == 16) ? 3 : 1) void k_score_mf
     __syncthreads();
     // lane = row. In sub-blocks of 16 candidates: mark the ones that beat the
     // row's current KM-th score, then insert them (all lanes step together).
-    const int lim = min(64, my_n - c0);
+    const int lim = min(CB, my_n - c0);
     int sb0 = 0;
     if (c0 == 0) {
       // the row's first 16 candidates fill its empty list in one sort
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(64, (D == 128 && KM == 16) ? 3 : 1) void k_score_mf
       sb0 = 1;
     }
 #pragma unroll 1
-    for (int sb = sb0; sb < 4; ++sb) {
+    for (int sb = sb0; sb < CB / 16; ++sb) {
       const float theta = top.s[KM - 1];
       // the 16 reads are unconditional and combined without short-circuit, so
       // they are all in flight together
