@@ -273,8 +273,6 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
   constexpr int PS = 64 / G;  // positions each wavefront selects for
   static_assert(G == 2 || G == 4, "group size");
   extern __shared__ __align__(16) float gsm2[];
-  float (*sS)[64][65] = reinterpret_cast<float (*)[64][65]>(gsm2);              // [G]
-  uint32_t* selb = reinterpret_cast<uint32_t*>(gsm2 + G * 64 * 65);              // [64][words]
   const int t = threadIdx.x, lane = t & 63, hh = t >> 6, c = lane & 15, g = lane >> 4;
   const int nqb = (dm.Tq + 63) / 64, L = blockIdx.x;
   const int gk = L % dm.Hkv, b = (L / dm.Hkv) % dm.B, K = dm.K;
@@ -283,6 +281,12 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
   const int npos = min(64, dm.Tq - i0);
   const int nmax = dm.ncand(dm.q_pos0 + i0 + npos - 1);
   const int words = (nmax + 31) / 32;
+  // LDS: the G score blocks, later reused by the second pass's prefix table
+  // (64 x words ints, larger than the blocks past 65 G 32 candidates), then the
+  // bitmask; layout as group_mfma_smem sizes it for nc candidates
+  float (*sS)[64][65] = reinterpret_cast<float (*)[64][65]>(gsm2);  // [G]
+  uint32_t* selb =
+      reinterpret_cast<uint32_t*>(gsm2 + max(G * 64 * 65, 64 * ((nc + 31) / 32)));  // [64][words]
   // selecting lane: position sp = hh PS + lane of the block
   const int sp = hh * PS + min(lane, PS - 1);
   const bool sel_lane = lane < PS && sp < npos;
@@ -449,7 +453,9 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
 }
 
 size_t group_mfma_smem(int G, int nmax) {
-  return (size_t)G * 64 * 65 * sizeof(float) + (size_t)64 * ((nmax + 31) / 32) * sizeof(uint32_t);
+  const size_t words = (nmax + 31) / 32;
+  return std::max<size_t>((size_t)G * 64 * 65, 64 * words) * sizeof(float) +
+         64 * words * sizeof(uint32_t);
 }
 
 // Decode split: grid (splits, rows); a workgroup of 4 wavefronts scores the

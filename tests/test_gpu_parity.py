@@ -367,6 +367,42 @@ def test_forward_group_max(name):
     check_group_forward(w, x, f)
 
 
+# Long contexts: the matrix-core group scorer's second pass keeps a per-(position,
+# bitmask word) prefix table that grows with the candidate count; past 65 G 32
+# candidates (4160 at G = 2, 8320 at G = 4) it is larger than the first pass's
+# score blocks. Summaries are drawn directly (float32 normals; the query rows are
+# bf16 values) and the 64 query positions sit at the end of the context.
+LONG_GROUP = {"g2_4800": (2, 4800), "g4_8500": (4, 8500)}
+
+
+@pytest.mark.parametrize("name", list(LONG_GROUP))
+def test_group_max_long_context(name):
+    G, NC = LONG_GROUP[name]
+    B, Hkv, d, S, K, Tq = 1, 1, 128, 64, 16, 64
+    H = G * Hkv
+    Tkv = NC * S + S // 2          # the last position's candidates: chunks 0 .. NC - 1
+    q_pos0 = Tkv - Tq
+    say(f"[group-max long context] G{G} candidates {NC}")
+    rng = np.random.default_rng(1000 + G)
+    Qg = torch.from_numpy(rng.standard_normal((B, Tq, H, d)).astype(np.float32)).to(torch.bfloat16)
+    Qo = Qg.double().numpy()
+    ksum = (0.5 * rng.standard_normal((B, NC + 1, H, d))).astype(np.float32)
+    ent = (0.3 * rng.standard_normal((B, NC + 1, H))).astype(np.float32)
+    idx, sc = hsa.score_topk(Qg.to(DEV), torch.from_numpy(ksum).to(DEV),
+                             torch.from_numpy(ent).to(DEV), K, S, q_pos0=q_pos0, Tkv=Tkv,
+                             Hkv=Hkv, group=True)
+    torch.cuda.synchronize()
+    ko, eo = ksum.astype(np.float64), ent.astype(np.float64)
+    oi, os_, gap = oracle.score_topk(Qo, ko, eo, S, K, q_pos0=q_pos0, group_hkv=Hkv)
+    gi, gs = host(idx), host(sc)
+    excl, eq = compare_selection(gi, oi, gap, K,
+                                 lambda r: all_scores(Qo, ko, eo, S, r, q_pos0, group_hkv=Hkv))
+    say(f"  near-tie rows excluded: {int(excl.sum())}/{excl.size}")
+    assert eq.sum() >= excl.size // 2
+    m = eq[..., None].repeat(K, -1) & (oi >= 0)
+    assert_close(gs[m], os_[m], TOL_F32, "score")
+
+
 def test_backward_with_group_selection():
     """The backward takes any fixed selection: here a group-max one (bf16, G = 4)."""
     w = synth.small("bwd_grp", B=1, T=768, H=8, Hkv=2, d=64, K=5, dtype="bf16", need_dO=True)
