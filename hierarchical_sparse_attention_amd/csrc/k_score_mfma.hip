@@ -87,21 +87,22 @@ struct TopList {
 #pragma unroll
     for (int k = 0; k < KM; ++k) { s[k] = -INFINITY; c[k] = 0x7fffffff; }
   }
+  // x enters after every entry it does not beat (strictly greater goes first,
+  // so an equal score from a later chunk stays behind). Updated in place from
+  // the tail: slot k's new score is the median of x, s[k - 1] and s[k] (the list
+  // is descending) and is written while s[k - 1] still holds its old value, so
+  // no copy of the list is made; each comparison serves two neighbouring slots.
   __device__ __forceinline__ void insert(float x, int xc) {
-    float ns[KM];
-    int nc[KM];
-    bool gprev = false;
+    bool gk = x > s[KM - 1];
 #pragma unroll
-    for (int k = 0; k < KM; ++k) {
-      const bool gk = x > s[k];
-      const float ts = gk ? x : s[k];
-      const int tc = gk ? xc : c[k];
-      ns[k] = gprev ? s[k - (k > 0)] : ts;
-      nc[k] = gprev ? c[k - (k > 0)] : tc;
-      gprev = gk;
+    for (int k = KM - 1; k > 0; --k) {
+      const bool gp = x > s[k - 1];
+      s[k] = __builtin_amdgcn_fmed3f(x, s[k - 1], s[k]);
+      c[k] = gp ? c[k - 1] : (gk ? xc : c[k]);
+      gk = gp;
     }
-#pragma unroll
-    for (int k = 0; k < KM; ++k) s[k] = ns[k], c[k] = nc[k];
+    s[0] = gk ? x : s[0];
+    c[0] = gk ? xc : c[0];
   }
 };
 
