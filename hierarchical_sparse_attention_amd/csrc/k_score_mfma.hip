@@ -106,6 +106,16 @@ struct TopList {
   }
 };
 
+// Largest v (0 .. 16) over the wavefront, by a binary search on ballots
+// (compares and scalar operations, no cross-lane data movement).
+__device__ __forceinline__ int wave_max16(int v) {
+  int m = 0;
+#pragma unroll
+  for (int bit = 16; bit > 0; bit >>= 1)
+    if (__builtin_amdgcn_ballot_w64(v >= m + bit) != 0) m += bit;
+  return m;
+}
+
 // Sorts 16 (score, chunk) pairs by (score desc, chunk asc) in registers with a
 // bitonic network (80 compare-exchanges at fixed positions).
 __device__ __forceinline__ void sort16(float* x, int* xc) {
@@ -219,9 +229,7 @@ __global__ __launch_bounds__(64, (D == 128 && KM == 16) ? 3 : 1) void k_score_mf
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj)
         mask |= ((16 * sb + jj < lim) & (xv[jj] > theta)) ? (1u << jj) : 0u;
-      int todo = __popc(mask);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) todo = max(todo, __shfl_xor(todo, o, 64));
+      const int todo = wave_max16(__popc(mask));
       // each insert's candidate is read one insert ahead
       int jj = mask ? __ffs(mask) - 1 : 0;
       float x = sS[lane][16 * sb + jj];
@@ -373,9 +381,7 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj)
         mask |= ((16 * sb + jj < lim) & (xv[jj] > theta)) ? (1u << jj) : 0u;
-      int todo = __popc(mask);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) todo = max(todo, __shfl_xor(todo, o, 64));
+      const int todo = wave_max16(__popc(mask));
       // each insert's candidate is read one insert ahead
       int jj = mask ? __ffs(mask) - 1 : 0;
       float x = gscore(16 * sb + jj);
