@@ -46,6 +46,9 @@ COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
 # kernels behind each measured call, and the sources they are built from (a
 # counter record is used only while those sources are unchanged)
 CALL_KERNELS = {
+    "summarize": (("k_summarize",), ("k_summarize.hip", "hils_internal.h")),
+    "score_topk": (("k_ksplit", "k_score_mfma"),
+                   ("k_score_mfma.hip", "k_score_topk.hip", "mfma_common.h", "hils_internal.h")),
     "attend_fuse": (("k_kv_prep", "k_attend_mfma"),
                     ("k_attend_mfma.hip", "k_attend_fuse.hip", "hils_internal.h")),
     "decode": (("k_score_split_mfma", "k_decode_merge_partial", "k_decode_combine"),
@@ -346,9 +349,10 @@ def measure_prefill(torch, ev_ms, w, f, calls, reps, workload, window=0):
     cnt = prefill_counts(w, f["idx"].cpu().numpy(), window)
     fwd_ms = km["summarize"] + km["score_topk"] + km["attend_fuse"]
     blocks = {
-        "summarize": roofline("hils_summarize (k_summarize)", "hbm", cnt["summarize_bytes"],
-                              km["summarize"]),
+        "summarize": roofline("hils_summarize (k_summarize_mfma)", "hbm", cnt["summarize_bytes"],
+                              km["summarize"], call_traffic(workload, "summarize")),
         "score_topk": roofline("hils_score_topk", "alu", cnt["score_flops"], km["score_topk"],
+                               call_traffic(workload, "score_topk"),
                                note="float32-accurate products on bf16 MFMAs over a hi/lo split "
                                     "of the summary key, against the float32 vector peak"),
         "attend_fuse": roofline("hils_attend_fuse (k_kv_prep + k_attend_mfma)", "mfma",

@@ -74,19 +74,30 @@ def test_summarize(name):
     assert_close(host(lse), olse, TOL_F32, "lse_l")
 
 
-# groups of 3 and 8 query heads per kv head: the summaries run a round with an
-# idle wavefront (3 heads on 2) and two rounds of 4
+# groups of query heads per kv head: bf16 takes up to 16 heads per matrix-core
+# round (3 and 8 in one round, 20 in rounds of 16 and 4); float32 runs a round
+# with an idle wavefront (3 heads on 2)
 GROUPS = {
     "bf16_g3": synth.small("sum_g3", B=1, T=640, H=3, Hkv=1, d=64, K=4, dtype="bf16"),
     "bf16_d128_g8": synth.small("sum_g8", B=2, T=512, H=16, Hkv=2, d=128, K=4, dtype="bf16"),
+    "bf16_g20": synth.small("sum_g20", B=1, T=320, H=40, Hkv=2, d=64, K=4, dtype="bf16"),
+    "bf16_d128_g20": synth.small("sum_g20d", B=1, T=256, H=20, Hkv=1, d=128, K=4, dtype="bf16"),
     "f32_g3": synth.small("sum_g3f", B=1, T=384, H=6, Hkv=2, d=64, K=4, dtype="f32"),
 }
 
 
-@pytest.mark.parametrize("name", list(GROUPS))
+@pytest.mark.parametrize("name", list(GROUPS) + ["peaked_bf16", "peaked_bf16_d128"])
 def test_summarize_head_groups(name):
-    w = GROUPS[name]
-    x = synth.make_inputs(w)
+    """Summaries per head group against the oracle. The peaked cases scale the
+    landmark queries by 16 (exact in bf16), so each chunk's landmark softmax
+    puts almost all of its mass on one or two keys (entropy near 0)."""
+    if name.startswith("peaked"):
+        w = GROUPS["bf16_d128_g8" if name.endswith("d128") else "bf16_g3"]
+        x = synth.make_inputs(w)
+        x["Ql"] = x["Ql"] * 16.0
+    else:
+        w = GROUPS[name]
+        x = synth.make_inputs(w)
     say(f"[summarize groups] {name}")
     t = {k: dev(x[k], w.dtype) for k in ("K", "Ql")}
     ksum, ent, lse = hsa.summarize(t["K"], t["Ql"], w.S)
