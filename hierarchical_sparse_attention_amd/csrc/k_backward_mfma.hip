@@ -211,7 +211,11 @@ __global__ __launch_bounds__(256) void k_dq_reduce(Dims dm, long long rows,
 // deterministic passes over blocks of kLBlk positions: per-block counts, an
 // exclusive scan per (b, h) in (chunk, block) order, and a fill that ranks each
 // selecting position within its block by popcounts of a block bitmap.
-constexpr int kLBlk = 512;  // positions per block (16 bitmap words)
+// 256 positions per block (8 bitmap words): the fill's LDS (bitmap, staged
+// records) then fits three workgroups per compute unit at K = 16, whose phases
+// overlap (one 512-position workgroup per compute unit left every barrier and
+// round trip exposed)
+constexpr int kLBlk = 256;
 
 // A row's K selection entries into registers (KM >= K slots, all reads issued
 // together; slots past K repeat entry K - 1 and are never used).
@@ -249,19 +253,29 @@ __global__ __launch_bounds__(256) void k_sel_count(Dims dm, int nblk, const int3
 }
 
 // In place: cnt[b][h][c][blk] -> offset of the block's entries of chunk c in the
-// (b, h) list space; lstart / llen per (b, h, c).
-__global__ __launch_bounds__(256) void k_sel_scan(Dims dm, int nblk, int* __restrict__ cnt,
-                                                  int* __restrict__ lstart, int* __restrict__ llen) {
-  __shared__ int wtot[4];
+// (b, h) list space; lstart / llen per (b, h, c). Each thread takes a contiguous
+// segment, sixteen counts' loads in flight at a time.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void k_sel_scan(Dims dm, int nblk, int* __restrict__ cnt,
+                                                           int* __restrict__ lstart,
+                                                           int* __restrict__ llen) {
+  constexpr int kW = kScanThreads / 64;
+  __shared__ int wtot[kW];
   const int NC = dm.Tkv / dm.S;
   const long long bh = (long long)blockIdx.y * dm.H + blockIdx.x;
   int* a = cnt + bh * NC * nblk;
   const int n = NC * nblk;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int seg = (n + 255) / 256;
+  const int seg = (n + kScanThreads - 1) / kScanThreads;
   const int lo = min(n, t * seg), hi = min(n, lo + seg);
   int s = 0;
-  for (int x = lo; x < hi; ++x) s += a[x];
+  for (int x0 = lo; x0 < hi; x0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = x0 + j < hi ? a[x0 + j] : 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += v[j];
+  }
   int incl = s;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -272,18 +286,23 @@ __global__ __launch_bounds__(256) void k_sel_scan(Dims dm, int nblk, int* __rest
   __syncthreads();
   int before = 0, total = 0;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
+  for (int x = 0; x < kW; ++x) {
     before += x < w ? wtot[x] : 0;
     total += wtot[x];
   }
   int run = before + incl - s;
-  for (int x = lo; x < hi; ++x) {
-    const int v = a[x];
-    a[x] = run;
-    run += v;
+  for (int x0 = lo; x0 < hi; x0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = x0 + j < hi ? a[x0 + j] : 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (x0 + j < hi) a[x0 + j] = run;
+      run += v[j];
+    }
   }
   __syncthreads();
-  for (int c = t; c < NC; c += 256) {
+  for (int c = t; c < NC; c += kScanThreads) {
     const int st = a[(long long)c * nblk];
     const int en = c + 1 < NC ? a[(long long)(c + 1) * nblk] : total;
     lstart[bh * NC + c] = st;
@@ -299,7 +318,7 @@ __global__ __launch_bounds__(256) void k_sel_scan(Dims dm, int nblk, int* __rest
 // own thread scatters 16-byte pieces over a line per chunk. Each row's entries
 // and scores are read once, all at a time. The records and their places are the
 // same either way.
-constexpr int kFillThreads = 512;  // one row of the block per thread
+constexpr int kFillThreads = kLBlk;  // one row of the block per thread
 template <bool STAGED, int KM>
 __global__ __launch_bounds__(kFillThreads) void k_sel_fill(Dims dm, int nblk, const int32_t* __restrict__ idx,
                                                   const float* __restrict__ score,
@@ -976,7 +995,8 @@ hipError_t launch_lists(const Dims& dm, const BPlan& p, const int32_t* idx, cons
                         int4* srec, hipStream_t st) {
   hipLaunchKernelGGL(k_sel_count<KM>, dim3(p.nblk, dm.H, dm.B), dim3(256),
                      (size_t)p.nct * sizeof(int), st, dm, p.nblk, idx, cnt);
-  hipLaunchKernelGGL(k_sel_scan, dim3(dm.H, dm.B), dim3(256), 0, st, dm, p.nblk, cnt, lstart, llen);
+  hipLaunchKernelGGL(k_sel_scan, dim3(dm.H, dm.B), dim3(kScanThreads), 0, st, dm, p.nblk, cnt,
+                     lstart, llen);
   const void* fk = p.staged ? reinterpret_cast<const void*>(k_sel_fill<true, KM>)
                             : reinterpret_cast<const void*>(k_sel_fill<false, KM>);
   hipError_t e = hipFuncSetAttribute(fk, hipFuncAttributeMaxDynamicSharedMemorySize,

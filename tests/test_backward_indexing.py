@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 S = 64
-LBLK = 512            # positions per block of the list passes
+LBLK = 256            # positions per block of the list passes
 TILE = 32             # rows per key-side tile
 KWAVES = 4            # wavefronts per key-side workgroup
 LIST_MAX = 64 + 64 * 32
