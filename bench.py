@@ -274,6 +274,22 @@ def decode_step_bytes(wd, K_sel, window, p):
             + 2 * H * d * 2 + H * K_sel * 8)
 
 
+def decode_call_unique_bytes(wd, K_sel, window, p, nb, idx):
+    """Algorithmic HBM bytes of one decode call of nb consecutive positions p ..
+    p + nb - 1 of one sequence (idx [nb, H, K] their selections): the summaries
+    and entropies of the last position's candidates once, each selected (head,
+    chunk) once however many positions picked it, the keys and values of the
+    local branch up to the last position once per head, and the queries,
+    outputs and selections of every position."""
+    H, d, S = wd.H, wd.d, wd.S
+    last = p + nb - 1
+    n = lstart_of(last, S, window) // S
+    sel = sum(len(np.unique(idx[:, h][idx[:, h] >= 0])) for h in range(H))
+    loc = last - lstart_of(p, S, window) + 1
+    return (n * H * (d + 1) * 4 + sel * S * d * 2 * 2 + H * loc * d * 2 * 2
+            + nb * (2 * H * d * 2 + H * K_sel * 8))
+
+
 def roofline(kernel, bound, work, ms, traffic=None, note=None):
     """Roofline block: achieved = algorithmic work per launch / launch duration."""
     if bound == "mfma":
@@ -387,15 +403,16 @@ def measure_decode(torch, hsa, stream, td, wd, K_sel, window, Kc, Vc, nsteps, de
     p0, S = wd.q_pos0, wd.S
     NCd = wd.T // S
     nsteps = nsteps // nb
-    dk = torch.empty(1, NCd, wd.H, wd.d, device=dev)
-    de = torch.empty(1, NCd, wd.H, device=dev)
-    dl = torch.empty(1, NCd, wd.H, device=dev)
+    Bq = Kc.shape[0]  # sequences decoding together, each with its own cache
+    dk = torch.empty(Bq, NCd, wd.H, wd.d, device=dev)
+    de = torch.empty(Bq, NCd, wd.H, device=dev)
+    dl = torch.empty(Bq, NCd, wd.H, device=dev)
     hsa.summarize(Kc, td["Ql"], S, 0, p0 // S, Tkv=p0, ksum=dk, ent=de, lse_l=dl)
-    didx = torch.empty(nsteps, 1, nb, wd.H, K_sel, dtype=torch.int32, device=dev)
-    dsc = torch.empty(nsteps, 1, nb, wd.H, K_sel, device=dev)
-    dO = torch.empty(1, nb, wd.H, wd.d, dtype=torch.bfloat16, device=dev)
-    dlo = torch.empty(1, nb, wd.H, device=dev)
-    dlt = torch.empty(1, nb, wd.H, device=dev)
+    didx = torch.empty(nsteps, Bq, nb, wd.H, K_sel, dtype=torch.int32, device=dev)
+    dsc = torch.empty(nsteps, Bq, nb, wd.H, K_sel, device=dev)
+    dO = torch.empty(Bq, nb, wd.H, wd.d, dtype=torch.bfloat16, device=dev)
+    dlo = torch.empty(Bq, nb, wd.H, device=dev)
+    dlt = torch.empty(Bq, nb, wd.H, device=dev)
     ws = hsa.decode_workspace(td["Q"][:, :nb], Kc, dk, K_sel, S, wd.T - nb, wd.T, window=window)
     qs = [td["Q"][:, nb * s:nb * s + nb].contiguous() for s in range(nsteps)]
 
@@ -435,10 +452,16 @@ def measure_decode(torch, hsa, stream, td, wd, K_sel, window, Kc, Vc, nsteps, de
     ev[1].record(stream)
     torch.cuda.synchronize()
     us = ev[0].elapsed_time(ev[1]) * 1e3 / (nsteps * reps)
-    mean_bytes = float(np.mean([sum(decode_step_bytes(wd, K_sel, window, p0 + nb * s + j)
-                                    for j in range(nb)) for s in range(nsteps)]))
-    rec = {"us_per_token": us / nb, "us_per_step": us, "us_per_token_eager": eager / nb,
-           "steps": nsteps, "rows_per_step": nb * wd.H, "bytes_per_step": mean_bytes,
+    if nb == 1:  # every sequence moves its own bytes
+        mean_bytes = Bq * float(np.mean([decode_step_bytes(wd, K_sel, window, p0 + s)
+                                         for s in range(nsteps)]))
+    else:  # nb positions of one sequence share its summaries and chunks
+        mean_bytes = float(np.mean([decode_call_unique_bytes(wd, K_sel, window, p0 + nb * s, nb,
+                                                             didx[s, 0].cpu().numpy())
+                                    for s in range(nsteps)]))
+    rec = {"us_per_token": us / (nb * Bq), "us_per_step": us,
+           "us_per_token_eager": eager / (nb * Bq), "steps": nsteps,
+           "rows_per_step": Bq * nb * wd.H, "bytes_per_step": mean_bytes,
            "roofline": roofline("hils_decode (split scoring; list merge and slot attention; slot "
                                 "fusion: three launches; a k_summarize every 64 positions)",
                                 "hbm", mean_bytes, us * 1e-3, traffic),
@@ -619,9 +642,31 @@ def main():
         del Kh, Vh
         rec, _ = measure_decode(torch, hsa, stream, td, wd, wd.K, 0, td["K"], td["V"], nsteps,
                                 dev, nb=16)
-        rec["rows"] = ("16 query positions per call, a stand-in for 16 sequences decoding "
-                       "together: per-row work and bytes are a sequence's")
-        extra["decode_128k_16_rows"] = rec
+        rec["rows"] = ("16 consecutive query positions of the one sequence per call (as in "
+                       "speculative or chunked decoding); bytes are the call's unique ones: the "
+                       "summaries once, each selected (head, chunk) once")
+        extra["decode_128k_16_positions"] = rec
+        # 16 sequences decoding together, each with its own 128K cache (8.6 GB of K and V,
+        # drawn on the GPU from a seeded generator: a timing input, not a parity case)
+        nbat = 16
+        log("generating decode_128k batch-16 inputs")
+        gen = torch.Generator(device=dev).manual_seed(wd.seed + 1000)
+        tb = {"Q": torch.randn(nbat, wd.rows_q, wd.H, wd.d, device=dev, generator=gen),
+              "Ql": torch.randn(nbat, wd.T // wd.S, wd.H, wd.d, device=dev, generator=gen)}
+        tb = {k: v.to(torch.bfloat16) for k, v in tb.items()}
+        for k in ("K", "V"):
+            x = torch.empty(nbat, wd.T, wd.Hkv, wd.d, dtype=torch.bfloat16, device=dev)
+            for i in range(nbat):
+                x[i] = torch.randn(wd.T, wd.Hkv, wd.d, device=dev, generator=gen)
+            tb[k] = x
+        rec, _ = measure_decode(torch, hsa, stream, tb, wd, wd.K, 0, tb["K"], tb["V"], nsteps,
+                                dev)
+        rec["batch"] = nbat
+        rec["inputs"] = ("16 independent 128K caches, N(0,1) from a seeded GPU generator; "
+                         "each sequence moves its own summaries and chunks")
+        extra["decode_128k_batch16"] = rec
+        del tb
+        torch.cuda.empty_cache()
     if oracle is not None:
         log("cpu baseline: 128K decode")
         cpu_extra["decode_128k"] = cpu_decode(oracle, xd, wd, wd.K, nsteps)

@@ -1,5 +1,6 @@
 // C-ABI entry points of libhils: argument validation, workspace sizing and
 // kernel dispatch. Every check happens before anything is enqueued.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -113,25 +114,44 @@ hils_status from_hip(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_ERR
 
 // A decode step of few rows runs as split scoring, then a slot kernel that
 // merges the split lists itself, then the combine: the lists and the slot
-// partials are live together, lists first. Otherwise the step is the two calls
-// one after the other on the stream, which share the larger of their workspaces.
-int decode_merged_plan(const hils::Dims& dm, int* km) {
-  if (!hils::attend_is_decode(dm)) return 0;
+// partials are live together, lists first. A step of many rows (sequences
+// decoding together) runs as split scoring, then one workgroup per row that
+// merges once, attends every slot and fuses them in LDS. Otherwise the step is
+// the two calls one after the other on the stream, which share the larger of
+// their workspaces.
+enum DecodePlan { kDecodeCalls = 0, kDecodeMerged = 1, kDecodeRow = 2 };
+// rows from which one workgroup per row pays: on 128K caches, 128 rows (8
+// sequences of 16 heads) 33.7 against 35.0 us per step with the merge, slot and
+// combine launches, 256 rows 48.0 against 51.0 us
+constexpr long long kDecodeRowMin = 128;
+DecodePlan decode_plan(const hils::Dims& dm, int* ns, int* km) {
+  *ns = 0;
+  if (!hils::attend_is_decode(dm)) return kDecodeCalls;
+  const long long rows = (long long)dm.B * dm.Tq * dm.H;
   // every slot's workgroup repeats its row's merge: worth it while the slots
   // fill the chip about once (a K = 16 step of 16 heads: 272 workgroups); with
   // more slots the separate merge launch costs less than the repeated merges
-  const long long slots = (long long)dm.B * dm.Tq * dm.H * (dm.K + dm.nlocal_max());
-  if (slots > 384) return 0;
-  return hils::decode_lists_plan(dm, km);
+  const long long slots = rows * (dm.K + dm.nlocal_max());
+  if (slots > 384 && rows < kDecodeRowMin) return kDecodeCalls;
+  *ns = hils::decode_lists_plan(dm, km);
+  if (*ns == 0) return kDecodeCalls;
+  if (slots <= 384) return kDecodeMerged;
+  return hils::decode_row_applies(dm, *ns, *km) ? kDecodeRow : kDecodeCalls;
 }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t decode_ws(const hils::Dims& dm) {
-  int km = 0;
-  const int ns = decode_merged_plan(dm, &km);
-  if (ns > 0) return align256(hils::decode_lists_ws_bytes(dm, ns)) + hils::attend_ws_bytes(dm);
+  int km = 0, ns = 0;
+  const DecodePlan pl = decode_plan(dm, &ns, &km);
+  if (pl == kDecodeMerged)
+    return align256(hils::decode_lists_ws_bytes(dm, ns)) + hils::attend_ws_bytes(dm);
   const size_t a = hils::score_topk_ws_bytes(dm), b = hils::attend_ws_bytes(dm);
-  return a > b ? a : b;
+  const size_t calls = a > b ? a : b;
+  // the row plan needs only the lists; it also covers the two calls, which the
+  // same shape takes at positions with no candidates, so a workspace sized for
+  // any position serves every position of the shape
+  if (pl == kDecodeRow) return std::max(hils::decode_lists_ws_bytes(dm, ns), calls);
+  return calls;
 }
 
 hils_status check_ws(size_t need, const void* ws, size_t ws_bytes) {
@@ -254,15 +274,18 @@ hils_status hils_decode(const hils_dims* dims, const void* Q, const void* K, con
   const void *Kd = nullptr, *Vd = nullptr;
   if ((st = kv_view(K, &Kd)) != HILS_OK || (st = kv_view(V, &Vd)) != HILS_OK) return st;
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  int km = 0;
-  const int ns = decode_merged_plan(dm, &km);
-  if (ns > 0) {
+  int km = 0, ns = 0;
+  const DecodePlan pl = decode_plan(dm, &ns, &km);
+  if (pl != kDecodeCalls) {
     const long long nl = (long long)dm.B * dm.Tq * dm.H * ns * dm.K;
     float* ws_s = reinterpret_cast<float*>(ws);
     int* ws_i = reinterpret_cast<int*>(ws_s + nl);
-    void* ws_a = reinterpret_cast<char*>(ws) + align256(hils::decode_lists_ws_bytes(dm, ns));
     hipError_t e = hils::launch_decode_lists(dm, Q, ksum, ent, ws_s, ws_i, ns, hs);
     if (e != hipSuccess) return HILS_ERR_HIP;
+    if (pl == kDecodeRow)
+      return from_hip(hils::launch_decode_row(dm, Q, Kd, Vd, ws_s, ws_i, ns, km, idx, score, O,
+                                              lse_own, lse_tot, hs));
+    void* ws_a = reinterpret_cast<char*>(ws) + align256(hils::decode_lists_ws_bytes(dm, ns));
     return from_hip(hils::launch_decode_merged(dm, Q, Kd, Vd, ws_s, ws_i, ns, km, idx, score, O,
                                                lse_own, lse_tot, ws_a, hs));
   }

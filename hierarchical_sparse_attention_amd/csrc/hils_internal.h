@@ -329,6 +329,14 @@ hipError_t launch_decode_merged(const Dims& dm, const void* Q, const void* K, co
                                 const float* ws_s, const int* ws_i, int nsplit, int km,
                                 int32_t* idx, float* score, void* O, float* lse_own,
                                 float* lse_tot, void* ws, hipStream_t st);
+// The same rest of the step with one workgroup per row (merge once, every slot,
+// combine in LDS): for calls of many rows. Same outputs bit for bit; needs no
+// workspace beyond the lists.
+bool decode_row_applies(const Dims& dm, int nsplit, int km);
+hipError_t launch_decode_row(const Dims& dm, const void* Q, const void* K, const void* V,
+                             const float* ws_s, const int* ws_i, int nsplit, int km, int32_t* idx,
+                             float* score, void* O, float* lse_own, float* lse_tot,
+                             hipStream_t st);
 
 size_t backward_ws_bytes(const Dims& dm);
 size_t backward_mfma_ws_bytes(const Dims& dm);

@@ -317,29 +317,27 @@ __global__ __launch_bounds__(1024) void k_decode_merge_partial(
   }
 }
 
-// Combine kernel: one wavefront per row applies the inter-chunk softmax to the
-// slots in a fixed order (selected slots by their chunk score, local slots by
-// their exact log-mass). Lane k holds slots k and 64 + k.
+// Inter-chunk softmax of one row over its slots in a fixed order (selected slots
+// by their chunk score, local slots by their exact log-mass), by one wavefront.
+// sc: the row's K selection scores by slot; po / pl: the row's slot outputs
+// [NS][D] and log-masses [NS] (-inf for padding). Lane k holds slots k and
+// 64 + k. The pointers may be global or LDS: the arithmetic is the same.
 template <bool BF16, int D>
-__global__ __launch_bounds__(64) void k_decode_combine(Dims dm, const float* __restrict__ score,
-                                                       const float* __restrict__ part_o,
-                                                       const float* __restrict__ part_l,
-                                                       void* __restrict__ O,
-                                                       float* __restrict__ lse_own,
-                                                       float* __restrict__ lse_tot) {
+__device__ __forceinline__ void combine_row(const Dims& dm, long long r, const float* sc_row,
+                                            const float* po, const float* pl_row,
+                                            void* __restrict__ O, float* __restrict__ lse_own,
+                                            float* __restrict__ lse_tot) {
   constexpr int X = D / kWave;
   constexpr int KF = 48 / X;  // slots whose partials are read in the first round trip
-  const long long r = blockIdx.x;
-  const int lane = threadIdx.x, Ks = dm.K, NS = Ks + dm.nlocal_max();
-  const long long pb = r * NS;
+  const int lane = threadIdx.x & (kWave - 1), Ks = dm.K, NS = Ks + dm.nlocal_max();
   // every read is issued before any is used; rows of padding slots were not
   // written and are read only to keep the loads unconditional (weight 0)
   float lg[2], loc[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int k = lane + 64 * u, kc = min(k, NS - 1);
-    const float pl = part_l[pb + kc];
-    const float sc = score[r * Ks + min(k, Ks - 1)];
+    const float pl = pl_row[kc];
+    const float sc = sc_row[min(k, Ks - 1)];
     lg[u] = k >= NS ? -INFINITY : k < Ks ? (pl != -INFINITY ? sc : -INFINITY) : pl;
     loc[u] = k >= Ks && k < NS ? pl : -INFINITY;
   }
@@ -347,7 +345,7 @@ __global__ __launch_bounds__(64) void k_decode_combine(Dims dm, const float* __r
 #pragma unroll
   for (int k = 0; k < KF; ++k)
 #pragma unroll
-    for (int x = 0; x < X; ++x) pv[k][x] = part_o[(pb + min(k, NS - 1)) * D + lane + kWave * x];
+    for (int x = 0; x < X; ++x) pv[k][x] = po[min(k, NS - 1) * D + lane + kWave * x];
   const float ml = wave_max(fmaxf(loc[0], loc[1]));
   const float l_own = ml + logf(wave_sum(expf(loc[0] - ml) + expf(loc[1] - ml)));
   const float mx = wave_max(fmaxf(lg[0], lg[1]));
@@ -371,7 +369,7 @@ __global__ __launch_bounds__(64) void k_decode_combine(Dims dm, const float* __r
     for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int x = 0; x < X; ++x)
-        pw[u][x] = part_o[(pb + min(k0 + u, NS - 1)) * D + lane + kWave * x];
+        pw[u][x] = po[min(k0 + u, NS - 1) * D + lane + kWave * x];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int k = k0 + u;
@@ -388,6 +386,110 @@ __global__ __launch_bounds__(64) void k_decode_combine(Dims dm, const float* __r
     if (lse_own) lse_own[r] = l_own;
     if (lse_tot) lse_tot[r] = Lambda;
   }
+}
+
+// Combine kernel: one wavefront per row (combine_row over the slot partials in
+// the workspace).
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void k_decode_combine(Dims dm, const float* __restrict__ score,
+                                                       const float* __restrict__ part_o,
+                                                       const float* __restrict__ part_l,
+                                                       void* __restrict__ O,
+                                                       float* __restrict__ lse_own,
+                                                       float* __restrict__ lse_tot) {
+  const long long r = blockIdx.x;
+  const long long pb = r * (dm.K + dm.nlocal_max());
+  combine_row<BF16, D>(dm, r, score + r * dm.K, part_o + pb * D, part_l + pb, O, lse_own,
+                       lse_tot);
+}
+
+// One decode row per workgroup, for calls of many rows (batched sequences): the
+// row's split lists are merged once (as the merge kernel does), its selected and
+// local slots are attended by the workgroup's wavefronts (slot u on wavefront u
+// mod waves, as the slot kernel does) into LDS, and the slots are fused from
+// LDS by combine_row. Same arithmetic as the merge, slot and combine kernels,
+// so the results are the same bit for bit, with no slot partials in global
+// memory. Dynamic LDS: the slot outputs [NS][D], log-masses [NS] and the
+// selection scores [K]. At d = 128 a slot's key and value rows take 128
+// registers, so the workgroup holds at most 512 threads.
+template <int D>
+constexpr int kRowThreads = D == 128 ? 512 : 1024;
+template <bool BF16, int D, int KM, int NL>
+__global__ __launch_bounds__(kRowThreads<D>) void k_decode_row(
+    Dims dm, const void* __restrict__ Q, const void* __restrict__ K, const void* __restrict__ V,
+    const float* __restrict__ ws_s, const int* __restrict__ ws_i, int nsplit,
+    int32_t* __restrict__ idx, float* __restrict__ score, void* __restrict__ O,
+    float* __restrict__ lse_own, float* __restrict__ lse_tot) {
+  __shared__ dec::MergeSmem<KM> sm;
+  __shared__ __align__(16) uint16_t qh[D];
+  __shared__ __align__(16) float qf[D];
+  __shared__ int sel_c[KM];
+  extern __shared__ __align__(16) float rdyn[];
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave, nw = blockDim.x / kWave;
+  const long long r = blockIdx.x;
+  const int h = (int)(r % dm.H), i = (int)((r / dm.H) % dm.Tq);
+  const int b = (int)(r / ((long long)dm.H * dm.Tq));
+  const int g = h / dm.G;
+  const long long pos = dm.q_pos0 + i;
+  const int ncand = dm.ncand(pos);
+  const int NS = dm.K + dm.nlocal_max();
+  float* po = rdyn;             // [NS][D]
+  float* pl = po + NS * D;      // [NS]
+  float* psc = pl + NS;         // [K]
+  const long long kv_base = ((long long)b * dm.Tcap * dm.Hkv + g) * D;
+  const long long kv_stride = (long long)dm.Hkv * D;
+  for (int e = t; e < D; e += blockDim.x) {  // read before the merge's barriers
+    if (BF16) qh[e] = reinterpret_cast<const uint16_t*>(Q)[r * D + e];
+    else qf[e] = reinterpret_cast<const float*>(Q)[r * D + e];
+  }
+  const int cnt = dec::merge_rank<KM, NL>(dm, r, ncand, ws_s, ws_i, nsplit, kSplitMfma, sm);
+  const long long o = r * dm.K;
+  if (t < cnt) {  // the selected entries in chunk order
+    const int p = dec::merge_place<KM>(sm, t, cnt);
+    const int c = dec::merge_chunk(sm.sel[t]);
+    const float s = dec::merge_score(sm.sel[t]);
+    sel_c[p] = c;
+    psc[p] = s;
+    idx[o + p] = c;
+    score[o + p] = s;
+  }
+  for (int k = cnt + t; k < dm.K; k += blockDim.x) {
+    idx[o + k] = -1;
+    score[o + k] = -INFINITY;
+    psc[k] = -INFINITY;
+  }
+  __syncthreads();
+  for (int slot = w; slot < NS; slot += nw) {  // uniform per wavefront
+    long long key0;
+    int nk;
+    bool have;
+    if (slot < dm.K) {  // a merged list is ascending with distinct candidate ids: all count
+      have = slot < cnt;
+      key0 = have ? (long long)sel_c[slot] * dm.S : 0;
+      nk = kChunk;
+    } else {  // local chunk l0 / S + slot - K, keys from max(l0, its start) to min(pos, its end)
+      const long long l0 = dm.lstart(pos), cc = l0 / kChunk + (slot - dm.K);
+      have = cc <= pos / kChunk;
+      key0 = cc * dm.S > l0 ? cc * dm.S : l0;
+      nk = (int)(min(pos, cc * dm.S + dm.S - 1) - key0) + 1;
+    }
+    if (!have) {
+      if (lane == 0) pl[slot] = -INFINITY;
+      continue;
+    }
+    if (BF16) {
+      SlotRegs<D> rg;
+      slot_load<D>(rg, reinterpret_cast<const uint16_t*>(K), reinterpret_cast<const uint16_t*>(V),
+                   kv_base, kv_stride, key0, nk);
+      slot_compute<D>(rg, dm, qh, nk, po + slot * D, pl + slot);
+    } else {
+      decode_slot_f32<D>(dm, qf, reinterpret_cast<const float*>(K),
+                         reinterpret_cast<const float*>(V), kv_base, key0, nk, po + slot * D,
+                         pl + slot);
+    }
+  }
+  __syncthreads();
+  if (w == 0) combine_row<BF16, D>(dm, r, psc, po, pl, O, lse_own, lse_tot);
 }
 
 // The slot kernels (one wavefront per selected or local chunk of a row, no
@@ -447,6 +549,51 @@ hipError_t launch_decode_merged_t(const Dims& dm, const void* Q, const void* K, 
   return hipGetLastError();
 }
 
+template <bool BF16, int D, int KM, int NL>
+hipError_t launch_decode_row_t(const Dims& dm, const void* Q, const void* K, const void* V,
+                               const float* ws_s, const int* ws_i, int nsplit, int32_t* idx,
+                               float* score, void* O, float* lse_own, float* lse_tot,
+                               hipStream_t st) {
+  const long long rows = (long long)dm.B * dm.Tq * dm.H;
+  const int NS = dm.K + dm.nlocal_max();
+  // enough wavefronts for the merge's list entries and for up to 16 slots at once
+  const int nt = std::min(kRowThreads<D>, std::max((nsplit * KM + kWave - 1) / kWave * kWave,
+                                                   kWave * std::min(NS, 16)));
+  if (nsplit * KM > nt) return hipErrorInvalidValue;
+  const size_t smem = ((size_t)NS * D + NS + dm.K) * sizeof(float);
+  const void* fn = reinterpret_cast<const void*>(k_decode_row<BF16, D, KM, NL>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_decode_row<BF16, D, KM, NL>), dim3((unsigned)rows), dim3(nt), smem, st,
+                     dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O, lse_own, lse_tot);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t launch_decode_row_d(const Dims& dm, const void* Q, const void* K, const void* V,
+                               const float* ws_s, const int* ws_i, int nsplit, int km,
+                               int32_t* idx, float* score, void* O, float* lse_own,
+                               float* lse_tot, hipStream_t st) {
+  const bool nl16 = nsplit <= 16;  // km = 64 holds at most 16 lists
+  if (km == 16 && nl16)
+    return launch_decode_row_t<BF16, D, 16, 16>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                                lse_own, lse_tot, st);
+  if (km == 16 && nsplit <= 24)
+    return launch_decode_row_t<BF16, D, 16, 24>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                                lse_own, lse_tot, st);
+  if (km == 16)
+    return launch_decode_row_t<BF16, D, 16, 32>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                                lse_own, lse_tot, st);
+  if (km == 32 && nl16)
+    return launch_decode_row_t<BF16, D, 32, 16>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                                lse_own, lse_tot, st);
+  if (km == 32)
+    return launch_decode_row_t<BF16, D, 32, 32>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                                lse_own, lse_tot, st);
+  return launch_decode_row_t<BF16, D, 64, 16>(dm, Q, K, V, ws_s, ws_i, nsplit, idx, score, O,
+                                              lse_own, lse_tot, st);
+}
+
 template <bool BF16, int D>
 hipError_t launch_decode_merged_d(const Dims& dm, const void* Q, const void* K, const void* V,
                                   const float* ws_s, const int* ws_i, int nsplit, int km,
@@ -502,6 +649,28 @@ hipError_t launch_decode_merged(const Dims& dm, const void* Q, const void* K, co
                                                         score, O, lse_own, lse_tot, ws, st)
                     : launch_decode_merged_d<false, 128>(dm, Q, K, V, ws_s, ws_i, nsplit, km, idx,
                                                          score, O, lse_own, lse_tot, ws, st);
+}
+
+hipError_t launch_decode_row(const Dims& dm, const void* Q, const void* K, const void* V,
+                             const float* ws_s, const int* ws_i, int nsplit, int km, int32_t* idx,
+                             float* score, void* O, float* lse_own, float* lse_tot,
+                             hipStream_t st) {
+  if (km != 16 && km != 32 && km != 64) return hipErrorInvalidValue;
+  if (nsplit < 1 || nsplit > 32 || nsplit * km > 1024) return hipErrorInvalidValue;
+  if ((long long)dm.B * dm.Tq * dm.H > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (dm.bf16)
+    return dm.d == 64 ? launch_decode_row_d<true, 64>(dm, Q, K, V, ws_s, ws_i, nsplit, km, idx,
+                                                      score, O, lse_own, lse_tot, st)
+                      : launch_decode_row_d<true, 128>(dm, Q, K, V, ws_s, ws_i, nsplit, km, idx,
+                                                       score, O, lse_own, lse_tot, st);
+  return dm.d == 64 ? launch_decode_row_d<false, 64>(dm, Q, K, V, ws_s, ws_i, nsplit, km, idx,
+                                                     score, O, lse_own, lse_tot, st)
+                    : launch_decode_row_d<false, 128>(dm, Q, K, V, ws_s, ws_i, nsplit, km, idx,
+                                                      score, O, lse_own, lse_tot, st);
+}
+
+bool decode_row_applies(const Dims& dm, int nsplit, int km) {
+  return nsplit * km <= (dm.d == 128 ? kRowThreads<128> : kRowThreads<64>);
 }
 
 size_t attend_ws_bytes(const Dims& dm) {

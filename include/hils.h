@@ -197,8 +197,10 @@ hils_status hils_attend_fuse(const hils_dims* dims, const void* Q, const void* K
  * bit, idx and score included). For a few rows it enqueues the candidate splits
  * scored into local top-K lists, then one workgroup per (selected or local
  * chunk, row) that merges the row's lists itself and attends to its chunk, then
- * the fusion of the slots; with many slots the merge runs once per row as its
- * own kernel before the slots. ws is one workspace of
+ * the fusion of the slots; with many rows (128 and more, e.g. sequences decoding
+ * together) one workgroup per row merges its lists once, attends every slot and
+ * fuses them; in between the merge runs once per row as its own kernel before
+ * the slots. ws is one workspace of
  * hils_workspace_size(.., HILS_OP_DECODE, ..) bytes for all of it (it may be
  * larger than either call's alone); its contents do not matter. K and V may be
  * pinned host memory as for hils_attend_fuse; lse_own and lse_tot may be NULL.

@@ -2,7 +2,8 @@
 
 Its results are those of hils_score_topk followed by hils_attend_fuse, bit for
 bit (selection, scores, outputs, log-masses), also where its slot kernel merges
-the candidate splits' lists itself (few rows, at most 32 splits). Also checked
+the candidate splits' lists itself (few rows, at most 32 splits) and where one
+workgroup per row merges, attends and fuses (128 rows and more). Also checked
 against the oracle, over many steps in a row on one workspace (whose contents do
 not matter), with windows, K = 64, several rows per call, rows with no
 candidates, d = 128, float32 and a host-resident cache.
@@ -52,6 +53,16 @@ CASES = {
     # 17 splits of 32-entry lists at the last positions (the 24-list merge)
     "bf16_k32_splits17": (synth.small("dec_k32s", B=1, T=17 * 128 * 64 + 128, H=4, Hkv=2,
                                       d=64, K=32, dtype="bf16"), 0, 1),
+    # 128 rows per call (4 sequences x 8 positions x 4 heads): one workgroup per
+    # row merges, attends every slot and fuses in LDS
+    "bf16_rows128": (synth.small("dec_r128", B=4, T=10240, H=4, Hkv=2, d=64, K=16,
+                                 dtype="bf16"), 0, 8),
+    "bf16_d128_rows128": (synth.small("dec_r128d", B=2, T=10240, H=8, Hkv=2, d=128, K=16,
+                                      dtype="bf16"), 0, 8),
+    "bf16_window_k32_rows128": (synth.small("dec_r128w", B=4, T=10240, H=4, Hkv=4, d=64, K=32,
+                                            dtype="bf16"), 512, 8),
+    "f32_rows128": (synth.small("dec_r128f", B=4, T=10240, H=4, Hkv=2, d=64, K=8,
+                                dtype="f32"), 0, 8),
 }
 
 
