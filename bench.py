@@ -76,6 +76,10 @@ def parse():
     ap.add_argument("--counters", nargs=2, metavar=("WORKLOAD", "DIR"),
                     help="summarise the counter passes DIR/p1..p4 of a --pmc-run of WORKLOAD "
                          "(FETCH_SIZE, WRITE_SIZE, SQ and TCC counters) into profiles/")
+    ap.add_argument("--trace", nargs=2, metavar=("WHAT", "STATS_CSV"),
+                    help="summarise a rocprofv3 --kernel-trace --stats kernel_stats.csv into "
+                         "profiles/kernel_trace_<WHAT>.txt (WHAT: bench_all_workloads for a "
+                         "run of bench.py --no-cpu-baseline, or a --pmc-run workload)")
     return ap.parse_args()
 
 
@@ -219,6 +223,40 @@ def write_counter_summary(workload, directory):
             f"{l2:7.3f} {avg(d.get('SQ_INSTS_LDS', [])):10.3g} "
             f"{avg(d.get('SQ_LDS_BANK_CONFLICT', [])):10.3g} {d['_vgpr'][0]:>5s}")
     out = os.path.join(PROFILES, f"counters_{workload}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def write_trace_summary(what, stats_csv):
+    """profiles/kernel_trace_<what>.txt: per kernel, calls and duration statistics
+    from a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    if what == "bench_all_workloads":
+        desc = ("one bench.py run: every workload and variant of the bench (7B GQA prefill "
+                "headline, 128K decode with K=16, K=32 + 512-key window, pinned host cache, 16 "
+                "positions per call and 16 sequences together, 345M prefill, 7B with group-max "
+                "selection, 345M main setting, training step plain / Q-Cal / main setting); per "
+                "kernel over all calls of the run (the per-workload figures are in bench.py's "
+                "JSON line)")
+        cmd = "python3 bench.py --no-cpu-baseline"
+    else:
+        desc = (f"bench.py --pmc-run {what}: the workload's inputs, one forward call of each "
+                "kernel, then 3 steps and a 256 MiB elementwise copy")
+        cmd = f"python3 bench.py --pmc-run {what}"
+    lines = [f"rocprofv3 kernel trace on MI355X (gfx950) of {desc}.",
+             "command: cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats "
+             f"--output-format csv -d <dir> -o t -- {cmd}",
+             f"then: python3 bench.py --trace {what} <dir>/t_kernel_stats.csv", "",
+             f"{'kernel':60s} {'calls':>8s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+             f"{'total_ms':>10s}"]
+    for r in csv.DictReader(open(stats_csv)):
+        n = r["Name"].replace("void ", "").replace("hils::(anonymous namespace)::", "")
+        n = n.split("(")[0] if not n.startswith("__amd") else n
+        lines.append(f"{n[:60]:60s} {int(r['Calls']):8d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:10.2f}")
+    out = os.path.join(PROFILES, f"kernel_trace_{what}.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -544,6 +582,9 @@ def main():
         return
     if args.counters:
         write_counter_summary(*args.counters)
+        return
+    if args.trace:
+        write_trace_summary(*args.trace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -445,6 +445,10 @@ __device__ __forceinline__ Smem carve(char* base, int R, int K, int ncr, int nlo
   return s;
 }
 
+// misc[kNextChunk]: the next selected chunk a wavefront claims (misc[0 .. 24)
+// serve the set-up's scans)
+constexpr int kNextChunk = 28;
+
 // In-place exclusive scan of n ints with kThreads threads; returns the total.
 template <int kThreads>
 __device__ __forceinline__ int block_exclusive_scan(int* a, int n, int* scratch) {
@@ -944,6 +948,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
     if (lse_own) lse_own[r] = lo;
     if (lse_tot) lse_tot[r] = lam;
   }
+  if (t == 0) sm.misc[kNextChunk] = kWaves;  // the chunks after each wave's first
   __syncthreads();
   // own contribution to fixed point: columns 2k, 2k + 1 become the 64-bit word
   // b 2^32 + a of their signed values
@@ -992,12 +997,17 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
     }
   }
 
-  // ---- selected chunks: chunk u belongs to wavefront u mod kWaves; no barriers.
-  // A wave waiting for its chunk's fragments is covered by the other waves of
-  // its SIMD (more waves per SIMD measured faster than a second fragment set).
-  for (int u = w; u < nnz; u += kWaves) {
+  // ---- selected chunks: wavefront w starts with chunk w, then claims the next
+  // unclaimed one from an LDS counter (chunks hold different numbers of tiles,
+  // so a fixed share leaves some wavefronts idle at the end); no barriers. A wave
+  // waiting for its chunk's fragments is covered by the other waves of its SIMD
+  // (more waves per SIMD measured faster than a second fragment set).
+  for (int u = w; u < nnz;) {
     if (!kFirst || u != w) load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[u]) * C::CH);
+    int nxt = 0;
+    if (lane == 0) nxt = atomicAdd(sm.misc + kNextChunk, 1);  // in flight during the tiles
     run_chunk<D>(f, sm, rs, Ksel, sm.cur[u], scale2);
+    u = __builtin_amdgcn_readfirstlane(nxt);
   }
   __syncthreads();
 
