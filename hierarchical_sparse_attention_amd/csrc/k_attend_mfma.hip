@@ -376,6 +376,14 @@ __host__ __device__ __forceinline__ int acc_col(int db, int g, int r) {
   return 64 * (db >> 2) + 16 * g + 4 * (db & 3) + r;
 }
 
+// misc: [0, 24) the set-up's scans; [kNextChunk] the next selected chunk a
+// wavefront claims
+constexpr int kNextChunk = 28, kMiscInts = 32;
+// Selected chunks of at least kHeavyRows rows come first in the claim order;
+// both groups keep ascending chunk order, which the workgroups of a kv head (on
+// one XCD) share, so a chunk's fragments serve several of them from L2
+constexpr int kHeavyRows = 33;
+
 struct Smem {
   int* acc;       // [R][AP] fixed point (float during the own-chunk phase)
   uint16_t* qs;   // [R][QP] the workgroup's query rows (bf16; none with QG)
@@ -412,7 +420,7 @@ __host__ __device__ inline size_t smem_bytes(int R, int K, int ncr, int nloc) {
   return up16((size_t)R * Cfg<D>::AP * 4) + (QG ? 0 : up16((size_t)R * Cfg<D>::QP * 2)) +
          (QG ? up16((size_t)R * K * 2) : 2 * up16((size_t)R * K * 4)) +
          4 * up16((size_t)(ncr + 1) * 4) + 7 * up16((size_t)R * 4) +
-         2 * up16((size_t)R * ((K + 7) / 8) * 4) + up16((size_t)R * nloc * 8) + 32 * 4;
+         2 * up16((size_t)R * ((K + 7) / 8) * 4) + up16((size_t)R * nloc * 8) + kMiscInts * 4;
 }
 
 template <int D>
@@ -445,9 +453,6 @@ __device__ __forceinline__ Smem carve(char* base, int R, int K, int ncr, int nlo
   return s;
 }
 
-// misc[kNextChunk]: the next selected chunk a wavefront claims (misc[0 .. 24)
-// serve the set-up's scans)
-constexpr int kNextChunk = 28;
 
 // In-place exclusive scan of n ints with kThreads threads; returns the total.
 template <int kThreads>
@@ -781,12 +786,14 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
   }
   __syncthreads();
   for (int c = t; c < ncr; c += kThreads) {
-    sm.off[c] = sm.cnt[c];
-    sm.nz[c] = sm.cnt[c] > 0 ? 1 : 0;
+    const int n = sm.cnt[c];
+    sm.off[c] = n;
+    sm.nz[c] = n >= kHeavyRows ? 1 << 16 : (n > 0 ? 1 : 0);  // heavy and light counts in one word
   }
   __syncthreads();
   block_exclusive_scan<kThreads>(sm.off, ncr, sm.misc);
-  const int nnz = block_exclusive_scan<kThreads>(sm.nz, ncr, sm.misc + 12);
+  const int nzt = block_exclusive_scan<kThreads>(sm.nz, ncr, sm.misc + 12);
+  const int nheavy = nzt >> 16, nnz = nheavy + (nzt & 0xFFFF);  // selected chunks
   for (int c = t; c < ncr; c += kThreads) sm.cur[c] = sm.off[c];
   __syncthreads();
   {
@@ -819,9 +826,14 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
     sm.pz[t] = z8;
   }
   __syncthreads();
-  // compacted list of non-empty chunks (chunk c goes to slot nz[c])
-  for (int c = t; c < ncr; c += kThreads)
-    if (sm.cnt[c] > 0) sm.cur[sm.nz[c]] = c;
+  // compacted list of the selected chunks in claim order: the heavy ones, then
+  // the rest, each in ascending chunk order (the wavefronts claim them in list
+  // order, so the last ones claimed are short and the wavefronts finish together)
+  for (int c = t; c < ncr; c += kThreads) {
+    const int n = sm.cnt[c], x = sm.nz[c];
+    if (n >= kHeavyRows) sm.cur[x >> 16] = c;
+    else if (n > 0) sm.cur[nheavy + (x & 0xFFFF)] = c;
+  }
   // per-row fixed point: every partial sum of a row is a sub-convex combination
   // of the values of the chunks it reads, so its magnitude is at most that
   // row's max|V| < 2^ex, mapped below 2^21 (each term then fits the one-fma
