@@ -395,13 +395,30 @@ def prefill_setup(torch, hsa, synth, dev, wname, K=None, group=False, window=0, 
     return w, x, t, f, calls
 
 
-def measure_prefill(torch, ev_ms, w, f, calls, reps, workload, window=0):
+def time_in_step(torch, stream, calls, reps):
+    """Average duration of each call with the calls run in step order (each one
+    sees the caches the previous ones left), HIP events between the calls on the
+    kernels' stream."""
+    names = list(calls)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(reps)]
+    for r in range(reps):
+        evs[r][0].record(stream)
+        for i, k in enumerate(names):
+            calls[k]()
+            evs[r][i + 1].record(stream)
+    torch.cuda.synchronize()
+    return {k: sum(evs[r][i].elapsed_time(evs[r][i + 1]) for r in range(reps)) / reps
+            for i, k in enumerate(names)}
+
+
+def measure_prefill(torch, ev_ms, w, f, calls, reps, workload, window=0, stream=None):
     for fn in calls.values():
         fn()
     torch.cuda.synchronize()
-    km = {k: ev_ms(fn, reps) for k, fn in calls.items()}
-    # calls of a few tens of microseconds: with a handful of repeats the first
-    # launch's latency would weigh on the average, so they are timed over 100
+    km = time_in_step(torch, stream, calls, reps)
+    # calls of a few tens of microseconds: an event pair around one launch weighs
+    # on them, so they are timed over 100 launches back to back
     for k, fn in calls.items():
         if km[k] < 0.1:
             km[k] = ev_ms(fn, 100)
@@ -646,7 +663,7 @@ def main():
     ms = wall_ms(step, args.steps)
     head = measure_prefill(torch, ev_ms, hw, hf, {k: hcalls[k] for k in
                                                    ("summarize", "score_topk", "attend_fuse")},
-                           args.steps, "prefill_7b_gqa")
+                           args.steps, "prefill_7b_gqa", stream=stream)
     head["step_ms_wallclock"] = ms
     dominant = max(head["kernels_ms"], key=head["kernels_ms"].get)
     roof = dict(head["roofline"][dominant])
@@ -725,7 +742,7 @@ def main():
     for rname, wname, opt in runs:
         w, x, t, f, calls = prefill_setup(torch, hsa, synth, dev, wname, **opt)
         rec = measure_prefill(torch, ev_ms, w, f, calls, 5, rname if not opt else "-",
-                              opt.get("window", 0))
+                              opt.get("window", 0), stream=stream)
         if opt.get("group"):
             rec["selection"] = "group max over the 4 query heads of each kv head"
         if opt.get("qcal"):
