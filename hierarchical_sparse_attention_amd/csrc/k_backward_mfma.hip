@@ -450,6 +450,39 @@ __global__ __launch_bounds__(kFillThreads) void k_sel_fill(Dims dm, int nblk, co
   }
 }
 
+// ------------------------------------------------------------------ key-side order
+// Launch order of the key side's workgroups, index L = (c B + b) Hkv + g: by
+// their 32-row tiles (the chunk's own rows and its selecting rows, over the G
+// heads), in buckets of log2 of the tile count, the largest bucket first. One
+// workgroup; the order within a bucket is free (every workgroup writes only its
+// own outputs, so the results do not depend on it).
+constexpr int kOrderThreads = 1024;
+__global__ __launch_bounds__(kOrderThreads) void k_bwd_order(Dims dm, const int* __restrict__ llen,
+                                                            int* __restrict__ order) {
+  __shared__ int hist[16], fill[16];
+  const int NC = dm.Tkv / dm.S;
+  const int n = NC * dm.Hkv * dm.B;
+  const int t = threadIdx.x;
+  if (t < 16) hist[t] = fill[t] = 0;
+  __syncthreads();
+  auto bucket = [&](int L) {
+    const int g = L % dm.Hkv, b = (L / dm.Hkv) % dm.B, c = L / (dm.Hkv * dm.B);
+    int rows = 0;
+    for (int hh = 0; hh < dm.G; ++hh)
+      rows += kChunk + llen[((long long)b * dm.H + (long long)g * dm.G + hh) * NC + c];
+    const int tiles = (rows + 31) / 32;
+    return min(15, 31 - __clz(max(tiles, 1)));
+  };
+  for (int L = t; L < n; L += kOrderThreads) atomicAdd(&hist[bucket(L)], 1);
+  __syncthreads();
+  for (int L = t; L < n; L += kOrderThreads) {
+    const int bk = bucket(L);
+    int start = 0;
+    for (int x = bk + 1; x < 16; ++x) start += hist[x];
+    order[start + atomicAdd(&fill[bk], 1)] = L;
+  }
+}
+
 // ------------------------------------------------------------------ key side
 // One workgroup per (chunk, kv head, batch) with four wavefronts. The chunk's
 // own 64 rows (two 32-row tiles) followed by the rows that selected it
@@ -554,14 +587,15 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
     const uint16_t* __restrict__ dO, const float* __restrict__ ws_D,
     const int* __restrict__ lstart, const int* __restrict__ llen, const int4* __restrict__ srec,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, uint16_t* __restrict__ dQl,
-    uint16_t* __restrict__ part) {
+    uint16_t* __restrict__ part, const int* __restrict__ order) {
   extern __shared__ __align__(16) char smem_raw[];
   KSmem& sm = *reinterpret_cast<KSmem*>(smem_raw);
-  // chunk slowest, from chunk 0 up: the early chunks, which most rows can
-  // select, start first and the cheap late ones fill in
+  // the (chunk, kv head, b) of this workgroup, the ones with the most rows first
+  // (k_bwd_order): a chunk that most rows selected would otherwise run alone at
+  // the end
   const int NC = dm.Tkv / dm.S, G = dm.G;
-  const int g = blockIdx.x % dm.Hkv, b = (blockIdx.x / dm.Hkv) % dm.B,
-            c = blockIdx.x / (dm.Hkv * dm.B);
+  const int L = order[blockIdx.x];
+  const int g = L % dm.Hkv, b = (L / dm.Hkv) % dm.B, c = L / (dm.Hkv * dm.B);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 15, gl = lane >> 4;
   const float scale2 = dm.scale * kLog2e;
   const float inv_scale = 1.0f / dm.scale;
@@ -962,7 +996,7 @@ __global__ __launch_bounds__(kKThreads) void k_bwd_kv_mfma(
 struct BPlan {
   int nct, nblk;
   bool staged;  // the list fill stages the block's records in LDS
-  size_t cnt_bytes, ls_bytes, rec_bytes, part_bytes, fill_smem;
+  size_t cnt_bytes, ls_bytes, rec_bytes, part_bytes, order_bytes, fill_smem;
 };
 
 bool bwd_plan(const Dims& dm, BPlan* p) {
@@ -974,6 +1008,7 @@ bool bwd_plan(const Dims& dm, BPlan* p) {
   const size_t rows = (size_t)dm.B * dm.Tq * dm.H;
   p->cnt_bytes = (size_t)dm.B * dm.H * p->nct * p->nblk * sizeof(int);
   p->ls_bytes = (size_t)dm.B * dm.H * p->nct * sizeof(int);
+  p->order_bytes = (size_t)dm.B * dm.Hkv * p->nct * sizeof(int);
   p->rec_bytes = rows * dm.K * sizeof(int4);
   // the dQ partials, then one discard row that padding rows store to
   p->part_bytes = (rows * (dm.K + dm.nlocal_max()) + 1) * D * sizeof(uint16_t);
@@ -1016,7 +1051,8 @@ hipError_t launch_lists(const Dims& dm, const BPlan& p, const int32_t* idx, cons
 size_t backward_mfma_ws_bytes(const Dims& dm) {
   BPlan p;
   if (!bwd_plan(dm, &p)) return 0;
-  return up256(p.cnt_bytes) + 2 * up256(p.ls_bytes) + up256(p.rec_bytes) + up256(p.part_bytes);
+  return up256(p.cnt_bytes) + 2 * up256(p.ls_bytes) + up256(p.rec_bytes) + up256(p.part_bytes) +
+         up256(p.order_bytes);
 }
 
 bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void* V,
@@ -1037,6 +1073,8 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
   int4* srec = reinterpret_cast<int4*>(base);
   base += up256(p.rec_bytes);
   uint16_t* part = reinterpret_cast<uint16_t*>(base);
+  base += up256(p.part_bytes);
+  int* order = reinterpret_cast<int*>(base);
   const long long rows = (long long)dm.B * dm.Tq * dm.H;
   const unsigned rblocks = (unsigned)((rows + 31) / 32);
   const auto* dOh = reinterpret_cast<const uint16_t*>(dO);
@@ -1052,6 +1090,7 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
     *err = e;
     return true;
   }
+  hipLaunchKernelGGL(k_bwd_order, dim3(1), dim3(kOrderThreads), 0, st, dm, llen, order);
   const bool qcal = Qs != nullptr;
   const void* kvk = qcal ? reinterpret_cast<const void*>(k_bwd_kv_mfma<true>)
                          : reinterpret_cast<const void*>(k_bwd_kv_mfma<false>);
@@ -1068,7 +1107,7 @@ bool backward_mfma_try(const Dims& dm, const void* Q, const void* K, const void*
                      reinterpret_cast<const uint16_t*>(V), reinterpret_cast<const uint16_t*>(Ql),   \
                      ksum, ent, lse_l, lse_tot, dOh, ws_D, lstart, llen, srec,                      \
                      reinterpret_cast<uint16_t*>(dK), reinterpret_cast<uint16_t*>(dV),              \
-                     reinterpret_cast<uint16_t*>(dQl), part)
+                     reinterpret_cast<uint16_t*>(dQl), part, order)
   if (qcal) HILS_KV(true); else HILS_KV(false);
 #undef HILS_KV
   auto* dQh = reinterpret_cast<uint16_t*>(dQ);
