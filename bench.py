@@ -247,14 +247,23 @@ def write_trace_summary(what, stats_csv):
     lines = [f"rocprofv3 kernel trace on MI355X (gfx950) of {desc}.",
              "command: cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats "
              f"--output-format csv -d <dir> -o t -- {cmd}",
-             f"then: python3 bench.py --trace {what} <dir>/t_kernel_stats.csv", "",
-             f"{'kernel':60s} {'calls':>8s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
-             f"{'total_ms':>10s}"]
+             f"then: python3 bench.py --trace {what} <dir>/t_kernel_stats.csv",
+             "median_us: the median dispatch (from t_kernel_trace.csv beside the stats), which "
+             "leaves out the first, cold calls", "",
+             f"{'kernel':60s} {'calls':>8s} {'avg_us':>10s} {'median_us':>10s} {'min_us':>10s} "
+             f"{'max_us':>10s} {'total_ms':>10s}"]
+    durs = {}
+    trace_csv = stats_csv.replace("kernel_stats", "kernel_trace")
+    if os.path.exists(trace_csv):
+        for r in csv.DictReader(open(trace_csv)):
+            durs.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     for r in csv.DictReader(open(stats_csv)):
         n = r["Name"].replace("void ", "").replace("hils::(anonymous namespace)::", "")
         n = n.split("(")[0] if not n.startswith("__amd") else n
+        med = float(np.median(durs[r["Name"]])) if r["Name"] in durs else float("nan")
         lines.append(f"{n[:60]:60s} {int(r['Calls']):8d} {float(r['AverageNs']) / 1e3:10.2f} "
-                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                     f"{med:10.2f} {float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
                      f"{float(r['TotalDurationNs']) / 1e6:10.2f}")
     out = os.path.join(PROFILES, f"kernel_trace_{what}.txt")
     with open(out, "w") as f:
