@@ -337,41 +337,53 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
       }
     }
   };
+  // Selection by the group maximum. With KM <= 32 every wavefront ranks all 64
+  // positions (lane = position) over its own share of the candidates (16-wide
+  // sub-blocks hh, hh + G, ... of each 64-candidate block, in chunk order), and
+  // the G sorted lists of a position are merged at the end (the position's top
+  // KM lies in the union of its lists' tops): all 64 lanes work where one
+  // position per lane over all candidates would keep 64 / G lanes. With KM = 64
+  // the G lists do not fit the score blocks' LDS, and each wavefront ranks its
+  // own 64 / G positions over all candidates.
+  constexpr bool kSplit = KM <= 32;
+  const int rp = kSplit ? lane : sp;  // the position this lane ranks
+  const int rn = kSplit ? (lane < npos ? dm.ncand(dm.q_pos0 + i0 + lane) : 0) : my_n;
   auto gscore = [&](int j) -> float {
-    float v = sS[0][sp][j];
+    float v = sS[0][rp][j];
 #pragma unroll
-    for (int x = 1; x < G; ++x) v = fmaxf(v, sS[x][sp][j]);
+    for (int x = 1; x < G; ++x) v = fmaxf(v, sS[x][rp][j]);
     return v;
   };
 
   TopList<KM> top;
   top.init();
+  bool first = true;  // the list's first sub-block is sorted in one go
   for (int c0 = 0; c0 < nmax; c0 += 64) {
     score_blocks(c0, [&](int mb, int nb, const floatx4& v) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) sS[hh][16 * mb + 4 * g + r][16 * nb + c] = v[r];
     });
     __syncthreads();
-    const int lim = min(64, my_n - c0);
-    int sb0 = 0;
-    if (c0 == 0) {
-      float xs[16];
-      int xc[16];
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) xs[jj] = gscore(jj);  // unconditional: in flight together
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const bool ok = jj < lim;
-        xs[jj] = ok ? xs[jj] : -INFINITY;
-        xc[jj] = ok ? jj : 0x7fffffff;
-      }
-      sort16(xs, xc);
-#pragma unroll
-      for (int k = 0; k < 16 && k < KM; ++k) top.s[k] = xs[k], top.c[k] = xc[k];
-      sb0 = 1;
-    }
+    const int lim = min(64, rn - c0);
 #pragma unroll 1
-    for (int sb = sb0; sb < 4; ++sb) {
+    for (int sb = kSplit ? hh : 0; sb < 4; sb += kSplit ? G : 1) {
+      if (first) {
+        float xs[16];
+        int xc[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) xs[jj] = gscore(16 * sb + jj);  // all in flight together
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const bool ok = 16 * sb + jj < lim;
+          xs[jj] = ok ? xs[jj] : -INFINITY;
+          xc[jj] = ok ? c0 + 16 * sb + jj : 0x7fffffff;
+        }
+        sort16(xs, xc);
+#pragma unroll
+        for (int k = 0; k < 16 && k < KM; ++k) top.s[k] = xs[k], top.c[k] = xc[k];
+        first = false;
+        continue;
+      }
       const float theta = top.s[KM - 1];
       // unconditional reads, combined without short-circuit (all in flight together)
       float xv[16];
@@ -394,6 +406,41 @@ __global__ __launch_bounds__(64 * G) void k_score_mfma_group(Dims dm, int nc,
         top.insert(have ? x : -INFINITY, c0 + 16 * sb + cj);
         x = xn;
       }
+    }
+    __syncthreads();
+  }
+  if constexpr (kSplit) {
+    // the G lists of every position through LDS (the score blocks are free now),
+    // then wavefront hh merges those of its positions by (score desc, chunk asc)
+    float* ml = reinterpret_cast<float*>(gsm2);            // [G][KM][64]
+    int* mi = reinterpret_cast<int*>(gsm2) + G * KM * 64;  // [G][KM][64]
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      ml[(hh * KM + k) * 64 + lane] = top.s[k];
+      mi[(hh * KM + k) * 64 + lane] = top.c[k];
+    }
+    __syncthreads();
+    int pk[G];
+#pragma unroll
+    for (int x = 0; x < G; ++x) pk[x] = 0;
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      float bs = -INFINITY;
+      int bc = 0x7fffffff, bx = 0;
+#pragma unroll
+      for (int x = 0; x < G; ++x) {
+        const int o = (x * KM + min(pk[x], KM - 1)) * 64 + sp;
+        const float vs = pk[x] < KM ? ml[o] : -INFINITY;
+        const int vc = pk[x] < KM ? mi[o] : 0x7fffffff;
+        const bool better = vs > bs || (vs == bs && vc < bc);
+        bs = better ? vs : bs;
+        bc = better ? vc : bc;
+        bx = better ? x : bx;
+      }
+      top.s[k] = bs;
+      top.c[k] = bc;
+#pragma unroll
+      for (int x = 0; x < G; ++x) pk[x] += x == bx ? 1 : 0;
     }
     __syncthreads();
   }
