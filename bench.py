@@ -79,7 +79,9 @@ def parse():
     ap.add_argument("--trace", nargs=2, metavar=("WHAT", "STATS_CSV"),
                     help="summarise a rocprofv3 --kernel-trace --stats kernel_stats.csv into "
                          "profiles/kernel_trace_<WHAT>.txt (WHAT: bench_all_workloads for a "
-                         "run of bench.py --no-cpu-baseline, or a --pmc-run workload)")
+                         "run of bench.py --no-cpu-baseline, bench_headline for one of "
+                         "bench.py --no-cpu-baseline --no-extra-configs, or a --pmc-run "
+                         "workload)")
     return ap.parse_args()
 
 
@@ -240,6 +242,12 @@ def write_trace_summary(what, stats_csv):
                 "kernel over all calls of the run (the per-workload figures are in bench.py's "
                 "JSON line)")
         cmd = "python3 bench.py --no-cpu-baseline"
+    elif what == "bench_headline":
+        desc = ("the bench's headline run: the 7B GQA prefill steps with per-head selection "
+                "(warmup and timed steps), then the 128K decode with K=16, its graph replays "
+                "and eager steps; k_attend_mfma<128, false> here is the headline's attention "
+                "launch alone")
+        cmd = "python3 bench.py --no-cpu-baseline --no-extra-configs"
     else:
         desc = (f"bench.py --pmc-run {what}: the workload's inputs, one forward call of each "
                 "kernel, then 3 steps and a 256 MiB elementwise copy")
