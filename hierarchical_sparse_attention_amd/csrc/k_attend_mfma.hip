@@ -675,20 +675,21 @@ __device__ __forceinline__ void run_chunk_lds(const Frag<D>& f, const Smem& sm, 
 // step, where the next chunk's first tile is read ahead, so the claim's latency
 // stays hidden behind the earlier tiles); returns it, wave-uniform.
 template <int D>
-__device__ __forceinline__ int run_chunk(const Frag<D>& f, const Smem& sm, const RowSrc& rs,
+__device__ __forceinline__ int run_chunk(Frag<D>& f, const uint4* __restrict__ KVf,
+                                         long long kvf_base, const Smem& sm, const RowSrc& rs,
                                          int Ksel, int c, int nxt, int nnz, float scale2,
                                          TileIn<D>& in) {
   const int col = threadIdx.x & 15;
   const int e0 = sm.off[c], n = sm.cnt[c];
   const int nstep = (n + 15) / 16;
-  int un = nnz;
+  int un = nnz, cn = -1;
   for (int st = 0; st < nstep; ++st) {
     TileIn<D> nx;
     int ce0 = e0, cnn = n, ce = 16 * (st + 1) + col;
     if (st + 1 == nstep) {
       un = __builtin_amdgcn_readfirstlane(nxt);
       if (un < nnz) {
-        const int cn = sm.cur[un];
+        cn = __builtin_amdgcn_readfirstlane(sm.cur[un]);
         ce0 = sm.off[cn], cnn = sm.cnt[cn], ce = col;
       }
     }
@@ -696,6 +697,9 @@ __device__ __forceinline__ int run_chunk(const Frag<D>& f, const Smem& sm, const
     floatx4 o[D / 16];
     float z;
     tile_sel<D>(f, in.q, scale2, !in.slow, o, &z);
+    // last step: the products of this chunk are done with f, so the next chunk's
+    // fragments load while this tile accumulates
+    if (cn >= 0) load_frag<D>(f, KVf, kvf_base + (long long)cn * Cfg<D>::CH);
     if (in.v) accumulate_tile<D>(sm, o, z, in.rho, in.lw, in.lm);
     in = nx;
   }
@@ -1073,11 +1077,13 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void k_attend_mfma(
       read_entry<D>(sm, rs, Ksel, sm.off[c], sm.cnt[c], col, &tin.v, &tin.rho, &tin.slow,
                     &tin.lw, &tin.lm, tin.q);
     }
+    // the first chunk's fragments load here (or earlier, see kFirst); every later
+    // chunk's during the last tile of the chunk before it
+    if (!kFirst && w < nnz) load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[w]) * C::CH);
     for (int u = w; u < nnz;) {
-      if (!kFirst || u != w) load_frag<D>(f, KVf, kvf_base + (long long)(sm.cur[u]) * C::CH);
       int nxt = 0;
       if (lane == 0) nxt = atomicAdd(sm.misc + kNextChunk, 1);  // in flight during the tiles
-      u = run_chunk<D>(f, sm, rs, Ksel, sm.cur[u], nxt, nnz, scale2, tin);
+      u = run_chunk<D>(f, KVf, kvf_base, sm, rs, Ksel, sm.cur[u], nxt, nnz, scale2, tin);
     }
   } else {
     for (int u = w; u < nnz;) {
