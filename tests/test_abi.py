@@ -117,3 +117,21 @@ def test_binding_refuses_cpu_tensors():
     Ql = torch.zeros(1, 2, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         hsa.summarize(K, Ql)
+
+
+@pytest.mark.parametrize("B,H", [(1, 16), (8, 16), (16, 16), (4, 32)])
+def test_decode_workspace_covers_both_calls(B, H):
+    """hils_decode takes the two calls (score_topk, then attend_fuse) where its
+    merged or per-row plans do not apply: in the first chunk, with no
+    candidates, and for a batch of 128 rows and more at shapes the per-row
+    kernel does not take. Wherever it may take them, its workspace is at least
+    what either call needs, so one workspace sized for a batch serves every
+    position."""
+    for p in (0, 1, 63, 64, 65, 1000, 4096, 65536, 131071):
+        d = base(B=B, Tq=1, Tkv=p + 1, q_pos0=p, H=H, Hkv=H, K=16)
+        st_dec, dec = ws_size(d, hsa.OP_DECODE)
+        st_sc, sc = ws_size(d, hsa.OP_SCORE_TOPK)
+        st_at, at = ws_size(d, hsa.OP_ATTEND_FUSE)
+        assert st_dec == st_sc == st_at == 0, (p, st_dec, st_sc, st_at)
+        if B * H >= 128 or p < 64:
+            assert dec >= max(sc, at), (B, H, p, dec, sc, at)
