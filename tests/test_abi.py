@@ -125,8 +125,9 @@ def test_decode_workspace_covers_both_calls(B, H):
     merged or per-row plans do not apply: in the first chunk, with no
     candidates, and for a batch of 128 rows and more at shapes the per-row
     kernel does not take. Wherever it may take them, its workspace is at least
-    what either call needs, so one workspace sized for a batch serves every
-    position."""
+    what either call needs; and it never shrinks as the cache grows, so a
+    workspace sized for the last position of a decode serves every earlier one."""
+    prev = 0
     for p in (0, 1, 63, 64, 65, 1000, 4096, 65536, 131071):
         d = base(B=B, Tq=1, Tkv=p + 1, q_pos0=p, H=H, Hkv=H, K=16)
         st_dec, dec = ws_size(d, hsa.OP_DECODE)
@@ -135,3 +136,5 @@ def test_decode_workspace_covers_both_calls(B, H):
         assert st_dec == st_sc == st_at == 0, (p, st_dec, st_sc, st_at)
         if B * H >= 128 or p < 64:
             assert dec >= max(sc, at), (B, H, p, dec, sc, at)
+        assert dec >= prev, (B, H, p, dec, prev)
+        prev = dec
